@@ -1,0 +1,48 @@
+"""Reference GEMM on dequantized NVFP4 operands (oracle; test infrastructure only).
+
+The pages place the format in the three linear-layer GEMMs of training, forward, backward
+(activation gradient) and weight gradient (artiverse.ca "NVIDIA's 4-bit floating point pushes
+AI training limits", paragraph on which parts run in 4-bit), and in the expert GEMMs of the
+mixture-of-experts layers ("Nemotron NVFP4" explainer, "The model underneath").
+
+Reading R13: D[m, n] = sum_k A_hat[m, k] * B_hat[n, k] with both operands stored along K
+("TN"); the reference is computed in binary64 (numpy/BLAS dgemm, whose rounding error
+~K * 2^-53 is far below the acceptance bound). A GPU result D (FP32 accumulation, FP32 output)
+is accepted iff |D - D64| <= 1e-5 * sum_k |A_hat[m,k]| |B_hat[n,k]| for every element.
+Reading R14: the grouped GEMM is one such GEMM per group g over rows
+m_offsets[g]..m_offsets[g+1] of A and rows g*N..(g+1)*N of the stacked B.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def gemm_fp64(a_hat: np.ndarray, b_hat: np.ndarray) -> np.ndarray:
+    """D64 = A_hat @ B_hat^T in binary64."""
+    return np.asarray(a_hat, np.float64) @ np.asarray(b_hat, np.float64).T
+
+
+def gemm_bound(a_hat: np.ndarray, b_hat: np.ndarray, rel: float = 1e-5) -> np.ndarray:
+    """Per-element acceptance bound rel * sum_k |a||b|."""
+    return rel * (np.abs(np.asarray(a_hat, np.float64)) @ np.abs(np.asarray(b_hat, np.float64)).T)
+
+
+def grouped_gemm_fp64(a_hat, b_hat, m_offsets, n: int) -> np.ndarray:
+    """Per-group D_g = A_g @ B_g^T stacked along rows; A_g rows come from m_offsets."""
+    off = np.asarray(m_offsets, dtype=np.int64)
+    out = np.zeros((int(off[-1]) - int(off[0]), n), dtype=np.float64)
+    for g in range(len(off) - 1):
+        lo, hi = int(off[g]) - int(off[0]), int(off[g + 1]) - int(off[0])
+        if hi > lo:
+            out[lo:hi] = gemm_fp64(a_hat[lo:hi], b_hat[g * n:(g + 1) * n])
+    return out
+
+
+def grouped_gemm_bound(a_hat, b_hat, m_offsets, n: int, rel: float = 1e-5) -> np.ndarray:
+    off = np.asarray(m_offsets, dtype=np.int64)
+    out = np.zeros((int(off[-1]) - int(off[0]), n), dtype=np.float64)
+    for g in range(len(off) - 1):
+        lo, hi = int(off[g]) - int(off[0]), int(off[g + 1]) - int(off[0])
+        if hi > lo:
+            out[lo:hi] = gemm_bound(a_hat[lo:hi], b_hat[g * n:(g + 1) * n], rel)
+    return out

@@ -1,0 +1,67 @@
+"""Pins for the oracle's reference GEMM and dequantization (CPU only)."""
+from fractions import Fraction
+
+import numpy as np
+import torch
+
+import oracle
+import workloads
+
+
+def _quant_pair(seed=0):
+    a_bits, w_bits = workloads.tiny()
+    a = workloads.bf16_bits_to_f32(a_bits)
+    w = workloads.bf16_bits_to_f32(w_bits)
+    qa = oracle.quantize_1x16(a)
+    qw = oracle.quantize_16x16(w)
+    return oracle.dequantize(*qa), oracle.dequantize(*qw)
+
+
+def test_dequantize_exhaustive_code_scale_pairs():
+    # x_hat = e2m1 * e4m3 * s_dec checked against float16 (E2M1 embedding) and torch's
+    # float8_e4m3fn decode, for every (code, scale) pair.
+    codes = np.arange(16, dtype=np.uint8)
+    e2m1 = (np.array([(int(c) & 7) << 9 for c in codes], np.uint16).view(np.float16)
+            .astype(np.float64) * 2.0 ** 14 * np.where(codes & 8, -1.0, 1.0))
+    e4m3 = (torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn)
+            .to(torch.float32).numpy().astype(np.float64))
+    s_dec = np.float32(0.37)
+    for s in range(0x7F):
+        packed = np.array([[c | (c << 4) for c in codes] * 1], np.uint8)    # 32 elements
+        scales = np.full((1, 2), s, np.uint8)
+        got = oracle.dequantize(packed, scales, [s_dec])
+        ref = np.repeat(e2m1, 2) * e4m3[s] * float(s_dec)
+        assert np.array_equal(got[0], ref)
+
+
+def test_fp64_gemm_matches_exact_rationals():
+    ah, bh = _quant_pair()
+    d = oracle.gemm_fp64(ah, bh)
+    rng = np.random.default_rng(0)
+    for _ in range(12):
+        m, n = rng.integers(0, 256, 2)
+        exact = sum(Fraction(float(ah[m, k])) * Fraction(float(bh[n, k])) for k in range(256))
+        assert abs(Fraction(float(d[m, n])) - exact) <= abs(exact) * Fraction(1, 2 ** 40) + Fraction(1, 2 ** 80)
+
+
+def test_one_hot_operand_selects_columns():
+    ah, _ = _quant_pair()
+    eye = np.eye(256)
+    assert np.array_equal(oracle.gemm_fp64(ah, eye[:8]), ah[:, :8])
+
+
+def test_bound_is_scaled_abs_product():
+    ah, bh = _quant_pair()
+    b = oracle.gemm_bound(ah, bh)
+    d = oracle.gemm_fp64(ah, bh)
+    assert np.all(b >= 0) and np.all(np.abs(d) <= b / 1e-5 * (1 + 1e-12))
+
+
+def test_grouped_equals_separate():
+    rng = np.random.default_rng(1)
+    a = rng.standard_normal((40, 32))
+    b = rng.standard_normal((3 * 8, 32))
+    off = np.array([0, 10, 10, 40])
+    d = oracle.grouped_gemm_fp64(a, b, off, 8)
+    assert np.array_equal(d[0:10], a[0:10] @ b[0:8].T)
+    assert np.array_equal(d[10:40], a[10:40] @ b[16:24].T)

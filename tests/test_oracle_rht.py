@@ -1,0 +1,120 @@
+"""Pins for the oracle's random Hadamard transform (CPU only).
+
+The pages say the transform multiplies the wgrad inputs by a random Hadamard matrix and is
+undone analytically. Pins: the butterfly's matrix equals the Kronecker power of H2 (numpy),
+H H^T = 16 I, exact rational arithmetic for the rounded output, exact undo, Parseval, and
+invariance of the wgrad GEMM when both operands are transformed."""
+from fractions import Fraction
+
+import numpy as np
+
+import oracle
+import workloads
+
+
+def _bf16(shape, seed, std=1.0):
+    return workloads.bf16_bits_to_f32(workloads.normal_bf16(shape, seed, std))
+
+
+def _fraction_to_f32(q: Fraction) -> np.float32:
+    """Correctly rounded (nearest-even) binary32 of an exact rational, by integer arithmetic."""
+    if q == 0:
+        return np.float32(0.0)
+    sign = -1 if q < 0 else 1
+    q = abs(q)
+    e = q.numerator.bit_length() - q.denominator.bit_length()
+    while Fraction(2) ** e > q:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= q:
+        e += 1
+    e = max(e, -126)
+    ulp = Fraction(2) ** (e - 23)
+    m = q / ulp
+    lo = m.numerator // m.denominator
+    rem = m - lo
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and lo % 2 == 1):
+        lo += 1
+    return np.float32(sign * float(lo * ulp))
+
+
+def test_butterfly_is_sylvester_kronecker_power():
+    h2 = np.array([[1.0, 1.0], [1.0, -1.0]])
+    h16 = np.kron(h2, np.kron(h2, np.kron(h2, h2)))
+    assert np.array_equal(oracle.hadamard_matrix_from_butterfly(), h16)
+
+
+def test_hadamard_orthogonality():
+    h = oracle.hadamard_matrix_from_butterfly()
+    assert np.array_equal(h @ h.T, 16 * np.eye(16))
+
+
+def test_rounded_output_equals_exact_rational():
+    x = _bf16((64, 8), 3)
+    x[5, 2] *= 50.0
+    for mask in (0, 0xFFFF, 0x6E04, 0x8001):
+        y = oracle.rht_columnwise(x, mask)
+        h = oracle.hadamard_matrix_from_butterfly().astype(int)
+        sig = [(-1 if (mask >> j) & 1 else 1) for j in range(16)]
+        for c in range(x.shape[1]):
+            for t in range(x.shape[0] // 16):
+                v = [Fraction(float(x[16 * t + j, c])) for j in range(16)]
+                for i in range(16):
+                    s = sum(Fraction(int(h[i, j]) * sig[j]) * v[j] for j in range(16)) / 4
+                    assert y[c, 16 * t + i] == _fraction_to_f32(s)
+
+
+def test_undo_restores_input_exactly():
+    x = _bf16((128, 16), 5)
+    mask = workloads.wgrad_sign_mask()
+    y64 = oracle.rht_columnwise_f64(x, mask)                 # [cols, tokens]
+    h = oracle.hadamard_matrix_from_butterfly()
+    sig = np.array([-1.0 if (mask >> j) & 1 else 1.0 for j in range(16)])
+    blocks = y64.reshape(16, -1, 16)                          # [col, tblock, 16]
+    back = 0.25 * np.einsum("j,ji,cti->ctj", sig, h, blocks)  # Q^T = 1/4 D H^T, H^T = H
+    assert np.array_equal(back.reshape(16, -1).T, x.astype(np.float64))
+    assert np.allclose((y64 ** 2).sum(axis=1), (x.astype(np.float64) ** 2).sum(axis=0), rtol=1e-14)
+
+
+def test_unit_vector_spreads_evenly():
+    x = np.zeros((16, 1), np.float32)
+    x[0, 0] = 1.0
+    for mask in (0, 1):
+        y = oracle.rht_columnwise(x, mask)
+        s0 = -1.0 if mask & 1 else 1.0
+        assert np.all(y == np.float32(0.25 * s0))
+
+
+def test_wgrad_gemm_invariant_under_shared_transform():
+    dy = _bf16((64, 24), 7, std=1e-3)
+    x = _bf16((64, 40), 8)
+    mask = 0x6E04
+    ref = dy.astype(np.float64).T @ x.astype(np.float64)
+    got = oracle.rht_columnwise_f64(dy, mask) @ oracle.rht_columnwise_f64(x, mask).T
+    assert np.allclose(got, ref, rtol=1e-12, atol=1e-15)
+
+
+def test_transform_spreads_a_spike_over_its_block():
+    # The pages' point of the rotation: an outlier no longer dominates its block. With one
+    # spike of 50 sigma among Gaussian entries, the block's max/RMS ratio drops from ~4 (a
+    # lone spike in 16 entries) to near 1 after the transform; energy is preserved.
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal((16 * 64, 1)).astype(np.float32)
+    x[np.arange(64) * 16 + rng.integers(0, 16, 64), 0] = 50.0
+    y = oracle.rht_columnwise_f64(x, workloads.wgrad_sign_mask()).reshape(64, 16)
+    v = x.astype(np.float64).reshape(64, 16)
+
+    def crest(b):
+        return np.abs(b).max(axis=1) / np.sqrt((b ** 2).mean(axis=1))
+
+    assert np.all(crest(y) < 0.5 * crest(v))
+    assert np.allclose((y ** 2).sum(axis=1), (v ** 2).sum(axis=1), rtol=1e-13)
+
+
+def test_rht_quantize_column_subset():
+    x = _bf16((64, 48), 9)
+    mask = 0x1234
+    full = oracle.rht_quantize(x, mask, "sr", seed=3, offset=2)
+    A = oracle.amax(oracle.rht_columnwise(x, mask))
+    cols = np.array([0, 7, 47])
+    sub = oracle.rht_quantize(x[:, cols], mask, "sr", seed=3, offset=2, amax_vals=A, col_ids=cols)
+    assert np.array_equal(sub[0], full[0][cols]) and np.array_equal(sub[1], full[1][cols])

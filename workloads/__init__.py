@@ -1,0 +1,139 @@
+"""Seeded synthetic inputs shared by the oracle tests, the GPU parity tests and the bench.
+
+This module only draws random numbers and rounds them to BF16 storage; it holds none of
+the NVFP4 arithmetic (no scales, no encoding, no transform), so both the CPU oracle and the
+HIP path can consume its outputs without sharing any of the method's code.
+
+Every tensor is produced on the CPU with ``numpy.random.default_rng(seed)`` in float32 and
+then rounded to BF16 with round-to-nearest-even, so it is identical on every machine.
+BF16 tensors are returned as ``uint16`` bit patterns (row-major).
+
+Workload shapes (the dense layer is the one a 12B-class hybrid model uses for its MLP
+up-projection; the MoE layer mirrors an expert layer with 128 experts, top-6 routing):
+  tiny    A[256,256], W[256,256] ~ N(0,1) with 0.1% of entries scaled x50
+  fprop   X[8192,5120] ~ N(0,1) + 0.1% x50 outliers ; W[20480,5120] ~ N(0, 0.02)
+  dgrad   dY[8192,20480] ~ N(0, 1e-3)
+  wgrad   dY and X as above, 16-bit random sign mask for the Hadamard transform
+  moe     16384 tokens pick 6 of 128 experts (Gumbel top-6 over Zipf(1.1) weights);
+          X[98304,2688] ~ N(0,1) in expert-sorted order; W[128*1856, 2688] ~ N(0,1)
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "f32_to_bf16_bits", "bf16_bits_to_f32", "normal_bf16", "with_outliers_bf16",
+    "tiny", "fprop", "dgrad", "wgrad_sign_mask", "moe_routing", "moe",
+    "SEEDS", "SR_SEED_DGRAD", "SR_SEED_WGRAD", "SR_OFFSET_WGRAD",
+]
+
+SEEDS = {
+    "tiny_a": 101, "tiny_w": 102,
+    "fprop_x": 201, "fprop_w": 202,
+    "dgrad_dy": 301,
+    "wgrad_sign": 401,
+    "moe_route": 501, "moe_x": 502, "moe_w": 503,
+}
+SR_SEED_DGRAD = 0x5EED0003
+SR_SEED_WGRAD = 0x5EED0004
+SR_OFFSET_WGRAD = 1 << 32
+
+MOE_EXPERTS = 128
+MOE_TOKENS = 16384
+MOE_TOPK = 6
+MOE_HIDDEN = 2688
+MOE_FFN = 1856
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 to BF16 (nearest, ties to even) and return the 16-bit patterns.
+
+    Inputs must be finite (the generators never produce NaN/Inf)."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    lsb = (u >> np.uint32(16)) & np.uint32(1)
+    r = (u + np.uint32(0x7FFF) + lsb) >> np.uint32(16)
+    return r.astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Exact widening of BF16 bit patterns to float32."""
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def _normal_f32(rng: np.random.Generator, shape, std: float) -> np.ndarray:
+    out = rng.standard_normal(size=shape, dtype=np.float32)
+    if std != 1.0:
+        out *= np.float32(std)
+    return out
+
+
+def normal_bf16(shape, seed: int, std: float = 1.0) -> np.ndarray:
+    """N(0, std^2) entries rounded to BF16 bits."""
+    rng = np.random.default_rng(seed)
+    return f32_to_bf16_bits(_normal_f32(rng, shape, std))
+
+
+def with_outliers_bf16(shape, seed: int, frac: float = 1e-3, factor: float = 50.0) -> np.ndarray:
+    """N(0,1) entries where exactly round(frac * numel) distinct entries are scaled by factor
+    before the BF16 rounding."""
+    rng = np.random.default_rng(seed)
+    x = _normal_f32(rng, shape, 1.0)
+    n = x.size
+    k = int(round(frac * n))
+    idx = rng.choice(n, size=k, replace=False)
+    flat = x.reshape(-1)
+    flat[idx] *= np.float32(factor)
+    return f32_to_bf16_bits(x)
+
+
+def tiny():
+    """A[256,256] (activations, 1x16 blocks) and W[256,256] (weights, 16x16 blocks)."""
+    a = with_outliers_bf16((256, 256), SEEDS["tiny_a"])
+    w = with_outliers_bf16((256, 256), SEEDS["tiny_w"])
+    return a, w
+
+
+def fprop(m: int = 8192, n: int = 20480, k: int = 5120):
+    """Activations X[m,k] with outliers and weights W[n,k] ~ N(0, 0.02)."""
+    x = with_outliers_bf16((m, k), SEEDS["fprop_x"])
+    w = normal_bf16((n, k), SEEDS["fprop_w"], std=0.02)
+    return x, w
+
+
+def dgrad(m: int = 8192, n: int = 20480):
+    """Output gradient dY[m,n] ~ N(0, 1e-3) (1e-3 read as the standard deviation)."""
+    return normal_bf16((m, n), SEEDS["dgrad_dy"], std=1e-3)
+
+
+def wgrad_sign_mask() -> int:
+    """The 16-bit sign mask of the random Hadamard transform used for the wgrad operands."""
+    return int(np.random.default_rng(SEEDS["wgrad_sign"]).integers(0, 65536))
+
+
+def moe_routing(tokens: int = MOE_TOKENS, experts: int = MOE_EXPERTS, topk: int = MOE_TOPK,
+                zipf_s: float = 1.1, seed: int = SEEDS["moe_route"]) -> np.ndarray:
+    """Rows per expert for top-k routing with Zipf-like expert popularity.
+
+    Each token draws Gumbel noise over log-weights p_e ~ rank^-s and keeps its top-k experts
+    (sampling k distinct experts without replacement, proportional to p). Returns the int64
+    row offsets [experts+1] of the expert-sorted activation matrix."""
+    rng = np.random.default_rng(seed)
+    ranks = np.arange(1, experts + 1, dtype=np.float64)
+    logp = -zipf_s * np.log(ranks)
+    logp -= np.log(np.exp(logp).sum())
+    g = rng.gumbel(size=(tokens, experts)) + logp[None, :]
+    top = np.argsort(-g, axis=1)[:, :topk]
+    counts = np.bincount(top.reshape(-1), minlength=experts).astype(np.int64)
+    offsets = np.zeros(experts + 1, dtype=np.int64)
+    np.cumsum(counts, out=offsets[1:])
+    return offsets
+
+
+def moe(rows_w_per_expert: int = MOE_FFN, hidden: int = MOE_HIDDEN):
+    """Expert-sorted activations X[sum M_g, hidden], stacked expert weights W[G*ffn, hidden]
+    and the row offsets of X per expert."""
+    offsets = moe_routing()
+    total = int(offsets[-1])
+    x = normal_bf16((total, hidden), SEEDS["moe_x"])
+    w = normal_bf16((MOE_EXPERTS * rows_w_per_expert, hidden), SEEDS["moe_w"])
+    return x, w, offsets
