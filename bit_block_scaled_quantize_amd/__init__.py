@@ -1,0 +1,229 @@
+"""Thin Python binding of libnvfp4 (include/nvfp4.h): NVFP4 quantization and block-scaled
+GEMMs on MI355X.
+
+Every function marshals torch tensors (device memory, current stream) into the C ABI and
+returns; all arithmetic runs in the HIP kernels. If the library is not built the import
+still succeeds but every call raises, so nothing can silently fall back to another path.
+
+Names follow the C entry points: quantize, rht_quantize, gemm, grouped_gemm, amax,
+dequantize.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libnvfp4.so")
+
+NVFP4_OK = 0
+_STATUS = {-1: "invalid argument", -2: "unsupported", -3: "workspace", -4: "HIP error"}
+_DTYPE = {torch.bfloat16: 0, torch.float32: 1}
+_BLOCK = {"1x16": 0, "16x16": 1}
+_ROUND = {"rn": 0, "sr": 1}
+OP_QUANTIZE, OP_RHT_QUANTIZE, OP_GEMM, OP_GROUPED_GEMM = 0, 1, 2, 3
+
+EXPORTED = ("nvfp4_quantize", "nvfp4_rht_quantize", "nvfp4_gemm", "nvfp4_grouped_gemm",
+            "nvfp4_amax", "nvfp4_workspace_size", "nvfp4_last_error", "nvfp4_dequantize")
+
+
+class NVFP4Error(RuntimeError):
+    pass
+
+
+class _CTensor(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("global_scale", ctypes.c_void_p), ("rows", ctypes.c_int64),
+                ("cols", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise NVFP4Error(f"{LIB_PATH} is not built; run bit_block_scaled_quantize_amd.build.build()")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i64, u64, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint64, ctypes.c_size_t
+    pt = ctypes.POINTER(_CTensor)
+    lib.nvfp4_quantize.argtypes = [vp, ctypes.c_int, i64, i64, i64, ctypes.c_int, ctypes.c_int,
+                                   u64, u64, vp, i64, vp, pt, pt, vp, sz, vp]
+    lib.nvfp4_rht_quantize.argtypes = [vp, ctypes.c_int, i64, i64, i64, ctypes.c_uint16,
+                                       ctypes.c_int, u64, u64, vp, pt, vp, sz, vp]
+    lib.nvfp4_gemm.argtypes = [pt, pt, vp, i64, vp]
+    lib.nvfp4_grouped_gemm.argtypes = [i64, vp, pt, pt, i64, vp, i64, vp, sz, vp]
+    lib.nvfp4_amax.argtypes = [vp, ctypes.c_int, i64, i64, i64, vp, i64, ctypes.c_int,
+                               ctypes.c_uint16, vp, vp]
+    lib.nvfp4_workspace_size.argtypes = [ctypes.c_int, i64, i64, i64]
+    lib.nvfp4_workspace_size.restype = sz
+    lib.nvfp4_last_error.restype = ctypes.c_char_p
+    lib.nvfp4_dequantize.argtypes = [pt, vp, i64, vp, vp]
+    for name in EXPORTED:
+        if name not in ("nvfp4_workspace_size", "nvfp4_last_error"):
+            getattr(lib, name).restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def library():
+    """The loaded ctypes library (raises NVFP4Error if it is not built)."""
+    return _load()
+
+
+def _check(status: int):
+    if status != NVFP4_OK:
+        msg = _load().nvfp4_last_error().decode()
+        raise NVFP4Error(f"{_STATUS.get(status, status)}: {msg}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+@dataclass
+class NVFP4Tensor:
+    """Device buffers of one NVFP4 tensor [rows, cols] quantized along cols."""
+    codes: torch.Tensor         # uint8 [rows, cols/2]
+    scales: torch.Tensor        # uint8 [rows, cols/16] (E4M3 codes)
+    global_scale: torch.Tensor  # float32 [nseg]
+    rows: int
+    cols: int
+
+    @classmethod
+    def empty(cls, rows: int, cols: int, nseg: int = 1, device="cuda"):
+        return cls(torch.empty((rows, cols // 2), dtype=torch.uint8, device=device),
+                   torch.empty((rows, cols // 16), dtype=torch.uint8, device=device),
+                   torch.empty((nseg,), dtype=torch.float32, device=device), rows, cols)
+
+    def c(self) -> _CTensor:
+        return _CTensor(self.codes.data_ptr(), self.scales.data_ptr(),
+                        self.global_scale.data_ptr(), self.rows, self.cols)
+
+
+def _input(x: torch.Tensor):
+    if x.dtype not in _DTYPE:
+        raise NVFP4Error(f"unsupported input dtype {x.dtype}")
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise NVFP4Error("input must be a 2-D tensor with unit column stride")
+    return _DTYPE[x.dtype], x.shape[0], x.shape[1], x.stride(0)
+
+
+def workspace_size(op: int, rows: int, cols: int, nseg: int = 1) -> int:
+    return int(_load().nvfp4_workspace_size(op, rows, cols, nseg))
+
+
+def _workspace(op, rows, cols, nseg, device):
+    n = workspace_size(op, rows, cols, nseg)
+    return torch.empty((max(n, 1),), dtype=torch.uint8, device=device), n
+
+
+def quantize(x: torch.Tensor, block: str = "1x16", rounding: str = "rn", seed: int = 0,
+             offset: int = 0, segments: torch.Tensor | None = None, amax: torch.Tensor | None = None,
+             emit_transposed: bool = False, out: NVFP4Tensor | None = None,
+             out_t: NVFP4Tensor | None = None, workspace: torch.Tensor | None = None, stream=None):
+    """nvfp4_quantize. Returns (q, q_t) where q_t is None unless emit_transposed."""
+    lib = _load()
+    dt, rows, cols, ld = _input(x)
+    nseg = 1 if segments is None else segments.numel() - 1
+    if out is None:
+        out = NVFP4Tensor.empty(rows, cols, nseg, x.device)
+    if emit_transposed and out_t is None:
+        out_t = NVFP4Tensor.empty(cols, rows, nseg, x.device)
+    ws_n = 0
+    if amax is None:
+        if workspace is None:
+            workspace, ws_n = _workspace(OP_QUANTIZE, rows, cols, nseg, x.device)
+        else:
+            ws_n = workspace.numel()
+    oc = out.c()
+    otc = out_t.c() if emit_transposed else None
+    st = lib.nvfp4_quantize(_ptr(x), dt, rows, cols, ld, _BLOCK[block], _ROUND[rounding],
+                            seed & (2 ** 64 - 1), offset & (2 ** 64 - 1), _ptr(segments), nseg,
+                            _ptr(amax), ctypes.byref(oc),
+                            ctypes.byref(otc) if otc is not None else None,
+                            _ptr(workspace) if amax is None else None, ws_n, _stream(stream))
+    _check(st)
+    return out, (out_t if emit_transposed else None)
+
+
+def rht_quantize(x: torch.Tensor, sign_mask: int, rounding: str = "rn", seed: int = 0,
+                 offset: int = 0, amax: torch.Tensor | None = None,
+                 out: NVFP4Tensor | None = None, workspace: torch.Tensor | None = None,
+                 stream=None) -> NVFP4Tensor:
+    """nvfp4_rht_quantize: x[tokens, cols] -> NVFP4 tensor [cols, tokens]."""
+    lib = _load()
+    dt, tokens, cols, ld = _input(x)
+    if out is None:
+        out = NVFP4Tensor.empty(cols, tokens, 1, x.device)
+    ws_n = 0
+    if amax is None:
+        if workspace is None:
+            workspace, ws_n = _workspace(OP_RHT_QUANTIZE, tokens, cols, 1, x.device)
+        else:
+            ws_n = workspace.numel()
+    oc = out.c()
+    st = lib.nvfp4_rht_quantize(_ptr(x), dt, tokens, cols, ld, sign_mask & 0xFFFF,
+                                _ROUND[rounding], seed & (2 ** 64 - 1), offset & (2 ** 64 - 1),
+                                _ptr(amax), ctypes.byref(oc),
+                                _ptr(workspace) if amax is None else None, ws_n, _stream(stream))
+    _check(st)
+    return out
+
+
+def gemm(a: NVFP4Tensor, b: NVFP4Tensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """nvfp4_gemm: D[M, N] = A[M, K] * B[N, K]^T (FP32)."""
+    lib = _load()
+    if out is None:
+        out = torch.empty((a.rows, b.rows), dtype=torch.float32, device=a.codes.device)
+    ac, bc = a.c(), b.c()
+    _check(lib.nvfp4_gemm(ctypes.byref(ac), ctypes.byref(bc), _ptr(out), out.stride(0),
+                          _stream(stream)))
+    return out
+
+
+def grouped_gemm(m_offsets: torch.Tensor, a: NVFP4Tensor, b: NVFP4Tensor, n: int,
+                 out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """nvfp4_grouped_gemm: per group g, rows m_offsets[g]:m_offsets[g+1] of A against rows
+    g*n:(g+1)*n of B."""
+    lib = _load()
+    G = m_offsets.numel() - 1
+    if out is None:
+        out = torch.empty((a.rows, n), dtype=torch.float32, device=a.codes.device)
+    ac, bc = a.c(), b.c()
+    _check(lib.nvfp4_grouped_gemm(G, _ptr(m_offsets), ctypes.byref(ac), ctypes.byref(bc), n,
+                                  _ptr(out), out.stride(0), None, 0, _stream(stream)))
+    return out
+
+
+def amax(x: torch.Tensor, segments: torch.Tensor | None = None, rht: bool = False,
+         sign_mask: int = 0, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """nvfp4_amax: max|x| per segment (or of the Hadamard-transformed tensor)."""
+    lib = _load()
+    dt, rows, cols, ld = _input(x)
+    nseg = 1 if segments is None else segments.numel() - 1
+    if out is None:
+        out = torch.empty((nseg,), dtype=torch.float32, device=x.device)
+    _check(lib.nvfp4_amax(_ptr(x), dt, rows, cols, ld, _ptr(segments), nseg, int(rht),
+                          sign_mask & 0xFFFF, _ptr(out), _stream(stream)))
+    return out
+
+
+def dequantize(q: NVFP4Tensor, segments: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """nvfp4_dequantize (test helper): FP32 [rows, cols]."""
+    lib = _load()
+    nseg = 1 if segments is None else segments.numel() - 1
+    y = torch.empty((q.rows, q.cols), dtype=torch.float32, device=q.codes.device)
+    qc = q.c()
+    _check(lib.nvfp4_dequantize(ctypes.byref(qc), _ptr(segments), nseg, _ptr(y), _stream(stream)))
+    return y

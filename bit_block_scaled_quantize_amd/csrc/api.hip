@@ -1,0 +1,211 @@
+// C ABI of libnvfp4 (declared in include/nvfp4.h): host-side validation, workspace
+// sizing and dispatch to the gfx950 kernels. Nothing here allocates device memory.
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/nvfp4.h"
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return NVFP4_OK;
+  return fail(NVFP4_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+constexpr size_t kWsAlign = 256;
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Checks an output tensor descriptor for a [rows, cols] quantization.
+int check_out(const nvfp4_tensor* t, int64_t rows, int64_t cols, const char* name) {
+  if (!t) return fail(NVFP4_ERR_INVALID, "%s is NULL", name);
+  if (!t->codes || !t->scales || !t->global_scale)
+    return fail(NVFP4_ERR_INVALID, "%s has a NULL codes/scales/global_scale pointer", name);
+  if (t->rows != rows || t->cols != cols)
+    return fail(NVFP4_ERR_INVALID, "%s shape [%lld, %lld] does not match [%lld, %lld]", name,
+                (long long)t->rows, (long long)t->cols, (long long)rows, (long long)cols);
+  if (!aligned(t->codes, 16))
+    return fail(NVFP4_ERR_INVALID, "%s codes must be 16-byte aligned", name);
+  return NVFP4_OK;
+}
+
+int check_input(const void* x, nvfp4_dtype dt, int64_t rows, int64_t cols, int64_t ld) {
+  if (!x) return fail(NVFP4_ERR_INVALID, "x is NULL");
+  if (dt != NVFP4_IN_BF16 && dt != NVFP4_IN_FP32) return fail(NVFP4_ERR_INVALID, "bad dtype %d", (int)dt);
+  if (rows < 0 || cols < 1) return fail(NVFP4_ERR_INVALID, "bad shape [%lld, %lld]", (long long)rows, (long long)cols);
+  if (ld < cols) return fail(NVFP4_ERR_INVALID, "ld (%lld) < cols (%lld)", (long long)ld, (long long)cols);
+  const int64_t vec = dt == NVFP4_IN_BF16 ? 8 : 4;      // elements per 16 bytes
+  if (!aligned(x, 16) || ld % vec != 0)
+    return fail(NVFP4_ERR_UNSUPPORTED, "x must be 16-byte aligned with ld a multiple of %lld", (long long)vec);
+  return NVFP4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* nvfp4_last_error(void) { return g_last_error.c_str(); }
+
+size_t nvfp4_workspace_size(int op, int64_t rows, int64_t cols, int64_t nseg) {
+  (void)rows;
+  (void)cols;
+  switch (op) {
+    case NVFP4_OP_QUANTIZE: return round_up((size_t)(nseg < 1 ? 1 : nseg) * sizeof(float), kWsAlign);
+    case NVFP4_OP_RHT_QUANTIZE: return kWsAlign;
+    default: return 0;
+  }
+}
+
+int nvfp4_amax(const void* x, nvfp4_dtype dt, int64_t rows, int64_t cols, int64_t ld,
+               const int64_t* segments, int64_t nseg, int rht, uint16_t sign_mask,
+               float* amax_out, void* hip_stream) {
+  int st = check_input(x, dt, rows, cols, ld);
+  if (st) return st;
+  if (!amax_out) return fail(NVFP4_ERR_INVALID, "amax_out is NULL");
+  if (nseg < 1 || (!segments && nseg != 1)) return fail(NVFP4_ERR_INVALID, "bad segment table (nseg=%lld)", (long long)nseg);
+  hipStream_t s = (hipStream_t)hip_stream;
+  if (rht) {
+    if (segments) return fail(NVFP4_ERR_UNSUPPORTED, "segments with the Hadamard transform");
+    if (rows % 16) return fail(NVFP4_ERR_INVALID, "tokens (%lld) must be a multiple of 16", (long long)rows);
+    return hip_status(nvfp4::launch_rht_amax(x, dt == NVFP4_IN_FP32, rows, cols, ld, sign_mask, amax_out, s), "rht amax");
+  }
+  if (cols % 16) return fail(NVFP4_ERR_INVALID, "cols (%lld) must be a multiple of 16", (long long)cols);
+  return hip_status(nvfp4::launch_amax(x, dt == NVFP4_IN_FP32, rows, cols, ld, segments, nseg, amax_out, s), "amax");
+}
+
+int nvfp4_quantize(const void* x, nvfp4_dtype dt, int64_t rows, int64_t cols, int64_t ld,
+                   nvfp4_block blk, nvfp4_round rnd, uint64_t seed, uint64_t offset,
+                   const int64_t* segments, int64_t nseg, const float* amax_in,
+                   nvfp4_tensor* out, nvfp4_tensor* out_t, void* workspace, size_t ws_bytes,
+                   void* hip_stream) {
+  int st = check_input(x, dt, rows, cols, ld);
+  if (st) return st;
+  if (blk != NVFP4_BLOCK_1X16 && blk != NVFP4_BLOCK_16X16) return fail(NVFP4_ERR_INVALID, "bad block mode %d", (int)blk);
+  if (rnd != NVFP4_ROUND_RN && rnd != NVFP4_ROUND_SR) return fail(NVFP4_ERR_INVALID, "bad rounding mode %d", (int)rnd);
+  if (cols % 16) return fail(NVFP4_ERR_INVALID, "cols (%lld) must be a multiple of 16", (long long)cols);
+  if (blk == NVFP4_BLOCK_16X16 && rows % 16) return fail(NVFP4_ERR_INVALID, "rows (%lld) must be a multiple of 16 for 16x16 blocks", (long long)rows);
+  if (nseg < 1 || (!segments && nseg != 1)) return fail(NVFP4_ERR_INVALID, "bad segment table (nseg=%lld)", (long long)nseg);
+  if (out_t && blk != NVFP4_BLOCK_16X16) return fail(NVFP4_ERR_INVALID, "out_t requires 16x16 blocks");
+  if (blk == NVFP4_BLOCK_16X16 && rnd == NVFP4_ROUND_SR) return fail(NVFP4_ERR_UNSUPPORTED, "stochastic rounding applies to 1x16 gradient blocks only");
+  if (out_t && segments) return fail(NVFP4_ERR_UNSUPPORTED, "transposed emission of a segmented tensor");
+  if ((st = check_out(out, rows, cols, "out"))) return st;
+  if (out_t && (st = check_out(out_t, cols, rows, "out_t"))) return st;
+  const float* amax = amax_in;
+  if (!amax) {
+    const size_t need = nvfp4_workspace_size(NVFP4_OP_QUANTIZE, rows, cols, nseg);
+    if (!workspace || ws_bytes < need || !aligned(workspace, kWsAlign))
+      return fail(NVFP4_ERR_WORKSPACE, "workspace of %zu bytes (256-byte aligned) required, got %zu", need, ws_bytes);
+  }
+  hipStream_t s = (hipStream_t)hip_stream;
+  const bool f32 = dt == NVFP4_IN_FP32;
+  if (!amax) {
+    float* ws = static_cast<float*>(workspace);
+    if ((st = hip_status(nvfp4::launch_amax(x, f32, rows, cols, ld, segments, nseg, ws, s), "amax"))) return st;
+    amax = ws;
+  }
+  const nvfp4::QuantOut q{out->codes, out->scales, out->global_scale};
+  if (blk == NVFP4_BLOCK_1X16)
+    return hip_status(nvfp4::launch_encode_1x16(x, f32, rows, cols, ld, rnd == NVFP4_ROUND_SR, seed,
+                                                offset, segments, nseg, amax, q, s), "encode 1x16");
+  nvfp4::QuantOut qt{};
+  if (out_t) qt = nvfp4::QuantOut{out_t->codes, out_t->scales, out_t->global_scale};
+  return hip_status(nvfp4::launch_encode_16x16(x, f32, rows, cols, ld, segments, nseg, amax, q,
+                                               out_t ? &qt : nullptr, s), "encode 16x16");
+}
+
+int nvfp4_rht_quantize(const void* x, nvfp4_dtype dt, int64_t tokens, int64_t cols, int64_t ld,
+                       uint16_t sign_mask, nvfp4_round rnd, uint64_t seed, uint64_t offset,
+                       const float* amax_in, nvfp4_tensor* out, void* workspace, size_t ws_bytes,
+                       void* hip_stream) {
+  int st = check_input(x, dt, tokens, cols, ld);
+  if (st) return st;
+  if (rnd != NVFP4_ROUND_RN && rnd != NVFP4_ROUND_SR) return fail(NVFP4_ERR_INVALID, "bad rounding mode %d", (int)rnd);
+  if (tokens % 16) return fail(NVFP4_ERR_INVALID, "tokens (%lld) must be a multiple of 16", (long long)tokens);
+  if ((st = check_out(out, cols, tokens, "out"))) return st;
+  const float* amax = amax_in;
+  if (!amax) {
+    const size_t need = nvfp4_workspace_size(NVFP4_OP_RHT_QUANTIZE, tokens, cols, 1);
+    if (!workspace || ws_bytes < need || !aligned(workspace, kWsAlign))
+      return fail(NVFP4_ERR_WORKSPACE, "workspace of %zu bytes (256-byte aligned) required, got %zu", need, ws_bytes);
+  }
+  hipStream_t s = (hipStream_t)hip_stream;
+  const bool f32 = dt == NVFP4_IN_FP32;
+  if (!amax) {
+    float* ws = static_cast<float*>(workspace);
+    if ((st = hip_status(nvfp4::launch_rht_amax(x, f32, tokens, cols, ld, sign_mask, ws, s), "rht amax"))) return st;
+    amax = ws;
+  }
+  if (tokens == 0) return NVFP4_OK;
+  const nvfp4::QuantOut q{out->codes, out->scales, out->global_scale};
+  return hip_status(nvfp4::launch_rht_encode(x, f32, tokens, cols, ld, sign_mask, rnd == NVFP4_ROUND_SR,
+                                             seed, offset, amax, q, s), "rht encode");
+}
+
+static int check_operand(const nvfp4_tensor* t, const char* name) {
+  if (!t) return fail(NVFP4_ERR_INVALID, "%s is NULL", name);
+  if (!t->codes || !t->scales || !t->global_scale)
+    return fail(NVFP4_ERR_INVALID, "%s has a NULL codes/scales/global_scale pointer", name);
+  if (t->rows < 0 || t->cols < 0 || t->cols % 16)
+    return fail(NVFP4_ERR_INVALID, "%s shape [%lld, %lld]: cols must be a non-negative multiple of 16", name,
+                (long long)t->rows, (long long)t->cols);
+  if (!aligned(t->codes, 16)) return fail(NVFP4_ERR_INVALID, "%s codes must be 16-byte aligned", name);
+  return NVFP4_OK;
+}
+
+int nvfp4_gemm(const nvfp4_tensor* A, const nvfp4_tensor* B, float* D, int64_t ldd, void* hip_stream) {
+  int st;
+  if ((st = check_operand(A, "A")) || (st = check_operand(B, "B"))) return st;
+  if (A->cols != B->cols) return fail(NVFP4_ERR_INVALID, "K mismatch: A has %lld, B has %lld", (long long)A->cols, (long long)B->cols);
+  if (!D) return fail(NVFP4_ERR_INVALID, "D is NULL");
+  if (ldd < B->rows) return fail(NVFP4_ERR_INVALID, "ldd (%lld) < N (%lld)", (long long)ldd, (long long)B->rows);
+  const nvfp4::GemmOperand a{A->codes, A->scales, A->global_scale};
+  const nvfp4::GemmOperand b{B->codes, B->scales, B->global_scale};
+  return hip_status(nvfp4::launch_gemm(a, b, A->rows, B->rows, A->cols, D, ldd, (hipStream_t)hip_stream), "gemm");
+}
+
+int nvfp4_grouped_gemm(int64_t G, const int64_t* m_offsets, const nvfp4_tensor* A,
+                       const nvfp4_tensor* B, int64_t N, float* D, int64_t ldd, void* workspace,
+                       size_t ws_bytes, void* hip_stream) {
+  (void)workspace;
+  (void)ws_bytes;
+  int st;
+  if (G < 1) return fail(NVFP4_ERR_INVALID, "G (%lld) must be >= 1", (long long)G);
+  if (!m_offsets) return fail(NVFP4_ERR_INVALID, "m_offsets is NULL");
+  if ((st = check_operand(A, "A")) || (st = check_operand(B, "B"))) return st;
+  if (A->cols != B->cols) return fail(NVFP4_ERR_INVALID, "K mismatch: A has %lld, B has %lld", (long long)A->cols, (long long)B->cols);
+  if (N < 1 || B->rows != G * N) return fail(NVFP4_ERR_INVALID, "B rows (%lld) must equal G*N (%lld)", (long long)B->rows, (long long)(G * N));
+  if (!D) return fail(NVFP4_ERR_INVALID, "D is NULL");
+  if (ldd < N) return fail(NVFP4_ERR_INVALID, "ldd (%lld) < N (%lld)", (long long)ldd, (long long)N);
+  const nvfp4::GemmOperand a{A->codes, A->scales, A->global_scale};
+  const nvfp4::GemmOperand b{B->codes, B->scales, B->global_scale};
+  return hip_status(nvfp4::launch_grouped_gemm(G, m_offsets, a, b, A->rows, N, A->cols, D, ldd,
+                                               (hipStream_t)hip_stream), "grouped gemm");
+}
+
+int nvfp4_dequantize(const nvfp4_tensor* q, const int64_t* segments, int64_t nseg, float* y,
+                     void* hip_stream) {
+  int st;
+  if ((st = check_operand(q, "q"))) return st;
+  if (!y) return fail(NVFP4_ERR_INVALID, "y is NULL");
+  if (nseg < 1 || (!segments && nseg != 1)) return fail(NVFP4_ERR_INVALID, "bad segment table (nseg=%lld)", (long long)nseg);
+  return hip_status(nvfp4::launch_dequantize(q->codes, q->scales, q->global_scale, segments, nseg,
+                                             q->rows, q->cols, y, (hipStream_t)hip_stream), "dequantize");
+}
+
+}  // extern "C"

@@ -1,0 +1,172 @@
+// Device-side building blocks shared by the quantize, Hadamard and GEMM kernels (gfx950).
+//
+// Element format ("Nemotron NVFP4" explainer, "What NVFP4 actually is"): E2M1 elements, one
+// E4M3 scale per 16 elements, one FP32 tensor scale. The bit-level conventions (E2M1 bias 1,
+// OCP E4M3 "FN", nearest-even rounding, the 8-bit stochastic-rounding rule, the
+// Philox4x32-10 counter layout) are the ones documented in include/nvfp4.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#pragma clang fp contract(off)
+
+namespace nvfp4 {
+
+constexpr float kE2M1Max = 6.0f;
+constexpr float kScaleNumerator = 2688.0f;   // largest element (6) x largest E4M3 (448)
+constexpr float kFltMax = 3.40282346638528859812e+38f;
+
+// ---- vector loads -------------------------------------------------------------------------
+typedef uint32_t v4u32 __attribute__((ext_vector_type(4)));
+typedef uint32_t v2u32 __attribute__((ext_vector_type(2)));
+typedef float v4f32 __attribute__((ext_vector_type(4)));
+typedef float v2f32 __attribute__((ext_vector_type(2)));
+
+template <typename T>
+__device__ __forceinline__ v4u32 ld_u32x4(const T* p) { return *reinterpret_cast<const v4u32*>(p); }
+template <typename T>
+__device__ __forceinline__ v4f32 ld_f32x4(const T* p) { return *reinterpret_cast<const v4f32*>(p); }
+
+// ---- BF16 / FP32 inputs --------------------------------------------------------------
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// ---- tensor scales ---------------------------------------------------------------------
+// Encode multiplier s_enc = rn32(2688 / amax) (FLT_MAX if that overflows), 1 for amax == 0.
+__device__ __forceinline__ float tensor_encode_scale(float amax) {
+  if (amax == 0.0f) return 1.0f;
+  return fminf(kScaleNumerator / amax, kFltMax);
+}
+// Stored decode scale s_dec = rn32(amax / 2688), 1 for amax == 0.
+__device__ __forceinline__ float tensor_decode_scale(float amax) {
+  if (amax == 0.0f) return 1.0f;
+  return amax / kScaleNumerator;
+}
+
+// ---- E4M3 block scale ------------------------------------------------------------------
+// Nearest-even E4M3 code of a non-negative value, saturating at 448 (code 0x7E).
+__device__ __forceinline__ uint32_t e4m3_encode(float t) {
+  if (!(t < 448.0f)) return 0x7Eu;
+  if (t < 0.015625f) {                           // below 2^-6: subnormal steps of 2^-9
+    return (uint32_t)__builtin_rintf(t * 512.0f);  // exact scaling, ties to even; 8 -> 0x08
+  }
+  const uint32_t b = __float_as_uint(t);
+  // keep 3 mantissa bits with round-half-even, then rebias the exponent 127 -> 7
+  const uint32_t r = b + 0x7FFFFu + ((b >> 20) & 1u);
+  return (r >> 20) - (120u << 3);
+}
+
+// Exact value of a non-negative E4M3 code (0x00..0x7E).
+__device__ __forceinline__ float e4m3_decode(uint32_t s) {
+  const uint32_t e = s >> 3, m = s & 7u;
+  const float sub = (float)m * 0.001953125f;     // m * 2^-9
+  const float nrm = __uint_as_float(((e + 120u) << 23) | (m << 20));
+  return e == 0 ? sub : nrm;
+}
+
+// ---- E2M1 elements ---------------------------------------------------------------------
+// Round-to-nearest-even to the E2M1 grid {0,.5,1,1.5,2,3,4,6}, saturating; sign from y.
+__device__ __forceinline__ uint32_t e2m1_rn(float y) {
+  const float a = fminf(fabsf(y), kE2M1Max);
+  const uint32_t b = __float_as_uint(a);
+  // normal range [1, 6]: round the fp32 mantissa to 1 bit, then rebias (127-1) -> 2 steps
+  const uint32_t nrm = (b + 0x1FFFFFu + ((b >> 22) & 1u) - 0x3F000000u) >> 22;
+  // subnormal range [0, 1): steps of 0.5
+  const uint32_t sub = (uint32_t)__builtin_rintf(a * 2.0f);
+  const uint32_t mag = a < 1.0f ? sub : nrm;
+  return mag | ((__float_as_uint(y) >> 28) & 8u);
+}
+
+// Stochastic rounding with random byte r: round up iff frac + r/256 >= 1, where frac is the
+// position of |y| between its two neighbouring grid values. X below is |y| in fixed point
+// with the kept grid step at bit 22, so the decision is the carry out of the low 22 bits.
+__device__ __forceinline__ uint32_t e2m1_sr(float y, uint32_t r) {
+  const float a = fminf(fabsf(y), kE2M1Max);
+  const uint32_t X = a >= 1.0f ? __float_as_uint(a) - 0x3F000000u
+                               : (uint32_t)(a * 8388608.0f);   // floor(a * 2^23)
+  const uint32_t mag = (X + (r << 14)) >> 22;
+  return mag | ((__float_as_uint(y) >> 28) & 8u);
+}
+
+// ---- Philox4x32-10 (Salmon et al., SC'11) ----------------------------------------------
+struct u32x4 { uint32_t x, y, z, w; };
+
+__device__ __forceinline__ u32x4 philox4x32_10(u32x4 c, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int i = 0; i < 10; ++i) {
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c.x;
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c.z;
+    c = u32x4{(uint32_t)(p1 >> 32) ^ c.y ^ k0, (uint32_t)p1,
+              (uint32_t)(p0 >> 32) ^ c.w ^ k1, (uint32_t)p0};
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return c;
+}
+
+// The 16 random bytes of quantization block `b`.
+__device__ __forceinline__ u32x4 block_random(uint64_t b, uint64_t seed, uint64_t offset) {
+  return philox4x32_10(u32x4{(uint32_t)b, (uint32_t)(b >> 32), (uint32_t)offset,
+                             (uint32_t)(offset >> 32)},
+                       (uint32_t)seed, (uint32_t)(seed >> 32));
+}
+
+// ---- one 16-element block ----------------------------------------------------------------
+// Block scale code and element multiplier from the block amax and the tensor encode scale:
+// t = rn32(rn32(a_b / 6) * s_enc), S = E4M3(t), r = min(rn32(s_enc / dec(S)), FLT_MAX),
+// r = 0 when S decodes to zero (every element then encodes as a signed zero).
+struct BlockScale { uint32_t code; float mult; };
+
+__device__ __forceinline__ BlockScale block_scale(float block_amax, float s_enc) {
+  const float t = (block_amax / 6.0f) * s_enc;
+  const uint32_t s = e4m3_encode(t);
+  const float d = e4m3_decode(s);
+  const float r = d > 0.0f ? fminf(s_enc / d, kFltMax) : 0.0f;
+  return BlockScale{s, r};
+}
+
+// Encode 16 values v[0..15] (already in float) into two code words (element j -> nibble j).
+template <bool SR>
+__device__ __forceinline__ void encode16(const float (&v)[16], float mult, u32x4 rnd,
+                                         uint32_t& lo, uint32_t& hi) {
+  uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const float y = v[j] * mult;
+    uint32_t c;
+    if constexpr (SR) {
+      const uint32_t word = j < 4 ? rnd.x : j < 8 ? rnd.y : j < 12 ? rnd.z : rnd.w;
+      c = e2m1_sr(y, (word >> (8 * (j & 3))) & 0xFFu);
+    } else {
+      c = e2m1_rn(y);
+    }
+    if (j < 8) w0 |= c << (4 * j); else w1 |= c << (4 * (j - 8));
+  }
+  lo = w0;
+  hi = w1;
+}
+
+// ---- reductions ----------------------------------------------------------------------------
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// atomic max of a non-negative float through its bit pattern (monotone for v >= 0)
+__device__ __forceinline__ void atomic_max_nonneg(float* p, float v) {
+  atomicMax(reinterpret_cast<unsigned int*>(p), __float_as_uint(v));
+}
+
+// Segment containing `row` for a non-decreasing offset table off[0..nseg] (clamped).
+__device__ __forceinline__ int64_t find_segment(const int64_t* off, int64_t nseg, int64_t row) {
+  int64_t lo = 0, hi = nseg - 1;
+  while (lo < hi) {
+    const int64_t mid = (lo + hi + 1) >> 1;
+    if (off[mid] <= row) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+}  // namespace nvfp4

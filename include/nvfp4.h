@@ -1,0 +1,189 @@
+/*
+ * nvfp4.h - C ABI of libnvfp4: NVFP4 block quantization and block-scaled GEMMs on MI355X.
+ *
+ * The format (from "Nemotron NVFP4" explainer, ai.thesatyajit.com, section "What NVFP4
+ * actually is"): every element is a 4-bit E2M1 float (1 sign, 2 exponent, 1 mantissa bit),
+ * every 16 consecutive elements share one FP8 E4M3 scale, and the whole tensor shares one
+ * FP32 scale, 4.5 bits per element in total. Activations and gradients use 1x16 blocks,
+ * weights use 16x16 blocks (artiverse.ca "NVIDIA's 4-bit floating point pushes AI training
+ * limits", stabilizer paragraph); gradients are rounded stochastically, everything else to
+ * nearest (same page; explainer section "Why 4-bit training normally falls apart - and the
+ * three fixes"); the weight-gradient GEMM's operands go through a 16-point random-sign
+ * Hadamard transform first (same explainer section).
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers on the current HIP device. The caller
+ *     allocates every buffer and owns it; the library allocates nothing and keeps no state
+ *     between calls, so calls are re-entrant on different streams.
+ *   - All work is enqueued asynchronously on `hip_stream` (a hipStream_t; NULL = the null
+ *     stream). The library never synchronizes; a device fault surfaces at the caller's next
+ *     synchronization.
+ *   - Arguments are validated on the host before anything is enqueued. On any non-OK status
+ *     nothing was enqueued (except NVFP4_ERR_HIP, where a launch itself failed) and
+ *     nvfp4_last_error() describes the problem (thread-local string).
+ *   - Device-resident arguments (segment/offset tables, amax values) cannot be checked on the
+ *     host; their preconditions are stated per function. Violating them gives unspecified
+ *     output but never an out-of-bounds access: kernels clamp table lookups.
+ *   - Non-finite inputs (Inf/NaN) are outside the contract: outputs are unspecified, the
+ *     kernels still terminate normally.
+ *
+ * NVFP4 tensor layout (nvfp4_tensor), for a logical matrix [rows, cols] quantized along cols:
+ *   codes        uint8 [rows, cols/2] row-major; element 2i in the low nibble, 2i+1 in the
+ *                high nibble; nibble = sign<<3 | exponent<<1 | mantissa (E2M1, bias 1).
+ *   scales       uint8 [rows, cols/16] row-major E4M3 (OCP "FN": bias 7, max 448) codes.
+ *                A 16x16 weight tile stores its one scale in each of its 16 rows.
+ *   global_scale float [nseg] decode scale s_dec = amax/2688 per segment (1.0 if amax = 0).
+ *   Dequantized value: e2m1(code) * e4m3(scale) * global_scale[segment of row].
+ */
+#ifndef NVFP4_H
+#define NVFP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  NVFP4_OK = 0,
+  NVFP4_ERR_INVALID = -1,      /* bad pointer, shape, enum or size                     */
+  NVFP4_ERR_UNSUPPORTED = -2,  /* valid request this library does not implement        */
+  NVFP4_ERR_WORKSPACE = -3,    /* workspace missing or smaller than nvfp4_workspace_size */
+  NVFP4_ERR_HIP = -4           /* a HIP launch failed (message holds hipGetErrorString) */
+} nvfp4_status;
+
+typedef enum { NVFP4_IN_BF16 = 0, NVFP4_IN_FP32 = 1 } nvfp4_dtype;
+typedef enum { NVFP4_BLOCK_1X16 = 0, NVFP4_BLOCK_16X16 = 1 } nvfp4_block;
+typedef enum { NVFP4_ROUND_RN = 0, NVFP4_ROUND_SR = 1 } nvfp4_round;
+typedef enum {
+  NVFP4_OP_QUANTIZE = 0, NVFP4_OP_RHT_QUANTIZE = 1, NVFP4_OP_GEMM = 2,
+  NVFP4_OP_GROUPED_GEMM = 3
+} nvfp4_op;
+
+typedef struct nvfp4_tensor {
+  uint8_t* codes;        /* device, [rows, cols/2]                       */
+  uint8_t* scales;       /* device, [rows, cols/16]                      */
+  float* global_scale;   /* device, [nseg] (1 for an unsegmented tensor) */
+  int64_t rows;
+  int64_t cols;          /* the quantized (contraction) dimension, % 16 == 0 */
+} nvfp4_tensor;
+
+/*
+ * nvfp4_quantize - two-level block quantization of x[rows, cols] along cols.
+ * Defined by: "Nemotron NVFP4" explainer, "What NVFP4 actually is" (E2M1 elements, one E4M3
+ * scale per 16 elements, one FP32 tensor scale) and "Why 4-bit training normally falls
+ * apart - and the three fixes" (2D weight blocks; stochastic rounding for gradients).
+ *
+ *   x         device BF16 or FP32 (dt), element (r, c) at x[r*ld + c]; ld >= cols.
+ *   blk       NVFP4_BLOCK_1X16 (scale per 16 consecutive elements of a row) or
+ *             NVFP4_BLOCK_16X16 (one scale per aligned 16x16 tile; rows % 16 == 0).
+ *   rnd       NVFP4_ROUND_RN, or NVFP4_ROUND_SR (1x16 only): element j of the block with
+ *             row-major index b uses byte j%4 of word j/4 of Philox4x32-10 with key
+ *             (lo32 seed, hi32 seed) and counter (lo32 b, hi32 b, lo32 offset, hi32 offset);
+ *             it rounds up iff frac + byte/256 >= 1.
+ *   segments  NULL (nseg must be 1) or device int64[nseg+1] row offsets with
+ *             segments[0] = 0 <= ... <= segments[nseg] = rows (non-decreasing; multiples
+ *             of 16 for 16X16). Each segment gets its own amax and global scale (expert
+ *             stacks of a mixture-of-experts layer).
+ *   amax_in   NULL, or device float[nseg] holding max|x| per segment; then the amax pass is
+ *             skipped and no workspace is needed.
+ *   out       codes/scales/global_scale as documented above; out->rows == rows,
+ *             out->cols == cols.
+ *   out_t     NULL, or (16X16, nseg == 1 only) a second tensor receiving the quantization of
+ *             x^T ([cols, rows] along rows): the same tile scales and codes, transposed.
+ *   workspace device scratch of at least nvfp4_workspace_size(NVFP4_OP_QUANTIZE, rows,
+ *             cols, nseg) bytes, 256-byte aligned; may be NULL when amax_in is given.
+ * Errors: NVFP4_ERR_INVALID (null pointers, cols % 16, rows % 16 for 16X16, ld < cols, bad
+ * enum, nseg < 1, segments == NULL with nseg != 1, out_t without 16X16, tensor shape
+ * mismatch), NVFP4_ERR_UNSUPPORTED (SR with 16X16, out_t with segments),
+ * NVFP4_ERR_WORKSPACE, NVFP4_ERR_HIP.
+ */
+int nvfp4_quantize(const void* x, nvfp4_dtype dt, int64_t rows, int64_t cols, int64_t ld,
+                   nvfp4_block blk, nvfp4_round rnd, uint64_t seed, uint64_t offset,
+                   const int64_t* segments, int64_t nseg, const float* amax_in,
+                   nvfp4_tensor* out, nvfp4_tensor* out_t,
+                   void* workspace, size_t ws_bytes, void* hip_stream);
+
+/*
+ * nvfp4_rht_quantize - random Hadamard transform along tokens, then 1x16 quantization of
+ * the transposed result. Defined by: "Nemotron NVFP4" explainer, "Why 4-bit training
+ * normally falls apart - and the three fixes" (a random Hadamard matrix on the wgrad inputs,
+ * undone analytically inside the GEMM) and thelatentdaily "What matters for NVFP4
+ * training?", "A methodological warning" (random sign vectors of the rotations).
+ *
+ *   x          device BF16/FP32 [tokens, cols], element (t, c) at x[t*ld + c];
+ *              tokens % 16 == 0.
+ *   sign_mask  bit j set => sign -1 on element j of every 16-token block. Both operands of
+ *              one wgrad GEMM must use the same mask so that the transform cancels.
+ *   transform  for column c and block t: y_i = rn32(1/4 * sum_j H[i][j] s_j x[16t+j, c]),
+ *              H[i][j] = (-1)^popcount(i & j), evaluated as the 4-stage binary64 butterfly.
+ *   out        tensor [cols, tokens]: row c holds column c's transformed values quantized in
+ *              1x16 blocks along tokens (out->rows == cols, out->cols == tokens).
+ *   rnd/seed/offset as for nvfp4_quantize (SR block index is over the output [cols, tokens]).
+ *   amax_in    NULL or device float[1] = max|y| of the transformed tensor.
+ *   workspace  >= nvfp4_workspace_size(NVFP4_OP_RHT_QUANTIZE, tokens, cols, 1) bytes unless
+ *              amax_in is given.
+ * Errors: as nvfp4_quantize (tokens % 16, cols < 1, ld < cols, ...).
+ */
+int nvfp4_rht_quantize(const void* x, nvfp4_dtype dt, int64_t tokens, int64_t cols, int64_t ld,
+                       uint16_t sign_mask, nvfp4_round rnd, uint64_t seed, uint64_t offset,
+                       const float* amax_in, nvfp4_tensor* out,
+                       void* workspace, size_t ws_bytes, void* hip_stream);
+
+/*
+ * nvfp4_gemm - D[M, N] (FP32, row stride ldd) = A[M, K] * B[N, K]^T with both operands
+ * NVFP4 (each quantized along K), products accumulated in FP32, scaled by
+ * A->global_scale[0] * B->global_scale[0]. Covers the forward, activation-gradient and
+ * weight-gradient GEMMs of a linear layer (artiverse.ca "NVIDIA's 4-bit floating point
+ * pushes AI training limits", paragraph on which parts run in 4-bit).
+ *   A: rows = M, cols = K; B: rows = N, cols = K (same K, % 16 == 0); ldd >= N.
+ * Errors: NVFP4_ERR_INVALID (null pointers, K mismatch, K % 16, ldd < N), NVFP4_ERR_HIP.
+ */
+int nvfp4_gemm(const nvfp4_tensor* A, const nvfp4_tensor* B, float* D, int64_t ldd,
+               void* hip_stream);
+
+/*
+ * nvfp4_grouped_gemm - one GEMM per group (mixture-of-experts expert GEMMs; "Nemotron
+ * NVFP4" explainer, "The model underneath" and "The honest part: this is not end-to-end
+ * FP4": the expert GEMMs carry most of the compute and run in NVFP4).
+ *   m_offsets  device int64[G+1], 0 = m_offsets[0] <= ... <= m_offsets[G] = A->rows.
+ *   A          [sum M_g, K], global_scale[G] (one per group, as produced by nvfp4_quantize
+ *              with segments = m_offsets).
+ *   B          [G*N, K] stacked per-group weights, global_scale[G].
+ *   D          [sum M_g, N] FP32, row stride ldd: rows of group g hold A_g * B_g^T scaled by
+ *              A->global_scale[g] * B->global_scale[g]. Empty groups are allowed.
+ *   workspace  may be NULL (nvfp4_workspace_size returns 0 for this op).
+ * Errors: NVFP4_ERR_INVALID (G < 1, B->rows != G*N, K mismatch, ...), NVFP4_ERR_HIP.
+ */
+int nvfp4_grouped_gemm(int64_t G, const int64_t* m_offsets, const nvfp4_tensor* A,
+                       const nvfp4_tensor* B, int64_t N, float* D, int64_t ldd,
+                       void* workspace, size_t ws_bytes, void* hip_stream);
+
+/*
+ * nvfp4_amax - max|x| of x[rows, cols] (row stride ld), per row segment, into device
+ * amax_out[nseg]. With rht != 0 the maximum is taken over the Hadamard-transformed tensor
+ * of nvfp4_rht_quantize (rows = tokens, nseg must be 1). Useful to precompute amax_in.
+ * Errors: as nvfp4_quantize.
+ */
+int nvfp4_amax(const void* x, nvfp4_dtype dt, int64_t rows, int64_t cols, int64_t ld,
+               const int64_t* segments, int64_t nseg, int rht, uint16_t sign_mask,
+               float* amax_out, void* hip_stream);
+
+/* Bytes of device workspace `op` needs for the given shape (0 if none). */
+size_t nvfp4_workspace_size(int op, int64_t rows, int64_t cols, int64_t nseg);
+
+/* Thread-local description of the last non-OK status returned on this thread. */
+const char* nvfp4_last_error(void);
+
+/*
+ * nvfp4_dequantize - test helper: y[r, c] = rn32(e2m1 * e4m3 * global_scale[segment(r)]),
+ * y FP32 [rows, cols] contiguous. segments as for nvfp4_quantize (NULL, nseg = 1 allowed).
+ */
+int nvfp4_dequantize(const nvfp4_tensor* q, const int64_t* segments, int64_t nseg, float* y,
+                     void* hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* NVFP4_H */

@@ -1,0 +1,125 @@
+"""C-ABI checks that need no GPU: the built library loads, exports every entry point that
+include/nvfp4.h declares, and rejects invalid arguments on the host with the documented
+status codes before anything is enqueued (all cases below fail validation, so no HIP call
+is made)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import bit_block_scaled_quantize_amd as nv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nvfp4.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, -1, -2, -3
+FAKE = 0x10000          # 16-byte aligned, never dereferenced: validation fails first
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(nvfp4_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(nv.LIB_PATH):
+        pytest.skip("libnvfp4.so not built")
+    return nv.library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared()
+    assert set(names) == set(nv.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def _tensor(rows, cols, codes=FAKE, scales=FAKE, gs=FAKE):
+    return nv._CTensor(codes, scales, gs, rows, cols)
+
+
+def _q(lib, **kw):
+    a = dict(x=FAKE, dt=0, rows=32, cols=64, ld=64, blk=0, rnd=0, seed=0, offset=0, seg=None,
+             nseg=1, amax=None, out=_tensor(32, 64), out_t=None, ws=FAKE, ws_n=4096, stream=None)
+    a.update(kw)
+    out_t = ctypes.byref(a["out_t"]) if a["out_t"] is not None else None
+    out = ctypes.byref(a["out"]) if a["out"] is not None else None
+    return lib.nvfp4_quantize(a["x"], a["dt"], a["rows"], a["cols"], a["ld"], a["blk"], a["rnd"],
+                              a["seed"], a["offset"], a["seg"], a["nseg"], a["amax"], out, out_t,
+                              a["ws"], a["ws_n"], a["stream"])
+
+
+def test_quantize_validation(lib):
+    assert _q(lib, x=None) == INVALID
+    assert b"x is NULL" in lib.nvfp4_last_error()
+    assert _q(lib, cols=60, ld=64) == INVALID
+    assert _q(lib, ld=32) == INVALID
+    assert _q(lib, dt=7) == INVALID
+    assert _q(lib, blk=5) == INVALID
+    assert _q(lib, rnd=9) == INVALID
+    assert _q(lib, blk=1, rows=24, out=_tensor(24, 64)) == INVALID         # 16x16 rows % 16
+    assert _q(lib, nseg=3) == INVALID                                       # nseg without table
+    assert _q(lib, nseg=0) == INVALID
+    assert _q(lib, out_t=_tensor(64, 32)) == INVALID                        # out_t needs 16x16
+    assert _q(lib, blk=1, rnd=1) == UNSUPPORTED                             # SR on weights
+    assert _q(lib, blk=1, seg=FAKE, nseg=2, out_t=_tensor(64, 32)) == UNSUPPORTED
+    assert _q(lib, out=None) == INVALID
+    assert _q(lib, out=_tensor(32, 48)) == INVALID                          # shape mismatch
+    assert _q(lib, out=_tensor(32, 64, codes=None)) == INVALID
+    assert _q(lib, blk=1, out_t=_tensor(32, 64)) == INVALID                 # out_t must be [cols, rows]
+    assert _q(lib, ws=None) == WORKSPACE
+    assert _q(lib, ws_n=4) == WORKSPACE
+    assert _q(lib, ws=FAKE + 4) == WORKSPACE                                # misaligned
+    assert _q(lib, x=FAKE + 2) == UNSUPPORTED                               # misaligned input
+    assert _q(lib, ld=68, cols=64) == UNSUPPORTED                           # row stride not 16-byte
+
+
+def test_rht_validation(lib):
+    out = _tensor(64, 32)
+    f = lib.nvfp4_rht_quantize
+    assert f(FAKE, 0, 30, 64, 64, 0, 0, 0, 0, None, ctypes.byref(out), FAKE, 4096, None) == INVALID
+    assert f(FAKE, 0, 32, 64, 64, 0, 3, 0, 0, None, ctypes.byref(out), FAKE, 4096, None) == INVALID
+    bad = _tensor(32, 64)                                                    # must be [cols, tokens]
+    assert f(FAKE, 0, 32, 64, 64, 0, 0, 0, 0, None, ctypes.byref(bad), FAKE, 4096, None) == INVALID
+    assert f(FAKE, 0, 32, 64, 64, 0, 0, 0, 0, None, ctypes.byref(out), None, 0, None) == WORKSPACE
+
+
+def test_gemm_validation(lib):
+    a, b = _tensor(64, 128), _tensor(32, 128)
+    g = lib.nvfp4_gemm
+    assert g(None, ctypes.byref(b), FAKE, 32, None) == INVALID
+    assert g(ctypes.byref(a), ctypes.byref(_tensor(32, 96)), FAKE, 32, None) == INVALID   # K
+    assert g(ctypes.byref(a), ctypes.byref(b), None, 32, None) == INVALID
+    assert g(ctypes.byref(a), ctypes.byref(b), FAKE, 16, None) == INVALID                # ldd
+    assert g(ctypes.byref(_tensor(64, 100)), ctypes.byref(b), FAKE, 32, None) == INVALID  # K % 16
+    gg = lib.nvfp4_grouped_gemm
+    assert gg(0, FAKE, ctypes.byref(a), ctypes.byref(b), 32, FAKE, 32, None, 0, None) == INVALID
+    assert gg(2, None, ctypes.byref(a), ctypes.byref(b), 16, FAKE, 16, None, 0, None) == INVALID
+    assert gg(2, FAKE, ctypes.byref(a), ctypes.byref(b), 8, FAKE, 8, None, 0, None) == INVALID  # B rows
+
+
+def test_workspace_sizes(lib):
+    assert lib.nvfp4_workspace_size(nv.OP_QUANTIZE, 10, 16, 1) == 256
+    assert lib.nvfp4_workspace_size(nv.OP_QUANTIZE, 10, 16, 100) == 512
+    assert lib.nvfp4_workspace_size(nv.OP_RHT_QUANTIZE, 16, 16, 1) == 256
+    assert lib.nvfp4_workspace_size(nv.OP_GEMM, 16, 16, 1) == 0
+    assert lib.nvfp4_workspace_size(nv.OP_GROUPED_GEMM, 16, 16, 1) == 0
+
+
+def test_python_binding_raises_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(nv, "_lib", None)
+    monkeypatch.setattr(nv, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(nv.NVFP4Error):
+        nv.library()
+
+
+def test_product_package_does_not_import_oracle():
+    pkg = os.path.dirname(nv.__file__)
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                src = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in src and "from oracle" not in src, f

@@ -1,0 +1,117 @@
+"""GPU parity of the block-scaled GEMM and grouped GEMM: every output element within
+1e-5 * sum_k |a||b| of the binary64 GEMM of the oracle's dequantized operands (operands are
+first checked bit-exact against the oracle, so the reference uses the oracle's own bytes)."""
+import numpy as np
+import pytest
+import torch
+
+import bit_block_scaled_quantize_amd as nv
+import oracle
+import workloads
+from helpers import (assert_gemm_within_bound, assert_quant_equal, f32, host, log,
+                     to_device_bf16)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _pair(m, n, k, seed, rnd_a="rn", wblk="16x16"):
+    a_bits = workloads.with_outliers_bf16((m, k), seed)
+    w_bits = workloads.normal_bf16((n, k), seed + 1, std=0.02)
+    qa, _ = nv.quantize(to_device_bf16(a_bits), "1x16", rnd_a, seed=5, offset=0)
+    ra = oracle.quantize_1x16(f32(a_bits), rnd_a, seed=5, offset=0)
+    assert_quant_equal(host(qa), ra, "A")
+    if wblk == "16x16":
+        qb, _ = nv.quantize(to_device_bf16(w_bits), "16x16", "rn")
+        rb = oracle.quantize_16x16(f32(w_bits))
+    else:
+        qb, _ = nv.quantize(to_device_bf16(w_bits), "1x16", "rn")
+        rb = oracle.quantize_1x16(f32(w_bits))
+    assert_quant_equal(host(qb), rb, "B")
+    return qa, qb, oracle.dequantize(*ra), oracle.dequantize(*rb)
+
+
+def test_tiny_config_end_to_end():
+    # 256 x 256 activations (1x16, RN) and weights (16x16, RN), GEMM 256^3.
+    log("tiny end to end")
+    a_bits, w_bits = workloads.tiny()
+    qa, _ = nv.quantize(to_device_bf16(a_bits), "1x16", "rn")
+    qw, qwt = nv.quantize(to_device_bf16(w_bits), "16x16", "rn", emit_transposed=True)
+    ra = oracle.quantize_1x16(f32(a_bits))
+    rw = oracle.quantize_16x16(f32(w_bits))
+    assert_quant_equal(host(qa), ra, "tiny A")
+    assert_quant_equal(host(qw), rw, "tiny W")
+    assert_quant_equal(host(qwt), oracle.quantize_16x16(f32(w_bits).T.copy()), "tiny W^T")
+    d = nv.gemm(qa, qw)
+    torch.cuda.synchronize()
+    assert_gemm_within_bound(d.cpu().numpy(), oracle.dequantize(*ra), oracle.dequantize(*rw), "tiny gemm")
+
+
+@pytest.mark.parametrize("mnk", [(1, 1, 16), (17, 33, 48), (130, 257, 272), (64, 128, 512),
+                                 (256, 200, 2688), (129, 130, 1040)])
+def test_gemm_ragged(mnk):
+    m, n, k = mnk
+    log(f"gemm {mnk}")
+    qa, qb, ah, bh = _pair(m, n, k, 100 + m + n + k)
+    d = nv.gemm(qa, qb)
+    torch.cuda.synchronize()
+    assert_gemm_within_bound(d.cpu().numpy(), ah, bh, f"gemm {mnk}")
+
+
+def test_gemm_output_row_stride_and_sr_operand():
+    log("gemm ldd + SR operand")
+    qa, qb, ah, bh = _pair(70, 90, 320, 7, rnd_a="sr", wblk="1x16")
+    out = torch.full((70, 128), -7.0, dtype=torch.float32, device="cuda")
+    nv.gemm(qa, qb, out=out[:, :90])
+    torch.cuda.synchronize()
+    o = out.cpu().numpy()
+    assert np.all(o[:, 90:] == -7.0)
+    assert_gemm_within_bound(o[:, :90], ah, bh, "gemm ldd")
+
+
+def test_gemm_zero_and_one_hot():
+    log("gemm special operands")
+    k = 64
+    x = np.zeros((16, k), np.float32)
+    eye = np.eye(32, k, dtype=np.float32) * 3.0
+    qa, _ = nv.quantize(torch.from_numpy(x).cuda(), "1x16", "rn")
+    qb, _ = nv.quantize(torch.from_numpy(eye).cuda(), "1x16", "rn")
+    d = nv.gemm(qa, qb)
+    torch.cuda.synchronize()
+    assert np.all(d.cpu().numpy() == 0.0)
+    rng = np.random.default_rng(3)
+    y = rng.standard_normal((40, k)).astype(np.float32)
+    qy, _ = nv.quantize(torch.from_numpy(y).cuda(), "1x16", "rn")
+    d = nv.gemm(qy, qb)
+    torch.cuda.synchronize()
+    yh = oracle.dequantize(*oracle.quantize_1x16(y))
+    eh = oracle.dequantize(*oracle.quantize_1x16(eye))
+    assert_gemm_within_bound(d.cpu().numpy(), yh, eh, "one hot")
+
+
+def test_grouped_gemm_ragged_groups():
+    log("grouped gemm")
+    G, n, k = 6, 48, 96
+    off = np.array([0, 0, 5, 140, 141, 141, 300], np.int64)      # empty, tiny and >128 groups
+    x_bits = workloads.normal_bf16((int(off[-1]), k), 61)
+    w_bits = workloads.normal_bf16((G * n, k), 62)
+    offd = torch.from_numpy(off).cuda()
+    wseg = np.arange(G + 1, dtype=np.int64) * n
+    qx, _ = nv.quantize(to_device_bf16(x_bits), "1x16", "rn", segments=offd)
+    qw, _ = nv.quantize(to_device_bf16(w_bits), "16x16", "rn", segments=torch.from_numpy(wseg).cuda())
+    rx = oracle.quantize_1x16(f32(x_bits), segments=off)
+    rw = oracle.quantize_16x16(f32(w_bits), segments=wseg)
+    assert_quant_equal(host(qx), rx, "grouped X")
+    assert_quant_equal(host(qw), rw, "grouped W")
+    d = nv.grouped_gemm(offd, qx, qw, n)
+    torch.cuda.synchronize()
+    xh = oracle.dequantize(*rx, segments=off)
+    wh = oracle.dequantize(*rw, segments=wseg)
+    d64 = oracle.grouped_gemm_fp64(xh, wh, off, n)
+    bound = oracle.grouped_gemm_bound(xh, wh, off, n)
+    assert np.all(np.abs(d.cpu().numpy() - d64) <= bound)

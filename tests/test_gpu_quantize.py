@@ -1,0 +1,163 @@
+"""GPU parity of the quantize kernels with the oracle: bit-exact codes, scales and tensor
+scales, on ragged shapes, both input dtypes, both rounding modes, segments, and the edge
+cases of the scale rule (zero tensors, subnormal inputs and amax, huge values, signed
+zeros). All calls go through the C ABI via the binding."""
+import numpy as np
+import pytest
+import torch
+
+import bit_block_scaled_quantize_amd as nv
+import oracle
+import workloads
+from helpers import (assert_bytes_equal, assert_quant_equal, f32, host, log, to_device_bf16,
+                     to_device_f32)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _bits(shape, seed, std=1.0, outliers=True):
+    return (workloads.with_outliers_bf16(shape, seed) if outliers
+            else workloads.normal_bf16(shape, seed, std))
+
+
+SHAPES = [(1, 16), (3, 48), (17, 1040), (64, 256), (130, 80), (33, 2048)]
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+@pytest.mark.parametrize("rounding", ["rn", "sr"])
+def test_1x16_bf16(shape, rounding):
+    log(f"1x16 bf16 {shape} {rounding}")
+    bits = _bits(shape, 1000 + shape[0] * 7 + shape[1])
+    q, _ = nv.quantize(to_device_bf16(bits), "1x16", rounding, seed=0xABCDEF0123, offset=77)
+    ref = oracle.quantize_1x16(f32(bits), rounding, seed=0xABCDEF0123, offset=77)
+    assert_quant_equal(host(q), ref, f"1x16 {shape} {rounding}")
+
+
+@pytest.mark.parametrize("rounding", ["rn", "sr"])
+def test_1x16_fp32_with_row_stride(rounding):
+    log(f"1x16 fp32 strided {rounding}")
+    rng = np.random.default_rng(5)
+    full = (rng.standard_normal((40, 160)) * rng.uniform(0.01, 100, (40, 1))).astype(np.float32)
+    x = full[:, :96]
+    xd = to_device_f32(full)[:, :96]
+    q, _ = nv.quantize(xd, "1x16", rounding, seed=3, offset=(5 << 32) | 1)
+    ref = oracle.quantize_1x16(x, rounding, seed=3, offset=(5 << 32) | 1)
+    assert_quant_equal(host(q), ref, f"1x16 fp32 {rounding}")
+
+
+def test_1x16_all_bf16_patterns():
+    # Every finite BF16 pattern, 16 per block, quantized against several tensor amax values
+    # (amax_in), so every element meets many block and tensor scales.
+    log("1x16 exhaustive bf16 patterns")
+    pats = np.arange(65536, dtype=np.uint32)
+    expo = (pats >> 7) & 0xFF
+    rng = np.random.default_rng(9)
+    # exponent windows so that each trial spans a different set of block / tensor scales
+    windows = [(0, 254), (117, 137), (200, 254), (0, 30), (120, 130)]
+    for trial, (lo, hi) in enumerate(windows):
+        sel = pats[(expo >= lo) & (expo <= hi)].astype(np.uint16)
+        sel = sel if trial == 0 else sel[rng.permutation(len(sel))]
+        sel = np.concatenate([sel, np.zeros((-len(sel)) % 256, np.uint16)])
+        bits = sel.reshape(-1, 256)
+        x = f32(bits)
+        amax = oracle.amax(x)
+        for rnd in ("rn", "sr"):
+            for use_amax_in in (False, True):
+                amax_d = torch.from_numpy(amax).cuda() if use_amax_in else None
+                q, _ = nv.quantize(to_device_bf16(bits), "1x16", rnd, seed=11, offset=trial, amax=amax_d)
+                ref = oracle.quantize_1x16(x, rnd, seed=11, offset=trial, amax_vals=amax)
+                assert_quant_equal(host(q), ref, f"exhaustive window {lo}-{hi} {rnd} amax_in={use_amax_in}")
+
+
+def test_1x16_scale_edge_cases():
+    cases = {
+        "zeros": np.zeros((4, 32), np.float32),
+        "signed_zeros": np.where(np.arange(128).reshape(4, 32) % 3 == 0, -0.0, 0.0).astype(np.float32),
+        "subnormal_amax": np.full((2, 32), 1e-40, np.float32) * np.sign(np.arange(64).reshape(2, 32) - 31.5).astype(np.float32),
+        "tiny_blocks": np.concatenate([np.full((1, 16), 1e4, np.float32), np.full((1, 16), 1e-4, np.float32)], axis=1),
+        "huge": np.array([[3.0e38, -1e38] + [1.0] * 14], np.float32),
+        "one_hot": np.eye(16, 64, dtype=np.float32) * 5.0,
+        "midpoints": np.array([[0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0] * 2], np.float32),
+    }
+    for name, x in cases.items():
+        for rnd in ("rn", "sr"):
+            log(f"1x16 edge {name} {rnd}")
+            q, _ = nv.quantize(to_device_f32(x), "1x16", rnd, seed=1, offset=2)
+            ref = oracle.quantize_1x16(x, rnd, seed=1, offset=2)
+            assert_quant_equal(host(q), ref, f"edge {name} {rnd}")
+
+
+def test_1x16_segments_and_amax_api():
+    log("1x16 segments")
+    bits = _bits((200, 96), 44)
+    seg = np.array([0, 0, 16, 17, 100, 100, 200], np.int64)      # empty and ragged segments
+    segd = torch.from_numpy(seg).cuda()
+    x = f32(bits)
+    a = nv.amax(to_device_bf16(bits), segd)
+    torch.cuda.synchronize()
+    assert_bytes_equal(a.cpu().numpy().view(np.uint32), oracle.amax(x, seg).view(np.uint32), "segment amax")
+    for rnd in ("rn", "sr"):
+        q, _ = nv.quantize(to_device_bf16(bits), "1x16", rnd, seed=9, offset=0, segments=segd)
+        ref = oracle.quantize_1x16(x, rnd, seed=9, offset=0, segments=seg)
+        assert_quant_equal(host(q), ref, f"segments {rnd}")
+
+
+@pytest.mark.parametrize("shape", [(16, 16), (48, 80), (64, 1024), (160, 528)])
+def test_16x16_with_transpose(shape):
+    log(f"16x16 {shape}")
+    bits = _bits(shape, 2000 + shape[1], outliers=True)
+    x = f32(bits)
+    q, qt = nv.quantize(to_device_bf16(bits), "16x16", "rn", emit_transposed=True)
+    ref = oracle.quantize_16x16(x)
+    assert_quant_equal(host(q), ref, f"16x16 {shape}")
+    reft = oracle.quantize_16x16(np.ascontiguousarray(x.T), amax_vals=oracle.amax(x))
+    assert_quant_equal(host(qt), reft, f"16x16 transposed {shape}")
+
+
+def test_16x16_fp32_segments():
+    log("16x16 fp32 segments")
+    rng = np.random.default_rng(8)
+    x = rng.standard_normal((96, 64)).astype(np.float32) * np.repeat(rng.uniform(0.1, 10, 6), 16)[:, None].astype(np.float32)
+    seg = np.array([0, 32, 32, 96], np.int64)
+    q, _ = nv.quantize(to_device_f32(x), "16x16", "rn", segments=torch.from_numpy(seg).cuda())
+    assert_quant_equal(host(q), oracle.quantize_16x16(x, segments=seg), "16x16 segments")
+
+
+@pytest.mark.parametrize("shape", [(16, 1), (32, 7), (256, 129), (48, 513)])
+@pytest.mark.parametrize("rounding", ["rn", "sr"])
+def test_rht_quantize(shape, rounding):
+    log(f"rht {shape} {rounding}")
+    bits = _bits(shape, 3000 + shape[1], outliers=True)
+    x = f32(bits)
+    mask = workloads.wgrad_sign_mask()
+    q = nv.rht_quantize(to_device_bf16(bits), mask, rounding, seed=0x5EED, offset=1 << 32)
+    ref = oracle.rht_quantize(x, mask, rounding, seed=0x5EED, offset=1 << 32)
+    assert_quant_equal(host(q), ref, f"rht {shape} {rounding}")
+    a = nv.amax(to_device_bf16(bits), rht=True, sign_mask=mask)
+    torch.cuda.synchronize()
+    assert a.cpu().numpy()[0] == oracle.amax(oracle.rht_columnwise(x, mask))[0]
+
+
+def test_rht_fp32_masks():
+    rng = np.random.default_rng(12)
+    x = (rng.standard_normal((64, 40)) * 3).astype(np.float32)
+    for mask in (0, 0xFFFF, 0x8001):
+        log(f"rht fp32 mask {mask:#x}")
+        q = nv.rht_quantize(to_device_f32(x), mask, "rn")
+        assert_quant_equal(host(q), oracle.rht_quantize(x, mask, "rn"), f"rht fp32 {mask:#x}")
+
+
+def test_dequantize_matches_oracle():
+    log("dequantize")
+    bits = _bits((64, 128), 55)
+    q, _ = nv.quantize(to_device_bf16(bits), "1x16", "rn")
+    y = nv.dequantize(q)
+    torch.cuda.synchronize()
+    ref = oracle.dequantize(*oracle.quantize_1x16(f32(bits))).astype(np.float32)
+    assert_bytes_equal(y.cpu().numpy().view(np.uint32), ref.view(np.uint32), "dequantize")
