@@ -1,0 +1,314 @@
+"""Benchmark of the NVFP4 training hot path on one MI355X.
+
+One step = the whole path of one dense linear layer (tokens 8192, in 5120, out 20480):
+  quantize X (1x16, RN) and W (16x16, RN, + transposed copy)       -> fprop GEMM
+  quantize dY (1x16, SR)                                             -> dgrad GEMM (W^T reused)
+  Hadamard-transform + quantize dY^T (SR) and X^T (RN) along tokens  -> wgrad GEMM
+`value` is the step's GEMM work (3 x 2*M*N*K) divided by the whole step time, inputs already
+resident in HBM. Per-kernel times come from HIP events on the stream the kernels run on;
+the mixture-of-experts rows (per-expert quantize, grouped GEMM) are timed the same way.
+
+Prints ONE JSON line. Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense FP16/BF16 MFMA, TFLOP/s
+
+M, K_IN, N_OUT = 8192, 5120, 20480
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--no-moe", action="store_true")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--kernel-reps", type=int, default=5, help="cold-cache repetitions per kernel")
+    return p.parse_args()
+
+
+def q_bytes(rows, cols, transposed=False):
+    """Algorithmic bytes of one quantize call: read BF16 once, write codes + scales."""
+    el = rows * cols
+    return el * 2 + el * 0.5625 * (2 if transposed else 1)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; multi-GPU sharding is "
+                                   "described in DESIGN.md and not implemented"}))
+        sys.exit(2)
+
+    import torch
+
+    import bit_block_scaled_quantize_amd as nv
+    import workloads
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+
+    def to_dev(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    t0 = time.time()
+    x_bits, w_bits = workloads.fprop()
+    dy_bits = workloads.dgrad()
+    mask = workloads.wgrad_sign_mask()
+    X, W, dY = to_dev(x_bits), to_dev(w_bits), to_dev(dy_bits)
+    gen_s = time.time() - t0
+
+    T = nv.NVFP4Tensor
+    Xq, Wq, WqT, dYq = T.empty(M, K_IN), T.empty(N_OUT, K_IN), T.empty(K_IN, N_OUT), T.empty(M, N_OUT)
+    dYtq, Xtq = T.empty(N_OUT, M), T.empty(K_IN, M)
+    Y = torch.empty((M, N_OUT), dtype=torch.float32, device=dev)
+    dX = torch.empty((M, K_IN), dtype=torch.float32, device=dev)
+    dW = torch.empty((N_OUT, K_IN), dtype=torch.float32, device=dev)
+    ws = torch.empty((4096,), dtype=torch.uint8, device=dev)
+    flush = torch.empty((512 << 20,), dtype=torch.uint8, device=dev)
+
+    stages = [
+        ("quantize_x_1x16_rn", lambda: nv.quantize(X, "1x16", "rn", out=Xq, workspace=ws)),
+        ("quantize_w_16x16_rn_t", lambda: nv.quantize(W, "16x16", "rn", emit_transposed=True,
+                                                      out=Wq, out_t=WqT, workspace=ws)),
+        ("gemm_fprop", lambda: nv.gemm(Xq, Wq, out=Y)),
+        ("quantize_dy_1x16_sr", lambda: nv.quantize(dY, "1x16", "sr", seed=workloads.SR_SEED_DGRAD,
+                                                    offset=0, out=dYq, workspace=ws)),
+        ("gemm_dgrad", lambda: nv.gemm(dYq, WqT, out=dX)),
+        ("rht_quantize_dy_sr", lambda: nv.rht_quantize(dY, mask, "sr", seed=workloads.SR_SEED_WGRAD,
+                                                       offset=workloads.SR_OFFSET_WGRAD, out=dYtq,
+                                                       workspace=ws)),
+        ("rht_quantize_x_rn", lambda: nv.rht_quantize(X, mask, "rn", out=Xtq, workspace=ws)),
+        ("gemm_wgrad", lambda: nv.gemm(dYtq, Xtq, out=dW)),
+    ]
+    work = {
+        "quantize_x_1x16_rn": ("GB/s", q_bytes(M, K_IN)),
+        "quantize_w_16x16_rn_t": ("GB/s", q_bytes(N_OUT, K_IN, transposed=True)),
+        "quantize_dy_1x16_sr": ("GB/s", q_bytes(M, N_OUT)),
+        "rht_quantize_dy_sr": ("GB/s", q_bytes(M, N_OUT)),
+        "rht_quantize_x_rn": ("GB/s", q_bytes(M, K_IN)),
+        "gemm_fprop": ("TFLOP/s", 2.0 * M * N_OUT * K_IN),
+        "gemm_dgrad": ("TFLOP/s", 2.0 * M * K_IN * N_OUT),
+        "gemm_wgrad": ("TFLOP/s", 2.0 * N_OUT * K_IN * M),
+    }
+    step_flops = sum(v for u, v in work.values() if u == "TFLOP/s")
+
+    def run_step(events=None):
+        for i, (_, fn) in enumerate(stages):
+            if events is not None:
+                events[i][0].record(stream)
+            fn()
+            if events is not None:
+                events[i][1].record(stream)
+
+    for _ in range(args.warmup):
+        run_step()
+    torch.cuda.synchronize()
+
+    # --- timed region: K whole steps, per-stage events inside -------------------------------
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in stages] for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for s in range(args.steps):
+        run_step(ev[s])
+    end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    ms_per_step = total_ms / args.steps
+    stage_ms = {name: float(np.mean([ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps)]))
+                for i, (name, _) in enumerate(stages)}
+
+    def rate(name, ms):
+        unit, amount = work[name]
+        if unit == "GB/s":
+            val = amount / (ms * 1e-3) / 1e9
+            return {"us": round(ms * 1e3, 2), "GB/s": round(val, 1), "frac_hbm": round(val / HBM_PEAK_GBS, 4)}
+        val = amount / (ms * 1e-3) / 1e12
+        return {"us": round(ms * 1e3, 2), "TFLOP/s": round(val, 1), "frac_mfma_f16": round(val / MFMA_F16_PEAK_TFLOPS, 4)}
+
+    breakdown = {name: rate(name, ms) for name, ms in stage_ms.items()}
+
+    # --- cold-cache per-kernel timing of the quantize calls (HBM-resident inputs) ----------
+    cold = {}
+    for name, fn in stages:
+        if work[name][0] != "GB/s":
+            continue
+        times = []
+        for _ in range(args.kernel_reps):
+            flush.fill_(1)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(b))
+        cold[name] = rate(name, float(np.median(times)))
+    # encode pass alone (amax supplied) for the 1x16 RN activation quantize
+    amx = nv.amax(X)
+    times = []
+    for _ in range(args.kernel_reps):
+        flush.fill_(1)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        nv.quantize(X, "1x16", "rn", out=Xq, amax=amx)
+        b.record(stream)
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b))
+    cold["quantize_x_1x16_rn_encode_only"] = rate("quantize_x_1x16_rn", float(np.median(times)))
+
+    gemm_names = ["gemm_fprop", "gemm_dgrad", "gemm_wgrad"]
+    gemm_avg_ms = float(np.mean([stage_ms[n] for n in gemm_names]))
+    achieved = (2.0 * M * N_OUT * K_IN) / (gemm_avg_ms * 1e-3) / 1e12
+
+    out = {
+        "metric": "NVFP4 GEMM TFLOP/s (fprop/dgrad/wgrad) + quantize GB/s, % of roofline",
+        "value": round(step_flops / (ms_per_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16-mfma/fp32-acc",
+        "data": "synthetic",
+        "config": {"workload": "dense linear layer NVFP4 training step (fprop+dgrad+wgrad), "
+                               "tokens 8192, in 5120, out 20480",
+                   "tokens": M, "in_features": K_IN, "out_features": N_OUT,
+                   "weights": "16x16 blocks", "grad_rounding": "stochastic",
+                   "wgrad_transform": "16-point random-sign Hadamard", "parallelism": "none"},
+        "roofline": {"bound": "mfma", "kernel": "k_gemm (fprop/dgrad/wgrad average)",
+                     "achieved": round(achieved, 1), "peak": MFMA_F16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4),
+                     "traffic": None},
+        "breakdown": breakdown,
+        "quantize_cold_cache": cold,
+        "input_gen_s": round(gen_s, 1),
+    }
+
+    if not args.no_moe:
+        out["moe"] = bench_moe(nv, workloads, torch, dev, stream, flush, args)
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(x_bits, w_bits, dy_bits, mask, step_flops)
+    print(json.dumps(out))
+
+
+def bench_moe(nv, workloads, torch, dev, stream, flush, args):
+    """Per-expert quantize of the expert-sorted activations and stacked weights, then the
+    grouped fprop GEMM (128 experts, top-6 of 16384 tokens, hidden 2688, expert FFN 1856)."""
+    x_bits, w_bits, off = workloads.moe()
+    G, n, k = workloads.MOE_EXPERTS, workloads.MOE_FFN, workloads.MOE_HIDDEN
+    total = int(off[-1])
+    X = torch.from_numpy(x_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    Wt = torch.from_numpy(w_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    offd = torch.from_numpy(off).to(dev)
+    wseg = torch.arange(G + 1, dtype=torch.int64, device=dev) * n
+    Xq, Wq = nv.NVFP4Tensor.empty(total, k, G), nv.NVFP4Tensor.empty(G * n, k, G)
+    D = torch.empty((total, n), dtype=torch.float32, device=dev)
+    ws = torch.empty((4096,), dtype=torch.uint8, device=dev)
+    calls = {
+        "quantize_x_experts_1x16_rn": (lambda: nv.quantize(X, "1x16", "rn", segments=offd, out=Xq, workspace=ws),
+                                       "GB/s", q_bytes(total, k)),
+        "quantize_w_experts_16x16_rn": (lambda: nv.quantize(Wt, "16x16", "rn", segments=wseg, out=Wq, workspace=ws),
+                                        "GB/s", q_bytes(G * n, k)),
+        "grouped_gemm": (lambda: nv.grouped_gemm(offd, Xq, Wq, n, out=D), "TFLOP/s", 2.0 * total * n * k),
+    }
+    res = {}
+    for name, (fn, unit, amount) in calls.items():
+        fn()
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(max(args.kernel_reps, 3)):
+            flush.fill_(1)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(b))
+        ms = float(np.median(times))
+        if unit == "GB/s":
+            v = amount / (ms * 1e-3) / 1e9
+            res[name] = {"us": round(ms * 1e3, 2), "GB/s": round(v, 1), "frac_hbm": round(v / HBM_PEAK_GBS, 4)}
+        else:
+            v = amount / (ms * 1e-3) / 1e12
+            res[name] = {"us": round(ms * 1e3, 2), "TFLOP/s": round(v, 1),
+                         "frac_mfma_f16": round(v / MFMA_F16_PEAK_TFLOPS, 4)}
+    res["config"] = {"experts": G, "tokens": workloads.MOE_TOKENS, "topk": workloads.MOE_TOPK,
+                     "hidden": k, "ffn": n, "rows_total": total,
+                     "rows_per_expert_max": int(np.diff(off).max()),
+                     "rows_per_expert_min": int(np.diff(off).min())}
+    return res
+
+
+def cpu_baseline(x_bits, w_bits, dy_bits, mask, step_flops):
+    """The oracle (numpy; BLAS dgemm for the FP64 reference GEMM) timed on a bounded sample
+    of the same step, scaled to the whole step."""
+    import oracle
+    import workloads
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = os.cpu_count() or 1
+    f32 = workloads.bf16_bits_to_f32
+    rng = np.random.default_rng(0)
+    parts = []
+
+    def timed(fn):
+        t = time.perf_counter()
+        r = fn()
+        return time.perf_counter() - t, r
+
+    rows = 64
+    xs = f32(x_bits[:rows])
+    A = oracle.amax(xs)
+    t, _ = timed(lambda: oracle.quantize_1x16(xs, amax_vals=A))
+    parts.append(t * M / rows)
+    ws_ = f32(w_bits[:rows])
+    t, _ = timed(lambda: (oracle.quantize_16x16(ws_, amax_vals=A),
+                          oracle.quantize_16x16(np.ascontiguousarray(ws_.T), amax_vals=A)))
+    parts.append(t * N_OUT / rows)
+    dys = f32(dy_bits[:16])
+    t, _ = timed(lambda: oracle.quantize_1x16(dys, "sr", seed=1, offset=0, amax_vals=A))
+    parts.append(t * M / 16)
+    cols = 32
+    t, _ = timed(lambda: oracle.rht_quantize(f32(dy_bits[:, :cols]), mask, "sr", seed=1,
+                                             amax_vals=A, col_ids=np.arange(cols)))
+    parts.append(t * N_OUT / cols)
+    t, _ = timed(lambda: oracle.rht_quantize(f32(x_bits[:, :cols]), mask, "rn",
+                                             amax_vals=A, col_ids=np.arange(cols)))
+    parts.append(t * K_IN / cols)
+    # reference GEMM: 32 output rows of each GEMM against the full other operand
+    a_hat = rng.standard_normal((32, K_IN))
+    b_hat = rng.standard_normal((N_OUT, K_IN))
+    t, _ = timed(lambda: oracle.gemm_fp64(a_hat, b_hat))
+    parts.append(3 * t * M / 32)
+    total_s = float(sum(parts))
+    return {"value": round(step_flops / total_s / 1e12, 6), "unit": "TFLOP/s",
+            "cores": int(blas_threads), "kind": "oracle",
+            "sample": "oracle on 64 rows of X/W, 16 rows of dY, 32 columns of each Hadamard "
+                      "operand and 32 output rows of each FP64 GEMM, scaled to the full step "
+                      f"(estimated {total_s:.1f} s per step; numpy elementwise on 1 core, "
+                      f"BLAS on {blas_threads} threads)"}
+
+
+if __name__ == "__main__":
+    main()

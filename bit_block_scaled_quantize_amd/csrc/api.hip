@@ -45,12 +45,20 @@ int check_out(const nvfp4_tensor* t, int64_t rows, int64_t cols, const char* nam
   return NVFP4_OK;
 }
 
-int check_input(const void* x, nvfp4_dtype dt, int64_t rows, int64_t cols, int64_t ld) {
+// Row-blocked kernels read 16-byte vectors along rows (rows_vec = true); the Hadamard kernel
+// reads column pairs across rows and only needs the pair to be aligned.
+int check_input(const void* x, nvfp4_dtype dt, int64_t rows, int64_t cols, int64_t ld,
+                bool rows_vec = true) {
   if (!x) return fail(NVFP4_ERR_INVALID, "x is NULL");
   if (dt != NVFP4_IN_BF16 && dt != NVFP4_IN_FP32) return fail(NVFP4_ERR_INVALID, "bad dtype %d", (int)dt);
   if (rows < 0 || cols < 1) return fail(NVFP4_ERR_INVALID, "bad shape [%lld, %lld]", (long long)rows, (long long)cols);
   if (ld < cols) return fail(NVFP4_ERR_INVALID, "ld (%lld) < cols (%lld)", (long long)ld, (long long)cols);
-  const int64_t vec = dt == NVFP4_IN_BF16 ? 8 : 4;      // elements per 16 bytes
+  const size_t esz = dt == NVFP4_IN_BF16 ? 2 : 4;
+  if (!rows_vec) {
+    if (!aligned(x, 2 * esz)) return fail(NVFP4_ERR_UNSUPPORTED, "x must be %zu-byte aligned", 2 * esz);
+    return NVFP4_OK;
+  }
+  const int64_t vec = (int64_t)(16 / esz);              // elements per 16 bytes
   if (!aligned(x, 16) || ld % vec != 0)
     return fail(NVFP4_ERR_UNSUPPORTED, "x must be 16-byte aligned with ld a multiple of %lld", (long long)vec);
   return NVFP4_OK;
@@ -75,7 +83,7 @@ size_t nvfp4_workspace_size(int op, int64_t rows, int64_t cols, int64_t nseg) {
 int nvfp4_amax(const void* x, nvfp4_dtype dt, int64_t rows, int64_t cols, int64_t ld,
                const int64_t* segments, int64_t nseg, int rht, uint16_t sign_mask,
                float* amax_out, void* hip_stream) {
-  int st = check_input(x, dt, rows, cols, ld);
+  int st = check_input(x, dt, rows, cols, ld, !rht);
   if (st) return st;
   if (!amax_out) return fail(NVFP4_ERR_INVALID, "amax_out is NULL");
   if (nseg < 1 || (!segments && nseg != 1)) return fail(NVFP4_ERR_INVALID, "bad segment table (nseg=%lld)", (long long)nseg);
@@ -133,7 +141,7 @@ int nvfp4_rht_quantize(const void* x, nvfp4_dtype dt, int64_t tokens, int64_t co
                        uint16_t sign_mask, nvfp4_round rnd, uint64_t seed, uint64_t offset,
                        const float* amax_in, nvfp4_tensor* out, void* workspace, size_t ws_bytes,
                        void* hip_stream) {
-  int st = check_input(x, dt, tokens, cols, ld);
+  int st = check_input(x, dt, tokens, cols, ld, false);
   if (st) return st;
   if (rnd != NVFP4_ROUND_RN && rnd != NVFP4_ROUND_SR) return fail(NVFP4_ERR_INVALID, "bad rounding mode %d", (int)rnd);
   if (tokens % 16) return fail(NVFP4_ERR_INVALID, "tokens (%lld) must be a multiple of 16", (long long)tokens);

@@ -24,30 +24,34 @@ constexpr int kColsPerLane = 2;
 constexpr int kColsPerBlock = kThreads * kColsPerLane;
 constexpr int kTokenBlocksPerTask = 8;
 
+// Columns c and c+1 of one token row. `both` says whether c+1 exists; `paired` whether the
+// pair is aligned for one vector load (even row stride), else two scalar loads are used.
 template <typename TIn>
-__device__ __forceinline__ void load_pair(const TIn* p, bool both, float& a, float& b);
+__device__ __forceinline__ void load_pair(const TIn* p, bool both, bool paired, float& a, float& b);
 
 template <>
-__device__ __forceinline__ void load_pair<uint16_t>(const uint16_t* p, bool both, float& a, float& b) {
-  if (both) {
+__device__ __forceinline__ void load_pair<uint16_t>(const uint16_t* p, bool both, bool paired,
+                                                    float& a, float& b) {
+  if (both && paired) {
     const uint32_t w = *reinterpret_cast<const uint32_t*>(p);
     a = bf16_lo(w);
     b = bf16_hi(w);
   } else {
-    a = __uint_as_float((uint32_t)(*p) << 16);
-    b = 0.0f;
+    a = __uint_as_float((uint32_t)p[0] << 16);
+    b = both ? __uint_as_float((uint32_t)p[1] << 16) : 0.0f;
   }
 }
 
 template <>
-__device__ __forceinline__ void load_pair<float>(const float* p, bool both, float& a, float& b) {
-  if (both) {
+__device__ __forceinline__ void load_pair<float>(const float* p, bool both, bool paired, float& a,
+                                                 float& b) {
+  if (both && paired) {
     const v2f32 w = *reinterpret_cast<const v2f32*>(p);
     a = w.x;
     b = w.y;
   } else {
-    a = *p;
-    b = 0.0f;
+    a = p[0];
+    b = both ? p[1] : 0.0f;
   }
 }
 
@@ -86,6 +90,7 @@ __global__ __launch_bounds__(kThreads) void k_rht(
   const bool valid0 = c < cols;
   const bool valid1 = c + 1 < cols;
   const int64_t cl = valid0 ? c : 0;                         // clamped column for loads
+  const bool paired = (ld & 1) == 0;
 
   float s_enc = 1.0f;
   if constexpr (ENCODE) {
@@ -97,7 +102,7 @@ __global__ __launch_bounds__(kThreads) void k_rht(
     float v0[16], v1[16];
 #pragma unroll
     for (int j = 0; j < 16; ++j)
-      load_pair<TIn>(x + (tb * 16 + j) * ld + cl, valid1, v0[j], v1[j]);
+      load_pair<TIn>(x + (tb * 16 + j) * ld + cl, valid1, paired, v0[j], v1[j]);
 #pragma unroll
     for (int k = 0; k < kColsPerLane; ++k) {
       const bool valid = k == 0 ? valid0 : valid1;
