@@ -16,8 +16,21 @@
 //
 // Operand layout inside a 16x16x32 MFMA: lane l supplies row (l % 16) of A (column of B)
 // and 8 K-values. Since the K order inside a dot product is free as long as A and B agree,
-// each lane loads one contiguous 16-byte run (32 codes) of its row per 128-K step and feeds
+// each lane holds one contiguous 16-byte run (32 codes) of its row per 128-K step and feeds
 // its 4 octets to 4 consecutive MFMAs; the 4 lane groups cover 4 different 32-element runs.
+//
+// Two kernels:
+//  * main (K % 64 == 0, every shape of the workloads): a workgroup of 4 waves (2 x 2) owns a
+//    256 x 256 output tile, each wave 128 x 128 (8 x 8 MFMA tiles, 256 FP32 accumulators per
+//    lane in AGPRs). Per 128-wide K step the workgroup's FP4 panels (2 x 16 KB) and their
+//    scale bytes (2 x 2 KB) go straight from global memory into LDS with buffer-to-LDS DMA,
+//    double-buffered: the DMA for step s+1 is issued right after step s's fragments are read,
+//    so it has the whole of step s's MFMA work to land, and no registers are spent on
+//    staging. Buffer bounds make rows past the end of an operand read as zero.
+//  * general (any K % 16 == 0): 128 x 128 tiles, each wave 64 x 64, operands loaded straight
+//    into registers one K step ahead.
+// In both, scale bytes at or past K are forced to 0, which zeroes whatever codes sit in a
+// partial last step.
 #include "device_common.h"
 #include "launch.h"
 
@@ -27,23 +40,18 @@ namespace {
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float float4v __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-constexpr int kThreads = 256;             // 4 waves, 2 x 2
-constexpr int kFragsM = 4;                // wave tile 64 x 64 = 4 x 4 MFMA tiles of 16 x 16
-constexpr int kFragsN = 4;
-constexpr int kWaveM = 16 * kFragsM;
-constexpr int kWaveN = 16 * kFragsN;
-constexpr int kBlockM = 2 * kWaveM;       // 128
-constexpr int kBlockN = 2 * kWaveN;       // 128
+constexpr int kThreads = 256;
 constexpr int kStepK = 128;
 
 // FP16 pair (S * 2^-8, S * 2^-8) from an E4M3 code: the code shifted into the FP16 exponent
 // and mantissa fields reads as S * 2^-8 for every code, subnormal ones included.
 __device__ __forceinline__ half2v scale_pair(uint32_t s) {
-  const uint32_t b = (s << 7) | (s << 23);
-  return __builtin_bit_cast(half2v, b);
+  return __builtin_bit_cast(half2v, (s << 7) | (s << 23));
 }
 
+// 8 codes (one 32-bit word) -> 8 FP16 values e2m1 * S.
 __device__ __forceinline__ half8 decode8(uint32_t codes, half2v s2) {
   const half2v p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 256.0f, 0) * s2;
   const half2v p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 256.0f, 1) * s2;
@@ -52,37 +60,13 @@ __device__ __forceinline__ half8 decode8(uint32_t codes, half2v s2) {
   return half8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
-struct FragLoad { uint4 codes; uint32_t scales; };
-
-// 32 codes of row `row` starting at element k (multiple of 32) and their two scale bytes;
-// elements at or beyond K read as zero codes.
-__device__ __forceinline__ FragLoad load_frag(const uint8_t* __restrict__ codes,
-                                              const uint8_t* __restrict__ scales, int64_t row,
-                                              int64_t K, int64_t k) {
-  FragLoad f{make_uint4(0, 0, 0, 0), 0};
-  const int64_t left = K - k;
-  if (left <= 0) return f;
-  const uint8_t* cp = codes + row * (K >> 1) + (k >> 1);
-  const uint8_t* sp = scales + row * (K >> 4) + (k >> 4);
-  if (left >= 32) {
-    if ((K & 31) == 0) {
-      f.codes = *reinterpret_cast<const uint4*>(cp);
-    } else {
-      const uint2 a = *reinterpret_cast<const uint2*>(cp);
-      const uint2 b = *reinterpret_cast<const uint2*>(cp + 8);
-      f.codes = make_uint4(a.x, a.y, b.x, b.y);
-    }
-    f.scales = (uint32_t)sp[0] | ((uint32_t)sp[1] << 8);
-  } else {                                  // exactly 16 elements remain (K % 16 == 0)
-    const uint2 a = *reinterpret_cast<const uint2*>(cp);
-    f.codes = make_uint4(a.x, a.y, 0, 0);
-    f.scales = (uint32_t)sp[0];
-  }
-  return f;
+__device__ __forceinline__ uint32_t word(const v4u32& v, int t) {
+  return t == 0 ? v.x : t == 1 ? v.y : t == 2 ? v.z : v.w;
 }
 
-__device__ __forceinline__ uint32_t word(const uint4& v, int t) {
-  return t == 0 ? v.x : t == 1 ? v.y : t == 2 ? v.z : v.w;
+// Scale-byte mask for the 32-element run starting at element k: bytes at or past K -> 0.
+__device__ __forceinline__ uint32_t k_mask(int64_t K, int64_t k) {
+  return (k < K ? 0xFFu : 0u) | (k + 16 < K ? 0xFF00u : 0u);
 }
 
 // Tile (tm, tn) of a grid of tiles_m x tiles_n tiles for workgroup `bid`. Workgroups are
@@ -104,11 +88,250 @@ __device__ __forceinline__ void tile_of(int64_t bid, int64_t tiles_m, int64_t ti
   tn = in_band / gm;
 }
 
-// One 128 x 128 output tile: rows [m0, m1) of A against rows [n0, n0 + 128) of B.
-__device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ ac, const uint8_t* __restrict__ as,
-                                          const uint8_t* __restrict__ bc, const uint8_t* __restrict__ bs,
-                                          int64_t m0, int64_t m1, int64_t n0, int64_t n1, int64_t K,
-                                          float alpha, float* __restrict__ D, int64_t ldd) {
+// Group of m-tile slot `slot_m` for tiles of height bm; returns false past the last tile.
+__device__ __forceinline__ bool group_of(int64_t G, const int64_t* __restrict__ off, int64_t total_m,
+                                         int64_t bm, int64_t slot_m, int64_t& g, int64_t& m0,
+                                         int64_t& m1) {
+  int64_t base = 0;
+  int64_t prev = off[0] < 0 ? 0 : (off[0] > total_m ? total_m : off[0]);
+  for (int64_t q = 0; q < G; ++q) {
+    int64_t hi = off[q + 1];
+    hi = hi < prev ? prev : (hi > total_m ? total_m : hi);   // clamp a malformed table
+    const int64_t t = (hi - prev + bm - 1) / bm;
+    if (slot_m < base + t) {
+      g = q;
+      m0 = prev + (slot_m - base) * bm;
+      m1 = m0 + bm < hi ? m0 + bm : hi;
+      return true;
+    }
+    base += t;
+    prev = hi;
+  }
+  return false;
+}
+
+struct Operand {
+  const uint8_t* codes;   // [rows, K/2]
+  const uint8_t* scales;  // [rows, K/16]
+  int64_t rows;           // rows addressable through this operand
+};
+
+// =========================================================================================
+// main kernel: 256 x 256 tiles, 32x32x16 MFMA, LDS DMA staging (K % 64 == 0)
+// =========================================================================================
+// In v_mfma_f32_32x32x16_f16 lane l supplies row (l % 32) of A (column of B) and 8 K-values;
+// lane half h = l / 32 picks which 8. Per 128-wide K step each lane therefore owns one
+// contiguous 64-code run (32 bytes, 4 scale blocks = one aligned scale dword) of its row,
+// bytes [32h, 32h + 32) of the step, and feeds its 8 octets to 8 consecutive MFMAs.
+namespace big {
+constexpr int kWaveM = 128, kWaveN = 128;
+constexpr int kFragsM = kWaveM / 32, kFragsN = kWaveN / 32;   // 4 x 4 MFMA tiles per wave
+constexpr int kBlockM = 2 * kWaveM, kBlockN = 2 * kWaveN;     // 256 x 256
+constexpr int kFragBytes = 32 * 64;                           // 32 rows x 128 codes
+constexpr int kFragScaleBytes = 32 * 8;                       // 32 rows x 8 scale bytes
+constexpr int kFragsA = kBlockM / 32;                         // 8
+constexpr int kPanelFrags = kFragsA + kBlockN / 32;           // 16 fragments per K step
+constexpr int kCodeBytes = kPanelFrags * kFragBytes;          // 32 KB
+constexpr int kStageBytes = kCodeBytes + kPanelFrags * kFragScaleBytes;   // 36 KB
+constexpr int kLdsBytes = 2 * kStageBytes;                    // 72 KB, double-buffered
+}  // namespace big
+
+typedef float float16v __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+
+// Scale-byte mask for the 64-element run starting at element k: blocks at or past K -> 0.
+__device__ __forceinline__ uint32_t k_mask4(int64_t K, int64_t k) {
+  return (k < K ? 0xFFu : 0u) | (k + 16 < K ? 0xFF00u : 0u) | (k + 32 < K ? 0xFF0000u : 0u) |
+         (k + 48 < K ? 0xFF000000u : 0u);
+}
+
+__device__ __forceinline__ void gemm_tile_big(Operand A, Operand B, int64_t m0, int64_t m1,
+                                              int64_t n0, int64_t n1, int64_t K, float alpha,
+                                              float* __restrict__ D, int64_t ldd, uint8_t* lds) {
+  using namespace big;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int r = lane & 31, h = lane >> 5;
+  const int wm = wave >> 1, wn = wave & 1;
+  const uint32_t rs_codes = (uint32_t)(K >> 1), rs_scales = (uint32_t)(K >> 4);
+
+  const __amdgpu_buffer_rsrc_t a_codes = make_rsrc(A.codes, A.rows * (K >> 1));
+  const __amdgpu_buffer_rsrc_t b_codes = make_rsrc(B.codes, B.rows * (K >> 1));
+  const __amdgpu_buffer_rsrc_t a_scales = make_rsrc(A.scales, A.rows * (K >> 4));
+  const __amdgpu_buffer_rsrc_t b_scales = make_rsrc(B.scales, B.rows * (K >> 4));
+
+  // DMA: this wave moves fragments f = wave + 4*i (i < 2: A, i >= 2: B), two 1 KB halves
+  // each; lane (r, h) of half q carries row 32*f' + r, bytes [32h + 16q, 32h + 16q + 16) of
+  // the step -> LDS f*2 KB + q*1 KB + lane*16. Its scale dword (bytes [4h, 4h + 4) of the
+  // row's 8 scale bytes of the step) -> LDS scales + f*256 + lane*4.
+  const uint32_t dma_a = (uint32_t)(m0 + wave * 32 + r) * rs_codes + (uint32_t)(h * 32);
+  const uint32_t dma_b = (uint32_t)(n0 + wave * 32 + r) * rs_codes + (uint32_t)(h * 32);
+  const uint32_t sdma_a = (uint32_t)(m0 + wave * 32 + r) * rs_scales + (uint32_t)(h * 4);
+  const uint32_t sdma_b = (uint32_t)(n0 + wave * 32 + r) * rs_scales + (uint32_t)(h * 4);
+  const uint32_t dma_stride = 128u * rs_codes;                // 4 fragments = 128 rows apart
+  const uint32_t sdma_stride = 128u * rs_scales;
+
+  auto issue_dma = [&](int64_t step, int buf) {
+    uint8_t* base = lds + buf * kStageBytes;
+    const uint32_t koff = (uint32_t)(step * (kStepK / 2));
+    const uint32_t soff = (uint32_t)(step * (kStepK / 16));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool is_a = i < 2;
+      const int f = wave + 4 * i;
+      const uint32_t off = (is_a ? dma_a : dma_b) + (uint32_t)(i & 1) * dma_stride + koff;
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a ? a_codes : b_codes,
+                                                 (lds_ptr_t)(base + f * kFragBytes + q * 1024),
+                                                 16, off + 16 * q, 0, 0, 0);
+      const uint32_t so = (is_a ? sdma_a : sdma_b) + (uint32_t)(i & 1) * sdma_stride + soff;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a ? a_scales : b_scales,
+                                               (lds_ptr_t)(base + kCodeBytes + f * kFragScaleBytes),
+                                               4, so, 0, 0, 0);
+    }
+  };
+
+  float16v acc[kFragsM][kFragsN];
+#pragma unroll
+  for (int i = 0; i < kFragsM; ++i)
+#pragma unroll
+    for (int j = 0; j < kFragsN; ++j) acc[i][j] = float16v{};
+
+  const int64_t steps = (K + kStepK - 1) / kStepK;
+  issue_dma(0, 0);
+
+  for (int64_t s = 0; s < steps; ++s) {
+    const int buf = (int)(s & 1);
+    __builtin_amdgcn_s_waitcnt(0x0F70);                       // vmcnt(0): this step's DMA landed
+    __syncthreads();
+
+    const uint8_t* cur = lds + buf * kStageBytes;
+    const uint32_t keep = k_mask4(K, s * kStepK + h * 64);
+    v4u32 araw[kFragsM][2], braw[kFragsN][2];
+    uint32_t sa[kFragsM], sb[kFragsN];
+#pragma unroll
+    for (int j = 0; j < kFragsN; ++j) {
+      const int f = kFragsA + wn * kFragsN + j;
+      braw[j][0] = *reinterpret_cast<const v4u32*>(cur + f * kFragBytes + lane * 16);
+      braw[j][1] = *reinterpret_cast<const v4u32*>(cur + f * kFragBytes + 1024 + lane * 16);
+      sb[j] = *reinterpret_cast<const uint32_t*>(cur + kCodeBytes + f * kFragScaleBytes + lane * 4) & keep;
+    }
+#pragma unroll
+    for (int i = 0; i < kFragsM; ++i) {
+      const int f = wm * kFragsM + i;
+      araw[i][0] = *reinterpret_cast<const v4u32*>(cur + f * kFragBytes + lane * 16);
+      araw[i][1] = *reinterpret_cast<const v4u32*>(cur + f * kFragBytes + 1024 + lane * 16);
+      sa[i] = *reinterpret_cast<const uint32_t*>(cur + kCodeBytes + f * kFragScaleBytes + lane * 4) & keep;
+    }
+
+    if (s + 1 < steps) issue_dma(s + 1, buf ^ 1);
+
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      half8 bv[kFragsN];
+#pragma unroll
+      for (int j = 0; j < kFragsN; ++j)
+        bv[j] = decode8(word(braw[j][t >> 2], t & 3), scale_pair((sb[j] >> (8 * (t >> 1))) & 0xFFu));
+#pragma unroll
+      for (int i = 0; i < kFragsM; ++i) {
+        const half8 av = decode8(word(araw[i][t >> 2], t & 3), scale_pair((sa[i] >> (8 * (t >> 1))) & 0xFFu));
+#pragma unroll
+        for (int j = 0; j < kFragsN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, bv[j], acc[i][j], 0, 0, 0);
+      }
+    }
+  }
+
+  // D fragment layout (32 x 32): lane l holds column l % 32 and, for q = 0..15, row
+  // 8*(q/4) + 4*(l/32) + q%4.
+#pragma unroll
+  for (int i = 0; i < kFragsM; ++i) {
+#pragma unroll
+    for (int j = 0; j < kFragsN; ++j) {
+      const int64_t col = n0 + wn * kWaveN + 32 * j + r;
+      if (col >= n1) continue;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int64_t row = m0 + wm * kWaveM + 32 * i + 8 * (q >> 2) + 4 * h + (q & 3);
+        if (row < m1) D[row * ldd + col] = acc[i][j][q] * alpha;
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void k_gemm_big(Operand A, const float* __restrict__ ag, Operand B, const float* __restrict__ bg,
+                int64_t K, float* __restrict__ D, int64_t ldd) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds_dyn[];
+  using namespace big;
+  const int64_t tiles_m = (A.rows + kBlockM - 1) / kBlockM;
+  const int64_t tiles_n = (B.rows + kBlockN - 1) / kBlockN;
+  int64_t tm, tn;
+  tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  const int64_t m0 = tm * kBlockM, n0 = tn * kBlockN;
+  const int64_t m1 = m0 + kBlockM < A.rows ? m0 + kBlockM : A.rows;
+  const int64_t n1 = n0 + kBlockN < B.rows ? n0 + kBlockN : B.rows;
+  gemm_tile_big(A, B, m0, m1, n0, n1, K, ag[0] * bg[0], D, ldd, lds_dyn);
+}
+
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void k_grouped_gemm_big(int64_t G, const int64_t* __restrict__ off, Operand A,
+                        const float* __restrict__ ag, Operand B, const float* __restrict__ bg,
+                        int64_t N, int64_t K, float* __restrict__ D, int64_t ldd) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds_dyn[];
+  using namespace big;
+  const int64_t tiles_n = (N + kBlockN - 1) / kBlockN;
+  const int64_t slot_m = blockIdx.x / tiles_n;
+  const int64_t tn = blockIdx.x - slot_m * tiles_n;
+  int64_t g, m0, m1;
+  if (!group_of(G, off, A.rows, kBlockM, slot_m, g, m0, m1)) return;
+  const int64_t n0 = tn * kBlockN;
+  const int64_t n1 = n0 + kBlockN < N ? n0 + kBlockN : N;
+  const Operand Bg{B.codes + g * N * (K >> 1), B.scales + g * N * (K >> 4), N};
+  gemm_tile_big(A, Bg, m0, m1, n0, n1, K, ag[g] * bg[g], D, ldd, lds_dyn);
+}
+
+// =========================================================================================
+// general kernel: 128 x 128 tiles, operands straight into registers (any K % 16 == 0)
+// =========================================================================================
+namespace small {
+constexpr int kFragsM = 4, kFragsN = 4;                       // wave tile 64 x 64
+constexpr int kWaveM = 16 * kFragsM, kWaveN = 16 * kFragsN;
+constexpr int kBlockM = 2 * kWaveM, kBlockN = 2 * kWaveN;     // 128 x 128
+}  // namespace small
+
+struct FragLoad { v4u32 codes; uint32_t scales; };
+
+// 32 codes of row `row` starting at element k (multiple of 32) and their two scale bytes;
+// elements at or beyond K read as zero codes and zero scales.
+__device__ __forceinline__ FragLoad load_frag(const uint8_t* __restrict__ codes,
+                                              const uint8_t* __restrict__ scales, int64_t row,
+                                              int64_t K, int64_t k) {
+  FragLoad f{v4u32{0, 0, 0, 0}, 0};
+  const int64_t left = K - k;
+  if (left <= 0) return f;
+  const uint8_t* cp = codes + row * (K >> 1) + (k >> 1);
+  const uint8_t* sp = scales + row * (K >> 4) + (k >> 4);
+  const v2u32 a = *reinterpret_cast<const v2u32*>(cp);
+  if (left >= 32) {
+    const v2u32 b = *reinterpret_cast<const v2u32*>(cp + 8);
+    f.codes = v4u32{a.x, a.y, b.x, b.y};
+    f.scales = (uint32_t)sp[0] | ((uint32_t)sp[1] << 8);
+  } else {                                  // exactly 16 elements remain (K % 16 == 0)
+    f.codes = v4u32{a.x, a.y, 0, 0};
+    f.scales = (uint32_t)sp[0];
+  }
+  return f;
+}
+
+__device__ __forceinline__ void gemm_tile_small(Operand A, Operand B, int64_t m0, int64_t m1,
+                                                int64_t n0, int64_t n1, int64_t K, float alpha,
+                                                float* __restrict__ D, int64_t ldd) {
+  using namespace small;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
@@ -119,7 +342,7 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ ac, const 
 #pragma unroll
   for (int i = 0; i < kFragsM; ++i) {
     const int64_t rr = wm0 + 16 * i + r;
-    arow[i] = rr < m1 ? rr : m0;                 // clamp: rows past the end load row m0
+    arow[i] = rr < m1 ? rr : m0;                 // rows past the end reload row m0
   }
 #pragma unroll
   for (int j = 0; j < kFragsN; ++j) {
@@ -134,20 +357,18 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ ac, const 
     for (int j = 0; j < kFragsN; ++j) acc[i][j] = float4v{0.f, 0.f, 0.f, 0.f};
 
   FragLoad fa[kFragsM], fb[kFragsN];
-  int64_t k = (int64_t)g * 32;
 #pragma unroll
-  for (int i = 0; i < kFragsM; ++i) fa[i] = load_frag(ac, as, arow[i], K, k);
+  for (int i = 0; i < kFragsM; ++i) fa[i] = load_frag(A.codes, A.scales, arow[i], K, g * 32);
 #pragma unroll
-  for (int j = 0; j < kFragsN; ++j) fb[j] = load_frag(bc, bs, brow[j], K, k);
+  for (int j = 0; j < kFragsN; ++j) fb[j] = load_frag(B.codes, B.scales, brow[j], K, g * 32);
 
   for (int64_t k0 = 0; k0 < K; k0 += kStepK) {
     FragLoad na[kFragsM], nb[kFragsN];
-    const int64_t kn = k0 + kStepK + (int64_t)g * 32;
+    const int64_t kn = k0 + kStepK + g * 32;
 #pragma unroll
-    for (int i = 0; i < kFragsM; ++i) na[i] = load_frag(ac, as, arow[i], K, kn);
+    for (int i = 0; i < kFragsM; ++i) na[i] = load_frag(A.codes, A.scales, arow[i], K, kn);
 #pragma unroll
-    for (int j = 0; j < kFragsN; ++j) nb[j] = load_frag(bc, bs, brow[j], K, kn);
-
+    for (int j = 0; j < kFragsN; ++j) nb[j] = load_frag(B.codes, B.scales, brow[j], K, kn);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       half8 av[kFragsM], bv[kFragsN];
@@ -169,7 +390,6 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ ac, const 
     for (int j = 0; j < kFragsN; ++j) fb[j] = nb[j];
   }
 
-  // D fragment layout: lane l holds rows 4*(l/16) + 0..3 of column l % 16.
 #pragma unroll
   for (int i = 0; i < kFragsM; ++i) {
 #pragma unroll
@@ -185,56 +405,47 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ ac, const 
   }
 }
 
-__global__ __launch_bounds__(kThreads) void k_gemm(const uint8_t* __restrict__ ac,
-                                                   const uint8_t* __restrict__ as,
-                                                   const float* __restrict__ ag,
-                                                   const uint8_t* __restrict__ bc,
-                                                   const uint8_t* __restrict__ bs,
-                                                   const float* __restrict__ bg, int64_t M,
-                                                   int64_t N, int64_t K, float* __restrict__ D,
-                                                   int64_t ldd) {
-  const int64_t tiles_m = (M + kBlockM - 1) / kBlockM;
-  const int64_t tiles_n = (N + kBlockN - 1) / kBlockN;
+__global__ __launch_bounds__(kThreads)
+void k_gemm_small(Operand A, const float* __restrict__ ag, Operand B, const float* __restrict__ bg,
+                  int64_t K, float* __restrict__ D, int64_t ldd) {
+  using namespace small;
+  const int64_t tiles_m = (A.rows + kBlockM - 1) / kBlockM;
+  const int64_t tiles_n = (B.rows + kBlockN - 1) / kBlockN;
   int64_t tm, tn;
   tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
   const int64_t m0 = tm * kBlockM, n0 = tn * kBlockN;
-  const int64_t m1 = m0 + kBlockM < M ? m0 + kBlockM : M;
-  const int64_t n1 = n0 + kBlockN < N ? n0 + kBlockN : N;
-  const float alpha = ag[0] * bg[0];
-  gemm_tile(ac, as, bc, bs, m0, m1, n0, n1, K, alpha, D, ldd);
+  const int64_t m1 = m0 + kBlockM < A.rows ? m0 + kBlockM : A.rows;
+  const int64_t n1 = n0 + kBlockN < B.rows ? n0 + kBlockN : B.rows;
+  gemm_tile_small(A, B, m0, m1, n0, n1, K, ag[0] * bg[0], D, ldd);
 }
 
-// Grouped GEMM: workgroup slot s enumerates (m-tile of some group, n-tile); groups are found
-// by walking the device offset table. Slots past the last tile exit at once.
-__global__ __launch_bounds__(kThreads) void k_grouped_gemm(
-    int64_t G, const int64_t* __restrict__ off, const uint8_t* __restrict__ ac,
-    const uint8_t* __restrict__ as, const float* __restrict__ ag, const uint8_t* __restrict__ bc,
-    const uint8_t* __restrict__ bs, const float* __restrict__ bg, int64_t total_m, int64_t N,
-    int64_t K, float* __restrict__ D, int64_t ldd) {
+__global__ __launch_bounds__(kThreads)
+void k_grouped_gemm_small(int64_t G, const int64_t* __restrict__ off, Operand A,
+                          const float* __restrict__ ag, Operand B, const float* __restrict__ bg,
+                          int64_t N, int64_t K, float* __restrict__ D, int64_t ldd) {
+  using namespace small;
   const int64_t tiles_n = (N + kBlockN - 1) / kBlockN;
   const int64_t slot_m = blockIdx.x / tiles_n;
   const int64_t tn = blockIdx.x - slot_m * tiles_n;
-  int64_t base = 0, g = -1, m0 = 0, m1 = 0;
-  int64_t prev = off[0] < 0 ? 0 : off[0];
-  for (int64_t q = 0; q < G; ++q) {
-    int64_t hi = off[q + 1];
-    hi = hi < prev ? prev : (hi > total_m ? total_m : hi);   // clamp a malformed table
-    const int64_t t = (hi - prev + kBlockM - 1) / kBlockM;
-    if (slot_m < base + t) {
-      g = q;
-      m0 = prev + (slot_m - base) * kBlockM;
-      m1 = m0 + kBlockM < hi ? m0 + kBlockM : hi;
-      break;
-    }
-    base += t;
-    prev = hi;
-  }
-  if (g < 0) return;
+  int64_t g, m0, m1;
+  if (!group_of(G, off, A.rows, kBlockM, slot_m, g, m0, m1)) return;
   const int64_t n0 = tn * kBlockN;
   const int64_t n1 = n0 + kBlockN < N ? n0 + kBlockN : N;
-  const float alpha = ag[g] * bg[g];
-  gemm_tile(ac, as, bc + g * N * (K >> 1), bs + g * N * (K >> 4), m0, m1, n0, n1, K, alpha, D,
-            ldd);
+  const Operand Bg{B.codes + g * N * (K >> 1), B.scales + g * N * (K >> 4), N};
+  gemm_tile_small(A, Bg, m0, m1, n0, n1, K, ag[g] * bg[g], D, ldd);
+}
+
+bool use_big(int64_t K) { return K > 0 && (K % 64) == 0; }
+
+hipError_t enable_big_lds() {
+  static hipError_t once = [] {
+    hipError_t e = hipFuncSetAttribute((const void*)k_gemm_big,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, big::kLdsBytes);
+    if (e != hipSuccess) return e;
+    return hipFuncSetAttribute((const void*)k_grouped_gemm_big,
+                               hipFuncAttributeMaxDynamicSharedMemorySize, big::kLdsBytes);
+  }();
+  return once;
 }
 
 }  // namespace
@@ -242,9 +453,18 @@ __global__ __launch_bounds__(kThreads) void k_grouped_gemm(
 hipError_t launch_gemm(GemmOperand a, GemmOperand b, int64_t M, int64_t N, int64_t K, float* D,
                        int64_t ldd, hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
-  const int64_t tiles = ((M + kBlockM - 1) / kBlockM) * ((N + kBlockN - 1) / kBlockN);
-  hipLaunchKernelGGL(k_gemm, dim3((unsigned)tiles), dim3(kThreads), 0, stream, a.codes, a.scales,
-                     a.global_scale, b.codes, b.scales, b.global_scale, M, N, K, D, ldd);
+  const Operand A{a.codes, a.scales, M}, B{b.codes, b.scales, N};
+  if (use_big(K)) {
+    const hipError_t e = enable_big_lds();
+    if (e != hipSuccess) return e;
+    const int64_t tiles = ((M + big::kBlockM - 1) / big::kBlockM) * ((N + big::kBlockN - 1) / big::kBlockN);
+    hipLaunchKernelGGL(k_gemm_big, dim3((unsigned)tiles), dim3(kThreads), big::kLdsBytes, stream,
+                       A, a.global_scale, B, b.global_scale, K, D, ldd);
+  } else {
+    const int64_t tiles = ((M + small::kBlockM - 1) / small::kBlockM) * ((N + small::kBlockN - 1) / small::kBlockN);
+    hipLaunchKernelGGL(k_gemm_small, dim3((unsigned)tiles), dim3(kThreads), 0, stream, A,
+                       a.global_scale, B, b.global_scale, K, D, ldd);
+  }
   return hipGetLastError();
 }
 
@@ -252,11 +472,21 @@ hipError_t launch_grouped_gemm(int64_t G, const int64_t* m_offsets, GemmOperand 
                                int64_t total_m, int64_t N, int64_t K, float* D, int64_t ldd,
                                hipStream_t stream) {
   if (total_m == 0 || N == 0) return hipSuccess;
-  const int64_t tiles_n = (N + kBlockN - 1) / kBlockN;
-  const int64_t slots_m = total_m / kBlockM + G;          // >= sum_g ceil(M_g / 128)
-  hipLaunchKernelGGL(k_grouped_gemm, dim3((unsigned)(slots_m * tiles_n)), dim3(kThreads), 0,
-                     stream, G, m_offsets, a.codes, a.scales, a.global_scale, b.codes, b.scales,
-                     b.global_scale, total_m, N, K, D, ldd);
+  const Operand A{a.codes, a.scales, total_m}, B{b.codes, b.scales, G * N};
+  if (use_big(K)) {
+    const hipError_t e = enable_big_lds();
+    if (e != hipSuccess) return e;
+    const int64_t tiles_n = (N + big::kBlockN - 1) / big::kBlockN;
+    const int64_t slots_m = total_m / big::kBlockM + G;       // >= sum_g ceil(M_g / 256)
+    hipLaunchKernelGGL(k_grouped_gemm_big, dim3((unsigned)(slots_m * tiles_n)), dim3(kThreads),
+                       big::kLdsBytes, stream, G, m_offsets, A, a.global_scale, B,
+                       b.global_scale, N, K, D, ldd);
+  } else {
+    const int64_t tiles_n = (N + small::kBlockN - 1) / small::kBlockN;
+    const int64_t slots_m = total_m / small::kBlockM + G;
+    hipLaunchKernelGGL(k_grouped_gemm_small, dim3((unsigned)(slots_m * tiles_n)), dim3(kThreads),
+                       0, stream, G, m_offsets, A, a.global_scale, B, b.global_scale, N, K, D, ldd);
+  }
   return hipGetLastError();
 }
 

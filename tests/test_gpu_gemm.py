@@ -53,7 +53,11 @@ def test_tiny_config_end_to_end():
 
 
 @pytest.mark.parametrize("mnk", [(1, 1, 16), (17, 33, 48), (130, 257, 272), (64, 128, 512),
-                                 (256, 200, 2688), (129, 130, 1040)])
+                                 (256, 200, 2688), (129, 130, 1040),
+                                 # K % 64 == 0: the 256 x 256 LDS-staged kernel, with ragged
+                                 # M/N edges and a partial last 128-wide K step
+                                 (300, 520, 192), (257, 33, 64), (1000, 700, 1344),
+                                 (513, 1024, 5120)])
 def test_gemm_ragged(mnk):
     m, n, k = mnk
     log(f"gemm {mnk}")
