@@ -59,7 +59,7 @@ def _load():
     lib.nvfp4_gemm.argtypes = [pt, pt, vp, i64, vp]
     lib.nvfp4_grouped_gemm.argtypes = [i64, vp, pt, pt, i64, vp, i64, vp, sz, vp]
     lib.nvfp4_amax.argtypes = [vp, ctypes.c_int, i64, i64, i64, vp, i64, ctypes.c_int,
-                               ctypes.c_uint16, vp, vp]
+                               ctypes.c_uint16, vp, vp, sz, vp]
     lib.nvfp4_workspace_size.argtypes = [ctypes.c_int, i64, i64, i64]
     lib.nvfp4_workspace_size.restype = sz
     lib.nvfp4_last_error.restype = ctypes.c_char_p
@@ -207,15 +207,20 @@ def grouped_gemm(m_offsets: torch.Tensor, a: NVFP4Tensor, b: NVFP4Tensor, n: int
 
 
 def amax(x: torch.Tensor, segments: torch.Tensor | None = None, rht: bool = False,
-         sign_mask: int = 0, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+         sign_mask: int = 0, out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+         stream=None) -> torch.Tensor:
     """nvfp4_amax: max|x| per segment (or of the Hadamard-transformed tensor)."""
     lib = _load()
     dt, rows, cols, ld = _input(x)
     nseg = 1 if segments is None else segments.numel() - 1
     if out is None:
         out = torch.empty((nseg,), dtype=torch.float32, device=x.device)
+    if workspace is None:
+        workspace, ws_n = _workspace(OP_RHT_QUANTIZE if rht else OP_QUANTIZE, rows, cols, nseg, x.device)
+    else:
+        ws_n = workspace.numel()
     _check(lib.nvfp4_amax(_ptr(x), dt, rows, cols, ld, _ptr(segments), nseg, int(rht),
-                          sign_mask & 0xFFFF, _ptr(out), _stream(stream)))
+                          sign_mask & 0xFFFF, _ptr(out), _ptr(workspace), ws_n, _stream(stream)))
     return out
 
 

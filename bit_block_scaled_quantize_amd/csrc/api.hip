@@ -73,28 +73,46 @@ const char* nvfp4_last_error(void) { return g_last_error.c_str(); }
 size_t nvfp4_workspace_size(int op, int64_t rows, int64_t cols, int64_t nseg) {
   (void)rows;
   (void)cols;
+  const size_t partials = (size_t)nvfp4::kMaxAmaxPartials * sizeof(float);
   switch (op) {
-    case NVFP4_OP_QUANTIZE: return round_up((size_t)(nseg < 1 ? 1 : nseg) * sizeof(float), kWsAlign);
-    case NVFP4_OP_RHT_QUANTIZE: return kWsAlign;
+    case NVFP4_OP_QUANTIZE: {
+      const size_t segs = (size_t)(nseg < 1 ? 1 : nseg) * sizeof(float);
+      return round_up(segs > partials ? segs : partials, kWsAlign);
+    }
+    case NVFP4_OP_RHT_QUANTIZE: return round_up(partials, kWsAlign);
     default: return 0;
   }
 }
 
 int nvfp4_amax(const void* x, nvfp4_dtype dt, int64_t rows, int64_t cols, int64_t ld,
                const int64_t* segments, int64_t nseg, int rht, uint16_t sign_mask,
-               float* amax_out, void* hip_stream) {
+               float* amax_out, void* workspace, size_t ws_bytes, void* hip_stream) {
   int st = check_input(x, dt, rows, cols, ld, !rht);
   if (st) return st;
   if (!amax_out) return fail(NVFP4_ERR_INVALID, "amax_out is NULL");
   if (nseg < 1 || (!segments && nseg != 1)) return fail(NVFP4_ERR_INVALID, "bad segment table (nseg=%lld)", (long long)nseg);
-  hipStream_t s = (hipStream_t)hip_stream;
-  if (rht) {
-    if (segments) return fail(NVFP4_ERR_UNSUPPORTED, "segments with the Hadamard transform");
-    if (rows % 16) return fail(NVFP4_ERR_INVALID, "tokens (%lld) must be a multiple of 16", (long long)rows);
-    return hip_status(nvfp4::launch_rht_amax(x, dt == NVFP4_IN_FP32, rows, cols, ld, sign_mask, amax_out, s), "rht amax");
+  if (rht && segments) return fail(NVFP4_ERR_UNSUPPORTED, "segments with the Hadamard transform");
+  if (rht && rows % 16) return fail(NVFP4_ERR_INVALID, "tokens (%lld) must be a multiple of 16", (long long)rows);
+  if (!rht && cols % 16) return fail(NVFP4_ERR_INVALID, "cols (%lld) must be a multiple of 16", (long long)cols);
+  const bool need_ws = rht || !segments;
+  if (need_ws) {
+    const size_t need = nvfp4_workspace_size(rht ? NVFP4_OP_RHT_QUANTIZE : NVFP4_OP_QUANTIZE, rows, cols, nseg);
+    if (!workspace || ws_bytes < need || !aligned(workspace, kWsAlign))
+      return fail(NVFP4_ERR_WORKSPACE, "workspace of %zu bytes (256-byte aligned) required, got %zu", need, ws_bytes);
   }
-  if (cols % 16) return fail(NVFP4_ERR_INVALID, "cols (%lld) must be a multiple of 16", (long long)cols);
-  return hip_status(nvfp4::launch_amax(x, dt == NVFP4_IN_FP32, rows, cols, ld, segments, nseg, amax_out, s), "amax");
+  hipStream_t s = (hipStream_t)hip_stream;
+  const bool f32 = dt == NVFP4_IN_FP32;
+  int parts = 1;
+  if (rht) {
+    float* ws = static_cast<float*>(workspace);
+    if ((st = hip_status(nvfp4::launch_rht_amax_parts(x, f32, rows, cols, ld, sign_mask, ws, &parts, s), "rht amax"))) return st;
+    return hip_status(nvfp4::launch_reduce_partials(ws, parts, amax_out, s), "amax reduce");
+  }
+  if (segments)
+    return hip_status(nvfp4::launch_amax_parts(x, f32, rows, cols, ld, segments, nseg, amax_out, &parts, s), "amax");
+  float* ws = static_cast<float*>(workspace);
+  if ((st = hip_status(nvfp4::launch_amax_parts(x, f32, rows, cols, ld, nullptr, 1, ws, &parts, s), "amax"))) return st;
+  return hip_status(nvfp4::launch_reduce_partials(ws, parts, amax_out, s), "amax reduce");
 }
 
 int nvfp4_quantize(const void* x, nvfp4_dtype dt, int64_t rows, int64_t cols, int64_t ld,
@@ -122,18 +140,19 @@ int nvfp4_quantize(const void* x, nvfp4_dtype dt, int64_t rows, int64_t cols, in
   }
   hipStream_t s = (hipStream_t)hip_stream;
   const bool f32 = dt == NVFP4_IN_FP32;
+  int parts = 1;
   if (!amax) {
     float* ws = static_cast<float*>(workspace);
-    if ((st = hip_status(nvfp4::launch_amax(x, f32, rows, cols, ld, segments, nseg, ws, s), "amax"))) return st;
+    if ((st = hip_status(nvfp4::launch_amax_parts(x, f32, rows, cols, ld, segments, nseg, ws, &parts, s), "amax"))) return st;
     amax = ws;
   }
   const nvfp4::QuantOut q{out->codes, out->scales, out->global_scale};
   if (blk == NVFP4_BLOCK_1X16)
     return hip_status(nvfp4::launch_encode_1x16(x, f32, rows, cols, ld, rnd == NVFP4_ROUND_SR, seed,
-                                                offset, segments, nseg, amax, q, s), "encode 1x16");
+                                                offset, segments, nseg, amax, parts, q, s), "encode 1x16");
   nvfp4::QuantOut qt{};
   if (out_t) qt = nvfp4::QuantOut{out_t->codes, out_t->scales, out_t->global_scale};
-  return hip_status(nvfp4::launch_encode_16x16(x, f32, rows, cols, ld, segments, nseg, amax, q,
+  return hip_status(nvfp4::launch_encode_16x16(x, f32, rows, cols, ld, segments, nseg, amax, parts, q,
                                                out_t ? &qt : nullptr, s), "encode 16x16");
 }
 
@@ -154,15 +173,15 @@ int nvfp4_rht_quantize(const void* x, nvfp4_dtype dt, int64_t tokens, int64_t co
   }
   hipStream_t s = (hipStream_t)hip_stream;
   const bool f32 = dt == NVFP4_IN_FP32;
+  int parts = 1;
   if (!amax) {
     float* ws = static_cast<float*>(workspace);
-    if ((st = hip_status(nvfp4::launch_rht_amax(x, f32, tokens, cols, ld, sign_mask, ws, s), "rht amax"))) return st;
+    if ((st = hip_status(nvfp4::launch_rht_amax_parts(x, f32, tokens, cols, ld, sign_mask, ws, &parts, s), "rht amax"))) return st;
     amax = ws;
   }
-  if (tokens == 0) return NVFP4_OK;
   const nvfp4::QuantOut q{out->codes, out->scales, out->global_scale};
   return hip_status(nvfp4::launch_rht_encode(x, f32, tokens, cols, ld, sign_mask, rnd == NVFP4_ROUND_SR,
-                                             seed, offset, amax, q, s), "rht encode");
+                                             seed, offset, amax, parts, q, s), "rht encode");
 }
 
 static int check_operand(const nvfp4_tensor* t, const char* name) {

@@ -13,27 +13,35 @@ struct QuantOut {
   float* global_scale;
 };
 
-// amax: zero amax_out[0..nseg) and accumulate max|x| per row segment.
-hipError_t launch_amax(const void* x, bool fp32, int64_t rows, int64_t cols, int64_t ld,
-                       const int64_t* segments, int64_t nseg, float* amax_out,
-                       hipStream_t stream);
+// Tensor amax of x[rows, cols]. With segments: amax_out[0..nseg) gets max|x| per segment
+// (*parts = 1). Without: amax_out[0..*parts) gets partial maxima (at most 1024) whose max is
+// the tensor amax; the encode launchers take (amax, parts) and fold the partials themselves.
+hipError_t launch_amax_parts(const void* x, bool fp32, int64_t rows, int64_t cols, int64_t ld,
+                             const int64_t* segments, int64_t nseg, float* amax_out, int* parts,
+                             hipStream_t stream);
+
+// out[0] = max of partial[0..parts).
+hipError_t launch_reduce_partials(const float* partial, int parts, float* out, hipStream_t stream);
 
 hipError_t launch_encode_1x16(const void* x, bool fp32, int64_t rows, int64_t cols, int64_t ld,
                               bool sr, uint64_t seed, uint64_t offset,
-                              const int64_t* segments, int64_t nseg, const float* amax,
+                              const int64_t* segments, int64_t nseg, const float* amax, int parts,
                               QuantOut out, hipStream_t stream);
 
 hipError_t launch_encode_16x16(const void* x, bool fp32, int64_t rows, int64_t cols, int64_t ld,
-                               const int64_t* segments, int64_t nseg, const float* amax,
+                               const int64_t* segments, int64_t nseg, const float* amax, int parts,
                                QuantOut out, const QuantOut* out_t, hipStream_t stream);
 
-// Hadamard transform along tokens: amax of the transformed tensor, and the transposed encode.
-hipError_t launch_rht_amax(const void* x, bool fp32, int64_t tokens, int64_t cols, int64_t ld,
-                           uint16_t sign_mask, float* amax_out, hipStream_t stream);
+// Hadamard transform along tokens: partial maxima of the transformed tensor (at most 1024),
+// and the transposed encode.
+hipError_t launch_rht_amax_parts(const void* x, bool fp32, int64_t tokens, int64_t cols, int64_t ld,
+                                 uint16_t sign_mask, float* partial, int* parts, hipStream_t stream);
 
 hipError_t launch_rht_encode(const void* x, bool fp32, int64_t tokens, int64_t cols, int64_t ld,
                              uint16_t sign_mask, bool sr, uint64_t seed, uint64_t offset,
-                             const float* amax, QuantOut out, hipStream_t stream);
+                             const float* amax, int parts, QuantOut out, hipStream_t stream);
+
+constexpr int kMaxAmaxPartials = 1024;
 
 struct GemmOperand {
   const uint8_t* codes;

@@ -7,12 +7,13 @@
 // artiverse.ca "NVIDIA's 4-bit floating point pushes AI training limits" (16x16 weight
 // blocks instead of 1x16, stochastic rounding on gradients only).
 //
-// All kernels are HBM-streaming: one wave owns whole rows (or a 16-row strip for 16x16
-// tiles), every lane loads 16-byte vectors so that a wave-wide load covers a contiguous
-// span of a row, and results are written as packed nibble words plus one scale byte per
-// block. The encode pass walks the tensor in the reverse order of the amax pass so that
-// its first reads hit the lines the amax pass touched last (still in the 256 MB
-// Infinity Cache for tensors of that order of size).
+// All kernels stream from HBM with 16-byte vector loads that cover contiguous row spans.
+// The tensor amax (needed before any block scale is final) is a separate pass: for an
+// unsegmented tensor each workgroup writes one partial maximum and the encode kernel folds
+// the partials itself (no same-address atomics, no extra launch); for per-expert segments
+// one atomic max per (wave, segment run) lands on that segment's slot. The encode pass walks
+// the tensor in the reverse order of the amax pass so that its first reads hit the lines
+// the amax pass touched last (still in the 256 MB Infinity Cache).
 #include "device_common.h"
 #include "launch.h"
 
@@ -21,6 +22,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWavesPerBlock = kThreads / 64;
+constexpr int kMaxPartials = 1024;
 
 // 16 consecutive inputs starting at p (16-byte aligned) as floats.
 template <typename TIn>
@@ -57,58 +59,134 @@ __device__ __forceinline__ float abs_max16(const float (&v)[16]) {
   return m;
 }
 
+// max |.| of one 16-byte vector of inputs (8 BF16 or 4 FP32)
+template <typename TIn>
+__device__ __forceinline__ float vec_absmax(const TIn* p);
+
+template <>
+__device__ __forceinline__ float vec_absmax<uint16_t>(const uint16_t* p) {
+  const v4u32 a = ld_u32x4(p);
+  return fmaxf(fmaxf(fmaxf(fabsf(bf16_lo(a.x)), fabsf(bf16_hi(a.x))),
+                     fmaxf(fabsf(bf16_lo(a.y)), fabsf(bf16_hi(a.y)))),
+               fmaxf(fmaxf(fabsf(bf16_lo(a.z)), fabsf(bf16_hi(a.z))),
+                     fmaxf(fabsf(bf16_lo(a.w)), fabsf(bf16_hi(a.w)))));
+}
+
+template <>
+__device__ __forceinline__ float vec_absmax<float>(const float* p) {
+  const v4f32 a = ld_f32x4(p);
+  return fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w)));
+}
+
+// Workgroup-wide max; every thread gets the result.
+__device__ __forceinline__ float block_max(float m, float* red) {
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  float r = red[0];
+#pragma unroll
+  for (int w = 1; w < kWavesPerBlock; ++w) r = fmaxf(r, red[w]);
+  __syncthreads();
+  return r;
+}
+
 // ---------------------------------------------------------------------------------------
-// amax: each wave owns rows r = wave, wave + nwaves, ...; lanes stride over 16-element
-// groups of the row. Per-segment maxima are flushed with one atomic per (wave, segment run).
-template <typename TIn, bool SEG>
-__global__ __launch_bounds__(kThreads) void k_amax(const TIn* __restrict__ x, int64_t rows,
-                                                   int64_t cols, int64_t ld,
-                                                   const int64_t* __restrict__ seg, int64_t nseg,
-                                                   float* __restrict__ amax_out) {
+// amax, unsegmented: workgroup b reduces its share of the 16-byte vectors of x (rows of
+// `vecs_per_row` vectors, row stride ld) into partial[b].
+template <typename TIn>
+__global__ __launch_bounds__(kThreads) void k_amax_partial(const TIn* __restrict__ x, int64_t rows,
+                                                           int64_t vecs_per_row, int64_t ld,
+                                                           float* __restrict__ partial) {
+  __shared__ float red[kWavesPerBlock];
+  constexpr int64_t kVec = 16 / sizeof(TIn);
+  const int64_t total = rows * vecs_per_row;
+  const int64_t per = (total + gridDim.x - 1) / gridDim.x;
+  const int64_t q0 = (int64_t)blockIdx.x * per;
+  const int64_t q1 = q0 + per < total ? q0 + per : total;
+  const bool contiguous = ld == vecs_per_row * kVec;
+  float m = 0.0f;
+  int64_t q = q0 + threadIdx.x;
+  for (; q + 3 * kThreads < q1; q += 4 * kThreads) {
+    float a[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t qq = q + u * kThreads;
+      const int64_t off = contiguous ? qq * kVec : (qq / vecs_per_row) * ld + (qq % vecs_per_row) * kVec;
+      a[u] = vec_absmax<TIn>(x + off);
+    }
+    m = fmaxf(m, fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3])));
+  }
+  for (; q < q1; q += kThreads) {
+    const int64_t off = contiguous ? q * kVec : (q / vecs_per_row) * ld + (q % vecs_per_row) * kVec;
+    m = fmaxf(m, vec_absmax<TIn>(x + off));
+  }
+  m = block_max(m, red);
+  if (threadIdx.x == 0) partial[blockIdx.x] = m;
+}
+
+// amax per row segment: each wave owns a contiguous row range and flushes one atomic max
+// per segment run it crosses (the slots start at zero).
+template <typename TIn>
+__global__ __launch_bounds__(kThreads) void k_amax_seg(const TIn* __restrict__ x, int64_t rows,
+                                                       int64_t vecs_per_row, int64_t ld,
+                                                       const int64_t* __restrict__ seg, int64_t nseg,
+                                                       float* __restrict__ amax_out) {
+  constexpr int64_t kVec = 16 / sizeof(TIn);
   const int lane = threadIdx.x & 63;
   const int64_t wave = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
   const int64_t nwaves = (int64_t)gridDim.x * kWavesPerBlock;
-  const int64_t groups = cols >> 4;
-  // contiguous row range per wave keeps segment runs long
   const int64_t per = (rows + nwaves - 1) / nwaves;
   const int64_t r0 = wave * per;
   const int64_t r1 = r0 + per < rows ? r0 + per : rows;
   float m = 0.0f;
   int64_t cur = -1;
   for (int64_t r = r0; r < r1; ++r) {
-    if constexpr (SEG) {
-      const int64_t s = find_segment(seg, nseg, r);
-      if (s != cur) {
-        if (cur >= 0) {
-          const float wm = wave_max(m);
-          if (lane == 0) atomic_max_nonneg(amax_out + cur, wm);
-        }
-        cur = s;
-        m = 0.0f;
+    const int64_t s = find_segment(seg, nseg, r);
+    if (s != cur) {
+      if (cur >= 0) {
+        const float wm = wave_max(m);
+        if (lane == 0) atomic_max_nonneg(amax_out + cur, wm);
       }
+      cur = s;
+      m = 0.0f;
     }
     const TIn* xr = x + r * ld;
-    int64_t gidx = lane;
-    for (; gidx + 64 < groups; gidx += 128) {
-      float v[16], u[16];
-      load16<TIn>(xr + gidx * 16, v);
-      load16<TIn>(xr + (gidx + 64) * 16, u);
-      m = fmaxf(m, fmaxf(abs_max16(v), abs_max16(u)));
+    int64_t v = lane;
+    for (; v + 192 < vecs_per_row; v += 256) {
+      const float a0 = vec_absmax<TIn>(xr + v * kVec), a1 = vec_absmax<TIn>(xr + (v + 64) * kVec);
+      const float a2 = vec_absmax<TIn>(xr + (v + 128) * kVec), a3 = vec_absmax<TIn>(xr + (v + 192) * kVec);
+      m = fmaxf(m, fmaxf(fmaxf(a0, a1), fmaxf(a2, a3)));
     }
-    if (gidx < groups) {
-      float v[16];
-      load16<TIn>(xr + gidx * 16, v);
-      m = fmaxf(m, abs_max16(v));
-    }
+    for (; v < vecs_per_row; v += 64) m = fmaxf(m, vec_absmax<TIn>(xr + v * kVec));
   }
-  const float wm = wave_max(m);
-  if (lane == 0 && r0 < r1) atomic_max_nonneg(amax_out + (SEG ? (cur < 0 ? 0 : cur) : 0), wm);
+  if (cur >= 0) {
+    const float wm = wave_max(m);
+    if (lane == 0) atomic_max_nonneg(amax_out + cur, wm);
+  }
 }
 
-__global__ void k_fill_zero(float* __restrict__ p, int64_t n) {
+__global__ void k_fill(float* __restrict__ p, int64_t n, float v) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
        i += (int64_t)gridDim.x * blockDim.x)
-    p[i] = 0.0f;
+    p[i] = v;
+}
+
+__global__ __launch_bounds__(kThreads) void k_reduce_partials(const float* __restrict__ partial,
+                                                              int parts, float* __restrict__ out) {
+  __shared__ float red[kWavesPerBlock];
+  float m = 0.0f;
+  for (int i = threadIdx.x; i < parts; i += kThreads) m = fmaxf(m, partial[i]);
+  m = block_max(m, red);
+  if (threadIdx.x == 0) out[0] = m;
+}
+
+// Tensor amax seen by an encode workgroup: either amax[seg] directly (parts == 1) or the
+// max of `parts` partial maxima of an unsegmented tensor.
+__device__ __forceinline__ float fold_amax(const float* __restrict__ amax, int parts, float* red) {
+  if (parts <= 1) return amax[0];
+  float m = 0.0f;
+  for (int i = threadIdx.x; i < parts; i += kThreads) m = fmaxf(m, amax[i]);
+  return block_max(m, red);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -116,17 +194,23 @@ __global__ void k_fill_zero(float* __restrict__ p, int64_t n) {
 template <typename TIn, bool SR, bool SEG>
 __global__ __launch_bounds__(kThreads) void k_encode_1x16(
     const TIn* __restrict__ x, int64_t rows, int64_t cols, int64_t ld,
-    const float* __restrict__ amax, const int64_t* __restrict__ seg, int64_t nseg,
+    const float* __restrict__ amax, int amax_parts, const int64_t* __restrict__ seg, int64_t nseg,
     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ gscale,
     uint64_t seed, uint64_t offset) {
+  __shared__ float red[kWavesPerBlock];
   const int lane = threadIdx.x & 63;
   const int64_t wave = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
   const int64_t nwaves = (int64_t)gridDim.x * kWavesPerBlock;
   const int64_t nb = cols >> 4;
-  if (blockIdx.x == 0)
-    for (int64_t i = threadIdx.x; i < nseg; i += kThreads) gscale[i] = tensor_decode_scale(amax[i]);
-
-  float s_enc = tensor_encode_scale(amax[0]);
+  const float a0 = fold_amax(amax, SEG ? 1 : amax_parts, red);
+  if (blockIdx.x == 0) {
+    if constexpr (SEG) {
+      for (int64_t i = threadIdx.x; i < nseg; i += kThreads) gscale[i] = tensor_decode_scale(amax[i]);
+    } else if (threadIdx.x == 0) {
+      gscale[0] = tensor_decode_scale(a0);
+    }
+  }
+  float s_enc = tensor_encode_scale(a0);
   int64_t cur = 0;
   for (int64_t it = wave; it < rows; it += nwaves) {
     const int64_t r = rows - 1 - it;                 // reverse of the amax pass
@@ -155,108 +239,135 @@ __global__ __launch_bounds__(kThreads) void k_encode_1x16(
 }
 
 // ---------------------------------------------------------------------------------------
-// 16x16 encode: a lane pair owns one 16x16 tile (each lane 16 rows x 8 columns); a wave
-// covers 32 tiles (512 columns) of one 16-row strip. The tile amax is combined across the
-// pair with one cross-lane max.
+// 16x16 encode. A workgroup owns a 256-row x 128-column tile: 16 strips of 16 rows x 8 tiles
+// of 16 columns. Lane pairs own one 16x16 tile (each lane 16 rows x 8 columns; the tile amax
+// is combined across the pair with one cross-lane max). Codes of x are written row by row
+// (4 bytes per lane); the transposed copy (x^T: row c holds column c) is assembled in LDS
+// and written as 128-byte row segments (256 rows of x = 128 bytes of x^T codes).
+constexpr int kTileRows = 256, kTileCols = 128;
+
 template <typename TIn>
-__device__ __forceinline__ void load8(const TIn* p, float (&v)[8]);
+struct Raw8;                                   // 8 consecutive inputs of one row
 
 template <>
-__device__ __forceinline__ void load8<uint16_t>(const uint16_t* p, float (&v)[8]) {
-  const v4u32 a = ld_u32x4(p);
-  const uint32_t w[4] = {a.x, a.y, a.z, a.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    v[2 * i] = bf16_lo(w[i]);
-    v[2 * i + 1] = bf16_hi(w[i]);
+struct Raw8<uint16_t> {
+  v4u32 w;
+  __device__ __forceinline__ void load(const uint16_t* p) { w = ld_u32x4(p); }
+  __device__ __forceinline__ float get(int i) const {
+    const uint32_t word = (i >> 1) == 0 ? w.x : (i >> 1) == 1 ? w.y : (i >> 1) == 2 ? w.z : w.w;
+    return (i & 1) ? bf16_hi(word) : bf16_lo(word);
   }
-}
+};
 
 template <>
-__device__ __forceinline__ void load8<float>(const float* p, float (&v)[8]) {
-  const v4f32 a = ld_f32x4(p);
-  const v4f32 b = ld_f32x4(p + 4);
-  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-}
+struct Raw8<float> {
+  v4f32 a, b;
+  __device__ __forceinline__ void load(const float* p) { a = ld_f32x4(p); b = ld_f32x4(p + 4); }
+  __device__ __forceinline__ float get(int i) const {
+    const v4f32& v = i < 4 ? a : b;
+    const int k = i & 3;
+    return k == 0 ? v.x : k == 1 ? v.y : k == 2 ? v.z : v.w;
+  }
+};
 
 template <typename TIn, bool SEG, bool TRANS>
 __global__ __launch_bounds__(kThreads) void k_encode_16x16(
     const TIn* __restrict__ x, int64_t rows, int64_t cols, int64_t ld,
-    const float* __restrict__ amax, const int64_t* __restrict__ seg, int64_t nseg,
+    const float* __restrict__ amax, int amax_parts, const int64_t* __restrict__ seg, int64_t nseg,
     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ gscale,
     uint8_t* __restrict__ tcodes, uint8_t* __restrict__ tscales, float* __restrict__ tgscale) {
-  const int lane = threadIdx.x & 63;
-  const int64_t wave = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
-  const int64_t nwaves = (int64_t)gridDim.x * kWavesPerBlock;
-  const int64_t strips = rows >> 4;
-  const int64_t half_tiles = cols >> 3;                 // 8-column pieces per row
-  const int64_t chunks = (half_tiles + 63) >> 6;
-  const int64_t tasks = strips * chunks;
-  const int64_t nb = cols >> 4;
+  __shared__ float red[kWavesPerBlock];
+  __shared__ __attribute__((aligned(16))) uint8_t tc[TRANS ? kTileCols : 1][kTileRows / 2];
+  __shared__ uint8_t ts[TRANS ? kTileCols : 1][kTileRows / 16];
+
+  const int64_t tiles_c = (cols + kTileCols - 1) / kTileCols;
+  const int64_t tiles_r = (rows + kTileRows - 1) / kTileRows;
+  // reverse order of the amax pass
+  const int64_t t = tiles_r * tiles_c - 1 - (int64_t)blockIdx.x;
+  const int64_t tile_r = t / tiles_c, tile_c = t - tile_r * tiles_c;
+  const int64_t R0 = tile_r * kTileRows, C0 = tile_c * kTileCols;
+
+  const float a0 = fold_amax(amax, SEG ? 1 : amax_parts, red);
   if (blockIdx.x == 0) {
-    for (int64_t i = threadIdx.x; i < nseg; i += kThreads) {
-      const float d = tensor_decode_scale(amax[i]);
-      gscale[i] = d;
-      if constexpr (TRANS) tgscale[i] = d;
+    if constexpr (SEG) {
+      for (int64_t i = threadIdx.x; i < nseg; i += kThreads) gscale[i] = tensor_decode_scale(amax[i]);
+    } else if (threadIdx.x == 0) {
+      gscale[0] = tensor_decode_scale(a0);
+      if constexpr (TRANS) tgscale[0] = gscale[0];
     }
   }
-  float s_enc = tensor_encode_scale(amax[0]);
-  int64_t cur = 0;
-  for (int64_t it = wave; it < tasks; it += nwaves) {
-    const int64_t task = tasks - 1 - it;
-    const int64_t strip = task / chunks;
-    const int64_t ht = (task - strip * chunks) * 64 + lane;   // this lane's 8-column piece
-    const int64_t r0 = strip << 4;
-    if constexpr (SEG) {
-      const int64_t s = find_segment(seg, nseg, r0);
-      if (s != cur) {
-        cur = s;
-        s_enc = tensor_encode_scale(amax[s]);
-      }
-    }
-    const bool active = ht < half_tiles;
-    const int64_t c0 = (active ? ht : 0) << 3;
-    float v[16][8];
-    float m = 0.0f;
+
+  const int lane = threadIdx.x & 63;
+  const int strip = (threadIdx.x >> 6) * 4 + (lane >> 4);   // 0..15
+  const int ht = lane & 15;                                 // 8-column piece within the tile
+  const int64_t r0 = R0 + strip * 16;
+  const int64_t c0 = C0 + ht * 8;
+  const bool active = r0 < rows && c0 < cols;
+  const int64_t nb = cols >> 4;
+
+  float s_enc;
+  if constexpr (SEG) {
+    s_enc = tensor_encode_scale(amax[find_segment(seg, nseg, active ? r0 : 0)]);
+  } else {
+    s_enc = tensor_encode_scale(a0);
+  }
+
+  Raw8<TIn> v[16];
+  float m = 0.0f;
+  const TIn* xp = x + (active ? r0 : 0) * ld + (active ? c0 : 0);
+#pragma unroll
+  for (int j = 0; j < 16; ++j) v[j].load(xp + j * ld);
+#pragma unroll
+  for (int j = 0; j < 16; ++j)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[j].get(i)));
+  m = fmaxf(m, __shfl_xor(m, 1, 64));                       // partner lane: other 8 columns
+  const BlockScale bs = block_scale(m, s_enc);
+
+  uint32_t w[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    uint32_t c = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) c |= e2m1_rn(v[j].get(i) * bs.mult) << (4 * i);
+    w[j] = c;
+  }
+  if (active) {
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      load8<TIn>(x + (r0 + j) * ld + c0, v[j]);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[j][i]));
+      *reinterpret_cast<uint32_t*>(codes + (r0 + j) * (cols >> 1) + (c0 >> 1)) = w[j];
+      if ((ht & 1) == 0) scales[(r0 + j) * nb + (c0 >> 4)] = (uint8_t)bs.code;
     }
-    m = fmaxf(m, __shfl_xor(m, 1, 64));                 // partner lane holds the other half
-    const BlockScale bs = block_scale(m, s_enc);
-    uint32_t w[16];
+  }
+  if constexpr (TRANS) {
+    // column i of this lane's piece -> row (ht*8 + i) of the transposed tile, 16 codes
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      uint32_t c = 0;
+    for (int i = 0; i < 8; ++i) {
+      uint32_t lo = 0, hi = 0;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) c |= e2m1_rn(v[j][i] * bs.mult) << (4 * i);
-      w[j] = c;
+      for (int j = 0; j < 8; ++j) {
+        lo |= ((w[j] >> (4 * i)) & 0xFu) << (4 * j);
+        hi |= ((w[j + 8] >> (4 * i)) & 0xFu) << (4 * j);
+      }
+      *reinterpret_cast<uint2*>(&tc[ht * 8 + i][strip * 8]) = make_uint2(lo, hi);
+      ts[ht * 8 + i][strip] = (uint8_t)bs.code;
     }
-    if (active) {
+    __syncthreads();
+    // write-out: x^T row C0 + cr, bytes [R0/2, R0/2 + 128), in 8-byte pieces (one strip each)
+    const int64_t valid_strips = (rows - R0) / 16 < 16 ? (rows - R0) / 16 : 16;
+    const int64_t valid_cols = cols - C0 < kTileCols ? cols - C0 : kTileCols;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        *reinterpret_cast<uint32_t*>(codes + (r0 + j) * (cols >> 1) + (c0 >> 1)) = w[j];
-        if ((ht & 1) == 0) scales[(r0 + j) * nb + (c0 >> 4)] = (uint8_t)bs.code;
-      }
-      if constexpr (TRANS) {
-        // x^T row (c0 + i) gets the 16 codes of column i, rows r0..r0+15 along its row.
-        const int64_t tnb = rows >> 4;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          uint32_t lo = 0, hi = 0;
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            lo |= ((w[j] >> (4 * i)) & 0xFu) << (4 * j);
-            hi |= ((w[j + 8] >> (4 * i)) & 0xFu) << (4 * j);
-          }
-          const int64_t tr = c0 + i;
-          *reinterpret_cast<uint2*>(tcodes + tr * (rows >> 1) + (r0 >> 1)) = make_uint2(lo, hi);
-          tscales[tr * tnb + (r0 >> 4)] = (uint8_t)bs.code;
-        }
-      }
+    for (int pass = 0; pass < kTileCols * 16 / kThreads; ++pass) {
+      const int idx = pass * kThreads + threadIdx.x;
+      const int cr = idx >> 4, sp = idx & 15;
+      if (cr < valid_cols && sp < valid_strips)
+        *reinterpret_cast<uint2*>(tcodes + (C0 + cr) * (rows >> 1) + (R0 >> 1) + sp * 8) =
+            *reinterpret_cast<const uint2*>(&tc[cr][sp * 8]);
+    }
+    if (threadIdx.x < kTileCols && threadIdx.x < valid_cols) {
+      const int cr = threadIdx.x;
+      uint8_t* dst = tscales + (C0 + cr) * (rows >> 4) + (R0 >> 4);
+      for (int sp = 0; sp < valid_strips; ++sp) dst[sp] = ts[cr][sp];
     }
   }
 }
@@ -294,47 +405,55 @@ int grid_for(int64_t work_items, int64_t items_per_block, int64_t cap) {
 
 constexpr int64_t kMaxBlocks = 256 * 16;   // 16 workgroups per CU is plenty for streaming
 
+template <typename TIn>
+void amax_t(const void* x, int64_t rows, int64_t cols, int64_t ld, const int64_t* segments,
+            int64_t nseg, float* out, int* parts, hipStream_t stream) {
+  const int64_t vpr = cols * (int64_t)sizeof(TIn) / 16;
+  if (segments) {
+    hipLaunchKernelGGL(k_fill, dim3(1), dim3(256), 0, stream, out, nseg, 0.0f);
+    const int grid = grid_for(rows, kWavesPerBlock, 1024);
+    hipLaunchKernelGGL((k_amax_seg<TIn>), dim3(grid), dim3(kThreads), 0, stream, (const TIn*)x,
+                       rows, vpr, ld, segments, nseg, out);
+    *parts = 1;
+  } else {
+    const int grid = grid_for(rows * vpr, kThreads * 8, kMaxPartials);
+    hipLaunchKernelGGL((k_amax_partial<TIn>), dim3(grid), dim3(kThreads), 0, stream,
+                       (const TIn*)x, rows, vpr, ld, out);
+    *parts = grid;
+  }
+}
+
 }  // namespace
 
-hipError_t launch_amax(const void* x, bool fp32, int64_t rows, int64_t cols, int64_t ld,
-                       const int64_t* segments, int64_t nseg, float* amax_out,
-                       hipStream_t stream) {
-  hipLaunchKernelGGL(k_fill_zero, dim3(1), dim3(256), 0, stream, amax_out, nseg);
-  const int grid = grid_for(rows, kWavesPerBlock, kMaxBlocks);
-  if (fp32) {
-    if (segments)
-      hipLaunchKernelGGL((k_amax<float, true>), dim3(grid), dim3(kThreads), 0, stream,
-                         (const float*)x, rows, cols, ld, segments, nseg, amax_out);
-    else
-      hipLaunchKernelGGL((k_amax<float, false>), dim3(grid), dim3(kThreads), 0, stream,
-                         (const float*)x, rows, cols, ld, segments, nseg, amax_out);
-  } else {
-    if (segments)
-      hipLaunchKernelGGL((k_amax<uint16_t, true>), dim3(grid), dim3(kThreads), 0, stream,
-                         (const uint16_t*)x, rows, cols, ld, segments, nseg, amax_out);
-    else
-      hipLaunchKernelGGL((k_amax<uint16_t, false>), dim3(grid), dim3(kThreads), 0, stream,
-                         (const uint16_t*)x, rows, cols, ld, segments, nseg, amax_out);
-  }
+hipError_t launch_amax_parts(const void* x, bool fp32, int64_t rows, int64_t cols, int64_t ld,
+                             const int64_t* segments, int64_t nseg, float* ws, int* parts,
+                             hipStream_t stream) {
+  if (fp32) amax_t<float>(x, rows, cols, ld, segments, nseg, ws, parts, stream);
+  else amax_t<uint16_t>(x, rows, cols, ld, segments, nseg, ws, parts, stream);
+  return hipGetLastError();
+}
+
+hipError_t launch_reduce_partials(const float* partials, int parts, float* out, hipStream_t stream) {
+  hipLaunchKernelGGL(k_reduce_partials, dim3(1), dim3(kThreads), 0, stream, partials, parts, out);
   return hipGetLastError();
 }
 
 template <typename TIn, bool SR, bool SEG>
 static void encode_1x16_t(const void* x, int64_t rows, int64_t cols, int64_t ld, uint64_t seed,
                           uint64_t offset, const int64_t* segments, int64_t nseg,
-                          const float* amax, QuantOut out, hipStream_t stream) {
+                          const float* amax, int parts, QuantOut out, hipStream_t stream) {
   const int grid = grid_for(rows, kWavesPerBlock, kMaxBlocks);
   hipLaunchKernelGGL((k_encode_1x16<TIn, SR, SEG>), dim3(grid), dim3(kThreads), 0, stream,
-                     (const TIn*)x, rows, cols, ld, amax, segments, nseg, out.codes, out.scales,
-                     out.global_scale, seed, offset);
+                     (const TIn*)x, rows, cols, ld, amax, parts, segments, nseg, out.codes,
+                     out.scales, out.global_scale, seed, offset);
 }
 
 hipError_t launch_encode_1x16(const void* x, bool fp32, int64_t rows, int64_t cols, int64_t ld,
                               bool sr, uint64_t seed, uint64_t offset,
-                              const int64_t* segments, int64_t nseg, const float* amax,
+                              const int64_t* segments, int64_t nseg, const float* amax, int parts,
                               QuantOut out, hipStream_t stream) {
   const bool seg = segments != nullptr;
-#define NVFP4_E1(T, S, G) encode_1x16_t<T, S, G>(x, rows, cols, ld, seed, offset, segments, nseg, amax, out, stream)
+#define NVFP4_E1(T, S, G) encode_1x16_t<T, S, G>(x, rows, cols, ld, seed, offset, segments, nseg, amax, parts, out, stream)
   if (fp32) {
     if (sr) { if (seg) NVFP4_E1(float, true, true); else NVFP4_E1(float, true, false); }
     else    { if (seg) NVFP4_E1(float, false, true); else NVFP4_E1(float, false, false); }
@@ -348,22 +467,28 @@ hipError_t launch_encode_1x16(const void* x, bool fp32, int64_t rows, int64_t co
 
 template <typename TIn, bool SEG, bool TRANS>
 static void encode_16x16_t(const void* x, int64_t rows, int64_t cols, int64_t ld,
-                           const int64_t* segments, int64_t nseg, const float* amax,
+                           const int64_t* segments, int64_t nseg, const float* amax, int parts,
                            QuantOut out, const QuantOut* out_t, hipStream_t stream) {
-  const int64_t tasks = (rows >> 4) * (((cols >> 3) + 63) >> 6);
-  const int grid = grid_for(tasks, kWavesPerBlock, kMaxBlocks);
-  hipLaunchKernelGGL((k_encode_16x16<TIn, SEG, TRANS>), dim3(grid), dim3(kThreads), 0, stream,
-                     (const TIn*)x, rows, cols, ld, amax, segments, nseg, out.codes, out.scales,
-                     out.global_scale, TRANS ? out_t->codes : nullptr,
+  const int64_t tiles = ((rows + kTileRows - 1) / kTileRows) * ((cols + kTileCols - 1) / kTileCols);
+  if (tiles == 0) return;
+  hipLaunchKernelGGL((k_encode_16x16<TIn, SEG, TRANS>), dim3((unsigned)tiles), dim3(kThreads), 0,
+                     stream, (const TIn*)x, rows, cols, ld, amax, parts, segments, nseg,
+                     out.codes, out.scales, out.global_scale, TRANS ? out_t->codes : nullptr,
                      TRANS ? out_t->scales : nullptr, TRANS ? out_t->global_scale : nullptr);
 }
 
 hipError_t launch_encode_16x16(const void* x, bool fp32, int64_t rows, int64_t cols, int64_t ld,
-                               const int64_t* segments, int64_t nseg, const float* amax,
+                               const int64_t* segments, int64_t nseg, const float* amax, int parts,
                                QuantOut out, const QuantOut* out_t, hipStream_t stream) {
   const bool seg = segments != nullptr;
   const bool tr = out_t != nullptr;
-#define NVFP4_E2(T, G, R) encode_16x16_t<T, G, R>(x, rows, cols, ld, segments, nseg, amax, out, out_t, stream)
+  if (rows == 0) {
+    // nothing to encode; the tensor scales of an empty tensor are 1
+    hipLaunchKernelGGL(k_fill, dim3(1), dim3(256), 0, stream, out.global_scale, nseg, 1.0f);
+    if (tr) hipLaunchKernelGGL(k_fill, dim3(1), dim3(256), 0, stream, out_t->global_scale, nseg, 1.0f);
+    return hipGetLastError();
+  }
+#define NVFP4_E2(T, G, R) encode_16x16_t<T, G, R>(x, rows, cols, ld, segments, nseg, amax, parts, out, out_t, stream)
   if (fp32) {
     if (seg) { if (tr) NVFP4_E2(float, true, true); else NVFP4_E2(float, true, false); }
     else     { if (tr) NVFP4_E2(float, false, true); else NVFP4_E2(float, false, false); }

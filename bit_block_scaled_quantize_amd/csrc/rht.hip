@@ -6,13 +6,17 @@
 // GEMM. The rotation acts along the contraction (token) dimension in blocks of 16 tokens:
 // for column c and token block t, y = 1/4 * H16 * diag(s) * x[16t..16t+15, c], with
 // H16[i][j] = (-1)^popcount(i & j) and signs s from a 16-bit mask. The butterfly runs in
-// binary64 (stages h = 1, 2, 4, 8), so for BF16 inputs every step is exact, and the result is
-// rounded once to FP32. The 16 outputs of one (column, token block) are exactly one 1x16
+// binary64 (stages h = 1, 2, 4, 8) on inputs pre-multiplied by +-1/4 (exact in binary64, so
+// every intermediate is exactly 1/4 of the unscaled butterfly's), and the result is rounded
+// once to FP32. The 16 outputs of one (column, token block) are exactly one 1x16
 // quantization block of the transposed output [cols, tokens].
 //
-// Layout: a lane owns two adjacent columns and walks a run of token blocks, so each 16-token
-// load is one 4-byte (BF16 pair) or 8-byte (FP32 pair) vector per lane and a wave-wide load
-// covers 128 contiguous columns of one token row.
+// Layout: a workgroup owns 128 columns x 256 tokens (16 token blocks). Lane l of every wave
+// owns columns 2l and 2l+1, so a wave-wide load of one token row is 64 x 4 bytes (BF16) of
+// contiguous memory; wave w handles token blocks w, w+4, w+8, w+12 and loads all of its rows
+// up front. Codes and scales are staged in LDS as [column][token block] and written out as
+// 128-byte row segments of the transposed tensor. The amax variant grid-strides over the
+// same tiles and leaves one partial maximum per workgroup.
 #include "device_common.h"
 #include "launch.h"
 
@@ -20,49 +24,43 @@ namespace nvfp4 {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kColsPerLane = 2;
-constexpr int kColsPerBlock = kThreads * kColsPerLane;
-constexpr int kTokenBlocksPerTask = 8;
+constexpr int kWaves = kThreads / 64;
+constexpr int kTileCols = 128;                  // 64 lanes x 2 columns
+constexpr int kTileBlocks = 16;                 // 256 tokens
+constexpr int kBlocksPerWave = kTileBlocks / kWaves;
+constexpr int kMaxPartials = 1024;
 
-// Columns c and c+1 of one token row. `both` says whether c+1 exists; `paired` whether the
-// pair is aligned for one vector load (even row stride), else two scalar loads are used.
+// Columns c and c+1 of one token row, kept packed until use. `both` says whether c+1
+// exists; `paired` whether the pair is aligned for one vector load (even row stride), else
+// two scalar loads are used.
 template <typename TIn>
-__device__ __forceinline__ void load_pair(const TIn* p, bool both, bool paired, float& a, float& b);
+struct Pair;
 
 template <>
-__device__ __forceinline__ void load_pair<uint16_t>(const uint16_t* p, bool both, bool paired,
-                                                    float& a, float& b) {
-  if (both && paired) {
-    const uint32_t w = *reinterpret_cast<const uint32_t*>(p);
-    a = bf16_lo(w);
-    b = bf16_hi(w);
-  } else {
-    a = __uint_as_float((uint32_t)p[0] << 16);
-    b = both ? __uint_as_float((uint32_t)p[1] << 16) : 0.0f;
+struct Pair<uint16_t> {
+  uint32_t w;
+  __device__ __forceinline__ void load(const uint16_t* p, bool both, bool paired) {
+    if (both && paired) w = *reinterpret_cast<const uint32_t*>(p);
+    else w = (uint32_t)p[0] | (both ? (uint32_t)p[1] << 16 : 0u);
   }
-}
+  __device__ __forceinline__ float get(int q) const { return q == 0 ? bf16_lo(w) : bf16_hi(w); }
+};
 
 template <>
-__device__ __forceinline__ void load_pair<float>(const float* p, bool both, bool paired, float& a,
-                                                 float& b) {
-  if (both && paired) {
-    const v2f32 w = *reinterpret_cast<const v2f32*>(p);
-    a = w.x;
-    b = w.y;
-  } else {
-    a = p[0];
-    b = both ? p[1] : 0.0f;
+struct Pair<float> {
+  v2f32 w;
+  __device__ __forceinline__ void load(const float* p, bool both, bool paired) {
+    if (both && paired) w = *reinterpret_cast<const v2f32*>(p);
+    else w = v2f32{p[0], both ? p[1] : 0.0f};
   }
-}
+  __device__ __forceinline__ float get(int q) const { return q == 0 ? w.x : w.y; }
+};
 
-// y[i] = rn32(0.25 * sum_j H[i][j] * s_j * v[j]) via the binary64 butterfly.
+// y[i] = rn32(1/4 * sum_j H[i][j] * s_j * v[j]) via the binary64 butterfly.
 __device__ __forceinline__ void rht16(const float (&v)[16], uint32_t mask, float (&y)[16]) {
   double u[16];
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const double d = (double)v[j];
-    u[j] = ((mask >> j) & 1u) ? -d : d;
-  }
+  for (int j = 0; j < 16; ++j) u[j] = (double)v[j] * (((mask >> j) & 1u) ? -0.25 : 0.25);
 #pragma unroll
   for (int h = 1; h < 16; h <<= 1) {
 #pragma unroll
@@ -75,100 +73,169 @@ __device__ __forceinline__ void rht16(const float (&v)[16], uint32_t mask, float
     }
   }
 #pragma unroll
-  for (int i = 0; i < 16; ++i) y[i] = (float)(u[i] * 0.25);
+  for (int i = 0; i < 16; ++i) y[i] = (float)u[i];
+}
+
+__device__ __forceinline__ float block_max(float m, float* red) {
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  float r = red[0];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) r = fmaxf(r, red[w]);
+  __syncthreads();
+  return r;
 }
 
 template <typename TIn, bool ENCODE, bool SR>
 __global__ __launch_bounds__(kThreads) void k_rht(
     const TIn* __restrict__ x, int64_t tokens, int64_t cols, int64_t ld, uint32_t mask,
-    const float* __restrict__ amax, float* __restrict__ amax_out, uint8_t* __restrict__ codes,
-    uint8_t* __restrict__ scales, float* __restrict__ gscale, uint64_t seed, uint64_t offset) {
-  const int64_t c = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * kColsPerLane;
-  const int64_t nbt = tokens >> 4;                          // token blocks = output blocks per row
-  const int64_t tb0 = (int64_t)blockIdx.y * kTokenBlocksPerTask;
-  const int64_t tb1 = tb0 + kTokenBlocksPerTask < nbt ? tb0 + kTokenBlocksPerTask : nbt;
-  const bool valid0 = c < cols;
-  const bool valid1 = c + 1 < cols;
-  const int64_t cl = valid0 ? c : 0;                         // clamped column for loads
+    const float* __restrict__ amax, int amax_parts, float* __restrict__ partial,
+    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ gscale,
+    uint64_t seed, uint64_t offset) {
+  __shared__ float red[kWaves];
+  __shared__ __attribute__((aligned(16))) uint8_t tc[ENCODE ? kTileCols : 1][kTileBlocks * 8];
+  __shared__ __attribute__((aligned(16))) uint8_t ts[ENCODE ? kTileCols : 1][kTileBlocks];
+  constexpr int kNB = sizeof(TIn) == 2 ? kBlocksPerWave : 2;   // token blocks loaded at once
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t nbt = tokens >> 4;
+  const int64_t tiles_c = (cols + kTileCols - 1) / kTileCols;
+  const int64_t tiles = tiles_c * ((nbt + kTileBlocks - 1) / kTileBlocks);
   const bool paired = (ld & 1) == 0;
 
   float s_enc = 1.0f;
   if constexpr (ENCODE) {
-    s_enc = tensor_encode_scale(amax[0]);
-    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) gscale[0] = tensor_decode_scale(amax[0]);
+    float a = 0.0f;
+    if (amax_parts <= 1) {
+      a = amax[0];
+    } else {
+      for (int i = threadIdx.x; i < amax_parts; i += kThreads) a = fmaxf(a, amax[i]);
+      a = block_max(a, red);
+    }
+    s_enc = tensor_encode_scale(a);
+    if (blockIdx.x == 0 && threadIdx.x == 0) gscale[0] = tensor_decode_scale(a);
   }
+
   float m = 0.0f;
-  for (int64_t tb = tb0; tb < tb1; ++tb) {
-    float v0[16], v1[16];
+  for (int64_t it = blockIdx.x; it < tiles; it += gridDim.x) {
+    const int64_t tile = ENCODE ? tiles - 1 - it : it;     // encode walks back over the amax order
+    const int64_t tt = tile / tiles_c;
+    const int64_t C0 = (tile - tt * tiles_c) * kTileCols, TB0 = tt * kTileBlocks;
+    const int64_t c = C0 + 2 * lane;
+    const bool valid0 = c < cols, valid1 = c + 1 < cols;
+    const int64_t cl = valid0 ? c : 0;                      // clamped column for loads
+
 #pragma unroll
-    for (int j = 0; j < 16; ++j)
-      load_pair<TIn>(x + (tb * 16 + j) * ld + cl, valid1, paired, v0[j], v1[j]);
+    for (int k0 = 0; k0 < kBlocksPerWave; k0 += kNB) {
+      Pair<TIn> raw[kNB][16];
 #pragma unroll
-    for (int k = 0; k < kColsPerLane; ++k) {
-      const bool valid = k == 0 ? valid0 : valid1;
-      float y[16];
-      rht16(k == 0 ? v0 : v1, mask, y);
-      float bm = 0.0f;
+      for (int k = 0; k < kNB; ++k) {
+        const int64_t tb = TB0 + wave + 4 * (k0 + k);
+        const int64_t tbl = tb < nbt ? tb : 0;              // clamped token block for loads
 #pragma unroll
-      for (int i = 0; i < 16; ++i) bm = fmaxf(bm, fabsf(y[i]));
-      if constexpr (!ENCODE) {
-        if (valid) m = fmaxf(m, bm);
-      } else {
-        if (valid) {
-          const int64_t row = c + k;                          // output row = input column
-          const BlockScale bs = block_scale(bm, s_enc);
-          u32x4 rnd{0, 0, 0, 0};
-          if constexpr (SR) rnd = block_random((uint64_t)(row * nbt + tb), seed, offset);
-          uint32_t lo, hi;
-          encode16<SR>(y, bs.mult, rnd, lo, hi);
-          *reinterpret_cast<uint2*>(codes + row * (tokens >> 1) + tb * 8) = make_uint2(lo, hi);
-          scales[row * nbt + tb] = (uint8_t)bs.code;
+        for (int j = 0; j < 16; ++j) raw[k][j].load(x + (tbl * 16 + j) * ld + cl, valid1, paired);
+      }
+#pragma unroll
+      for (int k = 0; k < kNB; ++k) {
+        const int bl = wave + 4 * (k0 + k);                 // token block within the tile
+        const int64_t tb = TB0 + bl;
+        if (tb >= nbt) continue;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const bool valid = q == 0 ? valid0 : valid1;
+          float v[16], y[16];
+#pragma unroll
+          for (int j = 0; j < 16; ++j) v[j] = raw[k][j].get(q);
+          rht16(v, mask, y);
+          float bm = 0.0f;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) bm = fmaxf(bm, fabsf(y[i]));
+          if constexpr (!ENCODE) {
+            if (valid) m = fmaxf(m, bm);
+          } else {
+            const int64_t row = c + q;                      // output row = input column
+            const BlockScale bs = block_scale(bm, s_enc);
+            u32x4 rnd{0, 0, 0, 0};
+            if constexpr (SR) rnd = block_random((uint64_t)(row * nbt + tb), seed, offset);
+            uint32_t lo, hi;
+            encode16<SR>(y, bs.mult, rnd, lo, hi);
+            *reinterpret_cast<uint2*>(&tc[2 * lane + q][bl * 8]) = make_uint2(lo, hi);
+            ts[2 * lane + q][bl] = (uint8_t)bs.code;
+          }
         }
       }
     }
+
+    if constexpr (ENCODE) {
+      __syncthreads();
+      const int64_t valid_cols = cols - C0 < kTileCols ? cols - C0 : kTileCols;
+      const int64_t valid_tb = nbt - TB0 < kTileBlocks ? nbt - TB0 : kTileBlocks;
+#pragma unroll
+      for (int pass = 0; pass < kTileCols * kTileBlocks / kThreads; ++pass) {
+        const int idx = pass * kThreads + threadIdx.x;
+        const int cr = idx >> 4, p = idx & 15;
+        if (cr < valid_cols && p < valid_tb)
+          *reinterpret_cast<uint2*>(codes + (C0 + cr) * (tokens >> 1) + (TB0 + p) * 8) =
+              *reinterpret_cast<const uint2*>(&tc[cr][p * 8]);
+      }
+      if (threadIdx.x < valid_cols) {
+        const int cr = threadIdx.x;
+        uint8_t* dst = scales + (C0 + cr) * nbt + TB0;
+        if (valid_tb == kTileBlocks && ((reinterpret_cast<uintptr_t>(dst) & 15) == 0)) {
+          *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(&ts[cr][0]);
+        } else {
+          for (int p = 0; p < valid_tb; ++p) dst[p] = ts[cr][p];
+        }
+      }
+      __syncthreads();                                      // LDS reused by the next tile
+    }
   }
   if constexpr (!ENCODE) {
-    const float wm = wave_max(m);
-    if ((threadIdx.x & 63) == 0) atomic_max_nonneg(amax_out, wm);
+    m = block_max(m, red);
+    if (threadIdx.x == 0) partial[blockIdx.x] = m;
   }
 }
 
-__global__ void k_zero1(float* p) { *p = 0.0f; }
+int64_t rht_tiles(int64_t tokens, int64_t cols) {
+  return ((cols + kTileCols - 1) / kTileCols) * (((tokens >> 4) + kTileBlocks - 1) / kTileBlocks);
+}
 
 template <typename TIn, bool ENCODE, bool SR>
 void launch_rht_t(const void* x, int64_t tokens, int64_t cols, int64_t ld, uint16_t mask,
-                  const float* amax, float* amax_out, QuantOut out, uint64_t seed,
-                  uint64_t offset, hipStream_t stream) {
-  if (tokens == 0 || cols == 0) return;
-  const dim3 grid((unsigned)((cols + kColsPerBlock - 1) / kColsPerBlock),
-                  (unsigned)(((tokens >> 4) + kTokenBlocksPerTask - 1) / kTokenBlocksPerTask));
-  hipLaunchKernelGGL((k_rht<TIn, ENCODE, SR>), grid, dim3(kThreads), 0, stream, (const TIn*)x,
-                     tokens, cols, ld, (uint32_t)mask, amax, amax_out, out.codes, out.scales,
-                     out.global_scale, seed, offset);
+                  const float* amax, int parts, float* partial, QuantOut out, uint64_t seed,
+                  uint64_t offset, int grid, hipStream_t stream) {
+  hipLaunchKernelGGL((k_rht<TIn, ENCODE, SR>), dim3(grid), dim3(kThreads), 0, stream,
+                     (const TIn*)x, tokens, cols, ld, (uint32_t)mask, amax, parts, partial,
+                     out.codes, out.scales, out.global_scale, seed, offset);
 }
 
 }  // namespace
 
-hipError_t launch_rht_amax(const void* x, bool fp32, int64_t tokens, int64_t cols, int64_t ld,
-                           uint16_t sign_mask, float* amax_out, hipStream_t stream) {
-  hipLaunchKernelGGL(k_zero1, dim3(1), dim3(1), 0, stream, amax_out);
+hipError_t launch_rht_amax_parts(const void* x, bool fp32, int64_t tokens, int64_t cols, int64_t ld,
+                                 uint16_t sign_mask, float* partial, int* parts, hipStream_t stream) {
+  const int64_t tiles = rht_tiles(tokens, cols);
+  const int grid = (int)(tiles < 1 ? 1 : (tiles < kMaxPartials ? tiles : kMaxPartials));
   const QuantOut none{nullptr, nullptr, nullptr};
   if (fp32)
-    launch_rht_t<float, false, false>(x, tokens, cols, ld, sign_mask, nullptr, amax_out, none, 0, 0, stream);
+    launch_rht_t<float, false, false>(x, tokens, cols, ld, sign_mask, nullptr, 0, partial, none, 0, 0, grid, stream);
   else
-    launch_rht_t<uint16_t, false, false>(x, tokens, cols, ld, sign_mask, nullptr, amax_out, none, 0, 0, stream);
+    launch_rht_t<uint16_t, false, false>(x, tokens, cols, ld, sign_mask, nullptr, 0, partial, none, 0, 0, grid, stream);
+  *parts = grid;
   return hipGetLastError();
 }
 
 hipError_t launch_rht_encode(const void* x, bool fp32, int64_t tokens, int64_t cols, int64_t ld,
                              uint16_t sign_mask, bool sr, uint64_t seed, uint64_t offset,
-                             const float* amax, QuantOut out, hipStream_t stream) {
+                             const float* amax, int parts, QuantOut out, hipStream_t stream) {
+  const int64_t tiles = rht_tiles(tokens, cols);
+  const int grid = (int)(tiles < 1 ? 1 : tiles);
   if (fp32) {
-    if (sr) launch_rht_t<float, true, true>(x, tokens, cols, ld, sign_mask, amax, nullptr, out, seed, offset, stream);
-    else    launch_rht_t<float, true, false>(x, tokens, cols, ld, sign_mask, amax, nullptr, out, seed, offset, stream);
+    if (sr) launch_rht_t<float, true, true>(x, tokens, cols, ld, sign_mask, amax, parts, nullptr, out, seed, offset, grid, stream);
+    else    launch_rht_t<float, true, false>(x, tokens, cols, ld, sign_mask, amax, parts, nullptr, out, seed, offset, grid, stream);
   } else {
-    if (sr) launch_rht_t<uint16_t, true, true>(x, tokens, cols, ld, sign_mask, amax, nullptr, out, seed, offset, stream);
-    else    launch_rht_t<uint16_t, true, false>(x, tokens, cols, ld, sign_mask, amax, nullptr, out, seed, offset, stream);
+    if (sr) launch_rht_t<uint16_t, true, true>(x, tokens, cols, ld, sign_mask, amax, parts, nullptr, out, seed, offset, grid, stream);
+    else    launch_rht_t<uint16_t, true, false>(x, tokens, cols, ld, sign_mask, amax, parts, nullptr, out, seed, offset, grid, stream);
   }
   return hipGetLastError();
 }

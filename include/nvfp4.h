@@ -162,13 +162,18 @@ int nvfp4_grouped_gemm(int64_t G, const int64_t* m_offsets, const nvfp4_tensor* 
 
 /*
  * nvfp4_amax - max|x| of x[rows, cols] (row stride ld), per row segment, into device
- * amax_out[nseg]. With rht != 0 the maximum is taken over the Hadamard-transformed tensor
- * of nvfp4_rht_quantize (rows = tokens, nseg must be 1). Useful to precompute amax_in.
+ * amax_out[nseg]: the first level of the two-level scale ("Nemotron NVFP4" explainer, "What
+ * NVFP4 actually is": one FP32 scale per tensor). With rht != 0 the maximum is taken over the
+ * Hadamard-transformed tensor of nvfp4_rht_quantize (rows = tokens, nseg must be 1). Useful
+ * to precompute amax_in.
+ *   workspace  device scratch of nvfp4_workspace_size(rht ? NVFP4_OP_RHT_QUANTIZE :
+ *              NVFP4_OP_QUANTIZE, rows, cols, nseg) bytes, 256-byte aligned, for the partial
+ *              maxima of an unsegmented tensor; may be NULL with segments.
  * Errors: as nvfp4_quantize.
  */
 int nvfp4_amax(const void* x, nvfp4_dtype dt, int64_t rows, int64_t cols, int64_t ld,
                const int64_t* segments, int64_t nseg, int rht, uint16_t sign_mask,
-               float* amax_out, void* hip_stream);
+               float* amax_out, void* workspace, size_t ws_bytes, void* hip_stream);
 
 /* Bytes of device workspace `op` needs for the given shape (0 if none). */
 size_t nvfp4_workspace_size(int op, int64_t rows, int64_t cols, int64_t nseg);

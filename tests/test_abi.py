@@ -43,7 +43,7 @@ def _tensor(rows, cols, codes=FAKE, scales=FAKE, gs=FAKE):
 
 def _q(lib, **kw):
     a = dict(x=FAKE, dt=0, rows=32, cols=64, ld=64, blk=0, rnd=0, seed=0, offset=0, seg=None,
-             nseg=1, amax=None, out=_tensor(32, 64), out_t=None, ws=FAKE, ws_n=4096, stream=None)
+             nseg=1, amax=None, out=_tensor(32, 64), out_t=None, ws=FAKE, ws_n=8192, stream=None)
     a.update(kw)
     out_t = ctypes.byref(a["out_t"]) if a["out_t"] is not None else None
     out = ctypes.byref(a["out"]) if a["out"] is not None else None
@@ -80,10 +80,10 @@ def test_quantize_validation(lib):
 def test_rht_validation(lib):
     out = _tensor(64, 32)
     f = lib.nvfp4_rht_quantize
-    assert f(FAKE, 0, 30, 64, 64, 0, 0, 0, 0, None, ctypes.byref(out), FAKE, 4096, None) == INVALID
-    assert f(FAKE, 0, 32, 64, 64, 0, 3, 0, 0, None, ctypes.byref(out), FAKE, 4096, None) == INVALID
+    assert f(FAKE, 0, 30, 64, 64, 0, 0, 0, 0, None, ctypes.byref(out), FAKE, 8192, None) == INVALID
+    assert f(FAKE, 0, 32, 64, 64, 0, 3, 0, 0, None, ctypes.byref(out), FAKE, 8192, None) == INVALID
     bad = _tensor(32, 64)                                                    # must be [cols, tokens]
-    assert f(FAKE, 0, 32, 64, 64, 0, 0, 0, 0, None, ctypes.byref(bad), FAKE, 4096, None) == INVALID
+    assert f(FAKE, 0, 32, 64, 64, 0, 0, 0, 0, None, ctypes.byref(bad), FAKE, 8192, None) == INVALID
     assert f(FAKE, 0, 32, 64, 64, 0, 0, 0, 0, None, ctypes.byref(out), None, 0, None) == WORKSPACE
 
 
@@ -102,9 +102,9 @@ def test_gemm_validation(lib):
 
 
 def test_workspace_sizes(lib):
-    assert lib.nvfp4_workspace_size(nv.OP_QUANTIZE, 10, 16, 1) == 256
-    assert lib.nvfp4_workspace_size(nv.OP_QUANTIZE, 10, 16, 100) == 512
-    assert lib.nvfp4_workspace_size(nv.OP_RHT_QUANTIZE, 16, 16, 1) == 256
+    assert lib.nvfp4_workspace_size(nv.OP_QUANTIZE, 10, 16, 1) == 4096      # 1024 partial maxima
+    assert lib.nvfp4_workspace_size(nv.OP_QUANTIZE, 10, 16, 2000) == 8192   # one slot per segment
+    assert lib.nvfp4_workspace_size(nv.OP_RHT_QUANTIZE, 16, 16, 1) == 4096
     assert lib.nvfp4_workspace_size(nv.OP_GEMM, 16, 16, 1) == 0
     assert lib.nvfp4_workspace_size(nv.OP_GROUPED_GEMM, 16, 16, 1) == 0
 
