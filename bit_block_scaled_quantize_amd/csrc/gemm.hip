@@ -133,7 +133,9 @@ constexpr int kFragsA = kBlockM / 32;                         // 8
 constexpr int kPanelFrags = kFragsA + kBlockN / 32;           // 16 fragments per K step
 constexpr int kCodeBytes = kPanelFrags * kFragBytes;          // 32 KB
 constexpr int kStageBytes = kCodeBytes + kPanelFrags * kFragScaleBytes;   // 36 KB
-constexpr int kLdsBytes = 2 * kStageBytes;                    // 72 KB, double-buffered
+constexpr int kStages = 3;                                    // DMA runs two K steps ahead
+constexpr int kLdsBytes = kStages * kStageBytes;              // 108 KB
+constexpr int kDmaPerWaveStep = 12;                           // 8 code + 4 scale DMAs
 }  // namespace big
 
 typedef float float16v __attribute__((ext_vector_type(16)));
@@ -201,50 +203,112 @@ __device__ __forceinline__ void gemm_tile_big(Operand A, Operand B, int64_t m0, 
 #pragma unroll
     for (int j = 0; j < kFragsN; ++j) acc[i][j] = float16v{};
 
+  // Pipeline. DMA runs up to 3 K steps ahead (3 LDS buffers). A lane's 64-code run of a step
+  // sits in two register halves: half 0 (octets 0-3) and half 1 (octets 4-7). Half 1 of step
+  // s is read from LDS when step s starts and lands while octets 0-3 compute; at octet 4 the
+  // wave meets the next step's barrier and refills half 0 (free by then) with step s+1, so
+  // no LDS latency sits between steps and the barrier wait overlaps in-flight MFMAs. Before
+  // that barrier each wave waits for its own DMA of step s+1 and for its LDS reads of step s,
+  // whose buffer the DMA of step s+3 refills right after it.
+  static_assert(kStages == 3 && kDmaPerWaveStep == 12, "waitcnt immediates below");
+  auto barrier = [] {
+    // plain s_barrier: a fence would also wait for the DMA still in flight; the empty asm
+    // statements keep the compiler from moving LDS accesses across it
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  v4u32 ar0[kFragsM], ar1[kFragsM], br0[kFragsN], br1[kFragsN];
+  uint32_t sa[kFragsM], sb[kFragsN];
+  auto read_half = [&](int b, int q, v4u32 (&ra)[kFragsM], v4u32 (&rb)[kFragsN]) {
+    const uint8_t* cur = lds + b * kStageBytes + q * 1024 + lane * 16;
+#pragma unroll
+    for (int j = 0; j < kFragsN; ++j)
+      rb[j] = *reinterpret_cast<const v4u32*>(cur + (kFragsA + wn * kFragsN + j) * kFragBytes);
+#pragma unroll
+    for (int i = 0; i < kFragsM; ++i)
+      ra[i] = *reinterpret_cast<const v4u32*>(cur + (wm * kFragsM + i) * kFragBytes);
+  };
+  auto read_scales = [&](int b, int64_t step) {
+    const uint8_t* cur = lds + b * kStageBytes + kCodeBytes + lane * 4;
+    const uint32_t keep = k_mask4(K, step * kStepK + h * 64);
+#pragma unroll
+    for (int j = 0; j < kFragsN; ++j)
+      sb[j] = *reinterpret_cast<const uint32_t*>(cur + (kFragsA + wn * kFragsN + j) * kFragScaleBytes) & keep;
+#pragma unroll
+    for (int i = 0; i < kFragsM; ++i)
+      sa[i] = *reinterpret_cast<const uint32_t*>(cur + (wm * kFragsM + i) * kFragScaleBytes) & keep;
+  };
+
   const int64_t steps = (K + kStepK - 1) / kStepK;
-  issue_dma(0, 0);
+#pragma unroll
+  for (int p = 0; p < kStages; ++p)
+    if (p < steps) issue_dma(p, p);
+  if (steps >= 3) __builtin_amdgcn_s_waitcnt(0x4F78);        // vmcnt(24)
+  else if (steps == 2) __builtin_amdgcn_s_waitcnt(0x0F7C);   // vmcnt(12)
+  else __builtin_amdgcn_s_waitcnt(0x0F70);                   // vmcnt(0)
+  barrier();
+  read_half(0, 0, ar0, br0);
+  read_scales(0, 0);
 
+  int b_cur = 0;
   for (int64_t s = 0; s < steps; ++s) {
-    const int buf = (int)(s & 1);
-    __builtin_amdgcn_s_waitcnt(0x0F70);                       // vmcnt(0): this step's DMA landed
-    __syncthreads();
+    const int b_next = b_cur == kStages - 1 ? 0 : b_cur + 1;
+    read_half(b_cur, 1, ar1, br1);
 
-    const uint8_t* cur = lds + buf * kStageBytes;
-    const uint32_t keep = k_mask4(K, s * kStepK + h * 64);
-    v4u32 araw[kFragsM][2], braw[kFragsN][2];
-    uint32_t sa[kFragsM], sb[kFragsN];
+    // FP16 scale pairs of the 4 blocks of every fragment: (b << 7) | (b << 23) = b * 0x00800080
+    half2v pa[kFragsM][4], pb[kFragsN][4];
 #pragma unroll
-    for (int j = 0; j < kFragsN; ++j) {
-      const int f = kFragsA + wn * kFragsN + j;
-      braw[j][0] = *reinterpret_cast<const v4u32*>(cur + f * kFragBytes + lane * 16);
-      braw[j][1] = *reinterpret_cast<const v4u32*>(cur + f * kFragBytes + 1024 + lane * 16);
-      sb[j] = *reinterpret_cast<const uint32_t*>(cur + kCodeBytes + f * kFragScaleBytes + lane * 4) & keep;
-    }
+    for (int q = 0; q < 4; ++q) {
 #pragma unroll
-    for (int i = 0; i < kFragsM; ++i) {
-      const int f = wm * kFragsM + i;
-      araw[i][0] = *reinterpret_cast<const v4u32*>(cur + f * kFragBytes + lane * 16);
-      araw[i][1] = *reinterpret_cast<const v4u32*>(cur + f * kFragBytes + 1024 + lane * 16);
-      sa[i] = *reinterpret_cast<const uint32_t*>(cur + kCodeBytes + f * kFragScaleBytes + lane * 4) & keep;
-    }
-
-    if (s + 1 < steps) issue_dma(s + 1, buf ^ 1);
-
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      half8 bv[kFragsN];
+      for (int i = 0; i < kFragsM; ++i)
+        pa[i][q] = __builtin_bit_cast(half2v, ((sa[i] >> (8 * q)) & 0xFFu) * 0x00800080u);
 #pragma unroll
       for (int j = 0; j < kFragsN; ++j)
-        bv[j] = decode8(word(braw[j][t >> 2], t & 3), scale_pair((sb[j] >> (8 * (t >> 1))) & 0xFFu));
+        pb[j][q] = __builtin_bit_cast(half2v, ((sb[j] >> (8 * q)) & 0xFFu) * 0x00800080u);
+    }
+
+    // 32 phases (t = K octet, i = A fragment), each 4 MFMAs. Decodes run one phase ahead:
+    // while phase (t, i) issues its MFMAs, the A fragment of the next phase and B fragment i
+    // of octet t+1 are decoded, so every MFMA finds its operands ready and the vector ALU
+    // works under the matrix core. sched_barrier keeps the compiler from regrouping phases.
+    auto araw = [&](int i, int t) { return word(t < 4 ? ar0[i] : ar1[i], t & 3); };
+    auto braw = [&](int j, int t) { return word(t < 4 ? br0[j] : br1[j], t & 3); };
+    half8 bv[kFragsN], bn[kFragsN], av;
+#pragma unroll
+    for (int j = 0; j < kFragsN; ++j) bv[j] = decode8(braw(j, 0), pb[j][0]);
+    av = decode8(araw(0, 0), pa[0][0]);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      if (t == 4 && s + 1 < steps) {
+        if (s + 2 < steps) __builtin_amdgcn_s_waitcnt(0x007C);   // vmcnt(12) lgkmcnt(0)
+        else __builtin_amdgcn_s_waitcnt(0x0070);               // vmcnt(0) lgkmcnt(0)
+        barrier();
+        read_half(b_next, 0, ar0, br0);
+        read_scales(b_next, s + 1);
+        if (s + 3 < steps) issue_dma(s + 3, b_cur);
+      }
 #pragma unroll
       for (int i = 0; i < kFragsM; ++i) {
-        const half8 av = decode8(word(araw[i][t >> 2], t & 3), scale_pair((sa[i] >> (8 * (t >> 1))) & 0xFFu));
+        const int tn = i + 1 < kFragsM ? t : t + 1;           // next phase
+        const int in_ = i + 1 < kFragsM ? i + 1 : 0;
+        half8 an = av;
+        if (tn < 8) {
+          an = decode8(araw(in_, tn), pa[in_][tn >> 1]);
+          if (t + 1 < 8) bn[i] = decode8(braw(i, t + 1), pb[i][(t + 1) >> 1]);
+        }
 #pragma unroll
         for (int j = 0; j < kFragsN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, bv[j], acc[i][j], 0, 0, 0);
+        av = an;
+        __builtin_amdgcn_sched_barrier(0);
       }
+#pragma unroll
+      for (int j = 0; j < kFragsN; ++j) bv[j] = bn[j];
     }
+    b_cur = b_next;
   }
+  __builtin_amdgcn_s_waitcnt(0x0F70);                         // no DMA may outlive the tile
 
   // D fragment layout (32 x 32): lane l holds column l % 32 and, for q = 0..15, row
   // 8*(q/4) + 4*(l/32) + q%4.
