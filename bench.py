@@ -28,6 +28,13 @@ MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense FP16/BF16 MFMA, TFLOP/s
 
 M, K_IN, N_OUT = 8192, 5120, 20480
 
+# HBM bytes per launch of the GEMM kernel on this workload (fprop/dgrad/wgrad average), from two
+# rocprofv3 counter runs of this script (FETCH_SIZE, then WRITE_SIZE), each scaled by what the same
+# counter reads for the 256 MiB copy kernel of --copy-kernel. The figure belongs to the GEMM source
+# whose SHA-256 is given; once that source changes it is reported as null until measured again.
+GEMM_SOURCE = os.path.join(ROOT, "bit_block_scaled_quantize_amd", "csrc", "gemm.hip")
+GEMM_TRAFFIC = {"source_sha256": None, "bytes_per_launch": None}
+
 
 def parse():
     p = argparse.ArgumentParser()
@@ -37,6 +44,9 @@ def parse():
     p.add_argument("--no-moe", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--kernel-reps", type=int, default=5, help="cold-cache repetitions per kernel")
+    p.add_argument("--copy-kernel", action="store_true",
+                   help="first run one plain 256 MiB fp32 copy kernel, the known-size reference "
+                        "that scales the HBM byte counters of a profiler run")
     return p.parse_args()
 
 
@@ -114,6 +124,13 @@ def main():
             fn()
             if events is not None:
                 events[i][1].record(stream)
+
+    if args.copy_kernel:
+        src = torch.ones((64 << 20,), dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     for _ in range(args.warmup):
         run_step()
@@ -197,7 +214,7 @@ def main():
         "roofline": {"bound": "mfma", "kernel": "k_gemm (fprop/dgrad/wgrad average)",
                      "achieved": round(achieved, 1), "peak": MFMA_F16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4),
-                     "traffic": None},
+                     "traffic": gemm_traffic()},
         "breakdown": breakdown,
         "quantize_cold_cache": cold,
         "input_gen_s": round(gen_s, 1),
@@ -208,6 +225,17 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(x_bits, w_bits, dy_bits, mask, step_flops)
     print(json.dumps(out))
+
+
+def gemm_traffic():
+    """Counter-derived HBM bytes per GEMM launch, or None when the kernel source differs from the
+    one the counters were taken on."""
+    import hashlib
+    with open(GEMM_SOURCE, "rb") as f:
+        digest = hashlib.sha256(f.read()).hexdigest()
+    if GEMM_TRAFFIC["source_sha256"] != digest:
+        return None
+    return GEMM_TRAFFIC["bytes_per_launch"]
 
 
 def bench_moe(nv, workloads, torch, dev, stream, flush, args):
@@ -272,12 +300,15 @@ def cpu_baseline(x_bits, w_bits, dy_bits, mask, step_flops):
     rng = np.random.default_rng(0)
     parts = []
 
+    sample_times = []
+
     def timed(fn):
         t = time.perf_counter()
         r = fn()
-        return time.perf_counter() - t, r
+        sample_times.append(time.perf_counter() - t)
+        return sample_times[-1], r
 
-    rows = 64
+    rows = 2048
     xs = f32(x_bits[:rows])
     A = oracle.amax(xs)
     t, _ = timed(lambda: oracle.quantize_1x16(xs, amax_vals=A))
@@ -286,26 +317,30 @@ def cpu_baseline(x_bits, w_bits, dy_bits, mask, step_flops):
     t, _ = timed(lambda: (oracle.quantize_16x16(ws_, amax_vals=A),
                           oracle.quantize_16x16(np.ascontiguousarray(ws_.T), amax_vals=A)))
     parts.append(t * N_OUT / rows)
-    dys = f32(dy_bits[:16])
+    dy_rows = 768
+    dys = f32(dy_bits[:dy_rows])
     t, _ = timed(lambda: oracle.quantize_1x16(dys, "sr", seed=1, offset=0, amax_vals=A))
-    parts.append(t * M / 16)
-    cols = 32
+    parts.append(t * M / dy_rows)
+    cols = 1024
     t, _ = timed(lambda: oracle.rht_quantize(f32(dy_bits[:, :cols]), mask, "sr", seed=1,
                                              amax_vals=A, col_ids=np.arange(cols)))
     parts.append(t * N_OUT / cols)
     t, _ = timed(lambda: oracle.rht_quantize(f32(x_bits[:, :cols]), mask, "rn",
                                              amax_vals=A, col_ids=np.arange(cols)))
     parts.append(t * K_IN / cols)
-    # reference GEMM: 32 output rows of each GEMM against the full other operand
-    a_hat = rng.standard_normal((32, K_IN))
+    # reference GEMM: a block of output rows of each GEMM against the full other operand
+    g_rows = 1536
+    a_hat = rng.standard_normal((g_rows, K_IN))
     b_hat = rng.standard_normal((N_OUT, K_IN))
     t, _ = timed(lambda: oracle.gemm_fp64(a_hat, b_hat))
-    parts.append(3 * t * M / 32)
+    parts.append(3 * t * M / g_rows)
+    sampled_s = float(sum(t for t in sample_times))
     total_s = float(sum(parts))
     return {"value": round(step_flops / total_s / 1e12, 6), "unit": "TFLOP/s",
             "cores": int(blas_threads), "kind": "oracle",
-            "sample": "oracle on 64 rows of X/W, 16 rows of dY, 32 columns of each Hadamard "
-                      "operand and 32 output rows of each FP64 GEMM, scaled to the full step "
+            "sample": f"oracle on {rows} rows of X and of W, {dy_rows} rows of dY, {cols} columns of "
+                      f"each Hadamard operand and {g_rows} output rows of each FP64 GEMM "
+                      f"({sampled_s:.1f} s measured), scaled to the full step "
                       f"(estimated {total_s:.1f} s per step; numpy elementwise on 1 core, "
                       f"BLAS on {blas_threads} threads)"}
 

@@ -13,7 +13,6 @@
 
 namespace nvfp4 {
 
-constexpr float kE2M1Max = 6.0f;
 constexpr float kScaleNumerator = 2688.0f;   // largest element (6) x largest E4M3 (448)
 constexpr float kFltMax = 3.40282346638528859812e+38f;
 
@@ -66,27 +65,48 @@ __device__ __forceinline__ float e4m3_decode(uint32_t s) {
 }
 
 // ---- E2M1 elements ---------------------------------------------------------------------
-// Round-to-nearest-even to the E2M1 grid {0,.5,1,1.5,2,3,4,6}, saturating; sign from y.
-__device__ __forceinline__ uint32_t e2m1_rn(float y) {
-  const float a = fminf(fabsf(y), kE2M1Max);
-  const uint32_t b = __float_as_uint(a);
-  // normal range [1, 6]: round the fp32 mantissa to 1 bit, then rebias (127-1) -> 2 steps
-  const uint32_t nrm = (b + 0x1FFFFFu + ((b >> 22) & 1u) - 0x3F000000u) >> 22;
-  // subnormal range [0, 1): steps of 0.5
-  const uint32_t sub = (uint32_t)__builtin_rintf(a * 2.0f);
-  const uint32_t mag = a < 1.0f ? sub : nrm;
-  return mag | ((__float_as_uint(y) >> 28) & 8u);
+// gfx950 converts FP32 to E2M1 in hardware. With its scale operand at 1 the pair conversion
+// rounds to nearest even and saturates at 6, with the sign taken from the input (zero included):
+// exactly the element rounding fixed above, so the element multiply rn32(x * r_b) is done in
+// FP32 first and the result is handed to the converter. The pair (y0, y1) lands in byte `sel`
+// of the result, y0 in the low nibble; the other bytes keep `old`.
+template <int sel>
+__device__ __forceinline__ uint32_t e2m1_rn_pair(uint32_t old, float y0, float y1) {
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, y0, y1, 1.0f, sel);
 }
 
-// Stochastic rounding with random byte r: round up iff frac + r/256 >= 1, where frac is the
-// position of |y| between its two neighbouring grid values. X below is |y| in fixed point
-// with the kept grid step at bit 22, so the decision is the carry out of the low 22 bits.
-__device__ __forceinline__ uint32_t e2m1_sr(float y, uint32_t r) {
-  const float a = fminf(fabsf(y), kE2M1Max);
-  const uint32_t X = a >= 1.0f ? __float_as_uint(a) - 0x3F000000u
-                               : (uint32_t)(a * 8388608.0f);   // floor(a * 2^23)
-  const uint32_t mag = (X + (r << 14)) >> 22;
-  return mag | ((__float_as_uint(y) >> 28) & 8u);
+// Eight codes (y[0] in the low nibble) rounded to nearest even.
+__device__ __forceinline__ uint32_t e2m1_rn8(const float* y) {
+  uint32_t w = e2m1_rn_pair<0>(0u, y[0], y[1]);
+  w = e2m1_rn_pair<1>(w, y[2], y[3]);
+  w = e2m1_rn_pair<2>(w, y[4], y[5]);
+  return e2m1_rn_pair<3>(w, y[6], y[7]);
+}
+
+// Stochastic rounding with the random byte r of the element: round up iff frac + r/256 >= 1.
+// The hardware stochastic converter adds bits 31..10 of its seed operand to the FP32 mantissa
+// of the first value of the pair, aligned just below the kept E2M1 bit (in fixed point for the
+// subnormal range), and truncates; a seed holding r in bits 31..24 and zeros below is therefore
+// the 8-bit rule above. Only the first slot is used: the second slot reads the seed one bit
+// further down, so a pair cannot carry two independent bytes. Byte `byte` (0..3) of `word` is
+// moved to bits 31..24 with a byte permute. The code is the low nibble of the result; the
+// other bits are not defined.
+template <int byte>
+__device__ __forceinline__ uint32_t e2m1_sr_one(float y, uint32_t word) {
+  const uint32_t seed = __builtin_amdgcn_perm(0u, word, 0x000C0C0Cu | ((uint32_t)byte << 24));
+  return __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, v2f32{y, 0.0f}, seed, 1.0f, 0);
+}
+
+// Eight stochastically rounded codes; element i takes byte i%4 of words w0 (i < 4), w1.
+__device__ __forceinline__ uint32_t e2m1_sr8(const float* y, uint32_t w0, uint32_t w1) {
+  // pair byte p = code(2p) | code(2p+1) << 4, valid in bits 0..7 only
+  const uint32_t p0 = (e2m1_sr_one<0>(y[0], w0) & 0xFu) | (e2m1_sr_one<1>(y[1], w0) << 4);
+  const uint32_t p1 = (e2m1_sr_one<2>(y[2], w0) & 0xFu) | (e2m1_sr_one<3>(y[3], w0) << 4);
+  const uint32_t p2 = (e2m1_sr_one<0>(y[4], w1) & 0xFu) | (e2m1_sr_one<1>(y[5], w1) << 4);
+  const uint32_t p3 = (e2m1_sr_one<2>(y[6], w1) & 0xFu) | (e2m1_sr_one<3>(y[7], w1) << 4);
+  const uint32_t lo = __builtin_amdgcn_perm(p1, p0, 0x0C0C0400u);   // bytes p0.b0, p1.b0, 0, 0
+  const uint32_t hi = __builtin_amdgcn_perm(p3, p2, 0x0C0C0400u);
+  return lo | (hi << 16);
 }
 
 // ---- Philox4x32-10 (Salmon et al., SC'11) ----------------------------------------------
@@ -130,21 +150,16 @@ __device__ __forceinline__ BlockScale block_scale(float block_amax, float s_enc)
 template <bool SR>
 __device__ __forceinline__ void encode16(const float (&v)[16], float mult, u32x4 rnd,
                                          uint32_t& lo, uint32_t& hi) {
-  uint32_t w0 = 0, w1 = 0;
+  float y[16];
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const float y = v[j] * mult;
-    uint32_t c;
-    if constexpr (SR) {
-      const uint32_t word = j < 4 ? rnd.x : j < 8 ? rnd.y : j < 12 ? rnd.z : rnd.w;
-      c = e2m1_sr(y, (word >> (8 * (j & 3))) & 0xFFu);
-    } else {
-      c = e2m1_rn(y);
-    }
-    if (j < 8) w0 |= c << (4 * j); else w1 |= c << (4 * (j - 8));
+  for (int j = 0; j < 16; ++j) y[j] = v[j] * mult;
+  if constexpr (SR) {
+    lo = e2m1_sr8(y, rnd.x, rnd.y);
+    hi = e2m1_sr8(y + 8, rnd.z, rnd.w);
+  } else {
+    lo = e2m1_rn8(y);
+    hi = e2m1_rn8(y + 8);
   }
-  lo = w0;
-  hi = w1;
 }
 
 // ---- reductions ----------------------------------------------------------------------------

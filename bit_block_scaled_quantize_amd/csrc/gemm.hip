@@ -9,26 +9,24 @@
 // lies in [2^-10, 2688], so it is exact in FP16. Each lane decodes 8 packed codes with one
 // v_cvt_scalef32_pk_f16_fp4 per code byte (scale operand 2^8, exponent-only) and multiplies
 // by the block scale held as FP16 bits (code << 7) = S * 2^-8, giving exactly e2m1 * S, then
-// feeds v_mfma_f32_16x16x32_f16 (FP32 accumulate). The per-tensor scales multiply the
+// feeds the FP16 matrix cores (FP32 accumulate). The per-tensor scales multiply the
 // accumulator in the epilogue. gfx950's native FP4 MFMA takes power-of-two scales per 32
-// elements, which cannot express an E4M3 scale per 16 elements without leaving most of each
-// instruction idle, so the FP16 path is the one used.
+// elements, which cannot express an E4M3 scale per 16 elements, so the FP16 path is the one
+// used.
 //
-// Operand layout inside a 16x16x32 MFMA: lane l supplies row (l % 16) of A (column of B)
-// and 8 K-values. Since the K order inside a dot product is free as long as A and B agree,
-// each lane holds one contiguous 16-byte run (32 codes) of its row per 128-K step and feeds
-// its 4 octets to 4 consecutive MFMAs; the 4 lane groups cover 4 different 32-element runs.
+// Since the K order inside a dot product is free as long as A and B agree, every lane holds
+// one contiguous run of codes of its row per K step and feeds consecutive octets of it to
+// consecutive MFMAs.
 //
 // Two kernels:
-//  * main (K % 64 == 0, every shape of the workloads): a workgroup of 4 waves (2 x 2) owns a
-//    256 x 256 output tile, each wave 128 x 128 (8 x 8 MFMA tiles, 256 FP32 accumulators per
-//    lane in AGPRs). Per 128-wide K step the workgroup's FP4 panels (2 x 16 KB) and their
-//    scale bytes (2 x 2 KB) go straight from global memory into LDS with buffer-to-LDS DMA,
-//    double-buffered: the DMA for step s+1 is issued right after step s's fragments are read,
-//    so it has the whole of step s's MFMA work to land, and no registers are spent on
-//    staging. Buffer bounds make rows past the end of an operand read as zero.
-//  * general (any K % 16 == 0): 128 x 128 tiles, each wave 64 x 64, operands loaded straight
-//    into registers one K step ahead.
+//  * main (K % 64 == 0, every shape of the workloads): v_mfma_f32_32x32x16_f16; a workgroup of
+//    4 waves (2 x 2) owns a 256 x 256 output tile, each wave 128 x 128 (4 x 4 MFMA tiles, 256
+//    FP32 accumulators per lane in AGPRs). Per 128-wide K step the workgroup's FP4 panels
+//    (2 x 16 KB) and scale bytes (2 x 2 KB) go straight from global memory into LDS with
+//    buffer-to-LDS DMA, three stages deep, so no registers are spent on staging. Buffer bounds
+//    make rows past the end of an operand read as zero.
+//  * general (any K % 16 == 0): v_mfma_f32_16x16x32_f16, 128 x 128 tiles, each wave 64 x 64,
+//    operands loaded straight into registers one K step ahead.
 // In both, scale bytes at or past K are forced to 0, which zeroes whatever codes sit in a
 // partial last step.
 #include "device_common.h"
@@ -176,25 +174,36 @@ __device__ __forceinline__ void gemm_tile_big(Operand A, Operand B, int64_t m0, 
   const uint32_t dma_stride = 128u * rs_codes;                // 4 fragments = 128 rows apart
   const uint32_t sdma_stride = 128u * rs_scales;
 
-  auto issue_dma = [&](int64_t step, int buf) {
+  // One of the wave's 12 DMA operations of a step: part p = 3*i + q moves half q (q < 2) of
+  // fragment wave + 4*i, or (q == 2) its scale dwords. Steps past the last one are issued too
+  // (the pipeline then has no branches and always the same number of operations in flight)
+  // with an offset beyond every buffer's range, which the buffer unit answers with zeros
+  // without touching memory; their LDS buffers are never read.
+  const int64_t steps = (K + kStepK - 1) / kStepK;
+  constexpr uint32_t kBeyond = 0x80000000u;                  // > any 31-bit buffer size
+  auto issue_dma_part = [&](int64_t step, int buf, int p) {
     uint8_t* base = lds + buf * kStageBytes;
-    const uint32_t koff = (uint32_t)(step * (kStepK / 2));
-    const uint32_t soff = (uint32_t)(step * (kStepK / 16));
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const bool is_a = i < 2;
-      const int f = wave + 4 * i;
-      const uint32_t off = (is_a ? dma_a : dma_b) + (uint32_t)(i & 1) * dma_stride + koff;
-#pragma unroll
-      for (int q = 0; q < 2; ++q)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a ? a_codes : b_codes,
-                                                 (lds_ptr_t)(base + f * kFragBytes + q * 1024),
-                                                 16, off + 16 * q, 0, 0, 0);
-      const uint32_t so = (is_a ? sdma_a : sdma_b) + (uint32_t)(i & 1) * sdma_stride + soff;
+    const int i = p / 3, q = p % 3;
+    const bool is_a = i < 2;
+    const int f = wave + 4 * i;
+    const bool live = step < steps;
+    if (q < 2) {
+      const uint32_t off = (is_a ? dma_a : dma_b) + (uint32_t)(i & 1) * dma_stride +
+                           (uint32_t)(step * (kStepK / 2)) + 16u * q;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a ? a_codes : b_codes,
+                                               (lds_ptr_t)(base + f * kFragBytes + q * 1024),
+                                               16, live ? off : kBeyond, 0, 0, 0);
+    } else {
+      const uint32_t so = (is_a ? sdma_a : sdma_b) + (uint32_t)(i & 1) * sdma_stride +
+                          (uint32_t)(step * (kStepK / 16));
       __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a ? a_scales : b_scales,
                                                (lds_ptr_t)(base + kCodeBytes + f * kFragScaleBytes),
-                                               4, so, 0, 0, 0);
+                                               4, live ? so : kBeyond, 0, 0, 0);
     }
+  };
+  auto issue_dma = [&](int64_t step, int buf) {
+#pragma unroll
+    for (int p = 0; p < kDmaPerWaveStep; ++p) issue_dma_part(step, buf, p);
   };
 
   float16v acc[kFragsM][kFragsN];
@@ -229,27 +238,24 @@ __device__ __forceinline__ void gemm_tile_big(Operand A, Operand B, int64_t m0, 
     for (int i = 0; i < kFragsM; ++i)
       ra[i] = *reinterpret_cast<const v4u32*>(cur + (wm * kFragsM + i) * kFragBytes);
   };
-  auto read_scales = [&](int b, int64_t step) {
+  // raw scale dwords; the mask for blocks past K is applied where they are consumed, so the
+  // loads need not land before the step that uses them
+  auto read_scales = [&](int b) {
     const uint8_t* cur = lds + b * kStageBytes + kCodeBytes + lane * 4;
-    const uint32_t keep = k_mask4(K, step * kStepK + h * 64);
 #pragma unroll
     for (int j = 0; j < kFragsN; ++j)
-      sb[j] = *reinterpret_cast<const uint32_t*>(cur + (kFragsA + wn * kFragsN + j) * kFragScaleBytes) & keep;
+      sb[j] = *reinterpret_cast<const uint32_t*>(cur + (kFragsA + wn * kFragsN + j) * kFragScaleBytes);
 #pragma unroll
     for (int i = 0; i < kFragsM; ++i)
-      sa[i] = *reinterpret_cast<const uint32_t*>(cur + (wm * kFragsM + i) * kFragScaleBytes) & keep;
+      sa[i] = *reinterpret_cast<const uint32_t*>(cur + (wm * kFragsM + i) * kFragScaleBytes);
   };
 
-  const int64_t steps = (K + kStepK - 1) / kStepK;
 #pragma unroll
-  for (int p = 0; p < kStages; ++p)
-    if (p < steps) issue_dma(p, p);
-  if (steps >= 3) __builtin_amdgcn_s_waitcnt(0x4F78);        // vmcnt(24)
-  else if (steps == 2) __builtin_amdgcn_s_waitcnt(0x0F7C);   // vmcnt(12)
-  else __builtin_amdgcn_s_waitcnt(0x0F70);                   // vmcnt(0)
+  for (int p = 0; p < kStages; ++p) issue_dma(p, p);
+  __builtin_amdgcn_s_waitcnt(0x4F78);                         // vmcnt(24): step 0 landed
   barrier();
   read_half(0, 0, ar0, br0);
-  read_scales(0, 0);
+  read_scales(0);
 
   int b_cur = 0;
   for (int64_t s = 0; s < steps; ++s) {
@@ -257,15 +263,16 @@ __device__ __forceinline__ void gemm_tile_big(Operand A, Operand B, int64_t m0, 
     read_half(b_cur, 1, ar1, br1);
 
     // FP16 scale pairs of the 4 blocks of every fragment: (b << 7) | (b << 23) = b * 0x00800080
+    const uint32_t keep = k_mask4(K, s * kStepK + h * 64);
     half2v pa[kFragsM][4], pb[kFragsN][4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
 #pragma unroll
       for (int i = 0; i < kFragsM; ++i)
-        pa[i][q] = __builtin_bit_cast(half2v, ((sa[i] >> (8 * q)) & 0xFFu) * 0x00800080u);
+        pa[i][q] = __builtin_bit_cast(half2v, (((sa[i] & keep) >> (8 * q)) & 0xFFu) * 0x00800080u);
 #pragma unroll
       for (int j = 0; j < kFragsN; ++j)
-        pb[j][q] = __builtin_bit_cast(half2v, ((sb[j] >> (8 * q)) & 0xFFu) * 0x00800080u);
+        pb[j][q] = __builtin_bit_cast(half2v, (((sb[j] & keep) >> (8 * q)) & 0xFFu) * 0x00800080u);
     }
 
     // 32 phases (t = K octet, i = A fragment), each 4 MFMAs. Decodes run one phase ahead:
@@ -280,16 +287,24 @@ __device__ __forceinline__ void gemm_tile_big(Operand A, Operand B, int64_t m0, 
     av = decode8(araw(0, 0), pa[0][0]);
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-      if (t == 4 && s + 1 < steps) {
-        if (s + 2 < steps) __builtin_amdgcn_s_waitcnt(0x007C);   // vmcnt(12) lgkmcnt(0)
-        else __builtin_amdgcn_s_waitcnt(0x0070);               // vmcnt(0) lgkmcnt(0)
+      if (t == 4) {
+        // unconditional (on the last step the reads fetch an unused buffer): with the block
+        // behind a branch the compiler's wait analysis, merging the two paths, would make
+        // the wave wait for these new reads before decoding data that has long landed.
+        // Steps s+1 and s+2 are in flight here; wait for s+1.
+        __builtin_amdgcn_s_waitcnt(0x007C);                     // vmcnt(12) lgkmcnt(0)
         barrier();
         read_half(b_next, 0, ar0, br0);
-        read_scales(b_next, s + 1);
-        if (s + 3 < steps) issue_dma(s + 3, b_cur);
+        read_scales(b_next);
       }
 #pragma unroll
       for (int i = 0; i < kFragsM; ++i) {
+        // the DMA of step s+3 refills the buffer step s was read from, one operation per
+        // phase in octets 5-7: a burst of 12 would stall the wave's issue while its matrix
+        // pipe runs dry, and the compiler orders each LDS-bound DMA after the wave's pending
+        // LDS reads (it cannot tell the buffers apart), so the DMA waits one octet for the
+        // reads issued at the barrier to land
+        if (t >= 5) issue_dma_part(s + 3, b_cur, (t - 5) * kFragsM + i);
         const int tn = i + 1 < kFragsM ? t : t + 1;           // next phase
         const int in_ = i + 1 < kFragsM ? i + 1 : 0;
         half8 an = av;

@@ -23,34 +23,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWavesPerBlock = kThreads / 64;
 constexpr int kMaxPartials = 1024;
-
-// 16 consecutive inputs starting at p (16-byte aligned) as floats.
-template <typename TIn>
-__device__ __forceinline__ void load16(const TIn* p, float (&v)[16]);
-
-template <>
-__device__ __forceinline__ void load16<uint16_t>(const uint16_t* p, float (&v)[16]) {
-  const v4u32 a = ld_u32x4(p);
-  const v4u32 b = ld_u32x4(p + 8);
-  const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    v[2 * i] = bf16_lo(w[i]);
-    v[2 * i + 1] = bf16_hi(w[i]);
-  }
-}
-
-template <>
-__device__ __forceinline__ void load16<float>(const float* p, float (&v)[16]) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const v4f32 a = ld_f32x4(p + 4 * i);
-    v[4 * i] = a.x;
-    v[4 * i + 1] = a.y;
-    v[4 * i + 2] = a.z;
-    v[4 * i + 3] = a.w;
-  }
-}
+constexpr int kAmaxUnroll = 8;         // 16-byte loads in flight per thread in the amax pass
 
 __device__ __forceinline__ float abs_max16(const float (&v)[16]) {
   float m = 0.0f;
@@ -106,15 +79,16 @@ __global__ __launch_bounds__(kThreads) void k_amax_partial(const TIn* __restrict
   const bool contiguous = ld == vecs_per_row * kVec;
   float m = 0.0f;
   int64_t q = q0 + threadIdx.x;
-  for (; q + 3 * kThreads < q1; q += 4 * kThreads) {
-    float a[4];
+  for (; q + (kAmaxUnroll - 1) * kThreads < q1; q += kAmaxUnroll * kThreads) {
+    float a[kAmaxUnroll];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < kAmaxUnroll; ++u) {
       const int64_t qq = q + u * kThreads;
       const int64_t off = contiguous ? qq * kVec : (qq / vecs_per_row) * ld + (qq % vecs_per_row) * kVec;
       a[u] = vec_absmax<TIn>(x + off);
     }
-    m = fmaxf(m, fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3])));
+#pragma unroll
+    for (int u = 0; u < kAmaxUnroll; ++u) m = fmaxf(m, a[u]);
   }
   for (; q < q1; q += kThreads) {
     const int64_t off = contiguous ? q * kVec : (q / vecs_per_row) * ld + (q % vecs_per_row) * kVec;
@@ -190,18 +164,102 @@ __device__ __forceinline__ float fold_amax(const float* __restrict__ amax, int p
 }
 
 // ---------------------------------------------------------------------------------------
-// 1x16 encode: lane = one 16-element block; wave = up to 64 consecutive blocks of a row.
+// 1x16 encode: lane = one 16-element block. A wave walks its rows (rows wave, wave + nwaves, ...
+// counted from the end of the tensor, the reverse of the amax pass) in chunks of U blocks per
+// lane (64*U consecutive blocks of a row) and keeps the next chunk's loads in flight while it
+// encodes the current one; the first chunk is requested before the tensor amax is folded, so
+// the fold hides under the load latency.
+// Lane-pair exchange (DPP quad permute [1,0,3,2]): every lane receives its partner's value.
+__device__ __forceinline__ uint32_t pair_swap(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);
+}
+
+// Chunk of U groups of 64 consecutive blocks of one row. BF16: each load instruction covers
+// 1 KiB of the row contiguously (lane l: bytes 16l..16l+15 of a group half), so lane l holds
+// half l%2 of block l/2 (first 1 KiB) and of block 32 + l/2 (second 1 KiB); one lane-pair
+// exchange then gives even lanes block l/2 and odd lanes block 32 + l/2 of the group whole.
+// FP32: each lane loads its own 64-byte block.
+template <typename TIn>
+struct Chunk;
+
+template <>
+struct Chunk<uint16_t> {
+  static constexpr int U = 4;
+  v4u32 h0[U], h1[U];                                   // first / second KiB of group u
+  __device__ __forceinline__ static int64_t block_of(int lane, int u) {
+    return 64 * u + ((lane & 1) << 5) + (lane >> 1);
+  }
+  __device__ __forceinline__ void load(const uint16_t* xr, int64_t b0, int64_t nb, int lane) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t g = b0 + 64 * u;
+      if (g + (lane >> 1) < nb) h0[u] = ld_u32x4(xr + g * 16 + lane * 8);
+      if (g + 32 + (lane >> 1) < nb) h1[u] = ld_u32x4(xr + g * 16 + 512 + lane * 8);
+    }
+  }
+  __device__ __forceinline__ void get(int u, int lane, float (&v)[16]) const {
+    const bool odd = lane & 1;
+    v4u32 send = odd ? h0[u] : h1[u], recv;
+    recv.x = pair_swap(send.x);
+    recv.y = pair_swap(send.y);
+    recv.z = pair_swap(send.z);
+    recv.w = pair_swap(send.w);
+    const v4u32 lo = odd ? recv : h0[u];                 // elements 0..7 of the lane's block
+    const v4u32 hi = odd ? h1[u] : recv;                 // elements 8..15
+    const uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      v[2 * i] = bf16_lo(w[i]);
+      v[2 * i + 1] = bf16_hi(w[i]);
+    }
+  }
+};
+
+template <>
+struct Chunk<float> {
+  static constexpr int U = 2;
+  v4f32 q[U][4];
+  __device__ __forceinline__ static int64_t block_of(int lane, int u) { return 64 * u + lane; }
+  __device__ __forceinline__ void load(const float* xr, int64_t b0, int64_t nb, int lane) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t b = b0 + block_of(lane, u);
+      if (b < nb) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) q[u][i] = ld_f32x4(xr + b * 16 + 4 * i);
+      }
+    }
+  }
+  __device__ __forceinline__ void get(int u, int, float (&v)[16]) const {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[4 * i] = q[u][i].x;
+      v[4 * i + 1] = q[u][i].y;
+      v[4 * i + 2] = q[u][i].z;
+      v[4 * i + 3] = q[u][i].w;
+    }
+  }
+};
+
 template <typename TIn, bool SR, bool SEG>
 __global__ __launch_bounds__(kThreads) void k_encode_1x16(
     const TIn* __restrict__ x, int64_t rows, int64_t cols, int64_t ld,
     const float* __restrict__ amax, int amax_parts, const int64_t* __restrict__ seg, int64_t nseg,
     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ gscale,
     uint64_t seed, uint64_t offset) {
+  using C = Chunk<TIn>;
+  constexpr int U = C::U;
+  constexpr int64_t kSpan = 64 * U;            // blocks of a row covered by one chunk
   __shared__ float red[kWavesPerBlock];
   const int lane = threadIdx.x & 63;
   const int64_t wave = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
   const int64_t nwaves = (int64_t)gridDim.x * kWavesPerBlock;
   const int64_t nb = cols >> 4;
+
+  C cur, nxt;
+  int64_t it = wave, b0 = 0;
+  if (it < rows) cur.load(x + (rows - 1 - it) * ld, b0, nb, lane);
+
   const float a0 = fold_amax(amax, SEG ? 1 : amax_parts, red);
   if (blockIdx.x == 0) {
     if constexpr (SEG) {
@@ -211,30 +269,44 @@ __global__ __launch_bounds__(kThreads) void k_encode_1x16(
     }
   }
   float s_enc = tensor_encode_scale(a0);
-  int64_t cur = 0;
-  for (int64_t it = wave; it < rows; it += nwaves) {
-    const int64_t r = rows - 1 - it;                 // reverse of the amax pass
+  int64_t cur_seg = -1;
+
+  while (it < rows) {
+    int64_t it_n = it, b0_n = b0 + kSpan;
+    if (b0_n >= nb) {
+      b0_n = 0;
+      it_n = it + nwaves;
+    }
+    if (it_n < rows) nxt.load(x + (rows - 1 - it_n) * ld, b0_n, nb, lane);
+
+    const int64_t r = rows - 1 - it;
     if constexpr (SEG) {
       const int64_t s = find_segment(seg, nseg, r);
-      if (s != cur) {
-        cur = s;
+      if (s != cur_seg) {
+        cur_seg = s;
         s_enc = tensor_encode_scale(amax[s]);
       }
     }
-    const TIn* xr = x + r * ld;
     uint2* cr = reinterpret_cast<uint2*>(codes + r * (cols >> 1));
     uint8_t* sr = scales + r * nb;
-    for (int64_t b = lane; b < nb; b += 64) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
       float v[16];
-      load16<TIn>(xr + b * 16, v);
-      const BlockScale bs = block_scale(abs_max16(v), s_enc);
-      u32x4 rnd{0, 0, 0, 0};
-      if constexpr (SR) rnd = block_random((uint64_t)(r * nb + b), seed, offset);
-      uint32_t lo, hi;
-      encode16<SR>(v, bs.mult, rnd, lo, hi);
-      cr[b] = make_uint2(lo, hi);
-      sr[b] = (uint8_t)bs.code;
+      cur.get(u, lane, v);                       // all lanes: the exchange is wave-wide
+      const int64_t b = b0 + C::block_of(lane, u);
+      if (b < nb) {
+        const BlockScale bs = block_scale(abs_max16(v), s_enc);
+        u32x4 rnd{0, 0, 0, 0};
+        if constexpr (SR) rnd = block_random((uint64_t)(r * nb + b), seed, offset);
+        uint32_t lo, hi;
+        encode16<SR>(v, bs.mult, rnd, lo, hi);
+        cr[b] = make_uint2(lo, hi);
+        sr[b] = (uint8_t)bs.code;
+      }
     }
+    cur = nxt;
+    it = it_n;
+    b0 = b0_n;
   }
 }
 
@@ -327,10 +399,10 @@ __global__ __launch_bounds__(kThreads) void k_encode_16x16(
   uint32_t w[16];
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
-    uint32_t c = 0;
+    float y[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) c |= e2m1_rn(v[j].get(i) * bs.mult) << (4 * i);
-    w[j] = c;
+    for (int i = 0; i < 8; ++i) y[i] = v[j].get(i) * bs.mult;
+    w[j] = e2m1_rn8(y);
   }
   if (active) {
 #pragma unroll
@@ -404,6 +476,7 @@ int grid_for(int64_t work_items, int64_t items_per_block, int64_t cap) {
 }
 
 constexpr int64_t kMaxBlocks = 256 * 16;   // 16 workgroups per CU is plenty for streaming
+constexpr int64_t kEncodeBlocks = 256 * 4;   // 1x16 encode: 4 workgroups per CU, waves loop over rows
 
 template <typename TIn>
 void amax_t(const void* x, int64_t rows, int64_t cols, int64_t ld, const int64_t* segments,
@@ -442,7 +515,7 @@ template <typename TIn, bool SR, bool SEG>
 static void encode_1x16_t(const void* x, int64_t rows, int64_t cols, int64_t ld, uint64_t seed,
                           uint64_t offset, const int64_t* segments, int64_t nseg,
                           const float* amax, int parts, QuantOut out, hipStream_t stream) {
-  const int grid = grid_for(rows, kWavesPerBlock, kMaxBlocks);
+  const int grid = grid_for(rows, kWavesPerBlock, kEncodeBlocks);
   hipLaunchKernelGGL((k_encode_1x16<TIn, SR, SEG>), dim3(grid), dim3(kThreads), 0, stream,
                      (const TIn*)x, rows, cols, ld, amax, parts, segments, nseg, out.codes,
                      out.scales, out.global_scale, seed, offset);
