@@ -257,34 +257,44 @@ __device__ __forceinline__ void gemm_tile_big(Operand A, Operand B, int64_t m0, 
   read_half(0, 0, ar0, br0);
   read_scales(0);
 
+  // FP16 scale pair (S * 2^-8 twice) of block q of a scale dword, blocks at or past K zeroed:
+  // (b << 7) | (b << 23) = b * 0x00800080
+  auto pair = [](uint32_t sc, uint32_t keep, int q) {
+    return __builtin_bit_cast(half2v, (((sc & keep) >> (8 * q)) & 0xFFu) * 0x00800080u);
+  };
+
+  // 32 phases per step (t = K octet, i = A fragment), each 4 MFMAs. Decodes run one phase
+  // ahead: while phase (t, i) issues its MFMAs, the A fragment of the next phase and B
+  // fragment i of octet t+1 are decoded, so every MFMA finds its operands ready and the vector
+  // ALU works under the matrix core; the last octet already decodes octet 0 of the next step
+  // (its half 0 and scales arrive at octet 4), so steps join without a gap. sched_barrier
+  // keeps the compiler from regrouping phases.
+  half8 bv[kFragsN], bn[kFragsN], av;
+  {
+    const uint32_t keep0 = k_mask4(K, h * 64);
+#pragma unroll
+    for (int j = 0; j < kFragsN; ++j) bv[j] = decode8(br0[j].x, pair(sb[j], keep0, 0));
+    av = decode8(ar0[0].x, pair(sa[0], keep0, 0));
+  }
+
   int b_cur = 0;
   for (int64_t s = 0; s < steps; ++s) {
     const int b_next = b_cur == kStages - 1 ? 0 : b_cur + 1;
     read_half(b_cur, 1, ar1, br1);
 
-    // FP16 scale pairs of the 4 blocks of every fragment: (b << 7) | (b << 23) = b * 0x00800080
     const uint32_t keep = k_mask4(K, s * kStepK + h * 64);
+    const uint32_t keep_next = k_mask4(K, (s + 1) * kStepK + h * 64);
     half2v pa[kFragsM][4], pb[kFragsN][4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
 #pragma unroll
-      for (int i = 0; i < kFragsM; ++i)
-        pa[i][q] = __builtin_bit_cast(half2v, (((sa[i] & keep) >> (8 * q)) & 0xFFu) * 0x00800080u);
+      for (int i = 0; i < kFragsM; ++i) pa[i][q] = pair(sa[i], keep, q);
 #pragma unroll
-      for (int j = 0; j < kFragsN; ++j)
-        pb[j][q] = __builtin_bit_cast(half2v, (((sb[j] & keep) >> (8 * q)) & 0xFFu) * 0x00800080u);
+      for (int j = 0; j < kFragsN; ++j) pb[j][q] = pair(sb[j], keep, q);
     }
 
-    // 32 phases (t = K octet, i = A fragment), each 4 MFMAs. Decodes run one phase ahead:
-    // while phase (t, i) issues its MFMAs, the A fragment of the next phase and B fragment i
-    // of octet t+1 are decoded, so every MFMA finds its operands ready and the vector ALU
-    // works under the matrix core. sched_barrier keeps the compiler from regrouping phases.
     auto araw = [&](int i, int t) { return word(t < 4 ? ar0[i] : ar1[i], t & 3); };
     auto braw = [&](int j, int t) { return word(t < 4 ? br0[j] : br1[j], t & 3); };
-    half8 bv[kFragsN], bn[kFragsN], av;
-#pragma unroll
-    for (int j = 0; j < kFragsN; ++j) bv[j] = decode8(braw(j, 0), pb[j][0]);
-    av = decode8(araw(0, 0), pa[0][0]);
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       if (t == 4) {
@@ -294,7 +304,7 @@ __device__ __forceinline__ void gemm_tile_big(Operand A, Operand B, int64_t m0, 
         // Steps s+1 and s+2 are in flight here; wait for s+1.
         __builtin_amdgcn_s_waitcnt(0x007C);                     // vmcnt(12) lgkmcnt(0)
         barrier();
-        read_half(b_next, 0, ar0, br0);
+        read_half(b_next, 0, ar0, br0);                         // sa, sb now step s+1's
         read_scales(b_next);
       }
 #pragma unroll
@@ -307,11 +317,10 @@ __device__ __forceinline__ void gemm_tile_big(Operand A, Operand B, int64_t m0, 
         if (t >= 5) issue_dma_part(s + 3, b_cur, (t - 5) * kFragsM + i);
         const int tn = i + 1 < kFragsM ? t : t + 1;           // next phase
         const int in_ = i + 1 < kFragsM ? i + 1 : 0;
-        half8 an = av;
-        if (tn < 8) {
-          an = decode8(araw(in_, tn), pa[in_][tn >> 1]);
-          if (t + 1 < 8) bn[i] = decode8(braw(i, t + 1), pb[i][(t + 1) >> 1]);
-        }
+        const half8 an = tn < 8 ? decode8(araw(in_, tn), pa[in_][tn >> 1])
+                                : decode8(ar0[0].x, pair(sa[0], keep_next, 0));
+        bn[i] = t + 1 < 8 ? decode8(braw(i, t + 1), pb[i][(t + 1) >> 1])
+                          : decode8(br0[i].x, pair(sb[i], keep_next, 0));
 #pragma unroll
         for (int j = 0; j < kFragsN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, bv[j], acc[i][j], 0, 0, 0);
