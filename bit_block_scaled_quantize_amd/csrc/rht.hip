@@ -11,12 +11,14 @@
 // once to FP32. The 16 outputs of one (column, token block) are exactly one 1x16
 // quantization block of the transposed output [cols, tokens].
 //
-// Layout: a workgroup owns 128 columns x 256 tokens (16 token blocks). Lane l of every wave
-// owns columns 2l and 2l+1, so a wave-wide load of one token row is 64 x 4 bytes (BF16) of
-// contiguous memory; wave w handles token blocks w, w+4, w+8, w+12 and loads all of its rows
-// up front. Codes and scales are staged in LDS as [column][token block] and written out as
-// 128-byte row segments of the transposed tensor. The amax variant grid-strides over the
-// same tiles and leaves one partial maximum per workgroup.
+// Layout: a tile is 128 columns x 256 tokens (16 token blocks). Lane l of every wave owns
+// columns 2l and 2l+1, so a wave-wide load of one token row is 64 x 4 bytes (BF16) of
+// contiguous memory; wave w handles token blocks w, w+4, w+8, w+12 of a tile. Workgroups walk
+// tiles with a stride of the grid (sized to what the device keeps resident), and each wave
+// requests the 16 rows of its next token block before transforming the current one, across
+// tile boundaries too. Codes and scales are staged in LDS as [column][token block] and written
+// out as 128-byte row segments of the transposed tensor. The amax variant walks the same tiles
+// and leaves one partial maximum per workgroup.
 #include "device_common.h"
 #include "launch.h"
 
@@ -56,11 +58,17 @@ struct Pair<float> {
   __device__ __forceinline__ float get(int q) const { return q == 0 ? w.x : w.y; }
 };
 
-// y[i] = rn32(1/4 * sum_j H[i][j] * s_j * v[j]) via the binary64 butterfly.
+// y[i] = rn32(1/4 * sum_j H[i][j] * s_j * v[j]) via the binary64 butterfly. For BF16 inputs
+// the factor +-1/4 is applied in binary32, where it is exact (a BF16 value times 2^-2 is a
+// multiple of 2^-135, inside binary32's subnormal grid); FP32 inputs take it in binary64.
+template <typename TIn>
 __device__ __forceinline__ void rht16(const float (&v)[16], uint32_t mask, float (&y)[16]) {
   double u[16];
 #pragma unroll
-  for (int j = 0; j < 16; ++j) u[j] = (double)v[j] * (((mask >> j) & 1u) ? -0.25 : 0.25);
+  for (int j = 0; j < 16; ++j) {
+    if constexpr (sizeof(TIn) == 2) u[j] = (double)(v[j] * (((mask >> j) & 1u) ? -0.25f : 0.25f));
+    else u[j] = (double)v[j] * (((mask >> j) & 1u) ? -0.25 : 0.25);
+  }
 #pragma unroll
   for (int h = 1; h < 16; h <<= 1) {
 #pragma unroll
@@ -96,13 +104,36 @@ __global__ __launch_bounds__(kThreads) void k_rht(
   __shared__ float red[kWaves];
   __shared__ __attribute__((aligned(16))) uint8_t tc[ENCODE ? kTileCols : 1][kTileBlocks * 8];
   __shared__ __attribute__((aligned(16))) uint8_t ts[ENCODE ? kTileCols : 1][kTileBlocks];
-  constexpr int kNB = sizeof(TIn) == 2 ? kBlocksPerWave : 2;   // token blocks loaded at once
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t nbt = tokens >> 4;
   const int64_t tiles_c = (cols + kTileCols - 1) / kTileCols;
   const int64_t tiles = tiles_c * ((nbt + kTileBlocks - 1) / kTileBlocks);
   const bool paired = (ld & 1) == 0;
+
+  // A workgroup walks tiles blockIdx.x, blockIdx.x + gridDim.x, ...; in each, wave w takes the
+  // token blocks w, w+4, w+8, w+12 (item k = 0..3). The next item's 16 rows are requested
+  // before the current item is transformed, also across tiles.
+  struct Geo { int64_t C0, TB0; };
+  auto geo = [&](int64_t it) {
+    const int64_t tile = ENCODE ? tiles - 1 - it : it;   // encode walks back over the amax order
+    const int64_t tt = tile / tiles_c;
+    return Geo{(tile - tt * tiles_c) * kTileCols, tt * kTileBlocks};
+  };
+  auto load_item = [&](Pair<TIn> (&raw)[16], int64_t it, int k) {
+    const Geo g = geo(it);
+    const int64_t c = g.C0 + 2 * lane;
+    const int64_t cl = c < cols ? c : 0;                    // clamped column for loads
+    const int64_t tb = g.TB0 + wave + 4 * k;
+    const int64_t tbl = tb < nbt ? tb : 0;                  // clamped token block for loads
+#pragma unroll
+    for (int j = 0; j < 16; ++j) raw[j].load(x + (tbl * 16 + j) * ld + cl, c + 1 < cols, paired);
+  };
+
+  Pair<TIn> cur[16], nxt[16];
+  int64_t it = blockIdx.x;
+  int k = 0;
+  if (it < tiles) load_item(cur, it, 0);
 
   float s_enc = 1.0f;
   if constexpr (ENCODE) {
@@ -118,78 +149,73 @@ __global__ __launch_bounds__(kThreads) void k_rht(
   }
 
   float m = 0.0f;
-  for (int64_t it = blockIdx.x; it < tiles; it += gridDim.x) {
-    const int64_t tile = ENCODE ? tiles - 1 - it : it;     // encode walks back over the amax order
-    const int64_t tt = tile / tiles_c;
-    const int64_t C0 = (tile - tt * tiles_c) * kTileCols, TB0 = tt * kTileBlocks;
-    const int64_t c = C0 + 2 * lane;
-    const bool valid0 = c < cols, valid1 = c + 1 < cols;
-    const int64_t cl = valid0 ? c : 0;                      // clamped column for loads
+  while (it < tiles) {                                      // uniform across the workgroup
+    int64_t it_n = it;
+    int k_n = k + 1;
+    if (k_n == kBlocksPerWave) {
+      k_n = 0;
+      it_n = it + gridDim.x;
+    }
+    if (it_n < tiles) load_item(nxt, it_n, k_n);
 
+    const Geo g = geo(it);
+    const int64_t c = g.C0 + 2 * lane;
+    const int bl = wave + 4 * k;                            // token block within the tile
+    const int64_t tb = g.TB0 + bl;
+    if (tb < nbt) {
 #pragma unroll
-    for (int k0 = 0; k0 < kBlocksPerWave; k0 += kNB) {
-      Pair<TIn> raw[kNB][16];
+      for (int q = 0; q < 2; ++q) {
+        float v[16], y[16];
 #pragma unroll
-      for (int k = 0; k < kNB; ++k) {
-        const int64_t tb = TB0 + wave + 4 * (k0 + k);
-        const int64_t tbl = tb < nbt ? tb : 0;              // clamped token block for loads
+        for (int j = 0; j < 16; ++j) v[j] = cur[j].get(q);
+        rht16<TIn>(v, mask, y);
+        float bm = 0.0f;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) raw[k][j].load(x + (tbl * 16 + j) * ld + cl, valid1, paired);
-      }
-#pragma unroll
-      for (int k = 0; k < kNB; ++k) {
-        const int bl = wave + 4 * (k0 + k);                 // token block within the tile
-        const int64_t tb = TB0 + bl;
-        if (tb >= nbt) continue;
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          const bool valid = q == 0 ? valid0 : valid1;
-          float v[16], y[16];
-#pragma unroll
-          for (int j = 0; j < 16; ++j) v[j] = raw[k][j].get(q);
-          rht16(v, mask, y);
-          float bm = 0.0f;
-#pragma unroll
-          for (int i = 0; i < 16; ++i) bm = fmaxf(bm, fabsf(y[i]));
-          if constexpr (!ENCODE) {
-            if (valid) m = fmaxf(m, bm);
-          } else {
-            const int64_t row = c + q;                      // output row = input column
-            const BlockScale bs = block_scale(bm, s_enc);
-            u32x4 rnd{0, 0, 0, 0};
-            if constexpr (SR) rnd = block_random((uint64_t)(row * nbt + tb), seed, offset);
-            uint32_t lo, hi;
-            encode16<SR>(y, bs.mult, rnd, lo, hi);
-            *reinterpret_cast<uint2*>(&tc[2 * lane + q][bl * 8]) = make_uint2(lo, hi);
-            ts[2 * lane + q][bl] = (uint8_t)bs.code;
-          }
+        for (int i = 0; i < 16; ++i) bm = fmaxf(bm, fabsf(y[i]));
+        if constexpr (!ENCODE) {
+          if (c + q < cols) m = fmaxf(m, bm);
+        } else {
+          const int64_t row = c + q;                        // output row = input column
+          const BlockScale bs = block_scale(bm, s_enc);
+          u32x4 rnd{0, 0, 0, 0};
+          if constexpr (SR) rnd = block_random((uint64_t)(row * nbt + tb), seed, offset);
+          uint32_t lo, hi;
+          encode16<SR>(y, bs.mult, rnd, lo, hi);
+          *reinterpret_cast<uint2*>(&tc[2 * lane + q][bl * 8]) = make_uint2(lo, hi);
+          ts[2 * lane + q][bl] = (uint8_t)bs.code;
         }
       }
     }
 
     if constexpr (ENCODE) {
-      __syncthreads();
-      const int64_t valid_cols = cols - C0 < kTileCols ? cols - C0 : kTileCols;
-      const int64_t valid_tb = nbt - TB0 < kTileBlocks ? nbt - TB0 : kTileBlocks;
+      if (k == kBlocksPerWave - 1) {                        // tile complete: write x^T rows
+        __syncthreads();
+        const int64_t valid_cols = cols - g.C0 < kTileCols ? cols - g.C0 : kTileCols;
+        const int64_t valid_tb = nbt - g.TB0 < kTileBlocks ? nbt - g.TB0 : kTileBlocks;
 #pragma unroll
-      for (int pass = 0; pass < kTileCols * kTileBlocks / kThreads; ++pass) {
-        const int idx = pass * kThreads + threadIdx.x;
-        const int cr = idx >> 4, p = idx & 15;
-        if (cr < valid_cols && p < valid_tb)
-          *reinterpret_cast<uint2*>(codes + (C0 + cr) * (tokens >> 1) + (TB0 + p) * 8) =
-              *reinterpret_cast<const uint2*>(&tc[cr][p * 8]);
-      }
-      if (threadIdx.x < valid_cols) {
-        const int cr = threadIdx.x;
-        uint8_t* dst = scales + (C0 + cr) * nbt + TB0;
-        if (valid_tb == kTileBlocks && ((reinterpret_cast<uintptr_t>(dst) & 15) == 0)) {
-          *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(&ts[cr][0]);
-        } else {
-          for (int p = 0; p < valid_tb; ++p) dst[p] = ts[cr][p];
+        for (int pass = 0; pass < kTileCols * kTileBlocks / kThreads; ++pass) {
+          const int idx = pass * kThreads + threadIdx.x;
+          const int cr = idx >> 4, p = idx & 15;
+          if (cr < valid_cols && p < valid_tb)
+            *reinterpret_cast<uint2*>(codes + (g.C0 + cr) * (tokens >> 1) + (g.TB0 + p) * 8) =
+                *reinterpret_cast<const uint2*>(&tc[cr][p * 8]);
         }
+        if (threadIdx.x < valid_cols) {
+          const int cr = threadIdx.x;
+          uint8_t* dst = scales + (g.C0 + cr) * nbt + g.TB0;
+          if (valid_tb == kTileBlocks && ((reinterpret_cast<uintptr_t>(dst) & 15) == 0)) {
+            *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(&ts[cr][0]);
+          } else {
+            for (int p = 0; p < valid_tb; ++p) dst[p] = ts[cr][p];
+          }
+        }
+        __syncthreads();                                    // LDS reused by the next tile
       }
-      __syncthreads();                                      // LDS reused by the next tile
     }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) cur[j] = nxt[j];
+    it = it_n;
+    k = k_n;
   }
   if constexpr (!ENCODE) {
     m = block_max(m, red);
@@ -201,10 +227,30 @@ int64_t rht_tiles(int64_t tokens, int64_t cols) {
   return ((cols + kTileCols - 1) / kTileCols) * (((tokens >> 4) + kTileBlocks - 1) / kTileBlocks);
 }
 
+// Workgroups of k_rht<...> that the device keeps resident at once (each walks tiles, so a
+// grid of exactly this many has no second wave of late starters). Queried once per kernel.
+template <typename TIn, bool ENCODE, bool SR>
+int64_t resident_groups() {
+  static const int64_t n = [] {
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_rht<TIn, ENCODE, SR>, kThreads, 0) !=
+            hipSuccess)
+      return (int64_t)1024;
+    return (int64_t)(cus > 0 ? cus : 1) * (per_cu > 0 ? per_cu : 1);
+  }();
+  return n;
+}
+
 template <typename TIn, bool ENCODE, bool SR>
 void launch_rht_t(const void* x, int64_t tokens, int64_t cols, int64_t ld, uint16_t mask,
                   const float* amax, int parts, float* partial, QuantOut out, uint64_t seed,
                   uint64_t offset, int grid, hipStream_t stream) {
+  if (ENCODE) {
+    const int64_t cap = resident_groups<TIn, ENCODE, SR>();
+    if (grid > cap) grid = (int)cap;
+  }
   hipLaunchKernelGGL((k_rht<TIn, ENCODE, SR>), dim3(grid), dim3(kThreads), 0, stream,
                      (const TIn*)x, tokens, cols, ld, (uint32_t)mask, amax, parts, partial,
                      out.codes, out.scales, out.global_scale, seed, offset);
@@ -229,7 +275,7 @@ hipError_t launch_rht_encode(const void* x, bool fp32, int64_t tokens, int64_t c
                              uint16_t sign_mask, bool sr, uint64_t seed, uint64_t offset,
                              const float* amax, int parts, QuantOut out, hipStream_t stream) {
   const int64_t tiles = rht_tiles(tokens, cols);
-  const int grid = (int)(tiles < 1 ? 1 : tiles);
+  const int grid = (int)(tiles < 1 ? 1 : (tiles < (1 << 30) ? tiles : (1 << 30)));   // capped at launch
   if (fp32) {
     if (sr) launch_rht_t<float, true, true>(x, tokens, cols, ld, sign_mask, amax, parts, nullptr, out, seed, offset, grid, stream);
     else    launch_rht_t<float, true, false>(x, tokens, cols, ld, sign_mask, amax, parts, nullptr, out, seed, offset, grid, stream);

@@ -144,6 +144,35 @@ def test_rht_quantize(shape, rounding):
     assert a.cpu().numpy()[0] == oracle.amax(oracle.rht_columnwise(x, mask))[0]
 
 
+@pytest.mark.parametrize("rounding", ["rn", "sr"])
+def test_rht_exponent_spread(rounding):
+    """Blocks on both sides of the binary32 fast path's range test, plus zeros, subnormals
+    and fields up to 251, bit-exact against the oracle."""
+    log(f"rht exponent spread {rounding}")
+    bits = workloads.exponent_spread_bf16(512, 272, 77)
+    x = f32(bits)
+    mask = workloads.wgrad_sign_mask()
+    q = nv.rht_quantize(to_device_bf16(bits), mask, rounding, seed=0x5EED, offset=3)
+    ref = oracle.rht_quantize(x, mask, rounding, seed=0x5EED, offset=3)
+    assert_quant_equal(host(q), ref, f"rht spread {rounding}")
+    a = nv.amax(to_device_bf16(bits), rht=True, sign_mask=mask)
+    torch.cuda.synchronize()
+    assert a.cpu().numpy()[0] == oracle.amax(oracle.rht_columnwise(x, mask))[0]
+
+
+def test_rht_exponent_spread_per_block_amax():
+    """max |y| of single 16-token blocks (one column each): the transform's largest output
+    per block, exact against the oracle."""
+    bits = workloads.exponent_spread_bf16(16, 48, 78)
+    mask = workloads.wgrad_sign_mask()
+    for c in range(48):
+        col = np.ascontiguousarray(bits[:, c:c + 1])
+        a = nv.amax(to_device_bf16(col), rht=True, sign_mask=mask)
+        torch.cuda.synchronize()
+        want = oracle.amax(oracle.rht_columnwise(f32(col), mask))[0]
+        assert a.cpu().numpy()[0] == want, f"column {c}"
+
+
 def test_rht_fp32_masks():
     rng = np.random.default_rng(12)
     x = (rng.standard_normal((64, 40)) * 3).astype(np.float32)

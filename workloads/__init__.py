@@ -137,3 +137,30 @@ def moe(rows_w_per_expert: int = MOE_FFN, hidden: int = MOE_HIDDEN):
     x = normal_bf16((total, hidden), SEEDS["moe_x"])
     w = normal_bf16((MOE_EXPERTS * rows_w_per_expert, hidden), SEEDS["moe_w"])
     return x, w, offsets
+
+
+def exponent_spread_bf16(tokens: int, cols: int, seed: int, spreads=(0, 6, 11, 12, 13, 16, 40)) -> np.ndarray:
+    """BF16 bits [tokens, cols] built per 16-token block of each column: a top exponent field
+    F (mostly mid-range, sometimes 249..251 or very small) and a spread s drawn from `spreads`;
+    fields uniform in [F - s, F] with F present, random signs and mantissas, about 5% exact
+    zeros; fields that fall to 0 or below give subnormals. Used to exercise the range
+    boundaries of the Hadamard transform's exactness test."""
+    if tokens % 16:
+        raise ValueError("tokens must be a multiple of 16")
+    rng = np.random.default_rng(seed)
+    nb = tokens // 16
+    spread = rng.choice(np.asarray(spreads, dtype=np.int64), size=(nb, cols))
+    top = rng.integers(60, 200, size=(nb, cols))
+    edge = rng.random((nb, cols))
+    top = np.where(edge < 0.1, rng.integers(249, 252, size=(nb, cols)), top)
+    top = np.where((edge >= 0.1) & (edge < 0.15), rng.integers(1, 14, size=(nb, cols)), top)
+    field = top[:, None, :] - rng.integers(0, spread[:, None, :] + 1, size=(nb, 16, cols))
+    first = rng.integers(0, 16, size=(nb, cols))
+    field[np.arange(nb)[:, None], first, np.arange(cols)[None, :]] = top
+    field = np.clip(field, 0, 254)
+    mant = rng.integers(0, 128, size=(nb, 16, cols))
+    mant = np.where(field == 0, np.maximum(mant, 1), mant)          # field 0: nonzero subnormal
+    sign = rng.integers(0, 2, size=(nb, 16, cols))
+    bits = (sign << 15) | (field << 7) | mant
+    bits = np.where(rng.random((nb, 16, cols)) < 0.05, 0, bits)
+    return bits.reshape(tokens, cols).astype(np.uint16)
