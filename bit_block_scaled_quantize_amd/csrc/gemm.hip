@@ -148,8 +148,12 @@ __device__ __forceinline__ uint32_t k_mask4(int64_t K, int64_t k) {
          (k + 48 < K ? 0xFF000000u : 0u);
 }
 
+// One output tile over K steps [s0, s1) (128 elements each). With `accumulate` the scaled
+// partial sums are added to D with hardware float atomics (D pre-zeroed by the caller),
+// else stored.
 __device__ __forceinline__ void gemm_tile_big(Operand A, Operand B, int64_t m0, int64_t m1,
-                                              int64_t n0, int64_t n1, int64_t K, float alpha,
+                                              int64_t n0, int64_t n1, int64_t K, int64_t s0,
+                                              int64_t s1, bool accumulate, float alpha,
                                               float* __restrict__ D, int64_t ldd, uint8_t* lds) {
   using namespace big;
   const int lane = threadIdx.x & 63;
@@ -179,14 +183,13 @@ __device__ __forceinline__ void gemm_tile_big(Operand A, Operand B, int64_t m0, 
   // (the pipeline then has no branches and always the same number of operations in flight)
   // with an offset beyond every buffer's range, which the buffer unit answers with zeros
   // without touching memory; their LDS buffers are never read.
-  const int64_t steps = (K + kStepK - 1) / kStepK;
   constexpr uint32_t kBeyond = 0x80000000u;                  // > any 31-bit buffer size
   auto issue_dma_part = [&](int64_t step, int buf, int p) {
     uint8_t* base = lds + buf * kStageBytes;
     const int i = p / 3, q = p % 3;
     const bool is_a = i < 2;
     const int f = wave + 4 * i;
-    const bool live = step < steps;
+    const bool live = step < s1;
     if (q < 2) {
       const uint32_t off = (is_a ? dma_a : dma_b) + (uint32_t)(i & 1) * dma_stride +
                            (uint32_t)(step * (kStepK / 2)) + 16u * q;
@@ -251,7 +254,7 @@ __device__ __forceinline__ void gemm_tile_big(Operand A, Operand B, int64_t m0, 
   };
 
 #pragma unroll
-  for (int p = 0; p < kStages; ++p) issue_dma(p, p);
+  for (int p = 0; p < kStages; ++p) issue_dma(s0 + p, p);
   __builtin_amdgcn_s_waitcnt(0x4F78);                         // vmcnt(24): step 0 landed
   barrier();
   read_half(0, 0, ar0, br0);
@@ -271,14 +274,14 @@ __device__ __forceinline__ void gemm_tile_big(Operand A, Operand B, int64_t m0, 
   // keeps the compiler from regrouping phases.
   half8 bv[kFragsN], bn[kFragsN], av;
   {
-    const uint32_t keep0 = k_mask4(K, h * 64);
+    const uint32_t keep0 = k_mask4(K, s0 * kStepK + h * 64);
 #pragma unroll
     for (int j = 0; j < kFragsN; ++j) bv[j] = decode8(br0[j].x, pair(sb[j], keep0, 0));
     av = decode8(ar0[0].x, pair(sa[0], keep0, 0));
   }
 
   int b_cur = 0;
-  for (int64_t s = 0; s < steps; ++s) {
+  for (int64_t s = s0; s < s1; ++s) {
     const int b_next = b_cur == kStages - 1 ? 0 : b_cur + 1;
     read_half(b_cur, 1, ar1, br1);
 
@@ -345,7 +348,10 @@ __device__ __forceinline__ void gemm_tile_big(Operand A, Operand B, int64_t m0, 
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
         const int64_t row = m0 + wm * kWaveM + 32 * i + 8 * (q >> 2) + 4 * h + (q & 3);
-        if (row < m1) D[row * ldd + col] = acc[i][j][q] * alpha;
+        if (row < m1) {
+          if (accumulate) unsafeAtomicAdd(&D[row * ldd + col], acc[i][j][q] * alpha);
+          else D[row * ldd + col] = acc[i][j][q] * alpha;
+        }
       }
     }
   }
@@ -353,17 +359,44 @@ __device__ __forceinline__ void gemm_tile_big(Operand A, Operand B, int64_t m0, 
 
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_gemm_big(Operand A, const float* __restrict__ ag, Operand B, const float* __restrict__ bg,
-                int64_t K, float* __restrict__ D, int64_t ldd) {
+                int64_t K, float* __restrict__ D, int64_t ldd, int64_t tail_first, int splits) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds_dyn[];
   using namespace big;
   const int64_t tiles_m = (A.rows + kBlockM - 1) / kBlockM;
   const int64_t tiles_n = (B.rows + kBlockN - 1) / kBlockN;
+  const int64_t steps = (K + kStepK - 1) / kStepK;
+  // workgroups past tail_first share the last tiles, `splits` per tile, each over a K range
+  int64_t t = blockIdx.x, s0 = 0, s1 = steps;
+  if (t >= tail_first) {
+    const int64_t part = (t - tail_first) % splits;
+    t = tail_first + (t - tail_first) / splits;
+    s0 = steps * part / splits;
+    s1 = steps * (part + 1) / splits;
+  }
   int64_t tm, tn;
-  tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  tile_of(t, tiles_m, tiles_n, tm, tn);
   const int64_t m0 = tm * kBlockM, n0 = tn * kBlockN;
   const int64_t m1 = m0 + kBlockM < A.rows ? m0 + kBlockM : A.rows;
   const int64_t n1 = n0 + kBlockN < B.rows ? n0 + kBlockN : B.rows;
-  gemm_tile_big(A, B, m0, m1, n0, n1, K, ag[0] * bg[0], D, ldd, lds_dyn);
+  gemm_tile_big(A, B, m0, m1, n0, n1, K, s0, s1, blockIdx.x >= tail_first, ag[0] * bg[0], D, ldd,
+                lds_dyn);
+}
+
+// Zeroes the D region of tiles tail_first + blockIdx.x (the K-split tiles of k_gemm_big).
+__global__ __launch_bounds__(kThreads) void k_zero_tiles(int64_t M, int64_t N, float* __restrict__ D,
+                                                         int64_t ldd, int64_t tail_first) {
+  using namespace big;
+  const int64_t tiles_m = (M + kBlockM - 1) / kBlockM;
+  const int64_t tiles_n = (N + kBlockN - 1) / kBlockN;
+  int64_t tm, tn;
+  tile_of(tail_first + blockIdx.x, tiles_m, tiles_n, tm, tn);
+  const int64_t m0 = tm * kBlockM, n0 = tn * kBlockN;
+  const int64_t c = n0 + (threadIdx.x & 63) * 4;
+  for (int64_t r = m0 + (threadIdx.x >> 6); r < m0 + kBlockM && r < M; r += kThreads / 64) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (c + q < N) D[r * ldd + c + q] = 0.0f;
+  }
 }
 
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
@@ -380,7 +413,8 @@ void k_grouped_gemm_big(int64_t G, const int64_t* __restrict__ off, Operand A,
   const int64_t n0 = tn * kBlockN;
   const int64_t n1 = n0 + kBlockN < N ? n0 + kBlockN : N;
   const Operand Bg{B.codes + g * N * (K >> 1), B.scales + g * N * (K >> 4), N};
-  gemm_tile_big(A, Bg, m0, m1, n0, n1, K, ag[g] * bg[g], D, ldd, lds_dyn);
+  gemm_tile_big(A, Bg, m0, m1, n0, n1, K, 0, (K + kStepK - 1) / kStepK, false, ag[g] * bg[g], D, ldd,
+                lds_dyn);
 }
 
 // =========================================================================================
@@ -525,6 +559,18 @@ void k_grouped_gemm_small(int64_t G, const int64_t* __restrict__ off, Operand A,
 
 bool use_big(int64_t K) { return K > 0 && (K % 64) == 0; }
 
+// Compute units of the current device (queried once).
+int64_t compute_units() {
+  static const int64_t n = [] {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      return (int64_t)256;
+    return (int64_t)cus;
+  }();
+  return n;
+}
+
 hipError_t enable_big_lds() {
   static hipError_t once = [] {
     hipError_t e = hipFuncSetAttribute((const void*)k_gemm_big,
@@ -546,8 +592,22 @@ hipError_t launch_gemm(GemmOperand a, GemmOperand b, int64_t M, int64_t N, int64
     const hipError_t e = enable_big_lds();
     if (e != hipSuccess) return e;
     const int64_t tiles = ((M + big::kBlockM - 1) / big::kBlockM) * ((N + big::kBlockN - 1) / big::kBlockN);
-    hipLaunchKernelGGL(k_gemm_big, dim3((unsigned)tiles), dim3(kThreads), big::kLdsBytes, stream,
-                       A, a.global_scale, B, b.global_scale, K, D, ldd);
+    // One workgroup per CU: when the tiles leave a partial last round, its tiles are split
+    // along K so that round fills the machine (2-4 parts, atomically added into zeroed D).
+    const int64_t cus = compute_units();
+    const int64_t steps = (K + kStepK - 1) / kStepK;
+    const int64_t rem = tiles % cus;
+    int64_t splits = rem ? cus / rem : 1;
+    splits = splits > 4 ? 4 : splits;
+    splits = splits > steps ? steps : splits;
+    const int64_t tail_first = splits >= 2 ? tiles - rem : tiles;
+    if (splits < 2) splits = 1;
+    if (tail_first < tiles)
+      hipLaunchKernelGGL(k_zero_tiles, dim3((unsigned)(tiles - tail_first)), dim3(kThreads), 0, stream,
+                         M, N, D, ldd, tail_first);
+    const int64_t grid = tail_first + (tiles - tail_first) * splits;
+    hipLaunchKernelGGL(k_gemm_big, dim3((unsigned)grid), dim3(kThreads), big::kLdsBytes, stream,
+                       A, a.global_scale, B, b.global_scale, K, D, ldd, tail_first, (int)splits);
   } else {
     const int64_t tiles = ((M + small::kBlockM - 1) / small::kBlockM) * ((N + small::kBlockN - 1) / small::kBlockN);
     hipLaunchKernelGGL(k_gemm_small, dim3((unsigned)tiles), dim3(kThreads), 0, stream, A,
