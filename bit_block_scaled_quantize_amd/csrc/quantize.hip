@@ -342,6 +342,30 @@ struct Raw8<float> {
   }
 };
 
+// In-place transpose of an 8x8 matrix of nibbles held as 8 words (word j, nibble i =
+// element (j, i)): swap the off-diagonal 4x4 blocks (16-bit halves), then the 2x2 blocks
+// (bytes), then single nibbles; afterwards word i, nibble j = the former element (j, i).
+__device__ __forceinline__ void nibble_transpose8(uint32_t (&w)[8]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t a = w[j], b = w[j + 4];
+    w[j] = __builtin_amdgcn_perm(b, a, 0x05040100u);      // a.h0 | b.h0 << 16
+    w[j + 4] = __builtin_amdgcn_perm(b, a, 0x07060302u);  // a.h1 | b.h1 << 16
+  }
+#pragma unroll
+  for (int j : {0, 1, 4, 5}) {
+    const uint32_t a = w[j], b = w[j + 2];
+    w[j] = __builtin_amdgcn_perm(b, a, 0x06020400u);      // a.b0 b.b0 a.b2 b.b2
+    w[j + 2] = __builtin_amdgcn_perm(b, a, 0x07030501u);  // a.b1 b.b1 a.b3 b.b3
+  }
+#pragma unroll
+  for (int j = 0; j < 8; j += 2) {
+    const uint32_t a = w[j], b = w[j + 1];
+    w[j] = (a & 0x0F0F0F0Fu) | ((b & 0x0F0F0F0Fu) << 4);
+    w[j + 1] = ((a >> 4) & 0x0F0F0F0Fu) | (b & 0xF0F0F0F0u);
+  }
+}
+
 template <typename TIn, bool SEG, bool TRANS>
 __global__ __launch_bounds__(kThreads) void k_encode_16x16(
     const TIn* __restrict__ x, int64_t rows, int64_t cols, int64_t ld,
@@ -350,7 +374,7 @@ __global__ __launch_bounds__(kThreads) void k_encode_16x16(
     uint8_t* __restrict__ tcodes, uint8_t* __restrict__ tscales, float* __restrict__ tgscale) {
   __shared__ float red[kWavesPerBlock];
   __shared__ __attribute__((aligned(16))) uint8_t tc[TRANS ? kTileCols : 1][kTileRows / 2];
-  __shared__ uint8_t ts[TRANS ? kTileCols : 1][kTileRows / 16];
+  __shared__ __attribute__((aligned(16))) uint8_t ts[TRANS ? kTileCols : 1][kTileRows / 16];
 
   const int64_t tiles_c = (cols + kTileCols - 1) / kTileCols;
   const int64_t tiles_r = (rows + kTileRows - 1) / kTileRows;
@@ -404,24 +428,40 @@ __global__ __launch_bounds__(kThreads) void k_encode_16x16(
     for (int i = 0; i < 8; ++i) y[i] = v[j].get(i) * bs.mult;
     w[j] = e2m1_rn8(y);
   }
+  // The strip's 8 tile scales are the same on each of its 16 rows: gather them from the lane
+  // pairs of the 16-lane group (all lanes take part in the exchange) and let lane ht write
+  // row r0 + ht's 8-byte segment in one store when the segment is whole and aligned.
+  const int grp = lane & ~15;
+  uint32_t srow[2] = {0, 0};
+#pragma unroll
+  for (int t = 0; t < 8; ++t)
+    srow[t >> 2] |= ((uint32_t)__shfl((int)bs.code, grp + 2 * t, 64) & 0xFFu) << (8 * (t & 3));
+  const bool whole_row = (nb & 7) == 0 && C0 + kTileCols <= cols;
   if (active) {
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
+    for (int j = 0; j < 16; ++j)
       *reinterpret_cast<uint32_t*>(codes + (r0 + j) * (cols >> 1) + (c0 >> 1)) = w[j];
-      if ((ht & 1) == 0) scales[(r0 + j) * nb + (c0 >> 4)] = (uint8_t)bs.code;
+    if (whole_row) {
+      *reinterpret_cast<uint2*>(scales + (r0 + ht) * nb + (C0 >> 4)) = make_uint2(srow[0], srow[1]);
+    } else if ((ht & 1) == 0) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) scales[(r0 + j) * nb + (c0 >> 4)] = (uint8_t)bs.code;
     }
   }
   if constexpr (TRANS) {
-    // column i of this lane's piece -> row (ht*8 + i) of the transposed tile, 16 codes
+    // column i of this lane's piece -> row (ht*8 + i) of the transposed tile, 16 codes:
+    // two 8x8 nibble transposes (rows 0-7 and 8-15 of the strip)
+    uint32_t lo[8], hi[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      lo[j] = w[j];
+      hi[j] = w[j + 8];
+    }
+    nibble_transpose8(lo);
+    nibble_transpose8(hi);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      uint32_t lo = 0, hi = 0;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        lo |= ((w[j] >> (4 * i)) & 0xFu) << (4 * j);
-        hi |= ((w[j + 8] >> (4 * i)) & 0xFu) << (4 * j);
-      }
-      *reinterpret_cast<uint2*>(&tc[ht * 8 + i][strip * 8]) = make_uint2(lo, hi);
+      *reinterpret_cast<uint2*>(&tc[ht * 8 + i][strip * 8]) = make_uint2(lo[i], hi[i]);
       ts[ht * 8 + i][strip] = (uint8_t)bs.code;
     }
     __syncthreads();
@@ -439,7 +479,11 @@ __global__ __launch_bounds__(kThreads) void k_encode_16x16(
     if (threadIdx.x < kTileCols && threadIdx.x < valid_cols) {
       const int cr = threadIdx.x;
       uint8_t* dst = tscales + (C0 + cr) * (rows >> 4) + (R0 >> 4);
-      for (int sp = 0; sp < valid_strips; ++sp) dst[sp] = ts[cr][sp];
+      if (valid_strips == 16 && (reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
+        *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(&ts[cr][0]);
+      } else {
+        for (int sp = 0; sp < valid_strips; ++sp) dst[sp] = ts[cr][sp];
+      }
     }
   }
 }
