@@ -349,8 +349,10 @@ __device__ __forceinline__ void gemm_tile_big(Operand A, Operand B, int64_t m0, 
       for (int q = 0; q < 16; ++q) {
         const int64_t row = m0 + wm * kWaveM + 32 * i + 8 * (q >> 2) + 4 * h + (q & 3);
         if (row < m1) {
+          // non-temporal: D goes out to HBM while this compute-bound kernel runs instead of
+          // sitting dirty in the caches and being written back during the next kernel
           if (accumulate) unsafeAtomicAdd(&D[row * ldd + col], acc[i][j][q] * alpha);
-          else D[row * ldd + col] = acc[i][j][q] * alpha;
+          else __builtin_nontemporal_store(acc[i][j][q] * alpha, &D[row * ldd + col]);
         }
       }
     }
