@@ -595,12 +595,14 @@ hipError_t launch_gemm(GemmOperand a, GemmOperand b, int64_t M, int64_t N, int64
     if (e != hipSuccess) return e;
     const int64_t tiles = ((M + big::kBlockM - 1) / big::kBlockM) * ((N + big::kBlockN - 1) / big::kBlockN);
     // One workgroup per CU: when the tiles leave a partial last round, its tiles are split
-    // along K so that round fills the machine (2-4 parts, atomically added into zeroed D).
+    // along K in two halves atomically added into zeroed D. Two parts keep D reproducible
+    // (0 + a + b rounds the same in either order); more parts would make the rounding depend
+    // on the order the atomics land in.
     const int64_t cus = compute_units();
     const int64_t steps = (K + kStepK - 1) / kStepK;
     const int64_t rem = tiles % cus;
     int64_t splits = rem ? cus / rem : 1;
-    splits = splits > 4 ? 4 : splits;
+    splits = splits > 2 ? 2 : splits;
     splits = splits > steps ? steps : splits;
     const int64_t tail_first = splits >= 2 ? tiles - rem : tiles;
     if (splits < 2) splits = 1;

@@ -119,3 +119,18 @@ def test_grouped_gemm_ragged_groups():
     d64 = oracle.grouped_gemm_fp64(xh, wh, off, n)
     bound = oracle.grouped_gemm_bound(xh, wh, off, n)
     assert np.all(np.abs(d.cpu().numpy() - d64) <= bound)
+
+
+@pytest.mark.parametrize("mnk", [(513, 1024, 5120), (1000, 700, 1344), (2304, 2560, 1024)])
+def test_gemm_reproducible(mnk):
+    """The same GEMM twice gives bitwise identical D, also where tiles of a partial last round
+    are split along K and added into D with atomics."""
+    m, n, k = mnk
+    log(f"gemm reproducible {mnk}")
+    rng = np.random.default_rng(m + n + k)
+    qa, _ = nv.quantize(torch.from_numpy(rng.standard_normal((m, k)).astype(np.float32)).cuda(), "1x16", "rn")
+    qb, _ = nv.quantize(torch.from_numpy(rng.standard_normal((n, k)).astype(np.float32)).cuda(), "1x16", "rn")
+    d1 = nv.gemm(qa, qb)
+    d2 = nv.gemm(qa, qb)
+    torch.cuda.synchronize()
+    assert torch.equal(d1, d2)
