@@ -1,8 +1,9 @@
 """Benchmark of the NVFP4 training hot path on one MI355X.
 
 One step = the whole path of one dense linear layer (tokens 8192, in 5120, out 20480):
-  quantize X (1x16, RN) and W (16x16, RN, + transposed copy)       -> fprop GEMM
-  quantize dY (1x16, SR)                                             -> dgrad GEMM (W^T reused)
+  amax pair of X (max|X|, max|HX|); quantize X (1x16, RN) and W (16x16, RN, + transposed
+  copy)                                                              -> fprop GEMM
+  amax pair of dY; quantize dY (1x16, SR)                            -> dgrad GEMM (W^T reused)
   Hadamard-transform + quantize dY^T (SR) and X^T (RN) along tokens  -> wgrad GEMM
 `value` is the step's GEMM work (3 x 2*M*N*K) divided by the whole step time, inputs already
 resident in HBM. Per-kernel times come from HIP events on the stream the kernels run on;
@@ -33,8 +34,8 @@ M, K_IN, N_OUT = 8192, 5120, 20480
 # counter reads for the 256 MiB copy kernel of --copy-kernel. The figure belongs to the GEMM source
 # whose SHA-256 is given; once that source changes it is reported as null until measured again.
 GEMM_SOURCE = os.path.join(ROOT, "bit_block_scaled_quantize_amd", "csrc", "gemm.hip")
-GEMM_TRAFFIC = {"source_sha256": "82aa24b622ed21ba2897c2e60158fd66dfac08688f0d0dd480d8fca03263a7d2",
-                "bytes_per_launch": 1204375215}
+GEMM_TRAFFIC = {"source_sha256": "0d039ead273d7fcc0e3ce307ce0e5eb707bdd9c7270ceb392dd59d8944c501d3",
+                "bytes_per_launch": 1206440399}
 
 
 def parse():
@@ -89,24 +90,33 @@ def main():
     Y = torch.empty((M, N_OUT), dtype=torch.float32, device=dev)
     dX = torch.empty((M, K_IN), dtype=torch.float32, device=dev)
     dW = torch.empty((N_OUT, K_IN), dtype=torch.float32, device=dev)
-    ws = torch.empty((4096,), dtype=torch.uint8, device=dev)
+    ws = torch.empty((8192,), dtype=torch.uint8, device=dev)
     flush = torch.empty((512 << 20,), dtype=torch.uint8, device=dev)
+    amax_xx = torch.empty((2,), dtype=torch.float32, device=dev)      # max|X|, max|H X|
+    amax_dd = torch.empty((2,), dtype=torch.float32, device=dev)      # max|dY|, max|H dY|
 
+    # X and dY are each quantized twice (rowwise for fprop/dgrad, Hadamard-transformed and
+    # transposed for wgrad); one amax_pair read of each gives both tensor scales, so those
+    # four quantize calls are single encode passes. W (one use) takes the two-pass call.
     stages = [
-        ("quantize_x_1x16_rn", lambda: nv.quantize(X, "1x16", "rn", out=Xq, workspace=ws)),
+        ("amax_pair_x", lambda: nv.amax_pair(X, mask, out=amax_xx, workspace=ws)),
+        ("quantize_x_1x16_rn", lambda: nv.quantize(X, "1x16", "rn", out=Xq, amax=amax_xx[0:1])),
         ("quantize_w_16x16_rn_t", lambda: nv.quantize(W, "16x16", "rn", emit_transposed=True,
                                                       out=Wq, out_t=WqT, workspace=ws)),
         ("gemm_fprop", lambda: nv.gemm(Xq, Wq, out=Y)),
+        ("amax_pair_dy", lambda: nv.amax_pair(dY, mask, out=amax_dd, workspace=ws)),
         ("quantize_dy_1x16_sr", lambda: nv.quantize(dY, "1x16", "sr", seed=workloads.SR_SEED_DGRAD,
-                                                    offset=0, out=dYq, workspace=ws)),
+                                                    offset=0, out=dYq, amax=amax_dd[0:1])),
         ("gemm_dgrad", lambda: nv.gemm(dYq, WqT, out=dX)),
         ("rht_quantize_dy_sr", lambda: nv.rht_quantize(dY, mask, "sr", seed=workloads.SR_SEED_WGRAD,
                                                        offset=workloads.SR_OFFSET_WGRAD, out=dYtq,
-                                                       workspace=ws)),
-        ("rht_quantize_x_rn", lambda: nv.rht_quantize(X, mask, "rn", out=Xtq, workspace=ws)),
+                                                       amax=amax_dd[1:2])),
+        ("rht_quantize_x_rn", lambda: nv.rht_quantize(X, mask, "rn", out=Xtq, amax=amax_xx[1:2])),
         ("gemm_wgrad", lambda: nv.gemm(dYtq, Xtq, out=dW)),
     ]
     work = {
+        "amax_pair_x": ("GB/s", M * K_IN * 2),
+        "amax_pair_dy": ("GB/s", M * N_OUT * 2),
         "quantize_x_1x16_rn": ("GB/s", q_bytes(M, K_IN)),
         "quantize_w_16x16_rn_t": ("GB/s", q_bytes(N_OUT, K_IN, transposed=True)),
         "quantize_dy_1x16_sr": ("GB/s", q_bytes(M, N_OUT)),
@@ -165,9 +175,9 @@ def main():
     # --- cold-cache timing of each quantize call (inputs in HBM, caches holding other data) --
     # Before every timed call a 512 MB buffer (written once, up front) is read, which evicts the
     # 256 MB Infinity Cache and the L2s without leaving dirty lines whose write-back would
-    # overlap the timed kernel. Each call is timed three ways: the whole two-pass call, the
-    # encode pass alone (tensor amax supplied, the pass the HBM roofline applies to), and the
-    # amax pass alone.
+    # overlap the timed kernel. Each quantize is timed three ways: the stand-alone two-pass call
+    # (workspace, no amax_in), the encode pass alone (tensor amax supplied, the pass the HBM
+    # roofline applies to), and its amax pass alone; the step's amax_pair calls are timed too.
     flush.fill_(1)
     fsum = torch.empty((1,), dtype=torch.int64, device=dev)
 
@@ -185,6 +195,17 @@ def main():
 
     amx_x, amx_w, amx_dy = nv.amax(X), nv.amax(W), nv.amax(dY)
     ramx_dy, ramx_x = nv.amax(dY, rht=True, sign_mask=mask), nv.amax(X, rht=True, sign_mask=mask)
+    two_pass = {
+        "quantize_x_1x16_rn": lambda: nv.quantize(X, "1x16", "rn", out=Xq, workspace=ws),
+        "quantize_w_16x16_rn_t": lambda: nv.quantize(W, "16x16", "rn", emit_transposed=True,
+                                                     out=Wq, out_t=WqT, workspace=ws),
+        "quantize_dy_1x16_sr": lambda: nv.quantize(dY, "1x16", "sr", seed=workloads.SR_SEED_DGRAD,
+                                                   offset=0, out=dYq, workspace=ws),
+        "rht_quantize_dy_sr": lambda: nv.rht_quantize(dY, mask, "sr", seed=workloads.SR_SEED_WGRAD,
+                                                      offset=workloads.SR_OFFSET_WGRAD, out=dYtq,
+                                                      workspace=ws),
+        "rht_quantize_x_rn": lambda: nv.rht_quantize(X, mask, "rn", out=Xtq, workspace=ws),
+    }
     encode_only = {
         "quantize_x_1x16_rn": lambda: nv.quantize(X, "1x16", "rn", out=Xq, amax=amx_x),
         "quantize_w_16x16_rn_t": lambda: nv.quantize(W, "16x16", "rn", emit_transposed=True,
@@ -204,15 +225,16 @@ def main():
         "rht_quantize_x_rn": (lambda: nv.amax(X, rht=True, sign_mask=mask, workspace=ws), M * K_IN * 2),
     }
     cold = {}
-    for name, fn in stages:
-        if work[name][0] != "GB/s":
-            continue
+    for name, fn in two_pass.items():
         row = {"two_pass": rate(name, cold_ms(fn)), "encode_pass": rate(name, cold_ms(encode_only[name]))}
         afn, abytes = amax_only[name]
         ams = cold_ms(afn)
         av = abytes / (ams * 1e-3) / 1e9
         row["amax_pass"] = {"us": round(ams * 1e3, 2), "GB/s": round(av, 1), "frac_hbm": round(av / HBM_PEAK_GBS, 4)}
         cold[name] = row
+    for name, fn in stages:
+        if name.startswith("amax_pair"):
+            cold[name] = rate(name, cold_ms(fn))
 
     gemm_names = ["gemm_fprop", "gemm_dgrad", "gemm_wgrad"]
     gemm_avg_ms = float(np.mean([stage_ms[n] for n in gemm_names]))

@@ -6,7 +6,7 @@ returns; all arithmetic runs in the HIP kernels. If the library is not built the
 still succeeds but every call raises, so nothing can silently fall back to another path.
 
 Names follow the C entry points: quantize, rht_quantize, gemm, grouped_gemm, amax,
-dequantize.
+amax_pair, dequantize.
 """
 from __future__ import annotations
 
@@ -24,10 +24,11 @@ _STATUS = {-1: "invalid argument", -2: "unsupported", -3: "workspace", -4: "HIP 
 _DTYPE = {torch.bfloat16: 0, torch.float32: 1}
 _BLOCK = {"1x16": 0, "16x16": 1}
 _ROUND = {"rn": 0, "sr": 1}
-OP_QUANTIZE, OP_RHT_QUANTIZE, OP_GEMM, OP_GROUPED_GEMM = 0, 1, 2, 3
+OP_QUANTIZE, OP_RHT_QUANTIZE, OP_GEMM, OP_GROUPED_GEMM, OP_AMAX_PAIR = 0, 1, 2, 3, 4
 
 EXPORTED = ("nvfp4_quantize", "nvfp4_rht_quantize", "nvfp4_gemm", "nvfp4_grouped_gemm",
-            "nvfp4_amax", "nvfp4_workspace_size", "nvfp4_last_error", "nvfp4_dequantize")
+            "nvfp4_amax", "nvfp4_amax_pair", "nvfp4_workspace_size", "nvfp4_last_error",
+            "nvfp4_dequantize")
 
 
 class NVFP4Error(RuntimeError):
@@ -60,6 +61,7 @@ def _load():
     lib.nvfp4_grouped_gemm.argtypes = [i64, vp, pt, pt, i64, vp, i64, vp, sz, vp]
     lib.nvfp4_amax.argtypes = [vp, ctypes.c_int, i64, i64, i64, vp, i64, ctypes.c_int,
                                ctypes.c_uint16, vp, vp, sz, vp]
+    lib.nvfp4_amax_pair.argtypes = [vp, ctypes.c_int, i64, i64, i64, ctypes.c_uint16, vp, vp, sz, vp]
     lib.nvfp4_workspace_size.argtypes = [ctypes.c_int, i64, i64, i64]
     lib.nvfp4_workspace_size.restype = sz
     lib.nvfp4_last_error.restype = ctypes.c_char_p
@@ -221,6 +223,22 @@ def amax(x: torch.Tensor, segments: torch.Tensor | None = None, rht: bool = Fals
         ws_n = workspace.numel()
     _check(lib.nvfp4_amax(_ptr(x), dt, rows, cols, ld, _ptr(segments), nseg, int(rht),
                           sign_mask & 0xFFFF, _ptr(out), _ptr(workspace), ws_n, _stream(stream)))
+    return out
+
+
+def amax_pair(x: torch.Tensor, sign_mask: int, out: torch.Tensor | None = None,
+              workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """nvfp4_amax_pair: float32 [2] = (max|x|, max of the Hadamard-transformed tensor)."""
+    lib = _load()
+    dt, tokens, cols, ld = _input(x)
+    if out is None:
+        out = torch.empty((2,), dtype=torch.float32, device=x.device)
+    if workspace is None:
+        workspace, ws_n = _workspace(OP_AMAX_PAIR, tokens, cols, 1, x.device)
+    else:
+        ws_n = workspace.numel()
+    _check(lib.nvfp4_amax_pair(_ptr(x), dt, tokens, cols, ld, sign_mask & 0xFFFF, _ptr(out),
+                               _ptr(workspace), ws_n, _stream(stream)))
     return out
 
 

@@ -80,6 +80,7 @@ size_t nvfp4_workspace_size(int op, int64_t rows, int64_t cols, int64_t nseg) {
       return round_up(segs > partials ? segs : partials, kWsAlign);
     }
     case NVFP4_OP_RHT_QUANTIZE: return round_up(partials, kWsAlign);
+    case NVFP4_OP_AMAX_PAIR: return round_up(2 * partials, kWsAlign);
     default: return 0;
   }
 }
@@ -105,7 +106,7 @@ int nvfp4_amax(const void* x, nvfp4_dtype dt, int64_t rows, int64_t cols, int64_
   int parts = 1;
   if (rht) {
     float* ws = static_cast<float*>(workspace);
-    if ((st = hip_status(nvfp4::launch_rht_amax_parts(x, f32, rows, cols, ld, sign_mask, ws, &parts, s), "rht amax"))) return st;
+    if ((st = hip_status(nvfp4::launch_rht_amax_parts(x, f32, rows, cols, ld, sign_mask, false, ws, &parts, s), "rht amax"))) return st;
     return hip_status(nvfp4::launch_reduce_partials(ws, parts, amax_out, s), "amax reduce");
   }
   if (segments)
@@ -113,6 +114,26 @@ int nvfp4_amax(const void* x, nvfp4_dtype dt, int64_t rows, int64_t cols, int64_
   float* ws = static_cast<float*>(workspace);
   if ((st = hip_status(nvfp4::launch_amax_parts(x, f32, rows, cols, ld, nullptr, 1, ws, &parts, s), "amax"))) return st;
   return hip_status(nvfp4::launch_reduce_partials(ws, parts, amax_out, s), "amax reduce");
+}
+
+int nvfp4_amax_pair(const void* x, nvfp4_dtype dt, int64_t tokens, int64_t cols, int64_t ld,
+                    uint16_t sign_mask, float* amax_out, void* workspace, size_t ws_bytes,
+                    void* hip_stream) {
+  int st = check_input(x, dt, tokens, cols, ld, false);
+  if (st) return st;
+  if (!amax_out) return fail(NVFP4_ERR_INVALID, "amax_out is NULL");
+  if (tokens % 16) return fail(NVFP4_ERR_INVALID, "tokens (%lld) must be a multiple of 16", (long long)tokens);
+  const size_t need = nvfp4_workspace_size(NVFP4_OP_AMAX_PAIR, tokens, cols, 1);
+  if (!workspace || ws_bytes < need || !aligned(workspace, kWsAlign))
+    return fail(NVFP4_ERR_WORKSPACE, "workspace of %zu bytes (256-byte aligned) required, got %zu", need, ws_bytes);
+  hipStream_t s = (hipStream_t)hip_stream;
+  float* ws = static_cast<float*>(workspace);
+  int parts = 1;
+  if ((st = hip_status(nvfp4::launch_rht_amax_parts(x, dt == NVFP4_IN_FP32, tokens, cols, ld, sign_mask,
+                                                    true, ws, &parts, s), "amax pair")))
+    return st;
+  // partials [0, parts) of |x| and [parts, 2 parts) of |Hx| fold into amax_out[0] and [1]
+  return hip_status(nvfp4::launch_reduce_partials(ws, parts, amax_out, s, 2), "amax reduce");
 }
 
 int nvfp4_quantize(const void* x, nvfp4_dtype dt, int64_t rows, int64_t cols, int64_t ld,
@@ -176,7 +197,7 @@ int nvfp4_rht_quantize(const void* x, nvfp4_dtype dt, int64_t tokens, int64_t co
   int parts = 1;
   if (!amax) {
     float* ws = static_cast<float*>(workspace);
-    if ((st = hip_status(nvfp4::launch_rht_amax_parts(x, f32, tokens, cols, ld, sign_mask, ws, &parts, s), "rht amax"))) return st;
+    if ((st = hip_status(nvfp4::launch_rht_amax_parts(x, f32, tokens, cols, ld, sign_mask, false, ws, &parts, s), "rht amax"))) return st;
     amax = ws;
   }
   const nvfp4::QuantOut q{out->codes, out->scales, out->global_scale};

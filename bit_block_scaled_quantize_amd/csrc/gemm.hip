@@ -384,20 +384,32 @@ void k_gemm_big(Operand A, const float* __restrict__ ag, Operand B, const float*
                 lds_dyn);
 }
 
-// Zeroes the D region of tiles tail_first + blockIdx.x (the K-split tiles of k_gemm_big).
+// Zeroes the D region of the K-split tiles tail_first, tail_first + 1, ... of k_gemm_big:
+// workgroup b clears rows 16 * (b % kZeroParts) .. +15 of tile tail_first + b / kZeroParts, one
+// 16-byte store per lane and row where the row stride and D allow it.
+constexpr int kZeroParts = big::kBlockM / 16;
+
 __global__ __launch_bounds__(kThreads) void k_zero_tiles(int64_t M, int64_t N, float* __restrict__ D,
-                                                         int64_t ldd, int64_t tail_first) {
+                                                         int64_t ldd, int64_t tail_first, int vec) {
   using namespace big;
   const int64_t tiles_m = (M + kBlockM - 1) / kBlockM;
   const int64_t tiles_n = (N + kBlockN - 1) / kBlockN;
   int64_t tm, tn;
-  tile_of(tail_first + blockIdx.x, tiles_m, tiles_n, tm, tn);
-  const int64_t m0 = tm * kBlockM, n0 = tn * kBlockN;
-  const int64_t c = n0 + (threadIdx.x & 63) * 4;
-  for (int64_t r = m0 + (threadIdx.x >> 6); r < m0 + kBlockM && r < M; r += kThreads / 64) {
+  tile_of(tail_first + blockIdx.x / kZeroParts, tiles_m, tiles_n, tm, tn);
+  const int64_t r0 = tm * kBlockM + (blockIdx.x % kZeroParts) * 16;
+  const int64_t c = tn * kBlockN + (threadIdx.x & 63) * 4;
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      if (c + q < N) D[r * ldd + c + q] = 0.0f;
+  for (int i = 0; i < 16 / (kThreads / 64); ++i) {
+    const int64_t r = r0 + (threadIdx.x >> 6) + i * (kThreads / 64);
+    if (r >= M) break;
+    float* p = D + r * ldd + c;
+    if (vec && c + 3 < N) {
+      *reinterpret_cast<float4*>(p) = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (c + q < N) p[q] = 0.0f;
+    }
   }
 }
 
@@ -606,9 +618,11 @@ hipError_t launch_gemm(GemmOperand a, GemmOperand b, int64_t M, int64_t N, int64
     splits = splits > steps ? steps : splits;
     const int64_t tail_first = splits >= 2 ? tiles - rem : tiles;
     if (splits < 2) splits = 1;
-    if (tail_first < tiles)
-      hipLaunchKernelGGL(k_zero_tiles, dim3((unsigned)(tiles - tail_first)), dim3(kThreads), 0, stream,
-                         M, N, D, ldd, tail_first);
+    if (tail_first < tiles) {
+      const int vec = (ldd % 4) == 0 && (reinterpret_cast<uintptr_t>(D) % 16) == 0;
+      hipLaunchKernelGGL(k_zero_tiles, dim3((unsigned)((tiles - tail_first) * kZeroParts)), dim3(kThreads), 0,
+                         stream, M, N, D, ldd, tail_first, vec);
+    }
     const int64_t grid = tail_first + (tiles - tail_first) * splits;
     hipLaunchKernelGGL(k_gemm_big, dim3((unsigned)grid), dim3(kThreads), big::kLdsBytes, stream,
                        A, a.global_scale, B, b.global_scale, K, D, ldd, tail_first, (int)splits);

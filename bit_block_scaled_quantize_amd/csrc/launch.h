@@ -20,8 +20,9 @@ hipError_t launch_amax_parts(const void* x, bool fp32, int64_t rows, int64_t col
                              const int64_t* segments, int64_t nseg, float* amax_out, int* parts,
                              hipStream_t stream);
 
-// out[0] = max of partial[0..parts).
-hipError_t launch_reduce_partials(const float* partial, int parts, float* out, hipStream_t stream);
+// out[i] = max of partial[i*parts .. (i+1)*parts) for i < count.
+hipError_t launch_reduce_partials(const float* partial, int parts, float* out, hipStream_t stream,
+                                  int count = 1);
 
 hipError_t launch_encode_1x16(const void* x, bool fp32, int64_t rows, int64_t cols, int64_t ld,
                               bool sr, uint64_t seed, uint64_t offset,
@@ -32,10 +33,12 @@ hipError_t launch_encode_16x16(const void* x, bool fp32, int64_t rows, int64_t c
                                const int64_t* segments, int64_t nseg, const float* amax, int parts,
                                QuantOut out, const QuantOut* out_t, hipStream_t stream);
 
-// Hadamard transform along tokens: partial maxima of the transformed tensor (at most 1024),
-// and the transposed encode.
+// Hadamard transform along tokens: partial maxima of the transformed tensor (at most 1024;
+// with `plain`, *parts partial maxima of |x| itself come first, then those of the transformed
+// tensor), and the transposed encode.
 hipError_t launch_rht_amax_parts(const void* x, bool fp32, int64_t tokens, int64_t cols, int64_t ld,
-                                 uint16_t sign_mask, float* partial, int* parts, hipStream_t stream);
+                                 uint16_t sign_mask, bool plain, float* partial, int* parts,
+                                 hipStream_t stream);
 
 hipError_t launch_rht_encode(const void* x, bool fp32, int64_t tokens, int64_t cols, int64_t ld,
                              uint16_t sign_mask, bool sr, uint64_t seed, uint64_t offset,

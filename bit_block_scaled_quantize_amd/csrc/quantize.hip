@@ -145,13 +145,15 @@ __global__ void k_fill(float* __restrict__ p, int64_t n, float v) {
     p[i] = v;
 }
 
+// Workgroup i folds the i-th array of `parts` partial maxima into out[i].
 __global__ __launch_bounds__(kThreads) void k_reduce_partials(const float* __restrict__ partial,
                                                               int parts, float* __restrict__ out) {
   __shared__ float red[kWavesPerBlock];
+  const float* p = partial + (int64_t)blockIdx.x * parts;
   float m = 0.0f;
-  for (int i = threadIdx.x; i < parts; i += kThreads) m = fmaxf(m, partial[i]);
+  for (int i = threadIdx.x; i < parts; i += kThreads) m = fmaxf(m, p[i]);
   m = block_max(m, red);
-  if (threadIdx.x == 0) out[0] = m;
+  if (threadIdx.x == 0) out[blockIdx.x] = m;
 }
 
 // Tensor amax seen by an encode workgroup: either amax[seg] directly (parts == 1) or the
@@ -550,8 +552,9 @@ hipError_t launch_amax_parts(const void* x, bool fp32, int64_t rows, int64_t col
   return hipGetLastError();
 }
 
-hipError_t launch_reduce_partials(const float* partials, int parts, float* out, hipStream_t stream) {
-  hipLaunchKernelGGL(k_reduce_partials, dim3(1), dim3(kThreads), 0, stream, partials, parts, out);
+hipError_t launch_reduce_partials(const float* partials, int parts, float* out, hipStream_t stream,
+                                  int count) {
+  hipLaunchKernelGGL(k_reduce_partials, dim3(count), dim3(kThreads), 0, stream, partials, parts, out);
   return hipGetLastError();
 }
 

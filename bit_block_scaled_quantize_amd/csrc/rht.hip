@@ -18,7 +18,9 @@
 // requests the 16 rows of its next token block before transforming the current one, across
 // tile boundaries too. Codes and scales are staged in LDS as [column][token block] and written
 // out as 128-byte row segments of the transposed tensor. The amax variant walks the same tiles
-// and leaves one partial maximum per workgroup.
+// and leaves one partial maximum per workgroup; its PLAIN form also keeps max|x| of the
+// untransformed input (a second array of partials), so one read of a tensor gives the tensor
+// scales of both its rowwise and its Hadamard quantization.
 #include "device_common.h"
 #include "launch.h"
 
@@ -95,7 +97,7 @@ __device__ __forceinline__ float block_max(float m, float* red) {
   return r;
 }
 
-template <typename TIn, bool ENCODE, bool SR>
+template <typename TIn, bool ENCODE, bool SR, bool PLAIN = false>
 __global__ __launch_bounds__(kThreads) void k_rht(
     const TIn* __restrict__ x, int64_t tokens, int64_t cols, int64_t ld, uint32_t mask,
     const float* __restrict__ amax, int amax_parts, float* __restrict__ partial,
@@ -148,7 +150,7 @@ __global__ __launch_bounds__(kThreads) void k_rht(
     if (blockIdx.x == 0 && threadIdx.x == 0) gscale[0] = tensor_decode_scale(a);
   }
 
-  float m = 0.0f;
+  float m = 0.0f, mp = 0.0f;                                // max|Hx|, max|x| (PLAIN)
   while (it < tiles) {                                      // uniform across the workgroup
     int64_t it_n = it;
     int k_n = k + 1;
@@ -168,12 +170,20 @@ __global__ __launch_bounds__(kThreads) void k_rht(
         float v[16], y[16];
 #pragma unroll
         for (int j = 0; j < 16; ++j) v[j] = cur[j].get(q);
+        float pm = 0.0f;
+        if constexpr (PLAIN) {
+#pragma unroll
+          for (int j = 0; j < 16; ++j) pm = fmaxf(pm, fabsf(v[j]));
+        }
         rht16<TIn>(v, mask, y);
         float bm = 0.0f;
 #pragma unroll
         for (int i = 0; i < 16; ++i) bm = fmaxf(bm, fabsf(y[i]));
         if constexpr (!ENCODE) {
-          if (c + q < cols) m = fmaxf(m, bm);
+          if (c + q < cols) {
+            m = fmaxf(m, bm);
+            if constexpr (PLAIN) mp = fmaxf(mp, pm);
+          }
         } else {
           const int64_t row = c + q;                        // output row = input column
           const BlockScale bs = block_scale(bm, s_enc);
@@ -219,7 +229,15 @@ __global__ __launch_bounds__(kThreads) void k_rht(
   }
   if constexpr (!ENCODE) {
     m = block_max(m, red);
-    if (threadIdx.x == 0) partial[blockIdx.x] = m;
+    if constexpr (PLAIN) {                                  // [max|x| partials][max|Hx| partials]
+      mp = block_max(mp, red);
+      if (threadIdx.x == 0) {
+        partial[blockIdx.x] = mp;
+        partial[gridDim.x + blockIdx.x] = m;
+      }
+    } else {
+      if (threadIdx.x == 0) partial[blockIdx.x] = m;
+    }
   }
 }
 
@@ -243,7 +261,7 @@ int64_t resident_groups() {
   return n;
 }
 
-template <typename TIn, bool ENCODE, bool SR>
+template <typename TIn, bool ENCODE, bool SR, bool PLAIN = false>
 void launch_rht_t(const void* x, int64_t tokens, int64_t cols, int64_t ld, uint16_t mask,
                   const float* amax, int parts, float* partial, QuantOut out, uint64_t seed,
                   uint64_t offset, int grid, hipStream_t stream) {
@@ -251,7 +269,7 @@ void launch_rht_t(const void* x, int64_t tokens, int64_t cols, int64_t ld, uint1
     const int64_t cap = resident_groups<TIn, ENCODE, SR>();
     if (grid > cap) grid = (int)cap;
   }
-  hipLaunchKernelGGL((k_rht<TIn, ENCODE, SR>), dim3(grid), dim3(kThreads), 0, stream,
+  hipLaunchKernelGGL((k_rht<TIn, ENCODE, SR, PLAIN>), dim3(grid), dim3(kThreads), 0, stream,
                      (const TIn*)x, tokens, cols, ld, (uint32_t)mask, amax, parts, partial,
                      out.codes, out.scales, out.global_scale, seed, offset);
 }
@@ -259,14 +277,15 @@ void launch_rht_t(const void* x, int64_t tokens, int64_t cols, int64_t ld, uint1
 }  // namespace
 
 hipError_t launch_rht_amax_parts(const void* x, bool fp32, int64_t tokens, int64_t cols, int64_t ld,
-                                 uint16_t sign_mask, float* partial, int* parts, hipStream_t stream) {
+                                 uint16_t sign_mask, bool plain, float* partial, int* parts,
+                                 hipStream_t stream) {
   const int64_t tiles = rht_tiles(tokens, cols);
   const int grid = (int)(tiles < 1 ? 1 : (tiles < kMaxPartials ? tiles : kMaxPartials));
   const QuantOut none{nullptr, nullptr, nullptr};
-  if (fp32)
-    launch_rht_t<float, false, false>(x, tokens, cols, ld, sign_mask, nullptr, 0, partial, none, 0, 0, grid, stream);
-  else
-    launch_rht_t<uint16_t, false, false>(x, tokens, cols, ld, sign_mask, nullptr, 0, partial, none, 0, 0, grid, stream);
+#define NVFP4_RA(T, P) launch_rht_t<T, false, false, P>(x, tokens, cols, ld, sign_mask, nullptr, 0, partial, none, 0, 0, grid, stream)
+  if (fp32) { if (plain) NVFP4_RA(float, true); else NVFP4_RA(float, false); }
+  else      { if (plain) NVFP4_RA(uint16_t, true); else NVFP4_RA(uint16_t, false); }
+#undef NVFP4_RA
   *parts = grid;
   return hipGetLastError();
 }

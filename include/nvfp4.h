@@ -58,7 +58,7 @@ typedef enum { NVFP4_BLOCK_1X16 = 0, NVFP4_BLOCK_16X16 = 1 } nvfp4_block;
 typedef enum { NVFP4_ROUND_RN = 0, NVFP4_ROUND_SR = 1 } nvfp4_round;
 typedef enum {
   NVFP4_OP_QUANTIZE = 0, NVFP4_OP_RHT_QUANTIZE = 1, NVFP4_OP_GEMM = 2,
-  NVFP4_OP_GROUPED_GEMM = 3
+  NVFP4_OP_GROUPED_GEMM = 3, NVFP4_OP_AMAX_PAIR = 4
 } nvfp4_op;
 
 typedef struct nvfp4_tensor {
@@ -174,6 +174,26 @@ int nvfp4_grouped_gemm(int64_t G, const int64_t* m_offsets, const nvfp4_tensor* 
 int nvfp4_amax(const void* x, nvfp4_dtype dt, int64_t rows, int64_t cols, int64_t ld,
                const int64_t* segments, int64_t nseg, int rht, uint16_t sign_mask,
                float* amax_out, void* workspace, size_t ws_bytes, void* hip_stream);
+
+/*
+ * nvfp4_amax_pair - both tensor maxima of x[tokens, cols] (row stride ld) from one read:
+ * amax_out[0] = max|x| (the tensor scale of its 1x16 quantization, as nvfp4_amax with
+ * rht = 0) and amax_out[1] = max|y| over the Hadamard-transformed tensor of
+ * nvfp4_rht_quantize with this sign_mask (as nvfp4_amax with rht = 1). A tensor that feeds
+ * both an fprop/dgrad GEMM and the wgrad GEMM is quantized both ways ("Nemotron NVFP4"
+ * explainer, "Why 4-bit training normally falls apart - and the three fixes": only the wgrad
+ * operands are transformed); each value can be passed as amax_in of the matching quantize.
+ *   x          device, BF16 or FP32; tokens % 16 == 0; element pairs aligned (ld any).
+ *   amax_out   device float[2].
+ *   workspace  device scratch of nvfp4_workspace_size(NVFP4_OP_AMAX_PAIR, ...) bytes,
+ *              256-byte aligned.
+ * Both values are exact maxima, so they equal the two nvfp4_amax results bit for bit.
+ * Errors: NVFP4_ERR_INVALID (NULL pointer, bad dtype/shape, tokens % 16 != 0),
+ * NVFP4_ERR_UNSUPPORTED (misaligned x), NVFP4_ERR_WORKSPACE, NVFP4_ERR_HIP.
+ */
+int nvfp4_amax_pair(const void* x, nvfp4_dtype dt, int64_t tokens, int64_t cols, int64_t ld,
+                    uint16_t sign_mask, float* amax_out, void* workspace, size_t ws_bytes,
+                    void* hip_stream);
 
 /* Bytes of device workspace `op` needs for the given shape (0 if none). */
 size_t nvfp4_workspace_size(int op, int64_t rows, int64_t cols, int64_t nseg);

@@ -87,6 +87,18 @@ def test_rht_validation(lib):
     assert f(FAKE, 0, 32, 64, 64, 0, 0, 0, 0, None, ctypes.byref(out), None, 0, None) == WORKSPACE
 
 
+def test_amax_pair_validation(lib):
+    f = lib.nvfp4_amax_pair
+    assert f(None, 0, 32, 64, 64, 0, FAKE, FAKE, 8192, None) == INVALID
+    assert f(FAKE, 0, 30, 64, 64, 0, FAKE, FAKE, 8192, None) == INVALID     # tokens % 16
+    assert f(FAKE, 0, 32, 64, 64, 0, None, FAKE, 8192, None) == INVALID     # amax_out
+    assert f(FAKE, 2, 32, 64, 64, 0, FAKE, FAKE, 8192, None) == INVALID     # dtype
+    assert f(FAKE, 0, 32, 64, 60, 0, FAKE, FAKE, 8192, None) == INVALID     # ld < cols
+    assert f(FAKE, 0, 32, 64, 64, 0, FAKE, None, 0, None) == WORKSPACE
+    assert f(FAKE, 0, 32, 64, 64, 0, FAKE, FAKE, 4096, None) == WORKSPACE   # needs two arrays
+    assert f(FAKE + 2, 0, 32, 64, 64, 0, FAKE, FAKE, 8192, None) == UNSUPPORTED
+
+
 def test_gemm_validation(lib):
     a, b = _tensor(64, 128), _tensor(32, 128)
     g = lib.nvfp4_gemm
@@ -105,6 +117,7 @@ def test_workspace_sizes(lib):
     assert lib.nvfp4_workspace_size(nv.OP_QUANTIZE, 10, 16, 1) == 4096      # 1024 partial maxima
     assert lib.nvfp4_workspace_size(nv.OP_QUANTIZE, 10, 16, 2000) == 8192   # one slot per segment
     assert lib.nvfp4_workspace_size(nv.OP_RHT_QUANTIZE, 16, 16, 1) == 4096
+    assert lib.nvfp4_workspace_size(nv.OP_AMAX_PAIR, 16, 16, 1) == 8192
     assert lib.nvfp4_workspace_size(nv.OP_GEMM, 16, 16, 1) == 0
     assert lib.nvfp4_workspace_size(nv.OP_GROUPED_GEMM, 16, 16, 1) == 0
 

@@ -76,6 +76,14 @@ def test_gemm_output_row_stride_and_sr_operand():
     o = out.cpu().numpy()
     assert np.all(o[:, 90:] == -7.0)
     assert_gemm_within_bound(o[:, :90], ah, bh, "gemm ldd")
+    # odd row stride and a D that is not 16-byte aligned (the K-split tile is zeroed by
+    # scalar stores), neighbours untouched
+    out2 = torch.full((70, 131), -7.0, dtype=torch.float32, device="cuda")
+    nv.gemm(qa, qb, out=out2[:, 1:91])
+    torch.cuda.synchronize()
+    o2 = out2.cpu().numpy()
+    assert np.all(o2[:, 0] == -7.0) and np.all(o2[:, 91:] == -7.0)
+    assert np.array_equal(o2[:, 1:91], o[:, :90])
 
 
 def test_gemm_zero_and_one_hot():

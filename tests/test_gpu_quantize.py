@@ -173,6 +173,33 @@ def test_rht_exponent_spread_per_block_amax():
         assert a.cpu().numpy()[0] == want, f"column {c}"
 
 
+@pytest.mark.parametrize("shape,dtype,ld", [((16, 1), "bf16", 1), ((48, 513), "bf16", 514),
+                                            ((256, 129), "fp32", 129), ((512, 272), "bf16", 272),
+                                            ((4096, 1040), "bf16", 1040)])
+def test_amax_pair(shape, dtype, ld):
+    """nvfp4_amax_pair equals max|x| and max|Hx| of the oracle, and the two single maxima of
+    the library, bit for bit (ragged column tiles, odd row strides, FP32 input)."""
+    log(f"amax pair {shape} {dtype} ld={ld}")
+    tokens, cols = shape
+    bits = workloads.exponent_spread_bf16(tokens, ld, 90 + cols) if cols >= 16 else _bits((tokens, ld), 91)
+    full = f32(bits)
+    x = np.ascontiguousarray(full[:, :cols])
+    mask = workloads.wgrad_sign_mask()
+    if dtype == "bf16":
+        dev = to_device_bf16(bits)[:, :cols]
+    else:
+        dev = to_device_f32(full)[:, :cols]
+    got = nv.amax_pair(dev, mask)
+    hx = nv.amax(dev, rht=True, sign_mask=mask)
+    torch.cuda.synchronize()
+    g = got.cpu().numpy()
+    want = np.array([oracle.amax(x)[0], oracle.amax(oracle.rht_columnwise(x, mask))[0]], np.float32)
+    assert_bytes_equal(g.view(np.uint32), want.view(np.uint32), f"amax pair {shape}")
+    assert g[1] == hx.cpu().numpy()[0]
+    if cols % 16 == 0 and ld % (8 if dtype == "bf16" else 4) == 0:   # the rowwise amax's layout
+        assert g[0] == nv.amax(dev).cpu().numpy()[0]
+
+
 def test_rht_fp32_masks():
     rng = np.random.default_rng(12)
     x = (rng.standard_normal((64, 40)) * 3).astype(np.float32)
