@@ -24,7 +24,10 @@
 //    FP32 accumulators per lane in AGPRs). Per 128-wide K step the workgroup's FP4 panels
 //    (2 x 16 KB) and scale bytes (2 x 2 KB) go straight from global memory into LDS with
 //    buffer-to-LDS DMA, three stages deep, so no registers are spent on staging. Buffer bounds
-//    make rows past the end of an operand read as zero.
+//    make rows past the end of an operand read as zero. The grouped (MoE) GEMM uses the same
+//    tile code with two narrower shapes for ragged edges: 256 x 64 (waves stacked 4 x 1) for a
+//    last column at most 64 wide, 128 x 256 (1 x 4) for a group's last slot of at most 128
+//    rows.
 //  * general (any K % 16 == 0): v_mfma_f32_16x16x32_f16, 128 x 128 tiles, each wave 64 x 64,
 //    operands loaded straight into registers one K step ahead.
 // In both, scale bytes at or past K are forced to 0, which zeroes whatever codes sit in a
@@ -86,26 +89,54 @@ __device__ __forceinline__ void tile_of(int64_t bid, int64_t tiles_m, int64_t ti
   tn = in_band / gm;
 }
 
-// Group of m-tile slot `slot_m` for tiles of height bm; returns false past the last tile.
+// Group g and rows [m0, m1) of m-tile slot `slot_m` for tiles of height bm; false past the
+// last slot. The whole workgroup (256 threads, all of which must call it) searches: thread q
+// counts the slots of group c + q, a workgroup prefix sum over those counts brackets slot_m.
+// Offsets are clamped to [0, total_m] (a malformed table gives unspecified rows, never an
+// access outside A or D).
 __device__ __forceinline__ bool group_of(int64_t G, const int64_t* __restrict__ off, int64_t total_m,
                                          int64_t bm, int64_t slot_m, int64_t& g, int64_t& m0,
                                          int64_t& m1) {
-  int64_t base = 0;
-  int64_t prev = off[0] < 0 ? 0 : (off[0] > total_m ? total_m : off[0]);
-  for (int64_t q = 0; q < G; ++q) {
-    int64_t hi = off[q + 1];
-    hi = hi < prev ? prev : (hi > total_m ? total_m : hi);   // clamp a malformed table
-    const int64_t t = (hi - prev + bm - 1) / bm;
-    if (slot_m < base + t) {
-      g = q;
-      m0 = prev + (slot_m - base) * bm;
-      m1 = m0 + bm < hi ? m0 + bm : hi;
-      return true;
+  __shared__ int wsum[4];
+  __shared__ int64_t found[3];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (threadIdx.x == 0) found[0] = -1;
+  int base = 0;                                   // slots of the groups before this chunk
+  for (int64_t c = 0; c < G; c += 256) {
+    const int64_t q = c + threadIdx.x;
+    int64_t lo = 0, hi = 0;
+    int t = 0;
+    if (q < G) {
+      lo = off[q];
+      lo = lo < 0 ? 0 : (lo > total_m ? total_m : lo);
+      hi = off[q + 1];
+      hi = hi < lo ? lo : (hi > total_m ? total_m : hi);
+      t = (int)((hi - lo + bm - 1) / bm);
     }
-    base += t;
-    prev = hi;
+    int x = t;                                    // inclusive scan within the wave
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int y = __shfl_up(x, d);
+      if (lane >= d) x += y;
+    }
+    if (lane == 63) wsum[wave] = x;
+    __syncthreads();
+    int before = base;
+    for (int w = 0; w < wave; ++w) before += wsum[w];
+    const int incl = before + x, excl = incl - t;
+    if (t > 0 && slot_m >= excl && slot_m < incl) {
+      found[0] = q;
+      found[1] = lo + (slot_m - excl) * bm;
+      found[2] = found[1] + bm < hi ? found[1] + bm : hi;
+    }
+    base += wsum[0] + wsum[1] + wsum[2] + wsum[3];
+    __syncthreads();
+    if (found[0] >= 0) break;                     // the same for every thread after the barrier
   }
-  return false;
+  g = found[0];
+  m0 = found[1];
+  m1 = found[2];
+  return g >= 0;
 }
 
 struct Operand {
@@ -122,18 +153,42 @@ struct Operand {
 // contiguous 64-code run (32 bytes, 4 scale blocks = one aligned scale dword) of its row,
 // bytes [32h, 32h + 32) of the step, and feeds its 8 octets to 8 consecutive MFMAs.
 namespace big {
-constexpr int kWaveM = 128, kWaveN = 128;
-constexpr int kFragsM = kWaveM / 32, kFragsN = kWaveN / 32;   // 4 x 4 MFMA tiles per wave
-constexpr int kBlockM = 2 * kWaveM, kBlockN = 2 * kWaveN;     // 256 x 256
 constexpr int kFragBytes = 32 * 64;                           // 32 rows x 128 codes
 constexpr int kFragScaleBytes = 32 * 8;                       // 32 rows x 8 scale bytes
-constexpr int kFragsA = kBlockM / 32;                         // 8
-constexpr int kPanelFrags = kFragsA + kBlockN / 32;           // 16 fragments per K step
-constexpr int kCodeBytes = kPanelFrags * kFragBytes;          // 32 KB
-constexpr int kStageBytes = kCodeBytes + kPanelFrags * kFragScaleBytes;   // 36 KB
 constexpr int kStages = 3;                                    // DMA runs two K steps ahead
-constexpr int kLdsBytes = kStages * kStageBytes;              // 108 KB
-constexpr int kDmaPerWaveStep = 12;                           // 8 code + 4 scale DMAs
+
+// Tile shape: 4 waves in a WM x WN grid, each wave FM x FN MFMA tiles of 32 x 32. A
+// "fragment" is 32 rows of A or B for one K step; wave w moves fragments w, w + 4, w + 8, ...
+// of the step (three DMA operations each: two 1 KB code halves and the scale dwords), every
+// wave the same number of operations (padded with out-of-range ones).
+template <int FM, int FN, int WM, int WN>
+struct Cfg {
+  static_assert(WM * WN == 4, "four waves");
+  static constexpr int kFragsM = FM, kFragsN = FN, kWavesM = WM, kWavesN = WN;
+  static constexpr int kWaveM = 32 * FM, kWaveN = 32 * FN;
+  static constexpr int kBlockM = WM * kWaveM, kBlockN = WN * kWaveN;
+  static constexpr int kFragsA = kBlockM / 32;
+  static constexpr int kPanelFrags = kFragsA + kBlockN / 32;
+  static_assert(kFragsA % 4 == 0, "A fragments of a wave's i-th DMA slot are A for every wave");
+  static constexpr int kCodeBytes = kPanelFrags * kFragBytes;
+  static constexpr int kStageBytes = kCodeBytes + kPanelFrags * kFragScaleBytes;
+  static constexpr int kFragsPerWave = (kPanelFrags + 3) / 4;
+  static constexpr int kLdsBytes = kStages * kStageBytes + (kPanelFrags % 4 ? 1024 : 0);   // + pad
+  static constexpr int kDmaPerWaveStep = 3 * kFragsPerWave;
+};
+using Full = Cfg<4, 4, 2, 2>;     // 256 x 256: 16 fragments, 12 DMA operations per wave, 108 KB
+using NTail = Cfg<2, 2, 4, 1>;    // 256 x 64 (a last column tile at most 64 wide)
+using MTail = Cfg<4, 2, 1, 4>;    // 128 x 256 (a group's last row slot at most 128 high)
+constexpr int kBlockM = Full::kBlockM, kBlockN = Full::kBlockN;
+constexpr int kLdsBytes = Full::kLdsBytes;
+static_assert(NTail::kLdsBytes <= kLdsBytes && MTail::kLdsBytes <= kLdsBytes, "LDS");
+
+// s_waitcnt immediate (gfx9 encoding): vmcnt(vm) lgkmcnt(lgkm), expcnt not waited on.
+constexpr int waitcnt_imm(int vm, int lgkm) {
+  return (vm & 0xF) | ((vm >> 4) << 14) | (0x7 << 4) | ((lgkm & 0xF) << 8);
+}
+static_assert(waitcnt_imm(24, 15) == 0x4F78 && waitcnt_imm(12, 0) == 0x007C &&
+              waitcnt_imm(0, 15) == 0x0F70, "waitcnt encoding");
 }  // namespace big
 
 typedef float float16v __attribute__((ext_vector_type(16)));
@@ -148,18 +203,25 @@ __device__ __forceinline__ uint32_t k_mask4(int64_t K, int64_t k) {
          (k + 48 < K ? 0xFF000000u : 0u);
 }
 
-// One output tile over K steps [s0, s1) (128 elements each). With `accumulate` the scaled
-// partial sums are added to D with hardware float atomics (D pre-zeroed by the caller),
-// else stored.
+// One output tile of shape C over K steps [s0, s1) (128 elements each). With `accumulate` the
+// scaled partial sums are added to D with hardware float atomics (D pre-zeroed by the
+// caller), else stored.
+template <class C>
 __device__ __forceinline__ void gemm_tile_big(Operand A, Operand B, int64_t m0, int64_t m1,
                                               int64_t n0, int64_t n1, int64_t K, int64_t s0,
                                               int64_t s1, bool accumulate, float alpha,
                                               float* __restrict__ D, int64_t ldd, uint8_t* lds) {
-  using namespace big;
+  using big::kFragBytes;
+  using big::kFragScaleBytes;
+  using big::kStages;
+  constexpr int kFragsM = C::kFragsM, kFragsN = C::kFragsN, kFragsA = C::kFragsA;
+  constexpr int kWaveM = C::kWaveM, kWaveN = C::kWaveN;
+  constexpr int kPanelFrags = C::kPanelFrags, kCodeBytes = C::kCodeBytes;
+  constexpr int kStageBytes = C::kStageBytes, kDmaPerWaveStep = C::kDmaPerWaveStep;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int r = lane & 31, h = lane >> 5;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / C::kWavesN, wn = wave % C::kWavesN;
   const uint32_t rs_codes = (uint32_t)(K >> 1), rs_scales = (uint32_t)(K >> 4);
 
   const __amdgpu_buffer_rsrc_t a_codes = make_rsrc(A.codes, A.rows * (K >> 1));
@@ -167,10 +229,11 @@ __device__ __forceinline__ void gemm_tile_big(Operand A, Operand B, int64_t m0, 
   const __amdgpu_buffer_rsrc_t a_scales = make_rsrc(A.scales, A.rows * (K >> 4));
   const __amdgpu_buffer_rsrc_t b_scales = make_rsrc(B.scales, B.rows * (K >> 4));
 
-  // DMA: this wave moves fragments f = wave + 4*i (i < 2: A, i >= 2: B), two 1 KB halves
-  // each; lane (r, h) of half q carries row 32*f' + r, bytes [32h + 16q, 32h + 16q + 16) of
-  // the step -> LDS f*2 KB + q*1 KB + lane*16. Its scale dword (bytes [4h, 4h + 4) of the
-  // row's 8 scale bytes of the step) -> LDS scales + f*256 + lane*4.
+  // DMA: this wave moves fragments f = wave + 4*i (A fragments f < kFragsA, then B), two 1 KB
+  // halves each; lane (r, h) of half q carries row 32*f' + r (f' = f, or f - kFragsA for B),
+  // bytes [32h + 16q, 32h + 16q + 16) of the step -> LDS f*2 KB + q*1 KB + lane*16. Its scale
+  // dword (bytes [4h, 4h + 4) of the row's 8 scale bytes of the step) -> LDS scales + f*256 +
+  // lane*4. Fragments past the panel (f >= kPanelFrags, only in the last slot) are padding.
   const uint32_t dma_a = (uint32_t)(m0 + wave * 32 + r) * rs_codes + (uint32_t)(h * 32);
   const uint32_t dma_b = (uint32_t)(n0 + wave * 32 + r) * rs_codes + (uint32_t)(h * 32);
   const uint32_t sdma_a = (uint32_t)(m0 + wave * 32 + r) * rs_scales + (uint32_t)(h * 4);
@@ -178,29 +241,33 @@ __device__ __forceinline__ void gemm_tile_big(Operand A, Operand B, int64_t m0, 
   const uint32_t dma_stride = 128u * rs_codes;                // 4 fragments = 128 rows apart
   const uint32_t sdma_stride = 128u * rs_scales;
 
-  // One of the wave's 12 DMA operations of a step: part p = 3*i + q moves half q (q < 2) of
+  // One of the wave's DMA operations of a step: part p = 3*i + q moves half q (q < 2) of
   // fragment wave + 4*i, or (q == 2) its scale dwords. Steps past the last one are issued too
   // (the pipeline then has no branches and always the same number of operations in flight)
   // with an offset beyond every buffer's range, which the buffer unit answers with zeros
-  // without touching memory; their LDS buffers are never read.
+  // without touching memory; their LDS buffers are never read. Padding operations are issued
+  // the same way (out of range) into a 1 KB LDS area behind the stages that nothing reads.
   constexpr uint32_t kBeyond = 0x80000000u;                  // > any 31-bit buffer size
   auto issue_dma_part = [&](int64_t step, int buf, int p) {
     uint8_t* base = lds + buf * kStageBytes;
     const int i = p / 3, q = p % 3;
-    const bool is_a = i < 2;
+    const bool is_a = 4 * i < kFragsA;                        // same for every wave
     const int f = wave + 4 * i;
-    const bool live = step < s1;
+    const int ib = is_a ? i : i - kFragsA / 4;                // slot among the wave's A or B
+    const bool real = 4 * i + 3 < kPanelFrags || f < kPanelFrags;
+    const bool live = step < s1 && real;
+    uint8_t* pad = lds + kStages * kStageBytes;
     if (q < 2) {
-      const uint32_t off = (is_a ? dma_a : dma_b) + (uint32_t)(i & 1) * dma_stride +
+      const uint32_t off = (is_a ? dma_a : dma_b) + (uint32_t)ib * dma_stride +
                            (uint32_t)(step * (kStepK / 2)) + 16u * q;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a ? a_codes : b_codes,
-                                               (lds_ptr_t)(base + f * kFragBytes + q * 1024),
+                                               (lds_ptr_t)(real ? base + f * kFragBytes + q * 1024 : pad),
                                                16, live ? off : kBeyond, 0, 0, 0);
     } else {
-      const uint32_t so = (is_a ? sdma_a : sdma_b) + (uint32_t)(i & 1) * sdma_stride +
+      const uint32_t so = (is_a ? sdma_a : sdma_b) + (uint32_t)ib * sdma_stride +
                           (uint32_t)(step * (kStepK / 16));
       __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a ? a_scales : b_scales,
-                                               (lds_ptr_t)(base + kCodeBytes + f * kFragScaleBytes),
+                                               (lds_ptr_t)(real ? base + kCodeBytes + f * kFragScaleBytes : pad),
                                                4, live ? so : kBeyond, 0, 0, 0);
     }
   };
@@ -222,7 +289,10 @@ __device__ __forceinline__ void gemm_tile_big(Operand A, Operand B, int64_t m0, 
   // no LDS latency sits between steps and the barrier wait overlaps in-flight MFMAs. Before
   // that barrier each wave waits for its own DMA of step s+1 and for its LDS reads of step s,
   // whose buffer the DMA of step s+3 refills right after it.
-  static_assert(kStages == 3 && kDmaPerWaveStep == 12, "waitcnt immediates below");
+  static_assert(kStages == 3, "waitcnt immediates below");
+  constexpr int kWaitStep0 = big::waitcnt_imm(2 * kDmaPerWaveStep, 15);   // 2 steps may fly
+  constexpr int kWaitNext = big::waitcnt_imm(kDmaPerWaveStep, 0);         // 1 step, no LDS
+  constexpr int kWaitAll = big::waitcnt_imm(0, 15);
   auto barrier = [] {
     // plain s_barrier: a fence would also wait for the DMA still in flight; the empty asm
     // statements keep the compiler from moving LDS accesses across it
@@ -255,7 +325,7 @@ __device__ __forceinline__ void gemm_tile_big(Operand A, Operand B, int64_t m0, 
 
 #pragma unroll
   for (int p = 0; p < kStages; ++p) issue_dma(s0 + p, p);
-  __builtin_amdgcn_s_waitcnt(0x4F78);                         // vmcnt(24): step 0 landed
+  __builtin_amdgcn_s_waitcnt(kWaitStep0);                     // step 0 landed
   barrier();
   read_half(0, 0, ar0, br0);
   read_scales(0);
@@ -266,9 +336,10 @@ __device__ __forceinline__ void gemm_tile_big(Operand A, Operand B, int64_t m0, 
     return __builtin_bit_cast(half2v, (((sc & keep) >> (8 * q)) & 0xFFu) * 0x00800080u);
   };
 
-  // 32 phases per step (t = K octet, i = A fragment), each 4 MFMAs. Decodes run one phase
-  // ahead: while phase (t, i) issues its MFMAs, the A fragment of the next phase and B
-  // fragment i of octet t+1 are decoded, so every MFMA finds its operands ready and the vector
+  // 8 * kFragsM phases per step (t = K octet, i = A fragment), each kFragsN MFMAs. Decodes run
+  // one phase ahead: while phase (t, i) issues its MFMAs, the A fragment of the next phase and
+  // B fragments i, i + kFragsM, ... of octet t+1 are decoded, so every MFMA finds its operands
+  // ready and the vector
   // ALU works under the matrix core; the last octet already decodes octet 0 of the next step
   // (its half 0 and scales arrive at octet 4), so steps join without a gap. sched_barrier
   // keeps the compiler from regrouping phases.
@@ -305,25 +376,32 @@ __device__ __forceinline__ void gemm_tile_big(Operand A, Operand B, int64_t m0, 
         // behind a branch the compiler's wait analysis, merging the two paths, would make
         // the wave wait for these new reads before decoding data that has long landed.
         // Steps s+1 and s+2 are in flight here; wait for s+1.
-        __builtin_amdgcn_s_waitcnt(0x007C);                     // vmcnt(12) lgkmcnt(0)
+        __builtin_amdgcn_s_waitcnt(kWaitNext);                  // step s+1 landed, LDS reads done
         barrier();
         read_half(b_next, 0, ar0, br0);                         // sa, sb now step s+1's
         read_scales(b_next);
       }
 #pragma unroll
       for (int i = 0; i < kFragsM; ++i) {
-        // the DMA of step s+3 refills the buffer step s was read from, one operation per
-        // phase in octets 5-7: a burst of 12 would stall the wave's issue while its matrix
+        // the DMA of step s+3 refills the buffer step s was read from, spread over the phases
+        // of octets 5-7 (one per phase for the 256 x 256 tile): a burst would stall the
+        // wave's issue while its matrix
         // pipe runs dry, and the compiler orders each LDS-bound DMA after the wave's pending
         // LDS reads (it cannot tell the buffers apart), so the DMA waits one octet for the
         // reads issued at the barrier to land
-        if (t >= 5) issue_dma_part(s + 3, b_cur, (t - 5) * kFragsM + i);
+        if (t >= 5) {
+#pragma unroll
+          for (int p = (t - 5) * kFragsM + i; p < kDmaPerWaveStep; p += 3 * kFragsM)
+            issue_dma_part(s + 3, b_cur, p);
+        }
         const int tn = i + 1 < kFragsM ? t : t + 1;           // next phase
         const int in_ = i + 1 < kFragsM ? i + 1 : 0;
         const half8 an = tn < 8 ? decode8(araw(in_, tn), pa[in_][tn >> 1])
                                 : decode8(ar0[0].x, pair(sa[0], keep_next, 0));
-        bn[i] = t + 1 < 8 ? decode8(braw(i, t + 1), pb[i][(t + 1) >> 1])
-                          : decode8(br0[i].x, pair(sb[i], keep_next, 0));
+#pragma unroll
+        for (int j = i; j < kFragsN; j += kFragsM)              // B fragment j of octet t+1
+          bn[j] = t + 1 < 8 ? decode8(braw(j, t + 1), pb[j][(t + 1) >> 1])
+                            : decode8(br0[j].x, pair(sb[j], keep_next, 0));
 #pragma unroll
         for (int j = 0; j < kFragsN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, bv[j], acc[i][j], 0, 0, 0);
@@ -335,7 +413,7 @@ __device__ __forceinline__ void gemm_tile_big(Operand A, Operand B, int64_t m0, 
     }
     b_cur = b_next;
   }
-  __builtin_amdgcn_s_waitcnt(0x0F70);                         // no DMA may outlive the tile
+  __builtin_amdgcn_s_waitcnt(kWaitAll);                       // no DMA may outlive the tile
 
   // D fragment layout (32 x 32): lane l holds column l % 32 and, for q = 0..15, row
   // 8*(q/4) + 4*(l/32) + q%4.
@@ -380,8 +458,8 @@ void k_gemm_big(Operand A, const float* __restrict__ ag, Operand B, const float*
   const int64_t m0 = tm * kBlockM, n0 = tn * kBlockN;
   const int64_t m1 = m0 + kBlockM < A.rows ? m0 + kBlockM : A.rows;
   const int64_t n1 = n0 + kBlockN < B.rows ? n0 + kBlockN : B.rows;
-  gemm_tile_big(A, B, m0, m1, n0, n1, K, s0, s1, blockIdx.x >= tail_first, ag[0] * bg[0], D, ldd,
-                lds_dyn);
+  gemm_tile_big<Full>(A, B, m0, m1, n0, n1, K, s0, s1, blockIdx.x >= tail_first, ag[0] * bg[0], D,
+                      ldd, lds_dyn);
 }
 
 // Zeroes the D region of the K-split tiles tail_first, tail_first + 1, ... of k_gemm_big:
@@ -416,19 +494,35 @@ __global__ __launch_bounds__(kThreads) void k_zero_tiles(int64_t M, int64_t N, f
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_grouped_gemm_big(int64_t G, const int64_t* __restrict__ off, Operand A,
                         const float* __restrict__ ag, Operand B, const float* __restrict__ bg,
-                        int64_t N, int64_t K, float* __restrict__ D, int64_t ldd) {
+                        int64_t N, int64_t K, float* __restrict__ D, int64_t ldd, int64_t slots_m) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds_dyn[];
   using namespace big;
   const int64_t tiles_n = (N + kBlockN - 1) / kBlockN;
-  const int64_t slot_m = blockIdx.x / tiles_n;
-  const int64_t tn = blockIdx.x - slot_m * tiles_n;
+  // A last column at most 64 wide is computed by the cheap 256 x 64 tiles; those workgroups
+  // come after all others (slots_m of them), so they fill the gaps the others leave at the
+  // end. Workgroups are dealt to the 8 XCDs round robin, so every XCD gets its share either
+  // way.
+  const bool narrow_last = tiles_n > 1 && N - (tiles_n - 1) * kBlockN <= NTail::kBlockN;
+  const int64_t cols_main = narrow_last ? tiles_n - 1 : tiles_n;
+  const int64_t main_wg = slots_m * cols_main;
+  const int64_t bid = blockIdx.x;
+  const int64_t slot_m = bid < main_wg ? bid / cols_main : bid - main_wg;
+  const int64_t tn = bid < main_wg ? bid - slot_m * cols_main : tiles_n - 1;
   int64_t g, m0, m1;
   if (!group_of(G, off, A.rows, kBlockM, slot_m, g, m0, m1)) return;
   const int64_t n0 = tn * kBlockN;
   const int64_t n1 = n0 + kBlockN < N ? n0 + kBlockN : N;
   const Operand Bg{B.codes + g * N * (K >> 1), B.scales + g * N * (K >> 4), N};
-  gemm_tile_big(A, Bg, m0, m1, n0, n1, K, 0, (K + kStepK - 1) / kStepK, false, ag[g] * bg[g], D, ldd,
-                lds_dyn);
+  const int64_t steps = (K + kStepK - 1) / kStepK;
+  const float alpha = ag[g] * bg[g];
+  // a last column at most 64 wide and a group's last slot at most 128 high take the narrower
+  // tiles, which cost about a quarter and a half of the full one
+  if (n1 - n0 <= NTail::kBlockN)
+    gemm_tile_big<NTail>(A, Bg, m0, m1, n0, n1, K, 0, steps, false, alpha, D, ldd, lds_dyn);
+  else if (m1 - m0 <= MTail::kBlockM)
+    gemm_tile_big<MTail>(A, Bg, m0, m1, n0, n1, K, 0, steps, false, alpha, D, ldd, lds_dyn);
+  else
+    gemm_tile_big<Full>(A, Bg, m0, m1, n0, n1, K, 0, steps, false, alpha, D, ldd, lds_dyn);
 }
 
 // =========================================================================================
@@ -646,7 +740,7 @@ hipError_t launch_grouped_gemm(int64_t G, const int64_t* m_offsets, GemmOperand 
     const int64_t slots_m = total_m / big::kBlockM + G;       // >= sum_g ceil(M_g / 256)
     hipLaunchKernelGGL(k_grouped_gemm_big, dim3((unsigned)(slots_m * tiles_n)), dim3(kThreads),
                        big::kLdsBytes, stream, G, m_offsets, A, a.global_scale, B,
-                       b.global_scale, N, K, D, ldd);
+                       b.global_scale, N, K, D, ldd, slots_m);
   } else {
     const int64_t tiles_n = (N + small::kBlockN - 1) / small::kBlockN;
     const int64_t slots_m = total_m / small::kBlockM + G;

@@ -129,6 +129,39 @@ def test_grouped_gemm_ragged_groups():
     assert np.all(np.abs(d.cpu().numpy() - d64) <= bound)
 
 
+@pytest.mark.parametrize("n,k", [(320, 192), (64, 128), (112, 2688), (576, 64)])
+def test_grouped_gemm_tile_shapes(n, k):
+    """The LDS-staged grouped kernel (K % 64 == 0) with every tile shape it picks: full
+    256 x 256 tiles, 128-row tiles for a group's last slot of at most 128 rows, and 64-wide
+    tiles for a last column of at most 64, over empty, tiny, exactly-128/256 and multi-slot
+    groups."""
+    log(f"grouped gemm tiles n={n} k={k}")
+    rows = [0, 5, 130, 128, 300, 513, 256, 1, 0, 129]
+    G = len(rows)
+    off = np.concatenate([[0], np.cumsum(rows)]).astype(np.int64)
+    x_bits = workloads.normal_bf16((int(off[-1]), k), 71 + n)
+    w_bits = workloads.with_outliers_bf16((G * n, k), 72 + k)
+    offd = torch.from_numpy(off).cuda()
+    wseg = np.arange(G + 1, dtype=np.int64) * n
+    qx, _ = nv.quantize(to_device_bf16(x_bits), "1x16", "rn", segments=offd)
+    qw, _ = nv.quantize(to_device_bf16(w_bits), "16x16", "rn", segments=torch.from_numpy(wseg).cuda())
+    rx = oracle.quantize_1x16(f32(x_bits), segments=off)
+    rw = oracle.quantize_16x16(f32(w_bits), segments=wseg)
+    assert_quant_equal(host(qx), rx, "grouped X")
+    assert_quant_equal(host(qw), rw, "grouped W")
+    out = torch.full((int(off[-1]), n + 3), -5.0, dtype=torch.float32, device="cuda")
+    d = nv.grouped_gemm(offd, qx, qw, n, out=out[:, :n])
+    torch.cuda.synchronize()
+    o = out.cpu().numpy()
+    assert np.all(o[:, n:] == -5.0)
+    xh = oracle.dequantize(*rx, segments=off)
+    wh = oracle.dequantize(*rw, segments=wseg)
+    d64 = oracle.grouped_gemm_fp64(xh, wh, off, n)
+    bound = oracle.grouped_gemm_bound(xh, wh, off, n)
+    assert np.all(np.abs(o[:, :n] - d64) <= bound)
+    del d
+
+
 @pytest.mark.parametrize("mnk", [(513, 1024, 5120), (1000, 700, 1344), (2304, 2560, 1024)])
 def test_gemm_reproducible(mnk):
     """The same GEMM twice gives bitwise identical D, also where tiles of a partial last round
