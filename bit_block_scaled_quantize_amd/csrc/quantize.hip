@@ -98,8 +98,9 @@ __global__ __launch_bounds__(kThreads) void k_amax_partial(const TIn* __restrict
   if (threadIdx.x == 0) partial[blockIdx.x] = m;
 }
 
-// amax per row segment: each wave owns a contiguous row range and flushes one atomic max
-// per segment run it crosses (the slots start at zero).
+// amax per row segment: each wave owns a contiguous row range, splits it at segment
+// boundaries (one table search per run, not per row), streams each run as one flat vector
+// range eight loads deep, and flushes one atomic max per run (the slots start at zero).
 template <typename TIn>
 __global__ __launch_bounds__(kThreads) void k_amax_seg(const TIn* __restrict__ x, int64_t rows,
                                                        int64_t vecs_per_row, int64_t ld,
@@ -112,30 +113,30 @@ __global__ __launch_bounds__(kThreads) void k_amax_seg(const TIn* __restrict__ x
   const int64_t per = (rows + nwaves - 1) / nwaves;
   const int64_t r0 = wave * per;
   const int64_t r1 = r0 + per < rows ? r0 + per : rows;
-  float m = 0.0f;
-  int64_t cur = -1;
-  for (int64_t r = r0; r < r1; ++r) {
-    const int64_t s = find_segment(seg, nseg, r);
-    if (s != cur) {
-      if (cur >= 0) {
-        const float wm = wave_max(m);
-        if (lane == 0) atomic_max_nonneg(amax_out + cur, wm);
-      }
-      cur = s;
-      m = 0.0f;
-    }
+  const bool contiguous = ld == vecs_per_row * kVec;
+  int64_t r = r0;
+  while (r < r1) {
+    const int64_t sg = find_segment(seg, nseg, r);
+    int64_t e = sg + 1 <= nseg ? seg[sg + 1] : r1;
+    e = e > r1 ? r1 : (e <= r ? r + 1 : e);              // progress on a malformed table too
     const TIn* xr = x + r * ld;
-    int64_t v = lane;
-    for (; v + 192 < vecs_per_row; v += 256) {
-      const float a0 = vec_absmax<TIn>(xr + v * kVec), a1 = vec_absmax<TIn>(xr + (v + 64) * kVec);
-      const float a2 = vec_absmax<TIn>(xr + (v + 128) * kVec), a3 = vec_absmax<TIn>(xr + (v + 192) * kVec);
-      m = fmaxf(m, fmaxf(fmaxf(a0, a1), fmaxf(a2, a3)));
+    const int64_t total = (e - r) * vecs_per_row;
+    auto at = [&](int64_t q) {
+      return contiguous ? xr + q * kVec : xr + (q / vecs_per_row) * ld + (q % vecs_per_row) * kVec;
+    };
+    float m = 0.0f;
+    int64_t q = lane;
+    for (; q + (kAmaxUnroll - 1) * 64 < total; q += kAmaxUnroll * 64) {
+      float a[kAmaxUnroll];
+#pragma unroll
+      for (int u = 0; u < kAmaxUnroll; ++u) a[u] = vec_absmax<TIn>(at(q + u * 64));
+#pragma unroll
+      for (int u = 0; u < kAmaxUnroll; ++u) m = fmaxf(m, a[u]);
     }
-    for (; v < vecs_per_row; v += 64) m = fmaxf(m, vec_absmax<TIn>(xr + v * kVec));
-  }
-  if (cur >= 0) {
+    for (; q < total; q += 64) m = fmaxf(m, vec_absmax<TIn>(at(q)));
     const float wm = wave_max(m);
-    if (lane == 0) atomic_max_nonneg(amax_out + cur, wm);
+    if (lane == 0) atomic_max_nonneg(amax_out + sg, wm);
+    r = e;
   }
 }
 
