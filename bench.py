@@ -45,6 +45,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--no-moe", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-reference", action="store_true",
+                   help="skip timing the vendor FP16/BF16 GEMMs on the same shapes")
     p.add_argument("--kernel-reps", type=int, default=5, help="cold-cache repetitions per kernel")
     p.add_argument("--copy-kernel", action="store_true",
                    help="first run one plain 256 MiB fp32 copy kernel, the known-size reference "
@@ -269,6 +271,8 @@ def main():
 
     if not args.no_moe:
         out["moe"] = bench_moe(nv, workloads, torch, dev, stream, flush, args)
+    if not args.no_reference:
+        out["reference_gemm"] = reference_gemm(torch, dev, stream)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(x_bits, w_bits, dy_bits, mask, step_flops)
     print(json.dumps(out))
@@ -286,9 +290,9 @@ def gemm_traffic():
 
 
 def bench_moe(nv, workloads, torch, dev, stream, flush, args):
-    fsum = torch.empty((1,), dtype=torch.int64, device=dev)
     """Per-expert quantize of the expert-sorted activations and stacked weights, then the
     grouped fprop GEMM (128 experts, top-6 of 16384 tokens, hidden 2688, expert FFN 1856)."""
+    fsum = torch.empty((1,), dtype=torch.int64, device=dev)
     x_bits, w_bits, off = workloads.moe()
     G, n, k = workloads.MOE_EXPERTS, workloads.MOE_FFN, workloads.MOE_HIDDEN
     total = int(off[-1])
@@ -331,6 +335,36 @@ def bench_moe(nv, workloads, torch, dev, stream, flush, args):
                      "hidden": k, "ffn": n, "rows_total": total,
                      "rows_per_expert_max": int(np.diff(off).max()),
                      "rows_per_expert_min": int(np.diff(off).min())}
+    return res
+
+
+def reference_gemm(torch, dev, stream):
+    """The vendor library's dense FP16 and BF16 GEMMs (torch.matmul -> hipBLASLt) on the three
+    GEMM shapes of the step, same box and clock regime: context for the NVFP4 GEMM, which
+    also decodes its operands and writes FP32. Random normal operands, output in the input
+    dtype, mean of 5 warm launches."""
+    res = {}
+    shapes = {"fprop": (M, N_OUT, K_IN), "dgrad": (M, K_IN, N_OUT), "wgrad": (N_OUT, K_IN, M)}
+    for name, (m, n, k) in shapes.items():
+        row = {}
+        for dt, tag in ((torch.float16, "fp16"), (torch.bfloat16, "bf16")):
+            a = torch.randn((m, k), device=dev, dtype=dt)
+            b = torch.randn((n, k), device=dev, dtype=dt)
+            d = torch.empty((m, n), device=dev, dtype=dt)
+            for _ in range(2):
+                torch.matmul(a, b.t(), out=d)
+            ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            ev0.record(stream)
+            for _ in range(5):
+                torch.matmul(a, b.t(), out=d)
+            ev1.record(stream)
+            torch.cuda.synchronize()
+            ms = ev0.elapsed_time(ev1) / 5
+            row[f"{tag}_TFLOP/s"] = round(2.0 * m * n * k / (ms * 1e-3) / 1e12, 1)
+            del a, b, d
+        res[name] = row
+    res["library"] = "torch.matmul (hipBLASLt), dense, operands already in FP16/BF16"
     return res
 
 

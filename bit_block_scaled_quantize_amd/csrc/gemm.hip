@@ -197,19 +197,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, int64
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
 }
 
-// Scale-byte mask for the 64-element run starting at element k: blocks at or past K -> 0.
-__device__ __forceinline__ uint32_t k_mask4(int64_t K, int64_t k) {
-  return (k < K ? 0xFFu : 0u) | (k + 16 < K ? 0xFF00u : 0u) | (k + 32 < K ? 0xFF0000u : 0u) |
-         (k + 48 < K ? 0xFF000000u : 0u);
-}
-
 // One output tile of shape C over K steps [s0, s1) (128 elements each). With `accumulate` the
 // scaled partial sums are added to D with hardware float atomics (D pre-zeroed by the
 // caller), else stored.
 template <class C>
 __device__ __forceinline__ void gemm_tile_big(Operand A, Operand B, int64_t m0, int64_t m1,
-                                              int64_t n0, int64_t n1, int64_t K, int64_t s0,
-                                              int64_t s1, bool accumulate, float alpha,
+                                              int64_t n0, int64_t n1, int64_t K, int64_t s0_,
+                                              int64_t s1_, bool accumulate, float alpha,
                                               float* __restrict__ D, int64_t ldd, uint8_t* lds) {
   using big::kFragBytes;
   using big::kFragScaleBytes;
@@ -219,10 +213,17 @@ __device__ __forceinline__ void gemm_tile_big(Operand A, Operand B, int64_t m0, 
   constexpr int kPanelFrags = C::kPanelFrags, kCodeBytes = C::kCodeBytes;
   constexpr int kStageBytes = C::kStageBytes, kDmaPerWaveStep = C::kDmaPerWaveStep;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  // the wave index is uniform: held in a scalar register, everything derived from it (DMA
+  // rows, LDS addresses) is scalar arithmetic
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 31, h = lane >> 5;
   const int wm = wave / C::kWavesN, wn = wave % C::kWavesN;
   const uint32_t rs_codes = (uint32_t)(K >> 1), rs_scales = (uint32_t)(K >> 4);
+  constexpr uint32_t kBeyond = 0x80000000u;                  // > any 31-bit buffer size
+  // K steps as uniform 32-bit values, so the step loop and the per-step DMA offsets stay in
+  // scalar registers
+  const int s0 = __builtin_amdgcn_readfirstlane((int)s0_);
+  const int s1 = __builtin_amdgcn_readfirstlane((int)s1_);
 
   const __amdgpu_buffer_rsrc_t a_codes = make_rsrc(A.codes, A.rows * (K >> 1));
   const __amdgpu_buffer_rsrc_t b_codes = make_rsrc(B.codes, B.rows * (K >> 1));
@@ -234,12 +235,19 @@ __device__ __forceinline__ void gemm_tile_big(Operand A, Operand B, int64_t m0, 
   // bytes [32h + 16q, 32h + 16q + 16) of the step -> LDS f*2 KB + q*1 KB + lane*16. Its scale
   // dword (bytes [4h, 4h + 4) of the row's 8 scale bytes of the step) -> LDS scales + f*256 +
   // lane*4. Fragments past the panel (f >= kPanelFrags, only in the last slot) are padding.
-  const uint32_t dma_a = (uint32_t)(m0 + wave * 32 + r) * rs_codes + (uint32_t)(h * 32);
-  const uint32_t dma_b = (uint32_t)(n0 + wave * 32 + r) * rs_codes + (uint32_t)(h * 32);
-  const uint32_t sdma_a = (uint32_t)(m0 + wave * 32 + r) * rs_scales + (uint32_t)(h * 4);
-  const uint32_t sdma_b = (uint32_t)(n0 + wave * 32 + r) * rs_scales + (uint32_t)(h * 4);
-  const uint32_t dma_stride = 128u * rs_codes;                // 4 fragments = 128 rows apart
-  const uint32_t sdma_stride = 128u * rs_scales;
+  // Offsets split into the lane's part (row r of the fragment, half h; a vector register) and
+  // the fragment's and step's part (uniform, scalar), so each DMA costs one vector add.
+  const uint32_t lane_codes = (uint32_t)r * rs_codes + (uint32_t)(h * 32);
+  const uint32_t lane_scales = (uint32_t)r * rs_scales + (uint32_t)(h * 4);
+  // Scale blocks at or past K. With K % 64 == 0 a lane's scale dword of a step (4 blocks)
+  // lies wholly inside K, except in a last half step (K % 128 == 64), where lanes of half 1
+  // would read the next row's scales: there their offset is pushed out of range so the DMA
+  // delivers zero scales, which zero whatever codes they meet. (When the step is not live
+  // either, the two pushes wrap to an in-range offset of a dummy load whose LDS buffer is
+  // never read.)
+  const int last_half_step = (K % kStepK) ? (int)(K / kStepK) : -1;
+  const uint32_t lane_scales_last = lane_scales + (h ? kBeyond : 0u);
+  const uint32_t row_a = (uint32_t)(m0 + wave * 32), row_b = (uint32_t)(n0 + wave * 32);
 
   // One of the wave's DMA operations of a step: part p = 3*i + q moves half q (q < 2) of
   // fragment wave + 4*i, or (q == 2) its scale dwords. Steps past the last one are issued too
@@ -247,8 +255,7 @@ __device__ __forceinline__ void gemm_tile_big(Operand A, Operand B, int64_t m0, 
   // with an offset beyond every buffer's range, which the buffer unit answers with zeros
   // without touching memory; their LDS buffers are never read. Padding operations are issued
   // the same way (out of range) into a 1 KB LDS area behind the stages that nothing reads.
-  constexpr uint32_t kBeyond = 0x80000000u;                  // > any 31-bit buffer size
-  auto issue_dma_part = [&](int64_t step, int buf, int p) {
+  auto issue_dma_part = [&](int step, int buf, int p) {
     uint8_t* base = lds + buf * kStageBytes;
     const int i = p / 3, q = p % 3;
     const bool is_a = 4 * i < kFragsA;                        // same for every wave
@@ -256,22 +263,22 @@ __device__ __forceinline__ void gemm_tile_big(Operand A, Operand B, int64_t m0, 
     const int ib = is_a ? i : i - kFragsA / 4;                // slot among the wave's A or B
     const bool real = 4 * i + 3 < kPanelFrags || f < kPanelFrags;
     const bool live = step < s1 && real;
+    const uint32_t row = (is_a ? row_a : row_b) + 128u * (uint32_t)ib;   // first row, uniform
     uint8_t* pad = lds + kStages * kStageBytes;
     if (q < 2) {
-      const uint32_t off = (is_a ? dma_a : dma_b) + (uint32_t)ib * dma_stride +
-                           (uint32_t)(step * (kStepK / 2)) + 16u * q;
+      const uint32_t su = row * rs_codes + (uint32_t)(step * (kStepK / 2)) + 16u * q;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a ? a_codes : b_codes,
                                                (lds_ptr_t)(real ? base + f * kFragBytes + q * 1024 : pad),
-                                               16, live ? off : kBeyond, 0, 0, 0);
+                                               16, lane_codes + (live ? su : kBeyond), 0, 0, 0);
     } else {
-      const uint32_t so = (is_a ? sdma_a : sdma_b) + (uint32_t)ib * sdma_stride +
-                          (uint32_t)(step * (kStepK / 16));
+      const uint32_t su = row * rs_scales + (uint32_t)(step * (kStepK / 16));
+      const uint32_t lsc = step == last_half_step ? lane_scales_last : lane_scales;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a ? a_scales : b_scales,
                                                (lds_ptr_t)(real ? base + kCodeBytes + f * kFragScaleBytes : pad),
-                                               4, live ? so : kBeyond, 0, 0, 0);
+                                               4, lsc + (live ? su : kBeyond), 0, 0, 0);
     }
   };
-  auto issue_dma = [&](int64_t step, int buf) {
+  auto issue_dma = [&](int step, int buf) {
 #pragma unroll
     for (int p = 0; p < kDmaPerWaveStep; ++p) issue_dma_part(step, buf, p);
   };
@@ -311,8 +318,8 @@ __device__ __forceinline__ void gemm_tile_big(Operand A, Operand B, int64_t m0, 
     for (int i = 0; i < kFragsM; ++i)
       ra[i] = *reinterpret_cast<const v4u32*>(cur + (wm * kFragsM + i) * kFragBytes);
   };
-  // raw scale dwords; the mask for blocks past K is applied where they are consumed, so the
-  // loads need not land before the step that uses them
+  // raw scale dwords (blocks past K arrive as zeros from the DMA); they need not land before
+  // the step that uses them
   auto read_scales = [&](int b) {
     const uint8_t* cur = lds + b * kStageBytes + kCodeBytes + lane * 4;
 #pragma unroll
@@ -330,10 +337,10 @@ __device__ __forceinline__ void gemm_tile_big(Operand A, Operand B, int64_t m0, 
   read_half(0, 0, ar0, br0);
   read_scales(0);
 
-  // FP16 scale pair (S * 2^-8 twice) of block q of a scale dword, blocks at or past K zeroed:
+  // FP16 scale pair (S * 2^-8 twice) of block q of a scale dword:
   // (b << 7) | (b << 23) = b * 0x00800080
-  auto pair = [](uint32_t sc, uint32_t keep, int q) {
-    return __builtin_bit_cast(half2v, (((sc & keep) >> (8 * q)) & 0xFFu) * 0x00800080u);
+  auto pair = [](uint32_t sc, int q) {
+    return __builtin_bit_cast(half2v, ((sc >> (8 * q)) & 0xFFu) * 0x00800080u);
   };
 
   // 8 * kFragsM phases per step (t = K octet, i = A fragment), each kFragsN MFMAs. Decodes run
@@ -344,27 +351,22 @@ __device__ __forceinline__ void gemm_tile_big(Operand A, Operand B, int64_t m0, 
   // (its half 0 and scales arrive at octet 4), so steps join without a gap. sched_barrier
   // keeps the compiler from regrouping phases.
   half8 bv[kFragsN], bn[kFragsN], av;
-  {
-    const uint32_t keep0 = k_mask4(K, s0 * kStepK + h * 64);
 #pragma unroll
-    for (int j = 0; j < kFragsN; ++j) bv[j] = decode8(br0[j].x, pair(sb[j], keep0, 0));
-    av = decode8(ar0[0].x, pair(sa[0], keep0, 0));
-  }
+  for (int j = 0; j < kFragsN; ++j) bv[j] = decode8(br0[j].x, pair(sb[j], 0));
+  av = decode8(ar0[0].x, pair(sa[0], 0));
 
   int b_cur = 0;
-  for (int64_t s = s0; s < s1; ++s) {
+  for (int s = s0; s < s1; ++s) {
     const int b_next = b_cur == kStages - 1 ? 0 : b_cur + 1;
     read_half(b_cur, 1, ar1, br1);
 
-    const uint32_t keep = k_mask4(K, s * kStepK + h * 64);
-    const uint32_t keep_next = k_mask4(K, (s + 1) * kStepK + h * 64);
     half2v pa[kFragsM][4], pb[kFragsN][4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
 #pragma unroll
-      for (int i = 0; i < kFragsM; ++i) pa[i][q] = pair(sa[i], keep, q);
+      for (int i = 0; i < kFragsM; ++i) pa[i][q] = pair(sa[i], q);
 #pragma unroll
-      for (int j = 0; j < kFragsN; ++j) pb[j][q] = pair(sb[j], keep, q);
+      for (int j = 0; j < kFragsN; ++j) pb[j][q] = pair(sb[j], q);
     }
 
     auto araw = [&](int i, int t) { return word(t < 4 ? ar0[i] : ar1[i], t & 3); };
@@ -397,11 +399,11 @@ __device__ __forceinline__ void gemm_tile_big(Operand A, Operand B, int64_t m0, 
         const int tn = i + 1 < kFragsM ? t : t + 1;           // next phase
         const int in_ = i + 1 < kFragsM ? i + 1 : 0;
         const half8 an = tn < 8 ? decode8(araw(in_, tn), pa[in_][tn >> 1])
-                                : decode8(ar0[0].x, pair(sa[0], keep_next, 0));
+                                : decode8(ar0[0].x, pair(sa[0], 0));
 #pragma unroll
         for (int j = i; j < kFragsN; j += kFragsM)              // B fragment j of octet t+1
           bn[j] = t + 1 < 8 ? decode8(braw(j, t + 1), pb[j][(t + 1) >> 1])
-                            : decode8(br0[j].x, pair(sb[j], keep_next, 0));
+                            : decode8(br0[j].x, pair(sb[j], 0));
 #pragma unroll
         for (int j = 0; j < kFragsN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, bv[j], acc[i][j], 0, 0, 0);
