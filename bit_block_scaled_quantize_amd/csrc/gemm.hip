@@ -247,7 +247,8 @@ __device__ __forceinline__ void gemm_tile_big(Operand A, Operand B, int64_t m0, 
   // never read.)
   const int last_half_step = (K % kStepK) ? (int)(K / kStepK) : -1;
   const uint32_t lane_scales_last = lane_scales + (h ? kBeyond : 0u);
-  const uint32_t row_a = (uint32_t)(m0 + wave * 32), row_b = (uint32_t)(n0 + wave * 32);
+  const uint32_t row_a = __builtin_amdgcn_readfirstlane((uint32_t)(m0 + wave * 32));
+  const uint32_t row_b = __builtin_amdgcn_readfirstlane((uint32_t)(n0 + wave * 32));
 
   // One of the wave's DMA operations of a step: part p = 3*i + q moves half q (q < 2) of
   // fragment wave + 4*i, or (q == 2) its scale dwords. Steps past the last one are issued too
