@@ -47,6 +47,7 @@ struct Pair<uint16_t> {
     if (both && paired) w = *reinterpret_cast<const uint32_t*>(p);
     else w = (uint32_t)p[0] | (both ? (uint32_t)p[1] << 16 : 0u);
   }
+  __device__ __forceinline__ void load_pair(const uint16_t* p) { w = *reinterpret_cast<const uint32_t*>(p); }
   __device__ __forceinline__ float get(int q) const { return q == 0 ? bf16_lo(w) : bf16_hi(w); }
 };
 
@@ -57,6 +58,7 @@ struct Pair<float> {
     if (both && paired) w = *reinterpret_cast<const v2f32*>(p);
     else w = v2f32{p[0], both ? p[1] : 0.0f};
   }
+  __device__ __forceinline__ void load_pair(const float* p) { w = *reinterpret_cast<const v2f32*>(p); }
   __device__ __forceinline__ float get(int q) const { return q == 0 ? w.x : w.y; }
 };
 
@@ -128,8 +130,14 @@ __global__ __launch_bounds__(kThreads) void k_rht(
     const int64_t cl = c < cols ? c : 0;                    // clamped column for loads
     const int64_t tb = g.TB0 + wave + 4 * k;
     const int64_t tbl = tb < nbt ? tb : 0;                  // clamped token block for loads
+    const TIn* p = x + tbl * 16 * ld + cl;
+    if (paired && g.C0 + kTileCols <= cols) {               // uniform: every pair whole, aligned
 #pragma unroll
-    for (int j = 0; j < 16; ++j) raw[j].load(x + (tbl * 16 + j) * ld + cl, c + 1 < cols, paired);
+      for (int j = 0; j < 16; ++j) raw[j].load_pair(p + j * ld);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) raw[j].load(p + j * ld, c + 1 < cols, paired);
+    }
   };
 
   Pair<TIn> cur[16], nxt[16];
