@@ -138,12 +138,43 @@ __device__ __forceinline__ u32x4 block_random(uint64_t b, uint64_t seed, uint64_
 // r = 0 when S decodes to zero (every element then encodes as a signed zero).
 struct BlockScale { uint32_t code; float mult; };
 
-__device__ __forceinline__ BlockScale block_scale(float block_amax, float s_enc) {
-  const float t = (block_amax / 6.0f) * s_enc;
-  const uint32_t s = e4m3_encode(t);
+// rn32(a / 6) for a >= 0. From 2^-125 up, the product with rn32(1/6) corrected by one fused
+// remainder step (Markstein's division method, "IA-64 and Elementary Functions", 2000) is the
+// correctly rounded quotient; an exhaustive device check against the IEEE division over every
+// non-negative binary32 found mismatches only below 2^-125 (subnormal quotients), which take
+// the IEEE division.
+__device__ __forceinline__ float div6(float a) {
+  constexpr float kSixth = 1.0f / 6.0f;
+  const float q0 = a * kSixth;
+  const float r = __builtin_fmaf(-q0, 6.0f, a);
+  float q = __builtin_fmaf(r, kSixth, q0);
+  if (a < 0x1p-125f) q = a / 6.0f;
+  return q;
+}
+
+// Element multiplier of a block with scale code s: min(rn32(s_enc / dec(s)), FLT_MAX), 0 for a
+// zero scale.
+__device__ __forceinline__ float block_recip(uint32_t s, float s_enc) {
   const float d = e4m3_decode(s);
-  const float r = d > 0.0f ? fminf(s_enc / d, kFltMax) : 0.0f;
-  return BlockScale{s, r};
+  return d > 0.0f ? fminf(s_enc / d, kFltMax) : 0.0f;
+}
+
+__device__ __forceinline__ BlockScale block_scale(float block_amax, float s_enc) {
+  const uint32_t s = e4m3_encode(div6(block_amax) * s_enc);
+  return BlockScale{s, block_recip(s, s_enc)};
+}
+
+// The same with the multipliers of all 127 scale codes precomputed for one tensor scale
+// (build_recip_table: once per workgroup, then a barrier), so a block costs a table read
+// instead of a division.
+__device__ __forceinline__ void build_recip_table(float s_enc, float* table) {
+  for (uint32_t c = threadIdx.x; c < 128u; c += blockDim.x) table[c] = block_recip(c, s_enc);
+}
+
+__device__ __forceinline__ BlockScale block_scale_table(float block_amax, float s_enc,
+                                                        const float* table) {
+  const uint32_t s = e4m3_encode(div6(block_amax) * s_enc);   // <= 0x7E
+  return BlockScale{s, table[s]};
 }
 
 // Encode 16 values v[0..15] (already in float) into two code words (element j -> nibble j).

@@ -273,6 +273,11 @@ __global__ __launch_bounds__(kThreads) void k_encode_1x16(
   }
   float s_enc = tensor_encode_scale(a0);
   int64_t cur_seg = -1;
+  __shared__ float rtab[SEG ? 1 : 128];          // block multipliers of the one tensor scale
+  if constexpr (!SEG) {
+    build_recip_table(s_enc, rtab);
+    __syncthreads();
+  }
 
   while (it < rows) {
     int64_t it_n = it, b0_n = b0 + kSpan;
@@ -298,7 +303,9 @@ __global__ __launch_bounds__(kThreads) void k_encode_1x16(
       cur.get(u, lane, v);                       // all lanes: the exchange is wave-wide
       const int64_t b = b0 + C::block_of(lane, u);
       if (b < nb) {
-        const BlockScale bs = block_scale(abs_max16(v), s_enc);
+        BlockScale bs;
+        if constexpr (SEG) bs = block_scale(abs_max16(v), s_enc);
+        else bs = block_scale_table(abs_max16(v), s_enc, rtab);
         u32x4 rnd{0, 0, 0, 0};
         if constexpr (SR) rnd = block_random((uint64_t)(r * nb + b), seed, offset);
         uint32_t lo, hi;

@@ -108,6 +108,7 @@ __global__ __launch_bounds__(kThreads) void k_rht(
   __shared__ float red[kWaves];
   __shared__ __attribute__((aligned(16))) uint8_t tc[ENCODE ? kTileCols : 1][kTileBlocks * 8];
   __shared__ __attribute__((aligned(16))) uint8_t ts[ENCODE ? kTileCols : 1][kTileBlocks];
+  __shared__ float rtab[ENCODE ? 128 : 1];       // block multipliers of the tensor scale
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t nbt = tokens >> 4;
@@ -156,6 +157,8 @@ __global__ __launch_bounds__(kThreads) void k_rht(
     }
     s_enc = tensor_encode_scale(a);
     if (blockIdx.x == 0 && threadIdx.x == 0) gscale[0] = tensor_decode_scale(a);
+    build_recip_table(s_enc, rtab);
+    __syncthreads();
   }
 
   float m = 0.0f, mp = 0.0f;                                // max|Hx|, max|x| (PLAIN)
@@ -194,7 +197,7 @@ __global__ __launch_bounds__(kThreads) void k_rht(
           }
         } else {
           const int64_t row = c + q;                        // output row = input column
-          const BlockScale bs = block_scale(bm, s_enc);
+          const BlockScale bs = block_scale_table(bm, s_enc, rtab);
           u32x4 rnd{0, 0, 0, 0};
           if constexpr (SR) rnd = block_random((uint64_t)(row * nbt + tb), seed, offset);
           uint32_t lo, hi;
