@@ -279,7 +279,9 @@ __global__ __launch_bounds__(kThreads) void k_encode_1x16(
     __syncthreads();
   }
 
-  while (it < rows) {
+  // One chunk: request the next chunk into `nxt`, encode `cur`. The loop alternates the two
+  // buffers (no register copies between chunks).
+  auto step = [&](C& cur, C& nxt) {
     int64_t it_n = it, b0_n = b0 + kSpan;
     if (b0_n >= nb) {
       b0_n = 0;
@@ -314,9 +316,13 @@ __global__ __launch_bounds__(kThreads) void k_encode_1x16(
         sr[b] = (uint8_t)bs.code;
       }
     }
-    cur = nxt;
     it = it_n;
     b0 = b0_n;
+  };
+  while (it < rows) {
+    step(cur, nxt);
+    if (it >= rows) break;
+    step(nxt, cur);
   }
 }
 
