@@ -162,7 +162,9 @@ __global__ __launch_bounds__(kThreads) void k_rht(
   }
 
   float m = 0.0f, mp = 0.0f;                                // max|Hx|, max|x| (PLAIN)
-  while (it < tiles) {                                      // uniform across the workgroup
+  // One token block: request the next one into `nxt`, transform `cur`. The loop alternates
+  // the two register sets (no copies between blocks).
+  auto step = [&](Pair<TIn> (&cur)[16], Pair<TIn> (&nxt)[16]) {
     int64_t it_n = it;
     int k_n = k + 1;
     if (k_n == kBlocksPerWave) {
@@ -233,10 +235,13 @@ __global__ __launch_bounds__(kThreads) void k_rht(
         __syncthreads();                                    // LDS reused by the next tile
       }
     }
-#pragma unroll
-    for (int j = 0; j < 16; ++j) cur[j] = nxt[j];
     it = it_n;
     k = k_n;
+  };
+  while (it < tiles) {                                      // uniform across the workgroup
+    step(cur, nxt);
+    if (it >= tiles) break;
+    step(nxt, cur);
   }
   if constexpr (!ENCODE) {
     m = block_max(m, red);
