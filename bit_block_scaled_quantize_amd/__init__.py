@@ -5,8 +5,8 @@ Every function marshals torch tensors (device memory, current stream) into the C
 returns; all arithmetic runs in the HIP kernels. If the library is not built the import
 still succeeds but every call raises, so nothing can silently fall back to another path.
 
-Names follow the C entry points: quantize, rht_quantize, gemm, grouped_gemm, amax,
-amax_pair, dequantize.
+Names follow the C entry points: quantize, rht_quantize, gemm, grouped_gemm, grouped_gemm_k,
+amax, amax_pair, dequantize.
 """
 from __future__ import annotations
 
@@ -27,6 +27,7 @@ _ROUND = {"rn": 0, "sr": 1}
 OP_QUANTIZE, OP_RHT_QUANTIZE, OP_GEMM, OP_GROUPED_GEMM, OP_AMAX_PAIR = 0, 1, 2, 3, 4
 
 EXPORTED = ("nvfp4_quantize", "nvfp4_rht_quantize", "nvfp4_gemm", "nvfp4_grouped_gemm",
+            "nvfp4_grouped_gemm_k",
             "nvfp4_amax", "nvfp4_amax_pair", "nvfp4_workspace_size", "nvfp4_last_error",
             "nvfp4_dequantize")
 
@@ -59,6 +60,7 @@ def _load():
                                        ctypes.c_int, u64, u64, vp, pt, vp, sz, vp]
     lib.nvfp4_gemm.argtypes = [pt, pt, vp, i64, vp]
     lib.nvfp4_grouped_gemm.argtypes = [i64, vp, pt, pt, i64, vp, i64, vp, sz, vp]
+    lib.nvfp4_grouped_gemm_k.argtypes = [i64, vp, pt, pt, vp, i64, vp]
     lib.nvfp4_amax.argtypes = [vp, ctypes.c_int, i64, i64, i64, vp, i64, ctypes.c_int,
                                ctypes.c_uint16, vp, vp, sz, vp]
     lib.nvfp4_amax_pair.argtypes = [vp, ctypes.c_int, i64, i64, i64, ctypes.c_uint16, vp, vp, sz, vp]
@@ -205,6 +207,20 @@ def grouped_gemm(m_offsets: torch.Tensor, a: NVFP4Tensor, b: NVFP4Tensor, n: int
     ac, bc = a.c(), b.c()
     _check(lib.nvfp4_grouped_gemm(G, _ptr(m_offsets), ctypes.byref(ac), ctypes.byref(bc), n,
                                   _ptr(out), out.stride(0), None, 0, _stream(stream)))
+    return out
+
+
+def grouped_gemm_k(k_offsets: torch.Tensor, a: NVFP4Tensor, b: NVFP4Tensor,
+                   out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """nvfp4_grouped_gemm_k: for each group g, columns k_offsets[g]:k_offsets[g+1] of A [M, K]
+    and B [N, K] into rows g*M:(g+1)*M of D [G*M, N] (FP32)."""
+    lib = _load()
+    G = k_offsets.numel() - 1
+    if out is None:
+        out = torch.empty((G * a.rows, b.rows), dtype=torch.float32, device=a.codes.device)
+    ac, bc = a.c(), b.c()
+    _check(lib.nvfp4_grouped_gemm_k(G, _ptr(k_offsets), ctypes.byref(ac), ctypes.byref(bc),
+                                    _ptr(out), out.stride(0), _stream(stream)))
     return out
 
 

@@ -63,6 +63,35 @@ def build(verbose: bool = False) -> str:
     return LIB_PATH
 
 
+def resource_usage() -> dict[str, dict[str, int]]:
+    """Per-kernel register and scratch use reported by the compiler for every source (device
+    code only, nothing written): {mangled kernel name: {"vgpr", "agpr", "scratch"}}."""
+    hipcc = _hipcc()
+    out: dict[str, dict[str, int]] = {}
+
+    def one(src):
+        cmd = [hipcc, *HIPCC_FLAGS, "--cuda-device-only", "-S", "-o", os.devnull, src,
+               "-Rpass-analysis=kernel-resource-usage"]
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError(f"hipcc failed for {src}:\n{res.stderr}")
+        return res.stderr
+
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(sources()))) as ex:
+        logs = list(ex.map(one, sources()))
+    for log in logs:
+        name = None
+        for line in log.splitlines():
+            if "Function Name:" in line:
+                name = line.split("Function Name:")[1].strip()
+                out[name] = {}
+            elif name is not None:
+                for key, tag in (("vgpr", "VGPRs:"), ("agpr", "AGPRs:"), ("scratch", "ScratchSize [bytes/lane]:")):
+                    if tag in line:
+                        out[name][key] = int(line.split(tag)[1].split()[0])
+    return out
+
+
 if __name__ == "__main__":
     build(verbose=True)
     sys.exit(0)

@@ -246,6 +246,22 @@ int nvfp4_grouped_gemm(int64_t G, const int64_t* m_offsets, const nvfp4_tensor* 
                                                (hipStream_t)hip_stream), "grouped gemm");
 }
 
+int nvfp4_grouped_gemm_k(int64_t G, const int64_t* k_offsets, const nvfp4_tensor* A,
+                         const nvfp4_tensor* B, float* D, int64_t ldd, void* hip_stream) {
+  int st;
+  if (G < 1) return fail(NVFP4_ERR_INVALID, "G (%lld) must be >= 1", (long long)G);
+  if (!k_offsets) return fail(NVFP4_ERR_INVALID, "k_offsets is NULL");
+  if ((st = check_operand(A, "A")) || (st = check_operand(B, "B"))) return st;
+  if (A->cols != B->cols) return fail(NVFP4_ERR_INVALID, "K mismatch: A has %lld, B has %lld", (long long)A->cols, (long long)B->cols);
+  if (A->cols % 64) return fail(NVFP4_ERR_UNSUPPORTED, "K (%lld) must be a multiple of 64", (long long)A->cols);
+  if (!D) return fail(NVFP4_ERR_INVALID, "D is NULL");
+  if (ldd < B->rows) return fail(NVFP4_ERR_INVALID, "ldd (%lld) < N (%lld)", (long long)ldd, (long long)B->rows);
+  const nvfp4::GemmOperand a{A->codes, A->scales, A->global_scale};
+  const nvfp4::GemmOperand b{B->codes, B->scales, B->global_scale};
+  return hip_status(nvfp4::launch_grouped_gemm_k(G, k_offsets, a, b, A->rows, B->rows, A->cols, D, ldd,
+                                                 (hipStream_t)hip_stream), "grouped gemm (K groups)");
+}
+
 int nvfp4_dequantize(const nvfp4_tensor* q, const int64_t* segments, int64_t nseg, float* y,
                      void* hip_stream) {
   int st;

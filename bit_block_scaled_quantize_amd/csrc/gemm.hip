@@ -197,13 +197,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, int64
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
 }
 
-// One output tile of shape C over K steps [s0, s1) (128 elements each). With `accumulate` the
-// scaled partial sums are added to D with hardware float atomics (D pre-zeroed by the
-// caller), else stored.
-template <class C>
+// One output tile of shape C summing over the elements [k_begin, k_end) of the contraction
+// (both multiples of 64; K is the operands' row length; a k_begin that is not a multiple of
+// 128 needs FIRST_HALF). With `accumulate` the scaled partial sums are added to D with
+// hardware float atomics (D pre-zeroed by the caller), else stored.
+template <class C, bool FIRST_HALF = false>
 __device__ __forceinline__ void gemm_tile_big(Operand A, Operand B, int64_t m0, int64_t m1,
-                                              int64_t n0, int64_t n1, int64_t K, int64_t s0_,
-                                              int64_t s1_, bool accumulate, float alpha,
+                                              int64_t n0, int64_t n1, int64_t K, int64_t k_begin,
+                                              int64_t k_end, bool accumulate, float alpha,
                                               float* __restrict__ D, int64_t ldd, uint8_t* lds) {
   using big::kFragBytes;
   using big::kFragScaleBytes;
@@ -220,10 +221,10 @@ __device__ __forceinline__ void gemm_tile_big(Operand A, Operand B, int64_t m0, 
   const int wm = wave / C::kWavesN, wn = wave % C::kWavesN;
   const uint32_t rs_codes = (uint32_t)(K >> 1), rs_scales = (uint32_t)(K >> 4);
   constexpr uint32_t kBeyond = 0x80000000u;                  // > any 31-bit buffer size
-  // K steps as uniform 32-bit values, so the step loop and the per-step DMA offsets stay in
-  // scalar registers
-  const int s0 = __builtin_amdgcn_readfirstlane((int)s0_);
-  const int s1 = __builtin_amdgcn_readfirstlane((int)s1_);
+  // K steps (128 elements) as uniform 32-bit values, so the step loop and the per-step DMA
+  // offsets stay in scalar registers
+  const int s0 = __builtin_amdgcn_readfirstlane((int)(k_begin / kStepK));
+  const int s1 = __builtin_amdgcn_readfirstlane((int)((k_end + kStepK - 1) / kStepK));
 
   const __amdgpu_buffer_rsrc_t a_codes = make_rsrc(A.codes, A.rows * (K >> 1));
   const __amdgpu_buffer_rsrc_t b_codes = make_rsrc(B.codes, B.rows * (K >> 1));
@@ -239,14 +240,15 @@ __device__ __forceinline__ void gemm_tile_big(Operand A, Operand B, int64_t m0, 
   // the fragment's and step's part (uniform, scalar), so each DMA costs one vector add.
   const uint32_t lane_codes = (uint32_t)r * rs_codes + (uint32_t)(h * 32);
   const uint32_t lane_scales = (uint32_t)r * rs_scales + (uint32_t)(h * 4);
-  // Scale blocks at or past K. With K % 64 == 0 a lane's scale dword of a step (4 blocks)
-  // lies wholly inside K, except in a last half step (K % 128 == 64), where lanes of half 1
-  // would read the next row's scales: there their offset is pushed out of range so the DMA
-  // delivers zero scales, which zero whatever codes they meet. (When the step is not live
-  // either, the two pushes wrap to an in-range offset of a dummy load whose LDS buffer is
-  // never read.)
-  const int last_half_step = (K % kStepK) ? (int)(K / kStepK) : -1;
-  const uint32_t lane_scales_last = lane_scales + (h ? kBeyond : 0u);
+  // Scale blocks outside [k_begin, k_end). With both ends multiples of 64 a lane's scale dword
+  // of a step (4 blocks) lies wholly inside or outside the range; only a first half step
+  // (k_begin % 128 == 64: half 0 lies before the range) and a last half step (k_end % 128 ==
+  // 64: half 1 lies past it, in the next group or the next row) have lanes outside. Their
+  // offset is pushed out of range so the DMA delivers zero scales, which zero whatever codes
+  // they meet. (When the step is not live either, the two pushes wrap to an in-range offset
+  // of a dummy load whose LDS buffer is never read.)
+  const int first_half_step = (k_begin % kStepK) ? (int)(k_begin / kStepK) : -1;
+  const int last_half_step = (k_end % kStepK) ? (int)(k_end / kStepK) : -1;
   const uint32_t row_a = __builtin_amdgcn_readfirstlane((uint32_t)(m0 + wave * 32));
   const uint32_t row_b = __builtin_amdgcn_readfirstlane((uint32_t)(n0 + wave * 32));
 
@@ -273,7 +275,14 @@ __device__ __forceinline__ void gemm_tile_big(Operand A, Operand B, int64_t m0, 
                                                16, lane_codes + (live ? su : kBeyond), 0, 0, 0);
     } else {
       const uint32_t su = row * rs_scales + (uint32_t)(step * (kStepK / 16));
-      const uint32_t lsc = step == last_half_step ? lane_scales_last : lane_scales;
+      uint32_t lsc;
+      if constexpr (FIRST_HALF) {
+        const uint32_t push_h0 = step == first_half_step ? kBeyond : 0u;   // uniform
+        const uint32_t push_h1 = step == last_half_step ? kBeyond : 0u;
+        lsc = lane_scales + (h ? push_h1 : push_h0);
+      } else {
+        lsc = lane_scales + (step == last_half_step ? (h ? kBeyond : 0u) : 0u);
+      }
       __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a ? a_scales : b_scales,
                                                (lds_ptr_t)(real ? base + kCodeBytes + f * kFragScaleBytes : pad),
                                                4, lsc + (live ? su : kBeyond), 0, 0, 0);
@@ -461,8 +470,9 @@ void k_gemm_big(Operand A, const float* __restrict__ ag, Operand B, const float*
   const int64_t m0 = tm * kBlockM, n0 = tn * kBlockN;
   const int64_t m1 = m0 + kBlockM < A.rows ? m0 + kBlockM : A.rows;
   const int64_t n1 = n0 + kBlockN < B.rows ? n0 + kBlockN : B.rows;
-  gemm_tile_big<Full>(A, B, m0, m1, n0, n1, K, s0, s1, blockIdx.x >= tail_first, ag[0] * bg[0], D,
-                      ldd, lds_dyn);
+  const int64_t k_end = s1 * kStepK < K ? s1 * kStepK : K;
+  gemm_tile_big<Full>(A, B, m0, m1, n0, n1, K, s0 * kStepK, k_end, blockIdx.x >= tail_first,
+                      ag[0] * bg[0], D, ldd, lds_dyn);
 }
 
 // Zeroes the D region of the K-split tiles tail_first, tail_first + 1, ... of k_gemm_big:
@@ -516,16 +526,42 @@ void k_grouped_gemm_big(int64_t G, const int64_t* __restrict__ off, Operand A,
   const int64_t n0 = tn * kBlockN;
   const int64_t n1 = n0 + kBlockN < N ? n0 + kBlockN : N;
   const Operand Bg{B.codes + g * N * (K >> 1), B.scales + g * N * (K >> 4), N};
-  const int64_t steps = (K + kStepK - 1) / kStepK;
   const float alpha = ag[g] * bg[g];
   // a last column at most 64 wide and a group's last slot at most 128 high take the narrower
   // tiles, which cost about a quarter and a half of the full one
   if (n1 - n0 <= NTail::kBlockN)
-    gemm_tile_big<NTail>(A, Bg, m0, m1, n0, n1, K, 0, steps, false, alpha, D, ldd, lds_dyn);
+    gemm_tile_big<NTail>(A, Bg, m0, m1, n0, n1, K, 0, K, false, alpha, D, ldd, lds_dyn);
   else if (m1 - m0 <= MTail::kBlockM)
-    gemm_tile_big<MTail>(A, Bg, m0, m1, n0, n1, K, 0, steps, false, alpha, D, ldd, lds_dyn);
+    gemm_tile_big<MTail>(A, Bg, m0, m1, n0, n1, K, 0, K, false, alpha, D, ldd, lds_dyn);
   else
-    gemm_tile_big<Full>(A, Bg, m0, m1, n0, n1, K, 0, steps, false, alpha, D, ldd, lds_dyn);
+    gemm_tile_big<Full>(A, Bg, m0, m1, n0, n1, K, 0, K, false, alpha, D, ldd, lds_dyn);
+}
+
+// Groups along the contraction: group g sums over elements [koff[g], koff[g+1]) of A's and B's
+// rows into its own M x N block of D (rows g*M ..). Workgroup b: group b / tiles, tile b % tiles
+// (XCD-aware order within the group). Offsets are clamped into [0, K] and made non-decreasing;
+// an empty group writes zeros.
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void k_grouped_gemm_k_big(int64_t G, const int64_t* __restrict__ koff, Operand A,
+                          const float* __restrict__ ag, Operand B, const float* __restrict__ bg,
+                          int64_t K, float* __restrict__ D, int64_t ldd) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds_dyn[];
+  using namespace big;
+  const int64_t tiles_m = (A.rows + kBlockM - 1) / kBlockM;
+  const int64_t tiles_n = (B.rows + kBlockN - 1) / kBlockN;
+  const int64_t tiles = tiles_m * tiles_n;
+  const int64_t g = blockIdx.x / tiles;
+  if (g >= G) return;
+  int64_t tm, tn;
+  tile_of(blockIdx.x - g * tiles, tiles_m, tiles_n, tm, tn);
+  int64_t k0 = koff[g], k1 = koff[g + 1];
+  k0 = k0 < 0 ? 0 : (k0 > K ? K : k0);
+  k1 = k1 < k0 ? k0 : (k1 > K ? K : k1);
+  const int64_t m0 = tm * kBlockM, n0 = tn * kBlockN;
+  const int64_t m1 = m0 + kBlockM < A.rows ? m0 + kBlockM : A.rows;
+  const int64_t n1 = n0 + kBlockN < B.rows ? n0 + kBlockN : B.rows;
+  gemm_tile_big<Full, true>(A, B, m0, m1, n0, n1, K, k0, k1, false, ag[g] * bg[g],
+                            D + g * A.rows * ldd, ldd, lds_dyn);
 }
 
 // =========================================================================================
@@ -687,7 +723,10 @@ hipError_t enable_big_lds() {
     hipError_t e = hipFuncSetAttribute((const void*)k_gemm_big,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, big::kLdsBytes);
     if (e != hipSuccess) return e;
-    return hipFuncSetAttribute((const void*)k_grouped_gemm_big,
+    e = hipFuncSetAttribute((const void*)k_grouped_gemm_big,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, big::kLdsBytes);
+    if (e != hipSuccess) return e;
+    return hipFuncSetAttribute((const void*)k_grouped_gemm_k_big,
                                hipFuncAttributeMaxDynamicSharedMemorySize, big::kLdsBytes);
   }();
   return once;
@@ -750,6 +789,19 @@ hipError_t launch_grouped_gemm(int64_t G, const int64_t* m_offsets, GemmOperand 
     hipLaunchKernelGGL(k_grouped_gemm_small, dim3((unsigned)(slots_m * tiles_n)), dim3(kThreads),
                        0, stream, G, m_offsets, A, a.global_scale, B, b.global_scale, N, K, D, ldd);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_grouped_gemm_k(int64_t G, const int64_t* k_offsets, GemmOperand a, GemmOperand b,
+                                 int64_t M, int64_t N, int64_t K, float* D, int64_t ldd,
+                                 hipStream_t stream) {
+  if (M == 0 || N == 0) return hipSuccess;
+  const hipError_t e = enable_big_lds();
+  if (e != hipSuccess) return e;
+  const Operand A{a.codes, a.scales, M}, B{b.codes, b.scales, N};
+  const int64_t tiles = ((M + big::kBlockM - 1) / big::kBlockM) * ((N + big::kBlockN - 1) / big::kBlockN);
+  hipLaunchKernelGGL(k_grouped_gemm_k_big, dim3((unsigned)(G * tiles)), dim3(kThreads), big::kLdsBytes,
+                     stream, G, k_offsets, A, a.global_scale, B, b.global_scale, K, D, ldd);
   return hipGetLastError();
 }
 

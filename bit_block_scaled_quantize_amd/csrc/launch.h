@@ -59,6 +59,11 @@ hipError_t launch_grouped_gemm(int64_t G, const int64_t* m_offsets, GemmOperand 
                                int64_t total_m, int64_t N, int64_t K, float* D, int64_t ldd,
                                hipStream_t stream);
 
+// Groups along K (k_offsets: G + 1 multiples of 64), D [G*M, N]; K % 64 == 0.
+hipError_t launch_grouped_gemm_k(int64_t G, const int64_t* k_offsets, GemmOperand a, GemmOperand b,
+                                 int64_t M, int64_t N, int64_t K, float* D, int64_t ldd,
+                                 hipStream_t stream);
+
 hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* scales, const float* gscale,
                              const int64_t* segments, int64_t nseg, int64_t rows, int64_t cols,
                              float* y, hipStream_t stream);

@@ -161,6 +161,25 @@ int nvfp4_grouped_gemm(int64_t G, const int64_t* m_offsets, const nvfp4_tensor* 
                        void* workspace, size_t ws_bytes, void* hip_stream);
 
 /*
+ * nvfp4_grouped_gemm_k - GEMMs grouped along the contraction dimension, as the MoE weight
+ * gradient needs: expert g's gradient sums over the tokens routed to it ("Nemotron NVFP4"
+ * explainer, "The model underneath": expert layers; "Why 4-bit training normally falls apart -
+ * and the three fixes": the weight-gradient GEMM). For g < G:
+ *   D[g*M + m, n] = A.global_scale[g] * B.global_scale[g] *
+ *                   sum over k in [k_offsets[g], k_offsets[g+1]) of a[m, k] * b[n, k]
+ * with a, b the E2M1 x E4M3 values, FP32 accumulation.
+ *   A          NVFP4 [M, K], B NVFP4 [N, K], quantized along K, each with global_scale[G]
+ *              (one per group of K).
+ *   k_offsets  device int64[G+1], non-decreasing, multiples of 64 (unchecked device data:
+ *              values are clamped into [0, K]; misaligned ones give unspecified output).
+ *   D          device FP32 [G*M, N] with row stride ldd >= N; an empty group writes zeros.
+ * Errors: NVFP4_ERR_INVALID (G < 1, NULL pointers, K mismatch, ldd < N), NVFP4_ERR_UNSUPPORTED
+ * (K % 64 != 0), NVFP4_ERR_HIP.
+ */
+int nvfp4_grouped_gemm_k(int64_t G, const int64_t* k_offsets, const nvfp4_tensor* A,
+                         const nvfp4_tensor* B, float* D, int64_t ldd, void* hip_stream);
+
+/*
  * nvfp4_amax - max|x| of x[rows, cols] (row stride ld), per row segment, into device
  * amax_out[nseg]: the first level of the two-level scale ("Nemotron NVFP4" explainer, "What
  * NVFP4 actually is": one FP32 scale per tensor). With rht != 0 the maximum is taken over the

@@ -11,6 +11,9 @@ Reading R13: D[m, n] = sum_k A_hat[m, k] * B_hat[n, k] with both operands stored
 is accepted iff |D - D64| <= 1e-5 * sum_k |A_hat[m,k]| |B_hat[n,k]| for every element.
 Reading R14: the grouped GEMM is one such GEMM per group g over rows
 m_offsets[g]..m_offsets[g+1] of A and rows g*N..(g+1)*N of the stacked B.
+Reading R15: the MoE weight gradient groups along the contraction instead: group g sums
+over columns k_offsets[g]..k_offsets[g+1] (the tokens routed to expert g) of A [M, K] and
+B [N, K] into its own [M, N] block, stacked along rows; an empty group gives zeros.
 """
 from __future__ import annotations
 
@@ -45,4 +48,31 @@ def grouped_gemm_bound(a_hat, b_hat, m_offsets, n: int, rel: float = 1e-5) -> np
         lo, hi = int(off[g]) - int(off[0]), int(off[g + 1]) - int(off[0])
         if hi > lo:
             out[lo:hi] = gemm_bound(a_hat[lo:hi], b_hat[g * n:(g + 1) * n], rel)
+    return out
+
+
+def grouped_gemm_k_fp64(a_hat, b_hat, k_offsets) -> np.ndarray:
+    """R15: D[g*M:(g+1)*M] = A[:, k_g] @ B[:, k_g]^T over k_g = k_offsets[g]..k_offsets[g+1]."""
+    a = np.asarray(a_hat, np.float64)
+    b = np.asarray(b_hat, np.float64)
+    off = np.asarray(k_offsets, dtype=np.int64)
+    m, n = a.shape[0], b.shape[0]
+    out = np.zeros(((len(off) - 1) * m, n), dtype=np.float64)
+    for g in range(len(off) - 1):
+        lo, hi = int(off[g]), int(off[g + 1])
+        if hi > lo:
+            out[g * m:(g + 1) * m] = gemm_fp64(a[:, lo:hi], b[:, lo:hi])
+    return out
+
+
+def grouped_gemm_k_bound(a_hat, b_hat, k_offsets, rel: float = 1e-5) -> np.ndarray:
+    a = np.asarray(a_hat, np.float64)
+    b = np.asarray(b_hat, np.float64)
+    off = np.asarray(k_offsets, dtype=np.int64)
+    m, n = a.shape[0], b.shape[0]
+    out = np.zeros(((len(off) - 1) * m, n), dtype=np.float64)
+    for g in range(len(off) - 1):
+        lo, hi = int(off[g]), int(off[g + 1])
+        if hi > lo:
+            out[g * m:(g + 1) * m] = gemm_bound(a[:, lo:hi], b[:, lo:hi], rel)
     return out

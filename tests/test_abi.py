@@ -113,6 +113,18 @@ def test_gemm_validation(lib):
     assert gg(2, FAKE, ctypes.byref(a), ctypes.byref(b), 8, FAKE, 8, None, 0, None) == INVALID  # B rows
 
 
+def test_grouped_gemm_k_validation(lib):
+    a, b = _tensor(64, 128), _tensor(32, 128)
+    f = lib.nvfp4_grouped_gemm_k
+    assert f(0, FAKE, ctypes.byref(a), ctypes.byref(b), FAKE, 32, None) == INVALID          # G
+    assert f(2, None, ctypes.byref(a), ctypes.byref(b), FAKE, 32, None) == INVALID          # offsets
+    assert f(2, FAKE, ctypes.byref(a), ctypes.byref(_tensor(32, 96)), FAKE, 32, None) == INVALID
+    assert f(2, FAKE, ctypes.byref(a), ctypes.byref(b), None, 32, None) == INVALID          # D
+    assert f(2, FAKE, ctypes.byref(a), ctypes.byref(b), FAKE, 16, None) == INVALID          # ldd
+    assert f(2, FAKE, ctypes.byref(_tensor(64, 96)), ctypes.byref(_tensor(32, 96)), FAKE, 32,
+             None) == UNSUPPORTED                                                         # K % 64
+
+
 def test_workspace_sizes(lib):
     assert lib.nvfp4_workspace_size(nv.OP_QUANTIZE, 10, 16, 1) == 4096      # 1024 partial maxima
     assert lib.nvfp4_workspace_size(nv.OP_QUANTIZE, 10, 16, 2000) == 8192   # one slot per segment

@@ -9,7 +9,7 @@ import bit_block_scaled_quantize_amd as nv
 import oracle
 import workloads
 from helpers import (assert_gemm_within_bound, assert_quant_equal, f32, host, log,
-                     to_device_bf16)
+                     to_device_bf16, to_device_f32)
 
 pytestmark = pytest.mark.gpu
 
@@ -160,6 +160,54 @@ def test_grouped_gemm_tile_shapes(n, k):
     bound = oracle.grouped_gemm_bound(xh, wh, off, n)
     assert np.all(np.abs(o[:, :n] - d64) <= bound)
     del d
+
+
+@pytest.mark.parametrize("m,n,offs", [
+    (300, 520, [0, 64, 64, 448, 1024, 1920]),     # empty group, half steps at both ends
+    (256, 256, [128, 192, 1856]),                 # groups not starting at 0 / ending before K
+    (70, 33, [0, 1920]),                          # one group, ragged M and N
+    (513, 300, [0, 640, 1280, 1344, 1920]),       # a 64-wide group inside one K step
+])
+def test_grouped_gemm_k(m, n, offs):
+    """GEMMs grouped along K (MoE weight gradient): each group's block against the FP64
+    reference on the group's columns, per-group global scales, a padded output row stride."""
+    log(f"grouped gemm K {m}x{n} {offs}")
+    k = 1920
+    G = len(offs) - 1
+    rng = np.random.default_rng(m + n + G)
+    a = (rng.standard_normal((m, k)) * 2).astype(np.float32)
+    b = rng.standard_normal((n, k)).astype(np.float32)
+    qa, _ = nv.quantize(to_device_f32(a), "1x16", "rn")
+    qb, _ = nv.quantize(to_device_f32(b), "1x16", "sr", seed=5)
+    ra = oracle.quantize_1x16(a)
+    rb = oracle.quantize_1x16(b, "sr", seed=5)
+    assert_quant_equal(host(qa), ra, "A")
+    assert_quant_equal(host(qb), rb, "B")
+    sa = np.array([2.0 ** (g % 3 - 1) for g in range(G)], np.float32) * ra[2][0]
+    sb = np.array([3.0 if g % 2 else 0.75 for g in range(G)], np.float32) * rb[2][0]
+    qa.global_scale = torch.from_numpy(sa).cuda()
+    qb.global_scale = torch.from_numpy(sb).cuda()
+    # dequantized operands with group g's columns scaled by its own global scale
+    ah = oracle.dequantize(ra[0], ra[1], np.ones(1, np.float32))
+    bh = oracle.dequantize(rb[0], rb[1], np.ones(1, np.float32))
+    colscale_a = np.ones(k)
+    colscale_b = np.ones(k)
+    for g in range(G):
+        colscale_a[offs[g]:offs[g + 1]] = sa[g]
+        colscale_b[offs[g]:offs[g + 1]] = sb[g]
+    ah = ah * colscale_a
+    bh = bh * colscale_b
+    out = torch.full((G * m, n + 5), -3.0, dtype=torch.float32, device="cuda")
+    nv.grouped_gemm_k(torch.tensor(offs, dtype=torch.int64, device="cuda"), qa, qb, out=out[:, :n])
+    torch.cuda.synchronize()
+    o = out.cpu().numpy()
+    assert np.all(o[:, n:] == -3.0)
+    d64 = oracle.grouped_gemm_k_fp64(ah, bh, offs)
+    bound = oracle.grouped_gemm_k_bound(ah, bh, offs)
+    assert np.all(np.abs(o[:, :n] - d64) <= bound)
+    for g in range(G):
+        if offs[g + 1] == offs[g]:
+            assert np.all(o[g * m:(g + 1) * m, :n] == 0.0)
 
 
 @pytest.mark.parametrize("mnk", [(513, 1024, 5120), (1000, 700, 1344), (2304, 2560, 1024)])

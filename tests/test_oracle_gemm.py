@@ -65,3 +65,35 @@ def test_grouped_equals_separate():
     d = oracle.grouped_gemm_fp64(a, b, off, 8)
     assert np.array_equal(d[0:10], a[0:10] @ b[0:8].T)
     assert np.array_equal(d[10:40], a[10:40] @ b[16:24].T)
+
+
+def test_k_grouped_blocks_add_up_to_the_whole_contraction():
+    # summing the group blocks over g gives the ungrouped product over the covered columns;
+    # the first group (columns before 5) and an empty group contribute their own blocks
+    rng = np.random.default_rng(2)
+    a = rng.standard_normal((6, 70))
+    b = rng.standard_normal((4, 70))
+    off = np.array([5, 21, 21, 64, 70])
+    d = oracle.grouped_gemm_k_fp64(a, b, off).reshape(4, 6, 4)
+    assert np.allclose(d.sum(axis=0), a[:, 5:] @ b[:, 5:].T, rtol=1e-12, atol=1e-12)
+    assert np.all(d[1] == 0.0)
+
+
+def test_k_grouped_exact_on_small_integers():
+    # integer operands: every partial sum is exact in binary64, so each block equals the
+    # exact integer dot product written out term by term
+    rng = np.random.default_rng(3)
+    a = rng.integers(-8, 9, (3, 40)).astype(np.float64)
+    b = rng.integers(-8, 9, (2, 40)).astype(np.float64)
+    off = [0, 16, 40]
+    d = oracle.grouped_gemm_k_fp64(a, b, off)
+    for g in range(2):
+        for i in range(3):
+            for j in range(2):
+                want = 0
+                for k in range(off[g], off[g + 1]):
+                    want += int(a[i, k]) * int(b[j, k])
+                assert d[g * 3 + i, j] == want
+    bound = oracle.grouped_gemm_k_bound(a, b, off)
+    assert np.all(bound[3:] == 1e-5 * (np.abs(a[:, 16:]) @ np.abs(b[:, 16:]).T))
+
