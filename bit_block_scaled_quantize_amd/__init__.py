@@ -57,7 +57,7 @@ def _load():
     lib.nvfp4_quantize.argtypes = [vp, ctypes.c_int, i64, i64, i64, ctypes.c_int, ctypes.c_int,
                                    u64, u64, vp, i64, vp, pt, pt, vp, sz, vp]
     lib.nvfp4_rht_quantize.argtypes = [vp, ctypes.c_int, i64, i64, i64, ctypes.c_uint16,
-                                       ctypes.c_int, u64, u64, vp, pt, vp, sz, vp]
+                                       ctypes.c_int, u64, u64, vp, i64, vp, pt, vp, sz, vp]
     lib.nvfp4_gemm.argtypes = [pt, pt, vp, i64, vp]
     lib.nvfp4_grouped_gemm.argtypes = [i64, vp, pt, pt, i64, vp, i64, vp, sz, vp]
     lib.nvfp4_grouped_gemm_k.argtypes = [i64, vp, pt, pt, vp, i64, vp]
@@ -164,22 +164,24 @@ def quantize(x: torch.Tensor, block: str = "1x16", rounding: str = "rn", seed: i
 def rht_quantize(x: torch.Tensor, sign_mask: int, rounding: str = "rn", seed: int = 0,
                  offset: int = 0, amax: torch.Tensor | None = None,
                  out: NVFP4Tensor | None = None, workspace: torch.Tensor | None = None,
-                 stream=None) -> NVFP4Tensor:
-    """nvfp4_rht_quantize: x[tokens, cols] -> NVFP4 tensor [cols, tokens]."""
+                 segments: torch.Tensor | None = None, stream=None) -> NVFP4Tensor:
+    """nvfp4_rht_quantize: x[tokens, cols] -> NVFP4 tensor [cols, tokens] (segments: token
+    ranges with one global scale each)."""
     lib = _load()
     dt, tokens, cols, ld = _input(x)
+    nseg = 1 if segments is None else segments.numel() - 1
     if out is None:
-        out = NVFP4Tensor.empty(cols, tokens, 1, x.device)
+        out = NVFP4Tensor.empty(cols, tokens, nseg, x.device)
     ws_n = 0
     if amax is None:
         if workspace is None:
-            workspace, ws_n = _workspace(OP_RHT_QUANTIZE, tokens, cols, 1, x.device)
+            workspace, ws_n = _workspace(OP_RHT_QUANTIZE, tokens, cols, nseg, x.device)
         else:
             ws_n = workspace.numel()
     oc = out.c()
     st = lib.nvfp4_rht_quantize(_ptr(x), dt, tokens, cols, ld, sign_mask & 0xFFFF,
                                 _ROUND[rounding], seed & (2 ** 64 - 1), offset & (2 ** 64 - 1),
-                                _ptr(amax), ctypes.byref(oc),
+                                _ptr(segments), nseg, _ptr(amax), ctypes.byref(oc),
                                 _ptr(workspace) if amax is None else None, ws_n, _stream(stream))
     _check(st)
     return out

@@ -79,7 +79,10 @@ size_t nvfp4_workspace_size(int op, int64_t rows, int64_t cols, int64_t nseg) {
       const size_t segs = (size_t)(nseg < 1 ? 1 : nseg) * sizeof(float);
       return round_up(segs > partials ? segs : partials, kWsAlign);
     }
-    case NVFP4_OP_RHT_QUANTIZE: return round_up(partials, kWsAlign);
+    case NVFP4_OP_RHT_QUANTIZE: {
+      const size_t segs = (size_t)(nseg < 1 ? 1 : nseg) * sizeof(float);
+      return round_up(segs > partials ? segs : partials, kWsAlign);
+    }
     case NVFP4_OP_AMAX_PAIR: return round_up(2 * partials, kWsAlign);
     default: return 0;
   }
@@ -92,10 +95,9 @@ int nvfp4_amax(const void* x, nvfp4_dtype dt, int64_t rows, int64_t cols, int64_
   if (st) return st;
   if (!amax_out) return fail(NVFP4_ERR_INVALID, "amax_out is NULL");
   if (nseg < 1 || (!segments && nseg != 1)) return fail(NVFP4_ERR_INVALID, "bad segment table (nseg=%lld)", (long long)nseg);
-  if (rht && segments) return fail(NVFP4_ERR_UNSUPPORTED, "segments with the Hadamard transform");
   if (rht && rows % 16) return fail(NVFP4_ERR_INVALID, "tokens (%lld) must be a multiple of 16", (long long)rows);
   if (!rht && cols % 16) return fail(NVFP4_ERR_INVALID, "cols (%lld) must be a multiple of 16", (long long)cols);
-  const bool need_ws = rht || !segments;
+  const bool need_ws = !segments;
   if (need_ws) {
     const size_t need = nvfp4_workspace_size(rht ? NVFP4_OP_RHT_QUANTIZE : NVFP4_OP_QUANTIZE, rows, cols, nseg);
     if (!workspace || ws_bytes < need || !aligned(workspace, kWsAlign))
@@ -105,8 +107,12 @@ int nvfp4_amax(const void* x, nvfp4_dtype dt, int64_t rows, int64_t cols, int64_
   const bool f32 = dt == NVFP4_IN_FP32;
   int parts = 1;
   if (rht) {
+    if (segments)                                 // token segments: per-segment maxima directly
+      return hip_status(nvfp4::launch_rht_amax_parts(x, f32, rows, cols, ld, sign_mask, false, segments,
+                                                     nseg, amax_out, &parts, s), "rht amax");
     float* ws = static_cast<float*>(workspace);
-    if ((st = hip_status(nvfp4::launch_rht_amax_parts(x, f32, rows, cols, ld, sign_mask, false, ws, &parts, s), "rht amax"))) return st;
+    if ((st = hip_status(nvfp4::launch_rht_amax_parts(x, f32, rows, cols, ld, sign_mask, false, nullptr, 1,
+                                                      ws, &parts, s), "rht amax"))) return st;
     return hip_status(nvfp4::launch_reduce_partials(ws, parts, amax_out, s), "amax reduce");
   }
   if (segments)
@@ -130,7 +136,7 @@ int nvfp4_amax_pair(const void* x, nvfp4_dtype dt, int64_t tokens, int64_t cols,
   float* ws = static_cast<float*>(workspace);
   int parts = 1;
   if ((st = hip_status(nvfp4::launch_rht_amax_parts(x, dt == NVFP4_IN_FP32, tokens, cols, ld, sign_mask,
-                                                    true, ws, &parts, s), "amax pair")))
+                                                    true, nullptr, 1, ws, &parts, s), "amax pair")))
     return st;
   // partials [0, parts) of |x| and [parts, 2 parts) of |Hx| fold into amax_out[0] and [1]
   return hip_status(nvfp4::launch_reduce_partials(ws, parts, amax_out, s, 2), "amax reduce");
@@ -179,16 +185,17 @@ int nvfp4_quantize(const void* x, nvfp4_dtype dt, int64_t rows, int64_t cols, in
 
 int nvfp4_rht_quantize(const void* x, nvfp4_dtype dt, int64_t tokens, int64_t cols, int64_t ld,
                        uint16_t sign_mask, nvfp4_round rnd, uint64_t seed, uint64_t offset,
-                       const float* amax_in, nvfp4_tensor* out, void* workspace, size_t ws_bytes,
-                       void* hip_stream) {
+                       const int64_t* segments, int64_t nseg, const float* amax_in,
+                       nvfp4_tensor* out, void* workspace, size_t ws_bytes, void* hip_stream) {
   int st = check_input(x, dt, tokens, cols, ld, false);
   if (st) return st;
   if (rnd != NVFP4_ROUND_RN && rnd != NVFP4_ROUND_SR) return fail(NVFP4_ERR_INVALID, "bad rounding mode %d", (int)rnd);
   if (tokens % 16) return fail(NVFP4_ERR_INVALID, "tokens (%lld) must be a multiple of 16", (long long)tokens);
+  if (nseg < 1 || (!segments && nseg != 1)) return fail(NVFP4_ERR_INVALID, "bad segment table (nseg=%lld)", (long long)nseg);
   if ((st = check_out(out, cols, tokens, "out"))) return st;
   const float* amax = amax_in;
   if (!amax) {
-    const size_t need = nvfp4_workspace_size(NVFP4_OP_RHT_QUANTIZE, tokens, cols, 1);
+    const size_t need = nvfp4_workspace_size(NVFP4_OP_RHT_QUANTIZE, tokens, cols, nseg);
     if (!workspace || ws_bytes < need || !aligned(workspace, kWsAlign))
       return fail(NVFP4_ERR_WORKSPACE, "workspace of %zu bytes (256-byte aligned) required, got %zu", need, ws_bytes);
   }
@@ -197,12 +204,13 @@ int nvfp4_rht_quantize(const void* x, nvfp4_dtype dt, int64_t tokens, int64_t co
   int parts = 1;
   if (!amax) {
     float* ws = static_cast<float*>(workspace);
-    if ((st = hip_status(nvfp4::launch_rht_amax_parts(x, f32, tokens, cols, ld, sign_mask, false, ws, &parts, s), "rht amax"))) return st;
+    if ((st = hip_status(nvfp4::launch_rht_amax_parts(x, f32, tokens, cols, ld, sign_mask, false, segments,
+                                                      nseg, ws, &parts, s), "rht amax"))) return st;
     amax = ws;
   }
   const nvfp4::QuantOut q{out->codes, out->scales, out->global_scale};
   return hip_status(nvfp4::launch_rht_encode(x, f32, tokens, cols, ld, sign_mask, rnd == NVFP4_ROUND_SR,
-                                             seed, offset, amax, parts, q, s), "rht encode");
+                                             seed, offset, segments, nseg, amax, parts, q, s), "rht encode");
 }
 
 static int check_operand(const nvfp4_tensor* t, const char* name) {

@@ -36,13 +36,20 @@ hipError_t launch_encode_16x16(const void* x, bool fp32, int64_t rows, int64_t c
 // Hadamard transform along tokens: partial maxima of the transformed tensor (at most 1024;
 // with `plain`, *parts partial maxima of |x| itself come first, then those of the transformed
 // tensor), and the transposed encode.
+// With token segments (device int64[nseg + 1], multiples of 16): partial[0..nseg) receives the
+// per-segment maxima of the transformed tensor (*parts = 1), and the encode takes one tensor
+// scale per segment from amax[segment].
 hipError_t launch_rht_amax_parts(const void* x, bool fp32, int64_t tokens, int64_t cols, int64_t ld,
-                                 uint16_t sign_mask, bool plain, float* partial, int* parts,
-                                 hipStream_t stream);
+                                 uint16_t sign_mask, bool plain, const int64_t* segments,
+                                 int64_t nseg, float* partial, int* parts, hipStream_t stream);
 
 hipError_t launch_rht_encode(const void* x, bool fp32, int64_t tokens, int64_t cols, int64_t ld,
                              uint16_t sign_mask, bool sr, uint64_t seed, uint64_t offset,
-                             const float* amax, int parts, QuantOut out, hipStream_t stream);
+                             const int64_t* segments, int64_t nseg, const float* amax, int parts,
+                             QuantOut out, hipStream_t stream);
+
+// p[0..n) = v
+hipError_t launch_fill(float* p, int64_t n, float v, hipStream_t stream);
 
 constexpr int kMaxAmaxPartials = 1024;
 

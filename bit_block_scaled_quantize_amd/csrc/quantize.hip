@@ -566,6 +566,11 @@ hipError_t launch_amax_parts(const void* x, bool fp32, int64_t rows, int64_t col
   return hipGetLastError();
 }
 
+hipError_t launch_fill(float* p, int64_t n, float v, hipStream_t stream) {
+  hipLaunchKernelGGL(k_fill, dim3(1), dim3(256), 0, stream, p, n, v);
+  return hipGetLastError();
+}
+
 hipError_t launch_reduce_partials(const float* partials, int parts, float* out, hipStream_t stream,
                                   int count) {
   hipLaunchKernelGGL(k_reduce_partials, dim3(count), dim3(kThreads), 0, stream, partials, parts, out);

@@ -99,12 +99,16 @@ __device__ __forceinline__ float block_max(float m, float* red) {
   return r;
 }
 
-template <typename TIn, bool ENCODE, bool SR, bool PLAIN = false>
+// SEG: token segments (the tokens of each expert, multiples of 16) with one tensor scale each:
+// the amax form flushes one atomic max per (wave, run of items in one segment) into
+// partial[segment] (zeroed by the caller), the encode form takes amax[segment] per item.
+template <typename TIn, bool ENCODE, bool SR, bool PLAIN = false, bool SEG = false>
 __global__ __launch_bounds__(kThreads) void k_rht(
     const TIn* __restrict__ x, int64_t tokens, int64_t cols, int64_t ld, uint32_t mask,
     const float* __restrict__ amax, int amax_parts, float* __restrict__ partial,
     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ gscale,
-    uint64_t seed, uint64_t offset) {
+    const int64_t* __restrict__ seg, int64_t nseg, uint64_t seed, uint64_t offset) {
+  static_assert(!(PLAIN && SEG), "the amax pair is unsegmented");
   __shared__ float red[kWaves];
   __shared__ __attribute__((aligned(16))) uint8_t tc[ENCODE ? kTileCols : 1][kTileBlocks * 8];
   __shared__ __attribute__((aligned(16))) uint8_t ts[ENCODE ? kTileCols : 1][kTileBlocks];
@@ -146,8 +150,22 @@ __global__ __launch_bounds__(kThreads) void k_rht(
   int k = 0;
   if (it < tiles) load_item(cur, it, 0);
 
+  // Segment of a token block (the last segment whose first token is at or before the block's
+  // first token, as find_segment): a per-wave cursor that moves from the previous item's
+  // segment, so a walk in either direction costs O(1) table reads per item.
+  int64_t sg = 0;
+  auto seg_of = [&](int64_t tb) {
+    const int64_t tok = tb * 16;
+    while (sg > 0 && seg[sg] > tok) --sg;
+    while (sg + 1 < nseg && seg[sg + 1] <= tok) ++sg;
+    return sg;
+  };
+
   float s_enc = 1.0f;
-  if constexpr (ENCODE) {
+  if constexpr (ENCODE && SEG) {
+    if (blockIdx.x == 0)
+      for (int64_t i = threadIdx.x; i < nseg; i += kThreads) gscale[i] = tensor_decode_scale(amax[i]);
+  } else if constexpr (ENCODE) {
     float a = 0.0f;
     if (amax_parts <= 1) {
       a = amax[0];
@@ -162,6 +180,7 @@ __global__ __launch_bounds__(kThreads) void k_rht(
   }
 
   float m = 0.0f, mp = 0.0f;                                // max|Hx|, max|x| (PLAIN)
+  int64_t m_seg = -1;                                       // SEG amax: segment of m
   // One token block: request the next one into `nxt`, transform `cur`. The loop alternates
   // the two register sets (no copies between blocks).
   auto step = [&](Pair<TIn> (&cur)[16], Pair<TIn> (&nxt)[16]) {
@@ -178,6 +197,20 @@ __global__ __launch_bounds__(kThreads) void k_rht(
     const int bl = wave + 4 * k;                            // token block within the tile
     const int64_t tb = g.TB0 + bl;
     if (tb < nbt) {
+      float se = s_enc;
+      if constexpr (SEG) {
+        const int64_t sgi = seg_of(tb);
+        if constexpr (ENCODE) {
+          se = tensor_encode_scale(amax[sgi]);
+        } else if (sgi != m_seg) {                          // uniform: flush the previous run
+          if (m_seg >= 0) {
+            const float wm = wave_max(m);
+            if (lane == 0) atomic_max_nonneg(partial + m_seg, wm);
+          }
+          m = 0.0f;
+          m_seg = sgi;
+        }
+      }
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
         float v[16], y[16];
@@ -199,7 +232,9 @@ __global__ __launch_bounds__(kThreads) void k_rht(
           }
         } else {
           const int64_t row = c + q;                        // output row = input column
-          const BlockScale bs = block_scale_table(bm, s_enc, rtab);
+          BlockScale bs;
+          if constexpr (SEG) bs = block_scale(bm, se);
+          else bs = block_scale_table(bm, s_enc, rtab);
           u32x4 rnd{0, 0, 0, 0};
           if constexpr (SR) rnd = block_random((uint64_t)(row * nbt + tb), seed, offset);
           uint32_t lo, hi;
@@ -243,7 +278,12 @@ __global__ __launch_bounds__(kThreads) void k_rht(
     if (it >= tiles) break;
     step(nxt, cur);
   }
-  if constexpr (!ENCODE) {
+  if constexpr (!ENCODE && SEG) {
+    if (m_seg >= 0) {
+      const float wm = wave_max(m);
+      if (lane == 0) atomic_max_nonneg(partial + m_seg, wm);
+    }
+  } else if constexpr (!ENCODE) {
     m = block_max(m, red);
     if constexpr (PLAIN) {                                  // [max|x| partials][max|Hx| partials]
       mp = block_max(mp, red);
@@ -263,13 +303,13 @@ int64_t rht_tiles(int64_t tokens, int64_t cols) {
 
 // Workgroups of k_rht<...> that the device keeps resident at once (each walks tiles, so a
 // grid of exactly this many has no second wave of late starters). Queried once per kernel.
-template <typename TIn, bool ENCODE, bool SR>
+template <typename TIn, bool ENCODE, bool SR, bool SEG>
 int64_t resident_groups() {
   static const int64_t n = [] {
     int dev = 0, cus = 0, per_cu = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_rht<TIn, ENCODE, SR>, kThreads, 0) !=
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_rht<TIn, ENCODE, SR, false, SEG>, kThreads, 0) !=
             hipSuccess)
       return (int64_t)1024;
     return (int64_t)(cus > 0 ? cus : 1) * (per_cu > 0 ? per_cu : 1);
@@ -277,28 +317,37 @@ int64_t resident_groups() {
   return n;
 }
 
-template <typename TIn, bool ENCODE, bool SR, bool PLAIN = false>
+template <typename TIn, bool ENCODE, bool SR, bool PLAIN = false, bool SEG = false>
 void launch_rht_t(const void* x, int64_t tokens, int64_t cols, int64_t ld, uint16_t mask,
-                  const float* amax, int parts, float* partial, QuantOut out, uint64_t seed,
-                  uint64_t offset, int grid, hipStream_t stream) {
+                  const float* amax, int parts, float* partial, QuantOut out,
+                  const int64_t* segments, int64_t nseg, uint64_t seed, uint64_t offset, int grid,
+                  hipStream_t stream) {
   if (ENCODE) {
-    const int64_t cap = resident_groups<TIn, ENCODE, SR>();
+    const int64_t cap = resident_groups<TIn, ENCODE, SR, SEG>();
     if (grid > cap) grid = (int)cap;
   }
-  hipLaunchKernelGGL((k_rht<TIn, ENCODE, SR, PLAIN>), dim3(grid), dim3(kThreads), 0, stream,
+  hipLaunchKernelGGL((k_rht<TIn, ENCODE, SR, PLAIN, SEG>), dim3(grid), dim3(kThreads), 0, stream,
                      (const TIn*)x, tokens, cols, ld, (uint32_t)mask, amax, parts, partial,
-                     out.codes, out.scales, out.global_scale, seed, offset);
+                     out.codes, out.scales, out.global_scale, segments, nseg, seed, offset);
 }
 
 }  // namespace
 
 hipError_t launch_rht_amax_parts(const void* x, bool fp32, int64_t tokens, int64_t cols, int64_t ld,
-                                 uint16_t sign_mask, bool plain, float* partial, int* parts,
-                                 hipStream_t stream) {
+                                 uint16_t sign_mask, bool plain, const int64_t* segments,
+                                 int64_t nseg, float* partial, int* parts, hipStream_t stream) {
   const int64_t tiles = rht_tiles(tokens, cols);
   const int grid = (int)(tiles < 1 ? 1 : (tiles < kMaxPartials ? tiles : kMaxPartials));
   const QuantOut none{nullptr, nullptr, nullptr};
-#define NVFP4_RA(T, P) launch_rht_t<T, false, false, P>(x, tokens, cols, ld, sign_mask, nullptr, 0, partial, none, 0, 0, grid, stream)
+  if (segments) {                                 // per-segment maxima straight into partial[nseg]
+    hipError_t e = launch_fill(partial, nseg, 0.0f, stream);
+    if (e != hipSuccess) return e;
+    if (fp32) launch_rht_t<float, false, false, false, true>(x, tokens, cols, ld, sign_mask, nullptr, 0, partial, none, segments, nseg, 0, 0, grid, stream);
+    else      launch_rht_t<uint16_t, false, false, false, true>(x, tokens, cols, ld, sign_mask, nullptr, 0, partial, none, segments, nseg, 0, 0, grid, stream);
+    *parts = 1;
+    return hipGetLastError();
+  }
+#define NVFP4_RA(T, P) launch_rht_t<T, false, false, P>(x, tokens, cols, ld, sign_mask, nullptr, 0, partial, none, nullptr, 1, 0, 0, grid, stream)
   if (fp32) { if (plain) NVFP4_RA(float, true); else NVFP4_RA(float, false); }
   else      { if (plain) NVFP4_RA(uint16_t, true); else NVFP4_RA(uint16_t, false); }
 #undef NVFP4_RA
@@ -308,16 +357,20 @@ hipError_t launch_rht_amax_parts(const void* x, bool fp32, int64_t tokens, int64
 
 hipError_t launch_rht_encode(const void* x, bool fp32, int64_t tokens, int64_t cols, int64_t ld,
                              uint16_t sign_mask, bool sr, uint64_t seed, uint64_t offset,
-                             const float* amax, int parts, QuantOut out, hipStream_t stream) {
+                             const int64_t* segments, int64_t nseg, const float* amax, int parts,
+                             QuantOut out, hipStream_t stream) {
   const int64_t tiles = rht_tiles(tokens, cols);
   const int grid = (int)(tiles < 1 ? 1 : (tiles < (1 << 30) ? tiles : (1 << 30)));   // capped at launch
+#define NVFP4_RE(T, S, G) launch_rht_t<T, true, S, false, G>(x, tokens, cols, ld, sign_mask, amax, parts, nullptr, out, segments, nseg, seed, offset, grid, stream)
+  const bool seg = segments != nullptr;
   if (fp32) {
-    if (sr) launch_rht_t<float, true, true>(x, tokens, cols, ld, sign_mask, amax, parts, nullptr, out, seed, offset, grid, stream);
-    else    launch_rht_t<float, true, false>(x, tokens, cols, ld, sign_mask, amax, parts, nullptr, out, seed, offset, grid, stream);
+    if (sr) { if (seg) NVFP4_RE(float, true, true); else NVFP4_RE(float, true, false); }
+    else    { if (seg) NVFP4_RE(float, false, true); else NVFP4_RE(float, false, false); }
   } else {
-    if (sr) launch_rht_t<uint16_t, true, true>(x, tokens, cols, ld, sign_mask, amax, parts, nullptr, out, seed, offset, grid, stream);
-    else    launch_rht_t<uint16_t, true, false>(x, tokens, cols, ld, sign_mask, amax, parts, nullptr, out, seed, offset, grid, stream);
+    if (sr) { if (seg) NVFP4_RE(uint16_t, true, true); else NVFP4_RE(uint16_t, true, false); }
+    else    { if (seg) NVFP4_RE(uint16_t, false, true); else NVFP4_RE(uint16_t, false, false); }
   }
+#undef NVFP4_RE
   return hipGetLastError();
 }
 

@@ -121,15 +121,24 @@ int nvfp4_quantize(const void* x, nvfp4_dtype dt, int64_t rows, int64_t cols, in
  *   out        tensor [cols, tokens]: row c holds column c's transformed values quantized in
  *              1x16 blocks along tokens (out->rows == cols, out->cols == tokens).
  *   rnd/seed/offset as for nvfp4_quantize (SR block index is over the output [cols, tokens]).
- *   amax_in    NULL or device float[1] = max|y| of the transformed tensor.
- *   workspace  >= nvfp4_workspace_size(NVFP4_OP_RHT_QUANTIZE, tokens, cols, 1) bytes unless
- *              amax_in is given.
- * Errors: as nvfp4_quantize (tokens % 16, cols < 1, ld < cols, ...).
+ *   segments   NULL (nseg must be 1) or device int64[nseg+1] TOKEN offsets, multiples of 16,
+ *              non-decreasing from 0 to tokens: the tokens routed to each expert of a
+ *              mixture-of-experts layer, whose weight gradients are separate GEMMs over their
+ *              own tokens (nvfp4_grouped_gemm_k). Each token range gets its own amax (over its
+ *              transformed values) and global scale: out->global_scale[nseg]; out's column
+ *              range of segment g uses global_scale[g]. A 16-token block belongs to the
+ *              segment of its first token; unchecked device data, never an out-of-bounds
+ *              access.
+ *   amax_in    NULL or device float[nseg] = max|y| of the transformed values per segment.
+ *   workspace  >= nvfp4_workspace_size(NVFP4_OP_RHT_QUANTIZE, tokens, cols, nseg) bytes
+ *              unless amax_in is given.
+ * Errors: as nvfp4_quantize (tokens % 16, cols < 1, ld < cols, nseg < 1, segments == NULL
+ * with nseg != 1, ...).
  */
 int nvfp4_rht_quantize(const void* x, nvfp4_dtype dt, int64_t tokens, int64_t cols, int64_t ld,
                        uint16_t sign_mask, nvfp4_round rnd, uint64_t seed, uint64_t offset,
-                       const float* amax_in, nvfp4_tensor* out,
-                       void* workspace, size_t ws_bytes, void* hip_stream);
+                       const int64_t* segments, int64_t nseg, const float* amax_in,
+                       nvfp4_tensor* out, void* workspace, size_t ws_bytes, void* hip_stream);
 
 /*
  * nvfp4_gemm - D[M, N] (FP32, row stride ldd) = A[M, K] * B[N, K]^T with both operands
@@ -183,11 +192,12 @@ int nvfp4_grouped_gemm_k(int64_t G, const int64_t* k_offsets, const nvfp4_tensor
  * nvfp4_amax - max|x| of x[rows, cols] (row stride ld), per row segment, into device
  * amax_out[nseg]: the first level of the two-level scale ("Nemotron NVFP4" explainer, "What
  * NVFP4 actually is": one FP32 scale per tensor). With rht != 0 the maximum is taken over the
- * Hadamard-transformed tensor of nvfp4_rht_quantize (rows = tokens, nseg must be 1). Useful
- * to precompute amax_in.
+ * Hadamard-transformed tensor of nvfp4_rht_quantize (rows = tokens; segments are token
+ * ranges as there, multiples of 16). Useful to precompute amax_in.
  *   workspace  device scratch of nvfp4_workspace_size(rht ? NVFP4_OP_RHT_QUANTIZE :
  *              NVFP4_OP_QUANTIZE, rows, cols, nseg) bytes, 256-byte aligned, for the partial
- *              maxima of an unsegmented tensor; may be NULL with segments.
+ *              maxima of an unsegmented tensor; may be NULL with segments (amax_out[nseg] is
+ *              then written directly).
  * Errors: as nvfp4_quantize.
  */
 int nvfp4_amax(const void* x, nvfp4_dtype dt, int64_t rows, int64_t cols, int64_t ld,

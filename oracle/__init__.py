@@ -27,18 +27,21 @@ known-answer vectors, exact rational arithmetic or invariants. No function is un
 from .formats import (E2M1_MAX, E4M3_MAX, e2m1_decode, e2m1_encode_rn, e2m1_encode_sr,
                       e4m3_decode, e4m3_encode)
 from .philox import philox4x32_10, block_random_bytes
-from .quantize import (amax, global_scales, quantize_1x16, quantize_16x16, pack_nibbles,
+from .quantize import (amax, global_scales, quantize_1x16, quantize_1x16_colsegments, quantize_16x16,
+                       pack_nibbles,
                        unpack_nibbles, dequantize)
-from .hadamard import rht_columnwise, rht_columnwise_f64, hadamard_matrix_from_butterfly, rht_quantize
+from .hadamard import (rht_columnwise, rht_columnwise_f64, hadamard_matrix_from_butterfly, rht_quantize,
+                       rht_quantize_segments)
 from .gemm import (gemm_fp64, gemm_bound, grouped_gemm_fp64, grouped_gemm_bound, grouped_gemm_k_fp64,
                    grouped_gemm_k_bound)
 
 __all__ = [
     "E2M1_MAX", "E4M3_MAX", "e2m1_decode", "e2m1_encode_rn", "e2m1_encode_sr",
     "e4m3_decode", "e4m3_encode", "philox4x32_10", "block_random_bytes",
-    "amax", "global_scales", "quantize_1x16", "quantize_16x16", "pack_nibbles",
+    "amax", "global_scales", "quantize_1x16", "quantize_1x16_colsegments", "quantize_16x16",
+    "pack_nibbles",
     "unpack_nibbles", "dequantize", "rht_columnwise", "rht_columnwise_f64",
-    "hadamard_matrix_from_butterfly", "rht_quantize",
+    "hadamard_matrix_from_butterfly", "rht_quantize", "rht_quantize_segments",
     "gemm_fp64", "gemm_bound", "grouped_gemm_fp64", "grouped_gemm_bound",
     "grouped_gemm_k_fp64", "grouped_gemm_k_bound",
 ]

@@ -27,7 +27,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .quantize import quantize_1x16
+from .quantize import quantize_1x16, quantize_1x16_colsegments
 
 
 def sign_vector(mask: int) -> np.ndarray:
@@ -69,6 +69,16 @@ def rht_columnwise_f64(x, sign_mask: int) -> np.ndarray:
 def rht_columnwise(x, sign_mask: int) -> np.ndarray:
     """The transform rounded once to float32 (R6). x[tokens, cols] -> y[cols, tokens]."""
     return rht_columnwise_f64(x, sign_mask).astype(np.float32)
+
+
+def rht_quantize_segments(x, sign_mask: int, token_segments, rounding: str = "rn", seed: int = 0,
+                          offset: int = 0):
+    """The transform along tokens, then 1x16 quantization of the transposed result with one
+    tensor scale per token segment (the tokens of one expert; multiples of 16), each from the
+    maximum of its own transformed values (R16). Returns (codes [cols, tokens/2],
+    scales [cols, tokens/16], s_dec [G])."""
+    y = rht_columnwise(x, sign_mask)
+    return quantize_1x16_colsegments(y, token_segments, rounding=rounding, seed=seed, offset=offset)
 
 
 def rht_quantize(x, sign_mask: int, rounding: str = "rn", seed: int = 0, offset: int = 0,

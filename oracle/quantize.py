@@ -145,6 +145,39 @@ def quantize_1x16(x, rounding: str = "rn", seed: int = 0, offset: int = 0, segme
     return pack_nibbles(codes.reshape(rows, cols)), S.reshape(rows, nb), s_dec
 
 
+def quantize_1x16_colsegments(x, col_segments, rounding: str = "rn", seed: int = 0,
+                              offset: int = 0, amax_vals=None):
+    """1x16 quantization of x[rows, cols] along cols with one tensor scale per range of
+    columns (R16): columns col_segments[g]..col_segments[g+1] (multiples of 16, covering
+    [0, cols]) use amax_vals[g], by default their own max|x|. This is the transposed
+    weight-gradient operand of an expert layer, whose columns are the tokens routed to each
+    expert. The stochastic-rounding block index is the block's place in the whole tensor,
+    as in quantize_1x16. Returns (codes [rows, cols/2], scales [rows, cols/16], s_dec [G])."""
+    x = _as_f32(x)
+    rows, cols = x.shape
+    seg = np.asarray(col_segments, dtype=np.int64)
+    if cols % 16 or np.any(seg % 16) or seg[0] != 0 or seg[-1] != cols or np.any(np.diff(seg) < 0):
+        raise ValueError("column segments must be multiples of 16 covering [0, cols]")
+    G = len(seg) - 1
+    if amax_vals is None:
+        a_t = np.array([np.abs(x[:, seg[g]:seg[g + 1]]).max() if seg[g + 1] > seg[g] else 0.0
+                        for g in range(G)], dtype=F32)
+    else:
+        a_t = _as_f32(amax_vals).reshape(-1)
+    s_enc, s_dec = global_scales(a_t)
+    nb = cols // 16
+    gid = np.searchsorted(seg, np.arange(nb, dtype=np.int64) * 16, side="right") - 1
+    xb = x.reshape(rows * nb, 16)
+    a_b = np.abs(xb).max(axis=1).astype(F32) if xb.size else np.zeros(0, F32)
+    s_enc_b = np.tile(s_enc[gid], rows)
+    rbytes = None
+    if rounding == "sr":
+        bidx = np.arange(rows * nb, dtype=np.int64)
+        rbytes = block_random_bytes(bidx, seed, offset)
+    codes, S = _encode_blocks(xb, a_b, s_enc_b, rounding, rbytes)
+    return pack_nibbles(codes.reshape(rows, cols)), S.reshape(rows, nb), s_dec
+
+
 def quantize_16x16(x, segments=None, amax_vals=None, row_ids=None):
     """Quantize x[rows, cols] with one scale per aligned 16x16 tile, round-to-nearest
     (weights). The scale is stored once per row of the tile (R11).

@@ -80,11 +80,13 @@ def test_quantize_validation(lib):
 def test_rht_validation(lib):
     out = _tensor(64, 32)
     f = lib.nvfp4_rht_quantize
-    assert f(FAKE, 0, 30, 64, 64, 0, 0, 0, 0, None, ctypes.byref(out), FAKE, 8192, None) == INVALID
-    assert f(FAKE, 0, 32, 64, 64, 0, 3, 0, 0, None, ctypes.byref(out), FAKE, 8192, None) == INVALID
+    assert f(FAKE, 0, 30, 64, 64, 0, 0, 0, 0, None, 1, None, ctypes.byref(out), FAKE, 8192, None) == INVALID
+    assert f(FAKE, 0, 32, 64, 64, 0, 3, 0, 0, None, 1, None, ctypes.byref(out), FAKE, 8192, None) == INVALID
     bad = _tensor(32, 64)                                                    # must be [cols, tokens]
-    assert f(FAKE, 0, 32, 64, 64, 0, 0, 0, 0, None, ctypes.byref(bad), FAKE, 8192, None) == INVALID
-    assert f(FAKE, 0, 32, 64, 64, 0, 0, 0, 0, None, ctypes.byref(out), None, 0, None) == WORKSPACE
+    assert f(FAKE, 0, 32, 64, 64, 0, 0, 0, 0, None, 1, None, ctypes.byref(bad), FAKE, 8192, None) == INVALID
+    assert f(FAKE, 0, 32, 64, 64, 0, 0, 0, 0, None, 1, None, ctypes.byref(out), None, 0, None) == WORKSPACE
+    assert f(FAKE, 0, 32, 64, 64, 0, 0, 0, 0, None, 3, None, ctypes.byref(out), FAKE, 8192, None) == INVALID
+    assert f(FAKE, 0, 32, 64, 64, 0, 0, 0, 0, FAKE, 0, None, ctypes.byref(out), FAKE, 8192, None) == INVALID
 
 
 def test_amax_pair_validation(lib):
@@ -129,6 +131,7 @@ def test_workspace_sizes(lib):
     assert lib.nvfp4_workspace_size(nv.OP_QUANTIZE, 10, 16, 1) == 4096      # 1024 partial maxima
     assert lib.nvfp4_workspace_size(nv.OP_QUANTIZE, 10, 16, 2000) == 8192   # one slot per segment
     assert lib.nvfp4_workspace_size(nv.OP_RHT_QUANTIZE, 16, 16, 1) == 4096
+    assert lib.nvfp4_workspace_size(nv.OP_RHT_QUANTIZE, 16, 16, 3000) == 12032   # one per segment
     assert lib.nvfp4_workspace_size(nv.OP_AMAX_PAIR, 16, 16, 1) == 8192
     assert lib.nvfp4_workspace_size(nv.OP_GEMM, 16, 16, 1) == 0
     assert lib.nvfp4_workspace_size(nv.OP_GROUPED_GEMM, 16, 16, 1) == 0

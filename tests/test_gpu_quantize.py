@@ -200,6 +200,30 @@ def test_amax_pair(shape, dtype, ld):
         assert g[0] == nv.amax(dev).cpu().numpy()[0]
 
 
+@pytest.mark.parametrize("rounding", ["rn", "sr"])
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_rht_quantize_token_segments(rounding, dtype):
+    """The expert-segmented transform-and-quantize (MoE weight gradient): one tensor scale per
+    token range (an empty range included), bit-exact against the oracle; the segmented amax
+    of the transformed tensor too."""
+    log(f"rht segments {rounding} {dtype}")
+    bits = workloads.with_outliers_bf16((512, 272), 95)
+    x = f32(bits)
+    mask = workloads.wgrad_sign_mask()
+    seg = np.array([0, 48, 48, 160, 496, 512], np.int64)
+    segd = torch.from_numpy(seg).cuda()
+    dev = to_device_bf16(bits) if dtype == "bf16" else to_device_f32(x)
+    q = nv.rht_quantize(dev, mask, rounding, seed=0x5EED, offset=77, segments=segd)
+    ref = oracle.rht_quantize_segments(x, mask, seg, rounding, seed=0x5EED, offset=77)
+    assert_quant_equal(host(q), ref, f"rht segments {rounding} {dtype}")
+    a = nv.amax(dev, segments=segd, rht=True, sign_mask=mask)
+    torch.cuda.synchronize()
+    y = oracle.rht_columnwise(x, mask)
+    want = np.array([np.abs(y[:, seg[g]:seg[g + 1]]).max() if seg[g + 1] > seg[g] else 0.0
+                     for g in range(len(seg) - 1)], np.float32)
+    assert_bytes_equal(a.cpu().numpy().view(np.uint32), want.view(np.uint32), "segment rht amax")
+
+
 def test_rht_fp32_masks():
     rng = np.random.default_rng(12)
     x = (rng.standard_normal((64, 40)) * 3).astype(np.float32)

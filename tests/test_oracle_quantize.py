@@ -196,3 +196,41 @@ def test_fp32_input_path(shape):
     x = rng.standard_normal(shape).astype(np.float32)
     c, s, sd = oracle.quantize_1x16(x)
     assert c.shape == (shape[0], shape[1] // 2) and s.shape == (shape[0], shape[1] // 16)
+
+
+def test_column_segments_one_range_is_the_plain_quantization():
+    x = _x((32, 96), 91)
+    for rnd in ("rn", "sr"):
+        got = oracle.quantize_1x16_colsegments(x, [0, 96], rnd, seed=4, offset=9)
+        want = oracle.quantize_1x16(x, rnd, seed=4, offset=9)
+        for g, w in zip(got, want):
+            assert np.array_equal(np.asarray(g), np.asarray(w))
+
+
+def test_column_segments_rn_are_separate_tensors():
+    # with nearest rounding nothing depends on a block's position, so each column range is
+    # the plain quantization of its own columns with its own tensor scale; an empty range
+    # keeps the unit decode scale
+    x = _x((24, 112), 92)
+    seg = [0, 32, 32, 80, 112]
+    codes, scales, s_dec = oracle.quantize_1x16_colsegments(x, seg)
+    assert s_dec[1] == 1.0
+    for g in range(4):
+        lo, hi = seg[g], seg[g + 1]
+        if hi == lo:
+            continue
+        c, s, sd = oracle.quantize_1x16(x[:, lo:hi])
+        assert np.array_equal(codes[:, lo // 2:hi // 2], c)
+        assert np.array_equal(scales[:, lo // 16:hi // 16], s)
+        assert s_dec[g] == sd[0]
+
+
+def test_column_segments_sr_use_whole_tensor_block_index():
+    # giving every range the whole tensor's amax makes the result the plain SR quantization,
+    # which numbers blocks over the whole row: the random bytes follow the global position
+    x = _x((16, 80), 93)
+    a = oracle.amax(x)[0]
+    got = oracle.quantize_1x16_colsegments(x, [0, 16, 64, 80], "sr", seed=7, offset=1,
+                                           amax_vals=[a, a, a])
+    want = oracle.quantize_1x16(x, "sr", seed=7, offset=1)
+    assert np.array_equal(got[0], want[0]) and np.array_equal(got[1], want[1])

@@ -118,3 +118,21 @@ def test_rht_quantize_column_subset():
     cols = np.array([0, 7, 47])
     sub = oracle.rht_quantize(x[:, cols], mask, "sr", seed=3, offset=2, amax_vals=A, col_ids=cols)
     assert np.array_equal(sub[0], full[0][cols]) and np.array_equal(sub[1], full[1][cols])
+
+
+def test_rht_quantize_segments_rn_equal_separate_token_ranges():
+    # each token range is transformed block by block (blocks never cross a range boundary)
+    # and quantized with its own tensor scale: with nearest rounding it is the plain
+    # transform-and-quantize of its own tokens
+    x = _bf16((96, 40), 10)
+    mask = workloads.wgrad_sign_mask()
+    seg = [0, 32, 32, 96]
+    codes, scales, s_dec = oracle.rht_quantize_segments(x, mask, seg)
+    for g in range(3):
+        lo, hi = seg[g], seg[g + 1]
+        if hi == lo:
+            assert s_dec[g] == 1.0
+            continue
+        c, s, sd = oracle.rht_quantize(x[lo:hi], mask)
+        assert np.array_equal(codes[:, lo // 2:hi // 2], c)
+        assert np.array_equal(scales[:, lo // 16:hi // 16], s) and s_dec[g] == sd[0]
