@@ -143,7 +143,9 @@ def quantize(x: torch.Tensor, block: str = "1x16", rounding: str = "rn", seed: i
     if out is None:
         out = NVFP4Tensor.empty(rows, cols, nseg, x.device)
     if emit_transposed and out_t is None:
-        out_t = NVFP4Tensor.empty(cols, rows, nseg, x.device)
+        # a segmented stack of nseg equal blocks: each block's transpose, stacked
+        out_t = (NVFP4Tensor.empty(cols, rows, 1, x.device) if segments is None
+                 else NVFP4Tensor.empty(nseg * cols, rows // nseg, nseg, x.device))
     ws_n = 0
     if amax is None:
         if workspace is None:

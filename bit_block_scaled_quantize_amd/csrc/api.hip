@@ -156,9 +156,11 @@ int nvfp4_quantize(const void* x, nvfp4_dtype dt, int64_t rows, int64_t cols, in
   if (nseg < 1 || (!segments && nseg != 1)) return fail(NVFP4_ERR_INVALID, "bad segment table (nseg=%lld)", (long long)nseg);
   if (out_t && blk != NVFP4_BLOCK_16X16) return fail(NVFP4_ERR_INVALID, "out_t requires 16x16 blocks");
   if (blk == NVFP4_BLOCK_16X16 && rnd == NVFP4_ROUND_SR) return fail(NVFP4_ERR_UNSUPPORTED, "stochastic rounding applies to 1x16 gradient blocks only");
-  if (out_t && segments) return fail(NVFP4_ERR_UNSUPPORTED, "transposed emission of a segmented tensor");
+  if (out_t && segments && (rows % nseg || (rows / nseg) % 16))
+    return fail(NVFP4_ERR_UNSUPPORTED, "transposed emission of a segmented tensor needs %lld equal segments of a multiple of 16 rows (rows = %lld)",
+                (long long)nseg, (long long)rows);
   if ((st = check_out(out, rows, cols, "out"))) return st;
-  if (out_t && (st = check_out(out_t, cols, rows, "out_t"))) return st;
+  if (out_t && (st = check_out(out_t, segments ? nseg * cols : cols, rows / nseg, "out_t"))) return st;
   const float* amax = amax_in;
   if (!amax) {
     const size_t need = nvfp4_workspace_size(NVFP4_OP_QUANTIZE, rows, cols, nseg);

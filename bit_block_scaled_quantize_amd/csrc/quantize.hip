@@ -382,12 +382,15 @@ __device__ __forceinline__ void nibble_transpose8(uint32_t (&w)[8]) {
   }
 }
 
+// With SEG and TRANS (an expert weight stack of nseg equal segments of seg_rows rows, a
+// multiple of 16), segment g's transpose goes to rows g*cols .. of x^T [nseg*cols, seg_rows].
 template <typename TIn, bool SEG, bool TRANS>
 __global__ __launch_bounds__(kThreads) void k_encode_16x16(
     const TIn* __restrict__ x, int64_t rows, int64_t cols, int64_t ld,
     const float* __restrict__ amax, int amax_parts, const int64_t* __restrict__ seg, int64_t nseg,
     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ gscale,
-    uint8_t* __restrict__ tcodes, uint8_t* __restrict__ tscales, float* __restrict__ tgscale) {
+    uint8_t* __restrict__ tcodes, uint8_t* __restrict__ tscales, float* __restrict__ tgscale,
+    int64_t seg_rows) {
   __shared__ float red[kWavesPerBlock];
   __shared__ __attribute__((aligned(16))) uint8_t tc[TRANS ? kTileCols : 1][kTileRows / 2];
   __shared__ __attribute__((aligned(16))) uint8_t ts[TRANS ? kTileCols : 1][kTileRows / 16];
@@ -402,7 +405,10 @@ __global__ __launch_bounds__(kThreads) void k_encode_16x16(
   const float a0 = fold_amax(amax, SEG ? 1 : amax_parts, red);
   if (blockIdx.x == 0) {
     if constexpr (SEG) {
-      for (int64_t i = threadIdx.x; i < nseg; i += kThreads) gscale[i] = tensor_decode_scale(amax[i]);
+      for (int64_t i = threadIdx.x; i < nseg; i += kThreads) {
+        gscale[i] = tensor_decode_scale(amax[i]);
+        if constexpr (TRANS) tgscale[i] = gscale[i];
+      }
     } else if (threadIdx.x == 0) {
       gscale[0] = tensor_decode_scale(a0);
       if constexpr (TRANS) tgscale[0] = gscale[0];
@@ -484,6 +490,24 @@ __global__ __launch_bounds__(kThreads) void k_encode_16x16(
     // write-out: x^T row C0 + cr, bytes [R0/2, R0/2 + 128), in 8-byte pieces (one strip each)
     const int64_t valid_strips = (rows - R0) / 16 < 16 ? (rows - R0) / 16 : 16;
     const int64_t valid_cols = cols - C0 < kTileCols ? cols - C0 : kTileCols;
+    if constexpr (SEG) {
+      // the rows R0 + 16 sp .. of a strip lie in one segment g: they go to x^T row
+      // g*cols + C0 + cr at the strip's offset within its segment
+#pragma unroll
+      for (int pass = 0; pass < kTileCols * 16 / kThreads; ++pass) {
+        const int idx = pass * kThreads + threadIdx.x;
+        const int cr = idx >> 4, sp = idx & 15;
+        if (cr < valid_cols && sp < valid_strips) {
+          const int64_t r = R0 + 16 * sp;
+          const int64_t g = r / seg_rows, lr = r - g * seg_rows;
+          const int64_t trow = g * cols + C0 + cr;
+          *reinterpret_cast<uint2*>(tcodes + trow * (seg_rows >> 1) + (lr >> 1)) =
+              *reinterpret_cast<const uint2*>(&tc[cr][sp * 8]);
+          tscales[trow * (seg_rows >> 4) + (lr >> 4)] = ts[cr][sp];
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int pass = 0; pass < kTileCols * 16 / kThreads; ++pass) {
       const int idx = pass * kThreads + threadIdx.x;
@@ -613,7 +637,8 @@ static void encode_16x16_t(const void* x, int64_t rows, int64_t cols, int64_t ld
   hipLaunchKernelGGL((k_encode_16x16<TIn, SEG, TRANS>), dim3((unsigned)tiles), dim3(kThreads), 0,
                      stream, (const TIn*)x, rows, cols, ld, amax, parts, segments, nseg,
                      out.codes, out.scales, out.global_scale, TRANS ? out_t->codes : nullptr,
-                     TRANS ? out_t->scales : nullptr, TRANS ? out_t->global_scale : nullptr);
+                     TRANS ? out_t->scales : nullptr, TRANS ? out_t->global_scale : nullptr,
+                     rows / (nseg > 0 ? nseg : 1));
 }
 
 hipError_t launch_encode_16x16(const void* x, bool fp32, int64_t rows, int64_t cols, int64_t ld,

@@ -90,13 +90,17 @@ typedef struct nvfp4_tensor {
  *             skipped and no workspace is needed.
  *   out       codes/scales/global_scale as documented above; out->rows == rows,
  *             out->cols == cols.
- *   out_t     NULL, or (16X16, nseg == 1 only) a second tensor receiving the quantization of
- *             x^T ([cols, rows] along rows): the same tile scales and codes, transposed.
+ *   out_t     NULL, or (16X16) a second tensor receiving the quantization of x^T ([cols, rows]
+ *             along rows): the same tile scales and codes, transposed. With segments (a
+ *             stack of nseg expert weights) they must be nseg equal blocks of n = rows/nseg
+ *             rows (n % 16 == 0; the table must match) and out_t is [nseg*cols, n]: rows
+ *             g*cols .. hold expert g's transpose, with global_scale[g] (the operand of the
+ *             grouped activation-gradient GEMM).
  *   workspace device scratch of at least nvfp4_workspace_size(NVFP4_OP_QUANTIZE, rows,
  *             cols, nseg) bytes, 256-byte aligned; may be NULL when amax_in is given.
  * Errors: NVFP4_ERR_INVALID (null pointers, cols % 16, rows % 16 for 16X16, ld < cols, bad
  * enum, nseg < 1, segments == NULL with nseg != 1, out_t without 16X16, tensor shape
- * mismatch), NVFP4_ERR_UNSUPPORTED (SR with 16X16, out_t with segments),
+ * mismatch), NVFP4_ERR_UNSUPPORTED (SR with 16X16, out_t with unequal or misaligned segments),
  * NVFP4_ERR_WORKSPACE, NVFP4_ERR_HIP.
  */
 int nvfp4_quantize(const void* x, nvfp4_dtype dt, int64_t rows, int64_t cols, int64_t ld,

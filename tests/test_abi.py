@@ -65,7 +65,9 @@ def test_quantize_validation(lib):
     assert _q(lib, nseg=0) == INVALID
     assert _q(lib, out_t=_tensor(64, 32)) == INVALID                        # out_t needs 16x16
     assert _q(lib, blk=1, rnd=1) == UNSUPPORTED                             # SR on weights
-    assert _q(lib, blk=1, seg=FAKE, nseg=2, out_t=_tensor(64, 32)) == UNSUPPORTED
+    assert _q(lib, blk=1, seg=FAKE, nseg=3, out_t=_tensor(192, 32)) == UNSUPPORTED  # 32 % 3
+    assert _q(lib, blk=1, seg=FAKE, nseg=4, out_t=_tensor(256, 8)) == UNSUPPORTED   # 8 rows each
+    assert _q(lib, blk=1, seg=FAKE, nseg=2, out_t=_tensor(64, 32)) == INVALID       # [2*64, 16]
     assert _q(lib, out=None) == INVALID
     assert _q(lib, out=_tensor(32, 48)) == INVALID                          # shape mismatch
     assert _q(lib, out=_tensor(32, 64, codes=None)) == INVALID

@@ -200,6 +200,29 @@ def test_amax_pair(shape, dtype, ld):
         assert g[0] == nv.amax(dev).cpu().numpy()[0]
 
 
+@pytest.mark.parametrize("n,k,G", [(48, 272, 3), (1856, 160, 2), (16, 32, 5)])
+def test_16x16_segments_with_transpose(n, k, G):
+    """An expert weight stack [G*n, k] quantized in 16x16 tiles with one tensor scale per
+    expert, and every expert's transpose stacked [G*k, n] (the grouped activation-gradient
+    GEMM's operand): bit-exact against the oracle, expert by expert."""
+    log(f"16x16 segments + transpose n={n} k={k} G={G}")
+    bits = workloads.with_outliers_bf16((G * n, k), 96 + n)
+    x = f32(bits)
+    x *= np.repeat(np.float32(2.0) ** np.arange(G, dtype=np.float32), n)[:, None]
+    bits = workloads.f32_to_bf16_bits(x)
+    x = f32(bits)
+    seg = np.arange(G + 1, dtype=np.int64) * n
+    q, qt = nv.quantize(to_device_bf16(bits), "16x16", "rn", emit_transposed=True,
+                        segments=torch.from_numpy(seg).cuda())
+    assert_quant_equal(host(q), oracle.quantize_16x16(x, segments=seg), "segmented W")
+    codes_t, scales_t, gs_t = host(qt)
+    for g in range(G):
+        xg = x[g * n:(g + 1) * n]
+        ref = oracle.quantize_16x16(np.ascontiguousarray(xg.T), amax_vals=oracle.amax(xg))
+        assert_quant_equal((codes_t[g * k:(g + 1) * k], scales_t[g * k:(g + 1) * k], gs_t[g:g + 1]),
+                           ref, f"W_{g}^T")
+
+
 @pytest.mark.parametrize("rounding", ["rn", "sr"])
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 def test_rht_quantize_token_segments(rounding, dtype):
