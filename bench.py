@@ -290,8 +290,13 @@ def gemm_traffic():
 
 
 def bench_moe(nv, workloads, torch, dev, stream, flush, args):
-    """Per-expert quantize of the expert-sorted activations and stacked weights, then the
-    grouped fprop GEMM (128 experts, top-6 of 16384 tokens, hidden 2688, expert FFN 1856)."""
+    """The expert layer (128 experts, top-6 of 16384 tokens, hidden 2688, expert FFN 1856).
+    Forward: per-expert quantize of the expert-sorted activations and stacked weights, then the
+    grouped fprop GEMM. Backward, on the layout with each expert's tokens padded to a multiple
+    of 64 with zero rows: the weights in 16x16 tiles with every expert's transpose, dY per
+    expert in 1x16 SR, the grouped activation-gradient GEMM; dY and X transformed along tokens
+    and quantized per expert, the weight-gradient GEMM grouped along K. GEMM rates count the
+    real tokens only (2 * tokens * ffn * hidden per GEMM)."""
     fsum = torch.empty((1,), dtype=torch.int64, device=dev)
     x_bits, w_bits, off = workloads.moe()
     G, n, k = workloads.MOE_EXPERTS, workloads.MOE_FFN, workloads.MOE_HIDDEN
@@ -303,13 +308,57 @@ def bench_moe(nv, workloads, torch, dev, stream, flush, args):
     Xq, Wq = nv.NVFP4Tensor.empty(total, k, G), nv.NVFP4Tensor.empty(G * n, k, G)
     D = torch.empty((total, n), dtype=torch.float32, device=dev)
     ws = torch.empty((4096,), dtype=torch.uint8, device=dev)
+    flops = 2.0 * total * n * k
     calls = {
         "quantize_x_experts_1x16_rn": (lambda: nv.quantize(X, "1x16", "rn", segments=offd, out=Xq, workspace=ws),
                                        "GB/s", q_bytes(total, k)),
         "quantize_w_experts_16x16_rn": (lambda: nv.quantize(Wt, "16x16", "rn", segments=wseg, out=Wq, workspace=ws),
                                         "GB/s", q_bytes(G * n, k)),
-        "grouped_gemm": (lambda: nv.grouped_gemm(offd, Xq, Wq, n, out=D), "TFLOP/s", 2.0 * total * n * k),
+        "grouped_gemm": (lambda: nv.grouped_gemm(offd, Xq, Wq, n, out=D), "TFLOP/s", flops),
     }
+    res = _time_calls(calls, torch, stream, flush, fsum, args)
+    del D, Xq
+
+    # backward on the padded token layout
+    x_pad, dy_pad, off_pad = workloads.moe_backward(x_bits, off)
+    tp = int(off_pad[-1])
+    Xp = torch.from_numpy(x_pad.view(np.int16)).view(torch.bfloat16).to(dev)
+    dY = torch.from_numpy(dy_pad.view(np.int16)).view(torch.bfloat16).to(dev)
+    del x_pad, dy_pad
+    offp = torch.from_numpy(off_pad).to(dev)
+    mask = workloads.wgrad_sign_mask()
+    WqT = nv.NVFP4Tensor.empty(G * k, n, G)
+    dYq = nv.NVFP4Tensor.empty(tp, n, G)
+    dYt, Xt = nv.NVFP4Tensor.empty(n, tp, G), nv.NVFP4Tensor.empty(k, tp, G)
+    dX = torch.empty((tp, k), dtype=torch.float32, device=dev)
+    dW = torch.empty((G * n, k), dtype=torch.float32, device=dev)
+    ws_r = torch.empty((nv.workspace_size(nv.OP_RHT_QUANTIZE, tp, n, G),), dtype=torch.uint8, device=dev)
+    calls = {
+        "quantize_w_experts_16x16_rn_transposed": (
+            lambda: nv.quantize(Wt, "16x16", "rn", emit_transposed=True, segments=wseg, out=Wq, out_t=WqT,
+                                workspace=ws), "GB/s", q_bytes(G * n, k, transposed=True)),
+        "quantize_dy_experts_1x16_sr": (
+            lambda: nv.quantize(dY, "1x16", "sr", seed=11, segments=offp, out=dYq, workspace=ws),
+            "GB/s", q_bytes(tp, n)),
+        "grouped_gemm_dgrad": (lambda: nv.grouped_gemm(offp, dYq, WqT, k, out=dX), "TFLOP/s", flops),
+        "rht_quantize_dy_experts_sr": (
+            lambda: nv.rht_quantize(dY, mask, "sr", seed=12, segments=offp, out=dYt, workspace=ws_r),
+            "GB/s", q_bytes(tp, n)),
+        "rht_quantize_x_experts_rn": (
+            lambda: nv.rht_quantize(Xp, mask, "rn", segments=offp, out=Xt, workspace=ws_r),
+            "GB/s", q_bytes(tp, k)),
+        "grouped_gemm_k_wgrad": (lambda: nv.grouped_gemm_k(offp, dYt, Xt, out=dW), "TFLOP/s", flops),
+    }
+    res.update(_time_calls(calls, torch, stream, flush, fsum, args))
+    res["config"] = {"experts": G, "tokens": workloads.MOE_TOKENS, "topk": workloads.MOE_TOPK,
+                     "hidden": k, "ffn": n, "rows_total": total, "rows_total_padded_64": tp,
+                     "rows_per_expert_max": int(np.diff(off).max()),
+                     "rows_per_expert_min": int(np.diff(off).min())}
+    return res
+
+
+def _time_calls(calls, torch, stream, flush, fsum, args):
+    """Median cold (L2 and MALL flushed) time of each call and its rate."""
     res = {}
     for name, (fn, unit, amount) in calls.items():
         fn()
@@ -331,10 +380,6 @@ def bench_moe(nv, workloads, torch, dev, stream, flush, args):
             v = amount / (ms * 1e-3) / 1e12
             res[name] = {"us": round(ms * 1e3, 2), "TFLOP/s": round(v, 1),
                          "frac_mfma_f16": round(v / MFMA_F16_PEAK_TFLOPS, 4)}
-    res["config"] = {"experts": G, "tokens": workloads.MOE_TOKENS, "topk": workloads.MOE_TOPK,
-                     "hidden": k, "ffn": n, "rows_total": total,
-                     "rows_per_expert_max": int(np.diff(off).max()),
-                     "rows_per_expert_min": int(np.diff(off).min())}
     return res
 
 

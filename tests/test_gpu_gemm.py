@@ -210,6 +210,82 @@ def test_grouped_gemm_k(m, n, offs):
             assert np.all(o[g * m:(g + 1) * m, :n] == 0.0)
 
 
+def _colseg_dequant(q, segments):
+    """Dequantized [rows, cols] of a tensor with one global scale per column segment."""
+    codes, scales, gs = q
+    y = oracle.dequantize(codes, scales, np.ones(1, np.float32))
+    col = np.ones(y.shape[1])
+    for g in range(len(segments) - 1):
+        col[segments[g]:segments[g + 1]] = gs[g]
+    return y * col
+
+
+def test_moe_backward_chain():
+    """The expert layer's backward pass end to end on a small layer (4 experts, one empty,
+    hidden 256, expert FFN 192, tokens padded to 64 per expert): weights in 16x16 tiles with
+    their per-expert transposes, dY in 1x16 SR per expert for the grouped activation-gradient
+    GEMM; dY and X transformed and quantized per expert along tokens for the weight-gradient
+    GEMM grouped along K. Every quantized operand is bit-exact against the oracle and both
+    GEMMs are within the bound of the FP64 reference on those operands."""
+    log("moe backward chain")
+    G, hidden, ffn = 4, 256, 192
+    off = np.array([0, 37, 37, 167, 231], np.int64)
+    x_bits = workloads.normal_bf16((231, hidden), 501)
+    w_bits = workloads.normal_bf16((G * ffn, hidden), 502)
+    x_pad, dy_pad, off_pad = workloads.moe_backward(x_bits, off, ffn=ffn, pad=64)
+    tp = int(off_pad[-1])
+    offd = torch.from_numpy(off_pad).cuda()
+    wseg = np.arange(G + 1, dtype=np.int64) * ffn
+    mask = workloads.wgrad_sign_mask()
+    wq, wqt = nv.quantize(to_device_bf16(w_bits), "16x16", "rn", emit_transposed=True,
+                          segments=torch.from_numpy(wseg).cuda())
+    dyq, _ = nv.quantize(to_device_bf16(dy_pad), "1x16", "sr", seed=21, segments=offd)
+    dyt = nv.rht_quantize(to_device_bf16(dy_pad), mask, "sr", seed=22, offset=5, segments=offd)
+    xt = nv.rht_quantize(to_device_bf16(x_pad), mask, "rn", segments=offd)
+    dx = nv.grouped_gemm(offd, dyq, wqt, hidden)
+    dw = nv.grouped_gemm_k(offd, dyt, xt)
+    torch.cuda.synchronize()
+
+    w, dy, x = f32(w_bits), f32(dy_pad), f32(x_pad)
+    r_dyq = oracle.quantize_1x16(dy, "sr", seed=21, segments=off_pad)
+    assert_quant_equal(host(dyq), r_dyq, "dY 1x16 SR per expert")
+    wt = np.concatenate([w[g * ffn:(g + 1) * ffn].T for g in range(G)])
+    wt_amax = oracle.amax(w, wseg)
+    r_wt = [oracle.quantize_16x16(np.ascontiguousarray(w[g * ffn:(g + 1) * ffn].T), amax_vals=wt_amax[g:g + 1])
+            for g in range(G)]
+    r_wqt = (np.concatenate([r[0] for r in r_wt]), np.concatenate([r[1] for r in r_wt]),
+             np.concatenate([r[2] for r in r_wt]))
+    assert_quant_equal(host(wqt), r_wqt, "W^T per expert")
+    r_dyt = oracle.rht_quantize_segments(dy, mask, off_pad, "sr", seed=22, offset=5)
+    r_xt = oracle.rht_quantize_segments(x, mask, off_pad, "rn")
+    assert_quant_equal(host(dyt), r_dyt, "H dY^T per expert")
+    assert_quant_equal(host(xt), r_xt, "H X^T per expert")
+
+    # dgrad: per expert g, dX_g = dY_g W_g (W_g^T stacked as B, N = hidden)
+    a_hat = oracle.dequantize(*r_dyq, segments=off_pad)
+    wt_seg = np.arange(G + 1, dtype=np.int64) * hidden
+    b_hat = oracle.dequantize(*r_wqt, segments=wt_seg)
+    d64 = oracle.grouped_gemm_fp64(a_hat, b_hat, off_pad, hidden)
+    bound = oracle.grouped_gemm_bound(a_hat, b_hat, off_pad, hidden)
+    assert np.all(np.abs(dx.cpu().numpy() - d64) <= bound)
+    assert np.all(dx.cpu().numpy()[37:64] == 0.0)                        # padding rows
+    # wgrad: per expert g, dW_g = (H dY_g)^T (H X_g) over the expert's tokens
+    ah = _colseg_dequant(r_dyt, off_pad)
+    bh = _colseg_dequant(r_xt, off_pad)
+    d64 = oracle.grouped_gemm_k_fp64(ah, bh, off_pad)
+    bound = oracle.grouped_gemm_k_bound(ah, bh, off_pad)
+    got = dw.cpu().numpy()
+    assert got.shape == (G * ffn, hidden)
+    assert np.all(np.abs(got - d64) <= bound)
+    assert np.all(got[ffn:2 * ffn] == 0.0)                               # the empty expert
+    # the transform cancels: the product is the unrotated dY_g^T X_g up to the FP4 noise of
+    # the two operands (about 0.17 relative here; a transform that did not cancel is near 1.4)
+    ref = np.concatenate([dy[off_pad[g]:off_pad[g + 1]].T.astype(np.float64) @
+                          x[off_pad[g]:off_pad[g + 1]].astype(np.float64) for g in range(G)])
+    rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+    assert rel < 0.25, rel
+
+
 @pytest.mark.parametrize("mnk", [(513, 1024, 5120), (1000, 700, 1344), (2304, 2560, 1024)])
 def test_gemm_reproducible(mnk):
     """The same GEMM twice gives bitwise identical D, also where tiles of a partial last round

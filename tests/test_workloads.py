@@ -27,3 +27,15 @@ def test_moe_routing_statistics():
     off = workloads.moe_routing()
     cnt = np.diff(off)
     assert off[-1] == 16384 * 6 and cnt.min() > 0 and cnt.max() == 13452
+
+
+def test_padded_token_layout():
+    off = np.array([0, 37, 37, 167, 231], np.int64)
+    pad = workloads.pad_offsets(off, 64)
+    assert list(pad) == [0, 64, 64, 256, 320]
+    bits = np.arange(231 * 3, dtype=np.uint16).reshape(231, 3)
+    out = workloads.scatter_rows(bits, off, pad)
+    assert out.shape == (320, 3)
+    assert np.array_equal(out[0:37], bits[0:37]) and np.all(out[37:64] == 0)
+    assert np.array_equal(out[64:194], bits[37:167]) and np.all(out[194:256] == 0)
+    assert np.array_equal(out[256:320], bits[167:231])

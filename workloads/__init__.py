@@ -31,6 +31,7 @@ SEEDS = {
     "tiny_a": 101, "tiny_w": 102,
     "fprop_x": 201, "fprop_w": 202,
     "dgrad_dy": 301,
+    "moe_dy": 504,
     "wgrad_sign": 401,
     "moe_route": 501, "moe_x": 502, "moe_w": 503,
 }
@@ -164,3 +165,33 @@ def exponent_spread_bf16(tokens: int, cols: int, seed: int, spreads=(0, 6, 11, 1
     bits = (sign << 15) | (field << 7) | mant
     bits = np.where(rng.random((nb, 16, cols)) < 0.05, 0, bits)
     return bits.reshape(tokens, cols).astype(np.uint16)
+
+
+def pad_offsets(offsets, multiple: int = 64) -> np.ndarray:
+    """Offsets of the same groups with each group's size rounded up to a multiple (the padded
+    token layout of the expert backward pass: every expert's tokens start on a 64-token
+    boundary)."""
+    sizes = np.diff(np.asarray(offsets, dtype=np.int64))
+    padded = (sizes + multiple - 1) // multiple * multiple
+    out = np.zeros(len(sizes) + 1, dtype=np.int64)
+    np.cumsum(padded, out=out[1:])
+    return out
+
+
+def scatter_rows(bits: np.ndarray, offsets, padded_offsets) -> np.ndarray:
+    """Rows of group g moved from offsets[g].. to padded_offsets[g]..; padding rows are zero."""
+    out = np.zeros((int(padded_offsets[-1]), bits.shape[1]), dtype=bits.dtype)
+    for g in range(len(offsets) - 1):
+        lo, hi = int(offsets[g]), int(offsets[g + 1])
+        out[int(padded_offsets[g]):int(padded_offsets[g]) + hi - lo] = bits[lo:hi]
+    return out
+
+
+def moe_backward(x_bits: np.ndarray, offsets, ffn: int = MOE_FFN, pad: int = 64):
+    """The expert layer's backward inputs in the padded token layout: X and the output gradient
+    dY[tokens, ffn] ~ N(0, 1e-3) (its rows of real tokens; padding rows zero), and the padded
+    offsets."""
+    off_pad = pad_offsets(offsets, pad)
+    dy = normal_bf16((int(offsets[-1]), ffn), SEEDS["moe_dy"], std=1e-3)
+    return scatter_rows(x_bits, offsets, off_pad), scatter_rows(dy, offsets, off_pad), off_pad
+
