@@ -259,9 +259,22 @@ __global__ __launch_bounds__(kThreads) void k_encode_1x16(
   const int64_t nwaves = (int64_t)gridDim.x * kWavesPerBlock;
   const int64_t nb = cols >> 4;
 
+  // Rows are walked downwards (the amax pass left the last rows in cache): without segments
+  // with a stride of all waves, with segments as one contiguous row range per wave, so a wave
+  // meets few segment changes. Row r = base - it for it = it0, it0 + stride, ... < lim.
+  int64_t base = rows - 1, it0 = wave, stride = nwaves, lim = rows;
+  if constexpr (SEG) {
+    const int64_t per = (rows + nwaves - 1) / nwaves;
+    const int64_t lo = wave * per < rows ? wave * per : rows;
+    const int64_t hi = lo + per < rows ? lo + per : rows;
+    base = hi - 1;
+    it0 = 0;
+    stride = 1;
+    lim = hi - lo;
+  }
   C cur, nxt;
-  int64_t it = wave, b0 = 0;
-  if (it < rows) cur.load(x + (rows - 1 - it) * ld, b0, nb, lane);
+  int64_t it = it0, b0 = 0;
+  if (it < lim) cur.load(x + (base - it) * ld, b0, nb, lane);
 
   const float a0 = fold_amax(amax, SEG ? 1 : amax_parts, red);
   if (blockIdx.x == 0) {
@@ -272,10 +285,14 @@ __global__ __launch_bounds__(kThreads) void k_encode_1x16(
     }
   }
   float s_enc = tensor_encode_scale(a0);
-  int64_t cur_seg = -1;
-  __shared__ float rtab[SEG ? 1 : 128];          // block multipliers of the one tensor scale
+  // Block multipliers of the tensor scale: one table per workgroup, or with segments one per
+  // wave, rebuilt when the wave enters another segment. seg_lo/seg_hi: the current segment's
+  // row range (empty before the first row).
+  __shared__ float rtab[SEG ? kWavesPerBlock : 1][128];
+  float* tab = rtab[SEG ? (threadIdx.x >> 6) : 0];
+  int64_t seg_lo = 0, seg_hi = 0;
   if constexpr (!SEG) {
-    build_recip_table(s_enc, rtab);
+    build_recip_table(s_enc, tab);
     __syncthreads();
   }
 
@@ -285,16 +302,21 @@ __global__ __launch_bounds__(kThreads) void k_encode_1x16(
     int64_t it_n = it, b0_n = b0 + kSpan;
     if (b0_n >= nb) {
       b0_n = 0;
-      it_n = it + nwaves;
+      it_n = it + stride;
     }
-    if (it_n < rows) nxt.load(x + (rows - 1 - it_n) * ld, b0_n, nb, lane);
+    if (it_n < lim) nxt.load(x + (base - it_n) * ld, b0_n, nb, lane);
 
-    const int64_t r = rows - 1 - it;
+    const int64_t r = base - it;
     if constexpr (SEG) {
-      const int64_t s = find_segment(seg, nseg, r);
-      if (s != cur_seg) {
-        cur_seg = s;
-        s_enc = tensor_encode_scale(amax[s]);
+      if (r < seg_lo || r >= seg_hi) {                       // uniform: another segment
+        const int64_t sg = find_segment(seg, nseg, r);
+        seg_lo = seg[sg];
+        seg_hi = seg[sg + 1];
+        s_enc = tensor_encode_scale(amax[sg]);
+        __builtin_amdgcn_wave_barrier();                     // the wave's reads of the old table
+        tab[lane] = block_recip(lane, s_enc);
+        tab[lane + 64] = block_recip(lane + 64, s_enc);
+        __builtin_amdgcn_wave_barrier();
       }
     }
     uint2* cr = reinterpret_cast<uint2*>(codes + r * (cols >> 1));
@@ -305,9 +327,7 @@ __global__ __launch_bounds__(kThreads) void k_encode_1x16(
       cur.get(u, lane, v);                       // all lanes: the exchange is wave-wide
       const int64_t b = b0 + C::block_of(lane, u);
       if (b < nb) {
-        BlockScale bs;
-        if constexpr (SEG) bs = block_scale(abs_max16(v), s_enc);
-        else bs = block_scale_table(abs_max16(v), s_enc, rtab);
+        const BlockScale bs = block_scale_table(abs_max16(v), s_enc, tab);
         u32x4 rnd{0, 0, 0, 0};
         if constexpr (SR) rnd = block_random((uint64_t)(r * nb + b), seed, offset);
         uint32_t lo, hi;
@@ -319,9 +339,9 @@ __global__ __launch_bounds__(kThreads) void k_encode_1x16(
     it = it_n;
     b0 = b0_n;
   };
-  while (it < rows) {
+  while (it < lim) {
     step(cur, nxt);
-    if (it >= rows) break;
+    if (it >= lim) break;
     step(nxt, cur);
   }
 }

@@ -33,6 +33,8 @@ constexpr int kTileCols = 128;                  // 64 lanes x 2 columns
 constexpr int kTileBlocks = 16;                 // 256 tokens
 constexpr int kBlocksPerWave = kTileBlocks / kWaves;
 constexpr int kMaxPartials = 1024;
+constexpr int kLdsSeg = 512;                    // segment tables up to this size live in LDS
+constexpr int kAccWin = 64;                     // SEG amax: per-workgroup window of segment maxima
 
 // Columns c and c+1 of one token row, kept packed until use. `both` says whether c+1
 // exists; `paired` whether the pair is aligned for one vector load (even row stride), else
@@ -99,9 +101,15 @@ __device__ __forceinline__ float block_max(float m, float* red) {
   return r;
 }
 
-// SEG: token segments (the tokens of each expert, multiples of 16) with one tensor scale each:
-// the amax form flushes one atomic max per (wave, run of items in one segment) into
-// partial[segment] (zeroed by the caller), the encode form takes amax[segment] per item.
+// SEG: token segments (the tokens of each expert, multiples of 16) with one tensor scale each.
+// Tables of up to kLdsSeg segments are copied into LDS (segment starts; for encode also each
+// segment's encode scale), so finding an item's segment costs no global round trip, and each
+// workgroup walks a contiguous range of tiles (instead of a grid stride; the encode form
+// backwards), so consecutive tiles share their token rows and a wave's segment cursor rarely
+// moves. The amax form folds each wave's runs of items in one segment into an LDS window of
+// per-segment maxima, and the workgroup ends with one global atomic max per segment it
+// touched (partial[segment], zeroed by the caller). The encode form takes the scale of the
+// item's segment.
 template <typename TIn, bool ENCODE, bool SR, bool PLAIN = false, bool SEG = false>
 __global__ __launch_bounds__(kThreads) void k_rht(
     const TIn* __restrict__ x, int64_t tokens, int64_t cols, int64_t ld, uint32_t mask,
@@ -113,6 +121,10 @@ __global__ __launch_bounds__(kThreads) void k_rht(
   __shared__ __attribute__((aligned(16))) uint8_t tc[ENCODE ? kTileCols : 1][kTileBlocks * 8];
   __shared__ __attribute__((aligned(16))) uint8_t ts[ENCODE ? kTileCols : 1][kTileBlocks];
   __shared__ float rtab[ENCODE ? 128 : 1];       // block multipliers of the tensor scale
+  __shared__ int64_t sseg[SEG ? kLdsSeg : 1];     // segment starts (nseg <= kLdsSeg)
+  __shared__ float ssenc[SEG && ENCODE ? kLdsSeg : 1];
+  __shared__ float sacc[SEG && !ENCODE ? kAccWin : 1];
+  constexpr bool kBlocked = SEG;                 // contiguous tile range per workgroup
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t nbt = tokens >> 4;
@@ -124,8 +136,12 @@ __global__ __launch_bounds__(kThreads) void k_rht(
   // token blocks w, w+4, w+8, w+12 (item k = 0..3). The next item's 16 rows are requested
   // before the current item is transformed, also across tiles.
   struct Geo { int64_t C0, TB0; };
+  const int64_t per = kBlocked ? (tiles + gridDim.x - 1) / gridDim.x : 0;
+  const int64_t it_begin = kBlocked ? (int64_t)blockIdx.x * per : (int64_t)blockIdx.x;
+  const int64_t it_end = kBlocked ? (it_begin + per < tiles ? it_begin + per : tiles) : tiles;
+  const int64_t rbase = kBlocked ? it_begin + it_end - 1 : tiles - 1;
   auto geo = [&](int64_t it) {
-    const int64_t tile = ENCODE ? tiles - 1 - it : it;   // encode walks back over the amax order
+    const int64_t tile = ENCODE ? rbase - it : it;       // encode walks back over the amax order
     const int64_t tt = tile / tiles_c;
     return Geo{(tile - tt * tiles_c) * kTileCols, tt * kTileBlocks};
   };
@@ -146,20 +162,50 @@ __global__ __launch_bounds__(kThreads) void k_rht(
   };
 
   Pair<TIn> cur[16], nxt[16];
-  int64_t it = blockIdx.x;
+  int64_t it = it_begin;
+  const int64_t it_stride = kBlocked ? 1 : gridDim.x;
   int k = 0;
-  if (it < tiles) load_item(cur, it, 0);
+  if (it < it_end) load_item(cur, it, 0);
+
+  const bool lds_seg = SEG && nseg <= kLdsSeg;
+  if constexpr (SEG) {
+    if (lds_seg) {
+      for (int64_t i = threadIdx.x; i < nseg; i += kThreads) {
+        sseg[i] = seg[i];
+        if constexpr (ENCODE) ssenc[i] = tensor_encode_scale(amax[i]);
+      }
+    }
+    if constexpr (!ENCODE) {
+      for (int i = threadIdx.x; i < kAccWin; i += kThreads) sacc[i] = 0.0f;
+    }
+    __syncthreads();
+  }
 
   // Segment of a token block (the last segment whose first token is at or before the block's
   // first token, as find_segment): a per-wave cursor that moves from the previous item's
   // segment, so a walk in either direction costs O(1) table reads per item.
   int64_t sg = 0;
-  auto seg_of = [&](int64_t tb) {
-    const int64_t tok = tb * 16;
-    while (sg > 0 && seg[sg] > tok) --sg;
-    while (sg + 1 < nseg && seg[sg + 1] <= tok) ++sg;
+  auto seg_walk = [&](const int64_t* t, int64_t tok) {
+    while (sg > 0 && t[sg] > tok) --sg;
+    while (sg + 1 < nseg && t[sg + 1] <= tok) ++sg;
     return sg;
   };
+  auto seg_of = [&](int64_t tb) { return lds_seg ? seg_walk(sseg, tb * 16) : seg_walk(seg, tb * 16); };
+  // SEG amax: the window of segments [win_lo, win_lo + kAccWin) is kept in LDS; win_lo is the
+  // segment of the workgroup's first token (segments only grow along the walk).
+  int64_t win_lo = 0;
+  if constexpr (SEG && !ENCODE) {
+    if (it < it_end) win_lo = seg_of(geo(it).TB0);
+  }
+  auto flush = [&](int64_t sgi, float mv) {            // uniform: one wave's run maximum
+    const float wm = wave_max(mv);
+    if (lane == 0) {
+      if (sgi - win_lo < kAccWin) atomicMax(reinterpret_cast<unsigned int*>(&sacc[sgi - win_lo]), __float_as_uint(wm));
+      else atomic_max_nonneg(partial + sgi, wm);
+    }
+  };
+  int64_t se_seg = -1;                                      // SEG encode: segment of se_cached
+  float se_cached = 1.0f;
 
   float s_enc = 1.0f;
   if constexpr (ENCODE && SEG) {
@@ -188,9 +234,9 @@ __global__ __launch_bounds__(kThreads) void k_rht(
     int k_n = k + 1;
     if (k_n == kBlocksPerWave) {
       k_n = 0;
-      it_n = it + gridDim.x;
+      it_n = it + it_stride;
     }
-    if (it_n < tiles) load_item(nxt, it_n, k_n);
+    if (it_n < it_end) load_item(nxt, it_n, k_n);
 
     const Geo g = geo(it);
     const int64_t c = g.C0 + 2 * lane;
@@ -201,12 +247,13 @@ __global__ __launch_bounds__(kThreads) void k_rht(
       if constexpr (SEG) {
         const int64_t sgi = seg_of(tb);
         if constexpr (ENCODE) {
-          se = tensor_encode_scale(amax[sgi]);
-        } else if (sgi != m_seg) {                          // uniform: flush the previous run
-          if (m_seg >= 0) {
-            const float wm = wave_max(m);
-            if (lane == 0) atomic_max_nonneg(partial + m_seg, wm);
+          if (sgi != se_seg) {
+            se_seg = sgi;
+            se_cached = lds_seg ? ssenc[sgi] : tensor_encode_scale(amax[sgi]);
           }
+          se = se_cached;
+        } else if (sgi != m_seg) {                          // uniform: flush the previous run
+          if (m_seg >= 0) flush(m_seg, m);
           m = 0.0f;
           m_seg = sgi;
         }
@@ -273,15 +320,17 @@ __global__ __launch_bounds__(kThreads) void k_rht(
     it = it_n;
     k = k_n;
   };
-  while (it < tiles) {                                      // uniform across the workgroup
+  while (it < it_end) {                                     // uniform across the workgroup
     step(cur, nxt);
-    if (it >= tiles) break;
+    if (it >= it_end) break;
     step(nxt, cur);
   }
   if constexpr (!ENCODE && SEG) {
-    if (m_seg >= 0) {
-      const float wm = wave_max(m);
-      if (lane == 0) atomic_max_nonneg(partial + m_seg, wm);
+    if (m_seg >= 0) flush(m_seg, m);
+    __syncthreads();
+    for (int i = threadIdx.x; i < kAccWin; i += kThreads) {
+      const float v = sacc[i];
+      if (__float_as_uint(v) != 0u && win_lo + i < nseg) atomic_max_nonneg(partial + win_lo + i, v);
     }
   } else if constexpr (!ENCODE) {
     m = block_max(m, red);
