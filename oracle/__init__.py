@@ -33,7 +33,8 @@ from .quantize import (amax, global_scales, quantize_1x16, quantize_1x16_colsegm
 from .hadamard import (rht_columnwise, rht_columnwise_f64, hadamard_matrix_from_butterfly, rht_quantize,
                        rht_quantize_segments)
 from .gemm import (gemm_fp64, gemm_bound, grouped_gemm_fp64, grouped_gemm_bound, grouped_gemm_k_fp64,
-                   grouped_gemm_k_bound)
+                   grouped_gemm_k_bound, round_bf16, gemm_bf16_bound, gemm_accumulate_fp64,
+                   gemm_accumulate_bound)
 
 __all__ = [
     "E2M1_MAX", "E4M3_MAX", "e2m1_decode", "e2m1_encode_rn", "e2m1_encode_sr",
@@ -43,5 +44,6 @@ __all__ = [
     "unpack_nibbles", "dequantize", "rht_columnwise", "rht_columnwise_f64",
     "hadamard_matrix_from_butterfly", "rht_quantize", "rht_quantize_segments",
     "gemm_fp64", "gemm_bound", "grouped_gemm_fp64", "grouped_gemm_bound",
-    "grouped_gemm_k_fp64", "grouped_gemm_k_bound",
+    "grouped_gemm_k_fp64", "grouped_gemm_k_bound", "round_bf16", "gemm_bf16_bound",
+    "gemm_accumulate_fp64", "gemm_accumulate_bound",
 ]

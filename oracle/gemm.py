@@ -14,6 +14,18 @@ m_offsets[g]..m_offsets[g+1] of A and rows g*N..(g+1)*N of the stacked B.
 Reading R15: the MoE weight gradient groups along the contraction instead: group g sums
 over columns k_offsets[g]..k_offsets[g+1] (the tokens routed to expert g) of A [M, K] and
 B [N, K] into its own [M, N] block, stacked along rows; an empty group gives zeros.
+
+The linear-layer wrapper around these GEMMs (the forward output feeds the next layer in
+16-bit, the weight gradient accumulates into an FP32 main gradient; artiverse.ca page, same
+paragraph: only the GEMMs run in 4-bit, the rest of the layer stays in higher precision):
+Reading R18: a BF16 output is the binary32 result rounded once more to BF16 (nearest, ties
+to even). Against D64 it is accepted within the FP32 bound plus BF16's relative rounding
+error 2^-8 of the result (and half its smallest subnormal spacing).
+Reading R19: with accumulation the output is D_old + the product in binary32 (one more
+rounding of the sum); against D_old + D64 it is accepted within the FP32 bound plus 2^-24 of
+the result.
+Reading R20: the output's amax is max |D| over the values as stored (after the BF16
+rounding for a BF16 output), the tensor amax a later quantization of D needs.
 """
 from __future__ import annotations
 
@@ -76,3 +88,30 @@ def grouped_gemm_k_bound(a_hat, b_hat, k_offsets, rel: float = 1e-5) -> np.ndarr
         if hi > lo:
             out[g * m:(g + 1) * m] = gemm_bound(a[:, lo:hi], b[:, lo:hi], rel)
     return out
+
+
+def round_bf16(x) -> np.ndarray:
+    """R18: binary32 values rounded to BF16 (8 significant bits, binary32's exponent range),
+    nearest with ties to even, returned as float32. Finite inputs; a value past the largest
+    BF16 rounds to infinity as the rule implies."""
+    u = np.ascontiguousarray(np.asarray(x, dtype=np.float32)).view(np.uint32).astype(np.uint64)
+    lsb = (u >> 16) & 1
+    r = ((u + 0x7FFF + lsb) >> 16) << 16
+    return r.astype(np.uint32).view(np.float32)
+
+
+def gemm_bf16_bound(a_hat, b_hat, rel: float = 1e-5) -> np.ndarray:
+    """R18: acceptance bound of a BF16 output against D64 = gemm_fp64(a_hat, b_hat)."""
+    s = gemm_bound(a_hat, b_hat, rel)
+    return s + 2.0 ** -8 * (np.abs(gemm_fp64(a_hat, b_hat)) + s) + 2.0 ** -134
+
+
+def gemm_accumulate_fp64(d_old, a_hat, b_hat) -> np.ndarray:
+    """R19: D_old + A_hat @ B_hat^T in binary64."""
+    return np.asarray(d_old, np.float64) + gemm_fp64(a_hat, b_hat)
+
+
+def gemm_accumulate_bound(d_old, a_hat, b_hat, rel: float = 1e-5) -> np.ndarray:
+    """R19: acceptance bound of an accumulated FP32 output against gemm_accumulate_fp64."""
+    s = gemm_bound(a_hat, b_hat, rel)
+    return s + 2.0 ** -24 * (np.abs(gemm_accumulate_fp64(d_old, a_hat, b_hat)) + s) + 2.0 ** -150

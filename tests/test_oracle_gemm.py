@@ -97,3 +97,53 @@ def test_k_grouped_exact_on_small_integers():
     bound = oracle.grouped_gemm_k_bound(a, b, off)
     assert np.all(bound[3:] == 1e-5 * (np.abs(a[:, 16:]) @ np.abs(b[:, 16:]).T))
 
+
+
+def test_round_bf16_matches_torch_cast():
+    # library routine: torch's float32 -> bfloat16 conversion (nearest, ties to even)
+    rng = np.random.default_rng(5)
+    e = rng.integers(-149, 128, 20000)
+    x = (rng.uniform(1, 2, 20000) * 2.0 ** e).astype(np.float32) * rng.choice([-1, 1], 20000)
+    u = np.arange(0, 1 << 16, dtype=np.uint32) << 16
+    ties = np.concatenate([u | 0x8000, u | 0x7FFF, u | 0x8001, u]).view(np.float32)
+    x = np.concatenate([x[np.isfinite(x)], ties[np.isfinite(ties)]])
+    want = torch.from_numpy(x).to(torch.bfloat16).to(torch.float32).numpy()
+    got = oracle.round_bf16(x)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
+def test_round_bf16_ties_to_even_closed_form():
+    # 1 + 2^-8 lies halfway between 1 and 1 + 2^-7: ties to the even significand (1);
+    # 1 + 3*2^-8 lies halfway between 1 + 2^-7 and 1 + 2^-6: ties to 1 + 2^-6
+    x = np.array([1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, -(1 + 2.0 ** -8), 1 + 2.0 ** -8 + 2.0 ** -20],
+                 np.float32)
+    assert list(oracle.round_bf16(x)) == [1.0, 1 + 2.0 ** -6, -1.0, 1 + 2.0 ** -7]
+
+
+def test_bf16_bound_covers_worst_fp32_error_then_rounding():
+    # a GPU result within the FP32 bound, pushed to its extremes, then rounded to BF16 stays
+    # within the BF16 bound; a one-hot product (exact in FP32 and BF16) is covered too
+    ah, bh = _quant_pair()
+    d = oracle.gemm_fp64(ah, bh)
+    s = oracle.gemm_bound(ah, bh)
+    b16 = oracle.gemm_bf16_bound(ah, bh)
+    for sign in (-1.0, 1.0):
+        d32 = (d + sign * s).astype(np.float32)
+        assert np.all(np.abs(oracle.round_bf16(d32).astype(np.float64) - d) <= b16)
+    eye = np.eye(256)[:8]
+    assert np.all(oracle.round_bf16(oracle.gemm_fp64(ah, eye).astype(np.float32)) == oracle.round_bf16(ah[:, :8].astype(np.float32)))
+    # the bound is not loose by orders of magnitude: at most 2^-7 relative above the FP32 one
+    assert np.all(b16 <= s + 2.0 ** -7 * (np.abs(d) + s) + 2.0 ** -134)
+
+
+def test_accumulate_exact_on_small_integers():
+    rng = np.random.default_rng(9)
+    a = rng.integers(-6, 7, (5, 32)).astype(np.float64)
+    b = rng.integers(-6, 7, (4, 32)).astype(np.float64)
+    d_old = rng.integers(-1000, 1000, (5, 4)).astype(np.float64)
+    want = np.array([[int(d_old[m, n]) + sum(int(a[m, k]) * int(b[n, k]) for k in range(32)) for n in range(4)]
+                     for m in range(5)], np.float64)
+    assert np.array_equal(oracle.gemm_accumulate_fp64(d_old, a, b), want)
+    # one binary32 rounding of the sum stays inside the accumulate bound
+    d32 = (oracle.gemm_accumulate_fp64(d_old, a, b) * (1 + 2.0 ** -24)).astype(np.float32)
+    assert np.all(np.abs(d32 - want) <= oracle.gemm_accumulate_bound(d_old, a, b))
