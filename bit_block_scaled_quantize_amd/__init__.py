@@ -5,8 +5,8 @@ Every function marshals torch tensors (device memory, current stream) into the C
 returns; all arithmetic runs in the HIP kernels. If the library is not built the import
 still succeeds but every call raises, so nothing can silently fall back to another path.
 
-Names follow the C entry points: quantize, rht_quantize, gemm, grouped_gemm, grouped_gemm_k,
-amax, amax_pair, dequantize.
+Names follow the C entry points: quantize, rht_quantize, gemm, gemm_ex, grouped_gemm,
+grouped_gemm_k, amax, amax_pair, dequantize.
 """
 from __future__ import annotations
 
@@ -24,9 +24,10 @@ _STATUS = {-1: "invalid argument", -2: "unsupported", -3: "workspace", -4: "HIP 
 _DTYPE = {torch.bfloat16: 0, torch.float32: 1}
 _BLOCK = {"1x16": 0, "16x16": 1}
 _ROUND = {"rn": 0, "sr": 1}
-OP_QUANTIZE, OP_RHT_QUANTIZE, OP_GEMM, OP_GROUPED_GEMM, OP_AMAX_PAIR = 0, 1, 2, 3, 4
+OP_QUANTIZE, OP_RHT_QUANTIZE, OP_GEMM, OP_GROUPED_GEMM, OP_AMAX_PAIR, OP_GEMM_EX = 0, 1, 2, 3, 4, 5
+OUT_FP32, OUT_FP32_ACCUMULATE, OUT_BF16 = 0, 1, 2
 
-EXPORTED = ("nvfp4_quantize", "nvfp4_rht_quantize", "nvfp4_gemm", "nvfp4_grouped_gemm",
+EXPORTED = ("nvfp4_quantize", "nvfp4_rht_quantize", "nvfp4_gemm", "nvfp4_gemm_ex", "nvfp4_grouped_gemm",
             "nvfp4_grouped_gemm_k",
             "nvfp4_amax", "nvfp4_amax_pair", "nvfp4_workspace_size", "nvfp4_last_error",
             "nvfp4_dequantize")
@@ -59,6 +60,7 @@ def _load():
     lib.nvfp4_rht_quantize.argtypes = [vp, ctypes.c_int, i64, i64, i64, ctypes.c_uint16,
                                        ctypes.c_int, u64, u64, vp, i64, vp, pt, vp, sz, vp]
     lib.nvfp4_gemm.argtypes = [pt, pt, vp, i64, vp]
+    lib.nvfp4_gemm_ex.argtypes = [pt, pt, vp, i64, ctypes.c_int, vp, vp, sz, vp]
     lib.nvfp4_grouped_gemm.argtypes = [i64, vp, pt, pt, i64, vp, i64, vp, sz, vp]
     lib.nvfp4_grouped_gemm_k.argtypes = [i64, vp, pt, pt, vp, i64, vp]
     lib.nvfp4_amax.argtypes = [vp, ctypes.c_int, i64, i64, i64, vp, i64, ctypes.c_int,
@@ -197,6 +199,37 @@ def gemm(a: NVFP4Tensor, b: NVFP4Tensor, out: torch.Tensor | None = None, stream
     ac, bc = a.c(), b.c()
     _check(lib.nvfp4_gemm(ctypes.byref(ac), ctypes.byref(bc), _ptr(out), out.stride(0),
                           _stream(stream)))
+    return out
+
+
+def gemm_ex(a: NVFP4Tensor, b: NVFP4Tensor, out: torch.Tensor | None = None,
+            out_dtype: torch.dtype = torch.float32, accumulate: bool = False,
+            amax_out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+            stream=None) -> torch.Tensor:
+    """nvfp4_gemm_ex: D = A * B^T stored as float32 or bfloat16, or (accumulate, float32) added
+    to `out`; amax_out (float32 [1]) receives max |D| as stored."""
+    lib = _load()
+    if accumulate:
+        if out is None or out.dtype != torch.float32:
+            raise NVFP4Error("accumulate needs a float32 `out`")
+        kind = OUT_FP32_ACCUMULATE
+    else:
+        kind = OUT_BF16 if out_dtype == torch.bfloat16 else OUT_FP32
+        if out_dtype not in (torch.float32, torch.bfloat16):
+            raise NVFP4Error(f"unsupported output dtype {out_dtype}")
+        if out is None:
+            out = torch.empty((a.rows, b.rows), dtype=out_dtype, device=a.codes.device)
+        elif out.dtype != out_dtype:
+            raise NVFP4Error("out dtype does not match out_dtype")
+    if out.dim() != 2 or out.stride(1) != 1:
+        raise NVFP4Error("out must be 2-D with unit column stride")
+    if workspace is None:
+        workspace, ws_n = _workspace(OP_GEMM_EX, a.rows, b.rows, 1, a.codes.device)
+    else:
+        ws_n = workspace.numel()
+    ac, bc = a.c(), b.c()
+    _check(lib.nvfp4_gemm_ex(ctypes.byref(ac), ctypes.byref(bc), _ptr(out), out.stride(0), kind,
+                             _ptr(amax_out), _ptr(workspace), ws_n, _stream(stream)))
     return out
 
 

@@ -84,6 +84,7 @@ size_t nvfp4_workspace_size(int op, int64_t rows, int64_t cols, int64_t nseg) {
       return round_up(segs > partials ? segs : partials, kWsAlign);
     }
     case NVFP4_OP_AMAX_PAIR: return round_up(2 * partials, kWsAlign);
+    case NVFP4_OP_GEMM_EX: return round_up(nvfp4::gemm_ex_workspace_bytes(rows, cols), kWsAlign);
     default: return 0;
   }
 }
@@ -235,6 +236,26 @@ int nvfp4_gemm(const nvfp4_tensor* A, const nvfp4_tensor* B, float* D, int64_t l
   const nvfp4::GemmOperand a{A->codes, A->scales, A->global_scale};
   const nvfp4::GemmOperand b{B->codes, B->scales, B->global_scale};
   return hip_status(nvfp4::launch_gemm(a, b, A->rows, B->rows, A->cols, D, ldd, (hipStream_t)hip_stream), "gemm");
+}
+
+int nvfp4_gemm_ex(const nvfp4_tensor* A, const nvfp4_tensor* B, void* D, int64_t ldd, nvfp4_out out_kind,
+                  float* amax_out, void* workspace, size_t ws_bytes, void* hip_stream) {
+  int st;
+  if ((st = check_operand(A, "A")) || (st = check_operand(B, "B"))) return st;
+  if (A->cols != B->cols) return fail(NVFP4_ERR_INVALID, "K mismatch: A has %lld, B has %lld", (long long)A->cols, (long long)B->cols);
+  if (!D) return fail(NVFP4_ERR_INVALID, "D is NULL");
+  if (out_kind != NVFP4_OUT_FP32 && out_kind != NVFP4_OUT_FP32_ACCUMULATE && out_kind != NVFP4_OUT_BF16)
+    return fail(NVFP4_ERR_INVALID, "bad output kind %d", (int)out_kind);
+  if (ldd < B->rows) return fail(NVFP4_ERR_INVALID, "ldd (%lld) < N (%lld)", (long long)ldd, (long long)B->rows);
+  if (!aligned(D, out_kind == NVFP4_OUT_BF16 ? 2 : 4)) return fail(NVFP4_ERR_INVALID, "D is not aligned to its element size");
+  const size_t need = nvfp4_workspace_size(NVFP4_OP_GEMM_EX, A->rows, B->rows, 1);
+  if (need && (!workspace || ws_bytes < need))
+    return fail(NVFP4_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? ws_bytes : (size_t)0);
+  if (need && !aligned(workspace, kWsAlign)) return fail(NVFP4_ERR_INVALID, "workspace must be 256-byte aligned");
+  const nvfp4::GemmOperand a{A->codes, A->scales, A->global_scale};
+  const nvfp4::GemmOperand b{B->codes, B->scales, B->global_scale};
+  return hip_status(nvfp4::launch_gemm_ex(a, b, A->rows, B->rows, A->cols, (int)out_kind, D, ldd, amax_out,
+                                          static_cast<float*>(workspace), (hipStream_t)hip_stream), "gemm_ex");
 }
 
 int nvfp4_grouped_gemm(int64_t G, const int64_t* m_offsets, const nvfp4_tensor* A,

@@ -152,6 +152,59 @@ struct Operand {
 // lane half h = l / 32 picks which 8. Per 128-wide K step each lane therefore owns one
 // contiguous 64-code run (32 bytes, 4 scale blocks = one aligned scale dword) of its row,
 // bytes [32h, 32h + 32) of the step, and feeds its 8 octets to 8 consecutive MFMAs.
+// Output of the linear-layer entry point (nvfp4_gemm_ex): FP32, FP32 added to what D holds
+// (the weight gradient accumulating into an FP32 main gradient), or BF16 (the activations and
+// activation gradients passed on in 16-bit), with the maximum |stored value| folded into
+// `amax` (the tensor amax the next quantization of D needs, so that quantization is one pass).
+// artiverse.ca "NVIDIA's 4-bit floating point pushes AI training limits": only the GEMMs run
+// in 4-bit, the layer's other tensors in higher precision.
+enum OutKind : int { kOutF32 = 0, kOutF32Add = 1, kOutBF16 = 2 };
+
+struct ExtOut {
+  void* d;          // output, row stride ldd elements
+  int64_t ldd;
+  float* part;      // a K-split tile's partial sums (tile-local, FP32), else null
+  float* amax;      // device float or null
+};
+
+// BF16 bits of finite v rounded to nearest, ties to even.
+__device__ __forceinline__ uint32_t bf16_rn_bits(float v) {
+  const uint32_t u = __float_as_uint(v);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Stores v as output element (row, col); returns |stored value|.
+template <int KIND>
+__device__ __forceinline__ float put_out(void* d, int64_t ldd, int64_t row, int64_t col, float v) {
+  if constexpr (KIND == kOutBF16) {
+    const uint32_t b = bf16_rn_bits(v);
+    __builtin_nontemporal_store((uint16_t)b, static_cast<uint16_t*>(d) + row * ldd + col);
+    return fabsf(__uint_as_float(b << 16));
+  } else if constexpr (KIND == kOutF32Add) {
+    float* p = static_cast<float*>(d) + row * ldd + col;
+    const float sum = *p + v;
+    *p = sum;
+    return fabsf(sum);
+  } else {
+    __builtin_nontemporal_store(v, static_cast<float*>(d) + row * ldd + col);
+    return fabsf(v);
+  }
+}
+
+// Workgroup maximum of every thread's mx into *amax (one atomic; all threads must call).
+__device__ __forceinline__ void group_amax(float mx, float* amax) {
+  __shared__ float red[kThreads / 64];
+  mx = wave_max(mx);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float m = red[0];
+#pragma unroll
+    for (int w = 1; w < kThreads / 64; ++w) m = fmaxf(m, red[w]);
+    atomic_max_nonneg(amax, m);
+  }
+}
+
 namespace big {
 constexpr int kFragBytes = 32 * 64;                           // 32 rows x 128 codes
 constexpr int kFragScaleBytes = 32 * 8;                       // 32 rows x 8 scale bytes
@@ -199,13 +252,15 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, int64
 
 // One output tile of shape C summing over the elements [k_begin, k_end) of the contraction
 // (both multiples of 64; K is the operands' row length; a k_begin that is not a multiple of
-// 128 needs FIRST_HALF). With `accumulate` the scaled partial sums are added to D with
-// hardware float atomics (D pre-zeroed by the caller), else stored.
-template <class C, bool FIRST_HALF = false>
+// 128 needs FIRST_HALF). With `accumulate` (a K-split tile) the scaled partial sums are added
+// to D with hardware float atomics (D pre-zeroed by the caller), else stored. EXT: the output
+// goes to `ext` as KIND instead, a K-split tile's partial sums to ext.part.
+template <class C, bool FIRST_HALF = false, int KIND = kOutF32, bool EXT = false>
 __device__ __forceinline__ void gemm_tile_big(Operand A, Operand B, int64_t m0, int64_t m1,
                                               int64_t n0, int64_t n1, int64_t K, int64_t k_begin,
                                               int64_t k_end, bool accumulate, float alpha,
-                                              float* __restrict__ D, int64_t ldd, uint8_t* lds) {
+                                              float* __restrict__ D, int64_t ldd, uint8_t* lds,
+                                              const ExtOut ext = ExtOut{nullptr, 0, nullptr, nullptr}) {
   using big::kFragBytes;
   using big::kFragScaleBytes;
   using big::kStages;
@@ -429,6 +484,7 @@ __device__ __forceinline__ void gemm_tile_big(Operand A, Operand B, int64_t m0, 
 
   // D fragment layout (32 x 32): lane l holds column l % 32 and, for q = 0..15, row
   // 8*(q/4) + 4*(l/32) + q%4.
+  float mx = 0.0f;
 #pragma unroll
   for (int i = 0; i < kFragsM; ++i) {
 #pragma unroll
@@ -439,13 +495,23 @@ __device__ __forceinline__ void gemm_tile_big(Operand A, Operand B, int64_t m0, 
       for (int q = 0; q < 16; ++q) {
         const int64_t row = m0 + wm * kWaveM + 32 * i + 8 * (q >> 2) + 4 * h + (q & 3);
         if (row < m1) {
+          const float v = acc[i][j][q] * alpha;
           // non-temporal: D goes out to HBM while this compute-bound kernel runs instead of
           // sitting dirty in the caches and being written back during the next kernel
-          if (accumulate) unsafeAtomicAdd(&D[row * ldd + col], acc[i][j][q] * alpha);
-          else __builtin_nontemporal_store(acc[i][j][q] * alpha, &D[row * ldd + col]);
+          if constexpr (!EXT) {
+            if (accumulate) unsafeAtomicAdd(&D[row * ldd + col], v);
+            else __builtin_nontemporal_store(v, &D[row * ldd + col]);
+          } else if (accumulate) {
+            __builtin_nontemporal_store(v, &ext.part[(row - m0) * C::kBlockN + (col - n0)]);
+          } else {
+            mx = fmaxf(mx, put_out<KIND>(ext.d, ext.ldd, row, col, v));
+          }
         }
       }
     }
+  }
+  if constexpr (EXT) {
+    if (ext.amax != nullptr && !accumulate) group_amax(mx, ext.amax);   // uniform
   }
 }
 
@@ -502,6 +568,74 @@ __global__ __launch_bounds__(kThreads) void k_zero_tiles(int64_t M, int64_t N, f
         if (c + q < N) p[q] = 0.0f;
     }
   }
+}
+
+// k_gemm_big with the extended output: a split tile's two parts store their partial sums in
+// the workspace, [split tile][part][256 x 256], and k_split_fixup finishes those tiles.
+template <int KIND>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void k_gemm_big_ext(Operand A, const float* __restrict__ ag, Operand B, const float* __restrict__ bg,
+                    int64_t K, void* D, int64_t ldd, float* amax, float* part, int64_t tail_first,
+                    int splits) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds_dyn[];
+  using namespace big;
+  const int64_t tiles_m = (A.rows + kBlockM - 1) / kBlockM;
+  const int64_t tiles_n = (B.rows + kBlockN - 1) / kBlockN;
+  const int64_t steps = (K + kStepK - 1) / kStepK;
+  int64_t t = blockIdx.x, s0 = 0, s1 = steps;
+  const bool split = t >= tail_first;
+  if (split) {
+    const int64_t part_i = (t - tail_first) % splits;
+    t = tail_first + (t - tail_first) / splits;
+    s0 = steps * part_i / splits;
+    s1 = steps * (part_i + 1) / splits;
+  }
+  int64_t tm, tn;
+  tile_of(t, tiles_m, tiles_n, tm, tn);
+  const int64_t m0 = tm * kBlockM, n0 = tn * kBlockN;
+  const int64_t m1 = m0 + kBlockM < A.rows ? m0 + kBlockM : A.rows;
+  const int64_t n1 = n0 + kBlockN < B.rows ? n0 + kBlockN : B.rows;
+  const int64_t k_end = s1 * kStepK < K ? s1 * kStepK : K;
+  const ExtOut ext{D, ldd, split ? part + (blockIdx.x - tail_first) * (int64_t)(kBlockM * kBlockN) : nullptr,
+                   amax};
+  gemm_tile_big<Full, false, KIND, true>(A, B, m0, m1, n0, n1, K, s0 * kStepK, k_end, split,
+                                         ag[0] * bg[0], nullptr, ldd, lds_dyn, ext);
+}
+
+// Finishes the split tiles of k_gemm_big_ext: element = part 0 + part 1 (the lower K half
+// first, so the result does not depend on which part ran first), stored as KIND. Workgroup b
+// takes rows 16 * (b % kZeroParts) .. +15 of split tile b / kZeroParts (tile tail_first + that).
+template <int KIND>
+__global__ __launch_bounds__(kThreads) void k_split_fixup(int64_t M, int64_t N, void* D, int64_t ldd,
+                                                          const float* __restrict__ part,
+                                                          int64_t tail_first, float* amax) {
+  using namespace big;
+  constexpr int64_t kTile = (int64_t)kBlockM * kBlockN;
+  const int64_t tiles_m = (M + kBlockM - 1) / kBlockM;
+  const int64_t tiles_n = (N + kBlockN - 1) / kBlockN;
+  const int64_t tl = blockIdx.x / kZeroParts;
+  int64_t tm, tn;
+  tile_of(tail_first + tl, tiles_m, tiles_n, tm, tn);
+  const float* p0 = part + tl * 2 * kTile;
+  const float* p1 = p0 + kTile;
+  const int lr0 = (int)(blockIdx.x % kZeroParts) * 16;
+  const int c4 = (threadIdx.x & 63) * 4;
+  float mx = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16 / (kThreads / 64); ++i) {
+    const int lr = lr0 + (threadIdx.x >> 6) + i * (kThreads / 64);
+    const int64_t row = tm * kBlockM + lr;
+    if (row >= M) break;
+    const float4 a = *reinterpret_cast<const float4*>(p0 + lr * kBlockN + c4);
+    const float4 b = *reinterpret_cast<const float4*>(p1 + lr * kBlockN + c4);
+    const float v[4] = {a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int64_t col = tn * kBlockN + c4 + q;
+      if (col < N) mx = fmaxf(mx, put_out<KIND>(D, ldd, row, col, v[q]));
+    }
+  }
+  if (amax != nullptr) group_amax(mx, amax);
 }
 
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
@@ -597,9 +731,11 @@ __device__ __forceinline__ FragLoad load_frag(const uint8_t* __restrict__ codes,
   return f;
 }
 
+template <int KIND = kOutF32, bool EXT = false>
 __device__ __forceinline__ void gemm_tile_small(Operand A, Operand B, int64_t m0, int64_t m1,
                                                 int64_t n0, int64_t n1, int64_t K, float alpha,
-                                                float* __restrict__ D, int64_t ldd) {
+                                                float* __restrict__ D, int64_t ldd,
+                                                const ExtOut ext = ExtOut{nullptr, 0, nullptr, nullptr}) {
   using namespace small;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -659,6 +795,7 @@ __device__ __forceinline__ void gemm_tile_small(Operand A, Operand B, int64_t m0
     for (int j = 0; j < kFragsN; ++j) fb[j] = nb[j];
   }
 
+  float mx = 0.0f;
 #pragma unroll
   for (int i = 0; i < kFragsM; ++i) {
 #pragma unroll
@@ -668,9 +805,15 @@ __device__ __forceinline__ void gemm_tile_small(Operand A, Operand B, int64_t m0
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int64_t row = wm0 + 16 * i + 4 * g + q;
-        if (row < m1) D[row * ldd + col] = acc[i][j][q] * alpha;
+        if (row < m1) {
+          if constexpr (EXT) mx = fmaxf(mx, put_out<KIND>(ext.d, ext.ldd, row, col, acc[i][j][q] * alpha));
+          else D[row * ldd + col] = acc[i][j][q] * alpha;
+        }
       }
     }
+  }
+  if constexpr (EXT) {
+    if (ext.amax != nullptr) group_amax(mx, ext.amax);
   }
 }
 
@@ -686,6 +829,22 @@ void k_gemm_small(Operand A, const float* __restrict__ ag, Operand B, const floa
   const int64_t m1 = m0 + kBlockM < A.rows ? m0 + kBlockM : A.rows;
   const int64_t n1 = n0 + kBlockN < B.rows ? n0 + kBlockN : B.rows;
   gemm_tile_small(A, B, m0, m1, n0, n1, K, ag[0] * bg[0], D, ldd);
+}
+
+template <int KIND>
+__global__ __launch_bounds__(kThreads)
+void k_gemm_small_ext(Operand A, const float* __restrict__ ag, Operand B, const float* __restrict__ bg,
+                      int64_t K, void* D, int64_t ldd, float* amax) {
+  using namespace small;
+  const int64_t tiles_m = (A.rows + kBlockM - 1) / kBlockM;
+  const int64_t tiles_n = (B.rows + kBlockN - 1) / kBlockN;
+  int64_t tm, tn;
+  tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  const int64_t m0 = tm * kBlockM, n0 = tn * kBlockN;
+  const int64_t m1 = m0 + kBlockM < A.rows ? m0 + kBlockM : A.rows;
+  const int64_t n1 = n0 + kBlockN < B.rows ? n0 + kBlockN : B.rows;
+  gemm_tile_small<KIND, true>(A, B, m0, m1, n0, n1, K, ag[0] * bg[0], nullptr, ldd,
+                              ExtOut{D, ldd, nullptr, amax});
 }
 
 __global__ __launch_bounds__(kThreads)
@@ -723,6 +882,11 @@ hipError_t enable_big_lds() {
     hipError_t e = hipFuncSetAttribute((const void*)k_gemm_big,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, big::kLdsBytes);
     if (e != hipSuccess) return e;
+    for (const void* f : {(const void*)k_gemm_big_ext<kOutF32>, (const void*)k_gemm_big_ext<kOutF32Add>,
+                          (const void*)k_gemm_big_ext<kOutBF16>}) {
+      e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, big::kLdsBytes);
+      if (e != hipSuccess) return e;
+    }
     e = hipFuncSetAttribute((const void*)k_grouped_gemm_big,
                             hipFuncAttributeMaxDynamicSharedMemorySize, big::kLdsBytes);
     if (e != hipSuccess) return e;
@@ -730,6 +894,25 @@ hipError_t enable_big_lds() {
                                hipFuncAttributeMaxDynamicSharedMemorySize, big::kLdsBytes);
   }();
   return once;
+}
+
+// One workgroup per CU: when the tiles leave a partial last round of at most half the CUs,
+// its tiles (tail_first ..) are split along K in two halves. In launch_gemm the halves are
+// atomically added into zeroed D: two parts keep D reproducible (0 + a + b rounds the same in
+// either order); more parts would make the rounding depend on the order the atomics land in.
+void split_plan(int64_t tiles, int64_t K, int64_t& tail_first, int64_t& splits) {
+  const int64_t cus = compute_units();
+  const int64_t steps = (K + kStepK - 1) / kStepK;
+  const int64_t rem = tiles % cus;
+  splits = rem ? cus / rem : 1;
+  splits = splits > 2 ? 2 : splits;
+  splits = splits > steps ? steps : splits;
+  tail_first = splits >= 2 ? tiles - rem : tiles;
+  if (splits < 2) splits = 1;
+}
+
+int64_t big_tiles(int64_t M, int64_t N) {
+  return ((M + big::kBlockM - 1) / big::kBlockM) * ((N + big::kBlockN - 1) / big::kBlockN);
 }
 
 }  // namespace
@@ -741,19 +924,9 @@ hipError_t launch_gemm(GemmOperand a, GemmOperand b, int64_t M, int64_t N, int64
   if (use_big(K)) {
     const hipError_t e = enable_big_lds();
     if (e != hipSuccess) return e;
-    const int64_t tiles = ((M + big::kBlockM - 1) / big::kBlockM) * ((N + big::kBlockN - 1) / big::kBlockN);
-    // One workgroup per CU: when the tiles leave a partial last round, its tiles are split
-    // along K in two halves atomically added into zeroed D. Two parts keep D reproducible
-    // (0 + a + b rounds the same in either order); more parts would make the rounding depend
-    // on the order the atomics land in.
-    const int64_t cus = compute_units();
-    const int64_t steps = (K + kStepK - 1) / kStepK;
-    const int64_t rem = tiles % cus;
-    int64_t splits = rem ? cus / rem : 1;
-    splits = splits > 2 ? 2 : splits;
-    splits = splits > steps ? steps : splits;
-    const int64_t tail_first = splits >= 2 ? tiles - rem : tiles;
-    if (splits < 2) splits = 1;
+    const int64_t tiles = big_tiles(M, N);
+    int64_t tail_first, splits;
+    split_plan(tiles, K, tail_first, splits);
     if (tail_first < tiles) {
       const int vec = (ldd % 4) == 0 && (reinterpret_cast<uintptr_t>(D) % 16) == 0;
       hipLaunchKernelGGL(k_zero_tiles, dim3((unsigned)((tiles - tail_first) * kZeroParts)), dim3(kThreads), 0,
@@ -766,6 +939,51 @@ hipError_t launch_gemm(GemmOperand a, GemmOperand b, int64_t M, int64_t N, int64
     const int64_t tiles = ((M + small::kBlockM - 1) / small::kBlockM) * ((N + small::kBlockN - 1) / small::kBlockN);
     hipLaunchKernelGGL(k_gemm_small, dim3((unsigned)tiles), dim3(kThreads), 0, stream, A,
                        a.global_scale, B, b.global_scale, K, D, ldd);
+  }
+  return hipGetLastError();
+}
+
+size_t gemm_ex_workspace_bytes(int64_t M, int64_t N) {
+  if (M <= 0 || N <= 0) return 0;
+  const int64_t tiles = big_tiles(M, N);
+  int64_t tail_first, splits;
+  split_plan(tiles, 2 * kStepK, tail_first, splits);          // any K of two or more steps
+  return (size_t)(tiles - tail_first) * (size_t)splits * big::kBlockM * big::kBlockN * sizeof(float);
+}
+
+hipError_t launch_gemm_ex(GemmOperand a, GemmOperand b, int64_t M, int64_t N, int64_t K, int kind,
+                          void* D, int64_t ldd, float* amax, float* ws, hipStream_t stream) {
+  if (amax) {
+    const hipError_t e = launch_fill(amax, 1, 0.0f, stream);
+    if (e != hipSuccess) return e;
+  }
+  if (M == 0 || N == 0) return hipGetLastError();
+  const Operand A{a.codes, a.scales, M}, B{b.codes, b.scales, N};
+  if (use_big(K)) {
+    const hipError_t e = enable_big_lds();
+    if (e != hipSuccess) return e;
+    const int64_t tiles = big_tiles(M, N);
+    int64_t tail_first, splits;
+    split_plan(tiles, K, tail_first, splits);
+    const int64_t grid = tail_first + (tiles - tail_first) * splits;
+#define NVFP4_GX(KD)                                                                                  \
+  hipLaunchKernelGGL(k_gemm_big_ext<KD>, dim3((unsigned)grid), dim3(kThreads), big::kLdsBytes, stream, \
+                     A, a.global_scale, B, b.global_scale, K, D, ldd, amax, ws, tail_first, (int)splits); \
+  if (tail_first < tiles)                                                                             \
+    hipLaunchKernelGGL(k_split_fixup<KD>, dim3((unsigned)((tiles - tail_first) * kZeroParts)),         \
+                       dim3(kThreads), 0, stream, M, N, D, ldd, ws, tail_first, amax)
+    if (kind == kOutBF16) { NVFP4_GX(kOutBF16); }
+    else if (kind == kOutF32Add) { NVFP4_GX(kOutF32Add); }
+    else { NVFP4_GX(kOutF32); }
+#undef NVFP4_GX
+  } else {
+    const int64_t tiles = ((M + small::kBlockM - 1) / small::kBlockM) * ((N + small::kBlockN - 1) / small::kBlockN);
+#define NVFP4_GS(KD) hipLaunchKernelGGL(k_gemm_small_ext<KD>, dim3((unsigned)tiles), dim3(kThreads), 0, stream, \
+                                        A, a.global_scale, B, b.global_scale, K, D, ldd, amax)
+    if (kind == kOutBF16) NVFP4_GS(kOutBF16);
+    else if (kind == kOutF32Add) NVFP4_GS(kOutF32Add);
+    else NVFP4_GS(kOutF32);
+#undef NVFP4_GS
   }
   return hipGetLastError();
 }

@@ -62,6 +62,13 @@ struct GemmOperand {
 hipError_t launch_gemm(GemmOperand a, GemmOperand b, int64_t M, int64_t N, int64_t K,
                        float* D, int64_t ldd, hipStream_t stream);
 
+// The linear-layer form: kind 0 = FP32, 1 = FP32 added to D, 2 = BF16; amax (optional) gets
+// max|stored D|. A partial last round is split along K with the parts' sums in ws
+// (gemm_ex_workspace_bytes(M, N) bytes) and finished by a fixup kernel.
+size_t gemm_ex_workspace_bytes(int64_t M, int64_t N);
+hipError_t launch_gemm_ex(GemmOperand a, GemmOperand b, int64_t M, int64_t N, int64_t K, int kind,
+                          void* D, int64_t ldd, float* amax, float* ws, hipStream_t stream);
+
 hipError_t launch_grouped_gemm(int64_t G, const int64_t* m_offsets, GemmOperand a, GemmOperand b,
                                int64_t total_m, int64_t N, int64_t K, float* D, int64_t ldd,
                                hipStream_t stream);

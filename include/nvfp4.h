@@ -58,8 +58,10 @@ typedef enum { NVFP4_BLOCK_1X16 = 0, NVFP4_BLOCK_16X16 = 1 } nvfp4_block;
 typedef enum { NVFP4_ROUND_RN = 0, NVFP4_ROUND_SR = 1 } nvfp4_round;
 typedef enum {
   NVFP4_OP_QUANTIZE = 0, NVFP4_OP_RHT_QUANTIZE = 1, NVFP4_OP_GEMM = 2,
-  NVFP4_OP_GROUPED_GEMM = 3, NVFP4_OP_AMAX_PAIR = 4
+  NVFP4_OP_GROUPED_GEMM = 3, NVFP4_OP_AMAX_PAIR = 4, NVFP4_OP_GEMM_EX = 5
 } nvfp4_op;
+/* Output of nvfp4_gemm_ex: FP32, FP32 added to what D holds, or BF16. */
+typedef enum { NVFP4_OUT_FP32 = 0, NVFP4_OUT_FP32_ACCUMULATE = 1, NVFP4_OUT_BF16 = 2 } nvfp4_out;
 
 typedef struct nvfp4_tensor {
   uint8_t* codes;        /* device, [rows, cols/2]                       */
@@ -155,6 +157,33 @@ int nvfp4_rht_quantize(const void* x, nvfp4_dtype dt, int64_t tokens, int64_t co
  */
 int nvfp4_gemm(const nvfp4_tensor* A, const nvfp4_tensor* B, float* D, int64_t ldd,
                void* hip_stream);
+
+/*
+ * nvfp4_gemm_ex - nvfp4_gemm with the outputs a linear layer needs around its three GEMMs
+ * (artiverse.ca "NVIDIA's 4-bit floating point pushes AI training limits", paragraph on which
+ * parts run in 4-bit: the GEMMs take NVFP4 operands, the layer's other tensors stay in higher
+ * precision): the forward output and the activation gradient handed on in BF16, the weight
+ * gradient accumulated into an FP32 main gradient, and the output's amax produced by the GEMM
+ * itself, so the next quantization of D (amax_in) is a single pass.
+ *   A, B       as nvfp4_gemm (rows M and N, same K, % 16 == 0).
+ *   D          device [M, N] with row stride ldd >= N elements:
+ *              NVFP4_OUT_FP32             float, D = s_A s_B A B^T (as nvfp4_gemm);
+ *              NVFP4_OUT_FP32_ACCUMULATE  float, D = D + s_A s_B A B^T (one FP32 addition per
+ *                                         element; D must hold finite values);
+ *              NVFP4_OUT_BF16             bfloat16 bits (uint16), the FP32 result rounded to
+ *                                         nearest, ties to even.
+ *   amax_out   NULL, or device float[1] receiving max |D| over the values as stored (after the
+ *              BF16 rounding; after the addition when accumulating). The library clears it.
+ *   workspace  device scratch of nvfp4_workspace_size(NVFP4_OP_GEMM_EX, M, N, 1) bytes, sized
+ *              for the current device, 256-byte aligned (0 bytes, NULL allowed, when the
+ *              tiles fill whole rounds of the device's compute units): a partial last round
+ *              is split along K and the two halves' sums meet there (lower half first), so D
+ *              is reproducible.
+ * The result is deterministic for a given device. Errors: NVFP4_ERR_INVALID (null pointers,
+ * K mismatch, K % 16, ldd < N, bad kind, misaligned D), NVFP4_ERR_WORKSPACE, NVFP4_ERR_HIP.
+ */
+int nvfp4_gemm_ex(const nvfp4_tensor* A, const nvfp4_tensor* B, void* D, int64_t ldd, nvfp4_out out_kind,
+                  float* amax_out, void* workspace, size_t ws_bytes, void* hip_stream);
 
 /*
  * nvfp4_grouped_gemm - one GEMM per group (mixture-of-experts expert GEMMs; "Nemotron

@@ -117,6 +117,26 @@ def test_gemm_validation(lib):
     assert gg(2, FAKE, ctypes.byref(a), ctypes.byref(b), 8, FAKE, 8, None, 0, None) == INVALID  # B rows
 
 
+def test_gemm_ex_validation(lib):
+    a, b = _tensor(64, 128), _tensor(32, 128)
+    g = lib.nvfp4_gemm_ex
+    A, B = ctypes.byref(a), ctypes.byref(b)
+    assert g(None, B, FAKE, 32, 0, None, None, 0, None) == INVALID
+    assert g(A, ctypes.byref(_tensor(32, 96)), FAKE, 32, 0, None, None, 0, None) == INVALID   # K
+    assert g(A, B, None, 32, 0, None, None, 0, None) == INVALID                              # D
+    assert g(A, B, FAKE, 16, 0, None, None, 0, None) == INVALID                              # ldd
+    assert g(A, B, FAKE, 32, 3, None, None, 0, None) == INVALID                              # kind
+    assert g(A, B, FAKE + 2, 32, 0, None, None, 0, None) == INVALID                          # FP32 align
+    assert g(A, B, FAKE + 1, 32, 2, None, None, 0, None) == INVALID                          # BF16 align
+    # a partial last round needs the split workspace: 640 tiles of 256 x 256 on 256 CUs
+    big_a, big_b = _tensor(8192, 128), _tensor(5120, 128)
+    need = lib.nvfp4_workspace_size(nv.OP_GEMM_EX, 8192, 5120, 1)
+    assert need > 0
+    assert g(ctypes.byref(big_a), ctypes.byref(big_b), FAKE, 5120, 2, None, None, 0, None) == WORKSPACE
+    assert g(ctypes.byref(big_a), ctypes.byref(big_b), FAKE, 5120, 2, None, FAKE, need - 256, None) == WORKSPACE
+    assert g(ctypes.byref(big_a), ctypes.byref(big_b), FAKE, 5120, 2, None, FAKE + 16, need, None) == INVALID
+
+
 def test_grouped_gemm_k_validation(lib):
     a, b = _tensor(64, 128), _tensor(32, 128)
     f = lib.nvfp4_grouped_gemm_k
@@ -137,6 +157,12 @@ def test_workspace_sizes(lib):
     assert lib.nvfp4_workspace_size(nv.OP_AMAX_PAIR, 16, 16, 1) == 8192
     assert lib.nvfp4_workspace_size(nv.OP_GEMM, 16, 16, 1) == 0
     assert lib.nvfp4_workspace_size(nv.OP_GROUPED_GEMM, 16, 16, 1) == 0
+    # K-split partial round of the linear-layer GEMM: two 256 x 256 FP32 partial tiles per
+    # split tile (sizes for 256 compute units, the count assumed without a device)
+    assert lib.nvfp4_workspace_size(nv.OP_GEMM_EX, 8192, 20480, 1) == 0          # 10 whole rounds
+    assert lib.nvfp4_workspace_size(nv.OP_GEMM_EX, 8192, 5120, 1) == 128 * 2 * 256 * 256 * 4
+    assert lib.nvfp4_workspace_size(nv.OP_GEMM_EX, 20480, 5120, 1) == 64 * 2 * 256 * 256 * 4
+    assert lib.nvfp4_workspace_size(nv.OP_GEMM_EX, 256 * 200, 256, 1) == 0       # 200 > 128 left over
 
 
 def test_python_binding_raises_without_library(monkeypatch, tmp_path):
