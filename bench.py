@@ -44,6 +44,8 @@ def parse():
     p.add_argument("--steps", type=int, default=10)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--no-moe", action="store_true")
+    p.add_argument("--no-linear", action="store_true",
+                   help="skip the linear-layer wrapper step (BF16 outputs, FP32 main gradient)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-reference", action="store_true",
                    help="skip timing the vendor FP16/BF16 GEMMs on the same shapes")
@@ -269,6 +271,9 @@ def main():
         "input_gen_s": round(gen_s, 1),
     }
 
+    if not args.no_linear:
+        out["linear_layer"] = bench_linear(nv, workloads, torch, dev, stream, flush, X, W, dY, mask,
+                                           step_flops, args)
     if not args.no_moe:
         out["moe"] = bench_moe(nv, workloads, torch, dev, stream, flush, args)
     if not args.no_reference:
@@ -287,6 +292,63 @@ def gemm_traffic():
     if GEMM_TRAFFIC["source_sha256"] != digest:
         return None
     return GEMM_TRAFFIC["bytes_per_launch"]
+
+
+def bench_linear(nv, workloads, torch, dev, stream, flush, X, W, dY, mask, step_flops, args):
+    """The same layer through the autograd wrapper (NVFP4Linear): forward output and activation
+    gradient stored in BF16 with their amax from the GEMM epilogue, the weight gradient
+    accumulated into an FP32 main gradient; one step = forward + backward, timed like the main
+    step. Also each linear-layer GEMM alone (cold), against the FP32-output GEMM."""
+    from bit_block_scaled_quantize_amd.linear import NVFP4Linear
+    layer = NVFP4Linear(K_IN, N_OUT, device=dev, sign_mask=mask, seed=workloads.SR_SEED_DGRAD)
+    with torch.no_grad():
+        layer.weight.copy_(W)
+    Xg = X.detach().requires_grad_(True)
+
+    def step():
+        Xg.grad = None
+        y = layer(Xg)
+        y.backward(dY)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    res = {"ms_per_step": round(ms, 4), "TFLOP/s": round(step_flops / (ms * 1e-3) / 1e12, 1),
+           "outputs": "y, dX BF16 with fused amax; dW accumulated into FP32 main_grad"}
+
+    T = nv.NVFP4Tensor
+    Xq, Wq, WqT, dYq = T.empty(M, K_IN), T.empty(N_OUT, K_IN), T.empty(K_IN, N_OUT), T.empty(M, N_OUT)
+    dYtq, Xtq = T.empty(N_OUT, M), T.empty(K_IN, M)
+    nv.quantize(X, "1x16", "rn", out=Xq)
+    nv.quantize(W, "16x16", "rn", emit_transposed=True, out=Wq, out_t=WqT)
+    nv.quantize(dY, "1x16", "sr", seed=1, out=dYq)
+    nv.rht_quantize(dY, mask, "sr", seed=2, out=dYtq)
+    nv.rht_quantize(X, mask, "rn", out=Xtq)
+    amax = torch.empty((1,), dtype=torch.float32, device=dev)
+    Y16 = torch.empty((M, N_OUT), dtype=torch.bfloat16, device=dev)
+    dX16 = torch.empty((M, K_IN), dtype=torch.bfloat16, device=dev)
+    G = torch.zeros((N_OUT, K_IN), dtype=torch.float32, device=dev)
+    wsz = max(nv.workspace_size(nv.OP_GEMM_EX, m_, n_) for m_, n_ in ((M, N_OUT), (M, K_IN), (N_OUT, K_IN)))
+    ws = torch.empty((max(wsz, 1),), dtype=torch.uint8, device=dev)
+    flops = 2.0 * M * N_OUT * K_IN
+    calls = {
+        "gemm_ex_fprop_bf16_amax": (lambda: nv.gemm_ex(Xq, Wq, out=Y16, out_dtype=torch.bfloat16,
+                                                       amax_out=amax, workspace=ws), "TFLOP/s", flops),
+        "gemm_ex_dgrad_bf16_amax": (lambda: nv.gemm_ex(dYq, WqT, out=dX16, out_dtype=torch.bfloat16,
+                                                       amax_out=amax, workspace=ws), "TFLOP/s", flops),
+        "gemm_ex_wgrad_fp32_accumulate": (lambda: nv.gemm_ex(dYtq, Xtq, out=G, accumulate=True,
+                                                             workspace=ws), "TFLOP/s", flops),
+    }
+    fsum = torch.empty((1,), dtype=torch.int64, device=dev)
+    res.update(_time_calls(calls, torch, stream, flush, fsum, args))
+    return res
 
 
 def bench_moe(nv, workloads, torch, dev, stream, flush, args):

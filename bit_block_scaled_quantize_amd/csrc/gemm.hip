@@ -485,6 +485,41 @@ __device__ __forceinline__ void gemm_tile_big(Operand A, Operand B, int64_t m0, 
   // D fragment layout (32 x 32): lane l holds column l % 32 and, for q = 0..15, row
   // 8*(q/4) + 4*(l/32) + q%4.
   float mx = 0.0f;
+  if constexpr (EXT && KIND == kOutF32Add) {
+    if (!accumulate) {
+      // D += tile: the old values of a row of fragments are all requested before any is
+      // used, so the loads overlap instead of paying one round trip per element
+      float* Df = static_cast<float*>(ext.d);
+#pragma unroll
+      for (int i = 0; i < kFragsM; ++i) {
+        float old[kFragsN][16];
+#pragma unroll
+        for (int j = 0; j < kFragsN; ++j) {
+          const int64_t col = n0 + wn * kWaveN + 32 * j + r;
+#pragma unroll
+          for (int q = 0; q < 16; ++q) {
+            const int64_t row = m0 + wm * kWaveM + 32 * i + 8 * (q >> 2) + 4 * h + (q & 3);
+            old[j][q] = (row < m1 && col < n1) ? Df[row * ext.ldd + col] : 0.0f;
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < kFragsN; ++j) {
+          const int64_t col = n0 + wn * kWaveN + 32 * j + r;
+#pragma unroll
+          for (int q = 0; q < 16; ++q) {
+            const int64_t row = m0 + wm * kWaveM + 32 * i + 8 * (q >> 2) + 4 * h + (q & 3);
+            if (row < m1 && col < n1) {
+              const float sum = old[j][q] + acc[i][j][q] * alpha;
+              Df[row * ext.ldd + col] = sum;
+              mx = fmaxf(mx, fabsf(sum));
+            }
+          }
+        }
+      }
+      if (ext.amax != nullptr) group_amax(mx, ext.amax);
+      return;
+    }
+  }
 #pragma unroll
   for (int i = 0; i < kFragsM; ++i) {
 #pragma unroll
