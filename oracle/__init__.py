@@ -13,6 +13,8 @@ The oracle is plain numpy, written from the format description on the pages:
   * same page, section "Why 4-bit training normally falls apart - and the three fixes":
     2D (16x16) weight blocks, a random Hadamard transform on the wgrad inputs that is undone
     analytically, stochastic rounding for gradients only.
+  * same page, the MXFP4 comparison: E2M1 elements with one power-of-two (E8M0) scale per
+    32 elements, 4.25 bits per element (mx.py).
   * artiverse.ca "NVIDIA's 4-bit floating point pushes AI training limits" (stabilizer
     paragraph): 16x16 weight blocks instead of 1x16; stochastic rounding on gradients, not on
     activations; the Hadamard transform on the weight-gradient path.
@@ -32,6 +34,7 @@ from .quantize import (amax, global_scales, quantize_1x16, quantize_1x16_colsegm
                        unpack_nibbles, dequantize)
 from .hadamard import (rht_columnwise, rht_columnwise_f64, hadamard_matrix_from_butterfly, rht_quantize,
                        rht_quantize_segments)
+from .mx import (MX_BLOCK, e8m0_decode, mx_shared_exponent, quantize_mxfp4, dequantize_mxfp4)
 from .gemm import (gemm_fp64, gemm_bound, grouped_gemm_fp64, grouped_gemm_bound, grouped_gemm_k_fp64,
                    grouped_gemm_k_bound, round_bf16, gemm_bf16_bound, gemm_accumulate_fp64,
                    gemm_accumulate_bound)
@@ -46,4 +49,5 @@ __all__ = [
     "gemm_fp64", "gemm_bound", "grouped_gemm_fp64", "grouped_gemm_bound",
     "grouped_gemm_k_fp64", "grouped_gemm_k_bound", "round_bf16", "gemm_bf16_bound",
     "gemm_accumulate_fp64", "gemm_accumulate_bound",
+    "MX_BLOCK", "e8m0_decode", "mx_shared_exponent", "quantize_mxfp4", "dequantize_mxfp4",
 ]
