@@ -28,6 +28,7 @@ OP_QUANTIZE, OP_RHT_QUANTIZE, OP_GEMM, OP_GROUPED_GEMM, OP_AMAX_PAIR, OP_GEMM_EX
 OUT_FP32, OUT_FP32_ACCUMULATE, OUT_BF16 = 0, 1, 2
 
 EXPORTED = ("nvfp4_quantize", "nvfp4_rht_quantize", "nvfp4_gemm", "nvfp4_gemm_ex", "nvfp4_grouped_gemm",
+            "mxfp4_quantize",
             "nvfp4_grouped_gemm_k",
             "nvfp4_amax", "nvfp4_amax_pair", "nvfp4_workspace_size", "nvfp4_last_error",
             "nvfp4_dequantize")
@@ -40,6 +41,11 @@ class NVFP4Error(RuntimeError):
 class _CTensor(ctypes.Structure):
     _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
                 ("global_scale", ctypes.c_void_p), ("rows", ctypes.c_int64),
+                ("cols", ctypes.c_int64)]
+
+
+class _CMXTensor(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("rows", ctypes.c_int64),
                 ("cols", ctypes.c_int64)]
 
 
@@ -60,6 +66,8 @@ def _load():
     lib.nvfp4_rht_quantize.argtypes = [vp, ctypes.c_int, i64, i64, i64, ctypes.c_uint16,
                                        ctypes.c_int, u64, u64, vp, i64, vp, pt, vp, sz, vp]
     lib.nvfp4_gemm.argtypes = [pt, pt, vp, i64, vp]
+    mpt = ctypes.POINTER(_CMXTensor)
+    lib.mxfp4_quantize.argtypes = [vp, ctypes.c_int, i64, i64, i64, ctypes.c_int, u64, u64, mpt, vp]
     lib.nvfp4_gemm_ex.argtypes = [pt, pt, vp, i64, ctypes.c_int, vp, vp, sz, vp]
     lib.nvfp4_grouped_gemm.argtypes = [i64, vp, pt, pt, i64, vp, i64, vp, sz, vp]
     lib.nvfp4_grouped_gemm_k.argtypes = [i64, vp, pt, pt, vp, i64, vp]
@@ -117,6 +125,23 @@ class NVFP4Tensor:
                         self.global_scale.data_ptr(), self.rows, self.cols)
 
 
+@dataclass
+class MXFP4Tensor:
+    """Device buffers of one MXFP4 tensor [rows, cols] quantized along cols."""
+    codes: torch.Tensor         # uint8 [rows, cols/2]
+    scales: torch.Tensor        # uint8 [rows, cols/32] (E8M0 codes)
+    rows: int
+    cols: int
+
+    @classmethod
+    def empty(cls, rows: int, cols: int, device="cuda"):
+        return cls(torch.empty((rows, cols // 2), dtype=torch.uint8, device=device),
+                   torch.empty((rows, cols // 32), dtype=torch.uint8, device=device), rows, cols)
+
+    def c(self) -> _CMXTensor:
+        return _CMXTensor(self.codes.data_ptr(), self.scales.data_ptr(), self.rows, self.cols)
+
+
 def _input(x: torch.Tensor):
     if x.dtype not in _DTYPE:
         raise NVFP4Error(f"unsupported input dtype {x.dtype}")
@@ -163,6 +188,19 @@ def quantize(x: torch.Tensor, block: str = "1x16", rounding: str = "rn", seed: i
                             _ptr(workspace) if amax is None else None, ws_n, _stream(stream))
     _check(st)
     return out, (out_t if emit_transposed else None)
+
+
+def mx_quantize(x: torch.Tensor, rounding: str = "rn", seed: int = 0, offset: int = 0,
+                out: MXFP4Tensor | None = None, stream=None) -> MXFP4Tensor:
+    """mxfp4_quantize: x[rows, cols] -> MXFP4 (E8M0 scale per 32 elements)."""
+    lib = _load()
+    dt, rows, cols, ld = _input(x)
+    if out is None:
+        out = MXFP4Tensor.empty(rows, cols, x.device)
+    oc = out.c()
+    _check(lib.mxfp4_quantize(_ptr(x), dt, rows, cols, ld, _ROUND[rounding], seed & (2 ** 64 - 1),
+                              offset & (2 ** 64 - 1), ctypes.byref(oc), _stream(stream)))
+    return out
 
 
 def rht_quantize(x: torch.Tensor, sign_mask: int, rounding: str = "rn", seed: int = 0,

@@ -238,6 +238,23 @@ int nvfp4_gemm(const nvfp4_tensor* A, const nvfp4_tensor* B, float* D, int64_t l
   return hip_status(nvfp4::launch_gemm(a, b, A->rows, B->rows, A->cols, D, ldd, (hipStream_t)hip_stream), "gemm");
 }
 
+int mxfp4_quantize(const void* x, nvfp4_dtype dt, int64_t rows, int64_t cols, int64_t ld,
+                   nvfp4_round rnd, uint64_t seed, uint64_t offset, mxfp4_tensor* out,
+                   void* hip_stream) {
+  int st;
+  if ((st = check_input(x, dt, rows, cols, ld))) return st;
+  if (cols % 32) return fail(NVFP4_ERR_INVALID, "cols (%lld) must be a multiple of 32", (long long)cols);
+  if (rnd != NVFP4_ROUND_RN && rnd != NVFP4_ROUND_SR) return fail(NVFP4_ERR_INVALID, "bad rounding %d", (int)rnd);
+  if (!out || !out->codes || !out->scales) return fail(NVFP4_ERR_INVALID, "out or its buffers are NULL");
+  if (out->rows != rows || out->cols != cols)
+    return fail(NVFP4_ERR_INVALID, "out shape [%lld, %lld] does not match [%lld, %lld]", (long long)out->rows,
+                (long long)out->cols, (long long)rows, (long long)cols);
+  if (!aligned(out->codes, 8)) return fail(NVFP4_ERR_INVALID, "out codes must be 8-byte aligned");
+  return hip_status(nvfp4::launch_encode_mx(x, dt == NVFP4_IN_FP32, rows, cols, ld, rnd == NVFP4_ROUND_SR, seed,
+                                            offset, out->codes, out->scales, (hipStream_t)hip_stream),
+                    "mxfp4 encode");
+}
+
 int nvfp4_gemm_ex(const nvfp4_tensor* A, const nvfp4_tensor* B, void* D, int64_t ldd, nvfp4_out out_kind,
                   float* amax_out, void* workspace, size_t ws_bytes, void* hip_stream) {
   int st;

@@ -48,6 +48,12 @@ hipError_t launch_rht_encode(const void* x, bool fp32, int64_t tokens, int64_t c
                              const int64_t* segments, int64_t nseg, const float* amax, int parts,
                              QuantOut out, hipStream_t stream);
 
+// MXFP4 (E8M0 scale per 32 elements, no tensor scale): codes [rows, cols/2], scales
+// [rows, cols/32]; cols % 32 == 0.
+hipError_t launch_encode_mx(const void* x, bool fp32, int64_t rows, int64_t cols, int64_t ld,
+                            bool sr, uint64_t seed, uint64_t offset, uint8_t* codes,
+                            uint8_t* scales, hipStream_t stream);
+
 // p[0..n) = v
 hipError_t launch_fill(float* p, int64_t n, float v, hipStream_t stream);
 

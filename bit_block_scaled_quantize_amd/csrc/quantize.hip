@@ -347,6 +347,75 @@ __global__ __launch_bounds__(kThreads) void k_encode_1x16(
 }
 
 // ---------------------------------------------------------------------------------------
+// MXFP4 encode, the format the pages compare NVFP4 with ("Nemotron NVFP4" explainer, "What
+// NVFP4 actually is"): 32-element blocks with one power-of-two (E8M0) scale and no tensor
+// scale, so one pass over the input. The shared exponent is floor(log2(block amax)) - 2,
+// clamped to [-127, 127] (the block's largest element lands in [4, 8)); elements are
+// x * 2^-e (exact) rounded to E2M1 as in the 1x16 encode, stochastically with the same
+// Philox bytes per 16-element half. Lane = one 16-element half, walked as k_encode_1x16
+// walks blocks; the halves of a 32-block sit in lanes l and l^2 (BF16 chunks) or l and l^1
+// (FP32 chunks) and swap their maxima.
+template <typename TIn>
+__device__ __forceinline__ uint32_t mx_partner(uint32_t v) {
+  constexpr int kCtrl = sizeof(TIn) == 2 ? 0x4E : 0xB1;        // quad_perm [2,3,0,1] / [1,0,3,2]
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kCtrl, 0xF, 0xF, false);
+}
+
+template <typename TIn, bool SR>
+__global__ __launch_bounds__(kThreads) void k_encode_mx(const TIn* __restrict__ x, int64_t rows,
+                                                        int64_t cols, int64_t ld,
+                                                        uint8_t* __restrict__ codes,
+                                                        uint8_t* __restrict__ scales, uint64_t seed,
+                                                        uint64_t offset) {
+  using C = Chunk<TIn>;
+  constexpr int U = C::U;
+  constexpr int64_t kSpan = 64 * U;
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  const int64_t nwaves = (int64_t)gridDim.x * kWavesPerBlock;
+  const int64_t nb = cols >> 4;                        // 16-element halves per row (even)
+
+  C cur, nxt;
+  int64_t r = wave, b0 = 0;
+  if (r < rows) cur.load(x + r * ld, b0, nb, lane);
+  auto step = [&](C& cur, C& nxt) {
+    int64_t r_n = r, b0_n = b0 + kSpan;
+    if (b0_n >= nb) {
+      b0_n = 0;
+      r_n = r + nwaves;
+    }
+    if (r_n < rows) nxt.load(x + r_n * ld, b0_n, nb, lane);
+    uint2* cr = reinterpret_cast<uint2*>(codes + r * (cols >> 1));
+    uint8_t* sr = scales + r * (nb >> 1);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float v[16];
+      cur.get(u, lane, v);
+      const float m16 = abs_max16(v);
+      const float am = fmaxf(m16, __uint_as_float(mx_partner<TIn>(__float_as_uint(m16))));
+      int e = am > 0.0f ? __builtin_amdgcn_frexp_expf(am) - 3 : -127;   // floor(log2 am) - 2
+      e = e < -127 ? -127 : (e > 127 ? 127 : e);
+      const int64_t b = b0 + C::block_of(lane, u);
+      if (b < nb) {
+        u32x4 rnd{0, 0, 0, 0};
+        if constexpr (SR) rnd = block_random((uint64_t)(r * nb + b), seed, offset);
+        uint32_t lo, hi;
+        encode16<SR>(v, __builtin_ldexpf(1.0f, -e), rnd, lo, hi);
+        cr[b] = make_uint2(lo, hi);
+        if ((b & 1) == 0) sr[b >> 1] = (uint8_t)(e + 127);
+      }
+    }
+    r = r_n;
+    b0 = b0_n;
+  };
+  while (r < rows) {
+    step(cur, nxt);
+    if (r >= rows) break;
+    step(nxt, cur);
+  }
+}
+
+// ---------------------------------------------------------------------------------------
 // 16x16 encode. A workgroup owns a 256-row x 128-column tile: 16 strips of 16 rows x 8 tiles
 // of 16 columns. Lane pairs own one 16x16 tile (each lane 16 rows x 8 columns; the tile amax
 // is combined across the pair with one cross-lane max). Codes of x are written row by row
@@ -629,6 +698,19 @@ static void encode_1x16_t(const void* x, int64_t rows, int64_t cols, int64_t ld,
   hipLaunchKernelGGL((k_encode_1x16<TIn, SR, SEG>), dim3(grid), dim3(kThreads), 0, stream,
                      (const TIn*)x, rows, cols, ld, amax, parts, segments, nseg, out.codes,
                      out.scales, out.global_scale, seed, offset);
+}
+
+hipError_t launch_encode_mx(const void* x, bool fp32, int64_t rows, int64_t cols, int64_t ld,
+                            bool sr, uint64_t seed, uint64_t offset, uint8_t* codes,
+                            uint8_t* scales, hipStream_t stream) {
+  if (rows == 0) return hipSuccess;
+  const int grid = grid_for(rows, kWavesPerBlock, kEncodeBlocks);
+#define NVFP4_MX(T, S) hipLaunchKernelGGL((k_encode_mx<T, S>), dim3(grid), dim3(kThreads), 0, stream, \
+                                          (const T*)x, rows, cols, ld, codes, scales, seed, offset)
+  if (fp32) { if (sr) NVFP4_MX(float, true); else NVFP4_MX(float, false); }
+  else      { if (sr) NVFP4_MX(uint16_t, true); else NVFP4_MX(uint16_t, false); }
+#undef NVFP4_MX
+  return hipGetLastError();
 }
 
 hipError_t launch_encode_1x16(const void* x, bool fp32, int64_t rows, int64_t cols, int64_t ld,

@@ -71,6 +71,15 @@ typedef struct nvfp4_tensor {
   int64_t cols;          /* the quantized (contraction) dimension, % 16 == 0 */
 } nvfp4_tensor;
 
+/* MXFP4 tensor [rows, cols] quantized along cols: codes as nvfp4_tensor, one E8M0 scale per
+ * 32 elements (value 2^(code - 127)), no tensor-level scale. */
+typedef struct mxfp4_tensor {
+  uint8_t* codes;        /* device, [rows, cols/2]  */
+  uint8_t* scales;       /* device, [rows, cols/32] */
+  int64_t rows;
+  int64_t cols;          /* % 32 == 0 */
+} mxfp4_tensor;
+
 /*
  * nvfp4_quantize - two-level block quantization of x[rows, cols] along cols.
  * Defined by: "Nemotron NVFP4" explainer, "What NVFP4 actually is" (E2M1 elements, one E4M3
@@ -145,6 +154,25 @@ int nvfp4_rht_quantize(const void* x, nvfp4_dtype dt, int64_t tokens, int64_t co
                        uint16_t sign_mask, nvfp4_round rnd, uint64_t seed, uint64_t offset,
                        const int64_t* segments, int64_t nseg, const float* amax_in,
                        nvfp4_tensor* out, void* workspace, size_t ws_bytes, void* hip_stream);
+
+/*
+ * mxfp4_quantize - MXFP4 quantization of x[rows, cols] along cols, the format the pages set
+ * against NVFP4 ("Nemotron NVFP4" explainer, "What NVFP4 actually is": E2M1 elements, one
+ * power-of-two E8M0 scale per 32 elements, 4.25 bits per element, no tensor scale). The
+ * scale rule is the OCP Microscaling v1.0 conversion: shared exponent e = floor(log2(block
+ * amax)) - 2 clamped to [-127, 127] (-127 for an all-zero block), element = E2M1(x * 2^-e)
+ * rounded to nearest even (RN) or stochastically with the Philox bytes of nvfp4_quantize's SR
+ * (16-element half-block index b = (row*cols + col)/16), saturating at 6. One pass, no
+ * workspace.
+ *   x    device BF16 or FP32 (dt), element (r, c) at x[r*ld + c]; 16-byte aligned, ld a
+ *        multiple of 16 bytes' worth of elements.
+ *   out  codes/scales, out->rows == rows, out->cols == cols (cols % 32 == 0).
+ * Errors: NVFP4_ERR_INVALID (null pointers, shapes, enums), NVFP4_ERR_UNSUPPORTED (alignment),
+ * NVFP4_ERR_HIP.
+ */
+int mxfp4_quantize(const void* x, nvfp4_dtype dt, int64_t rows, int64_t cols, int64_t ld,
+                   nvfp4_round rnd, uint64_t seed, uint64_t offset, mxfp4_tensor* out,
+                   void* hip_stream);
 
 /*
  * nvfp4_gemm - D[M, N] (FP32, row stride ldd) = A[M, K] * B[N, K]^T with both operands

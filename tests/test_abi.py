@@ -20,7 +20,7 @@ FAKE = 0x10000          # 16-byte aligned, never dereferenced: validation fails 
 def _declared():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(nvfp4_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b((?:nvfp4|mxfp4)_[a-z_0-9]+)\s*\(", text)))
 
 
 @pytest.fixture(scope="module")
@@ -179,3 +179,15 @@ def test_product_package_does_not_import_oracle():
             if f.endswith((".py", ".hip", ".h", ".cpp")):
                 src = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in src and "from oracle" not in src, f
+
+
+def test_mx_quantize_validation(lib):
+    f = lib.mxfp4_quantize
+    out = nv._CMXTensor(FAKE, FAKE, 32, 64)
+    o = ctypes.byref(out)
+    assert f(None, 0, 32, 64, 64, 0, 0, 0, o, None) == INVALID                  # x
+    assert f(FAKE, 0, 32, 48, 48, 0, 0, 0, ctypes.byref(nv._CMXTensor(FAKE, FAKE, 32, 48)), None) == INVALID
+    assert f(FAKE, 0, 32, 64, 64, 2, 0, 0, o, None) == INVALID                  # rounding
+    assert f(FAKE, 0, 32, 64, 64, 0, 0, 0, None, None) == INVALID               # out
+    assert f(FAKE, 0, 16, 64, 64, 0, 0, 0, o, None) == INVALID                  # shape
+    assert f(FAKE + 2, 0, 32, 64, 64, 0, 0, 0, o, None) == UNSUPPORTED          # alignment

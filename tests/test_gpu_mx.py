@@ -1,0 +1,70 @@
+"""GPU parity of the MXFP4 path (E8M0 scale per 32 elements): quantization bit-exact against
+the oracle (RN and SR, BF16 and FP32, ragged shapes, every exponent range)."""
+import numpy as np
+import pytest
+import torch
+
+import bit_block_scaled_quantize_amd as nv
+import oracle
+import workloads
+from helpers import assert_bytes_equal, f32, log, to_device_bf16, to_device_f32
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _host(q):
+    torch.cuda.synchronize()
+    return q.codes.cpu().numpy(), q.scales.cpu().numpy()
+
+
+def _same(q, ref, what):
+    c, s = _host(q)
+    assert_bytes_equal(c, ref[0], what + " codes")
+    assert_bytes_equal(s, ref[1], what + " scales")
+
+
+@pytest.mark.parametrize("shape", [(1, 32), (3, 96), (37, 160), (130, 2048), (64, 5120), (257, 2688)])
+@pytest.mark.parametrize("rounding", ["rn", "sr"])
+def test_mx_quantize_bf16(shape, rounding):
+    log(f"mx bf16 {shape} {rounding}")
+    bits = workloads.with_outliers_bf16(shape, 700 + shape[0])
+    q = nv.mx_quantize(to_device_bf16(bits), rounding, seed=0x5EED, offset=3)
+    _same(q, oracle.quantize_mxfp4(f32(bits), rounding, seed=0x5EED, offset=3), f"mx {shape} {rounding}")
+
+
+@pytest.mark.parametrize("rounding", ["rn", "sr"])
+def test_mx_quantize_fp32_strided_and_wide_exponents(rounding):
+    log(f"mx fp32 {rounding}")
+    rng = np.random.default_rng(17)
+    rows, cols, ld = 45, 192, 200
+    x = (rng.standard_normal((rows, ld)) * np.ldexp(1.0, rng.integers(-150, 126, (rows, 1)))).astype(np.float32)
+    x[0, :32] = 0.0
+    x[1, :32] = -0.0
+    x[2, 5] = np.float32(3.0e38)
+    x[3, :64] = np.float32(2.0 ** -149)
+    dev = to_device_f32(x)[:, :cols]
+    q = nv.mx_quantize(dev, rounding, seed=99, offset=1 << 33)
+    _same(q, oracle.quantize_mxfp4(x[:, :cols], rounding, seed=99, offset=1 << 33), f"mx fp32 {rounding}")
+
+
+def test_mx_quantize_every_bf16_pattern():
+    # all 65536 BF16 bit patterns except NaN/Inf, in blocks with a shared top exponent spread
+    u = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    e = (u >> 7) & 0xFF
+    u = u[e != 0xFF]
+    n = len(u) // 32 * 32
+    bits = u[:n].reshape(-1, 128)[: (n // 128)]
+    q = nv.mx_quantize(to_device_bf16(bits), "rn")
+    _same(q, oracle.quantize_mxfp4(f32(bits), "rn"), "every bf16")
+
+
+def test_mx_validation_errors():
+    x = torch.zeros((4, 48), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(nv.NVFP4Error):
+        nv.mx_quantize(x)                                  # cols % 32
