@@ -28,7 +28,7 @@ OP_QUANTIZE, OP_RHT_QUANTIZE, OP_GEMM, OP_GROUPED_GEMM, OP_AMAX_PAIR, OP_GEMM_EX
 OUT_FP32, OUT_FP32_ACCUMULATE, OUT_BF16 = 0, 1, 2
 
 EXPORTED = ("nvfp4_quantize", "nvfp4_rht_quantize", "nvfp4_gemm", "nvfp4_gemm_ex", "nvfp4_grouped_gemm",
-            "mxfp4_quantize",
+            "mxfp4_quantize", "mxfp4_gemm",
             "nvfp4_grouped_gemm_k",
             "nvfp4_amax", "nvfp4_amax_pair", "nvfp4_workspace_size", "nvfp4_last_error",
             "nvfp4_dequantize")
@@ -68,6 +68,7 @@ def _load():
     lib.nvfp4_gemm.argtypes = [pt, pt, vp, i64, vp]
     mpt = ctypes.POINTER(_CMXTensor)
     lib.mxfp4_quantize.argtypes = [vp, ctypes.c_int, i64, i64, i64, ctypes.c_int, u64, u64, mpt, vp]
+    lib.mxfp4_gemm.argtypes = [mpt, mpt, vp, i64, vp]
     lib.nvfp4_gemm_ex.argtypes = [pt, pt, vp, i64, ctypes.c_int, vp, vp, sz, vp]
     lib.nvfp4_grouped_gemm.argtypes = [i64, vp, pt, pt, i64, vp, i64, vp, sz, vp]
     lib.nvfp4_grouped_gemm_k.argtypes = [i64, vp, pt, pt, vp, i64, vp]
@@ -200,6 +201,16 @@ def mx_quantize(x: torch.Tensor, rounding: str = "rn", seed: int = 0, offset: in
     oc = out.c()
     _check(lib.mxfp4_quantize(_ptr(x), dt, rows, cols, ld, _ROUND[rounding], seed & (2 ** 64 - 1),
                               offset & (2 ** 64 - 1), ctypes.byref(oc), _stream(stream)))
+    return out
+
+
+def mx_gemm(a: MXFP4Tensor, b: MXFP4Tensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """mxfp4_gemm: D[M, N] = A[M, K] * B[N, K]^T (FP32) on the block-scaled FP4 matrix cores."""
+    lib = _load()
+    if out is None:
+        out = torch.empty((a.rows, b.rows), dtype=torch.float32, device=a.codes.device)
+    ac, bc = a.c(), b.c()
+    _check(lib.mxfp4_gemm(ctypes.byref(ac), ctypes.byref(bc), _ptr(out), out.stride(0), _stream(stream)))
     return out
 
 

@@ -255,6 +255,29 @@ int mxfp4_quantize(const void* x, nvfp4_dtype dt, int64_t rows, int64_t cols, in
                     "mxfp4 encode");
 }
 
+static int check_mx_operand(const mxfp4_tensor* t, const char* name) {
+  if (!t) return fail(NVFP4_ERR_INVALID, "%s is NULL", name);
+  if (!t->codes || !t->scales) return fail(NVFP4_ERR_INVALID, "%s has a NULL codes/scales pointer", name);
+  if (t->rows < 0 || t->cols < 0 || t->cols % 32)
+    return fail(NVFP4_ERR_INVALID, "%s shape [%lld, %lld]: cols must be a non-negative multiple of 32", name,
+                (long long)t->rows, (long long)t->cols);
+  if (!aligned(t->codes, 16)) return fail(NVFP4_ERR_INVALID, "%s codes must be 16-byte aligned", name);
+  if (t->rows * (t->cols / 2) > (int64_t)0x7FFFFFFF)
+    return fail(NVFP4_ERR_UNSUPPORTED, "%s codes exceed 2 GiB", name);
+  return NVFP4_OK;
+}
+
+int mxfp4_gemm(const mxfp4_tensor* A, const mxfp4_tensor* B, float* D, int64_t ldd, void* hip_stream) {
+  int st;
+  if ((st = check_mx_operand(A, "A")) || (st = check_mx_operand(B, "B"))) return st;
+  if (A->cols != B->cols) return fail(NVFP4_ERR_INVALID, "K mismatch: A has %lld, B has %lld", (long long)A->cols, (long long)B->cols);
+  if (!D) return fail(NVFP4_ERR_INVALID, "D is NULL");
+  if (ldd < B->rows) return fail(NVFP4_ERR_INVALID, "ldd (%lld) < N (%lld)", (long long)ldd, (long long)B->rows);
+  if (A->cols % 128) return fail(NVFP4_ERR_UNSUPPORTED, "K (%lld) must be a multiple of 128", (long long)A->cols);
+  return hip_status(nvfp4::launch_gemm_mx(A->codes, A->scales, B->codes, B->scales, A->rows, B->rows, A->cols, D, ldd,
+                                          (hipStream_t)hip_stream), "mxfp4 gemm");
+}
+
 int nvfp4_gemm_ex(const nvfp4_tensor* A, const nvfp4_tensor* B, void* D, int64_t ldd, nvfp4_out out_kind,
                   float* amax_out, void* workspace, size_t ws_bytes, void* hip_stream) {
   int st;

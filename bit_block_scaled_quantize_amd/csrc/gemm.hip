@@ -898,6 +898,200 @@ void k_grouped_gemm_small(int64_t G, const int64_t* __restrict__ off, Operand A,
   gemm_tile_small(A, Bg, m0, m1, n0, n1, K, ag[g] * bg[g], D, ldd);
 }
 
+// ---------------------------------------------------------------------------------------
+// MXFP4 GEMM on gfx950's block-scaled FP4 matrix instruction (v_mfma_scale_f32_32x32x64_f8f6f4
+// with both operands E2M1): the format's power-of-two scale per 32 elements is exactly what
+// the instruction applies per lane, so the codes go from LDS to the matrix core untouched.
+// Lane l of a 32x32x64 instruction holds row l % 32, elements 32*(l/32) .. +31 of the 64
+// (16 bytes) and that block's E8M0 scale in byte 0 of its scale operand (checked on the
+// device). D = sum over k of a*b with FP32 accumulation; MXFP4 has no tensor scale.
+//
+// Tile 256 x 256, 4 waves of 128 x 128 (4 x 4 instructions per 64 elements), K steps of 128
+// (K % 128 == 0). Per step the workgroup's FP4 panels (2 x 16 KB) and E8M0 bytes (2 x 1 KB)
+// go from global memory to LDS by buffer-to-LDS DMA, three steps deep, in the same fragment
+// layout as the NVFP4 kernel: fragment f's 32 rows x 64 bytes at f * 2 KB, lane (r, h) of
+// half q holding row r, bytes [32h + 16q, +16). The instruction for elements 64s.. of the
+// step then reads, for lane (r, h), half h at lane slot r + 32s: one 16-byte LDS read.
+// Scales: per fragment 32 dwords (a row's 4 scale bytes of the step) at 128 B apart.
+namespace mx {
+constexpr int kBlockM = 256, kBlockN = 256, kFragsA = 8, kFrags = 16;
+constexpr int kFragBytes = 2048, kScaleFragBytes = 128;
+constexpr int kCodeBytes = kFrags * kFragBytes;                  // 32 KB
+constexpr int kStageBytes = kCodeBytes + kFrags * kScaleFragBytes;  // 34 KB
+constexpr int kStages = 3;
+constexpr int kLdsBytes = kStages * kStageBytes;
+constexpr int kDmaCodes = kFrags * 2 / 4;                        // 1 KB operations per wave
+constexpr int kDmaScales = kFrags / 2 / 4;                       // 256 B operations per wave
+constexpr int kDmaPerWave = kDmaCodes + kDmaScales;              // 10
+}  // namespace mx
+
+typedef int int32x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ float16v mfma_mx(v4u32 a, v4u32 b, float16v c, uint32_t sa, uint32_t sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+      int32x8{(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0},
+      int32x8{(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0}, c, 4, 4, 0, (int)sa, 0, (int)sb);
+}
+
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void k_gemm_mx(Operand A, Operand B, int64_t K, float* __restrict__ D, int64_t ldd) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds_dyn[];
+  uint8_t* lds = lds_dyn;
+  using namespace mx;
+  const int64_t tiles_m = (A.rows + kBlockM - 1) / kBlockM;
+  const int64_t tiles_n = (B.rows + kBlockN - 1) / kBlockN;
+  int64_t tm, tn;
+  tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  const int64_t m0 = tm * kBlockM, n0 = tn * kBlockN;
+  const int64_t m1 = m0 + kBlockM < A.rows ? m0 + kBlockM : A.rows;
+  const int64_t n1 = n0 + kBlockN < B.rows ? n0 + kBlockN : B.rows;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = lane & 31, h = lane >> 5;
+  const int wm = wave >> 1, wn = wave & 1;
+  const uint32_t rs_codes = (uint32_t)(K >> 1), rs_scales = (uint32_t)(K >> 5);
+  constexpr uint32_t kBeyond = 0x80000000u;
+  const int steps = __builtin_amdgcn_readfirstlane((int)(K / kStepK));
+
+  const __amdgpu_buffer_rsrc_t a_codes = make_rsrc(A.codes, A.rows * (K >> 1));
+  const __amdgpu_buffer_rsrc_t b_codes = make_rsrc(B.codes, B.rows * (K >> 1));
+  const __amdgpu_buffer_rsrc_t a_scales = make_rsrc(A.scales, A.rows * (K >> 5));
+  const __amdgpu_buffer_rsrc_t b_scales = make_rsrc(B.scales, B.rows * (K >> 5));
+
+  // DMA of a step: code operation i (0..7) of this wave moves half q = i & 1 of fragment
+  // f = wave + 4 * (i >> 1) (f < 8: A rows m0 + 32 f.., else B rows n0 + 32 (f - 8)..); scale
+  // operation j (0..1) moves the dwords of fragments 2g and 2g + 1, g = wave + 4 j (lane half h
+  // takes fragment 2g + h). Steps past the last are issued with an out-of-range offset (zeros,
+  // no memory traffic) into the buffer nobody reads again, so the loop has no branches.
+  const uint32_t lane_codes = (uint32_t)r * rs_codes + (uint32_t)(h * 32);
+  const uint32_t lane_scales = (uint32_t)r * rs_scales;
+  auto issue_dma_part = [&](int step, int buf, int p) {
+    uint8_t* base = lds + buf * kStageBytes;
+    const bool live = step < steps;
+    if (p < kDmaCodes) {
+      const int i = p;
+      const int q = i & 1, f = wave + 4 * (i >> 1);
+      const bool is_a = (i >> 1) < 2;                            // f < 8 for every wave
+      const uint32_t row = __builtin_amdgcn_readfirstlane(
+          (uint32_t)((is_a ? m0 : n0) + 32 * (is_a ? f : f - kFragsA)));
+      const uint32_t su = row * rs_codes + (uint32_t)(step * (kStepK / 2)) + 16u * q;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a ? a_codes : b_codes,
+                                               (lds_ptr_t)(base + f * kFragBytes + q * 1024), 16,
+                                               lane_codes + (live ? su : kBeyond), 0, 0, 0);
+    } else {
+      const int j = p - kDmaCodes;
+      const int g = wave + 4 * j;                                 // fragments 2g, 2g + 1
+      const bool is_a = j == 0;                                   // 2g + 1 < 8 for every wave
+      const uint32_t row0 = (uint32_t)((is_a ? m0 : n0) + 32 * (is_a ? 2 * g : 2 * g - kFragsA));
+      const uint32_t su = (row0 + 32u * (uint32_t)h) * rs_scales + (uint32_t)(step * (kStepK / 32));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a ? a_scales : b_scales,
+                                               (lds_ptr_t)(base + kCodeBytes + 2 * g * kScaleFragBytes), 4,
+                                               lane_scales + (live ? su : kBeyond), 0, 0, 0);
+    }
+  };
+  auto issue_dma = [&](int step, int buf) {
+#pragma unroll
+    for (int p = 0; p < kDmaPerWave; ++p) issue_dma_part(step, buf, p);
+  };
+
+  float16v acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = float16v{};
+
+  // operands of one step: [fragment][64-element half] and the scale dwords
+  struct Ops { v4u32 a[4][2], b[4][2]; uint32_t sa[4], sb[4]; };
+  auto read_ops = [&](int buf, Ops& o) {
+    const uint8_t* base = lds + buf * kStageBytes;
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const int off = h * 1024 + (r + 32 * s2) * 16;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        o.a[i][s2] = *reinterpret_cast<const v4u32*>(base + (wm * 4 + i) * kFragBytes + off);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        o.b[j][s2] = *reinterpret_cast<const v4u32*>(base + (kFragsA + wn * 4 + j) * kFragBytes + off);
+    }
+    const uint8_t* sc = base + kCodeBytes + r * 4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o.sa[i] = *reinterpret_cast<const uint32_t*>(sc + (wm * 4 + i) * kScaleFragBytes);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) o.sb[j] = *reinterpret_cast<const uint32_t*>(sc + (kFragsA + wn * 4 + j) * kScaleFragBytes);
+  };
+  auto barrier = [] {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  constexpr int kWaitFirst = big::waitcnt_imm(2 * kDmaPerWave, 15);   // steps 1, 2 may fly
+  constexpr int kWaitNext = big::waitcnt_imm(kDmaPerWave, 0);        // step s+2 may fly
+
+#pragma unroll
+  for (int p = 0; p < kStages; ++p) issue_dma(p, p);
+  __builtin_amdgcn_s_waitcnt(kWaitFirst);
+  barrier();
+
+  // the block scale of lane (r, h) for the 64-element half s2 of the step: byte 2*s2 + h of
+  // the row's scale dword, moved to byte 0 (the byte the instruction reads)
+  // With dma_step >= 0 the DMA of that step into dma_buf is spread over the row groups: the
+  // compiler orders an LDS-bound DMA after the wave's pending LDS reads (it cannot tell the
+  // buffers apart), so issuing it behind a few instructions lets the reads land first.
+  auto mma_half = [&](const Ops& o, int s2, int dma_step, int dma_buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t sa = o.sa[i] >> (8 * (2 * s2 + h));
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = mfma_mx(o.a[i][s2], o.b[j][s2], acc[i][j], sa, o.sb[j] >> (8 * (2 * s2 + h)));
+      if (dma_step >= 0) {
+#pragma unroll
+        for (int p = i * kDmaPerWave / 4; p < (i + 1) * kDmaPerWave / 4; ++p) issue_dma_part(dma_step, dma_buf, p);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // One step: half 0 of `cur`; the barrier (every wave has read step s's buffer, step s+1
+  // has landed); the reads of step s+1 into `nxt`, then half 1 of `cur` with the DMA of step
+  // s+3 into step s's buffer spread over it.
+  int b_cur = 0;
+  Ops cur, nxt;
+  read_ops(0, cur);
+  auto step = [&](int s, Ops& c, Ops& n) {
+    const int b_next = b_cur == kStages - 1 ? 0 : b_cur + 1;
+    mma_half(c, 0, -1, 0);
+    __builtin_amdgcn_s_waitcnt(kWaitNext);
+    barrier();
+    read_ops(b_next, n);
+    mma_half(c, 1, s + 3, b_cur);
+    b_cur = b_next;
+  };
+  int s = 0;
+  for (; s + 1 < steps; s += 2) {
+    step(s, cur, nxt);
+    step(s + 1, nxt, cur);
+  }
+  if (s < steps) step(s, cur, nxt);
+  __builtin_amdgcn_s_waitcnt(big::waitcnt_imm(0, 15));             // no DMA may outlive the tile
+
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t col = n0 + wn * 128 + 32 * j + r;
+      if (col >= n1) continue;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int64_t row = m0 + wm * 128 + 32 * i + 8 * (q >> 2) + 4 * h + (q & 3);
+        if (row < m1) __builtin_nontemporal_store(acc[i][j][q], &D[row * ldd + col]);
+      }
+    }
+  }
+}
+
 bool use_big(int64_t K) { return K > 0 && (K % 64) == 0; }
 
 // Compute units of the current device (queried once).
@@ -975,6 +1169,19 @@ hipError_t launch_gemm(GemmOperand a, GemmOperand b, int64_t M, int64_t N, int64
     hipLaunchKernelGGL(k_gemm_small, dim3((unsigned)tiles), dim3(kThreads), 0, stream, A,
                        a.global_scale, B, b.global_scale, K, D, ldd);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_mx(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
+                          const uint8_t* b_scales, int64_t M, int64_t N, int64_t K, float* D,
+                          int64_t ldd, hipStream_t stream) {
+  if (M == 0 || N == 0) return hipSuccess;
+  static const hipError_t attr = hipFuncSetAttribute((const void*)k_gemm_mx,
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, mx::kLdsBytes);
+  if (attr != hipSuccess) return attr;
+  const Operand A{a_codes, a_scales, M}, B{b_codes, b_scales, N};
+  const int64_t tiles = ((M + mx::kBlockM - 1) / mx::kBlockM) * ((N + mx::kBlockN - 1) / mx::kBlockN);
+  hipLaunchKernelGGL(k_gemm_mx, dim3((unsigned)tiles), dim3(kThreads), mx::kLdsBytes, stream, A, B, K, D, ldd);
   return hipGetLastError();
 }
 

@@ -68,6 +68,11 @@ struct GemmOperand {
 hipError_t launch_gemm(GemmOperand a, GemmOperand b, int64_t M, int64_t N, int64_t K,
                        float* D, int64_t ldd, hipStream_t stream);
 
+// MXFP4 GEMM (E8M0 scale per 32 along K, no tensor scale): D[M, N] FP32 = A B^T; K % 128 == 0.
+hipError_t launch_gemm_mx(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
+                          const uint8_t* b_scales, int64_t M, int64_t N, int64_t K, float* D,
+                          int64_t ldd, hipStream_t stream);
+
 // The linear-layer form: kind 0 = FP32, 1 = FP32 added to D, 2 = BF16; amax (optional) gets
 // max|stored D|. A partial last round is split along K with the parts' sums in ws
 // (gemm_ex_workspace_bytes(M, N) bytes) and finished by a fixup kernel.

@@ -175,6 +175,18 @@ int mxfp4_quantize(const void* x, nvfp4_dtype dt, int64_t rows, int64_t cols, in
                    void* hip_stream);
 
 /*
+ * mxfp4_gemm - D[M, N] (FP32, row stride ldd) = A[M, K] * B[N, K]^T with both operands MXFP4
+ * (mxfp4_quantize along K): the comparison format of the pages ("Nemotron NVFP4" explainer,
+ * "What NVFP4 actually is") on gfx950's block-scaled FP4 matrix instruction, which applies
+ * the E8M0 scales of each 32-element block itself. Products exact, FP32 accumulation.
+ *   A: rows = M, cols = K; B: rows = N, cols = K (same K, K % 128 == 0); ldd >= N; each
+ *   operand's codes below 2 GiB.
+ * Errors: NVFP4_ERR_INVALID (null pointers, K mismatch, cols % 32, ldd < N),
+ * NVFP4_ERR_UNSUPPORTED (K % 128, operand size), NVFP4_ERR_HIP.
+ */
+int mxfp4_gemm(const mxfp4_tensor* A, const mxfp4_tensor* B, float* D, int64_t ldd, void* hip_stream);
+
+/*
  * nvfp4_gemm - D[M, N] (FP32, row stride ldd) = A[M, K] * B[N, K]^T with both operands
  * NVFP4 (each quantized along K), products accumulated in FP32, scaled by
  * A->global_scale[0] * B->global_scale[0]. Covers the forward, activation-gradient and

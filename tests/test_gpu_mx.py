@@ -68,3 +68,37 @@ def test_mx_validation_errors():
     x = torch.zeros((4, 48), dtype=torch.bfloat16, device="cuda")
     with pytest.raises(nv.NVFP4Error):
         nv.mx_quantize(x)                                  # cols % 32
+
+
+def _mx_pair(m, n, k, seed):
+    a_bits = workloads.with_outliers_bf16((m, k), seed)
+    b_bits = workloads.normal_bf16((n, k), seed + 1, std=0.02)
+    qa = nv.mx_quantize(to_device_bf16(a_bits), "rn")
+    qb = nv.mx_quantize(to_device_bf16(b_bits), "sr", seed=4, offset=2)
+    ra = oracle.quantize_mxfp4(f32(a_bits))
+    rb = oracle.quantize_mxfp4(f32(b_bits), "sr", seed=4, offset=2)
+    _same(qa, ra, "A")
+    _same(qb, rb, "B")
+    return qa, qb, oracle.dequantize_mxfp4(*ra), oracle.dequantize_mxfp4(*rb)
+
+
+@pytest.mark.parametrize("mnk", [(1, 1, 128), (37, 70, 256), (256, 256, 128), (300, 520, 640),
+                                 (513, 1024, 2688), (1000, 33, 5120)])
+def test_mx_gemm_within_bound(mnk):
+    from helpers import assert_gemm_within_bound
+    m, n, k = mnk
+    log(f"mx gemm {mnk}")
+    qa, qb, ah, bh = _mx_pair(m, n, k, 800 + m + k)
+    out = torch.full((m, n + 3), -5.0, device="cuda")
+    nv.mx_gemm(qa, qb, out=out[:, :n])
+    torch.cuda.synchronize()
+    o = out.cpu().numpy()
+    assert np.all(o[:, n:] == -5.0)
+    assert_gemm_within_bound(o[:, :n], ah, bh, f"mx gemm {mnk}")
+
+
+def test_mx_gemm_unsupported_k():
+    qa = nv.MXFP4Tensor.empty(16, 96)
+    qb = nv.MXFP4Tensor.empty(16, 96)
+    with pytest.raises(nv.NVFP4Error):
+        nv.mx_gemm(qa, qb)
