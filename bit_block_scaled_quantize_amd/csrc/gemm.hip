@@ -907,22 +907,26 @@ void k_grouped_gemm_small(int64_t G, const int64_t* __restrict__ off, Operand A,
 // device). D = sum over k of a*b with FP32 accumulation; MXFP4 has no tensor scale.
 //
 // Tile 256 x 256, 4 waves of 128 x 128 (4 x 4 instructions per 64 elements), K steps of 128
-// (K % 128 == 0). Per step the workgroup's FP4 panels (2 x 16 KB) and E8M0 bytes (2 x 1 KB)
-// go from global memory to LDS by buffer-to-LDS DMA, three steps deep, in the same fragment
-// layout as the NVFP4 kernel: fragment f's 32 rows x 64 bytes at f * 2 KB, lane (r, h) of
-// half q holding row r, bytes [32h + 16q, +16). The instruction for elements 64s.. of the
-// step then reads, for lane (r, h), half h at lane slot r + 32s: one 16-byte LDS read.
-// Scales: per fragment 32 dwords (a row's 4 scale bytes of the step) at 128 B apart.
+// (K % 128 == 0), DMA four steps deep. The matrix instruction consumes a step's operands
+// four times faster than the FP16 path, so what limits this kernel is the number of L2
+// requests the buffer-to-LDS DMA makes, not bytes: four lanes read a row's 64 bytes of a
+// step (one request per row and step instead of two), and the E8M0 bytes move 16 per row
+// (four steps) per request into a two-deep ring. In LDS a fragment is 32 rows x 64 bytes,
+// row-major, with the 16-byte chunk c of row r stored at chunk c ^ ((r >> 2) & 3), so the
+// instruction's 16-byte reads (row r, chunk 2s + h) fall in distinct banks.
 namespace mx {
 constexpr int kBlockM = 256, kBlockN = 256, kFragsA = 8, kFrags = 16;
-constexpr int kFragBytes = 2048, kScaleFragBytes = 128;
-constexpr int kCodeBytes = kFrags * kFragBytes;                  // 32 KB
-constexpr int kStageBytes = kCodeBytes + kFrags * kScaleFragBytes;  // 34 KB
-constexpr int kStages = 3;
-constexpr int kLdsBytes = kStages * kStageBytes;
-constexpr int kDmaCodes = kFrags * 2 / 4;                        // 1 KB operations per wave
-constexpr int kDmaScales = kFrags / 2 / 4;                       // 256 B operations per wave
-constexpr int kDmaPerWave = kDmaCodes + kDmaScales;              // 10
+constexpr int kFragBytes = 2048;                                  // 32 rows x 64 bytes
+constexpr int kCodeBytes = kFrags * kFragBytes;                   // 32 KB per K step
+constexpr int kStages = 4;
+constexpr int kGroupSteps = 4;                                    // K steps per scale move
+constexpr int kScaleGroupBytes = (kBlockM + kBlockN) * 16;        // 16 bytes per row: 8 KB
+constexpr int kScaleBase = kStages * kCodeBytes;
+constexpr int kPadBase = kScaleBase + 2 * kScaleGroupBytes;       // target of idle scale moves
+constexpr int kLdsBytes = kPadBase + 1024;                        // 145 KB
+constexpr int kDmaScales = (kBlockM + kBlockN) / 64 / 4;          // 2 per wave
+constexpr int kDmaCodes = kFrags * 2 / 4;                         // 8 per wave
+constexpr int kDmaPerWave = kDmaScales + kDmaCodes;               // per step, idle or not
 }  // namespace mx
 
 typedef int int32x8 __attribute__((ext_vector_type(8)));
@@ -959,35 +963,41 @@ void k_gemm_mx(Operand A, Operand B, int64_t K, float* __restrict__ D, int64_t l
   const __amdgpu_buffer_rsrc_t a_scales = make_rsrc(A.scales, A.rows * (K >> 5));
   const __amdgpu_buffer_rsrc_t b_scales = make_rsrc(B.scales, B.rows * (K >> 5));
 
-  // DMA of a step: code operation i (0..7) of this wave moves half q = i & 1 of fragment
-  // f = wave + 4 * (i >> 1) (f < 8: A rows m0 + 32 f.., else B rows n0 + 32 (f - 8)..); scale
-  // operation j (0..1) moves the dwords of fragments 2g and 2g + 1, g = wave + 4 j (lane half h
-  // takes fragment 2g + h). Steps past the last are issued with an out-of-range offset (zeros,
-  // no memory traffic) into the buffer nobody reads again, so the loop has no branches.
-  const uint32_t lane_codes = (uint32_t)r * rs_codes + (uint32_t)(h * 32);
-  const uint32_t lane_scales = (uint32_t)r * rs_scales;
+  // DMA for K step `step` (prefetched into code buffer `buf`), 10 operations per wave:
+  //  p = 0, 1: the E8M0 bytes of steps step .. step+3 when step % 4 == 0 (group step/4 into
+  //    scale buffer (step/4) % 2), rows 64 (wave + 4p) .. +63 of the 512 (A then B), lane l
+  //    one row's 16 bytes; other steps issue the operation idle (out of range, into a pad
+  //    area), so every step issues the same number of operations and the waits are constant.
+  //  p = 2..9: code operation i = p - 2: half q = i & 1 (rows 16q .. +15) of fragment
+  //    f = wave + 4 (i >> 1); lane l reads row 16q + l/4, chunk (l & 3) ^ ((l >> 4) & 3) of
+  //    the step's 64 bytes (the swizzle of the LDS layout: the chunk's row has (r >> 2) & 3 =
+  //    (l >> 4) & 3) into LDS f * 2 KB + q * 1 KB + l * 16.
+  // Steps past the last are issued out of range too (zeros, no memory traffic) into buffers
+  // nobody reads again, so the loop has no branches.
+  const uint32_t lane_codes = (uint32_t)(lane >> 2) * rs_codes + 16u * (uint32_t)((lane & 3) ^ ((lane >> 4) & 3));
+  const uint32_t lane_scales = (uint32_t)lane * rs_scales;
   auto issue_dma_part = [&](int step, int buf, int p) {
-    uint8_t* base = lds + buf * kStageBytes;
     const bool live = step < steps;
-    if (p < kDmaCodes) {
-      const int i = p;
-      const int q = i & 1, f = wave + 4 * (i >> 1);
-      const bool is_a = (i >> 1) < 2;                            // f < 8 for every wave
-      const uint32_t row = __builtin_amdgcn_readfirstlane(
-          (uint32_t)((is_a ? m0 : n0) + 32 * (is_a ? f : f - kFragsA)));
-      const uint32_t su = row * rs_codes + (uint32_t)(step * (kStepK / 2)) + 16u * q;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a ? a_codes : b_codes,
-                                               (lds_ptr_t)(base + f * kFragBytes + q * 1024), 16,
-                                               lane_codes + (live ? su : kBeyond), 0, 0, 0);
+    if (p < kDmaScales) {
+      const bool real = live && (step % kGroupSteps) == 0;         // uniform
+      const int blk = wave + 4 * p;                                 // 64-row block of the 512
+      const bool is_a = p == 0;
+      const uint32_t row0 = (uint32_t)((is_a ? m0 : n0) + 64 * (is_a ? blk : blk - 4));
+      const uint32_t su = row0 * rs_scales + (uint32_t)(step * (kStepK / 32));
+      uint8_t* dst = real ? lds + kScaleBase + ((step / kGroupSteps) & 1) * kScaleGroupBytes + blk * 1024
+                          : lds + kPadBase;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a ? a_scales : b_scales, (lds_ptr_t)dst, 16,
+                                               lane_scales + (real ? su : kBeyond), 0, 0, 0);
     } else {
-      const int j = p - kDmaCodes;
-      const int g = wave + 4 * j;                                 // fragments 2g, 2g + 1
-      const bool is_a = j == 0;                                   // 2g + 1 < 8 for every wave
-      const uint32_t row0 = (uint32_t)((is_a ? m0 : n0) + 32 * (is_a ? 2 * g : 2 * g - kFragsA));
-      const uint32_t su = (row0 + 32u * (uint32_t)h) * rs_scales + (uint32_t)(step * (kStepK / 32));
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a ? a_scales : b_scales,
-                                               (lds_ptr_t)(base + kCodeBytes + 2 * g * kScaleFragBytes), 4,
-                                               lane_scales + (live ? su : kBeyond), 0, 0, 0);
+      const int i = p - kDmaScales;
+      const int q = i & 1, f = wave + 4 * (i >> 1);
+      const bool is_a = (i >> 1) < 2;                               // f < 8 for every wave
+      const uint32_t row = __builtin_amdgcn_readfirstlane(
+          (uint32_t)((is_a ? m0 : n0) + 32 * (is_a ? f : f - kFragsA) + 16 * q));
+      const uint32_t su = row * rs_codes + (uint32_t)(step * (kStepK / 2));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a ? a_codes : b_codes,
+                                               (lds_ptr_t)(lds + buf * kCodeBytes + f * kFragBytes + q * 1024), 16,
+                                               lane_codes + (live ? su : kBeyond), 0, 0, 0);
     }
   };
   auto issue_dma = [&](int step, int buf) {
@@ -1001,44 +1011,46 @@ void k_gemm_mx(Operand A, Operand B, int64_t K, float* __restrict__ D, int64_t l
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = float16v{};
 
-  // operands of one step: [fragment][64-element half] and the scale dwords
+  // operands of one step: [fragment][64-element half] and the scale dwords. Lane (r, h) reads
+  // row r, chunk 2 s2 + h, stored at chunk (2 s2 + h) ^ ((r >> 2) & 3).
+  const int off0 = r * 64 + ((h ^ ((r >> 2) & 3)) << 4);
+  const int off1 = r * 64 + (((2 + h) ^ ((r >> 2) & 3)) << 4);
   struct Ops { v4u32 a[4][2], b[4][2]; uint32_t sa[4], sb[4]; };
-  auto read_ops = [&](int buf, Ops& o) {
-    const uint8_t* base = lds + buf * kStageBytes;
+  auto read_ops = [&](int step, int buf, Ops& o) {
+    const uint8_t* base = lds + buf * kCodeBytes;
 #pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      const int off = h * 1024 + (r + 32 * s2) * 16;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        o.a[i][s2] = *reinterpret_cast<const v4u32*>(base + (wm * 4 + i) * kFragBytes + off);
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        o.b[j][s2] = *reinterpret_cast<const v4u32*>(base + (kFragsA + wn * 4 + j) * kFragBytes + off);
+    for (int i = 0; i < 4; ++i) {
+      o.a[i][0] = *reinterpret_cast<const v4u32*>(base + (wm * 4 + i) * kFragBytes + off0);
+      o.a[i][1] = *reinterpret_cast<const v4u32*>(base + (wm * 4 + i) * kFragBytes + off1);
     }
-    const uint8_t* sc = base + kCodeBytes + r * 4;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) o.sa[i] = *reinterpret_cast<const uint32_t*>(sc + (wm * 4 + i) * kScaleFragBytes);
+    for (int j = 0; j < 4; ++j) {
+      o.b[j][0] = *reinterpret_cast<const v4u32*>(base + (kFragsA + wn * 4 + j) * kFragBytes + off0);
+      o.b[j][1] = *reinterpret_cast<const v4u32*>(base + (kFragsA + wn * 4 + j) * kFragBytes + off1);
+    }
+    const uint8_t* sc = lds + kScaleBase + ((step / kGroupSteps) & 1) * kScaleGroupBytes +
+                        (step % kGroupSteps) * 4 + r * 16;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) o.sb[j] = *reinterpret_cast<const uint32_t*>(sc + (kFragsA + wn * 4 + j) * kScaleFragBytes);
+    for (int i = 0; i < 4; ++i) o.sa[i] = *reinterpret_cast<const uint32_t*>(sc + ((wm * 4 + i) * 32) * 16);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) o.sb[j] = *reinterpret_cast<const uint32_t*>(sc + (kBlockM + (wn * 4 + j) * 32) * 16);
   };
   auto barrier = [] {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   };
-  constexpr int kWaitFirst = big::waitcnt_imm(2 * kDmaPerWave, 15);   // steps 1, 2 may fly
-  constexpr int kWaitNext = big::waitcnt_imm(kDmaPerWave, 0);        // step s+2 may fly
+  constexpr int kWaitFirst = big::waitcnt_imm((kStages - 1) * kDmaPerWave, 15);   // step 0 landed
+  constexpr int kWaitNext = big::waitcnt_imm((kStages - 2) * kDmaPerWave, 0);     // step s+1 landed
 
 #pragma unroll
   for (int p = 0; p < kStages; ++p) issue_dma(p, p);
   __builtin_amdgcn_s_waitcnt(kWaitFirst);
   barrier();
 
-  // the block scale of lane (r, h) for the 64-element half s2 of the step: byte 2*s2 + h of
-  // the row's scale dword, moved to byte 0 (the byte the instruction reads)
-  // With dma_step >= 0 the DMA of that step into dma_buf is spread over the row groups: the
-  // compiler orders an LDS-bound DMA after the wave's pending LDS reads (it cannot tell the
-  // buffers apart), so issuing it behind a few instructions lets the reads land first.
+  // With dma_step >= 0 that step's DMA into dma_buf is spread over the row groups, behind
+  // the instructions, so the wave's pending LDS reads land before the compiler's ordering of
+  // LDS-bound DMA after them can stall issue.
   auto mma_half = [&](const Ops& o, int s2, int dma_step, int dma_buf) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -1055,18 +1067,18 @@ void k_gemm_mx(Operand A, Operand B, int64_t K, float* __restrict__ D, int64_t l
   };
 
   // One step: half 0 of `cur`; the barrier (every wave has read step s's buffer, step s+1
-  // has landed); the reads of step s+1 into `nxt`, then half 1 of `cur` with the DMA of step
-  // s+3 into step s's buffer spread over it.
+  // and its scale group have landed); the reads of step s+1 into `nxt`, then half 1 of `cur`
+  // with the DMA of step s+4 into step s's buffer spread over it.
   int b_cur = 0;
   Ops cur, nxt;
-  read_ops(0, cur);
+  read_ops(0, 0, cur);
   auto step = [&](int s, Ops& c, Ops& n) {
     const int b_next = b_cur == kStages - 1 ? 0 : b_cur + 1;
     mma_half(c, 0, -1, 0);
     __builtin_amdgcn_s_waitcnt(kWaitNext);
     barrier();
-    read_ops(b_next, n);
-    mma_half(c, 1, s + 3, b_cur);
+    read_ops(s + 1, b_next, n);
+    mma_half(c, 1, s + kStages, b_cur);
     b_cur = b_next;
   };
   int s = 0;
