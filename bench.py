@@ -26,6 +26,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense FP16/BF16 MFMA, TFLOP/s
+MFMA_FP4_PEAK_TFLOPS = 10100.0  # MI355X dense FP4 (MX-scaled) MFMA, TFLOP/s
 
 M, K_IN, N_OUT = 8192, 5120, 20480
 
@@ -44,6 +45,7 @@ def parse():
     p.add_argument("--steps", type=int, default=10)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--no-moe", action="store_true")
+    p.add_argument("--no-mx", action="store_true", help="skip the MXFP4 comparison path")
     p.add_argument("--no-linear", action="store_true",
                    help="skip the linear-layer wrapper step (BF16 outputs, FP32 main gradient)")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -274,6 +276,8 @@ def main():
     if not args.no_linear:
         out["linear_layer"] = bench_linear(nv, workloads, torch, dev, stream, flush, X, W, dY, mask,
                                            step_flops, args)
+    if not args.no_mx:
+        out["mxfp4"] = bench_mx(nv, workloads, torch, dev, stream, flush, X, W, dY, args)
     if not args.no_moe:
         out["moe"] = bench_moe(nv, workloads, torch, dev, stream, flush, args)
     if not args.no_reference:
@@ -348,6 +352,41 @@ def bench_linear(nv, workloads, torch, dev, stream, flush, X, W, dY, mask, step_
     }
     fsum = torch.empty((1,), dtype=torch.int64, device=dev)
     res.update(_time_calls(calls, torch, stream, flush, fsum, args))
+    return res
+
+
+def bench_mx(nv, workloads, torch, dev, stream, flush, X, W, dY, args):
+    """The comparison format of the pages, MXFP4 (E8M0 scale per 32 elements, no tensor scale),
+    on the same layer: quantize (single pass: no amax) and the three GEMMs on gfx950's
+    block-scaled FP4 matrix instruction, against its 10.1 PFLOP/s peak. Each GEMM operand is
+    quantized along its contraction; the transposed sources (W^T, dY^T, X^T) are laid out by
+    torch before timing. Cold caches, median of --kernel-reps."""
+    T = nv.MXFP4Tensor
+    Wt, dYt, Xt = W.t().contiguous(), dY.t().contiguous(), X.t().contiguous()
+    qX, qW, qdY, qWt = T.empty(M, K_IN), T.empty(N_OUT, K_IN), T.empty(M, N_OUT), T.empty(K_IN, N_OUT)
+    qdYt, qXt = T.empty(N_OUT, M), T.empty(K_IN, M)
+    for src, q, rnd in ((X, qX, "rn"), (W, qW, "rn"), (dY, qdY, "sr"), (Wt, qWt, "rn"), (dYt, qdYt, "sr"),
+                        (Xt, qXt, "rn")):
+        nv.mx_quantize(src, rnd, seed=7, out=q)
+    Y = torch.empty((M, N_OUT), dtype=torch.float32, device=dev)
+    dX = torch.empty((M, K_IN), dtype=torch.float32, device=dev)
+    dW = torch.empty((N_OUT, K_IN), dtype=torch.float32, device=dev)
+    flops = 2.0 * M * N_OUT * K_IN
+    mxq = lambda rows, cols: rows * cols * (2 + 0.5 + 1.0 / 32)     # BF16 in, codes + E8M0 out
+    calls = {
+        "mx_quantize_x_rn": (lambda: nv.mx_quantize(X, "rn", out=qX), "GB/s", mxq(M, K_IN)),
+        "mx_quantize_dy_sr": (lambda: nv.mx_quantize(dY, "sr", seed=7, out=qdY), "GB/s", mxq(M, N_OUT)),
+        "mx_quantize_w_rn": (lambda: nv.mx_quantize(W, "rn", out=qW), "GB/s", mxq(N_OUT, K_IN)),
+        "mx_gemm_fprop": (lambda: nv.mx_gemm(qX, qW, out=Y), "TFLOP/s", flops),
+        "mx_gemm_dgrad": (lambda: nv.mx_gemm(qdY, qWt, out=dX), "TFLOP/s", flops),
+        "mx_gemm_wgrad": (lambda: nv.mx_gemm(qdYt, qXt, out=dW), "TFLOP/s", flops),
+    }
+    fsum = torch.empty((1,), dtype=torch.int64, device=dev)
+    res = _time_calls(calls, torch, stream, flush, fsum, args)
+    for k in ("mx_gemm_fprop", "mx_gemm_dgrad", "mx_gemm_wgrad"):
+        res[k]["frac_mfma_fp4"] = round(res[k]["TFLOP/s"] / MFMA_FP4_PEAK_TFLOPS, 4)
+        del res[k]["frac_mfma_f16"]
+    res["bits_per_element"] = 4.25
     return res
 
 
