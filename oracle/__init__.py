@@ -33,7 +33,7 @@ from .quantize import (amax, global_scales, quantize_1x16, quantize_1x16_colsegm
                        pack_nibbles,
                        unpack_nibbles, dequantize)
 from .hadamard import (rht_columnwise, rht_columnwise_f64, hadamard_matrix_from_butterfly, rht_quantize,
-                       rht_quantize_segments)
+                       rht_quantize_segments, rht_rowwise, rht_rowwise_quantize)
 from .mx import (MX_BLOCK, e8m0_decode, mx_shared_exponent, quantize_mxfp4, dequantize_mxfp4)
 from .gemm import (gemm_fp64, gemm_bound, grouped_gemm_fp64, grouped_gemm_bound, grouped_gemm_k_fp64,
                    grouped_gemm_k_bound, round_bf16, gemm_bf16_bound, gemm_accumulate_fp64,
@@ -45,7 +45,8 @@ __all__ = [
     "amax", "global_scales", "quantize_1x16", "quantize_1x16_colsegments", "quantize_16x16",
     "pack_nibbles",
     "unpack_nibbles", "dequantize", "rht_columnwise", "rht_columnwise_f64",
-    "hadamard_matrix_from_butterfly", "rht_quantize", "rht_quantize_segments",
+    "hadamard_matrix_from_butterfly", "rht_quantize", "rht_quantize_segments", "rht_rowwise",
+    "rht_rowwise_quantize",
     "gemm_fp64", "gemm_bound", "grouped_gemm_fp64", "grouped_gemm_bound",
     "grouped_gemm_k_fp64", "grouped_gemm_k_bound", "round_bf16", "gemm_bf16_bound",
     "gemm_accumulate_fp64", "gemm_accumulate_bound",

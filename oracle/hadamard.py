@@ -22,6 +22,17 @@ Reading R6 (where the pages are silent)
     exact product (pinned against exact rational arithmetic).
   * The output is written transposed: y[c, t] for input x[t, c], so that the quantization
     that follows runs along tokens in ordinary 1x16 row blocks.
+
+Reading R23 (the Mosaic variant: thelatentdaily "What matters for NVFP4 training?", the
+combined recipe applies random Hadamard transforms on both backward GEMMs, with 1D weight
+quantization, which pairs naturally with rotations in the backward pass)
+  * dgrad contracts over the layer's output features N: dX = dY W = (dY Q^T)(W^T Q^T)^T
+    with Q acting on blocks of 16 consecutive output features. dY's rows are transformed
+    in place (each row's 16-blocks, the "rowwise" transform, same butterfly and rounding as
+    R6) and quantized 1x16 along the row (SR); W's columns are transformed along N exactly
+    as the wgrad operands are along tokens (rht_quantize(W) gives W^T Q^T as [K, N]
+    quantized along N).
+  * Weights in that variant are quantized 1x16 (1D) for the forward GEMM.
 """
 from __future__ import annotations
 
@@ -90,3 +101,18 @@ def rht_quantize(x, sign_mask: int, rounding: str = "rn", seed: int = 0, offset:
     y = rht_columnwise(x, sign_mask)
     return quantize_1x16(y, rounding=rounding, seed=seed, offset=offset,
                          amax_vals=amax_vals, row_ids=col_ids)
+
+
+def rht_rowwise(x, sign_mask: int) -> np.ndarray:
+    """R23: the transform of each row's 16-element blocks (the R6 butterfly on x^T), rounded
+    once to float32. x[rows, cols] -> y[rows, cols]."""
+    x = np.asarray(x, dtype=np.float32)
+    return np.ascontiguousarray(rht_columnwise(np.ascontiguousarray(x.T), sign_mask))
+
+
+def rht_rowwise_quantize(x, sign_mask: int, rounding: str = "rn", seed: int = 0, offset: int = 0,
+                         amax_vals=None):
+    """R23: rowwise transform, then 1x16 quantization along the rows (tensor scale from the
+    transformed values unless amax_vals is given). Returns (codes, scales, s_dec)."""
+    return quantize_1x16(rht_rowwise(x, sign_mask), rounding=rounding, seed=seed, offset=offset,
+                         amax_vals=amax_vals)

@@ -136,3 +136,37 @@ def test_rht_quantize_segments_rn_equal_separate_token_ranges():
         c, s, sd = oracle.rht_quantize(x[lo:hi], mask)
         assert np.array_equal(codes[:, lo // 2:hi // 2], c)
         assert np.array_equal(scales[:, lo // 16:hi // 16], s) and s_dec[g] == sd[0]
+
+
+def test_rowwise_transform_is_the_block_matrix_on_each_row():
+    # each row's 16-blocks times (1/4 H16 D)^T, against the explicit matrix product in
+    # binary64 (exact for these values) rounded once to float32
+    x = _bf16((8, 48), 21)
+    mask = 0x6E04
+    H = oracle.hadamard_matrix_from_butterfly()
+    T = 0.25 * H @ np.diag(oracle.hadamard.sign_vector(mask))
+    want = (x.astype(np.float64).reshape(8, 3, 16) @ T.T).reshape(8, 48).astype(np.float32)
+    assert np.array_equal(oracle.rht_rowwise(x, mask), want)
+
+
+def test_dgrad_gemm_invariant_under_rowwise_and_columnwise_transforms():
+    # R23: (dY Q^T) against (W^T Q^T) contracts to dY W: the rowwise transform of dY and the
+    # columnwise (along N) transform of W cancel, with the same mask
+    dy = _bf16((32, 64), 22, std=1e-3)
+    w = _bf16((64, 48), 23, std=0.02)          # [N, K]
+    mask = 0x1234
+    ref = dy.astype(np.float64) @ w.astype(np.float64)
+    a = oracle.rht_columnwise_f64(np.ascontiguousarray(dy.T), mask)                # [M, N] rowwise, exact
+    b = oracle.rht_columnwise_f64(w, mask)                                         # [K, N]
+    assert np.allclose(a @ b.T, ref, rtol=1e-12, atol=1e-18)
+
+
+def test_rowwise_quantize_is_quantize_of_the_transformed_rows():
+    x = _bf16((16, 64), 24)
+    q = oracle.rht_rowwise_quantize(x, 0x00FF, "sr", seed=3, offset=9)
+    y = oracle.rht_rowwise(x, 0x00FF)
+    r = oracle.quantize_1x16(y, "sr", seed=3, offset=9)
+    for u, v in zip(q, r):
+        assert np.array_equal(u, v)
+    # the transformed block's largest element maps near the grid's top, as any 1x16 block
+    assert oracle.amax(y)[0] > 0
