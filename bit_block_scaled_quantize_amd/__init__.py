@@ -28,7 +28,7 @@ OP_QUANTIZE, OP_RHT_QUANTIZE, OP_GEMM, OP_GROUPED_GEMM, OP_AMAX_PAIR, OP_GEMM_EX
 OUT_FP32, OUT_FP32_ACCUMULATE, OUT_BF16 = 0, 1, 2
 
 EXPORTED = ("nvfp4_quantize", "nvfp4_rht_quantize", "nvfp4_gemm", "nvfp4_gemm_ex", "nvfp4_grouped_gemm",
-            "mxfp4_quantize", "mxfp4_gemm",
+            "mxfp4_quantize", "mxfp4_gemm", "nvfp4_rht_rows_quantize",
             "nvfp4_grouped_gemm_k",
             "nvfp4_amax", "nvfp4_amax_pair", "nvfp4_workspace_size", "nvfp4_last_error",
             "nvfp4_dequantize")
@@ -69,6 +69,8 @@ def _load():
     mpt = ctypes.POINTER(_CMXTensor)
     lib.mxfp4_quantize.argtypes = [vp, ctypes.c_int, i64, i64, i64, ctypes.c_int, u64, u64, mpt, vp]
     lib.mxfp4_gemm.argtypes = [mpt, mpt, vp, i64, vp]
+    lib.nvfp4_rht_rows_quantize.argtypes = [vp, ctypes.c_int, i64, i64, i64, ctypes.c_uint16, ctypes.c_int,
+                                            u64, u64, vp, pt, vp, sz, vp]
     lib.nvfp4_gemm_ex.argtypes = [pt, pt, vp, i64, ctypes.c_int, vp, vp, sz, vp]
     lib.nvfp4_grouped_gemm.argtypes = [i64, vp, pt, pt, i64, vp, i64, vp, sz, vp]
     lib.nvfp4_grouped_gemm_k.argtypes = [i64, vp, pt, pt, vp, i64, vp]
@@ -191,6 +193,29 @@ def quantize(x: torch.Tensor, block: str = "1x16", rounding: str = "rn", seed: i
     return out, (out_t if emit_transposed else None)
 
 
+def rht_rows_quantize(x: torch.Tensor, sign_mask: int, rounding: str = "rn", seed: int = 0,
+                      offset: int = 0, amax: torch.Tensor | None = None, out: NVFP4Tensor | None = None,
+                      workspace: torch.Tensor | None = None, stream=None) -> NVFP4Tensor:
+    """nvfp4_rht_rows_quantize: each row's 16-blocks through the random-sign Hadamard
+    transform, then 1x16 quantization along the rows (same shape as x)."""
+    lib = _load()
+    dt, rows, cols, ld = _input(x)
+    if out is None:
+        out = NVFP4Tensor.empty(rows, cols, 1, x.device)
+    ws_n = 0
+    if amax is None:
+        if workspace is None:
+            workspace, ws_n = _workspace(OP_QUANTIZE, rows, cols, 1, x.device)
+        else:
+            ws_n = workspace.numel()
+    oc = out.c()
+    _check(lib.nvfp4_rht_rows_quantize(_ptr(x), dt, rows, cols, ld, sign_mask & 0xFFFF, _ROUND[rounding],
+                                       seed & (2 ** 64 - 1), offset & (2 ** 64 - 1), _ptr(amax),
+                                       ctypes.byref(oc), _ptr(workspace) if amax is None else None, ws_n,
+                                       _stream(stream)))
+    return out
+
+
 def mx_quantize(x: torch.Tensor, rounding: str = "rn", seed: int = 0, offset: int = 0,
                 out: MXFP4Tensor | None = None, stream=None) -> MXFP4Tensor:
     """mxfp4_quantize: x[rows, cols] -> MXFP4 (E8M0 scale per 32 elements)."""
@@ -310,17 +335,18 @@ def grouped_gemm_k(k_offsets: torch.Tensor, a: NVFP4Tensor, b: NVFP4Tensor,
     return out
 
 
-def amax(x: torch.Tensor, segments: torch.Tensor | None = None, rht: bool = False,
+def amax(x: torch.Tensor, segments: torch.Tensor | None = None, rht: bool | int = False,
          sign_mask: int = 0, out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
          stream=None) -> torch.Tensor:
-    """nvfp4_amax: max|x| per segment (or of the Hadamard-transformed tensor)."""
+    """nvfp4_amax: max|x| per segment, or of the Hadamard-transformed tensor: rht = True (or 1)
+    along tokens as rht_quantize, rht = 2 along each row as rht_rows_quantize."""
     lib = _load()
     dt, rows, cols, ld = _input(x)
     nseg = 1 if segments is None else segments.numel() - 1
     if out is None:
         out = torch.empty((nseg,), dtype=torch.float32, device=x.device)
     if workspace is None:
-        workspace, ws_n = _workspace(OP_RHT_QUANTIZE if rht else OP_QUANTIZE, rows, cols, nseg, x.device)
+        workspace, ws_n = _workspace(OP_RHT_QUANTIZE if int(rht) == 1 else OP_QUANTIZE, rows, cols, nseg, x.device)
     else:
         ws_n = workspace.numel()
     _check(lib.nvfp4_amax(_ptr(x), dt, rows, cols, ld, _ptr(segments), nseg, int(rht),

@@ -92,10 +92,24 @@ size_t nvfp4_workspace_size(int op, int64_t rows, int64_t cols, int64_t nseg) {
 int nvfp4_amax(const void* x, nvfp4_dtype dt, int64_t rows, int64_t cols, int64_t ld,
                const int64_t* segments, int64_t nseg, int rht, uint16_t sign_mask,
                float* amax_out, void* workspace, size_t ws_bytes, void* hip_stream) {
-  int st = check_input(x, dt, rows, cols, ld, !rht);
+  if (rht < 0 || rht > 2) return fail(NVFP4_ERR_INVALID, "bad rht selector %d", rht);
+  int st = check_input(x, dt, rows, cols, ld, rht != 1);
   if (st) return st;
   if (!amax_out) return fail(NVFP4_ERR_INVALID, "amax_out is NULL");
   if (nseg < 1 || (!segments && nseg != 1)) return fail(NVFP4_ERR_INVALID, "bad segment table (nseg=%lld)", (long long)nseg);
+  if (rht == 2) {                                   // rowwise rotation, unsegmented
+    if (segments) return fail(NVFP4_ERR_UNSUPPORTED, "the rowwise rotation takes no segments");
+    if (cols % 16) return fail(NVFP4_ERR_INVALID, "cols (%lld) must be a multiple of 16", (long long)cols);
+    const size_t need = nvfp4_workspace_size(NVFP4_OP_QUANTIZE, rows, cols, 1);
+    if (!workspace || ws_bytes < need || !aligned(workspace, kWsAlign))
+      return fail(NVFP4_ERR_WORKSPACE, "workspace of %zu bytes (256-byte aligned) required, got %zu", need, ws_bytes);
+    float* ws = static_cast<float*>(workspace);
+    int parts = 1;
+    hipStream_t s = (hipStream_t)hip_stream;
+    if ((st = hip_status(nvfp4::launch_rot_amax_parts(x, dt == NVFP4_IN_FP32, rows, cols, ld, sign_mask, ws, &parts, s),
+                         "rotated amax"))) return st;
+    return hip_status(nvfp4::launch_reduce_partials(ws, parts, amax_out, s), "amax reduce");
+  }
   if (rht && rows % 16) return fail(NVFP4_ERR_INVALID, "tokens (%lld) must be a multiple of 16", (long long)rows);
   if (!rht && cols % 16) return fail(NVFP4_ERR_INVALID, "cols (%lld) must be a multiple of 16", (long long)cols);
   const bool need_ws = !segments;
@@ -121,6 +135,33 @@ int nvfp4_amax(const void* x, nvfp4_dtype dt, int64_t rows, int64_t cols, int64_
   float* ws = static_cast<float*>(workspace);
   if ((st = hip_status(nvfp4::launch_amax_parts(x, f32, rows, cols, ld, nullptr, 1, ws, &parts, s), "amax"))) return st;
   return hip_status(nvfp4::launch_reduce_partials(ws, parts, amax_out, s), "amax reduce");
+}
+
+int nvfp4_rht_rows_quantize(const void* x, nvfp4_dtype dt, int64_t rows, int64_t cols, int64_t ld,
+                            uint16_t sign_mask, nvfp4_round rnd, uint64_t seed, uint64_t offset,
+                            const float* amax_in, nvfp4_tensor* out, void* workspace, size_t ws_bytes,
+                            void* hip_stream) {
+  int st;
+  if ((st = check_input(x, dt, rows, cols, ld))) return st;
+  if (cols % 16) return fail(NVFP4_ERR_INVALID, "cols (%lld) must be a multiple of 16", (long long)cols);
+  if (rnd != NVFP4_ROUND_RN && rnd != NVFP4_ROUND_SR) return fail(NVFP4_ERR_INVALID, "bad rounding %d", (int)rnd);
+  if ((st = check_out(out, rows, cols, "out"))) return st;
+  hipStream_t s = (hipStream_t)hip_stream;
+  const bool f32 = dt == NVFP4_IN_FP32;
+  const float* amax = amax_in;
+  int parts = 1;
+  if (!amax) {
+    const size_t need = nvfp4_workspace_size(NVFP4_OP_QUANTIZE, rows, cols, 1);
+    if (!workspace || ws_bytes < need || !aligned(workspace, kWsAlign))
+      return fail(NVFP4_ERR_WORKSPACE, "workspace of %zu bytes (256-byte aligned) required, got %zu", need, ws_bytes);
+    float* ws = static_cast<float*>(workspace);
+    if ((st = hip_status(nvfp4::launch_rot_amax_parts(x, f32, rows, cols, ld, sign_mask, ws, &parts, s), "rotated amax")))
+      return st;
+    amax = ws;
+  }
+  const nvfp4::QuantOut q{out->codes, out->scales, out->global_scale};
+  return hip_status(nvfp4::launch_encode_rot(x, f32, rows, cols, ld, sign_mask, rnd == NVFP4_ROUND_SR, seed, offset,
+                                             amax, parts, q, s), "rotated encode");
 }
 
 int nvfp4_amax_pair(const void* x, nvfp4_dtype dt, int64_t tokens, int64_t cols, int64_t ld,

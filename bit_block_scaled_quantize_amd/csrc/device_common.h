@@ -205,6 +205,35 @@ __device__ __forceinline__ void atomic_max_nonneg(float* p, float v) {
   atomicMax(reinterpret_cast<unsigned int*>(p), __float_as_uint(v));
 }
 
+// The 16-point random-sign Hadamard transform of one block ("Nemotron NVFP4" explainer, "Why
+// 4-bit training normally falls apart - and the three fixes"); the Hadamard kernels apply it
+// along tokens, the rowwise quantization along each row.
+// y[i] = rn32(1/4 * sum_j H[i][j] * s_j * v[j]) via the binary64 butterfly. For BF16 inputs
+// the factor +-1/4 is applied in binary32, where it is exact (a BF16 value times 2^-2 is a
+// multiple of 2^-135, inside binary32's subnormal grid); FP32 inputs take it in binary64.
+template <typename TIn>
+__device__ __forceinline__ void rht16(const float (&v)[16], uint32_t mask, float (&y)[16]) {
+  double u[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    if constexpr (sizeof(TIn) == 2) u[j] = (double)(v[j] * (((mask >> j) & 1u) ? -0.25f : 0.25f));
+    else u[j] = (double)v[j] * (((mask >> j) & 1u) ? -0.25 : 0.25);
+  }
+#pragma unroll
+  for (int h = 1; h < 16; h <<= 1) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      if ((j & h) == 0) {
+        const double a = u[j], b = u[j + h];
+        u[j] = a + b;
+        u[j + h] = a - b;
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) y[i] = (float)u[i];
+}
+
 // Segment containing `row` for a non-decreasing offset table off[0..nseg] (clamped).
 __device__ __forceinline__ int64_t find_segment(const int64_t* off, int64_t nseg, int64_t row) {
   int64_t lo = 0, hi = nseg - 1;

@@ -48,6 +48,14 @@ hipError_t launch_rht_encode(const void* x, bool fp32, int64_t tokens, int64_t c
                              const int64_t* segments, int64_t nseg, const float* amax, int parts,
                              QuantOut out, hipStream_t stream);
 
+// Rowwise rotation (each row's 16-blocks through the random-sign Hadamard transform) then
+// 1x16 encode: partial maxima of the rotated tensor (*parts of them), and the encode.
+hipError_t launch_rot_amax_parts(const void* x, bool fp32, int64_t rows, int64_t cols, int64_t ld,
+                                 uint16_t mask, float* partial, int* parts, hipStream_t stream);
+hipError_t launch_encode_rot(const void* x, bool fp32, int64_t rows, int64_t cols, int64_t ld, uint16_t mask,
+                             bool sr, uint64_t seed, uint64_t offset, const float* amax, int parts,
+                             QuantOut out, hipStream_t stream);
+
 // MXFP4 (E8M0 scale per 32 elements, no tensor scale): codes [rows, cols/2], scales
 // [rows, cols/32]; cols % 32 == 0.
 hipError_t launch_encode_mx(const void* x, bool fp32, int64_t rows, int64_t cols, int64_t ld,

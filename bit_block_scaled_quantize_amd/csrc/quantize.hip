@@ -244,12 +244,16 @@ struct Chunk<float> {
   }
 };
 
-template <typename TIn, bool SR, bool SEG>
+// ROT: each block is first put through the 16-point random-sign Hadamard transform (sign
+// mask `mask`), the rowwise rotation of the activation gradient of the Mosaic variant's dgrad
+// GEMM (thelatentdaily "What matters for NVFP4 training?": transforms on both backward GEMMs).
+template <typename TIn, bool SR, bool SEG, bool ROT = false>
 __global__ __launch_bounds__(kThreads) void k_encode_1x16(
     const TIn* __restrict__ x, int64_t rows, int64_t cols, int64_t ld,
     const float* __restrict__ amax, int amax_parts, const int64_t* __restrict__ seg, int64_t nseg,
     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ gscale,
-    uint64_t seed, uint64_t offset) {
+    uint64_t seed, uint64_t offset, uint32_t mask = 0) {
+  static_assert(!(SEG && ROT), "the rotated encode is unsegmented");
   using C = Chunk<TIn>;
   constexpr int U = C::U;
   constexpr int64_t kSpan = 64 * U;            // blocks of a row covered by one chunk
@@ -325,6 +329,12 @@ __global__ __launch_bounds__(kThreads) void k_encode_1x16(
     for (int u = 0; u < U; ++u) {
       float v[16];
       cur.get(u, lane, v);                       // all lanes: the exchange is wave-wide
+      if constexpr (ROT) {
+        float y[16];
+        rht16<TIn>(v, mask, y);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) v[j] = y[j];
+      }
       const int64_t b = b0 + C::block_of(lane, u);
       if (b < nb) {
         const BlockScale bs = block_scale_table(abs_max16(v), s_enc, tab);
@@ -344,6 +354,49 @@ __global__ __launch_bounds__(kThreads) void k_encode_1x16(
     if (it >= lim) break;
     step(nxt, cur);
   }
+}
+
+// Partial maxima of the rowwise-rotated tensor (the amax of k_encode_1x16<.., ROT>): waves walk
+// rows as the encode does, one partial per workgroup.
+template <typename TIn>
+__global__ __launch_bounds__(kThreads) void k_amax_rot(const TIn* __restrict__ x, int64_t rows, int64_t cols,
+                                                       int64_t ld, uint32_t mask, float* __restrict__ partial) {
+  using C = Chunk<TIn>;
+  constexpr int U = C::U;
+  constexpr int64_t kSpan = 64 * U;
+  __shared__ float red[kWavesPerBlock];
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  const int64_t nwaves = (int64_t)gridDim.x * kWavesPerBlock;
+  const int64_t nb = cols >> 4;
+  C cur, nxt;
+  int64_t r = wave, b0 = 0;
+  float m = 0.0f;
+  if (r < rows) cur.load(x + r * ld, b0, nb, lane);
+  auto step = [&](C& cur, C& nxt) {
+    int64_t r_n = r, b0_n = b0 + kSpan;
+    if (b0_n >= nb) {
+      b0_n = 0;
+      r_n = r + nwaves;
+    }
+    if (r_n < rows) nxt.load(x + r_n * ld, b0_n, nb, lane);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float v[16], y[16];
+      cur.get(u, lane, v);
+      rht16<TIn>(v, mask, y);
+      if (b0 + C::block_of(lane, u) < nb) m = fmaxf(m, abs_max16(y));
+    }
+    r = r_n;
+    b0 = b0_n;
+  };
+  while (r < rows) {
+    step(cur, nxt);
+    if (r >= rows) break;
+    step(nxt, cur);
+  }
+  m = block_max(m, red);
+  if (threadIdx.x == 0) partial[blockIdx.x] = m;
 }
 
 // ---------------------------------------------------------------------------------------
@@ -698,6 +751,29 @@ static void encode_1x16_t(const void* x, int64_t rows, int64_t cols, int64_t ld,
   hipLaunchKernelGGL((k_encode_1x16<TIn, SR, SEG>), dim3(grid), dim3(kThreads), 0, stream,
                      (const TIn*)x, rows, cols, ld, amax, parts, segments, nseg, out.codes,
                      out.scales, out.global_scale, seed, offset);
+}
+
+hipError_t launch_rot_amax_parts(const void* x, bool fp32, int64_t rows, int64_t cols, int64_t ld,
+                                 uint16_t mask, float* partial, int* parts, hipStream_t stream) {
+  const int grid = grid_for(rows, kWavesPerBlock, kMaxPartials);
+  if (fp32) hipLaunchKernelGGL((k_amax_rot<float>), dim3(grid), dim3(kThreads), 0, stream, (const float*)x, rows, cols, ld, (uint32_t)mask, partial);
+  else hipLaunchKernelGGL((k_amax_rot<uint16_t>), dim3(grid), dim3(kThreads), 0, stream, (const uint16_t*)x, rows, cols, ld, (uint32_t)mask, partial);
+  *parts = grid;
+  return hipGetLastError();
+}
+
+hipError_t launch_encode_rot(const void* x, bool fp32, int64_t rows, int64_t cols, int64_t ld, uint16_t mask,
+                             bool sr, uint64_t seed, uint64_t offset, const float* amax, int parts,
+                             QuantOut out, hipStream_t stream) {
+  if (rows == 0) return hipSuccess;
+  const int grid = grid_for(rows, kWavesPerBlock, kEncodeBlocks);
+#define NVFP4_ER(T, S) hipLaunchKernelGGL((k_encode_1x16<T, S, false, true>), dim3(grid), dim3(kThreads), 0, stream, \
+                                          (const T*)x, rows, cols, ld, amax, parts, nullptr, 1, out.codes,        \
+                                          out.scales, out.global_scale, seed, offset, (uint32_t)mask)
+  if (fp32) { if (sr) NVFP4_ER(float, true); else NVFP4_ER(float, false); }
+  else      { if (sr) NVFP4_ER(uint16_t, true); else NVFP4_ER(uint16_t, false); }
+#undef NVFP4_ER
+  return hipGetLastError();
 }
 
 hipError_t launch_encode_mx(const void* x, bool fp32, int64_t rows, int64_t cols, int64_t ld,

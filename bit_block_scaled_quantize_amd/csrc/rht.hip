@@ -64,31 +64,6 @@ struct Pair<float> {
   __device__ __forceinline__ float get(int q) const { return q == 0 ? w.x : w.y; }
 };
 
-// y[i] = rn32(1/4 * sum_j H[i][j] * s_j * v[j]) via the binary64 butterfly. For BF16 inputs
-// the factor +-1/4 is applied in binary32, where it is exact (a BF16 value times 2^-2 is a
-// multiple of 2^-135, inside binary32's subnormal grid); FP32 inputs take it in binary64.
-template <typename TIn>
-__device__ __forceinline__ void rht16(const float (&v)[16], uint32_t mask, float (&y)[16]) {
-  double u[16];
-#pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    if constexpr (sizeof(TIn) == 2) u[j] = (double)(v[j] * (((mask >> j) & 1u) ? -0.25f : 0.25f));
-    else u[j] = (double)v[j] * (((mask >> j) & 1u) ? -0.25 : 0.25);
-  }
-#pragma unroll
-  for (int h = 1; h < 16; h <<= 1) {
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      if ((j & h) == 0) {
-        const double a = u[j], b = u[j + h];
-        u[j] = a + b;
-        u[j + h] = a - b;
-      }
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < 16; ++i) y[i] = (float)u[i];
-}
 
 __device__ __forceinline__ float block_max(float m, float* red) {
   m = wave_max(m);

@@ -187,6 +187,27 @@ int mxfp4_quantize(const void* x, nvfp4_dtype dt, int64_t rows, int64_t cols, in
 int mxfp4_gemm(const mxfp4_tensor* A, const mxfp4_tensor* B, float* D, int64_t ldd, void* hip_stream);
 
 /*
+ * nvfp4_rht_rows_quantize - the rowwise random-sign Hadamard transform then 1x16 quantization
+ * along the rows: every 16-element block of a row goes through y = 1/4 * H16 * diag(s) * v
+ * (the butterfly and rounding of nvfp4_rht_quantize, signs from sign_mask) and is quantized
+ * as nvfp4_quantize's 1x16 blocks, with the tensor scale from max|y|. This is the activation
+ * gradient of the Mosaic variant's activation-gradient GEMM (thelatentdaily "What matters for
+ * NVFP4 training?": Hadamard transforms on both backward GEMMs, 1D weight quantization): with
+ * B = nvfp4_rht_quantize(W, same mask) (W^T transformed along the output features), the
+ * product of the two equals dY * W since the transform is orthogonal.
+ *   x          device BF16/FP32 [rows, cols], cols % 16 == 0, 16-byte aligned rows.
+ *   rnd, seed, offset  as nvfp4_quantize (block index b = row*(cols/16) + col/16).
+ *   amax_in    NULL or device float[1] = max|y| (nvfp4_amax with rht = 2); then no workspace.
+ *   out        [rows, cols], global_scale[1].
+ *   workspace  nvfp4_workspace_size(NVFP4_OP_QUANTIZE, rows, cols, 1) bytes when amax_in is NULL.
+ * Errors: NVFP4_ERR_INVALID, NVFP4_ERR_UNSUPPORTED (alignment), NVFP4_ERR_WORKSPACE, NVFP4_ERR_HIP.
+ */
+int nvfp4_rht_rows_quantize(const void* x, nvfp4_dtype dt, int64_t rows, int64_t cols, int64_t ld,
+                            uint16_t sign_mask, nvfp4_round rnd, uint64_t seed, uint64_t offset,
+                            const float* amax_in, nvfp4_tensor* out, void* workspace, size_t ws_bytes,
+                            void* hip_stream);
+
+/*
  * nvfp4_gemm - D[M, N] (FP32, row stride ldd) = A[M, K] * B[N, K]^T with both operands
  * NVFP4 (each quantized along K), products accumulated in FP32, scaled by
  * A->global_scale[0] * B->global_scale[0]. Covers the forward, activation-gradient and
@@ -264,14 +285,15 @@ int nvfp4_grouped_gemm_k(int64_t G, const int64_t* k_offsets, const nvfp4_tensor
 /*
  * nvfp4_amax - max|x| of x[rows, cols] (row stride ld), per row segment, into device
  * amax_out[nseg]: the first level of the two-level scale ("Nemotron NVFP4" explainer, "What
- * NVFP4 actually is": one FP32 scale per tensor). With rht != 0 the maximum is taken over the
+ * NVFP4 actually is": one FP32 scale per tensor). With rht = 1 the maximum is taken over the
  * Hadamard-transformed tensor of nvfp4_rht_quantize (rows = tokens; segments are token
- * ranges as there, multiples of 16). Useful to precompute amax_in.
- *   workspace  device scratch of nvfp4_workspace_size(rht ? NVFP4_OP_RHT_QUANTIZE :
+ * ranges as there, multiples of 16); with rht = 2 over the rowwise-transformed tensor of
+ * nvfp4_rht_rows_quantize (no segments). Useful to precompute amax_in.
+ *   workspace  device scratch of nvfp4_workspace_size(rht == 1 ? NVFP4_OP_RHT_QUANTIZE :
  *              NVFP4_OP_QUANTIZE, rows, cols, nseg) bytes, 256-byte aligned, for the partial
  *              maxima of an unsegmented tensor; may be NULL with segments (amax_out[nseg] is
  *              then written directly).
- * Errors: as nvfp4_quantize.
+ * Errors: as nvfp4_quantize; NVFP4_ERR_UNSUPPORTED for rht = 2 with segments.
  */
 int nvfp4_amax(const void* x, nvfp4_dtype dt, int64_t rows, int64_t cols, int64_t ld,
                const int64_t* segments, int64_t nseg, int rht, uint16_t sign_mask,
