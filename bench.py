@@ -46,6 +46,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--no-moe", action="store_true")
     p.add_argument("--no-mx", action="store_true", help="skip the MXFP4 comparison path")
+    p.add_argument("--no-mosaic", action="store_true", help="skip the Mosaic recipe variant step")
     p.add_argument("--no-linear", action="store_true",
                    help="skip the linear-layer wrapper step (BF16 outputs, FP32 main gradient)")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -276,6 +277,8 @@ def main():
     if not args.no_linear:
         out["linear_layer"] = bench_linear(nv, workloads, torch, dev, stream, flush, X, W, dY, mask,
                                            step_flops, args)
+    if not args.no_mosaic:
+        out["mosaic"] = bench_mosaic(nv, workloads, torch, dev, stream, X, W, dY, mask, step_flops, args)
     if not args.no_mx:
         out["mxfp4"] = bench_mx(nv, workloads, torch, dev, stream, flush, X, W, dY, args)
     if not args.no_moe:
@@ -353,6 +356,54 @@ def bench_linear(nv, workloads, torch, dev, stream, flush, X, W, dY, mask, step_
     fsum = torch.empty((1,), dtype=torch.int64, device=dev)
     res.update(_time_calls(calls, torch, stream, flush, fsum, args))
     return res
+
+
+def bench_mosaic(nv, workloads, torch, dev, stream, X, W, dY, mask, step_flops, args):
+    """The Mosaic recipe variant of the same layer step (Hadamard transforms on both backward
+    GEMMs, 1D weights): W 1x16 RN for fprop and W^T transformed along the output features for
+    dgrad; dY transformed rowwise (SR) for dgrad and along tokens (SR) for wgrad; X as in the
+    main step. Timed like the main step (K steps between events on the kernels' stream)."""
+    T = nv.NVFP4Tensor
+    Xq, Wq, WqR, dYr = T.empty(M, K_IN), T.empty(N_OUT, K_IN), T.empty(K_IN, N_OUT), T.empty(M, N_OUT)
+    dYtq, Xtq = T.empty(N_OUT, M), T.empty(K_IN, M)
+    Y = torch.empty((M, N_OUT), dtype=torch.float32, device=dev)
+    dX = torch.empty((M, K_IN), dtype=torch.float32, device=dev)
+    dW = torch.empty((N_OUT, K_IN), dtype=torch.float32, device=dev)
+    ws = torch.empty((8192,), dtype=torch.uint8, device=dev)
+    ax = torch.empty((2,), dtype=torch.float32, device=dev)
+    ady = torch.empty((2,), dtype=torch.float32, device=dev)
+    stages = [
+        lambda: nv.amax_pair(X, mask, out=ax, workspace=ws),
+        lambda: nv.quantize(X, "1x16", "rn", out=Xq, amax=ax[0:1]),
+        lambda: nv.quantize(W, "1x16", "rn", out=Wq, workspace=ws),
+        lambda: nv.rht_quantize(W, mask, "rn", out=WqR, workspace=ws),
+        lambda: nv.gemm(Xq, Wq, out=Y),
+        lambda: nv.amax(dY, rht=2, sign_mask=mask, out=ady[0:1], workspace=ws),
+        lambda: nv.amax(dY, rht=True, sign_mask=mask, out=ady[1:2], workspace=ws),
+        lambda: nv.rht_rows_quantize(dY, mask, "sr", seed=workloads.SR_SEED_DGRAD, out=dYr, amax=ady[0:1]),
+        lambda: nv.gemm(dYr, WqR, out=dX),
+        lambda: nv.rht_quantize(dY, mask, "sr", seed=workloads.SR_SEED_WGRAD, offset=workloads.SR_OFFSET_WGRAD,
+                                out=dYtq, amax=ady[1:2]),
+        lambda: nv.rht_quantize(X, mask, "rn", out=Xtq, amax=ax[1:2]),
+        lambda: nv.gemm(dYtq, Xtq, out=dW),
+    ]
+
+    def step():
+        for fn in stages:
+            fn()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    return {"ms_per_step": round(ms, 4), "TFLOP/s": round(step_flops / (ms * 1e-3) / 1e12, 1),
+            "recipe": "1x16 weights; Hadamard on dgrad (rowwise dY, W along N) and wgrad (along tokens)"}
 
 
 def bench_mx(nv, workloads, torch, dev, stream, flush, X, W, dY, args):
