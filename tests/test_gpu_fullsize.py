@@ -1,0 +1,159 @@
+"""GPU parity at the full workload sizes, through the calls and launch configurations the bench
+times: the dense layer (tokens 8192, in 5120, out 20480) and the expert layer (128 experts,
+98304 routed rows, hidden 2688, expert FFN 1856). Quantized rows and columns are compared
+bit for bit with the oracle on seeded samples (the oracle quantizes just those rows with the
+full tensor's amax, which it computes itself), tensor maxima in full, and GEMM outputs on
+sampled elements against the FP64 dot product of the oracle's own quantized rows."""
+import numpy as np
+import pytest
+import torch
+
+import bit_block_scaled_quantize_amd as nv
+import oracle
+import workloads
+from helpers import assert_bytes_equal, f32, host, log, to_device_bf16
+
+pytestmark = pytest.mark.gpu
+
+M, K_IN, N_OUT = 8192, 5120, 20480
+SAMPLE = 48
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+@pytest.fixture(scope="module")
+def dense():
+    x_bits, w_bits = workloads.fprop()
+    dy_bits = workloads.dgrad()
+    return f32(x_bits), f32(w_bits), f32(dy_bits), x_bits, w_bits, dy_bits
+
+
+def _rows_equal(gpu, ref, rows, what):
+    codes, scales, gs = gpu
+    assert_bytes_equal(codes[rows], ref[0], what + " codes")
+    assert_bytes_equal(scales[rows], ref[1], what + " scales")
+    assert_bytes_equal(gs.view(np.uint32), np.asarray(ref[2], np.float32).view(np.uint32), what + " scale")
+
+
+def _rht_amax(x, mask, chunk=1024):
+    """max |H x| over the whole tensor, column chunk by column chunk (oracle transform)."""
+    m = np.float32(0)
+    for c in range(0, x.shape[1], chunk):
+        m = max(m, np.abs(oracle.rht_columnwise(x[:, c:c + chunk], mask)).max())
+    return np.float32(m)
+
+
+def _check_samples(d, pick, a_rows, b_rows, what):
+    """d: GPU output; pick: (m, n) pairs; a_rows(m) / b_rows(n): the oracle's dequantized row."""
+    for m_, n_ in pick:
+        a, b = a_rows(m_), b_rows(n_)
+        ref = float(np.dot(a, b))
+        bound = 1e-5 * float(np.dot(np.abs(a), np.abs(b)))
+        got = float(d[m_, n_])
+        assert abs(got - ref) <= bound, f"{what} [{m_}, {n_}]: gpu {got!r} ref {ref!r} bound {bound!r}"
+
+
+def test_dense_layer_full_size(dense):
+    x, w, dy, x_bits, w_bits, dy_bits = dense
+    mask = workloads.wgrad_sign_mask()
+    rng = np.random.default_rng(2024)
+    log("dense layer full size: quantize")
+    X, W, dY = to_device_bf16(x_bits), to_device_bf16(w_bits), to_device_bf16(dy_bits)
+    ax, ady = nv.amax_pair(X, mask), nv.amax_pair(dY, mask)
+    qx, _ = nv.quantize(X, "1x16", "rn", amax=ax[0:1])
+    qw, qwt = nv.quantize(W, "16x16", "rn", emit_transposed=True)
+    qdy, _ = nv.quantize(dY, "1x16", "sr", seed=workloads.SR_SEED_DGRAD, offset=0, amax=ady[0:1])
+    qhdy = nv.rht_quantize(dY, mask, "sr", seed=workloads.SR_SEED_WGRAD, offset=workloads.SR_OFFSET_WGRAD,
+                           amax=ady[1:2])
+    qhx = nv.rht_quantize(X, mask, "rn", amax=ax[1:2])
+    torch.cuda.synchronize()
+    # tensor maxima, in full
+    a_x, a_w, a_dy = oracle.amax(x), oracle.amax(w), oracle.amax(dy)
+    h_x, h_dy = _rht_amax(x, mask), _rht_amax(dy, mask)
+    assert_bytes_equal(ax.cpu().numpy().view(np.uint32), np.array([a_x[0], h_x], np.float32).view(np.uint32), "pair X")
+    assert_bytes_equal(ady.cpu().numpy().view(np.uint32), np.array([a_dy[0], h_dy], np.float32).view(np.uint32), "pair dY")
+    # sampled rows / columns, bit for bit
+    rx = np.sort(rng.choice(M, SAMPLE, replace=False))
+    g16 = np.sort(rng.choice(N_OUT // 16, 8, replace=False))
+    rw = (g16[:, None] * 16 + np.arange(16)).reshape(-1)
+    gt16 = np.sort(rng.choice(K_IN // 16, 8, replace=False))
+    cw = (gt16[:, None] * 16 + np.arange(16)).reshape(-1)                    # rows of W^T
+    cdy = np.sort(rng.choice(N_OUT, SAMPLE, replace=False))                  # rows of (H dY)^T
+    cx = np.sort(rng.choice(K_IN, SAMPLE, replace=False))                    # rows of (H X)^T
+    ref_x = oracle.quantize_1x16(x[rx], amax_vals=a_x, row_ids=rx)
+    ref_w = oracle.quantize_16x16(w[rw], amax_vals=a_w, row_ids=rw)
+    ref_wt = oracle.quantize_16x16(np.ascontiguousarray(w[:, cw].T), amax_vals=a_w, row_ids=cw)
+    ref_dy = oracle.quantize_1x16(dy[rx], "sr", seed=workloads.SR_SEED_DGRAD, offset=0, amax_vals=a_dy, row_ids=rx)
+    ref_hdy = oracle.rht_quantize(dy[:, cdy], mask, "sr", seed=workloads.SR_SEED_WGRAD,
+                                  offset=workloads.SR_OFFSET_WGRAD, amax_vals=np.float32(h_dy), col_ids=cdy)
+    ref_hx = oracle.rht_quantize(x[:, cx], mask, "rn", amax_vals=np.float32(h_x), col_ids=cx)
+    gx, gw, gwt, gdy, ghdy, ghx = host(qx), host(qw), host(qwt), host(qdy), host(qhdy), host(qhx)
+    _rows_equal(gx, ref_x, rx, "X")
+    _rows_equal(gw, ref_w, rw, "W")
+    _rows_equal(gwt, ref_wt, cw, "W^T")
+    _rows_equal(gdy, ref_dy, rx, "dY")
+    _rows_equal(ghdy, ref_hdy, cdy, "(H dY)^T")
+    _rows_equal(ghx, ref_hx, cx, "(H X)^T")
+
+    log("dense layer full size: GEMMs")
+    y = nv.gemm(qx, qw)
+    dx = nv.gemm(qdy, qwt)
+    dw = nv.gemm(qhdy, qhx)
+    torch.cuda.synchronize()
+    # the oracle dequantizes its own quantization of each sampled output's operand rows
+    sx_d = dict(zip(rx, oracle.dequantize(*ref_x)))
+    sw_d = dict(zip(rw, oracle.dequantize(*ref_w)))
+    sdy_d = dict(zip(rx, oracle.dequantize(*ref_dy)))
+    swt_d = dict(zip(cw, oracle.dequantize(*ref_wt)))
+    shdy_d = dict(zip(cdy, oracle.dequantize(*ref_hdy)))
+    shx_d = dict(zip(cx, oracle.dequantize(*ref_hx)))
+    pick = lambda rows, cols: [(int(a), int(b)) for a, b in zip(rng.choice(rows, 64), rng.choice(cols, 64))]
+    _check_samples(y.cpu().numpy(), pick(rx, rw), sx_d.__getitem__, sw_d.__getitem__, "fprop")
+    _check_samples(dx.cpu().numpy(), pick(rx, cw), sdy_d.__getitem__, swt_d.__getitem__, "dgrad")
+    _check_samples(dw.cpu().numpy(), pick(cdy, cx), shdy_d.__getitem__, shx_d.__getitem__, "wgrad")
+
+
+def test_moe_layer_full_size():
+    log("moe full size")
+    x_bits, w_bits, off = workloads.moe()
+    G, n, k = workloads.MOE_EXPERTS, workloads.MOE_FFN, workloads.MOE_HIDDEN
+    x, w = f32(x_bits), f32(w_bits)
+    rng = np.random.default_rng(77)
+    offd = torch.from_numpy(off).cuda()
+    wseg = np.arange(G + 1, dtype=np.int64) * n
+    qx, _ = nv.quantize(to_device_bf16(x_bits), "1x16", "rn", segments=offd)
+    qw, _ = nv.quantize(to_device_bf16(w_bits), "16x16", "rn", segments=torch.from_numpy(wseg).cuda())
+    d = nv.grouped_gemm(offd, qx, qw, n)
+    torch.cuda.synchronize()
+    a_x, a_w = oracle.amax(x, off), oracle.amax(w, wseg)
+    gx, gw = host(qx), host(qw)
+    assert_bytes_equal(gx[2].view(np.uint32), oracle.global_scales(a_x)[1].astype(np.float32).view(np.uint32),
+                       "X scale per expert")
+    # sampled rows: the first and last row of a few experts (the largest and smallest among them)
+    sizes = np.diff(off)
+    experts = np.unique(np.concatenate([[np.argmax(sizes), np.argmin(sizes)], rng.choice(G, 6, replace=False)]))
+    rx = np.unique(np.concatenate([[off[g], off[g + 1] - 1, rng.integers(off[g], off[g + 1])] for g in experts]))
+    ref_x = oracle.quantize_1x16(x[rx], segments=off, amax_vals=a_x, row_ids=rx)
+    _rows_equal(gx, ref_x, rx, "expert X")
+    g16 = np.unique(np.concatenate([[g * n // 16, (g + 1) * n // 16 - 1] for g in experts]))
+    rw = (g16[:, None] * 16 + np.arange(16)).reshape(-1)
+    ref_w = oracle.quantize_16x16(w[rw], segments=wseg, amax_vals=a_w, row_ids=rw)
+    _rows_equal(gw, ref_w, rw, "expert W")
+    sx_d = dict(zip(rx, oracle.dequantize(*ref_x, segments=off, row_ids=rx)))
+    sw_d = dict(zip(rw, oracle.dequantize(*ref_w, segments=wseg, row_ids=rw)))
+    dh = d.cpu().numpy()
+    checked = 0
+    for r in rx:
+        g = int(np.searchsorted(off, r, side="right") - 1)
+        cols = [c - g * n for c in rw if g * n <= c < (g + 1) * n]
+        for c in cols[:: max(1, len(cols) // 8)]:
+            a, b = sx_d[r], sw_d[g * n + c]
+            ref = float(np.dot(a, b))
+            bound = 1e-5 * float(np.dot(np.abs(a), np.abs(b)))
+            assert abs(float(dh[r, c]) - ref) <= bound, (r, c)
+            checked += 1
+    assert checked >= 16
