@@ -265,6 +265,9 @@ static int check_operand(const nvfp4_tensor* t, const char* name) {
     return fail(NVFP4_ERR_INVALID, "%s shape [%lld, %lld]: cols must be a non-negative multiple of 16", name,
                 (long long)t->rows, (long long)t->cols);
   if (!aligned(t->codes, 16)) return fail(NVFP4_ERR_INVALID, "%s codes must be 16-byte aligned", name);
+  // the GEMM kernels address an operand through 32-bit buffer offsets
+  if (t->rows * (t->cols / 2) > (int64_t)0x7FFFFFFF)
+    return fail(NVFP4_ERR_UNSUPPORTED, "%s codes exceed 2 GiB", name);
   return NVFP4_OK;
 }
 

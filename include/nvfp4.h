@@ -214,7 +214,9 @@ int nvfp4_rht_rows_quantize(const void* x, nvfp4_dtype dt, int64_t rows, int64_t
  * weight-gradient GEMMs of a linear layer (artiverse.ca "NVIDIA's 4-bit floating point
  * pushes AI training limits", paragraph on which parts run in 4-bit).
  *   A: rows = M, cols = K; B: rows = N, cols = K (same K, % 16 == 0); ldd >= N.
- * Errors: NVFP4_ERR_INVALID (null pointers, K mismatch, K % 16, ldd < N), NVFP4_ERR_HIP.
+ * Errors: NVFP4_ERR_INVALID (null pointers, K mismatch, K % 16, ldd < N),
+ * NVFP4_ERR_UNSUPPORTED (an operand's codes above 2 GiB: the kernels use 32-bit buffer
+ * offsets; the same limit holds for every GEMM entry point), NVFP4_ERR_HIP.
  */
 int nvfp4_gemm(const nvfp4_tensor* A, const nvfp4_tensor* B, float* D, int64_t ldd,
                void* hip_stream);

@@ -117,6 +117,14 @@ def test_gemm_validation(lib):
     assert gg(2, FAKE, ctypes.byref(a), ctypes.byref(b), 8, FAKE, 8, None, 0, None) == INVALID  # B rows
 
 
+def test_gemm_operand_size_limit(lib):
+    # 2^20 rows x 4096 codes bytes = 4 GiB: beyond the kernels' 32-bit buffer offsets
+    a, b = _tensor(1 << 20, 8192), _tensor(32, 8192)
+    assert lib.nvfp4_gemm(ctypes.byref(a), ctypes.byref(b), FAKE, 32, None) == UNSUPPORTED
+    assert lib.nvfp4_gemm(ctypes.byref(b), ctypes.byref(a), FAKE, 1 << 20, None) == UNSUPPORTED
+    assert lib.nvfp4_grouped_gemm_k(1, FAKE, ctypes.byref(a), ctypes.byref(b), FAKE, 32, None) == UNSUPPORTED
+
+
 def test_gemm_ex_validation(lib):
     a, b = _tensor(64, 128), _tensor(32, 128)
     g = lib.nvfp4_gemm_ex
