@@ -175,8 +175,11 @@ __global__ __launch_bounds__(kThreads) void k_rht(
   auto flush = [&](int64_t sgi, float mv) {            // uniform: one wave's run maximum
     const float wm = wave_max(mv);
     if (lane == 0) {
-      if (sgi - win_lo < kAccWin) atomicMax(reinterpret_cast<unsigned int*>(&sacc[sgi - win_lo]), __float_as_uint(wm));
-      else atomic_max_nonneg(partial + sgi, wm);
+      // (a malformed, decreasing table can put sgi below the window: the global path then)
+      if ((uint64_t)(sgi - win_lo) < (uint64_t)kAccWin)
+        atomicMax(reinterpret_cast<unsigned int*>(&sacc[sgi - win_lo]), __float_as_uint(wm));
+      else
+        atomic_max_nonneg(partial + sgi, wm);
     }
   };
   int64_t se_seg = -1;                                      // SEG encode: segment of se_cached
