@@ -906,8 +906,10 @@ void k_grouped_gemm_small(int64_t G, const int64_t* __restrict__ off, Operand A,
 // (16 bytes) and that block's E8M0 scale in byte 0 of its scale operand (checked on the
 // device). D = sum over k of a*b with FP32 accumulation; MXFP4 has no tensor scale.
 //
-// Tile 256 x 256, 4 waves of 128 x 128 (4 x 4 instructions per 64 elements), K steps of 128
-// (K % 128 == 0), DMA four steps deep. The matrix instruction consumes a step's operands
+// Tile 256 x 256, 8 waves (two per SIMD, so one wave's waits hide under the other's
+// instructions; 0-7% faster than 4 waves of 128 x 128 in interleaved timing, bit-identical)
+// of 64 x 128
+// (2 x 4 instructions per 64 elements), K steps of 128 (K % 128 == 0), DMA four steps deep. The matrix instruction consumes a step's operands
 // four times faster than the FP16 path, so what limits this kernel is the number of L2
 // requests the buffer-to-LDS DMA makes, not bytes: four lanes read a row's 64 bytes of a
 // step (one request per row and step instead of two), and the E8M0 bytes move 16 per row
@@ -924,10 +926,8 @@ constexpr int kScaleGroupBytes = (kBlockM + kBlockN) * 16;        // 16 bytes pe
 constexpr int kScaleBase = kStages * kCodeBytes;
 constexpr int kPadBase = kScaleBase + 2 * kScaleGroupBytes;       // target of idle scale moves
 constexpr int kLdsBytes = kPadBase + 1024;                        // 145 KB
-constexpr int kDmaScales = (kBlockM + kBlockN) / 64 / 4;          // 2 per wave
-constexpr int kDmaCodes = kFrags * 2 / 4;                         // 8 per wave
-constexpr int kDmaPerWave = kDmaScales + kDmaCodes;               // per step, idle or not
 }  // namespace mx
+constexpr int kMxThreads = 512;                                   // 8 waves, 2 per SIMD
 
 typedef int int32x8 __attribute__((ext_vector_type(8)));
 
@@ -937,7 +937,7 @@ __device__ __forceinline__ float16v mfma_mx(v4u32 a, v4u32 b, float16v c, uint32
       int32x8{(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0}, c, 4, 4, 0, (int)sa, 0, (int)sb);
 }
 
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(kMxThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_gemm_mx(Operand A, Operand B, int64_t K, float* __restrict__ D, int64_t ldd) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds_dyn[];
   uint8_t* lds = lds_dyn;
@@ -949,7 +949,6 @@ void k_gemm_mx(Operand A, Operand B, int64_t K, float* __restrict__ D, int64_t l
   const int64_t m0 = tm * kBlockM, n0 = tn * kBlockN;
   const int64_t m1 = m0 + kBlockM < A.rows ? m0 + kBlockM : A.rows;
   const int64_t n1 = n0 + kBlockN < B.rows ? n0 + kBlockN : B.rows;
-
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 31, h = lane >> 5;
@@ -957,41 +956,38 @@ void k_gemm_mx(Operand A, Operand B, int64_t K, float* __restrict__ D, int64_t l
   const uint32_t rs_codes = (uint32_t)(K >> 1), rs_scales = (uint32_t)(K >> 5);
   constexpr uint32_t kBeyond = 0x80000000u;
   const int steps = __builtin_amdgcn_readfirstlane((int)(K / kStepK));
-
   const __amdgpu_buffer_rsrc_t a_codes = make_rsrc(A.codes, A.rows * (K >> 1));
   const __amdgpu_buffer_rsrc_t b_codes = make_rsrc(B.codes, B.rows * (K >> 1));
   const __amdgpu_buffer_rsrc_t a_scales = make_rsrc(A.scales, A.rows * (K >> 5));
   const __amdgpu_buffer_rsrc_t b_scales = make_rsrc(B.scales, B.rows * (K >> 5));
-
-  // DMA for K step `step` (prefetched into code buffer `buf`), 10 operations per wave:
-  //  p = 0, 1: the E8M0 bytes of steps step .. step+3 when step % 4 == 0 (group step/4 into
-  //    scale buffer (step/4) % 2), rows 64 (wave + 4p) .. +63 of the 512 (A then B), lane l
-  //    one row's 16 bytes; other steps issue the operation idle (out of range, into a pad
-  //    area), so every step issues the same number of operations and the waits are constant.
-  //  p = 2..9: code operation i = p - 2: half q = i & 1 (rows 16q .. +15) of fragment
-  //    f = wave + 4 (i >> 1); lane l reads row 16q + l/4, chunk (l & 3) ^ ((l >> 4) & 3) of
-  //    the step's 64 bytes (the swizzle of the LDS layout: the chunk's row has (r >> 2) & 3 =
-  //    (l >> 4) & 3) into LDS f * 2 KB + q * 1 KB + l * 16.
+  // DMA for K step `step` (into code buffer `buf`), 5 operations per wave:
+  //  p = 0..3: half q = p & 1 (rows 16q .. +15) of fragment f = wave + 8 (p >> 1) (A for
+  //    p < 2, B after); lane l reads row 16q + l/4, chunk (l & 3) ^ ((l >> 4) & 3) of the
+  //    step's 64 bytes (the LDS swizzle: that row has (r >> 2) & 3 = (l >> 4) & 3) into LDS
+  //    f * 2 KB + q * 1 KB + l * 16.
+  //  p = 4: the E8M0 bytes of steps step .. step+3 when step % 4 == 0 (group step/4 into scale
+  //    buffer (step/4) % 2), rows 64 wave .. +63 of the 512 (A then B), lane l one row's 16
+  //    bytes; other steps issue it idle (out of range, into a pad area), so every step issues
+  //    the same number of operations and the waits are constant.
   // Steps past the last are issued out of range too (zeros, no memory traffic) into buffers
   // nobody reads again, so the loop has no branches.
+  constexpr int kOps = 5;
   const uint32_t lane_codes = (uint32_t)(lane >> 2) * rs_codes + 16u * (uint32_t)((lane & 3) ^ ((lane >> 4) & 3));
   const uint32_t lane_scales = (uint32_t)lane * rs_scales;
   auto issue_dma_part = [&](int step, int buf, int p) {
     const bool live = step < steps;
-    if (p < kDmaScales) {
-      const bool real = live && (step % kGroupSteps) == 0;         // uniform
-      const int blk = wave + 4 * p;                                 // 64-row block of the 512
-      const bool is_a = p == 0;
+    if (p == 4) {
+      const bool real = live && (step % kGroupSteps) == 0;
+      const int blk = wave;
+      const bool is_a = blk < 4;
       const uint32_t row0 = (uint32_t)((is_a ? m0 : n0) + 64 * (is_a ? blk : blk - 4));
       const uint32_t su = row0 * rs_scales + (uint32_t)(step * (kStepK / 32));
-      uint8_t* dst = real ? lds + kScaleBase + ((step / kGroupSteps) & 1) * kScaleGroupBytes + blk * 1024
-                          : lds + kPadBase;
+      uint8_t* dst = real ? lds + kScaleBase + ((step / kGroupSteps) & 1) * kScaleGroupBytes + blk * 1024 : lds + kPadBase;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a ? a_scales : b_scales, (lds_ptr_t)dst, 16,
                                                lane_scales + (real ? su : kBeyond), 0, 0, 0);
     } else {
-      const int i = p - kDmaScales;
-      const int q = i & 1, f = wave + 4 * (i >> 1);
-      const bool is_a = (i >> 1) < 2;                               // f < 8 for every wave
+      const int q = p & 1, f = wave + 8 * (p >> 1);
+      const bool is_a = (p >> 1) == 0;
       const uint32_t row = __builtin_amdgcn_readfirstlane(
           (uint32_t)((is_a ? m0 : n0) + 32 * (is_a ? f : f - kFragsA) + 16 * q));
       const uint32_t su = row * rs_codes + (uint32_t)(step * (kStepK / 2));
@@ -1000,108 +996,83 @@ void k_gemm_mx(Operand A, Operand B, int64_t K, float* __restrict__ D, int64_t l
                                                lane_codes + (live ? su : kBeyond), 0, 0, 0);
     }
   };
-  auto issue_dma = [&](int step, int buf) {
+  float16v acc[2][4];
 #pragma unroll
-    for (int p = 0; p < kDmaPerWave; ++p) issue_dma_part(step, buf, p);
-  };
-
-  float16v acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = float16v{};
-
-  // operands of one step: [fragment][64-element half] and the scale dwords. Lane (r, h) reads
-  // row r, chunk 2 s2 + h, stored at chunk (2 s2 + h) ^ ((r >> 2) & 3).
-  const int off0 = r * 64 + ((h ^ ((r >> 2) & 3)) << 4);
-  const int off1 = r * 64 + (((2 + h) ^ ((r >> 2) & 3)) << 4);
-  struct Ops { v4u32 a[4][2], b[4][2]; uint32_t sa[4], sb[4]; };
-  auto read_ops = [&](int step, int buf, Ops& o) {
-    const uint8_t* base = lds + buf * kCodeBytes;
+  // operands of the 64-element half s2 of a step: lane (r, h) reads row r, chunk 2 s2 + h,
+  // stored at chunk (2 s2 + h) ^ ((r >> 2) & 3); the E8M0 byte 2 s2 + h of the row's scale
+  // dword moved to byte 0 (the byte the instruction reads).
+  struct Ops { v4u32 a[2], b[4]; uint32_t sa[2], sb[4]; };
+  auto read_ops = [&](int step, int buf, int s2, Ops& o) {
+    const int off = r * 64 + (((2 * s2 + h) ^ ((r >> 2) & 3)) << 4);
+    const uint8_t* base = lds + buf * kCodeBytes + off;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      o.a[i][0] = *reinterpret_cast<const v4u32*>(base + (wm * 4 + i) * kFragBytes + off0);
-      o.a[i][1] = *reinterpret_cast<const v4u32*>(base + (wm * 4 + i) * kFragBytes + off1);
-    }
+    for (int i = 0; i < 2; ++i) o.a[i] = *reinterpret_cast<const v4u32*>(base + (wm * 2 + i) * kFragBytes);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      o.b[j][0] = *reinterpret_cast<const v4u32*>(base + (kFragsA + wn * 4 + j) * kFragBytes + off0);
-      o.b[j][1] = *reinterpret_cast<const v4u32*>(base + (kFragsA + wn * 4 + j) * kFragBytes + off1);
-    }
-    const uint8_t* sc = lds + kScaleBase + ((step / kGroupSteps) & 1) * kScaleGroupBytes +
-                        (step % kGroupSteps) * 4 + r * 16;
+    for (int j = 0; j < 4; ++j) o.b[j] = *reinterpret_cast<const v4u32*>(base + (kFragsA + wn * 4 + j) * kFragBytes);
+    const uint8_t* sc = lds + kScaleBase + ((step / kGroupSteps) & 1) * kScaleGroupBytes + (step % kGroupSteps) * 4 + r * 16;
+    const int sh = 8 * (2 * s2 + h);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) o.sa[i] = *reinterpret_cast<const uint32_t*>(sc + ((wm * 4 + i) * 32) * 16);
+    for (int i = 0; i < 2; ++i) o.sa[i] = *reinterpret_cast<const uint32_t*>(sc + ((wm * 2 + i) * 32) * 16) >> sh;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) o.sb[j] = *reinterpret_cast<const uint32_t*>(sc + (kBlockM + (wn * 4 + j) * 32) * 16);
+    for (int j = 0; j < 4; ++j) o.sb[j] = *reinterpret_cast<const uint32_t*>(sc + (kBlockM + (wn * 4 + j) * 32) * 16) >> sh;
   };
   auto barrier = [] {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   };
-  constexpr int kWaitFirst = big::waitcnt_imm((kStages - 1) * kDmaPerWave, 15);   // step 0 landed
-  constexpr int kWaitNext = big::waitcnt_imm((kStages - 2) * kDmaPerWave, 0);     // step s+1 landed
-
+  // With dma_step >= 0 that step's DMA into dma_buf is issued behind the first instructions,
+  // so the wave's pending LDS reads land before the compiler's ordering of LDS-bound DMA after
+  // them can stall issue.
+  auto mma = [&](const Ops& o, int dma_step, int dma_buf) {
 #pragma unroll
-  for (int p = 0; p < kStages; ++p) issue_dma(p, p);
-  __builtin_amdgcn_s_waitcnt(kWaitFirst);
-  barrier();
-
-  // With dma_step >= 0 that step's DMA into dma_buf is spread over the row groups, behind
-  // the instructions, so the wave's pending LDS reads land before the compiler's ordering of
-  // LDS-bound DMA after them can stall issue.
-  auto mma_half = [&](const Ops& o, int s2, int dma_step, int dma_buf) {
+    for (int i = 0; i < 2; ++i) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t sa = o.sa[i] >> (8 * (2 * s2 + h));
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[i][j] = mfma_mx(o.a[i][s2], o.b[j][s2], acc[i][j], sa, o.sb[j] >> (8 * (2 * s2 + h)));
-      if (dma_step >= 0) {
-#pragma unroll
-        for (int p = i * kDmaPerWave / 4; p < (i + 1) * kDmaPerWave / 4; ++p) issue_dma_part(dma_step, dma_buf, p);
+      for (int j = 0; j < 4; ++j) {
+        acc[i][j] = mfma_mx(o.a[i], o.b[j], acc[i][j], o.sa[i], o.sb[j]);
+        if (dma_step >= 0 && (i * 4 + j) < kOps) issue_dma_part(dma_step, dma_buf, i * 4 + j);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-
-  // One step: half 0 of `cur`; the barrier (every wave has read step s's buffer, step s+1
-  // and its scale group have landed); the reads of step s+1 into `nxt`, then half 1 of `cur`
-  // with the DMA of step s+4 into step s's buffer spread over it.
+#pragma unroll
+  for (int p = 0; p < kStages; ++p)
+#pragma unroll
+    for (int q = 0; q < kOps; ++q) issue_dma_part(p, p, q);
+  __builtin_amdgcn_s_waitcnt(big::waitcnt_imm((kStages - 1) * kOps, 15));
+  barrier();
+  // One step: half 1 is read while half 0's instructions run; then the barrier (every wave
+  // has read step s's buffer, step s+1 and its scale group have landed); then half 0 of step
+  // s+1 is read while half 1 runs with the DMA of step s+4 into step s's buffer.
   int b_cur = 0;
   Ops cur, nxt;
-  read_ops(0, 0, cur);
-  auto step = [&](int s, Ops& c, Ops& n) {
+  read_ops(0, 0, 0, cur);
+  for (int s = 0; s < steps; ++s) {
     const int b_next = b_cur == kStages - 1 ? 0 : b_cur + 1;
-    mma_half(c, 0, -1, 0);
-    __builtin_amdgcn_s_waitcnt(kWaitNext);
+    read_ops(s, b_cur, 1, nxt);
+    mma(cur, -1, 0);
+    __builtin_amdgcn_s_waitcnt(big::waitcnt_imm((kStages - 2) * kOps, 0));
     barrier();
-    read_ops(s + 1, b_next, n);
-    mma_half(c, 1, s + kStages, b_cur);
+    read_ops(s + 1, b_next, 0, cur);
+    mma(nxt, s + kStages, b_cur);
     b_cur = b_next;
-  };
-  int s = 0;
-  for (; s + 1 < steps; s += 2) {
-    step(s, cur, nxt);
-    step(s + 1, nxt, cur);
   }
-  if (s < steps) step(s, cur, nxt);
-  __builtin_amdgcn_s_waitcnt(big::waitcnt_imm(0, 15));             // no DMA may outlive the tile
-
+  __builtin_amdgcn_s_waitcnt(big::waitcnt_imm(0, 15));
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int64_t col = n0 + wn * 128 + 32 * j + r;
       if (col >= n1) continue;
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
-        const int64_t row = m0 + wm * 128 + 32 * i + 8 * (q >> 2) + 4 * h + (q & 3);
+        const int64_t row = m0 + wm * 64 + 32 * i + 8 * (q >> 2) + 4 * h + (q & 3);
         if (row < m1) __builtin_nontemporal_store(acc[i][j][q], &D[row * ldd + col]);
       }
     }
-  }
 }
 
 bool use_big(int64_t K) { return K > 0 && (K % 64) == 0; }
@@ -1193,7 +1164,7 @@ hipError_t launch_gemm_mx(const uint8_t* a_codes, const uint8_t* a_scales, const
   if (attr != hipSuccess) return attr;
   const Operand A{a_codes, a_scales, M}, B{b_codes, b_scales, N};
   const int64_t tiles = ((M + mx::kBlockM - 1) / mx::kBlockM) * ((N + mx::kBlockN - 1) / mx::kBlockN);
-  hipLaunchKernelGGL(k_gemm_mx, dim3((unsigned)tiles), dim3(kThreads), mx::kLdsBytes, stream, A, B, K, D, ldd);
+  hipLaunchKernelGGL(k_gemm_mx, dim3((unsigned)tiles), dim3(kMxThreads), mx::kLdsBytes, stream, A, B, K, D, ldd);
   return hipGetLastError();
 }
 
