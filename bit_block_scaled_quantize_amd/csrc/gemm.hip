@@ -906,14 +906,15 @@ void k_grouped_gemm_small(int64_t G, const int64_t* __restrict__ off, Operand A,
 // (16 bytes) and that block's E8M0 scale in byte 0 of its scale operand (checked on the
 // device). D = sum over k of a*b with FP32 accumulation; MXFP4 has no tensor scale.
 //
-// Tile 256 x 256, 8 waves (two per SIMD, so one wave's waits hide under the other's
-// instructions; 0-7% faster than 4 waves of 128 x 128 in interleaved timing, bit-identical)
-// of 64 x 128
-// (2 x 4 instructions per 64 elements), K steps of 128 (K % 128 == 0), DMA four steps deep. The matrix instruction consumes a step's operands
-// four times faster than the FP16 path, so what limits this kernel is the number of L2
-// requests the buffer-to-LDS DMA makes, not bytes: four lanes read a row's 64 bytes of a
-// step (one request per row and step instead of two), and the E8M0 bytes move 16 per row
-// (four steps) per request into a two-deep ring. In LDS a fragment is 32 rows x 64 bytes,
+// Tile 256 x 256, 8 waves of 64 x 128 (2 x 4 instructions per 64 elements; two waves per
+// SIMD, so one wave's waits hide under the other's instructions: 0-7% faster than 4 waves of
+// 128 x 128 in interleaved timing, bit-identical), K steps of 128 (K % 128 == 0), DMA four
+// steps deep. The matrix instruction consumes a step's operands four times faster than the
+// FP16 path, so what limits this kernel is the number of L2 requests the buffer-to-LDS DMA
+// makes, not bytes: four lanes read a row's 64 bytes of a step (one request per row and step
+// instead of two), and the E8M0 bytes move 16 per row (four steps) per request into a
+// two-deep ring. (Stages of 256 elements, whose rows are whole 128-byte lines, fit only two
+// deep in LDS and were slower: the prefetch distance matters more than the request count.) In LDS a fragment is 32 rows x 64 bytes,
 // row-major, with the 16-byte chunk c of row r stored at chunk c ^ ((r >> 2) & 3), so the
 // instruction's 16-byte reads (row r, chunk 2s + h) fall in distinct banks.
 namespace mx {
