@@ -148,9 +148,42 @@ class MXFP4Tensor:
 def _input(x: torch.Tensor):
     if x.dtype not in _DTYPE:
         raise NVFP4Error(f"unsupported input dtype {x.dtype}")
-    if x.dim() != 2 or x.stride(1) != 1:
-        raise NVFP4Error("input must be a 2-D tensor with unit column stride")
+    if x.dim() != 2 or x.stride(1) != 1 or x.device.type != "cuda":
+        raise NVFP4Error("input must be a 2-D GPU tensor with unit column stride")
     return _DTYPE[x.dtype], x.shape[0], x.shape[1], x.stride(0)
+
+
+def _check_q(q, nseg: int = 1, what: str = "tensor"):
+    """The C ABI sees only pointers: make sure the torch buffers behind an NVFP4/MXFP4 tensor
+    are as large as its rows and cols say (and contiguous), so no kernel writes past them."""
+    mx = isinstance(q, MXFP4Tensor)
+    need = ((q.codes, q.rows * (q.cols // 2)), (q.scales, q.rows * (q.cols // (32 if mx else 16))))
+    if not mx:
+        need += ((q.global_scale, nseg),)
+    for t, n in need:
+        if t.numel() < n or not t.is_contiguous() or t.device.type != "cuda":
+            raise NVFP4Error(f"{what}: buffer of {t.numel()} elements (contiguous, on the GPU) needed {n}")
+
+
+def _check_out(out: torch.Tensor, rows: int, cols: int, dtype, what: str = "out"):
+    """A 2-D output with at least rows x cols elements, unit column stride, the given dtype."""
+    if out.dtype != dtype or out.dim() != 2 or out.stride(1) != 1 or out.device.type != "cuda":
+        raise NVFP4Error(f"{what} must be a 2-D {dtype} GPU tensor with unit column stride")
+    if out.shape[0] < rows or out.shape[1] < cols:
+        raise NVFP4Error(f"{what} shape {tuple(out.shape)} smaller than ({rows}, {cols})")
+
+
+def _check_table(t, what: str):
+    """Segment / offset tables are int64 GPU tensors with at least two entries."""
+    if t is not None and (t.dtype != torch.int64 or t.device.type != "cuda" or t.numel() < 2
+                          or not t.is_contiguous()):
+        raise NVFP4Error(f"{what} must be a contiguous int64 GPU tensor of at least 2 entries")
+
+
+def _check_vec(t, n: int, what: str):
+    if t is not None and (t.dtype != torch.float32 or t.numel() < n or t.device.type != "cuda"
+                          or not t.is_contiguous()):
+        raise NVFP4Error(f"{what} must be a contiguous float32 GPU tensor of at least {n} elements")
 
 
 def workspace_size(op: int, rows: int, cols: int, nseg: int = 1) -> int:
@@ -182,6 +215,11 @@ def quantize(x: torch.Tensor, block: str = "1x16", rounding: str = "rn", seed: i
             workspace, ws_n = _workspace(OP_QUANTIZE, rows, cols, nseg, x.device)
         else:
             ws_n = workspace.numel()
+    _check_table(segments, "segments")
+    _check_vec(amax, nseg, "amax")
+    _check_q(out, nseg, "out")
+    if emit_transposed:
+        _check_q(out_t, nseg if segments is not None else 1, "out_t")
     oc = out.c()
     otc = out_t.c() if emit_transposed else None
     st = lib.nvfp4_quantize(_ptr(x), dt, rows, cols, ld, _BLOCK[block], _ROUND[rounding],
@@ -208,6 +246,8 @@ def rht_rows_quantize(x: torch.Tensor, sign_mask: int, rounding: str = "rn", see
             workspace, ws_n = _workspace(OP_QUANTIZE, rows, cols, 1, x.device)
         else:
             ws_n = workspace.numel()
+    _check_vec(amax, 1, "amax")
+    _check_q(out, 1, "out")
     oc = out.c()
     _check(lib.nvfp4_rht_rows_quantize(_ptr(x), dt, rows, cols, ld, sign_mask & 0xFFFF, _ROUND[rounding],
                                        seed & (2 ** 64 - 1), offset & (2 ** 64 - 1), _ptr(amax),
@@ -223,6 +263,7 @@ def mx_quantize(x: torch.Tensor, rounding: str = "rn", seed: int = 0, offset: in
     dt, rows, cols, ld = _input(x)
     if out is None:
         out = MXFP4Tensor.empty(rows, cols, x.device)
+    _check_q(out, what="out")
     oc = out.c()
     _check(lib.mxfp4_quantize(_ptr(x), dt, rows, cols, ld, _ROUND[rounding], seed & (2 ** 64 - 1),
                               offset & (2 ** 64 - 1), ctypes.byref(oc), _stream(stream)))
@@ -234,6 +275,9 @@ def mx_gemm(a: MXFP4Tensor, b: MXFP4Tensor, out: torch.Tensor | None = None, str
     lib = _load()
     if out is None:
         out = torch.empty((a.rows, b.rows), dtype=torch.float32, device=a.codes.device)
+    _check_q(a, what="A")
+    _check_q(b, what="B")
+    _check_out(out, a.rows, b.rows, torch.float32)
     ac, bc = a.c(), b.c()
     _check(lib.mxfp4_gemm(ctypes.byref(ac), ctypes.byref(bc), _ptr(out), out.stride(0), _stream(stream)))
     return out
@@ -256,6 +300,9 @@ def rht_quantize(x: torch.Tensor, sign_mask: int, rounding: str = "rn", seed: in
             workspace, ws_n = _workspace(OP_RHT_QUANTIZE, tokens, cols, nseg, x.device)
         else:
             ws_n = workspace.numel()
+    _check_table(segments, "segments")
+    _check_vec(amax, nseg, "amax")
+    _check_q(out, nseg, "out")
     oc = out.c()
     st = lib.nvfp4_rht_quantize(_ptr(x), dt, tokens, cols, ld, sign_mask & 0xFFFF,
                                 _ROUND[rounding], seed & (2 ** 64 - 1), offset & (2 ** 64 - 1),
@@ -270,6 +317,9 @@ def gemm(a: NVFP4Tensor, b: NVFP4Tensor, out: torch.Tensor | None = None, stream
     lib = _load()
     if out is None:
         out = torch.empty((a.rows, b.rows), dtype=torch.float32, device=a.codes.device)
+    _check_q(a, what="A")
+    _check_q(b, what="B")
+    _check_out(out, a.rows, b.rows, torch.float32)
     ac, bc = a.c(), b.c()
     _check(lib.nvfp4_gemm(ctypes.byref(ac), ctypes.byref(bc), _ptr(out), out.stride(0),
                           _stream(stream)))
@@ -295,8 +345,11 @@ def gemm_ex(a: NVFP4Tensor, b: NVFP4Tensor, out: torch.Tensor | None = None,
             out = torch.empty((a.rows, b.rows), dtype=out_dtype, device=a.codes.device)
         elif out.dtype != out_dtype:
             raise NVFP4Error("out dtype does not match out_dtype")
-    if out.dim() != 2 or out.stride(1) != 1:
-        raise NVFP4Error("out must be 2-D with unit column stride")
+    _check_q(a, what="A")
+    _check_q(b, what="B")
+    _check_out(out, a.rows, b.rows, out.dtype)
+    if amax_out is not None and (amax_out.numel() < 1 or amax_out.dtype != torch.float32):
+        raise NVFP4Error("amax_out must be a float32 tensor of at least one element")
     if workspace is None:
         workspace, ws_n = _workspace(OP_GEMM_EX, a.rows, b.rows, 1, a.codes.device)
     else:
@@ -315,6 +368,11 @@ def grouped_gemm(m_offsets: torch.Tensor, a: NVFP4Tensor, b: NVFP4Tensor, n: int
     G = m_offsets.numel() - 1
     if out is None:
         out = torch.empty((a.rows, n), dtype=torch.float32, device=a.codes.device)
+    _check_q(a, G, "A")
+    _check_q(b, G, "B")
+    _check_out(out, a.rows, n, torch.float32)
+    if m_offsets.dtype != torch.int64 or m_offsets.device.type != "cuda":
+        raise NVFP4Error("m_offsets must be an int64 GPU tensor")
     ac, bc = a.c(), b.c()
     _check(lib.nvfp4_grouped_gemm(G, _ptr(m_offsets), ctypes.byref(ac), ctypes.byref(bc), n,
                                   _ptr(out), out.stride(0), None, 0, _stream(stream)))
@@ -329,6 +387,11 @@ def grouped_gemm_k(k_offsets: torch.Tensor, a: NVFP4Tensor, b: NVFP4Tensor,
     G = k_offsets.numel() - 1
     if out is None:
         out = torch.empty((G * a.rows, b.rows), dtype=torch.float32, device=a.codes.device)
+    _check_q(a, G, "A")
+    _check_q(b, G, "B")
+    _check_out(out, G * a.rows, b.rows, torch.float32)
+    if k_offsets.dtype != torch.int64 or k_offsets.device.type != "cuda":
+        raise NVFP4Error("k_offsets must be an int64 GPU tensor")
     ac, bc = a.c(), b.c()
     _check(lib.nvfp4_grouped_gemm_k(G, _ptr(k_offsets), ctypes.byref(ac), ctypes.byref(bc),
                                     _ptr(out), out.stride(0), _stream(stream)))
@@ -349,6 +412,8 @@ def amax(x: torch.Tensor, segments: torch.Tensor | None = None, rht: bool | int 
         workspace, ws_n = _workspace(OP_RHT_QUANTIZE if int(rht) == 1 else OP_QUANTIZE, rows, cols, nseg, x.device)
     else:
         ws_n = workspace.numel()
+    _check_table(segments, "segments")
+    _check_vec(out, nseg, "out")
     _check(lib.nvfp4_amax(_ptr(x), dt, rows, cols, ld, _ptr(segments), nseg, int(rht),
                           sign_mask & 0xFFFF, _ptr(out), _ptr(workspace), ws_n, _stream(stream)))
     return out
@@ -365,6 +430,7 @@ def amax_pair(x: torch.Tensor, sign_mask: int, out: torch.Tensor | None = None,
         workspace, ws_n = _workspace(OP_AMAX_PAIR, tokens, cols, 1, x.device)
     else:
         ws_n = workspace.numel()
+    _check_vec(out, 2, "out")
     _check(lib.nvfp4_amax_pair(_ptr(x), dt, tokens, cols, ld, sign_mask & 0xFFFF, _ptr(out),
                                _ptr(workspace), ws_n, _stream(stream)))
     return out
@@ -374,6 +440,8 @@ def dequantize(q: NVFP4Tensor, segments: torch.Tensor | None = None, stream=None
     """nvfp4_dequantize (test helper): FP32 [rows, cols]."""
     lib = _load()
     nseg = 1 if segments is None else segments.numel() - 1
+    _check_table(segments, "segments")
+    _check_q(q, nseg, "q")
     y = torch.empty((q.rows, q.cols), dtype=torch.float32, device=q.codes.device)
     qc = q.c()
     _check(lib.nvfp4_dequantize(ctypes.byref(qc), _ptr(segments), nseg, _ptr(y), _stream(stream)))

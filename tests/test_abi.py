@@ -7,6 +7,7 @@ import os
 import re
 
 import pytest
+import torch
 
 import bit_block_scaled_quantize_amd as nv
 
@@ -199,3 +200,20 @@ def test_mx_quantize_validation(lib):
     assert f(FAKE, 0, 32, 64, 64, 0, 0, 0, None, None) == INVALID               # out
     assert f(FAKE, 0, 16, 64, 64, 0, 0, 0, o, None) == INVALID                  # shape
     assert f(FAKE + 2, 0, 32, 64, 64, 0, 0, 0, o, None) == UNSUPPORTED          # alignment
+
+
+def test_binding_checks_buffers_before_calling(lib):
+    # the C ABI sees only pointers: the binding refuses host tensors, short buffers and
+    # outputs smaller than the result before anything reaches the library
+    with pytest.raises(nv.NVFP4Error):
+        nv.quantize(torch.zeros((16, 32), dtype=torch.bfloat16))            # host input
+    q = nv.NVFP4Tensor(torch.zeros(8, dtype=torch.uint8), torch.zeros(2, dtype=torch.uint8),
+                       torch.ones(1), 16, 32)
+    with pytest.raises(nv.NVFP4Error):
+        nv._check_q(q, 1, "q")                                              # 8 < 16*16 codes
+    with pytest.raises(nv.NVFP4Error):
+        nv._check_out(torch.zeros((4, 8)), 4, 8, torch.float32)             # host output
+    with pytest.raises(nv.NVFP4Error):
+        nv._check_table(torch.zeros(3, dtype=torch.int32), "segments")      # not int64 / GPU
+    with pytest.raises(nv.NVFP4Error):
+        nv._check_vec(torch.zeros(1), 2, "amax")
