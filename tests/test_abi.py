@@ -217,3 +217,19 @@ def test_binding_checks_buffers_before_calling(lib):
         nv._check_table(torch.zeros(3, dtype=torch.int32), "segments")      # not int64 / GPU
     with pytest.raises(nv.NVFP4Error):
         nv._check_vec(torch.zeros(1), 2, "amax")
+
+
+def test_rht_rows_quantize_validation(lib):
+    f = lib.nvfp4_rht_rows_quantize
+    out = _tensor(32, 64)
+    o = ctypes.byref(out)
+    assert f(None, 0, 32, 64, 64, 0x6E04, 0, 0, 0, None, o, FAKE, 4096, None) == INVALID       # x
+    assert f(FAKE, 0, 32, 40, 40, 0x6E04, 0, 0, 0, None, ctypes.byref(_tensor(32, 40)), FAKE, 4096,
+             None) in (INVALID, UNSUPPORTED)                                                    # cols % 16
+    assert f(FAKE, 0, 32, 64, 64, 0x6E04, 7, 0, 0, None, o, FAKE, 4096, None) == INVALID         # rounding
+    assert f(FAKE, 0, 16, 64, 64, 0x6E04, 0, 0, 0, None, o, FAKE, 4096, None) == INVALID         # out shape
+    assert f(FAKE, 0, 32, 64, 64, 0x6E04, 0, 0, 0, None, o, None, 0, None) == WORKSPACE         # no amax, no ws
+    # nvfp4_amax with the rowwise selector takes no segments
+    a = lib.nvfp4_amax
+    assert a(FAKE, 0, 32, 64, 64, FAKE, 2, 2, 0x6E04, FAKE, None, 0, None) == UNSUPPORTED
+    assert a(FAKE, 0, 32, 64, 64, None, 1, 3, 0x6E04, FAKE, FAKE, 4096, None) == INVALID         # selector
