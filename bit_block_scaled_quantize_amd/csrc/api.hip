@@ -33,13 +33,15 @@ constexpr size_t kWsAlign = 256;
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 // Checks an output tensor descriptor for a [rows, cols] quantization.
+// An empty output (no rows or no columns) is never written, so its buffers may be NULL.
 int check_out(const nvfp4_tensor* t, int64_t rows, int64_t cols, const char* name) {
   if (!t) return fail(NVFP4_ERR_INVALID, "%s is NULL", name);
-  if (!t->codes || !t->scales || !t->global_scale)
-    return fail(NVFP4_ERR_INVALID, "%s has a NULL codes/scales/global_scale pointer", name);
   if (t->rows != rows || t->cols != cols)
     return fail(NVFP4_ERR_INVALID, "%s shape [%lld, %lld] does not match [%lld, %lld]", name,
                 (long long)t->rows, (long long)t->cols, (long long)rows, (long long)cols);
+  if (rows == 0 || cols == 0) return NVFP4_OK;
+  if (!t->codes || !t->scales || !t->global_scale)
+    return fail(NVFP4_ERR_INVALID, "%s has a NULL codes/scales/global_scale pointer", name);
   if (!aligned(t->codes, 16))
     return fail(NVFP4_ERR_INVALID, "%s codes must be 16-byte aligned", name);
   return NVFP4_OK;
@@ -49,10 +51,11 @@ int check_out(const nvfp4_tensor* t, int64_t rows, int64_t cols, const char* nam
 // reads column pairs across rows and only needs the pair to be aligned.
 int check_input(const void* x, nvfp4_dtype dt, int64_t rows, int64_t cols, int64_t ld,
                 bool rows_vec = true) {
-  if (!x) return fail(NVFP4_ERR_INVALID, "x is NULL");
   if (dt != NVFP4_IN_BF16 && dt != NVFP4_IN_FP32) return fail(NVFP4_ERR_INVALID, "bad dtype %d", (int)dt);
   if (rows < 0 || cols < 1) return fail(NVFP4_ERR_INVALID, "bad shape [%lld, %lld]", (long long)rows, (long long)cols);
   if (ld < cols) return fail(NVFP4_ERR_INVALID, "ld (%lld) < cols (%lld)", (long long)ld, (long long)cols);
+  if (rows == 0) return NVFP4_OK;                 // an empty input is never read (x may be NULL)
+  if (!x) return fail(NVFP4_ERR_INVALID, "x is NULL");
   const size_t esz = dt == NVFP4_IN_BF16 ? 2 : 4;
   if (!rows_vec) {
     if (!aligned(x, 2 * esz)) return fail(NVFP4_ERR_UNSUPPORTED, "x must be %zu-byte aligned", 2 * esz);
@@ -97,6 +100,7 @@ int nvfp4_amax(const void* x, nvfp4_dtype dt, int64_t rows, int64_t cols, int64_
   if (st) return st;
   if (!amax_out) return fail(NVFP4_ERR_INVALID, "amax_out is NULL");
   if (nseg < 1 || (!segments && nseg != 1)) return fail(NVFP4_ERR_INVALID, "bad segment table (nseg=%lld)", (long long)nseg);
+  if (rows == 0) return hip_status(nvfp4::launch_fill(amax_out, nseg, 0.0f, (hipStream_t)hip_stream), "amax of nothing");
   if (rht == 2) {                                   // rowwise rotation, unsegmented
     if (segments) return fail(NVFP4_ERR_UNSUPPORTED, "the rowwise rotation takes no segments");
     if (cols % 16) return fail(NVFP4_ERR_INVALID, "cols (%lld) must be a multiple of 16", (long long)cols);
@@ -146,6 +150,7 @@ int nvfp4_rht_rows_quantize(const void* x, nvfp4_dtype dt, int64_t rows, int64_t
   if (cols % 16) return fail(NVFP4_ERR_INVALID, "cols (%lld) must be a multiple of 16", (long long)cols);
   if (rnd != NVFP4_ROUND_RN && rnd != NVFP4_ROUND_SR) return fail(NVFP4_ERR_INVALID, "bad rounding %d", (int)rnd);
   if ((st = check_out(out, rows, cols, "out"))) return st;
+  if (rows == 0) return NVFP4_OK;
   hipStream_t s = (hipStream_t)hip_stream;
   const bool f32 = dt == NVFP4_IN_FP32;
   const float* amax = amax_in;
@@ -171,6 +176,7 @@ int nvfp4_amax_pair(const void* x, nvfp4_dtype dt, int64_t tokens, int64_t cols,
   if (st) return st;
   if (!amax_out) return fail(NVFP4_ERR_INVALID, "amax_out is NULL");
   if (tokens % 16) return fail(NVFP4_ERR_INVALID, "tokens (%lld) must be a multiple of 16", (long long)tokens);
+  if (tokens == 0) return hip_status(nvfp4::launch_fill(amax_out, 2, 0.0f, (hipStream_t)hip_stream), "amax of nothing");
   const size_t need = nvfp4_workspace_size(NVFP4_OP_AMAX_PAIR, tokens, cols, 1);
   if (!workspace || ws_bytes < need || !aligned(workspace, kWsAlign))
     return fail(NVFP4_ERR_WORKSPACE, "workspace of %zu bytes (256-byte aligned) required, got %zu", need, ws_bytes);
@@ -203,6 +209,7 @@ int nvfp4_quantize(const void* x, nvfp4_dtype dt, int64_t rows, int64_t cols, in
                 (long long)nseg, (long long)rows);
   if ((st = check_out(out, rows, cols, "out"))) return st;
   if (out_t && (st = check_out(out_t, segments ? nseg * cols : cols, rows / nseg, "out_t"))) return st;
+  if (rows == 0) return NVFP4_OK;
   const float* amax = amax_in;
   if (!amax) {
     const size_t need = nvfp4_workspace_size(NVFP4_OP_QUANTIZE, rows, cols, nseg);
@@ -237,6 +244,7 @@ int nvfp4_rht_quantize(const void* x, nvfp4_dtype dt, int64_t tokens, int64_t co
   if (tokens % 16) return fail(NVFP4_ERR_INVALID, "tokens (%lld) must be a multiple of 16", (long long)tokens);
   if (nseg < 1 || (!segments && nseg != 1)) return fail(NVFP4_ERR_INVALID, "bad segment table (nseg=%lld)", (long long)nseg);
   if ((st = check_out(out, cols, tokens, "out"))) return st;
+  if (tokens == 0) return NVFP4_OK;
   const float* amax = amax_in;
   if (!amax) {
     const size_t need = nvfp4_workspace_size(NVFP4_OP_RHT_QUANTIZE, tokens, cols, nseg);
@@ -257,13 +265,16 @@ int nvfp4_rht_quantize(const void* x, nvfp4_dtype dt, int64_t tokens, int64_t co
                                              seed, offset, segments, nseg, amax, parts, q, s), "rht encode");
 }
 
+// An operand without rows is never read (no output row or column depends on it), so its
+// buffers may be NULL.
 static int check_operand(const nvfp4_tensor* t, const char* name) {
   if (!t) return fail(NVFP4_ERR_INVALID, "%s is NULL", name);
-  if (!t->codes || !t->scales || !t->global_scale)
-    return fail(NVFP4_ERR_INVALID, "%s has a NULL codes/scales/global_scale pointer", name);
   if (t->rows < 0 || t->cols < 0 || t->cols % 16)
     return fail(NVFP4_ERR_INVALID, "%s shape [%lld, %lld]: cols must be a non-negative multiple of 16", name,
                 (long long)t->rows, (long long)t->cols);
+  if (t->rows == 0) return NVFP4_OK;
+  if (!t->codes || !t->scales || !t->global_scale)
+    return fail(NVFP4_ERR_INVALID, "%s has a NULL codes/scales/global_scale pointer", name);
   if (!aligned(t->codes, 16)) return fail(NVFP4_ERR_INVALID, "%s codes must be 16-byte aligned", name);
   // the GEMM kernels address an operand through 32-bit buffer offsets
   if (t->rows * (t->cols / 2) > (int64_t)0x7FFFFFFF)
@@ -275,7 +286,7 @@ int nvfp4_gemm(const nvfp4_tensor* A, const nvfp4_tensor* B, float* D, int64_t l
   int st;
   if ((st = check_operand(A, "A")) || (st = check_operand(B, "B"))) return st;
   if (A->cols != B->cols) return fail(NVFP4_ERR_INVALID, "K mismatch: A has %lld, B has %lld", (long long)A->cols, (long long)B->cols);
-  if (!D) return fail(NVFP4_ERR_INVALID, "D is NULL");
+  if (!D && A->rows > 0 && B->rows > 0) return fail(NVFP4_ERR_INVALID, "D is NULL");   // an empty D is never written
   if (ldd < B->rows) return fail(NVFP4_ERR_INVALID, "ldd (%lld) < N (%lld)", (long long)ldd, (long long)B->rows);
   const nvfp4::GemmOperand a{A->codes, A->scales, A->global_scale};
   const nvfp4::GemmOperand b{B->codes, B->scales, B->global_scale};
@@ -289,10 +300,12 @@ int mxfp4_quantize(const void* x, nvfp4_dtype dt, int64_t rows, int64_t cols, in
   if ((st = check_input(x, dt, rows, cols, ld))) return st;
   if (cols % 32) return fail(NVFP4_ERR_INVALID, "cols (%lld) must be a multiple of 32", (long long)cols);
   if (rnd != NVFP4_ROUND_RN && rnd != NVFP4_ROUND_SR) return fail(NVFP4_ERR_INVALID, "bad rounding %d", (int)rnd);
-  if (!out || !out->codes || !out->scales) return fail(NVFP4_ERR_INVALID, "out or its buffers are NULL");
+  if (!out) return fail(NVFP4_ERR_INVALID, "out is NULL");
   if (out->rows != rows || out->cols != cols)
     return fail(NVFP4_ERR_INVALID, "out shape [%lld, %lld] does not match [%lld, %lld]", (long long)out->rows,
                 (long long)out->cols, (long long)rows, (long long)cols);
+  if (rows == 0) return NVFP4_OK;
+  if (!out->codes || !out->scales) return fail(NVFP4_ERR_INVALID, "out buffers are NULL");
   if (!aligned(out->codes, 8)) return fail(NVFP4_ERR_INVALID, "out codes must be 8-byte aligned");
   return hip_status(nvfp4::launch_encode_mx(x, dt == NVFP4_IN_FP32, rows, cols, ld, rnd == NVFP4_ROUND_SR, seed,
                                             offset, out->codes, out->scales, (hipStream_t)hip_stream),
@@ -301,10 +314,11 @@ int mxfp4_quantize(const void* x, nvfp4_dtype dt, int64_t rows, int64_t cols, in
 
 static int check_mx_operand(const mxfp4_tensor* t, const char* name) {
   if (!t) return fail(NVFP4_ERR_INVALID, "%s is NULL", name);
-  if (!t->codes || !t->scales) return fail(NVFP4_ERR_INVALID, "%s has a NULL codes/scales pointer", name);
   if (t->rows < 0 || t->cols < 0 || t->cols % 32)
     return fail(NVFP4_ERR_INVALID, "%s shape [%lld, %lld]: cols must be a non-negative multiple of 32", name,
                 (long long)t->rows, (long long)t->cols);
+  if (t->rows == 0) return NVFP4_OK;
+  if (!t->codes || !t->scales) return fail(NVFP4_ERR_INVALID, "%s has a NULL codes/scales pointer", name);
   if (!aligned(t->codes, 16)) return fail(NVFP4_ERR_INVALID, "%s codes must be 16-byte aligned", name);
   if (t->rows * (t->cols / 2) > (int64_t)0x7FFFFFFF)
     return fail(NVFP4_ERR_UNSUPPORTED, "%s codes exceed 2 GiB", name);
@@ -315,7 +329,7 @@ int mxfp4_gemm(const mxfp4_tensor* A, const mxfp4_tensor* B, float* D, int64_t l
   int st;
   if ((st = check_mx_operand(A, "A")) || (st = check_mx_operand(B, "B"))) return st;
   if (A->cols != B->cols) return fail(NVFP4_ERR_INVALID, "K mismatch: A has %lld, B has %lld", (long long)A->cols, (long long)B->cols);
-  if (!D) return fail(NVFP4_ERR_INVALID, "D is NULL");
+  if (!D && A->rows > 0 && B->rows > 0) return fail(NVFP4_ERR_INVALID, "D is NULL");   // an empty D is never written
   if (ldd < B->rows) return fail(NVFP4_ERR_INVALID, "ldd (%lld) < N (%lld)", (long long)ldd, (long long)B->rows);
   if (A->cols % 128) return fail(NVFP4_ERR_UNSUPPORTED, "K (%lld) must be a multiple of 128", (long long)A->cols);
   return hip_status(nvfp4::launch_gemm_mx(A->codes, A->scales, B->codes, B->scales, A->rows, B->rows, A->cols, D, ldd,
@@ -327,7 +341,7 @@ int nvfp4_gemm_ex(const nvfp4_tensor* A, const nvfp4_tensor* B, void* D, int64_t
   int st;
   if ((st = check_operand(A, "A")) || (st = check_operand(B, "B"))) return st;
   if (A->cols != B->cols) return fail(NVFP4_ERR_INVALID, "K mismatch: A has %lld, B has %lld", (long long)A->cols, (long long)B->cols);
-  if (!D) return fail(NVFP4_ERR_INVALID, "D is NULL");
+  if (!D && A->rows > 0 && B->rows > 0) return fail(NVFP4_ERR_INVALID, "D is NULL");   // an empty D is never written
   if (out_kind != NVFP4_OUT_FP32 && out_kind != NVFP4_OUT_FP32_ACCUMULATE && out_kind != NVFP4_OUT_BF16)
     return fail(NVFP4_ERR_INVALID, "bad output kind %d", (int)out_kind);
   if (ldd < B->rows) return fail(NVFP4_ERR_INVALID, "ldd (%lld) < N (%lld)", (long long)ldd, (long long)B->rows);
@@ -353,7 +367,7 @@ int nvfp4_grouped_gemm(int64_t G, const int64_t* m_offsets, const nvfp4_tensor* 
   if ((st = check_operand(A, "A")) || (st = check_operand(B, "B"))) return st;
   if (A->cols != B->cols) return fail(NVFP4_ERR_INVALID, "K mismatch: A has %lld, B has %lld", (long long)A->cols, (long long)B->cols);
   if (N < 1 || B->rows != G * N) return fail(NVFP4_ERR_INVALID, "B rows (%lld) must equal G*N (%lld)", (long long)B->rows, (long long)(G * N));
-  if (!D) return fail(NVFP4_ERR_INVALID, "D is NULL");
+  if (!D && A->rows > 0) return fail(NVFP4_ERR_INVALID, "D is NULL");   // an empty D is never written
   if (ldd < N) return fail(NVFP4_ERR_INVALID, "ldd (%lld) < N (%lld)", (long long)ldd, (long long)N);
   const nvfp4::GemmOperand a{A->codes, A->scales, A->global_scale};
   const nvfp4::GemmOperand b{B->codes, B->scales, B->global_scale};
@@ -369,7 +383,7 @@ int nvfp4_grouped_gemm_k(int64_t G, const int64_t* k_offsets, const nvfp4_tensor
   if ((st = check_operand(A, "A")) || (st = check_operand(B, "B"))) return st;
   if (A->cols != B->cols) return fail(NVFP4_ERR_INVALID, "K mismatch: A has %lld, B has %lld", (long long)A->cols, (long long)B->cols);
   if (A->cols % 64) return fail(NVFP4_ERR_UNSUPPORTED, "K (%lld) must be a multiple of 64", (long long)A->cols);
-  if (!D) return fail(NVFP4_ERR_INVALID, "D is NULL");
+  if (!D && A->rows > 0 && B->rows > 0) return fail(NVFP4_ERR_INVALID, "D is NULL");   // an empty D is never written
   if (ldd < B->rows) return fail(NVFP4_ERR_INVALID, "ldd (%lld) < N (%lld)", (long long)ldd, (long long)B->rows);
   const nvfp4::GemmOperand a{A->codes, A->scales, A->global_scale};
   const nvfp4::GemmOperand b{B->codes, B->scales, B->global_scale};
@@ -381,6 +395,7 @@ int nvfp4_dequantize(const nvfp4_tensor* q, const int64_t* segments, int64_t nse
                      void* hip_stream) {
   int st;
   if ((st = check_operand(q, "q"))) return st;
+  if (q->rows == 0 || q->cols == 0) return NVFP4_OK;
   if (!y) return fail(NVFP4_ERR_INVALID, "y is NULL");
   if (nseg < 1 || (!segments && nseg != 1)) return fail(NVFP4_ERR_INVALID, "bad segment table (nseg=%lld)", (long long)nseg);
   return hip_status(nvfp4::launch_dequantize(q->codes, q->scales, q->global_scale, segments, nseg,

@@ -26,6 +26,9 @@
  *     output but never an out-of-bounds access: kernels clamp table lookups.
  *   - Non-finite inputs (Inf/NaN) are outside the contract: outputs are unspecified, the
  *     kernels still terminate normally.
+ *   - Empty tensors are valid: with no rows (or an output without rows or columns) nothing is
+ *     read or written and the buffer pointers may be NULL; the amax of an empty tensor is 0
+ *     (amax_out is still written).
  *
  * NVFP4 tensor layout (nvfp4_tensor), for a logical matrix [rows, cols] quantized along cols:
  *   codes        uint8 [rows, cols/2] row-major; element 2i in the low nibble, 2i+1 in the

@@ -264,3 +264,33 @@ def test_dequantize_matches_oracle():
     torch.cuda.synchronize()
     ref = oracle.dequantize(*oracle.quantize_1x16(f32(bits))).astype(np.float32)
     assert_bytes_equal(y.cpu().numpy().view(np.uint32), ref.view(np.uint32), "dequantize")
+
+
+def test_empty_inputs_are_no_ops():
+    """Zero rows (torch hands over NULL data pointers): every entry point returns without
+    touching memory; the amax of nothing is 0."""
+    log("empty inputs")
+    mask = workloads.wgrad_sign_mask()
+    x = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
+    q, qt = nv.quantize(x, "16x16", "rn", emit_transposed=True)
+    assert q.rows == 0 and qt.cols == 0
+    nv.quantize(x, "1x16", "sr", seed=1)
+    nv.rht_quantize(x, mask, "sr")
+    nv.rht_rows_quantize(x, mask, "rn")
+    nv.mx_quantize(x)
+    a = torch.full((1,), 7.0, device="cuda")
+    nv.amax(x, out=a)
+    p = torch.full((2,), 7.0, device="cuda")
+    nv.amax_pair(x, mask, out=p)
+    assert nv.dequantize(q).shape == (0, 64)
+    # GEMMs with no rows on either side
+    qb, _ = nv.quantize(to_device_bf16(workloads.normal_bf16((32, 64), 5)), "1x16", "rn")
+    assert nv.gemm(q, qb).shape == (0, 32)
+    assert nv.gemm(qb, q).shape == (32, 0)
+    assert nv.gemm_ex(q, qb, out_dtype=torch.bfloat16).shape == (0, 32)
+    off = torch.zeros((3,), dtype=torch.int64, device="cuda")
+    qw, _ = nv.quantize(to_device_bf16(workloads.normal_bf16((64, 64), 6)), "1x16", "rn",
+                        segments=torch.tensor([0, 32, 64], dtype=torch.int64, device="cuda"))
+    assert nv.grouped_gemm(off, nv.NVFP4Tensor.empty(0, 64, 2), qw, 32).shape == (0, 32)
+    torch.cuda.synchronize()
+    assert a.item() == 0.0 and p.cpu().tolist() == [0.0, 0.0]
