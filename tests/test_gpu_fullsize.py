@@ -157,3 +157,47 @@ def test_moe_layer_full_size():
             assert abs(float(dh[r, c]) - ref) <= bound, (r, c)
             checked += 1
     assert checked >= 16
+
+
+def test_two_to_the_31_elements():
+    """A 65536 x 32768 BF16 tensor (2^31 elements, 4 GiB): every index past 32 bits. Uniform
+    values in [-1, 1] with one spike of 1000, so both tensor maxima come from the spike's block
+    (every other transformed block is at most 16 * 1/4 = 4): the oracle computes them from
+    that block, checks them in full, and checks sampled rows (1x16) and columns (transform)
+    bit for bit, including the spike's."""
+    rows, cols = 65536, 32768
+    log("2^31 elements")
+    g = torch.Generator(device="cuda").manual_seed(31)
+    x = torch.empty((rows, cols), dtype=torch.bfloat16, device="cuda")
+    for r0 in range(0, rows, 4096):
+        x[r0:r0 + 4096] = (torch.rand((4096, cols), generator=g, device="cuda") * 2 - 1).to(torch.bfloat16)
+    rs, cs = 54321, 23456
+    x[rs, cs] = 1000.0
+    mask = workloads.wgrad_sign_mask()
+    a = nv.amax(x)
+    ah = nv.amax(x, rht=True, sign_mask=mask)
+    q, _ = nv.quantize(x, "1x16", "rn")
+    qh = nv.rht_quantize(x, mask, "rn")
+    torch.cuda.synchronize()
+    assert a.item() == 1000.0
+    tb = rs // 16 * 16
+    blk = x[tb:tb + 16, cs:cs + 1].float().cpu().numpy()
+    want_h = np.float32(np.abs(oracle.rht_columnwise(blk, mask)).max())
+    assert want_h > 4.0
+    assert_bytes_equal(ah.cpu().numpy().view(np.uint32), np.array([want_h], np.float32).view(np.uint32), "rht amax")
+    rng = np.random.default_rng(31)
+    sr = np.unique(np.concatenate([[0, rows - 1, rs], rng.integers(0, rows, 5)]))
+    sc = np.unique(np.concatenate([[0, cols - 1, cs], rng.integers(0, cols, 5)]))
+    xr = x[torch.from_numpy(sr).cuda()].float().cpu().numpy()
+    xc = x[:, torch.from_numpy(sc).cuda()].float().cpu().numpy()
+    ref = oracle.quantize_1x16(xr, amax_vals=np.array([1000.0], np.float32), row_ids=sr)
+    gq = (q.codes[torch.from_numpy(sr).cuda()].cpu().numpy(), q.scales[torch.from_numpy(sr).cuda()].cpu().numpy(),
+          q.global_scale.cpu().numpy())
+    assert_bytes_equal(gq[0], ref[0], "rows codes")
+    assert_bytes_equal(gq[1], ref[1], "rows scales")
+    refh = oracle.rht_quantize(xc, mask, "rn", amax_vals=np.array([want_h], np.float32), col_ids=sc)
+    ic = torch.from_numpy(sc).cuda()
+    assert_bytes_equal(qh.codes[ic].cpu().numpy(), refh[0], "columns codes")
+    assert_bytes_equal(qh.scales[ic].cpu().numpy(), refh[1], "columns scales")
+    assert_bytes_equal(qh.global_scale.cpu().numpy().view(np.uint32), np.asarray(refh[2], np.float32).view(np.uint32),
+                       "columns scale")
