@@ -89,6 +89,26 @@ __device__ __forceinline__ void tile_of(int64_t bid, int64_t tiles_m, int64_t ti
   tn = in_band / gm;
 }
 
+// Number of m-tile slots of height bm over all groups, offsets clamped as group_of clamps
+// them. The whole workgroup (all threads) calls it.
+__device__ __forceinline__ int64_t count_slots(int64_t G, const int64_t* __restrict__ off,
+                                               int64_t total_m, int64_t bm) {
+  __shared__ int64_t part[4];
+  int64_t n = 0;
+  for (int64_t q = threadIdx.x; q < G; q += 256) {
+    int64_t lo = off[q];
+    lo = lo < 0 ? 0 : (lo > total_m ? total_m : lo);
+    int64_t hi = off[q + 1];
+    hi = hi < lo ? lo : (hi > total_m ? total_m : hi);
+    n += (hi - lo + bm - 1) / bm;
+  }
+#pragma unroll
+  for (int d = 32; d > 0; d >>= 1) n += __shfl_xor(n, d);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = n;
+  __syncthreads();
+  return part[0] + part[1] + part[2] + part[3];
+}
+
 // Group g and rows [m0, m1) of m-tile slot `slot_m` for tiles of height bm; false past the
 // last slot. The whole workgroup (256 threads, all of which must call it) searches: thread q
 // counts the slots of group c + q, a workgroup prefix sum over those counts brackets slot_m.
@@ -232,9 +252,11 @@ struct Cfg {
 using Full = Cfg<4, 4, 2, 2>;     // 256 x 256: 16 fragments, 12 DMA operations per wave, 108 KB
 using NTail = Cfg<2, 2, 4, 1>;    // 256 x 64 (a last column tile at most 64 wide)
 using MTail = Cfg<4, 2, 1, 4>;    // 128 x 256 (a group's last row slot at most 128 high)
+using NHalf = Cfg<4, 2, 2, 2>;    // 256 x 128 (a last column tile at most 128 wide)
 constexpr int kBlockM = Full::kBlockM, kBlockN = Full::kBlockN;
 constexpr int kLdsBytes = Full::kLdsBytes;
-static_assert(NTail::kLdsBytes <= kLdsBytes && MTail::kLdsBytes <= kLdsBytes, "LDS");
+static_assert(NTail::kLdsBytes <= kLdsBytes && MTail::kLdsBytes <= kLdsBytes &&
+              NHalf::kLdsBytes <= kLdsBytes, "LDS");
 
 // s_waitcnt immediate (gfx9 encoding): vmcnt(vm) lgkmcnt(lgkm), expcnt not waited on.
 constexpr int waitcnt_imm(int vm, int lgkm) {
@@ -676,20 +698,31 @@ __global__ __launch_bounds__(kThreads) void k_split_fixup(int64_t M, int64_t N, 
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_grouped_gemm_big(int64_t G, const int64_t* __restrict__ off, Operand A,
                         const float* __restrict__ ag, Operand B, const float* __restrict__ bg,
-                        int64_t N, int64_t K, float* __restrict__ D, int64_t ldd, int64_t slots_m) {
+                        int64_t N, int64_t K, float* __restrict__ D, int64_t ldd) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds_dyn[];
   using namespace big;
   const int64_t tiles_n = (N + kBlockN - 1) / kBlockN;
-  // A last column at most 64 wide is computed by the cheap 256 x 64 tiles; those workgroups
-  // come after all others (slots_m of them), so they fill the gaps the others leave at the
-  // end. Workgroups are dealt to the 8 XCDs round robin, so every XCD gets its share either
-  // way.
+  // A last column at most 64 wide is computed by the cheap 256 x 64 tiles.
   const bool narrow_last = tiles_n > 1 && N - (tiles_n - 1) * kBlockN <= NTail::kBlockN;
   const int64_t cols_main = narrow_last ? tiles_n - 1 : tiles_n;
-  const int64_t main_wg = slots_m * cols_main;
-  const int64_t bid = blockIdx.x;
-  const int64_t slot_m = bid < main_wg ? bid / cols_main : bid - main_wg;
-  const int64_t tn = bid < main_wg ? bid - slot_m * cols_main : tiles_n - 1;
+  // Workgroups are dealt to the 8 XCDs round robin (XCD x runs ids x, x + 8, ...). XCD x takes
+  // the slots [S x / 8, S (x + 1) / 8) of the S real ones whole: every column tile of a slot
+  // runs on one XCD, so the slot's A panel and its group's B panels enter that XCD's L2 once,
+  // and the XCDs get equal shares of real slots. Its full-width tiles go first, slot by slot,
+  // then its narrow last-column tiles, which fill the gaps at the end.
+  const int64_t S = count_slots(G, off, A.rows, kBlockM);
+  const int64_t xcd = blockIdx.x % 8, j = blockIdx.x / 8;
+  const int64_t sa = S * xcd / 8, ns = S * (xcd + 1) / 8 - sa;
+  int64_t slot_m, tn;
+  if (j < ns * cols_main) {
+    slot_m = sa + j / cols_main;
+    tn = j % cols_main;
+  } else if (j < ns * tiles_n) {
+    slot_m = sa + (j - ns * cols_main);
+    tn = tiles_n - 1;
+  } else {
+    return;                                                  // uniform over the workgroup
+  }
   int64_t g, m0, m1;
   if (!group_of(G, off, A.rows, kBlockM, slot_m, g, m0, m1)) return;
   const int64_t n0 = tn * kBlockN;
@@ -729,8 +762,16 @@ void k_grouped_gemm_k_big(int64_t G, const int64_t* __restrict__ koff, Operand A
   const int64_t m0 = tm * kBlockM, n0 = tn * kBlockN;
   const int64_t m1 = m0 + kBlockM < A.rows ? m0 + kBlockM : A.rows;
   const int64_t n1 = n0 + kBlockN < B.rows ? n0 + kBlockN : B.rows;
-  gemm_tile_big<Full, true>(A, B, m0, m1, n0, n1, K, k0, k1, false, ag[g] * bg[g],
-                            D + g * A.rows * ldd, ldd, lds_dyn);
+  const float alpha = ag[g] * bg[g];
+  float* Dg = D + g * A.rows * ldd;
+  // a last row tile at most 128 high or a last column tile at most 128 wide takes the
+  // narrower tile (about half the work of the full one; the corner takes the 128-high one)
+  if (m1 - m0 <= MTail::kBlockM)
+    gemm_tile_big<MTail, true>(A, B, m0, m1, n0, n1, K, k0, k1, false, alpha, Dg, ldd, lds_dyn);
+  else if (n1 - n0 <= NHalf::kBlockN)
+    gemm_tile_big<NHalf, true>(A, B, m0, m1, n0, n1, K, k0, k1, false, alpha, Dg, ldd, lds_dyn);
+  else
+    gemm_tile_big<Full, true>(A, B, m0, m1, n0, n1, K, k0, k1, false, alpha, Dg, ldd, lds_dyn);
 }
 
 // =========================================================================================
@@ -1224,9 +1265,10 @@ hipError_t launch_grouped_gemm(int64_t G, const int64_t* m_offsets, GemmOperand 
     if (e != hipSuccess) return e;
     const int64_t tiles_n = (N + big::kBlockN - 1) / big::kBlockN;
     const int64_t slots_m = total_m / big::kBlockM + G;       // >= sum_g ceil(M_g / 256)
-    hipLaunchKernelGGL(k_grouped_gemm_big, dim3((unsigned)(slots_m * tiles_n)), dim3(kThreads),
-                       big::kLdsBytes, stream, G, m_offsets, A, a.global_scale, B,
-                       b.global_scale, N, K, D, ldd, slots_m);
+    // 8 XCDs, each with at most ceil(slots_m / 8) slots of tiles_n tiles
+    hipLaunchKernelGGL(k_grouped_gemm_big, dim3((unsigned)(8 * ((slots_m + 7) / 8) * tiles_n)),
+                       dim3(kThreads), big::kLdsBytes, stream, G, m_offsets, A, a.global_scale, B,
+                       b.global_scale, N, K, D, ldd);
   } else {
     const int64_t tiles_n = (N + small::kBlockN - 1) / small::kBlockN;
     const int64_t slots_m = total_m / small::kBlockM + G;

@@ -167,6 +167,7 @@ def test_grouped_gemm_tile_shapes(n, k):
     (256, 256, [128, 192, 1856]),                 # groups not starting at 0 / ending before K
     (70, 33, [0, 1920]),                          # one group, ragged M and N
     (513, 300, [0, 640, 1280, 1344, 1920]),       # a 64-wide group inside one K step
+    (448, 384, [0, 512, 1920]),                   # last row tile 192 high, last column 128 wide
 ])
 def test_grouped_gemm_k(m, n, offs):
     """GEMMs grouped along K (MoE weight gradient): each group's block against the FP64
