@@ -68,8 +68,8 @@ def q_bytes(rows, cols, transposed=False):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; multi-GPU sharding is "
-                                   "described in DESIGN.md and not implemented"}))
+        print(json.dumps({"error": "the library runs on one GPU; sharding across GPUs is not "
+                                   "implemented, so only --gpus 1 is measured"}))
         sys.exit(2)
 
     import torch

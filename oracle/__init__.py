@@ -20,7 +20,7 @@ The oracle is plain numpy, written from the format description on the pages:
     activations; the Hadamard transform on the weight-gradient path.
 
 Where the pages are silent (bit-level conventions, rounding order) the oracle follows the
-readings listed in formats.py / quantize.py / hadamard.py; each is also listed in the design doc.
+readings stated in formats.py / quantize.py / hadamard.py / gemm.py / mx.py, each where it is used.
 
 Parity status: every function here is pinned by tests under tests/test_oracle_*.py against
 closed forms, library routines (numpy float16, torch float8_e4m3fn), published Philox

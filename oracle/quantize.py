@@ -8,7 +8,7 @@ What the pages fix
     combined with a per-tensor adjustment; weights use 16x16 blocks instead of 1x16 so the
     forward and backward passes see the same values; stochastic rounding only on gradients.
 
-Readings (where the pages are silent; listed in the design doc as R3-R8, R11, R12)
+Readings (where the pages are silent; labels R3-R8, R11, R12, shared with the other oracle modules)
   R3  BF16 input widens exactly to FP32; FP32 input is used as is.
   R4  A = max |x| over the tensor (per segment for expert-stacked tensors). If A == 0 then
       s_enc = s_dec = 1; else s_enc = fl32(2688 / A) (clamped to FLT_MAX) and
