@@ -129,6 +129,35 @@ def test_grouped_gemm_ragged_groups():
     assert np.all(np.abs(d.cpu().numpy() - d64) <= bound)
 
 
+@pytest.mark.parametrize("rows", [[3, 0, 200, 0], [700], [0, 0, 0, 1]])
+def test_grouped_gemm_fewer_slots_than_xcds(rows):
+    """The LDS-staged grouped kernel when the groups need fewer 256-row slots than the chip has
+    XCDs (the slots are split over the XCDs by count, so some XCDs get none): every row
+    within bound, the columns past N untouched."""
+    log(f"grouped gemm few slots {rows}")
+    n, k = 208, 128                      # N: the weights' 16x16 segments need multiples of 16
+    G = len(rows)
+    off = np.concatenate([[0], np.cumsum(rows)]).astype(np.int64)
+    x_bits = workloads.normal_bf16((int(off[-1]), k), 81 + G)
+    w_bits = workloads.normal_bf16((G * n, k), 82 + G)
+    offd = torch.from_numpy(off).cuda()
+    wseg = np.arange(G + 1, dtype=np.int64) * n
+    qx, _ = nv.quantize(to_device_bf16(x_bits), "1x16", "rn", segments=offd)
+    qw, _ = nv.quantize(to_device_bf16(w_bits), "16x16", "rn", segments=torch.from_numpy(wseg).cuda())
+    rx = oracle.quantize_1x16(f32(x_bits), segments=off)
+    rw = oracle.quantize_16x16(f32(w_bits), segments=wseg)
+    out = torch.full((int(off[-1]), n + 3), -5.0, dtype=torch.float32, device="cuda")
+    nv.grouped_gemm(offd, qx, qw, n, out=out[:, :n])
+    torch.cuda.synchronize()
+    o = out.cpu().numpy()
+    assert np.all(o[:, n:] == -5.0)
+    xh = oracle.dequantize(*rx, segments=off)
+    wh = oracle.dequantize(*rw, segments=wseg)
+    d64 = oracle.grouped_gemm_fp64(xh, wh, off, n)
+    bound = oracle.grouped_gemm_bound(xh, wh, off, n)
+    assert np.all(np.abs(o[:, :n] - d64) <= bound)
+
+
 @pytest.mark.parametrize("n,k", [(320, 192), (64, 128), (112, 2688), (576, 64)])
 def test_grouped_gemm_tile_shapes(n, k):
     """The LDS-staged grouped kernel (K % 64 == 0) with every tile shape it picks: full
