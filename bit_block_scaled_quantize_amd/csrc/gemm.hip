@@ -955,9 +955,10 @@ void k_grouped_gemm_small(int64_t G, const int64_t* __restrict__ off, Operand A,
 // makes, not bytes: four lanes read a row's 64 bytes of a step (one request per row and step
 // instead of two), and the E8M0 bytes move 16 per row (four steps) per request into a
 // two-deep ring. (Stages of 256 elements, whose rows are whole 128-byte lines, fit only two
-// deep in LDS and were slower: the prefetch distance matters more than the request count.) In LDS a fragment is 32 rows x 64 bytes,
-// row-major, with the 16-byte chunk c of row r stored at chunk c ^ ((r >> 2) & 3), so the
-// instruction's 16-byte reads (row r, chunk 2s + h) fall in distinct banks.
+// deep in LDS and were slower: the prefetch distance matters more than the request count.)
+// In LDS a fragment is 32 rows x 64 bytes, row-major, with the 16-byte chunk c of row r
+// stored at slot c ^ sw(r) (below), so the instruction's 16-byte reads (row r, chunk 2s + h)
+// fall in distinct banks.
 namespace mx {
 constexpr int kBlockM = 256, kBlockN = 256, kFragsA = 8, kFrags = 16;
 constexpr int kFragBytes = 2048;                                  // 32 rows x 64 bytes
@@ -1004,9 +1005,9 @@ void k_gemm_mx(Operand A, Operand B, int64_t K, float* __restrict__ D, int64_t l
   const __amdgpu_buffer_rsrc_t b_scales = make_rsrc(B.scales, B.rows * (K >> 5));
   // DMA for K step `step` (into code buffer `buf`), 5 operations per wave:
   //  p = 0..3: half q = p & 1 (rows 16q .. +15) of fragment f = wave + 8 (p >> 1) (A for
-  //    p < 2, B after); lane l reads row 16q + l/4, chunk (l & 3) ^ ((l >> 4) & 3) of the
-  //    step's 64 bytes (the LDS swizzle: that row has (r >> 2) & 3 = (l >> 4) & 3) into LDS
-  //    f * 2 KB + q * 1 KB + l * 16.
+  //    p < 2, B after); lane l reads row 16q + l/4, chunk (l & 3) ^ sw(16q + l/4) of the
+  //    step's 64 bytes into LDS f * 2 KB + q * 1 KB + l * 16 (row r's chunk c sits at 16-byte
+  //    slot c ^ sw(r) of the row's 64 bytes; sw(16q + l/4) = ((l >> 3) & 3) ^ ((l >> 5) & 1)).
   //  p = 4: the E8M0 bytes of steps step .. step+3 when step % 4 == 0 (group step/4 into scale
   //    buffer (step/4) % 2), rows 64 wave .. +63 of the 512 (A then B), lane l one row's 16
   //    bytes; other steps issue it idle (out of range, into a pad area), so every step issues
@@ -1014,7 +1015,8 @@ void k_gemm_mx(Operand A, Operand B, int64_t K, float* __restrict__ D, int64_t l
   // Steps past the last are issued out of range too (zeros, no memory traffic) into buffers
   // nobody reads again, so the loop has no branches.
   constexpr int kOps = 5;
-  const uint32_t lane_codes = (uint32_t)(lane >> 2) * rs_codes + 16u * (uint32_t)((lane & 3) ^ ((lane >> 4) & 3));
+  const uint32_t lane_codes = (uint32_t)(lane >> 2) * rs_codes +
+                              16u * (uint32_t)((lane & 3) ^ ((lane >> 3) & 3) ^ ((lane >> 5) & 1));
   const uint32_t lane_scales = (uint32_t)lane * rs_scales;
   auto issue_dma_part = [&](int step, int buf, int p) {
     const bool live = step < steps;
@@ -1044,22 +1046,34 @@ void k_gemm_mx(Operand A, Operand B, int64_t K, float* __restrict__ D, int64_t l
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = float16v{};
   // operands of the 64-element half s2 of a step: lane (r, h) reads row r, chunk 2 s2 + h,
-  // stored at chunk (2 s2 + h) ^ ((r >> 2) & 3); the E8M0 byte 2 s2 + h of the row's scale
-  // dword moved to byte 0 (the byte the instruction reads).
+  // stored at slot (2 s2 + h) ^ sw(r); the E8M0 byte 2 s2 + h of the row's scale dword moved
+  // to byte 0 (the byte the instruction reads). The swizzle sw(r) = ((r >> 1) & 3) ^
+  // ((r >> 3) & 1) spreads the 16-byte reads of any 8 consecutive rows over the 128 bytes of
+  // 32 banks and of any 16 consecutive rows over the 256 bytes of 64 banks.
+  // The step's scale dwords are read from LDS with half 0 and kept for half 1 (the reads
+  // stride 16 bytes per row, so they meet bank conflicts: once per step halves them; whole
+  // 16-byte groups kept over four steps would not fit the registers of two waves per SIMD).
   struct Ops { v4u32 a[2], b[4]; uint32_t sa[2], sb[4]; };
+  uint32_t raw_sa[2], raw_sb[4];
   auto read_ops = [&](int step, int buf, int s2, Ops& o) {
-    const int off = r * 64 + (((2 * s2 + h) ^ ((r >> 2) & 3)) << 4);
+    const int off = r * 64 + (((2 * s2 + h) ^ ((r >> 1) & 3) ^ ((r >> 3) & 1)) << 4);
     const uint8_t* base = lds + buf * kCodeBytes + off;
 #pragma unroll
     for (int i = 0; i < 2; ++i) o.a[i] = *reinterpret_cast<const v4u32*>(base + (wm * 2 + i) * kFragBytes);
 #pragma unroll
     for (int j = 0; j < 4; ++j) o.b[j] = *reinterpret_cast<const v4u32*>(base + (kFragsA + wn * 4 + j) * kFragBytes);
-    const uint8_t* sc = lds + kScaleBase + ((step / kGroupSteps) & 1) * kScaleGroupBytes + (step % kGroupSteps) * 4 + r * 16;
+    if (s2 == 0) {
+      const uint8_t* sc = lds + kScaleBase + ((step / kGroupSteps) & 1) * kScaleGroupBytes + (step % kGroupSteps) * 4 + r * 16;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) raw_sa[i] = *reinterpret_cast<const uint32_t*>(sc + ((wm * 2 + i) * 32) * 16);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) raw_sb[j] = *reinterpret_cast<const uint32_t*>(sc + (kBlockM + (wn * 4 + j) * 32) * 16);
+    }
     const int sh = 8 * (2 * s2 + h);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) o.sa[i] = *reinterpret_cast<const uint32_t*>(sc + ((wm * 2 + i) * 32) * 16) >> sh;
+    for (int i = 0; i < 2; ++i) o.sa[i] = raw_sa[i] >> sh;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) o.sb[j] = *reinterpret_cast<const uint32_t*>(sc + (kBlockM + (wn * 4 + j) * 32) * 16) >> sh;
+    for (int j = 0; j < 4; ++j) o.sb[j] = raw_sb[j] >> sh;
   };
   auto barrier = [] {
     asm volatile("" ::: "memory");
