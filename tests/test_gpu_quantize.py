@@ -294,3 +294,44 @@ def test_empty_inputs_are_no_ops():
     assert nv.grouped_gemm(off, nv.NVFP4Tensor.empty(0, 64, 2), qw, 32).shape == (0, 32)
     torch.cuda.synchronize()
     assert a.item() == 0.0 and p.cpu().tolist() == [0.0, 0.0]
+
+
+def test_side_stream_matches_default_stream():
+    """Every call takes the stream it is given: the layer's chain (amax pair, 1x16 SR, 16x16 with
+    transpose, Hadamard along tokens, GEMM) issued on a side stream, with its inputs written on
+    the default stream just before, gives bit-identical results to the same chain on the
+    default stream. The stochastic bits depend on the counter offset only: the same seed and
+    offset repeat the codes, another offset changes some."""
+    log("side stream")
+    mask = workloads.wgrad_sign_mask()
+    x_bits = _bits((256, 512), 91)
+    w_bits = _bits((384, 512), 92)
+
+    def chain(stream):
+        x = to_device_bf16(x_bits)
+        w = to_device_bf16(w_bits)
+        if stream is not None:
+            stream.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(stream if stream is not None else torch.cuda.current_stream()):
+            pair = nv.amax_pair(x, mask, stream=stream)
+            qx, _ = nv.quantize(x, "1x16", "sr", seed=5, offset=9, amax=pair[0:1], stream=stream)
+            qw, qwt = nv.quantize(w, "16x16", "rn", emit_transposed=True, stream=stream)
+            qh = nv.rht_quantize(x, mask, "rn", amax=pair[1:2], stream=stream)
+            d = nv.gemm(qx, qw, stream=stream)
+        if stream is not None:
+            stream.synchronize()
+        torch.cuda.synchronize()
+        return [t.cpu() for t in (pair, qx.codes, qx.scales, qw.codes, qwt.codes, qh.codes, qh.scales, d)]
+
+    ref = chain(None)
+    side = chain(torch.cuda.Stream())
+    for i, (a, b) in enumerate(zip(ref, side)):
+        assert torch.equal(a, b), f"output {i} differs between streams"
+    x = to_device_bf16(x_bits)
+    q1, _ = nv.quantize(x, "1x16", "sr", seed=5, offset=9)
+    q2, _ = nv.quantize(x, "1x16", "sr", seed=5, offset=9)
+    q3, _ = nv.quantize(x, "1x16", "sr", seed=5, offset=10)
+    torch.cuda.synchronize()
+    assert torch.equal(q1.codes, q2.codes)
+    assert not torch.equal(q1.codes, q3.codes)
+    assert torch.equal(q1.scales, q3.scales)
