@@ -187,11 +187,13 @@ struct ExtOut {
   float* amax;      // device float or null
 };
 
-// BF16 bits of finite v rounded to nearest, ties to even.
-__device__ __forceinline__ uint32_t bf16_rn_bits(float v) {
-  const uint32_t u = __float_as_uint(v);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+// BF16 bits of v and w rounded to nearest, ties to even (low and high half; one
+// v_cvt_pk_bf16_f32).
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16_rn_pair(float v, float w) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v2f32{v, w}, bf16x2));
 }
+__device__ __forceinline__ uint32_t bf16_rn_bits(float v) { return bf16_rn_pair(v, 0.0f) & 0xFFFFu; }
 
 // Stores v as output element (row, col); returns |stored value|.
 template <int KIND>
@@ -534,6 +536,35 @@ __device__ __forceinline__ void gemm_tile_big(Operand A, Operand B, int64_t m0, 
               const float sum = old[j][q] + acc[i][j][q] * alpha;
               Df[row * ext.ldd + col] = sum;
               mx = fmaxf(mx, fabsf(sum));
+            }
+          }
+        }
+      }
+      if (ext.amax != nullptr) group_amax(mx, ext.amax);
+      return;
+    }
+  }
+  if constexpr (EXT && KIND == kOutBF16) {
+    if (!accumulate) {
+      // BF16: the lane's values q and q + 1 (rows row and row + 1) converted by one instruction
+      uint16_t* Db = static_cast<uint16_t*>(ext.d);
+#pragma unroll
+      for (int i = 0; i < kFragsM; ++i) {
+#pragma unroll
+        for (int j = 0; j < kFragsN; ++j) {
+          const int64_t col = n0 + wn * kWaveN + 32 * j + r;
+          if (col >= n1) continue;
+#pragma unroll
+          for (int q = 0; q < 16; q += 2) {
+            const int64_t row = m0 + wm * kWaveM + 32 * i + 8 * (q >> 2) + 4 * h + (q & 3);
+            const uint32_t b = bf16_rn_pair(acc[i][j][q] * alpha, acc[i][j][q + 1] * alpha);
+            if (row < m1) {
+              __builtin_nontemporal_store((uint16_t)b, Db + row * ext.ldd + col);
+              mx = fmaxf(mx, fabsf(__uint_as_float(b << 16)));
+            }
+            if (row + 1 < m1) {
+              __builtin_nontemporal_store((uint16_t)(b >> 16), Db + (row + 1) * ext.ldd + col);
+              mx = fmaxf(mx, fabsf(__uint_as_float(b & 0xFFFF0000u)));
             }
           }
         }
