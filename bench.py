@@ -468,6 +468,18 @@ def bench_moe(nv, workloads, torch, dev, stream, flush, args):
                                         "GB/s", q_bytes(G * n, k)),
         "grouped_gemm": (lambda: nv.grouped_gemm(offd, Xq, Wq, n, out=D), "TFLOP/s", flops),
     }
+    # the two passes of each per-expert call timed apart: the amax pass (per-expert maxima) and
+    # the encode pass with those maxima supplied (the pass the HBM roofline applies to)
+    ax = nv.amax(X, segments=offd)
+    aw = nv.amax(Wt, segments=wseg)
+    calls.update({
+        "amax_x_experts": (lambda: nv.amax(X, segments=offd, out=ax), "GB/s", 2.0 * total * k),
+        "quantize_x_experts_1x16_rn_encode_pass": (
+            lambda: nv.quantize(X, "1x16", "rn", segments=offd, amax=ax, out=Xq, workspace=ws), "GB/s", q_bytes(total, k)),
+        "amax_w_experts": (lambda: nv.amax(Wt, segments=wseg, out=aw), "GB/s", 2.0 * G * n * k),
+        "quantize_w_experts_16x16_rn_encode_pass": (
+            lambda: nv.quantize(Wt, "16x16", "rn", segments=wseg, amax=aw, out=Wq, workspace=ws), "GB/s", q_bytes(G * n, k)),
+    })
     res = _time_calls(calls, torch, stream, flush, fsum, args)
     del D, Xq
 
@@ -501,6 +513,26 @@ def bench_moe(nv, workloads, torch, dev, stream, flush, args):
             "GB/s", q_bytes(tp, k)),
         "grouped_gemm_k_wgrad": (lambda: nv.grouped_gemm_k(offp, dYt, Xt, out=dW), "TFLOP/s", flops),
     }
+    ady = nv.amax(dY, segments=offp)
+    ahdy = nv.amax(dY, segments=offp, rht=True, sign_mask=mask)
+    ahx = nv.amax(Xp, segments=offp, rht=True, sign_mask=mask)
+    calls.update({
+        "quantize_w_experts_16x16_rn_transposed_encode_pass": (
+            lambda: nv.quantize(Wt, "16x16", "rn", emit_transposed=True, segments=wseg, amax=aw, out=Wq, out_t=WqT,
+                                workspace=ws), "GB/s", q_bytes(G * n, k, transposed=True)),
+        "amax_dy_experts": (lambda: nv.amax(dY, segments=offp, out=ady), "GB/s", 2.0 * tp * n),
+        "quantize_dy_experts_1x16_sr_encode_pass": (
+            lambda: nv.quantize(dY, "1x16", "sr", seed=11, segments=offp, amax=ady, out=dYq, workspace=ws),
+            "GB/s", q_bytes(tp, n)),
+        "amax_rht_dy_experts": (lambda: nv.amax(dY, segments=offp, rht=True, sign_mask=mask, out=ahdy), "GB/s", 2.0 * tp * n),
+        "rht_quantize_dy_experts_sr_encode_pass": (
+            lambda: nv.rht_quantize(dY, mask, "sr", seed=12, segments=offp, amax=ahdy, out=dYt, workspace=ws_r),
+            "GB/s", q_bytes(tp, n)),
+        "amax_rht_x_experts": (lambda: nv.amax(Xp, segments=offp, rht=True, sign_mask=mask, out=ahx), "GB/s", 2.0 * tp * k),
+        "rht_quantize_x_experts_rn_encode_pass": (
+            lambda: nv.rht_quantize(Xp, mask, "rn", segments=offp, amax=ahx, out=Xt, workspace=ws_r),
+            "GB/s", q_bytes(tp, k)),
+    })
     res.update(_time_calls(calls, torch, stream, flush, fsum, args))
     res["config"] = {"experts": G, "tokens": workloads.MOE_TOKENS, "topk": workloads.MOE_TOPK,
                      "hidden": k, "ffn": n, "rows_total": total, "rows_total_padded_64": tp,
