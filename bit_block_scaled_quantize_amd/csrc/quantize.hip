@@ -776,10 +776,24 @@ hipError_t launch_encode_rot(const void* x, bool fp32, int64_t rows, int64_t col
   return hipGetLastError();
 }
 
+// A contiguous tensor (ld == cols) is a flat run of blocks: codes, scales and the blocks'
+// stochastic-rounding counters (row * cols/16 + col/16) all follow the flat order. The encode
+// kernels give each wave one row per chunk of 64 * U blocks, so rows shorter than a chunk, or
+// not a multiple of it, leave lanes idle; such a tensor is encoded as rows of exactly one chunk
+// (4096 BF16 or 2048 FP32 elements) when its size allows, with identical output.
+static void flatten_rows(bool fp32, int64_t& rows, int64_t& cols, int64_t& ld) {
+  const int64_t L = fp32 ? 2048 : 4096;
+  if (ld == cols && cols % L != 0 && (rows * cols) % L == 0) {
+    rows = rows * cols / L;
+    cols = ld = L;
+  }
+}
+
 hipError_t launch_encode_mx(const void* x, bool fp32, int64_t rows, int64_t cols, int64_t ld,
                             bool sr, uint64_t seed, uint64_t offset, uint8_t* codes,
                             uint8_t* scales, hipStream_t stream) {
   if (rows == 0) return hipSuccess;
+  flatten_rows(fp32, rows, cols, ld);
   const int grid = grid_for(rows, kWavesPerBlock, kEncodeBlocks);
 #define NVFP4_MX(T, S) hipLaunchKernelGGL((k_encode_mx<T, S>), dim3(grid), dim3(kThreads), 0, stream, \
                                           (const T*)x, rows, cols, ld, codes, scales, seed, offset)
@@ -794,6 +808,7 @@ hipError_t launch_encode_1x16(const void* x, bool fp32, int64_t rows, int64_t co
                               const int64_t* segments, int64_t nseg, const float* amax, int parts,
                               QuantOut out, hipStream_t stream) {
   const bool seg = segments != nullptr;
+  if (!seg) flatten_rows(fp32, rows, cols, ld);
 #define NVFP4_E1(T, S, G) encode_1x16_t<T, S, G>(x, rows, cols, ld, seed, offset, segments, nseg, amax, parts, out, stream)
   if (fp32) {
     if (sr) { if (seg) NVFP4_E1(float, true, true); else NVFP4_E1(float, true, false); }
