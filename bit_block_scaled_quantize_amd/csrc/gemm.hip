@@ -733,8 +733,8 @@ void k_grouped_gemm_big(int64_t G, const int64_t* __restrict__ off, Operand A,
   extern __shared__ __attribute__((aligned(16))) uint8_t lds_dyn[];
   using namespace big;
   const int64_t tiles_n = (N + kBlockN - 1) / kBlockN;
-  // A last column at most 64 wide is computed by the cheap 256 x 64 tiles.
-  const bool narrow_last = tiles_n > 1 && N - (tiles_n - 1) * kBlockN <= NTail::kBlockN;
+  // A last column at most 128 wide is computed by the narrower 256 x 64 / 256 x 128 tiles.
+  const bool narrow_last = tiles_n > 1 && N - (tiles_n - 1) * kBlockN <= NHalf::kBlockN;
   const int64_t cols_main = narrow_last ? tiles_n - 1 : tiles_n;
   // Workgroups are dealt to the 8 XCDs round robin (XCD x runs ids x, x + 8, ...). XCD x takes
   // the slots [S x / 8, S (x + 1) / 8) of the S real ones whole: every column tile of a slot
@@ -760,10 +760,12 @@ void k_grouped_gemm_big(int64_t G, const int64_t* __restrict__ off, Operand A,
   const int64_t n1 = n0 + kBlockN < N ? n0 + kBlockN : N;
   const Operand Bg{B.codes + g * N * (K >> 1), B.scales + g * N * (K >> 4), N};
   const float alpha = ag[g] * bg[g];
-  // a last column at most 64 wide and a group's last slot at most 128 high take the narrower
-  // tiles, which cost about a quarter and a half of the full one
+  // a last column at most 64 or 128 wide and a group's last slot at most 128 high take the
+  // narrower tiles, which cost about 0.4, 0.55 and 0.7 of the full one
   if (n1 - n0 <= NTail::kBlockN)
     gemm_tile_big<NTail>(A, Bg, m0, m1, n0, n1, K, 0, K, false, alpha, D, ldd, lds_dyn);
+  else if (n1 - n0 <= NHalf::kBlockN)
+    gemm_tile_big<NHalf>(A, Bg, m0, m1, n0, n1, K, 0, K, false, alpha, D, ldd, lds_dyn);
   else if (m1 - m0 <= MTail::kBlockM)
     gemm_tile_big<MTail>(A, Bg, m0, m1, n0, n1, K, 0, K, false, alpha, D, ldd, lds_dyn);
   else

@@ -158,12 +158,12 @@ def test_grouped_gemm_fewer_slots_than_xcds(rows):
     assert np.all(np.abs(o[:, :n] - d64) <= bound)
 
 
-@pytest.mark.parametrize("n,k", [(320, 192), (64, 128), (112, 2688), (576, 64)])
+@pytest.mark.parametrize("n,k", [(320, 192), (64, 128), (112, 2688), (576, 64), (352, 1856)])
 def test_grouped_gemm_tile_shapes(n, k):
     """The LDS-staged grouped kernel (K % 64 == 0) with every tile shape it picks: full
-    256 x 256 tiles, 128-row tiles for a group's last slot of at most 128 rows, and 64-wide
-    tiles for a last column of at most 64, over empty, tiny, exactly-128/256 and multi-slot
-    groups."""
+    256 x 256 tiles, 128-row tiles for a group's last slot of at most 128 rows, and 64- or
+    128-wide tiles for a last column of at most 64 or 128, over empty, tiny, exactly-128/256
+    and multi-slot groups."""
     log(f"grouped gemm tiles n={n} k={k}")
     rows = [0, 5, 130, 128, 300, 513, 256, 1, 0, 129]
     G = len(rows)
