@@ -201,3 +201,54 @@ def test_two_to_the_31_elements():
     assert_bytes_equal(qh.scales[ic].cpu().numpy(), refh[1], "columns scales")
     assert_bytes_equal(qh.global_scale.cpu().numpy().view(np.uint32), np.asarray(refh[2], np.float32).view(np.uint32),
                        "columns scale")
+
+
+def test_moe_dgrad_full_size():
+    """The expert layer's activation gradient at full size on the padded token layout (128
+    experts, tokens padded to 64 per expert, N = hidden 2688, K = FFN 1856): dY in 1x16 SR per
+    expert, the weights' per-expert transposes from the 16x16 call, then the grouped GEMM (its
+    last column tiles are 128 wide). Sampled rows of both operands bit-exact against the
+    oracle, sampled outputs within the bound of the FP64 reference."""
+    log("moe dgrad full size")
+    x_bits, w_bits, off = workloads.moe()
+    G, n, k = workloads.MOE_EXPERTS, workloads.MOE_FFN, workloads.MOE_HIDDEN
+    _, dy_pad, off_pad = workloads.moe_backward(x_bits, off)
+    del x_bits
+    rng = np.random.default_rng(78)
+    offp = torch.from_numpy(off_pad).cuda()
+    wseg = np.arange(G + 1, dtype=np.int64) * n
+    qdy, _ = nv.quantize(to_device_bf16(dy_pad), "1x16", "sr", seed=21, segments=offp)
+    _, qwt = nv.quantize(to_device_bf16(w_bits), "16x16", "rn", emit_transposed=True,
+                         segments=torch.from_numpy(wseg).cuda())
+    dx = nv.grouped_gemm(offp, qdy, qwt, k)
+    torch.cuda.synchronize()
+    dy, w = f32(dy_pad), f32(w_bits)
+    a_dy, a_w = oracle.amax(dy, off_pad), oracle.amax(w, wseg)
+    sizes = np.diff(off_pad)
+    experts = np.unique(np.concatenate([[np.argmax(sizes), np.argmin(sizes)], rng.choice(G, 5, replace=False)]))
+    rows = np.unique(np.concatenate([[off_pad[g], off_pad[g + 1] - 1, rng.integers(off_pad[g], off_pad[g + 1])]
+                                     for g in experts]))
+    ref_dy = oracle.quantize_1x16(dy[rows], "sr", seed=21, segments=off_pad, amax_vals=a_dy, row_ids=rows)
+    _rows_equal(host(qdy), ref_dy, rows, "expert dY")
+    sdy = dict(zip(rows, oracle.dequantize(*ref_dy, segments=off_pad, row_ids=rows)))
+    # columns of dX: 16-aligned groups at the start, the 128-wide last tile and one inside
+    c16 = np.array([0, k // 16 - 1, (k - 128) // 16, rng.integers(0, k // 16)])
+    gwt = host(qwt)
+    checked = 0
+    for g in experts:
+        wt = w[g * n:(g + 1) * n].T                                # [hidden, ffn] of expert g
+        for cg in c16:
+            cols = cg * 16 + np.arange(16)
+            ref_wt = oracle.quantize_16x16(wt[cols], amax_vals=np.array([a_w[g]], np.float32))
+            trows = g * k + cols
+            assert_bytes_equal(gwt[0][trows], ref_wt[0], f"expert {g} W^T codes")
+            assert_bytes_equal(gwt[1][trows], ref_wt[1], f"expert {g} W^T scales")
+            wdq = oracle.dequantize(*ref_wt)
+            for r in rows[(rows >= off_pad[g]) & (rows < off_pad[g + 1])]:
+                for i in (0, 7, 15):
+                    a, b = sdy[r], wdq[i]
+                    ref = float(np.dot(a, b))
+                    bound = 1e-5 * float(np.dot(np.abs(a), np.abs(b)))
+                    assert abs(float(dx[r, cols[i]].item()) - ref) <= bound, (g, r, cols[i])
+                    checked += 1
+    assert checked >= 48
