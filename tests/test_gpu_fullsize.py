@@ -252,3 +252,55 @@ def test_moe_dgrad_full_size():
                     assert abs(float(dx[r, cols[i]].item()) - ref) <= bound, (g, r, cols[i])
                     checked += 1
     assert checked >= 48
+
+
+def test_moe_wgrad_full_size():
+    """The expert layer's weight gradient at full size (the GEMM grouped along K): dY and X on
+    the padded token layout, transformed along tokens and quantized per expert (nearest; both
+    sides take the same per-expert maxima, 4 max|x| per expert, which bounds |H x|), then
+    nvfp4_grouped_gemm_k into dW [128 * 1856, 2688] (its last row tiles are 64 high and its
+    last column tiles 128 wide). Sampled rows of both transposed operands bit-exact against
+    the oracle, sampled dW entries within the bound of the FP64 sum over the expert's
+    tokens."""
+    log("moe wgrad full size")
+    x_bits, _, off = workloads.moe()
+    G, n, k = workloads.MOE_EXPERTS, workloads.MOE_FFN, workloads.MOE_HIDDEN
+    x_pad, dy_pad, off_pad = workloads.moe_backward(x_bits, off)
+    del x_bits
+    mask = workloads.wgrad_sign_mask()
+    rng = np.random.default_rng(79)
+    offp = torch.from_numpy(off_pad).cuda()
+    dy, x = f32(dy_pad), f32(x_pad)
+    a_dy = (oracle.amax(dy, off_pad) * np.float32(4)).astype(np.float32)
+    a_x = (oracle.amax(x, off_pad) * np.float32(4)).astype(np.float32)
+    qdy = nv.rht_quantize(to_device_bf16(dy_pad), mask, "rn", segments=offp, amax=torch.from_numpy(a_dy).cuda())
+    qx = nv.rht_quantize(to_device_bf16(x_pad), mask, "rn", segments=offp, amax=torch.from_numpy(a_x).cuda())
+    dw = nv.grouped_gemm_k(offp, qdy, qx)
+    torch.cuda.synchronize()
+    i_rows = np.unique(np.concatenate([[0, n - 1, n - 64, n - 65], rng.integers(0, n, 3)]))      # FFN rows
+    c_cols = np.unique(np.concatenate([[0, k - 1, k - 128, k - 129], rng.integers(0, k, 3)]))    # hidden
+    ref_dy = oracle.quantize_1x16_colsegments(oracle.rht_columnwise(dy[:, i_rows], mask), off_pad, amax_vals=a_dy)
+    ref_x = oracle.quantize_1x16_colsegments(oracle.rht_columnwise(x[:, c_cols], mask), off_pad, amax_vals=a_x)
+    gdy, gx = host(qdy), host(qx)
+    assert_bytes_equal(gdy[0][i_rows], ref_dy[0], "H dY codes")
+    assert_bytes_equal(gdy[1][i_rows], ref_dy[1], "H dY scales")
+    assert_bytes_equal(gx[0][c_cols], ref_x[0], "H X codes")
+    assert_bytes_equal(gx[1][c_cols], ref_x[1], "H X scales")
+    dqa = oracle.dequantize(ref_dy[0], ref_dy[1], np.ones(1, np.float32))
+    dqb = oracle.dequantize(ref_x[0], ref_x[1], np.ones(1, np.float32))
+    sizes = np.diff(off_pad)
+    experts = np.unique(np.concatenate([[np.argmax(sizes), np.argmin(sizes)], rng.choice(G, 4, replace=False)]))
+    dwh = {}
+    checked = 0
+    for g in experts:
+        t0, t1 = int(off_pad[g]), int(off_pad[g + 1])
+        sg = float(ref_dy[2][g]) * float(ref_x[2][g])
+        block = dw[g * n:(g + 1) * n].cpu().numpy()
+        for a_i, i in enumerate(i_rows):
+            for b_i, c in enumerate(c_cols):
+                a, b = dqa[a_i, t0:t1], dqb[b_i, t0:t1]
+                ref = float(np.dot(a, b)) * sg
+                bound = 1e-5 * float(np.dot(np.abs(a), np.abs(b))) * sg
+                assert abs(float(block[i, c]) - ref) <= bound, (g, i, c)
+                checked += 1
+    assert checked >= 100
