@@ -14,12 +14,18 @@ Reading R6 (where the pages are silent)
   * Q = (1/4) H16 D: D = diag(sigma_j) with sigma_j = -1 iff bit j of a 16-bit sign mask is
     set (one mask per GEMM, shared by both operands and all blocks); H16 is the Sylvester
     Hadamard matrix in natural order, H[i][j] = (-1)^popcount(i & j).
-  * It is computed by the fast Walsh-Hadamard butterfly in binary64: signs applied first
-    (exact), then stages h = 1, 2, 4, 8 replacing (u_j, u_{j+h}) by (u_j + u_{j+h},
-    u_j - u_{j+h}) for j with (j & h) == 0, then a multiply by 0.25 (exact), then one
-    round-to-nearest-even to binary32. For BF16 inputs whose 16-block exponent spread is at
-    most 40 binades every binary64 step is exact, so the result is the correctly rounded
-    exact product (pinned against exact rational arithmetic).
+  * Each output is the exact rational y_i = 1/4 * sum_j H[i][j] * sigma_j * v_j rounded once
+    to binary32 (nearest, ties to even). An exactly zero sum is +0; a nonzero sum keeps its
+    sign when it rounds to zero; a sum beyond the binary32 range rounds to infinity.
+  * How the oracle evaluates it: the fast Walsh-Hadamard butterfly in binary64 (terms
+    sigma_j * v_j / 4 + 0, which is exact and turns -0 into +0; stages h = 1, 2, 4, 8 replacing
+    (u_j, u_{j+h}) by (u_j + u_{j+h}, u_j - u_{j+h})) followed by one rounding to binary32,
+    for every block where a range check proves each butterfly step exact: every partial sum
+    is a multiple of the smallest nonzero term's last significant bit 2^q and at most
+    sum_j |u_j| in magnitude, so all of them are binary64 numbers when
+    sum_j |u_j| < 2^(q + 53). With no -0 among the terms no step can produce -0, so the
+    butterfly's zeros are +0 as the definition asks. Every other block is summed in exact
+    rational arithmetic (fractions.Fraction) and rounded by _round_to_f32.
   * The output is written transposed: y[c, t] for input x[t, c], so that the quantization
     that follows runs along tokens in ordinary 1x16 row blocks.
 
@@ -35,6 +41,8 @@ quantization, which pairs naturally with rotations in the backward pass)
   * Weights in that variant are quantized 1x16 (1D) for the forward GEMM.
 """
 from __future__ import annotations
+
+from fractions import Fraction
 
 import numpy as np
 
@@ -65,21 +73,100 @@ def hadamard_matrix_from_butterfly() -> np.ndarray:
     return _butterfly16(np.eye(16)).T
 
 
-def rht_columnwise_f64(x, sign_mask: int) -> np.ndarray:
-    """0.25 * H16 * D applied to each 16-token block of each column, in binary64, before
-    the final rounding. x[tokens, cols] -> [cols, tokens]."""
+def _terms(x, sign_mask: int) -> np.ndarray:
+    """sigma_j * v_j / 4 (+0, so no term is -0) per block: x[tokens, cols] -> [cols, tokens/16, 16]
+    in binary64 (exact: a power-of-two scale of a binary32 value)."""
     x = np.asarray(x, dtype=np.float32)
     t, c = x.shape
     if t % 16:
         raise ValueError("tokens must be a multiple of 16")
     v = x.astype(np.float64).T.reshape(c, t // 16, 16)
-    u = v * sign_vector(sign_mask)
-    return (_butterfly16(u) * 0.25).reshape(c, t)
+    return v * (sign_vector(sign_mask) * 0.25) + 0.0
+
+
+def _butterfly_exact(u: np.ndarray) -> np.ndarray:
+    """Per block (last axis): True when every partial sum of the binary64 butterfly over u is
+    exact, i.e. sum |u_j| < 2^(q + 53) with 2^q the smallest last-significant-bit weight of a
+    nonzero u_j. The float64 sum of |u_j| is enlarged by 2^-40 to cover its own rounding."""
+    a = np.abs(u)
+    nz = a != 0
+    m, e = np.frexp(np.where(nz, a, 1.0))                 # a = m * 2^e, 0.5 <= m < 1
+    mi = (m * 2.0 ** 53).astype(np.int64)                 # integer significand (exact)
+    low = mi & -mi                                        # its lowest set bit
+    q = e - 53 + np.round(np.log2(low.astype(np.float64))).astype(np.int64)
+    qmin = np.where(nz, q, 1 << 20).min(axis=-1)               # all-zero blocks: see below
+    total = a.sum(axis=-1) * (1.0 + 2.0 ** -40)
+    lim = np.ldexp(1.0, np.clip(qmin + 53, -1074, 1023).astype(np.int64))
+    return (~nz.any(axis=-1)) | (total < lim)
+
+
+def _round_to_f32(q: Fraction) -> np.float32:
+    """An exact rational rounded once to binary32: nearest, ties to the even significand;
+    +0 for zero, the sign kept for a nonzero value that rounds to zero, infinity beyond the
+    largest finite value (IEEE 754 round-to-nearest-even with gradual underflow)."""
+    if q == 0:
+        return np.float32(0.0)
+    neg = q < 0
+    mag = -q if neg else q
+    n, d = mag.numerator, mag.denominator
+    e = n.bit_length() - d.bit_length()                   # 2^(e-1) < mag < 2^(e+1)
+    if Fraction(2) ** e > mag:
+        e -= 1                                            # now 2^e <= mag < 2^(e+1)
+    lsb = max(e, -126) - 23                                # weight of the last kept bit
+    scaled = mag / Fraction(2) ** lsb                      # mag in units of that bit
+    k = scaled.numerator // scaled.denominator
+    rest = scaled - k
+    if rest > Fraction(1, 2) or (rest == Fraction(1, 2) and k % 2 == 1):
+        k += 1
+    val = k * Fraction(2) ** lsb
+    if val >= Fraction(2) ** 128:
+        out = np.float32(np.inf)
+    else:
+        out = np.float32(float(val))                       # k < 2^25: exact in binary32
+    return -out if neg else out
+
+
+def _exact_block(v32: np.ndarray, sign_mask: int) -> np.ndarray:
+    """The 16 outputs of one block by exact arithmetic: every binary32 value is an integer
+    multiple of 2^-149, so 2^151 * sigma_j * v_j / 4 is an integer and each output is an
+    integer sum over 2^151, rounded by _round_to_f32."""
+    sig = sign_vector(sign_mask)
+    h = hadamard_matrix_from_butterfly()
+    units = []
+    for a in v32:
+        n, d = float(a).as_integer_ratio()                # d = 2^k with k <= 149
+        units.append(n * ((1 << 149) // d))               # v_j * 2^149
+    out = np.empty(16, dtype=np.float32)
+    for i in range(16):
+        s = sum(int(h[i, j] * sig[j]) * units[j] for j in range(16))
+        out[i] = _round_to_f32(Fraction(s, 1 << 151))     # (v-sum * 2^149) / 4 / 2^149
+    return out
+
+
+def rht_columnwise_f64(x, sign_mask: int) -> np.ndarray:
+    """0.25 * H16 * D applied to each 16-token block of each column, in binary64, before the
+    final rounding: x[tokens, cols] -> [cols, tokens]. Only defined where the butterfly is
+    exact (raises otherwise), so these values are the exact products."""
+    u = _terms(x, sign_mask)
+    if not _butterfly_exact(u).all():
+        raise ValueError("a block is outside the range where the binary64 butterfly is exact")
+    c, nb, _ = u.shape
+    return _butterfly16(u).reshape(c, nb * 16)
 
 
 def rht_columnwise(x, sign_mask: int) -> np.ndarray:
     """The transform rounded once to float32 (R6). x[tokens, cols] -> y[cols, tokens]."""
-    return rht_columnwise_f64(x, sign_mask).astype(np.float32)
+    x32 = np.asarray(x, dtype=np.float32)
+    u = _terms(x32, sign_mask)
+    c, nb, _ = u.shape
+    with np.errstate(over="ignore"):
+        y = _butterfly16(u).astype(np.float32)
+    wide = ~_butterfly_exact(u)
+    if wide.any():
+        v = x32.T.reshape(c, nb, 16)
+        for ci, bi in zip(*np.nonzero(wide)):
+            y[ci, bi] = _exact_block(v[ci, bi], sign_mask)
+    return y.reshape(c, nb * 16)
 
 
 def rht_quantize_segments(x, sign_mask: int, token_segments, rounding: str = "rn", seed: int = 0,

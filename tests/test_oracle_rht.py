@@ -2,8 +2,12 @@
 
 The pages say the transform multiplies the wgrad inputs by a random Hadamard matrix and is
 undone analytically. Pins: the butterfly's matrix equals the Kronecker power of H2 (numpy),
-H H^T = 16 I, exact rational arithmetic for the rounded output, exact undo, Parseval, and
-invariance of the wgrad GEMM when both operands are transformed."""
+H H^T = 16 I, the rounded output against exact rational arithmetic (narrow blocks) and
+against math.fsum's exact summation for blocks of any exponent spread (BF16 and FP32 inputs,
+hand-made corner blocks), a worked wide-spread block whose correct rounding differs from a
+binary64 evaluation, signed zeros, overflow, exact undo, Parseval, and invariance of the
+wgrad GEMM when both operands are transformed."""
+import math
 from fractions import Fraction
 
 import numpy as np
@@ -170,3 +174,128 @@ def test_rowwise_quantize_is_quantize_of_the_transformed_rows():
         assert np.array_equal(u, v)
     # the transformed block's largest element maps near the grid's top, as any 1x16 block
     assert oracle.amax(y)[0] > 0
+
+
+def _rn32_of_exact_sum(terms) -> np.float32:
+    """binary32 nearest-even of the exact sum of binary64 terms, built on math.fsum (exact
+    summation, correctly rounded to binary64) instead of rational arithmetic: s = fsum(terms)
+    is the sum rounded to binary64 and r = fsum(terms + [-s]) carries the sign of what that
+    rounding dropped. Rounding s once more to binary32 is correct unless s is exactly halfway
+    between two binary32 values; then r decides (r = 0: a true tie, nearest-even)."""
+    s = math.fsum(terms)
+    if s == 0.0:
+        return np.float32(0.0)              # the terms are multiples of 2^-151: exact zero
+    r = math.fsum(list(terms) + [-s])
+    a = np.float32(s)
+    if not np.isfinite(a) or float(a) == s:
+        return a
+    b = np.nextafter(a, np.float32(np.inf) if s > float(a) else np.float32(-np.inf))
+    if (float(a) + float(b)) / 2 != s or r == 0.0:
+        return a
+    hi, lo = (a, b) if a > b else (b, a)
+    return hi if r > 0 else lo
+
+
+def _reference(x, mask):
+    """y[c, 16t+i] from _rn32_of_exact_sum over the 16 terms H[i][j] sigma_j x[16t+j, c] / 4."""
+    x = np.asarray(x, np.float32)
+    h = oracle.hadamard_matrix_from_butterfly()
+    sig = [(-1.0 if (mask >> j) & 1 else 1.0) for j in range(16)]
+    out = np.empty((x.shape[1], x.shape[0]), np.float32)
+    for c in range(x.shape[1]):
+        for t in range(x.shape[0] // 16):
+            v = [float(x[16 * t + j, c]) for j in range(16)]
+            for i in range(16):
+                out[c, 16 * t + i] = _rn32_of_exact_sum([h[i, j] * sig[j] * v[j] / 4 for j in range(16)])
+    return out
+
+
+def _same_bits(a, b):
+    return np.array_equal(np.asarray(a, np.float32).view(np.uint32), np.asarray(b, np.float32).view(np.uint32))
+
+
+def test_tie_broken_by_a_far_term_rounds_up():
+    # the column (1, 2^-24, 2^-70, 0, ...) with no sign flips: y_0 = (1 + 2^-24 + 2^-70) / 4 =
+    # 2^-2 + 2^-26 + 2^-72. binary32's spacing above 2^-2 is 2^-25, so 2^-2 + 2^-26 is a tie
+    # that the 2^-72 term breaks upwards: 2^-2 + 2^-25. A binary64 sum drops 2^-72 and then
+    # rounds the tie to even (2^-2). Outputs with H[i][2] = -1 sit just below the tie (2^-2);
+    # odd outputs are 2^-2 - 2^-26 (exact below 2^-2) minus or plus 2^-72, which rounds away.
+    x = np.zeros((16, 1), np.float32)
+    x[0:3, 0] = [1.0, 2.0 ** -24, 2.0 ** -70]
+    y = oracle.rht_columnwise(x, 0)[0]
+    want = np.array([0.25 + 2.0 ** -25 if i % 4 == 0 else 0.25 if i % 2 == 0 else 0.25 - 2.0 ** -26
+                     for i in range(16)], np.float32)
+    assert _same_bits(y, want)
+    assert float(np.float32(np.float64(0.25) + 2.0 ** -26)) == 0.25       # the binary64 route
+
+
+def test_any_exponent_spread_equals_exact_sum_bf16():
+    x = workloads.bf16_bits_to_f32(workloads.exponent_spread_bf16(64, 24, 31))
+    for mask in (0, 0x6E04, 0xFFFF):
+        assert _same_bits(oracle.rht_columnwise(x, mask), _reference(x, mask))
+
+
+def test_any_exponent_spread_equals_exact_sum_fp32():
+    x = workloads.exponent_spread_f32(64, 24, 32)
+    for mask in (0, 0x8001, 0x6E04):
+        assert _same_bits(oracle.rht_columnwise(x, mask), _reference(x, mask))
+
+
+def test_corner_blocks_equal_exact_sum():
+    x = workloads.bf16_bits_to_f32(workloads.hadamard_edge_blocks_bf16())
+    for mask in (0, 0x6E04, 0xFFFF):
+        with np.errstate(over="ignore"):
+            ref = _reference(x, mask)
+        assert _same_bits(oracle.rht_columnwise(x, mask), ref)
+
+
+def test_zero_sums_are_positive_zero():
+    # all-zero blocks (with -0 inputs) and blocks whose terms cancel give +0 for every mask
+    x = np.zeros((48, 1), np.float32)
+    x[0:16:3, 0] = -0.0
+    x[16, 0], x[17, 0] = 1.0, 1.0                       # outputs with H[i][1] = -1 cancel
+    x[32:48, 0] = -0.0
+    for mask in (0, 1, 0x8000, 0xFFFF, 0x6E04):
+        y = oracle.rht_columnwise(x, mask)[0]
+        zero = y == 0
+        assert zero[:16].all() and zero[32:].all() and zero[16:32].sum() == 8
+        assert not np.signbit(y[zero]).any()
+
+
+def test_underflow_keeps_the_sign():
+    # one FP32 subnormal 2^-149: every output is +-2^-151, which rounds to a zero carrying the
+    # sign of H[i][0] * sigma_0 * v = sigma_0 * v
+    for v in (2.0 ** -149, -(2.0 ** -149)):
+        x = np.zeros((16, 1), np.float32)
+        x[0, 0] = v
+        for mask in (0, 1):
+            y = oracle.rht_columnwise(x, mask)[0]
+            neg = (v < 0) != bool(mask & 1)
+            assert np.all(y == 0) and np.all(np.signbit(y) == neg)
+    # the same next to terms 2^149 times larger that cancel in the odd outputs (a block far
+    # outside binary64's exact range): those are +-2^-151 again, H[i][2] = (-1)^popcount(i & 2)
+    for v in (2.0 ** -149, -(2.0 ** -149)):
+        x = np.zeros((16, 1), np.float32)
+        x[0:3, 0] = [1.0, 1.0, v]
+        y = oracle.rht_columnwise(x, 0)[0]
+        for i in range(1, 16, 2):
+            neg = (v < 0) != bool(i & 2)
+            assert y[i] == 0 and np.signbit(y[i]) == neg
+
+
+def test_sum_beyond_binary32_range_is_infinite():
+    big = np.float32(workloads.bf16_bits_to_f32(np.array([0x7F7F], np.uint16))[0])
+    x = np.full((16, 1), big, np.float32)
+    with np.errstate(over="ignore"):
+        y = oracle.rht_columnwise(x, 0)[0]
+    assert y[0] == np.inf and np.all(y[1:] == 0)        # 16 * big / 4 > FLT_MAX
+
+
+def test_binary64_values_refuse_blocks_outside_the_exact_range():
+    x = np.zeros((16, 1), np.float32)
+    x[0:3, 0] = [1.0, 2.0 ** -24, 2.0 ** -70]
+    try:
+        oracle.rht_columnwise_f64(x, 0)
+    except ValueError:
+        return
+    raise AssertionError("the binary64 values of a wide block were returned as exact")

@@ -25,6 +25,7 @@ __all__ = [
     "f32_to_bf16_bits", "bf16_bits_to_f32", "normal_bf16", "with_outliers_bf16",
     "tiny", "fprop", "dgrad", "wgrad_sign_mask", "moe_routing", "moe",
     "SEEDS", "SR_SEED_DGRAD", "SR_SEED_WGRAD", "SR_OFFSET_WGRAD",
+    "exponent_spread_bf16", "exponent_spread_f32", "hadamard_edge_blocks_bf16", "WIDE_SPREADS",
 ]
 
 SEEDS = {
@@ -140,12 +141,18 @@ def moe(rows_w_per_expert: int = MOE_FFN, hidden: int = MOE_HIDDEN):
     return x, w, offsets
 
 
-def exponent_spread_bf16(tokens: int, cols: int, seed: int, spreads=(0, 6, 11, 12, 13, 16, 40)) -> np.ndarray:
+# Exponent spreads (binades between a block's largest and smallest nonzero value) around the
+# limits where a 16-term sum needs more than binary32's 24 or binary64's 53 bits, up to the
+# whole finite range.
+WIDE_SPREADS = (0, 6, 11, 12, 13, 14, 16, 24, 25, 26, 40, 41, 42, 60, 120, 253)
+
+
+def exponent_spread_bf16(tokens: int, cols: int, seed: int, spreads=WIDE_SPREADS) -> np.ndarray:
     """BF16 bits [tokens, cols] built per 16-token block of each column: a top exponent field
     F (mostly mid-range, sometimes 249..251 or very small) and a spread s drawn from `spreads`;
     fields uniform in [F - s, F] with F present, random signs and mantissas, about 5% exact
-    zeros; fields that fall to 0 or below give subnormals. Used to exercise the range
-    boundaries of the Hadamard transform's exactness test."""
+    zeros; fields that fall to 0 or below give subnormals. Used to exercise blocks whose
+    16-term sums need more bits than binary32 or binary64 hold."""
     if tokens % 16:
         raise ValueError("tokens must be a multiple of 16")
     rng = np.random.default_rng(seed)
@@ -195,3 +202,73 @@ def moe_backward(x_bits: np.ndarray, offsets, ffn: int = MOE_FFN, pad: int = 64)
     dy = normal_bf16((int(offsets[-1]), ffn), SEEDS["moe_dy"], std=1e-3)
     return scatter_rows(x_bits, offsets, off_pad), scatter_rows(dy, offsets, off_pad), off_pad
 
+
+
+def exponent_spread_f32(tokens: int, cols: int, seed: int, spreads=WIDE_SPREADS) -> np.ndarray:
+    """float32 [tokens, cols] built like exponent_spread_bf16 with 23 random mantissa bits:
+    per 16-token block of a column a top exponent field and a spread, fields uniform below the
+    top (subnormals where they reach 0), random signs, about 5% exact zeros."""
+    if tokens % 16:
+        raise ValueError("tokens must be a multiple of 16")
+    rng = np.random.default_rng(seed)
+    nb = tokens // 16
+    spread = rng.choice(np.asarray(spreads, dtype=np.int64), size=(nb, cols))
+    top = rng.integers(60, 200, size=(nb, cols))
+    edge = rng.random((nb, cols))
+    top = np.where(edge < 0.1, rng.integers(249, 252, size=(nb, cols)), top)
+    top = np.where((edge >= 0.1) & (edge < 0.15), rng.integers(1, 14, size=(nb, cols)), top)
+    field = top[:, None, :] - rng.integers(0, spread[:, None, :] + 1, size=(nb, 16, cols))
+    first = rng.integers(0, 16, size=(nb, cols))
+    field[np.arange(nb)[:, None], first, np.arange(cols)[None, :]] = top
+    field = np.clip(field, 0, 254).astype(np.uint32)
+    mant = rng.integers(0, 1 << 23, size=(nb, 16, cols)).astype(np.uint32)
+    mant = np.where(field == 0, np.maximum(mant, 1), mant).astype(np.uint32)
+    sign = rng.integers(0, 2, size=(nb, 16, cols)).astype(np.uint32)
+    bits = (sign << np.uint32(31)) | (field << np.uint32(23)) | mant
+    bits = np.where(rng.random((nb, 16, cols)) < 0.05, np.uint32(0), bits).astype(np.uint32)
+    return bits.reshape(tokens, cols).view(np.float32)
+
+
+def hadamard_edge_blocks_bf16(seed: int = 0) -> np.ndarray:
+    """BF16 bits [16 * n, 1]: one 16-token block per column entry of a list of hand-made
+    blocks for the Hadamard transform's corner cases: all zeros (some -0), a pair that cancels,
+    a lone value, a value and its negation among zeros, tiny values far below large ones
+    (1, 2^-24, 2^-70 as in a tie broken by a far term), exact ties next to cancelling far
+    terms, sums one to three bits wider than binary64, the smallest subnormal, the largest
+    finite values (sums beyond binary32's range), every exponent field once, and random
+    blocks with one term 100 or more binades below the rest. Returned as rows of one column
+    per block stacked along tokens."""
+    rng = np.random.default_rng(seed)
+
+    def b(vals):
+        v = np.zeros(16, np.float32)
+        v[:len(vals)] = np.asarray(vals, np.float32)
+        return f32_to_bf16_bits(v)
+
+    blocks = [
+        np.zeros(16, np.uint16),
+        np.full(16, 0x8000, np.uint16),                                   # all -0
+        np.where(np.arange(16) % 3 == 0, 0x8000, 0).astype(np.uint16),
+        b([1.0, 1.0]), b([1.0, -1.0]), b([3.0]), b([0.0, -5.0]),
+        b([1.0, 2.0 ** -24, 2.0 ** -70]), b([1.0, -(2.0 ** -24), 2.0 ** -70]),
+        b([1.0, 2.0 ** -24, -(2.0 ** -70)]), b([2.0 ** 100, 2.0 ** -100, 2.0 ** -126]),
+        b([1.0, 2.0 ** -24, 2.0 ** -70, -(2.0 ** -70)]),                 # exact ties, far terms
+        b([1.0, 2.0 ** -23, 2.0 ** -24, 2.0 ** -70, -(2.0 ** -70)]),
+        b([1.0, 2.0 ** -24, 2.0 ** -53]), b([1.0, 2.0 ** -24, 2.0 ** -54]),  # 54..56-bit sums
+        b([1.0, 2.0 ** -24, 2.0 ** -55]), b([1.0, 2.0 ** -24, -(2.0 ** -53)]),
+        np.array([1] + [0] * 15, np.uint16),                             # 2^-133
+        np.array([0x8001] + [1] * 15, np.uint16),
+        np.full(16, 0x7F7F, np.uint16),                                   # largest finite
+        np.where(np.arange(16) % 2 == 0, 0x7F7F, 0xFF7F).astype(np.uint16),
+        np.array([0x7F7F, 0x0001] + [0] * 14, np.uint16),
+    ]
+    fields = np.arange(0, 255, dtype=np.uint16)                          # every exponent field
+    fb = ((fields << 7) | rng.integers(0, 128, fields.size).astype(np.uint16)).astype(np.uint16)
+    fb = np.concatenate([fb, np.zeros((-fb.size) % 16, np.uint16)])
+    blocks += list(fb.reshape(-1, 16))
+    for _ in range(48):
+        v = (rng.integers(100, 140, 16) << 7) | rng.integers(0, 128, 16)
+        v[rng.integers(0, 16)] = rng.integers(0, 20) << 7 | rng.integers(1, 128)
+        v |= rng.integers(0, 2, 16) << 15
+        blocks.append(v.astype(np.uint16))
+    return np.concatenate(blocks).astype(np.uint16).reshape(-1, 1)
