@@ -11,6 +11,8 @@ grouped_gemm_k, amax, amax_pair, dequantize.
 from __future__ import annotations
 
 import ctypes
+import functools
+import inspect
 import os
 from dataclasses import dataclass
 
@@ -108,6 +110,24 @@ def _stream(stream=None):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _on_stream(fn):
+    """Runs a binding function with its `stream` argument (when given) as torch's current
+    stream, so every workspace and default output it allocates belongs to the stream its
+    kernels are enqueued on. torch's caching allocator hands a freed block out again only to
+    work on the stream it belongs to, so a workspace freed when the function returns cannot be
+    given to other work while these kernels may still be using it."""
+    sig = inspect.signature(fn)
+
+    @functools.wraps(fn)
+    def wrapper(*args, **kwargs):
+        stream = sig.bind(*args, **kwargs).arguments.get("stream")
+        if stream is None:
+            return fn(*args, **kwargs)
+        with torch.cuda.stream(stream):
+            return fn(*args, **kwargs)
+    return wrapper
+
+
 @dataclass
 class NVFP4Tensor:
     """Device buffers of one NVFP4 tensor [rows, cols] quantized along cols."""
@@ -195,6 +215,7 @@ def _workspace(op, rows, cols, nseg, device):
     return torch.empty((max(n, 1),), dtype=torch.uint8, device=device), n
 
 
+@_on_stream
 def quantize(x: torch.Tensor, block: str = "1x16", rounding: str = "rn", seed: int = 0,
              offset: int = 0, segments: torch.Tensor | None = None, amax: torch.Tensor | None = None,
              emit_transposed: bool = False, out: NVFP4Tensor | None = None,
@@ -231,6 +252,7 @@ def quantize(x: torch.Tensor, block: str = "1x16", rounding: str = "rn", seed: i
     return out, (out_t if emit_transposed else None)
 
 
+@_on_stream
 def rht_rows_quantize(x: torch.Tensor, sign_mask: int, rounding: str = "rn", seed: int = 0,
                       offset: int = 0, amax: torch.Tensor | None = None, out: NVFP4Tensor | None = None,
                       workspace: torch.Tensor | None = None, stream=None) -> NVFP4Tensor:
@@ -256,6 +278,7 @@ def rht_rows_quantize(x: torch.Tensor, sign_mask: int, rounding: str = "rn", see
     return out
 
 
+@_on_stream
 def mx_quantize(x: torch.Tensor, rounding: str = "rn", seed: int = 0, offset: int = 0,
                 out: MXFP4Tensor | None = None, stream=None) -> MXFP4Tensor:
     """mxfp4_quantize: x[rows, cols] -> MXFP4 (E8M0 scale per 32 elements)."""
@@ -270,6 +293,7 @@ def mx_quantize(x: torch.Tensor, rounding: str = "rn", seed: int = 0, offset: in
     return out
 
 
+@_on_stream
 def mx_gemm(a: MXFP4Tensor, b: MXFP4Tensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     """mxfp4_gemm: D[M, N] = A[M, K] * B[N, K]^T (FP32) on the block-scaled FP4 matrix cores."""
     lib = _load()
@@ -283,6 +307,7 @@ def mx_gemm(a: MXFP4Tensor, b: MXFP4Tensor, out: torch.Tensor | None = None, str
     return out
 
 
+@_on_stream
 def rht_quantize(x: torch.Tensor, sign_mask: int, rounding: str = "rn", seed: int = 0,
                  offset: int = 0, amax: torch.Tensor | None = None,
                  out: NVFP4Tensor | None = None, workspace: torch.Tensor | None = None,
@@ -312,6 +337,7 @@ def rht_quantize(x: torch.Tensor, sign_mask: int, rounding: str = "rn", seed: in
     return out
 
 
+@_on_stream
 def gemm(a: NVFP4Tensor, b: NVFP4Tensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     """nvfp4_gemm: D[M, N] = A[M, K] * B[N, K]^T (FP32)."""
     lib = _load()
@@ -326,6 +352,7 @@ def gemm(a: NVFP4Tensor, b: NVFP4Tensor, out: torch.Tensor | None = None, stream
     return out
 
 
+@_on_stream
 def gemm_ex(a: NVFP4Tensor, b: NVFP4Tensor, out: torch.Tensor | None = None,
             out_dtype: torch.dtype = torch.float32, accumulate: bool = False,
             amax_out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
@@ -360,6 +387,7 @@ def gemm_ex(a: NVFP4Tensor, b: NVFP4Tensor, out: torch.Tensor | None = None,
     return out
 
 
+@_on_stream
 def grouped_gemm(m_offsets: torch.Tensor, a: NVFP4Tensor, b: NVFP4Tensor, n: int,
                  out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     """nvfp4_grouped_gemm: per group g, rows m_offsets[g]:m_offsets[g+1] of A against rows
@@ -379,6 +407,7 @@ def grouped_gemm(m_offsets: torch.Tensor, a: NVFP4Tensor, b: NVFP4Tensor, n: int
     return out
 
 
+@_on_stream
 def grouped_gemm_k(k_offsets: torch.Tensor, a: NVFP4Tensor, b: NVFP4Tensor,
                    out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     """nvfp4_grouped_gemm_k: for each group g, columns k_offsets[g]:k_offsets[g+1] of A [M, K]
@@ -398,6 +427,7 @@ def grouped_gemm_k(k_offsets: torch.Tensor, a: NVFP4Tensor, b: NVFP4Tensor,
     return out
 
 
+@_on_stream
 def amax(x: torch.Tensor, segments: torch.Tensor | None = None, rht: bool | int = False,
          sign_mask: int = 0, out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
          stream=None) -> torch.Tensor:
@@ -419,6 +449,7 @@ def amax(x: torch.Tensor, segments: torch.Tensor | None = None, rht: bool | int 
     return out
 
 
+@_on_stream
 def amax_pair(x: torch.Tensor, sign_mask: int, out: torch.Tensor | None = None,
               workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     """nvfp4_amax_pair: float32 [2] = (max|x|, max of the Hadamard-transformed tensor)."""
@@ -436,6 +467,7 @@ def amax_pair(x: torch.Tensor, sign_mask: int, out: torch.Tensor | None = None,
     return out
 
 
+@_on_stream
 def dequantize(q: NVFP4Tensor, segments: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     """nvfp4_dequantize (test helper): FP32 [rows, cols]."""
     lib = _load()

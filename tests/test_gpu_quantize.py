@@ -335,3 +335,40 @@ def test_side_stream_matches_default_stream():
     assert torch.equal(q1.codes, q2.codes)
     assert not torch.equal(q1.codes, q3.codes)
     assert torch.equal(q1.scales, q3.scales)
+
+
+def test_side_stream_temporaries_outlive_the_call():
+    """stream= without entering a stream context: the binding's workspaces and default outputs
+    must belong to that stream. The side stream is held back by a sleep kernel so its kernels
+    run after the call has returned and the workspace has been freed; the default stream then
+    allocates buffers of the same sizes and fills them with garbage before anything is
+    synchronized. Results must still equal the oracle (quantize's partial maxima live in its
+    workspace; the BF16 GEMM's K-split halves live in its workspace)."""
+    log("side stream temporaries")
+    x_bits = _bits((512, 1024), 93)
+    w_bits = _bits((320, 1024), 94)
+    x_dev, w_dev = to_device_bf16(x_bits), to_device_bf16(w_bits)
+    ref_x = oracle.quantize_1x16(f32(x_bits), "sr", seed=11, offset=4)
+    ref_w = oracle.quantize_16x16(f32(w_bits))
+    qx0, _ = nv.quantize(x_dev, "1x16", "sr", seed=11, offset=4)
+    qw0, _ = nv.quantize(w_dev, "16x16", "rn")
+    d_ref = nv.gemm_ex(qx0, qw0, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    for _ in range(3):
+        with torch.cuda.stream(side):
+            torch.cuda._sleep(100_000_000)                  # tens of milliseconds, bounded
+        qx, _ = nv.quantize(x_dev, "1x16", "sr", seed=11, offset=4, stream=side)
+        qw, _ = nv.quantize(w_dev, "16x16", "rn", stream=side)
+        d = nv.gemm_ex(qx, qw, out_dtype=torch.bfloat16, stream=side)
+        junk = [torch.full((n,), 0x7F, dtype=torch.uint8, device="cuda")
+                for n in (nv.workspace_size(nv.OP_QUANTIZE, 512, 1024),
+                          nv.workspace_size(nv.OP_QUANTIZE, 320, 1024),
+                          max(nv.workspace_size(nv.OP_GEMM_EX, 512, 320), 1), 512 * 512, 320 * 512)]
+        side.synchronize()
+        torch.cuda.synchronize()
+        del junk
+        assert_quant_equal(host(qx), ref_x, "side-stream 1x16 SR")
+        assert_quant_equal(host(qw), ref_w, "side-stream 16x16")
+        assert torch.equal(d.cpu(), d_ref.cpu()), "side-stream BF16 GEMM differs"
