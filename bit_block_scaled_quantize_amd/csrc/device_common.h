@@ -9,6 +9,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "rht_exact.h"
+
 #pragma clang fp contract(off)
 
 namespace nvfp4 {
@@ -208,16 +210,38 @@ __device__ __forceinline__ void atomic_max_nonneg(float* p, float v) {
 // The 16-point random-sign Hadamard transform of one block ("Nemotron NVFP4" explainer, "Why
 // 4-bit training normally falls apart - and the three fixes"); the Hadamard kernels apply it
 // along tokens, the rowwise quantization along each row.
-// y[i] = rn32(1/4 * sum_j H[i][j] * s_j * v[j]) via the binary64 butterfly. For BF16 inputs
-// the factor +-1/4 is applied in binary32, where it is exact (a BF16 value times 2^-2 is a
-// multiple of 2^-135, inside binary32's subnormal grid); FP32 inputs take it in binary64.
+// y[i] = rn32(1/4 * sum_j H[i][j] * s_j * v[j]), the exact value rounded once (+0 for an exact
+// zero), in two steps:
+//  * rht16_f64: the butterfly in binary64 on the terms fma(v_j, +-1/4, +0) (exact, and -0
+//    becomes +0, so no step yields -0 and a zero output is +0), rounded once at the end, plus
+//    a range test that proves every step exact;
+//  * rht16_exact, for the blocks the test rejects (values spread over very many binades):
+//    exact integer sums (exact_quarter_sum_at), one output at a time.
+// Range test: every partial sum of the butterfly is a +- sum of a subset of the terms u_j, so it
+// is at most sum |u_j| in magnitude and a multiple of the smallest nonzero term's last-bit
+// weight 2^q; all are binary64 numbers when sum |u_j| < 2^(q + 53). Since v = 1/4 D H y, each
+// |v_j| <= 4 max|y| and sum |u_j| <= 16 max|y|, so max|y| < 2^(q + 49) suffices. With the
+// smallest nonzero exponent field f (1 for subnormals), q = f - 136 for BF16 inputs (8
+// significant bits) and f - 152 for FP32 ones, so the test is max|y| < 2^(f - 87) or 2^(f - 103).
+// max|y| is the maximum of the binary64 results rounded to binary32, within a relative
+// 2^-40 of the exact one even when a step rounded; the factor 1 - 2^-16 on the bound covers it.
+// Bounds past the binary32 range are taken as FLT_MAX (conservative), and an infinite max|y|
+// (a sum beyond the binary32 range) fails the test, so the exact path produces the infinity.
+__device__ __forceinline__ float pow2_or_max(uint32_t biased) {
+  return biased >= 255u ? kFltMax : __uint_as_float(biased << 23);
+}
+
+// Returns true when the range test proves the result exact; bm = max_i |y_i|. `fmin`: the
+// block's smallest nonzero exponent field, 255 for an all-zero block.
 template <typename TIn>
-__device__ __forceinline__ void rht16(const float (&v)[16], uint32_t mask, float (&y)[16]) {
+__device__ __forceinline__ bool rht16_f64(const float (&v)[16], uint32_t mask, uint32_t fmin,
+                                          float (&y)[16], float& bm) {
+  constexpr bool kBf16 = sizeof(TIn) == 2;
   double u[16];
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
-    if constexpr (sizeof(TIn) == 2) u[j] = (double)(v[j] * (((mask >> j) & 1u) ? -0.25f : 0.25f));
-    else u[j] = (double)v[j] * (((mask >> j) & 1u) ? -0.25 : 0.25);
+    if constexpr (kBf16) u[j] = (double)__builtin_fmaf(v[j], ((mask >> j) & 1u) ? -0.25f : 0.25f, 0.0f);
+    else u[j] = __builtin_fma((double)v[j], ((mask >> j) & 1u) ? -0.25 : 0.25, 0.0);
   }
 #pragma unroll
   for (int h = 1; h < 16; h <<= 1) {
@@ -230,8 +254,83 @@ __device__ __forceinline__ void rht16(const float (&v)[16], uint32_t mask, float
       }
     }
   }
+  float m = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) y[i] = (float)u[i];
+  for (int i = 0; i < 16; ++i) {
+    y[i] = (float)u[i];
+    m = fmaxf(m, fabsf(y[i]));
+  }
+  bm = m;
+  return m <= pow2_or_max(kBf16 ? fmin + 40u : fmin + 24u) * 0.9999847412109375f;   // 1 - 2^-16
+}
+
+// Exact outputs of one block (rarely taken; divergent). The block's 16 inputs are parked in this
+// lane's slots of `lds` (the wave's kRhtExactLds floats: slot j of lane l at [j * 64 + l]) and read
+// back one term at a time, so the path holds few registers beyond the outputs; the kernels that
+// contain it keep their register count. Returns max_i |y_i|.
+// WANT_Y = false computes only the maximum (the amax kernels), leaving y untouched.
+constexpr int kRhtExactLds = 16 * 64;
+
+template <bool WANT_Y = true>
+__device__ __forceinline__ float rht16_exact(const float (&v)[16], uint32_t mask, float (&y)[16], float* lds) {
+  const int lane = threadIdx.x & 63;
+  uint32_t signs = 0;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    lds[j * 64 + lane] = v[j];
+    signs |= (__float_as_uint(v[j]) >> 31) << j;
+  }
+  float out[16];
+  if constexpr (WANT_Y) {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) out[k] = 0.0f;          // the binary64 values are not needed here
+  }
+  float m = 0.0f;
+#pragma unroll 1
+  for (uint32_t i = 0; i < 16; ++i) {
+    const float r = exact_quarter_sum_at(lds + lane, 64, signs ^ mask ^ hadamard_row_negatives(i));
+    if constexpr (WANT_Y) {
+#pragma unroll
+      for (uint32_t k = 0; k < 16; ++k) out[k] = (k == i) ? r : out[k];
+    }
+    m = fmaxf(m, fabsf(r));
+  }
+  if constexpr (WANT_Y) {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) y[k] = out[k];
+  }
+  return m;
+}
+
+// Smallest nonzero exponent field (1 for subnormals; 255 if all are zero) from a running
+// minimum of (magnitude << 1) - 1, where zero wraps to all ones. BF16: two values per word,
+// packed 16-bit arithmetic (both halves at once): h * 2 + 0xFFFF drops the sign bit and
+// subtracts one in a single packed multiply-add when the 2 comes from a register the compiler
+// cannot see through (opaque_two; a literal 2 becomes a shift and a separate add). FP32: one
+// value per word.
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ u16x2 opaque_two() {
+  u16x2 two = {2, 2};
+  asm volatile("" : "+v"(two));
+  return two;
+}
+__device__ __forceinline__ u16x2 min_mag_bf16x2(u16x2 acc, uint32_t w, u16x2 two) {
+  const u16x2 h = __builtin_bit_cast(u16x2, w);
+  return __builtin_elementwise_min(acc, (u16x2)(h * two + (unsigned short)0xFFFF));
+}
+__device__ __forceinline__ uint32_t field_from_min_bf16(uint32_t mn) {
+  if (mn == 0xFFFFu) return 255u;
+  const uint32_t f = ((mn + 1u) & 0xFFFFu) >> 8;
+  return f > 1u ? f : 1u;
+}
+__device__ __forceinline__ uint32_t min_field_f32(const float (&v)[16]) {
+  uint32_t mn = 0xFFFFFFFFu;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) mn = min(mn, (__float_as_uint(v[j]) << 1) - 1u);
+  if (mn == 0xFFFFFFFFu) return 255u;
+  const uint32_t f = (mn + 1u) >> 24;
+  return f > 1u ? f : 1u;
 }
 
 // Segment containing `row` for a non-decreasing offset table off[0..nseg] (clamped).

@@ -192,15 +192,21 @@ struct Chunk<uint16_t> {
   __device__ __forceinline__ static int64_t block_of(int lane, int u) {
     return 64 * u + ((lane & 1) << 5) + (lane >> 1);
   }
+  __device__ __forceinline__ void load_group(const uint16_t* xr, int64_t b0, int64_t nb, int lane, int u) {
+    const int64_t g = b0 + 64 * u;
+    if (g + (lane >> 1) < nb) h0[u] = ld_u32x4(xr + g * 16 + lane * 8);
+    if (g + 32 + (lane >> 1) < nb) h1[u] = ld_u32x4(xr + g * 16 + 512 + lane * 8);
+  }
   __device__ __forceinline__ void load(const uint16_t* xr, int64_t b0, int64_t nb, int lane) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t g = b0 + 64 * u;
-      if (g + (lane >> 1) < nb) h0[u] = ld_u32x4(xr + g * 16 + lane * 8);
-      if (g + 32 + (lane >> 1) < nb) h1[u] = ld_u32x4(xr + g * 16 + 512 + lane * 8);
-    }
+    for (int u = 0; u < U; ++u) load_group(xr, b0, nb, lane, u);
   }
   __device__ __forceinline__ void get(int u, int lane, float (&v)[16]) const {
+    uint32_t w[8];
+    get(u, lane, v, w);
+  }
+  // the same, also returning the block's 8 words (element 2i in the low half of word i)
+  __device__ __forceinline__ void get(int u, int lane, float (&v)[16], uint32_t (&w)[8]) const {
     const bool odd = lane & 1;
     v4u32 send = odd ? h0[u] : h1[u], recv;
     recv.x = pair_swap(send.x);
@@ -209,7 +215,8 @@ struct Chunk<uint16_t> {
     recv.w = pair_swap(send.w);
     const v4u32 lo = odd ? recv : h0[u];                 // elements 0..7 of the lane's block
     const v4u32 hi = odd ? h1[u] : recv;                 // elements 8..15
-    const uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    w[0] = lo.x; w[1] = lo.y; w[2] = lo.z; w[3] = lo.w;
+    w[4] = hi.x; w[5] = hi.y; w[6] = hi.z; w[7] = hi.w;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       v[2 * i] = bf16_lo(w[i]);
@@ -223,15 +230,16 @@ struct Chunk<float> {
   static constexpr int U = 2;
   v4f32 q[U][4];
   __device__ __forceinline__ static int64_t block_of(int lane, int u) { return 64 * u + lane; }
+  __device__ __forceinline__ void load_group(const float* xr, int64_t b0, int64_t nb, int lane, int u) {
+    const int64_t b = b0 + block_of(lane, u);
+    if (b < nb) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) q[u][i] = ld_f32x4(xr + b * 16 + 4 * i);
+    }
+  }
   __device__ __forceinline__ void load(const float* xr, int64_t b0, int64_t nb, int lane) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t b = b0 + block_of(lane, u);
-      if (b < nb) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) q[u][i] = ld_f32x4(xr + b * 16 + 4 * i);
-      }
-    }
+    for (int u = 0; u < U; ++u) load_group(xr, b0, nb, lane, u);
   }
   __device__ __forceinline__ void get(int u, int, float (&v)[16]) const {
 #pragma unroll
@@ -243,6 +251,52 @@ struct Chunk<float> {
     }
   }
 };
+
+// The lane's block u of a chunk put through the Hadamard transform (rowwise rotation) by the
+// binary64 butterfly; returns its range test (rht16_f64). The smallest nonzero exponent field
+// comes from the BF16 words with packed 16-bit arithmetic, or from the FP32 values.
+// bm = max_i |y_i|.
+template <typename TIn>
+__device__ __forceinline__ bool rot_block(const Chunk<TIn>& c, int u, int lane, uint32_t mask,
+                                          float (&y)[16], float& bm) {
+  float v[16];
+  uint32_t fmin;
+  if constexpr (sizeof(TIn) == 2) {
+    uint32_t w[8];
+    c.get(u, lane, v, w);
+    u16x2 acc = {0xFFFF, 0xFFFF};
+    const u16x2 two = opaque_two();
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc = min_mag_bf16x2(acc, w[i], two);
+    fmin = field_from_min_bf16(min((uint32_t)acc.x, (uint32_t)acc.y));
+  } else {
+    c.get(u, lane, v);
+    fmin = min_field_f32(v);
+  }
+  return rht16_f64<TIn>(v, mask, fmin, y, bm);
+}
+
+// The blocks of a chunk whose range test failed (bit u of `pending`, per lane), once the chunk's
+// registers are no longer needed: block group u is read again from memory (row pointer xr,
+// first block b0; wave-wide, like the exchange inside get()), the failing lanes compute exact
+// sums and hand them to finish(u, y, bm). Rarely taken; keeps the main path's registers.
+template <bool WANT_Y, typename TIn, typename Finish>
+__device__ __forceinline__ void rot_pending(uint32_t pending, const TIn* xr, int64_t b0, int64_t nb, int lane,
+                                            uint32_t mask, float* lds, Finish finish) {
+  if (!__any(pending != 0)) return;
+#pragma unroll 1
+  for (int u = 0; u < Chunk<TIn>::U; ++u) {
+    if (!__any((pending >> u) & 1u)) continue;
+    Chunk<TIn> c;                                 // group u of the chunk, held as group 0
+    c.load_group(xr, b0 + 64 * u, nb, lane, 0);
+    float v[16], y[16];
+    c.get(0, lane, v);
+    if ((pending >> u) & 1u) {
+      const float bm = rht16_exact<WANT_Y>(v, mask, y, lds);
+      finish(u, y, bm);
+    }
+  }
+}
 
 // ROT: each block is first put through the 16-point random-sign Hadamard transform (sign
 // mask `mask`), the rowwise rotation of the activation gradient of the Mosaic variant's dgrad
@@ -258,6 +312,7 @@ __global__ __launch_bounds__(kThreads) void k_encode_1x16(
   constexpr int U = C::U;
   constexpr int64_t kSpan = 64 * U;            // blocks of a row covered by one chunk
   __shared__ float red[kWavesPerBlock];
+  __shared__ float rexact[ROT ? kWavesPerBlock : 1][ROT ? kRhtExactLds : 1];   // exact transform slots
   const int lane = threadIdx.x & 63;
   const int64_t wave = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
   const int64_t nwaves = (int64_t)gridDim.x * kWavesPerBlock;
@@ -325,19 +380,10 @@ __global__ __launch_bounds__(kThreads) void k_encode_1x16(
     }
     uint2* cr = reinterpret_cast<uint2*>(codes + r * (cols >> 1));
     uint8_t* sr = scales + r * nb;
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      float v[16];
-      cur.get(u, lane, v);                       // all lanes: the exchange is wave-wide
-      if constexpr (ROT) {
-        float y[16];
-        rht16<TIn>(v, mask, y);
-#pragma unroll
-        for (int j = 0; j < 16; ++j) v[j] = y[j];
-      }
+    auto finish = [&](int u, const float (&v)[16], float bm) {
       const int64_t b = b0 + C::block_of(lane, u);
       if (b < nb) {
-        const BlockScale bs = block_scale_table(abs_max16(v), s_enc, tab);
+        const BlockScale bs = block_scale_table(bm, s_enc, tab);
         u32x4 rnd{0, 0, 0, 0};
         if constexpr (SR) rnd = block_random((uint64_t)(r * nb + b), seed, offset);
         uint32_t lo, hi;
@@ -345,7 +391,23 @@ __global__ __launch_bounds__(kThreads) void k_encode_1x16(
         cr[b] = make_uint2(lo, hi);
         sr[b] = (uint8_t)bs.code;
       }
+    };
+    uint32_t pending = 0;                        // ROT: bit u: block u needs exact sums
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float v[16], bm = 0.0f;
+      if constexpr (ROT) {
+        if (!rot_block(cur, u, lane, mask, v, bm)) {
+          pending |= 1u << u;                    // encoded below, after the exact sums
+          continue;
+        }
+      } else {
+        cur.get(u, lane, v);                     // all lanes: the exchange is wave-wide
+        bm = abs_max16(v);
+      }
+      finish(u, v, bm);
     }
+    if constexpr (ROT) rot_pending<true>(pending, x + r * ld, b0, nb, lane, mask, rexact[threadIdx.x >> 6], finish);
     it = it_n;
     b0 = b0_n;
   };
@@ -365,6 +427,7 @@ __global__ __launch_bounds__(kThreads) void k_amax_rot(const TIn* __restrict__ x
   constexpr int U = C::U;
   constexpr int64_t kSpan = 64 * U;
   __shared__ float red[kWavesPerBlock];
+  __shared__ float rexact[kWavesPerBlock][kRhtExactLds];                   // exact transform slots
   const int lane = threadIdx.x & 63;
   const int64_t wave = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
   const int64_t nwaves = (int64_t)gridDim.x * kWavesPerBlock;
@@ -380,13 +443,17 @@ __global__ __launch_bounds__(kThreads) void k_amax_rot(const TIn* __restrict__ x
       r_n = r + nwaves;
     }
     if (r_n < rows) nxt.load(x + r_n * ld, b0_n, nb, lane);
+    auto finish = [&](int u, const float (&)[16], float bm) {
+      if (b0 + C::block_of(lane, u) < nb) m = fmaxf(m, bm);
+    };
+    uint32_t pending = 0;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      float v[16], y[16];
-      cur.get(u, lane, v);
-      rht16<TIn>(v, mask, y);
-      if (b0 + C::block_of(lane, u) < nb) m = fmaxf(m, abs_max16(y));
+      float y[16], bm;
+      if (rot_block(cur, u, lane, mask, y, bm)) finish(u, y, bm);
+      else pending |= 1u << u;
     }
+    rot_pending<false>(pending, x + r * ld, b0, nb, lane, mask, rexact[threadIdx.x >> 6], finish);
     r = r_n;
     b0 = b0_n;
   };

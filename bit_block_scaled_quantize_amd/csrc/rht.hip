@@ -5,11 +5,10 @@
 // quantization, which spreads an outlier over its block, and the rotation cancels inside the
 // GEMM. The rotation acts along the contraction (token) dimension in blocks of 16 tokens:
 // for column c and token block t, y = 1/4 * H16 * diag(s) * x[16t..16t+15, c], with
-// H16[i][j] = (-1)^popcount(i & j) and signs s from a 16-bit mask. The butterfly runs in
-// binary64 (stages h = 1, 2, 4, 8) on inputs pre-multiplied by +-1/4 (exact in binary64, so
-// every intermediate is exactly 1/4 of the unscaled butterfly's), and the result is rounded
-// once to FP32. The 16 outputs of one (column, token block) are exactly one 1x16
-// quantization block of the transposed output [cols, tokens].
+// H16[i][j] = (-1)^popcount(i & j) and signs s from a 16-bit mask, each output the exact
+// value rounded once to FP32 (rht16_f64: a binary64 butterfly where a range test proves it
+// exact; rht16_exact: exact integer sums otherwise). The 16 outputs of one (column, token block)
+// are exactly one 1x16 quantization block of the transposed output [cols, tokens].
 //
 // Layout: a tile is 128 columns x 256 tokens (16 token blocks). Lane l of every wave owns
 // columns 2l and 2l+1, so a wave-wide load of one token row is 64 x 4 bytes (BF16) of
@@ -99,10 +98,12 @@ __global__ __launch_bounds__(kThreads) void k_rht(
   __shared__ int64_t sseg[SEG ? kLdsSeg : 1];     // segment starts (nseg <= kLdsSeg)
   __shared__ float ssenc[SEG && ENCODE ? kLdsSeg : 1];
   __shared__ float sacc[SEG && !ENCODE ? kAccWin : 1];
+  __shared__ float sexact[kWaves][kRhtExactLds];  // the exact transform's per-wave slots
   constexpr bool kBlocked = SEG;                 // contiguous tile range per workgroup
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t nbt = tokens >> 4;
+  const u16x2 two = opaque_two();                  // for the range test's packed minimum
   const int64_t tiles_c = (cols + kTileCols - 1) / kTileCols;
   const int64_t tiles = tiles_c * ((nbt + kTileBlocks - 1) / kTileBlocks);
   const bool paired = (ld & 1) == 0;
@@ -236,25 +237,28 @@ __global__ __launch_bounds__(kThreads) void k_rht(
           m_seg = sgi;
         }
       }
+      // smallest nonzero exponent field of each column's block (the transform's range test)
+      // and, for the amax pair, each column's max|x|: packed 16-bit arithmetic on BF16 words
+      uint32_t fmin[2] = {255u, 255u};
+      float pmax[2] = {0.0f, 0.0f};
+      if constexpr (sizeof(TIn) == 2) {
+        u16x2 acc = {0xFFFF, 0xFFFF}, mag = {0, 0};
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        float v[16], y[16];
-#pragma unroll
-        for (int j = 0; j < 16; ++j) v[j] = cur[j].get(q);
-        float pm = 0.0f;
-        if constexpr (PLAIN) {
-#pragma unroll
-          for (int j = 0; j < 16; ++j) pm = fmaxf(pm, fabsf(v[j]));
+        for (int j = 0; j < 16; ++j) {
+          acc = min_mag_bf16x2(acc, cur[j].w, two);
+          if constexpr (PLAIN)
+            mag = __builtin_elementwise_max(mag, __builtin_bit_cast(u16x2, cur[j].w & 0x7FFF7FFFu));
         }
-        rht16<TIn>(v, mask, y);
-        float bm = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) bm = fmaxf(bm, fabsf(y[i]));
+        fmin[0] = field_from_min_bf16(acc.x);
+        fmin[1] = field_from_min_bf16(acc.y);
+        pmax[0] = __uint_as_float((uint32_t)mag.x << 16);
+        pmax[1] = __uint_as_float((uint32_t)mag.y << 16);
+      }
+      // The block of column c + q: its maximum into the tensor maximum, or its scale and codes
+      // into the tile's LDS staging.
+      auto finish = [&](int q, const float (&y)[16], float bm) {
         if constexpr (!ENCODE) {
-          if (c + q < cols) {
-            m = fmaxf(m, bm);
-            if constexpr (PLAIN) mp = fmaxf(mp, pm);
-          }
+          if (c + q < cols) m = fmaxf(m, bm);
         } else {
           const int64_t row = c + q;                        // output row = input column
           BlockScale bs;
@@ -266,6 +270,41 @@ __global__ __launch_bounds__(kThreads) void k_rht(
           encode16<SR>(y, bs.mult, rnd, lo, hi);
           *reinterpret_cast<uint2*>(&tc[2 * lane + q][bl * 8]) = make_uint2(lo, hi);
           ts[2 * lane + q][bl] = (uint8_t)bs.code;
+        }
+      };
+      uint32_t pending = 0;                                 // bit q: block q needs exact sums
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        float v[16], y[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) v[j] = cur[j].get(q);
+        if constexpr (PLAIN) {
+          float pm = pmax[q];
+          if constexpr (sizeof(TIn) != 2) {
+#pragma unroll
+            for (int j = 0; j < 16; ++j) pm = fmaxf(pm, fabsf(v[j]));
+          }
+          if (c + q < cols) mp = fmaxf(mp, pm);
+        }
+        float bm;
+        if (rht16_f64<TIn>(v, mask, sizeof(TIn) == 2 ? fmin[q] : min_field_f32(v), y, bm)) finish(q, y, bm);
+        else pending |= 1u << q;
+      }
+      if (pending) {
+        // rare (divergent): exact sums for the blocks the range test rejected, once the item's
+        // loaded words are no longer needed; their inputs are read again from memory, so
+        // nothing is kept in registers across the butterflies above for this path.
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          if ((pending >> q) & 1u) {
+            Pair<TIn> again[16];
+            load_item(again, it, k);
+            float v[16], y[16];
+#pragma unroll
+            for (int j = 0; j < 16; ++j) v[j] = again[j].get(q);
+            const float bm = rht16_exact<ENCODE>(v, mask, y, sexact[wave]);
+            finish(q, y, bm);
+          }
         }
       }
     }
@@ -330,13 +369,13 @@ int64_t rht_tiles(int64_t tokens, int64_t cols) {
 
 // Workgroups of k_rht<...> that the device keeps resident at once (each walks tiles, so a
 // grid of exactly this many has no second wave of late starters). Queried once per kernel.
-template <typename TIn, bool ENCODE, bool SR, bool SEG>
+template <typename TIn, bool ENCODE, bool SR, bool PLAIN, bool SEG>
 int64_t resident_groups() {
   static const int64_t n = [] {
     int dev = 0, cus = 0, per_cu = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_rht<TIn, ENCODE, SR, false, SEG>, kThreads, 0) !=
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_rht<TIn, ENCODE, SR, PLAIN, SEG>, kThreads, 0) !=
             hipSuccess)
       return (int64_t)1024;
     return (int64_t)(cus > 0 ? cus : 1) * (per_cu > 0 ? per_cu : 1);
@@ -344,15 +383,16 @@ int64_t resident_groups() {
   return n;
 }
 
+// Every form walks tiles with a stride of its grid, so a grid of more workgroups than stay
+// resident would only add a tail of late starters: the grid is capped at the resident count
+// (the amax forms then leave that many partial maxima, at most kMaxPartials).
 template <typename TIn, bool ENCODE, bool SR, bool PLAIN = false, bool SEG = false>
 void launch_rht_t(const void* x, int64_t tokens, int64_t cols, int64_t ld, uint16_t mask,
                   const float* amax, int parts, float* partial, QuantOut out,
-                  const int64_t* segments, int64_t nseg, uint64_t seed, uint64_t offset, int grid,
+                  const int64_t* segments, int64_t nseg, uint64_t seed, uint64_t offset, int& grid,
                   hipStream_t stream) {
-  if (ENCODE) {
-    const int64_t cap = resident_groups<TIn, ENCODE, SR, SEG>();
-    if (grid > cap) grid = (int)cap;
-  }
+  const int64_t cap = resident_groups<TIn, ENCODE, SR, PLAIN, SEG>();
+  if (grid > cap) grid = (int)cap;
   hipLaunchKernelGGL((k_rht<TIn, ENCODE, SR, PLAIN, SEG>), dim3(grid), dim3(kThreads), 0, stream,
                      (const TIn*)x, tokens, cols, ld, (uint32_t)mask, amax, parts, partial,
                      out.codes, out.scales, out.global_scale, segments, nseg, seed, offset);
@@ -364,7 +404,7 @@ hipError_t launch_rht_amax_parts(const void* x, bool fp32, int64_t tokens, int64
                                  uint16_t sign_mask, bool plain, const int64_t* segments,
                                  int64_t nseg, float* partial, int* parts, hipStream_t stream) {
   const int64_t tiles = rht_tiles(tokens, cols);
-  const int grid = (int)(tiles < 1 ? 1 : (tiles < kMaxPartials ? tiles : kMaxPartials));
+  int grid = (int)(tiles < 1 ? 1 : (tiles < kMaxPartials ? tiles : kMaxPartials));
   const QuantOut none{nullptr, nullptr, nullptr};
   if (segments) {                                 // per-segment maxima straight into partial[nseg]
     hipError_t e = launch_fill(partial, nseg, 0.0f, stream);
@@ -387,7 +427,7 @@ hipError_t launch_rht_encode(const void* x, bool fp32, int64_t tokens, int64_t c
                              const int64_t* segments, int64_t nseg, const float* amax, int parts,
                              QuantOut out, hipStream_t stream) {
   const int64_t tiles = rht_tiles(tokens, cols);
-  const int grid = (int)(tiles < 1 ? 1 : (tiles < (1 << 30) ? tiles : (1 << 30)));   // capped at launch
+  int grid = (int)(tiles < 1 ? 1 : (tiles < (1 << 30) ? tiles : (1 << 30)));   // capped at launch
 #define NVFP4_RE(T, S, G) launch_rht_t<T, true, S, false, G>(x, tokens, cols, ld, sign_mask, amax, parts, nullptr, out, segments, nseg, seed, offset, grid, stream)
   const bool seg = segments != nullptr;
   if (fp32) {

@@ -135,7 +135,9 @@ int nvfp4_quantize(const void* x, nvfp4_dtype dt, int64_t rows, int64_t cols, in
  *   sign_mask  bit j set => sign -1 on element j of every 16-token block. Both operands of
  *              one wgrad GEMM must use the same mask so that the transform cancels.
  *   transform  for column c and block t: y_i = rn32(1/4 * sum_j H[i][j] s_j x[16t+j, c]),
- *              H[i][j] = (-1)^popcount(i & j), evaluated as the 4-stage binary64 butterfly.
+ *              H[i][j] = (-1)^popcount(i & j): the exact sum rounded once to FP32 (nearest,
+ *              ties to even), +0 for an exactly zero sum, for every input (blocks of any
+ *              exponent spread; a sum beyond the FP32 range gives infinity).
  *   out        tensor [cols, tokens]: row c holds column c's transformed values quantized in
  *              1x16 blocks along tokens (out->rows == cols, out->cols == tokens).
  *   rnd/seed/offset as for nvfp4_quantize (SR block index is over the output [cols, tokens]).
@@ -324,15 +326,24 @@ int nvfp4_amax_pair(const void* x, nvfp4_dtype dt, int64_t tokens, int64_t cols,
                     uint16_t sign_mask, float* amax_out, void* workspace, size_t ws_bytes,
                     void* hip_stream);
 
-/* Bytes of device workspace `op` needs for the given shape (0 if none). */
+/* Bytes of device workspace `op` needs for the given shape (0 if none). The library allocates
+ * no memory itself (caller-owned buffers, see the conventions above), so the partial maxima of
+ * the tensor amax (the FP32 tensor scale of "Nemotron NVFP4" explainer, "What NVFP4 actually
+ * is") and the K-split partial sums of nvfp4_gemm_ex live in a workspace the caller sizes with
+ * this call. ops: nvfp4_op; rows/cols/nseg as in the call the workspace is for. */
 size_t nvfp4_workspace_size(int op, int64_t rows, int64_t cols, int64_t nseg);
 
-/* Thread-local description of the last non-OK status returned on this thread. */
+/* Thread-local description of the last non-OK status returned on this thread: the error
+ * behaviour shared by every entry point (host validation before anything is enqueued). The
+ * string stays valid until the thread's next failing call. */
 const char* nvfp4_last_error(void);
 
 /*
- * nvfp4_dequantize - test helper: y[r, c] = rn32(e2m1 * e4m3 * global_scale[segment(r)]),
- * y FP32 [rows, cols] contiguous. segments as for nvfp4_quantize (NULL, nseg = 1 allowed).
+ * nvfp4_dequantize - test helper: the decoded value of every element, the two-level scale of
+ * "Nemotron NVFP4" explainer, "What NVFP4 actually is" (E2M1 element times its block's E4M3
+ * scale times the tensor's FP32 scale): y[r, c] = rn32(e2m1 * e4m3 * global_scale[segment(r)])
+ * (e2m1 * e4m3 is exact), y FP32 [rows, cols] contiguous. segments as for nvfp4_quantize
+ * (NULL, nseg = 1 allowed). Errors: NVFP4_ERR_INVALID (null pointers, shapes), NVFP4_ERR_HIP.
  */
 int nvfp4_dequantize(const nvfp4_tensor* q, const int64_t* segments, int64_t nseg, float* y,
                      void* hip_stream);

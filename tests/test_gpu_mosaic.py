@@ -50,8 +50,8 @@ def test_rows_rht_quantize_fp32_strided(mask):
 
 
 def test_rows_rht_every_bf16_pattern_blocks():
-    # every finite BF16 pattern (any exponent spread inside a block: both sides run the same
-    # binary64 butterfly, so the rounding of wide-spread blocks is shared too)
+    # every finite BF16 pattern, 16 random ones per block: blocks of any exponent spread, most
+    # beyond binary64's exact range, against the oracle's correctly rounded transform
     u = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
     u = u[((u >> 7) & 0xFF) != 0xFF]
     n = len(u) // 256 * 256
@@ -83,3 +83,26 @@ def test_mosaic_dgrad_gemm(mnk):
     assert_gemm_within_bound(got, ah, bh, f"mosaic dgrad {mnk}")
     ref = f32(dy_bits).astype(np.float64) @ f32(w_bits).astype(np.float64)
     assert np.linalg.norm(got - ref) / np.linalg.norm(ref) < 0.2
+
+
+@pytest.mark.parametrize("rounding", ["rn", "sr"])
+def test_rows_rht_wide_spreads(rounding):
+    """Rowwise transform of blocks of any exponent spread: BF16 (rows of the spread
+    generator's columns), FP32 with 23-bit mantissas, and the corner blocks as rows."""
+    mask = 0x6E04
+    bf = np.ascontiguousarray(workloads.exponent_spread_bf16(256, 64, 81).T)      # [64, 256]
+    corner = workloads.hadamard_edge_blocks_bf16(6).reshape(-1, 16)
+    corner = corner[~((corner & 0x7FFF) >= 0x7F00).any(axis=1)]
+    corner = corner[: len(corner) // 4 * 4].reshape(-1, 64)                          # 4 blocks per row
+    fp = np.ascontiguousarray(workloads.exponent_spread_f32(128, 48, 82).T)         # [48, 128]
+    for name, dev, host_x in (("bf16 spread", to_device_bf16(bf), f32(bf)),
+                              ("corner rows", to_device_bf16(corner), f32(corner)),
+                              ("fp32 spread", to_device_f32(fp), fp)):
+        log(f"rows rht {name} {rounding}")
+        q = nv.rht_rows_quantize(dev, mask, rounding, seed=7, offset=3)
+        assert_quant_equal(host(q), oracle.rht_rowwise_quantize(host_x, mask, rounding, seed=7, offset=3),
+                           f"rows rht {name} {rounding}")
+        a = nv.amax(dev, rht=2, sign_mask=mask)
+        torch.cuda.synchronize()
+        want = oracle.amax(oracle.rht_rowwise(host_x, mask))
+        assert_bytes_equal(a.cpu().numpy().view(np.uint32), want.view(np.uint32), f"rotated amax {name}")

@@ -146,8 +146,10 @@ def test_rht_quantize(shape, rounding):
 
 @pytest.mark.parametrize("rounding", ["rn", "sr"])
 def test_rht_exponent_spread(rounding):
-    """Blocks on both sides of the binary32 fast path's range test, plus zeros, subnormals
-    and fields up to 251, bit-exact against the oracle."""
+    """Blocks of every exponent spread up to the whole BF16 range (each side of the range
+    tests of the binary32 and binary64 butterflies, and the exact path beyond), plus zeros,
+    subnormals and fields up to 251, bit-exact against the oracle's correctly rounded
+    transform."""
     log(f"rht exponent spread {rounding}")
     bits = workloads.exponent_spread_bf16(512, 272, 77)
     x = f32(bits)
@@ -158,6 +160,59 @@ def test_rht_exponent_spread(rounding):
     a = nv.amax(to_device_bf16(bits), rht=True, sign_mask=mask)
     torch.cuda.synchronize()
     assert a.cpu().numpy()[0] == oracle.amax(oracle.rht_columnwise(x, mask))[0]
+
+
+@pytest.mark.parametrize("rounding", ["rn", "sr"])
+def test_rht_exponent_spread_fp32(rounding):
+    """FP32 inputs with 23-bit mantissas and exponent spreads up to the whole range (the
+    binary64 butterfly is exact only up to about 25 binades): bit-exact, amax too."""
+    log(f"rht fp32 exponent spread {rounding}")
+    x = workloads.exponent_spread_f32(256, 144, 79)
+    mask = 0x6E04
+    q = nv.rht_quantize(to_device_f32(x), mask, rounding, seed=0x5EED, offset=11)
+    ref = oracle.rht_quantize(x, mask, rounding, seed=0x5EED, offset=11)
+    assert_quant_equal(host(q), ref, f"rht fp32 spread {rounding}")
+    a = nv.amax(to_device_f32(x), rht=True, sign_mask=mask)
+    torch.cuda.synchronize()
+    assert a.cpu().numpy()[0] == oracle.amax(oracle.rht_columnwise(x, mask))[0]
+
+
+def _corner_block_columns(finite_only: bool):
+    """The hand-made corner blocks as the columns of a [16, n] BF16 tensor; without the
+    blocks whose transform exceeds the binary32 range when finite_only."""
+    blocks = workloads.hadamard_edge_blocks_bf16(5).reshape(-1, 16)
+    if finite_only:
+        big = ((blocks & 0x7FFF) >= 0x7F00).any(axis=1)
+        blocks = blocks[~big]
+    return np.ascontiguousarray(blocks.T)
+
+
+@pytest.mark.parametrize("rounding", ["rn", "sr"])
+def test_rht_corner_blocks(rounding):
+    """Ties broken by terms 46+ binades below, exact ties next to cancelling far terms, sums
+    one to three bits wider than binary64, all-zero blocks with -0 inputs (their outputs are
+    +0, so codes carry no sign), subnormals, one block per exponent field: bit-exact for
+    several sign masks."""
+    bits = _corner_block_columns(finite_only=True)
+    x = f32(bits)
+    for mask in (0, 0x6E04, 0xFFFF):
+        log(f"rht corner blocks {rounding} mask {mask:#x}")
+        q = nv.rht_quantize(to_device_bf16(bits), mask, rounding, seed=0x5EED, offset=2)
+        ref = oracle.rht_quantize(x, mask, rounding, seed=0x5EED, offset=2)
+        assert_quant_equal(host(q), ref, f"rht corner blocks {rounding} {mask:#x}")
+
+
+def test_rht_corner_blocks_per_block_amax():
+    """max|y| of each corner block alone, including blocks whose transform is beyond the
+    binary32 range (infinite maximum), against the oracle."""
+    bits = _corner_block_columns(finite_only=False)
+    mask = 0x6E04
+    want = np.abs(oracle.rht_columnwise(f32(bits), mask)).reshape(bits.shape[1], 16).max(axis=1)
+    got = np.empty_like(want)
+    for c in range(bits.shape[1]):
+        col = np.ascontiguousarray(bits[:, c:c + 1])
+        got[c] = nv.amax(to_device_bf16(col), rht=True, sign_mask=mask).cpu().numpy()[0]
+    assert_bytes_equal(got.view(np.uint32), want.astype(np.float32).view(np.uint32), "corner block amax")
 
 
 def test_rht_exponent_spread_per_block_amax():
@@ -225,12 +280,15 @@ def test_16x16_segments_with_transpose(n, k, G):
 
 @pytest.mark.parametrize("rounding", ["rn", "sr"])
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
-def test_rht_quantize_token_segments(rounding, dtype):
+@pytest.mark.parametrize("data", ["gauss", "spread"])
+def test_rht_quantize_token_segments(rounding, dtype, data):
     """The expert-segmented transform-and-quantize (MoE weight gradient): one tensor scale per
     token range (an empty range included), bit-exact against the oracle; the segmented amax
-    of the transformed tensor too."""
-    log(f"rht segments {rounding} {dtype}")
-    bits = workloads.with_outliers_bf16((512, 272), 95)
+    of the transformed tensor too. Gaussian inputs with outliers, or blocks of any exponent
+    spread."""
+    log(f"rht segments {rounding} {dtype} {data}")
+    bits = (workloads.with_outliers_bf16((512, 272), 95) if data == "gauss"
+            else workloads.exponent_spread_bf16(512, 272, 97))
     x = f32(bits)
     mask = workloads.wgrad_sign_mask()
     seg = np.array([0, 48, 48, 160, 496, 512], np.int64)
