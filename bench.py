@@ -597,16 +597,44 @@ def reference_gemm(torch, dev, stream):
     return res
 
 
+def _oracle_tiny_step():
+    """The whole step of the tiny 256 x 256 x 256 layer through the oracle, timed in full (no
+    sampling): tensor maxima, X 1x16 RN, W 16x16 RN and W^T, dY 1x16 SR, both Hadamard
+    operands, and the three FP64 GEMMs of the dequantized operands."""
+    import oracle
+    import workloads
+    f32 = workloads.bf16_bits_to_f32
+    a_bits, w_bits = workloads.tiny()
+    x, w = f32(a_bits), f32(w_bits)
+    dy = f32(workloads.normal_bf16((256, 256), workloads.SEEDS["dgrad_dy"], std=1e-3))
+    mask = workloads.wgrad_sign_mask()
+    t0 = time.perf_counter()
+    deq = oracle.dequantize
+    xq = oracle.quantize_1x16(x)
+    wq = oracle.quantize_16x16(w)
+    wtq = oracle.quantize_16x16(np.ascontiguousarray(w.T))
+    dyq = oracle.quantize_1x16(dy, "sr", seed=workloads.SR_SEED_DGRAD, offset=0)
+    hdy = oracle.rht_quantize(dy, mask, "sr", seed=workloads.SR_SEED_WGRAD, offset=workloads.SR_OFFSET_WGRAD)
+    hx = oracle.rht_quantize(x, mask, "rn")
+    oracle.gemm_fp64(deq(*xq), deq(*wq))
+    oracle.gemm_fp64(deq(*dyq), deq(*wtq))
+    oracle.gemm_fp64(deq(*hdy), deq(*hx))
+    return time.perf_counter() - t0
+
+
 def cpu_baseline(x_bits, w_bits, dy_bits, mask, step_flops):
-    """The oracle (numpy; BLAS dgemm for the FP64 reference GEMM) timed on a bounded sample
-    of the same step, scaled to the whole step."""
+    """The oracle (numpy; BLAS dgemm for the FP64 reference GEMM) on the machine's host: timed on a
+    bounded sample of the same step and scaled to the whole step (value), and timed in full on
+    the tiny 256^3 layer (tiny_full, no extrapolation)."""
     import oracle
     import workloads
     try:
         from threadpoolctl import threadpool_info
         blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
-        blas_threads = os.cpu_count() or 1
+        blas_threads = None
+    tiny_s = min(_oracle_tiny_step() for _ in range(3))
+    tiny_flops = 3 * 2 * 256 ** 3
     f32 = workloads.bf16_bits_to_f32
     rng = np.random.default_rng(0)
     parts = []
@@ -648,12 +676,17 @@ def cpu_baseline(x_bits, w_bits, dy_bits, mask, step_flops):
     sampled_s = float(sum(t for t in sample_times))
     total_s = float(sum(parts))
     return {"value": round(step_flops / total_s / 1e12, 6), "unit": "TFLOP/s",
-            "cores": int(blas_threads), "kind": "oracle",
+            "cores": int(os.cpu_count() or 1), "blas_threads": blas_threads, "kind": "oracle",
             "sample": f"oracle on {rows} rows of X and of W, {dy_rows} rows of dY, {cols} columns of "
                       f"each Hadamard operand and {g_rows} output rows of each FP64 GEMM "
-                      f"({sampled_s:.1f} s measured), scaled to the full step "
-                      f"(estimated {total_s:.1f} s per step; numpy elementwise on 1 core, "
-                      f"BLAS on {blas_threads} threads)"}
+                      f"({sampled_s:.1f} s measured), scaled to the full step: an estimate "
+                      f"({total_s:.1f} s per step; numpy elementwise on 1 core, BLAS on "
+                      f"{blas_threads} threads)",
+            "tiny_full": {"seconds": round(tiny_s, 4),
+                          "value": round(tiny_flops / tiny_s / 1e12, 9), "unit": "TFLOP/s",
+                          "what": "the whole oracle step of the 256x256x256 layer (maxima, X 1x16, "
+                                  "W 16x16 and W^T, dY SR, both Hadamard operands, three FP64 "
+                                  "GEMMs), measured in full, best of 3"}}
 
 
 if __name__ == "__main__":

@@ -9,7 +9,8 @@ call into libnvfp4, the wrapper only orders the calls and holds the buffers:
             W [out, in]       -> 16x16, nearest, + W^T   -> Wq, WqT
             Y = Xq Wq^T, stored in BF16, with max|Y| from the GEMM epilogue (so the next
             layer's input quantization is a single pass: pass it as ``x_amax``)
-  backward  dY [T, out]       -> max|dY| and max|H dY| from one read (amax pair)
+  backward  dY [T, out]       -> max|dY| and max|H dY| from one read (amax pair); BF16 or
+            FP32 gradients are quantized as they are
             dY -> 1x16, stochastic rounding                   -> dYq
             dX = dYq WqT^T, stored in BF16
             dY, X -> 16-point random-sign Hadamard transform along tokens, then 1x16 along
@@ -62,7 +63,10 @@ class _LinearFn(torch.autograd.Function):
     def backward(ctx, dy):
         layer = ctx.layer
         (t,) = ctx.saved_tensors
-        g = dy.reshape(-1, dy.shape[-1]).to(torch.bfloat16).contiguous()
+        g = dy.reshape(-1, dy.shape[-1])
+        if g.dtype not in (torch.bfloat16, torch.float32):
+            g = g.float()                                    # exact widening; FP32 goes in as is
+        g = g.contiguous()
         pair = amax_pair(g, layer.sign_mask)                 # max|dY|, max|H dY| from one read
         qdy, _ = quantize(g, "1x16", "sr", seed=layer.seed, offset=2 * ctx.call, amax=pair[0:1])
         dx = gemm_ex(qdy, ctx.qwt, out_dtype=torch.bfloat16)
@@ -76,7 +80,8 @@ class _LinearFn(torch.autograd.Function):
         if layer.main_grad is not None:
             gemm_ex(qhdy, qhx, out=layer.main_grad, accumulate=True)
         else:
-            dw = gemm_ex(qhdy, qhx).to(ctx.weight_dtype)
+            out_dtype = ctx.weight_dtype if ctx.weight_dtype in (torch.bfloat16, torch.float32) else torch.float32
+            dw = gemm_ex(qhdy, qhx, out_dtype=out_dtype).to(ctx.weight_dtype)   # rounded in the epilogue
         return dx.view(ctx.x_shape), dw, None, None
 
 
