@@ -146,13 +146,14 @@ def quantize_1x16(x, rounding: str = "rn", seed: int = 0, offset: int = 0, segme
 
 
 def quantize_1x16_colsegments(x, col_segments, rounding: str = "rn", seed: int = 0,
-                              offset: int = 0, amax_vals=None):
+                              offset: int = 0, amax_vals=None, row_ids=None):
     """1x16 quantization of x[rows, cols] along cols with one tensor scale per range of
     columns (R16): columns col_segments[g]..col_segments[g+1] (multiples of 16, covering
     [0, cols]) use amax_vals[g], by default their own max|x|. This is the transposed
     weight-gradient operand of an expert layer, whose columns are the tokens routed to each
     expert. The stochastic-rounding block index is the block's place in the whole tensor,
-    as in quantize_1x16. Returns (codes [rows, cols/2], scales [rows, cols/16], s_dec [G])."""
+    as in quantize_1x16; x may be a subset of the tensor's rows given by ``row_ids`` (then
+    amax_vals must be given). Returns (codes [rows, cols/2], scales [rows, cols/16], s_dec [G])."""
     x = _as_f32(x)
     rows, cols = x.shape
     seg = np.asarray(col_segments, dtype=np.int64)
@@ -160,6 +161,8 @@ def quantize_1x16_colsegments(x, col_segments, rounding: str = "rn", seed: int =
         raise ValueError("column segments must be multiples of 16 covering [0, cols]")
     G = len(seg) - 1
     if amax_vals is None:
+        if row_ids is not None:
+            raise ValueError("a row subset needs the full tensor's amax_vals")
         a_t = np.array([np.abs(x[:, seg[g]:seg[g + 1]]).max() if seg[g + 1] > seg[g] else 0.0
                         for g in range(G)], dtype=F32)
     else:
@@ -172,7 +175,8 @@ def quantize_1x16_colsegments(x, col_segments, rounding: str = "rn", seed: int =
     s_enc_b = np.tile(s_enc[gid], rows)
     rbytes = None
     if rounding == "sr":
-        bidx = np.arange(rows * nb, dtype=np.int64)
+        rid = np.arange(rows, dtype=np.int64) if row_ids is None else np.asarray(row_ids, np.int64)
+        bidx = (rid[:, None] * nb + np.arange(nb, dtype=np.int64)[None, :]).reshape(-1)
         rbytes = block_random_bytes(bidx, seed, offset)
     codes, S = _encode_blocks(xb, a_b, s_enc_b, rounding, rbytes)
     return pack_nibbles(codes.reshape(rows, cols)), S.reshape(rows, nb), s_dec

@@ -1,9 +1,15 @@
 """GPU parity at the full workload sizes, through the calls and launch configurations the bench
-times: the dense layer (tokens 8192, in 5120, out 20480) and the expert layer (128 experts,
-98304 routed rows, hidden 2688, expert FFN 1856). Quantized rows and columns are compared
-bit for bit with the oracle on seeded samples (the oracle quantizes just those rows with the
-full tensor's amax, which it computes itself), tensor maxima in full, and GEMM outputs on
-sampled elements against the FP64 dot product of the oracle's own quantized rows."""
+times: the dense layer (tokens 8192, in 5120, out 20480: fprop, dgrad with stochastic rounding,
+wgrad with the Hadamard transform) and the expert layer (128 experts, 98304 routed rows, hidden
+2688, expert FFN 1856: forward, and the backward on the padded token layout). Every byte of
+every quantized operand (codes, block scales, tensor scales) is compared with the oracle, and
+every element of every GEMM output with the bound 1e-5 * sum |a||b| around the FP64 product of
+the oracle's dequantized operands (BLAS dgemm, row chunks). The oracle runs on row or column
+chunks in a thread pool (numpy releases the interpreter lock inside its array operations), sized
+to the host's CPU share."""
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import pytest
 import torch
@@ -16,13 +22,85 @@ from helpers import assert_bytes_equal, f32, host, log, to_device_bf16
 pytestmark = pytest.mark.gpu
 
 M, K_IN, N_OUT = 8192, 5120, 20480
-SAMPLE = 48
+WORKERS = max(1, min(16, os.cpu_count() or 1))
 
 
 @pytest.fixture(autouse=True)
 def _need_gpu():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
+
+
+def _ranges(n, parts, align=16):
+    step = max(align, (n + parts - 1) // parts // align * align)
+    return [(a, min(n, a + step)) for a in range(0, n, step)]
+
+
+def _pmap(fn, items):
+    with ThreadPoolExecutor(WORKERS) as ex:
+        return list(ex.map(fn, items))
+
+
+def _cat(parts, i):
+    return np.concatenate([p[i] for p in parts], axis=0)
+
+
+def _q1x16(x, rounding="rn", seed=0, offset=0, segments=None, amax_vals=None):
+    """oracle.quantize_1x16 of the whole tensor, row chunks in parallel (the block index of SR
+    and the segment of a row come from row_ids, so chunks give the full tensor's bytes)."""
+    a = oracle.amax(x, segments) if amax_vals is None else amax_vals
+    parts = _pmap(lambda r: oracle.quantize_1x16(x[r[0]:r[1]], rounding, seed, offset, segments, a,
+                                                 np.arange(r[0], r[1])), _ranges(len(x), 4 * WORKERS))
+    return _cat(parts, 0), _cat(parts, 1), oracle.global_scales(a)[1]
+
+
+def _q16x16(x, segments=None, amax_vals=None):
+    a = oracle.amax(x, segments) if amax_vals is None else amax_vals
+    parts = _pmap(lambda r: oracle.quantize_16x16(x[r[0]:r[1]], segments, a, np.arange(r[0], r[1])),
+                  _ranges(len(x), 4 * WORKERS))
+    return _cat(parts, 0), _cat(parts, 1), oracle.global_scales(a)[1]
+
+
+def _rht(x, mask):
+    """The transformed tensor y [cols, tokens] (oracle), column chunks in parallel."""
+    parts = _pmap(lambda r: oracle.rht_columnwise(x[:, r[0]:r[1]], mask), _ranges(x.shape[1], 4 * WORKERS, 1))
+    return np.concatenate(parts, axis=0)
+
+
+def _deq(q, segments=None):
+    """oracle.dequantize in row chunks (float64)."""
+    codes, scales, s_dec = q
+    parts = _pmap(lambda r: oracle.dequantize(codes[r[0]:r[1]], scales[r[0]:r[1]], s_dec, segments,
+                                              np.arange(r[0], r[1])), _ranges(len(codes), 4 * WORKERS))
+    return np.concatenate(parts, axis=0)
+
+
+def _same(gpu, ref, what):
+    codes, scales, gs = gpu
+    assert_bytes_equal(codes, ref[0], what + " codes")
+    assert_bytes_equal(scales, ref[1], what + " scales")
+    assert_bytes_equal(gs.view(np.uint32), np.asarray(ref[2], np.float32).view(np.uint32), what + " tensor scales")
+
+
+def _gemm_in_bound(d_gpu, a_hat, b_hat, what, chunk=1024):
+    """Every element of d_gpu [M, N] (a GPU tensor) against a_hat @ b_hat^T in FP64 within
+    1e-5 * |a_hat| @ |b_hat|^T."""
+    b_abs = np.abs(b_hat)
+    worst = 0.0
+    for r0 in range(0, a_hat.shape[0], chunk):
+        r1 = min(a_hat.shape[0], r0 + chunk)
+        a = a_hat[r0:r1]
+        ref = a @ b_hat.T
+        bound = 1e-5 * (np.abs(a) @ b_abs.T)
+        got = d_gpu[r0:r1].float().cpu().numpy().astype(np.float64)
+        err = np.abs(got - ref)
+        bad = err > bound
+        if bad.any():
+            i, j = np.argwhere(bad)[0]
+            raise AssertionError(f"{what}: {int(bad.sum())} elements out of bound; first [{r0 + i}, {j}]: "
+                                 f"gpu {got[i, j]!r} ref {ref[i, j]!r} bound {bound[i, j]!r}")
+        worst = max(worst, float((err / np.maximum(bound, 1e-300)).max()))
+    log(f"{what}: every element within bound (largest error {worst:.3g} of the bound)")
 
 
 @pytest.fixture(scope="module")
@@ -32,36 +110,10 @@ def dense():
     return f32(x_bits), f32(w_bits), f32(dy_bits), x_bits, w_bits, dy_bits
 
 
-def _rows_equal(gpu, ref, rows, what):
-    codes, scales, gs = gpu
-    assert_bytes_equal(codes[rows], ref[0], what + " codes")
-    assert_bytes_equal(scales[rows], ref[1], what + " scales")
-    assert_bytes_equal(gs.view(np.uint32), np.asarray(ref[2], np.float32).view(np.uint32), what + " scale")
-
-
-def _rht_amax(x, mask, chunk=1024):
-    """max |H x| over the whole tensor, column chunk by column chunk (oracle transform)."""
-    m = np.float32(0)
-    for c in range(0, x.shape[1], chunk):
-        m = max(m, np.abs(oracle.rht_columnwise(x[:, c:c + chunk], mask)).max())
-    return np.float32(m)
-
-
-def _check_samples(d, pick, a_rows, b_rows, what):
-    """d: GPU output; pick: (m, n) pairs; a_rows(m) / b_rows(n): the oracle's dequantized row."""
-    for m_, n_ in pick:
-        a, b = a_rows(m_), b_rows(n_)
-        ref = float(np.dot(a, b))
-        bound = 1e-5 * float(np.dot(np.abs(a), np.abs(b)))
-        got = float(d[m_, n_])
-        assert abs(got - ref) <= bound, f"{what} [{m_}, {n_}]: gpu {got!r} ref {ref!r} bound {bound!r}"
-
-
 def test_dense_layer_full_size(dense):
     x, w, dy, x_bits, w_bits, dy_bits = dense
     mask = workloads.wgrad_sign_mask()
-    rng = np.random.default_rng(2024)
-    log("dense layer full size: quantize")
+    log("dense layer full size: GPU quantize")
     X, W, dY = to_device_bf16(x_bits), to_device_bf16(w_bits), to_device_bf16(dy_bits)
     ax, ady = nv.amax_pair(X, mask), nv.amax_pair(dY, mask)
     qx, _ = nv.quantize(X, "1x16", "rn", amax=ax[0:1])
@@ -71,92 +123,102 @@ def test_dense_layer_full_size(dense):
                            amax=ady[1:2])
     qhx = nv.rht_quantize(X, mask, "rn", amax=ax[1:2])
     torch.cuda.synchronize()
-    # tensor maxima, in full
+    del X, W, dY
+
+    log("dense layer full size: oracle X, W, W^T, dY")
     a_x, a_w, a_dy = oracle.amax(x), oracle.amax(w), oracle.amax(dy)
-    h_x, h_dy = _rht_amax(x, mask), _rht_amax(dy, mask)
-    assert_bytes_equal(ax.cpu().numpy().view(np.uint32), np.array([a_x[0], h_x], np.float32).view(np.uint32), "pair X")
-    assert_bytes_equal(ady.cpu().numpy().view(np.uint32), np.array([a_dy[0], h_dy], np.float32).view(np.uint32), "pair dY")
-    # sampled rows / columns, bit for bit
-    rx = np.sort(rng.choice(M, SAMPLE, replace=False))
-    g16 = np.sort(rng.choice(N_OUT // 16, 8, replace=False))
-    rw = (g16[:, None] * 16 + np.arange(16)).reshape(-1)
-    gt16 = np.sort(rng.choice(K_IN // 16, 8, replace=False))
-    cw = (gt16[:, None] * 16 + np.arange(16)).reshape(-1)                    # rows of W^T
-    cdy = np.sort(rng.choice(N_OUT, SAMPLE, replace=False))                  # rows of (H dY)^T
-    cx = np.sort(rng.choice(K_IN, SAMPLE, replace=False))                    # rows of (H X)^T
-    ref_x = oracle.quantize_1x16(x[rx], amax_vals=a_x, row_ids=rx)
-    ref_w = oracle.quantize_16x16(w[rw], amax_vals=a_w, row_ids=rw)
-    ref_wt = oracle.quantize_16x16(np.ascontiguousarray(w[:, cw].T), amax_vals=a_w, row_ids=cw)
-    ref_dy = oracle.quantize_1x16(dy[rx], "sr", seed=workloads.SR_SEED_DGRAD, offset=0, amax_vals=a_dy, row_ids=rx)
-    ref_hdy = oracle.rht_quantize(dy[:, cdy], mask, "sr", seed=workloads.SR_SEED_WGRAD,
-                                  offset=workloads.SR_OFFSET_WGRAD, amax_vals=np.float32(h_dy), col_ids=cdy)
-    ref_hx = oracle.rht_quantize(x[:, cx], mask, "rn", amax_vals=np.float32(h_x), col_ids=cx)
-    gx, gw, gwt, gdy, ghdy, ghx = host(qx), host(qw), host(qwt), host(qdy), host(qhdy), host(qhx)
-    _rows_equal(gx, ref_x, rx, "X")
-    _rows_equal(gw, ref_w, rw, "W")
-    _rows_equal(gwt, ref_wt, cw, "W^T")
-    _rows_equal(gdy, ref_dy, rx, "dY")
-    _rows_equal(ghdy, ref_hdy, cdy, "(H dY)^T")
-    _rows_equal(ghx, ref_hx, cx, "(H X)^T")
+    ref_x = _q1x16(x, amax_vals=a_x)
+    _same(host(qx), ref_x, "X 1x16")
+    ref_w = _q16x16(w, amax_vals=a_w)
+    _same(host(qw), ref_w, "W 16x16")
+    ref_wt = _q16x16(np.ascontiguousarray(w.T), amax_vals=a_w)
+    _same(host(qwt), ref_wt, "W^T 16x16")
+    ref_dy = _q1x16(dy, "sr", seed=workloads.SR_SEED_DGRAD, offset=0, amax_vals=a_dy)
+    _same(host(qdy), ref_dy, "dY 1x16 SR")
+    log("dense layer full size: oracle Hadamard operands")
+    y_dy = _rht(dy, mask)
+    h_dy = oracle.amax(y_dy)
+    ref_hdy = _q1x16(y_dy, "sr", seed=workloads.SR_SEED_WGRAD, offset=workloads.SR_OFFSET_WGRAD, amax_vals=h_dy)
+    del y_dy
+    _same(host(qhdy), ref_hdy, "(H dY)^T SR")
+    y_x = _rht(x, mask)
+    h_x = oracle.amax(y_x)
+    ref_hx = _q1x16(y_x, amax_vals=h_x)
+    del y_x
+    _same(host(qhx), ref_hx, "(H X)^T RN")
+    want_ax = np.array([a_x[0], h_x[0]], np.float32)
+    want_ady = np.array([a_dy[0], h_dy[0]], np.float32)
+    assert_bytes_equal(ax.cpu().numpy().view(np.uint32), want_ax.view(np.uint32), "amax pair X")
+    assert_bytes_equal(ady.cpu().numpy().view(np.uint32), want_ady.view(np.uint32), "amax pair dY")
 
     log("dense layer full size: GEMMs")
-    y = nv.gemm(qx, qw)
-    dx = nv.gemm(qdy, qwt)
-    dw = nv.gemm(qhdy, qhx)
-    torch.cuda.synchronize()
-    # the oracle dequantizes its own quantization of each sampled output's operand rows
-    sx_d = dict(zip(rx, oracle.dequantize(*ref_x)))
-    sw_d = dict(zip(rw, oracle.dequantize(*ref_w)))
-    sdy_d = dict(zip(rx, oracle.dequantize(*ref_dy)))
-    swt_d = dict(zip(cw, oracle.dequantize(*ref_wt)))
-    shdy_d = dict(zip(cdy, oracle.dequantize(*ref_hdy)))
-    shx_d = dict(zip(cx, oracle.dequantize(*ref_hx)))
-    pick = lambda rows, cols: [(int(a), int(b)) for a, b in zip(rng.choice(rows, 64), rng.choice(cols, 64))]
-    _check_samples(y.cpu().numpy(), pick(rx, rw), sx_d.__getitem__, sw_d.__getitem__, "fprop")
-    _check_samples(dx.cpu().numpy(), pick(rx, cw), sdy_d.__getitem__, swt_d.__getitem__, "dgrad")
-    _check_samples(dw.cpu().numpy(), pick(cdy, cx), shdy_d.__getitem__, shx_d.__getitem__, "wgrad")
+    y_d = nv.gemm(qx, qw)
+    x_hat, w_hat = _deq(ref_x), _deq(ref_w)
+    _gemm_in_bound(y_d, x_hat, w_hat, "fprop 8192x20480x5120")
+    del y_d, x_hat, w_hat
+    dx_d = nv.gemm(qdy, qwt)
+    dy_hat, wt_hat = _deq(ref_dy), _deq(ref_wt)
+    _gemm_in_bound(dx_d, dy_hat, wt_hat, "dgrad 8192x5120x20480")
+    del dx_d, dy_hat, wt_hat
+    dw_d = nv.gemm(qhdy, qhx)
+    hdy_hat, hx_hat = _deq(ref_hdy), _deq(ref_hx)
+    _gemm_in_bound(dw_d, hdy_hat, hx_hat, "wgrad 20480x5120x8192")
+
+
+def _grouped_in_bound(d_gpu, a_hat, b_hat, off, n, what):
+    """Grouped GEMM: rows off[g]..off[g+1] of d against a_hat rows and b_hat rows g*n..(g+1)*n."""
+    rows = 0
+    for g in range(len(off) - 1):
+        lo, hi = int(off[g]), int(off[g + 1])
+        if hi == lo:
+            continue
+        _gemm_in_bound_quiet(d_gpu[lo:hi], a_hat[lo:hi], b_hat[g * n:(g + 1) * n], f"{what} group {g}")
+        rows += hi - lo
+    log(f"{what}: every element of {rows} rows within bound")
+
+
+def _gemm_in_bound_quiet(d_gpu, a_hat, b_hat, what, chunk=2048):
+    b_abs = np.abs(b_hat)
+    for r0 in range(0, a_hat.shape[0], chunk):
+        a = a_hat[r0:r0 + chunk]
+        ref = a @ b_hat.T
+        bound = 1e-5 * (np.abs(a) @ b_abs.T)
+        got = d_gpu[r0:r0 + chunk].float().cpu().numpy().astype(np.float64)
+        bad = np.abs(got - ref) > bound
+        if bad.any():
+            i, j = np.argwhere(bad)[0]
+            raise AssertionError(f"{what}: {int(bad.sum())} out of bound; first [{r0 + i}, {j}]: "
+                                 f"gpu {got[i, j]!r} ref {ref[i, j]!r} bound {bound[i, j]!r}")
 
 
 def test_moe_layer_full_size():
-    log("moe full size")
+    log("moe full size: GPU")
     x_bits, w_bits, off = workloads.moe()
     G, n, k = workloads.MOE_EXPERTS, workloads.MOE_FFN, workloads.MOE_HIDDEN
-    x, w = f32(x_bits), f32(w_bits)
-    rng = np.random.default_rng(77)
     offd = torch.from_numpy(off).cuda()
     wseg = np.arange(G + 1, dtype=np.int64) * n
     qx, _ = nv.quantize(to_device_bf16(x_bits), "1x16", "rn", segments=offd)
-    qw, _ = nv.quantize(to_device_bf16(w_bits), "16x16", "rn", segments=torch.from_numpy(wseg).cuda())
+    qw, qwt = nv.quantize(to_device_bf16(w_bits), "16x16", "rn", emit_transposed=True,
+                          segments=torch.from_numpy(wseg).cuda())
     d = nv.grouped_gemm(offd, qx, qw, n)
     torch.cuda.synchronize()
+    log("moe full size: oracle X, W, W^T per expert")
+    x, w = f32(x_bits), f32(w_bits)
+    del x_bits, w_bits
     a_x, a_w = oracle.amax(x, off), oracle.amax(w, wseg)
-    gx, gw = host(qx), host(qw)
-    assert_bytes_equal(gx[2].view(np.uint32), oracle.global_scales(a_x)[1].astype(np.float32).view(np.uint32),
-                       "X scale per expert")
-    # sampled rows: the first and last row of a few experts (the largest and smallest among them)
-    sizes = np.diff(off)
-    experts = np.unique(np.concatenate([[np.argmax(sizes), np.argmin(sizes)], rng.choice(G, 6, replace=False)]))
-    rx = np.unique(np.concatenate([[off[g], off[g + 1] - 1, rng.integers(off[g], off[g + 1])] for g in experts]))
-    ref_x = oracle.quantize_1x16(x[rx], segments=off, amax_vals=a_x, row_ids=rx)
-    _rows_equal(gx, ref_x, rx, "expert X")
-    g16 = np.unique(np.concatenate([[g * n // 16, (g + 1) * n // 16 - 1] for g in experts]))
-    rw = (g16[:, None] * 16 + np.arange(16)).reshape(-1)
-    ref_w = oracle.quantize_16x16(w[rw], segments=wseg, amax_vals=a_w, row_ids=rw)
-    _rows_equal(gw, ref_w, rw, "expert W")
-    sx_d = dict(zip(rx, oracle.dequantize(*ref_x, segments=off, row_ids=rx)))
-    sw_d = dict(zip(rw, oracle.dequantize(*ref_w, segments=wseg, row_ids=rw)))
-    dh = d.cpu().numpy()
-    checked = 0
-    for r in rx:
-        g = int(np.searchsorted(off, r, side="right") - 1)
-        cols = [c - g * n for c in rw if g * n <= c < (g + 1) * n]
-        for c in cols[:: max(1, len(cols) // 8)]:
-            a, b = sx_d[r], sw_d[g * n + c]
-            ref = float(np.dot(a, b))
-            bound = 1e-5 * float(np.dot(np.abs(a), np.abs(b)))
-            assert abs(float(dh[r, c]) - ref) <= bound, (r, c)
-            checked += 1
-    assert checked >= 16
+    ref_x = _q1x16(x, segments=off, amax_vals=a_x)
+    _same(host(qx), ref_x, "expert X 1x16")
+    ref_w = _q16x16(w, segments=wseg, amax_vals=a_w)
+    _same(host(qw), ref_w, "expert W 16x16")
+    gwt = host(qwt)
+    parts = _pmap(lambda g: oracle.quantize_16x16(np.ascontiguousarray(w[g * n:(g + 1) * n].T),
+                                                  amax_vals=a_w[g:g + 1]), range(G))
+    _same(gwt, (_cat(parts, 0), _cat(parts, 1), oracle.global_scales(a_w)[1]), "expert W^T 16x16")
+    del parts
+    log("moe full size: grouped GEMM")
+    x_hat = _deq(ref_x, off)
+    w_hat = _deq(ref_w, wseg)
+    _grouped_in_bound(d, x_hat, w_hat, off, n, "grouped fprop")
 
 
 def test_two_to_the_31_elements():
@@ -206,15 +268,14 @@ def test_two_to_the_31_elements():
 def test_moe_dgrad_full_size():
     """The expert layer's activation gradient at full size on the padded token layout (128
     experts, tokens padded to 64 per expert, N = hidden 2688, K = FFN 1856): dY in 1x16 SR per
-    expert, the weights' per-expert transposes from the 16x16 call, then the grouped GEMM (its
-    last column tiles are 128 wide). Sampled rows of both operands bit-exact against the
-    oracle, sampled outputs within the bound of the FP64 reference."""
-    log("moe dgrad full size")
+    expert and the weights' per-expert transposes from the 16x16 call, every byte against the
+    oracle; every output of the grouped GEMM (its last column tiles are 128 wide) within the
+    bound of the FP64 product."""
+    log("moe dgrad full size: GPU")
     x_bits, w_bits, off = workloads.moe()
     G, n, k = workloads.MOE_EXPERTS, workloads.MOE_FFN, workloads.MOE_HIDDEN
     _, dy_pad, off_pad = workloads.moe_backward(x_bits, off)
     del x_bits
-    rng = np.random.default_rng(78)
     offp = torch.from_numpy(off_pad).cuda()
     wseg = np.arange(G + 1, dtype=np.int64) * n
     qdy, _ = nv.quantize(to_device_bf16(dy_pad), "1x16", "sr", seed=21, segments=offp)
@@ -222,85 +283,67 @@ def test_moe_dgrad_full_size():
                          segments=torch.from_numpy(wseg).cuda())
     dx = nv.grouped_gemm(offp, qdy, qwt, k)
     torch.cuda.synchronize()
+    log("moe dgrad full size: oracle dY, W^T per expert")
     dy, w = f32(dy_pad), f32(w_bits)
+    del dy_pad, w_bits
     a_dy, a_w = oracle.amax(dy, off_pad), oracle.amax(w, wseg)
-    sizes = np.diff(off_pad)
-    experts = np.unique(np.concatenate([[np.argmax(sizes), np.argmin(sizes)], rng.choice(G, 5, replace=False)]))
-    rows = np.unique(np.concatenate([[off_pad[g], off_pad[g + 1] - 1, rng.integers(off_pad[g], off_pad[g + 1])]
-                                     for g in experts]))
-    ref_dy = oracle.quantize_1x16(dy[rows], "sr", seed=21, segments=off_pad, amax_vals=a_dy, row_ids=rows)
-    _rows_equal(host(qdy), ref_dy, rows, "expert dY")
-    sdy = dict(zip(rows, oracle.dequantize(*ref_dy, segments=off_pad, row_ids=rows)))
-    # columns of dX: 16-aligned groups at the start, the 128-wide last tile and one inside
-    c16 = np.array([0, k // 16 - 1, (k - 128) // 16, rng.integers(0, k // 16)])
-    gwt = host(qwt)
-    checked = 0
-    for g in experts:
-        wt = w[g * n:(g + 1) * n].T                                # [hidden, ffn] of expert g
-        for cg in c16:
-            cols = cg * 16 + np.arange(16)
-            ref_wt = oracle.quantize_16x16(wt[cols], amax_vals=np.array([a_w[g]], np.float32))
-            trows = g * k + cols
-            assert_bytes_equal(gwt[0][trows], ref_wt[0], f"expert {g} W^T codes")
-            assert_bytes_equal(gwt[1][trows], ref_wt[1], f"expert {g} W^T scales")
-            wdq = oracle.dequantize(*ref_wt)
-            for r in rows[(rows >= off_pad[g]) & (rows < off_pad[g + 1])]:
-                for i in (0, 7, 15):
-                    a, b = sdy[r], wdq[i]
-                    ref = float(np.dot(a, b))
-                    bound = 1e-5 * float(np.dot(np.abs(a), np.abs(b)))
-                    assert abs(float(dx[r, cols[i]].item()) - ref) <= bound, (g, r, cols[i])
-                    checked += 1
-    assert checked >= 48
+    ref_dy = _q1x16(dy, "sr", seed=21, segments=off_pad, amax_vals=a_dy)
+    _same(host(qdy), ref_dy, "expert dY 1x16 SR")
+    parts = _pmap(lambda g: oracle.quantize_16x16(np.ascontiguousarray(w[g * n:(g + 1) * n].T),
+                                                  amax_vals=a_w[g:g + 1]), range(G))
+    ref_wt = (_cat(parts, 0), _cat(parts, 1), oracle.global_scales(a_w)[1])
+    del parts, w
+    _same(host(qwt), ref_wt, "expert W^T 16x16")
+    log("moe dgrad full size: grouped GEMM")
+    tseg = np.arange(G + 1, dtype=np.int64) * k                     # W^T rows of expert g
+    _grouped_in_bound(dx, _deq(ref_dy, off_pad), _deq(ref_wt, tseg), off_pad, k, "grouped dgrad")
 
 
 def test_moe_wgrad_full_size():
     """The expert layer's weight gradient at full size (the GEMM grouped along K): dY and X on
-    the padded token layout, transformed along tokens and quantized per expert (nearest; both
-    sides take the same per-expert maxima, 4 max|x| per expert, which bounds |H x|), then
-    nvfp4_grouped_gemm_k into dW [128 * 1856, 2688] (its last row tiles are 64 high and its
-    last column tiles 128 wide). Sampled rows of both transposed operands bit-exact against
-    the oracle, sampled dW entries within the bound of the FP64 sum over the expert's
-    tokens."""
-    log("moe wgrad full size")
+    the padded token layout, transformed along tokens and quantized per expert (dY stochastic,
+    X nearest; both sides take the same per-expert maxima, 4 max|x| per expert, which bounds
+    |H x|), every byte against the oracle; then nvfp4_grouped_gemm_k into dW [128 * 1856, 2688]
+    (its last row tiles are 64 high and its last column tiles 128 wide), every entry within the
+    bound of the FP64 sum over the expert's tokens."""
+    log("moe wgrad full size: GPU")
     x_bits, _, off = workloads.moe()
     G, n, k = workloads.MOE_EXPERTS, workloads.MOE_FFN, workloads.MOE_HIDDEN
     x_pad, dy_pad, off_pad = workloads.moe_backward(x_bits, off)
     del x_bits
     mask = workloads.wgrad_sign_mask()
-    rng = np.random.default_rng(79)
     offp = torch.from_numpy(off_pad).cuda()
     dy, x = f32(dy_pad), f32(x_pad)
     a_dy = (oracle.amax(dy, off_pad) * np.float32(4)).astype(np.float32)
     a_x = (oracle.amax(x, off_pad) * np.float32(4)).astype(np.float32)
-    qdy = nv.rht_quantize(to_device_bf16(dy_pad), mask, "rn", segments=offp, amax=torch.from_numpy(a_dy).cuda())
+    qdy = nv.rht_quantize(to_device_bf16(dy_pad), mask, "sr", seed=23, offset=5, segments=offp,
+                          amax=torch.from_numpy(a_dy).cuda())
     qx = nv.rht_quantize(to_device_bf16(x_pad), mask, "rn", segments=offp, amax=torch.from_numpy(a_x).cuda())
     dw = nv.grouped_gemm_k(offp, qdy, qx)
     torch.cuda.synchronize()
-    i_rows = np.unique(np.concatenate([[0, n - 1, n - 64, n - 65], rng.integers(0, n, 3)]))      # FFN rows
-    c_cols = np.unique(np.concatenate([[0, k - 1, k - 128, k - 129], rng.integers(0, k, 3)]))    # hidden
-    ref_dy = oracle.quantize_1x16_colsegments(oracle.rht_columnwise(dy[:, i_rows], mask), off_pad, amax_vals=a_dy)
-    ref_x = oracle.quantize_1x16_colsegments(oracle.rht_columnwise(x[:, c_cols], mask), off_pad, amax_vals=a_x)
-    gdy, gx = host(qdy), host(qx)
-    assert_bytes_equal(gdy[0][i_rows], ref_dy[0], "H dY codes")
-    assert_bytes_equal(gdy[1][i_rows], ref_dy[1], "H dY scales")
-    assert_bytes_equal(gx[0][c_cols], ref_x[0], "H X codes")
-    assert_bytes_equal(gx[1][c_cols], ref_x[1], "H X scales")
-    dqa = oracle.dequantize(ref_dy[0], ref_dy[1], np.ones(1, np.float32))
-    dqb = oracle.dequantize(ref_x[0], ref_x[1], np.ones(1, np.float32))
-    sizes = np.diff(off_pad)
-    experts = np.unique(np.concatenate([[np.argmax(sizes), np.argmin(sizes)], rng.choice(G, 4, replace=False)]))
-    dwh = {}
-    checked = 0
-    for g in experts:
+    del dy_pad, x_pad
+    log("moe wgrad full size: oracle Hadamard operands per expert")
+
+    def colseg(y, rounding, seed, offset, amax_vals):
+        parts = _pmap(lambda r: oracle.quantize_1x16_colsegments(y[r[0]:r[1]], off_pad, rounding, seed, offset,
+                                                                 amax_vals, np.arange(r[0], r[1])),
+                      _ranges(len(y), 4 * WORKERS, 1))
+        return _cat(parts, 0), _cat(parts, 1), parts[0][2]
+
+    y_dy = _rht(dy, mask)
+    ref_dy = colseg(y_dy, "sr", 23, 5, a_dy)
+    del y_dy
+    _same(host(qdy), ref_dy, "expert (H dY)^T SR")
+    y_x = _rht(x, mask)
+    ref_x = colseg(y_x, "rn", 0, 0, a_x)
+    del y_x
+    _same(host(qx), ref_x, "expert (H X)^T RN")
+    log("moe wgrad full size: K-grouped GEMM")
+    one = np.ones(1, np.float32)
+    dqa = _deq((ref_dy[0], ref_dy[1], one))
+    dqb = _deq((ref_x[0], ref_x[1], one))
+    for g in range(G):
         t0, t1 = int(off_pad[g]), int(off_pad[g + 1])
         sg = float(ref_dy[2][g]) * float(ref_x[2][g])
-        block = dw[g * n:(g + 1) * n].cpu().numpy()
-        for a_i, i in enumerate(i_rows):
-            for b_i, c in enumerate(c_cols):
-                a, b = dqa[a_i, t0:t1], dqb[b_i, t0:t1]
-                ref = float(np.dot(a, b)) * sg
-                bound = 1e-5 * float(np.dot(np.abs(a), np.abs(b))) * sg
-                assert abs(float(block[i, c]) - ref) <= bound, (g, i, c)
-                checked += 1
-    assert checked >= 100
+        _gemm_in_bound_quiet(dw[g * n:(g + 1) * n], dqa[:, t0:t1] * sg, dqb[:, t0:t1], f"K-grouped wgrad expert {g}")
+    log(f"K-grouped wgrad: every element of {G * n} x {k} within bound")

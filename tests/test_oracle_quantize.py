@@ -234,3 +234,15 @@ def test_column_segments_sr_use_whole_tensor_block_index():
                                            amax_vals=[a, a, a])
     want = oracle.quantize_1x16(x, "sr", seed=7, offset=1)
     assert np.array_equal(got[0], want[0]) and np.array_equal(got[1], want[1])
+
+
+def test_colsegments_row_subsets_equal_the_whole_tensor():
+    # row subsets (with the full tensor's maxima) give the whole tensor's rows, stochastic
+    # rounding included: the block index is the block's place in the whole tensor
+    x = workloads.bf16_bits_to_f32(workloads.with_outliers_bf16((24, 96), 61))
+    seg = [0, 32, 32, 96]
+    full = oracle.quantize_1x16_colsegments(x, seg, "sr", seed=4, offset=9)
+    rows = np.array([0, 5, 23])
+    a = np.array([np.abs(x[:, seg[g]:seg[g + 1]]).max() if seg[g + 1] > seg[g] else 0.0 for g in range(3)], np.float32)
+    sub = oracle.quantize_1x16_colsegments(x[rows], seg, "sr", seed=4, offset=9, amax_vals=a, row_ids=rows)
+    assert np.array_equal(sub[0], full[0][rows]) and np.array_equal(sub[1], full[1][rows])
