@@ -5,8 +5,8 @@ Every function marshals torch tensors (device memory, current stream) into the C
 returns; all arithmetic runs in the HIP kernels. If the library is not built the import
 still succeeds but every call raises, so nothing can silently fall back to another path.
 
-Names follow the C entry points: quantize, rht_quantize, gemm, gemm_ex, grouped_gemm,
-grouped_gemm_k, amax, amax_pair, dequantize.
+Names follow the C entry points: quantize, quantize_noalloc, rht_quantize, rht_rows_quantize,
+gemm, gemm_ex, grouped_gemm, grouped_gemm_k, amax, amax_pair, mx_quantize, mx_gemm, dequantize.
 """
 from __future__ import annotations
 
@@ -29,7 +29,7 @@ _ROUND = {"rn": 0, "sr": 1}
 OP_QUANTIZE, OP_RHT_QUANTIZE, OP_GEMM, OP_GROUPED_GEMM, OP_AMAX_PAIR, OP_GEMM_EX = 0, 1, 2, 3, 4, 5
 OUT_FP32, OUT_FP32_ACCUMULATE, OUT_BF16 = 0, 1, 2
 
-EXPORTED = ("nvfp4_quantize", "nvfp4_rht_quantize", "nvfp4_gemm", "nvfp4_gemm_ex", "nvfp4_grouped_gemm",
+EXPORTED = ("nvfp4_quantize", "nvfp4_quantize_noalloc", "nvfp4_rht_quantize", "nvfp4_gemm", "nvfp4_gemm_ex", "nvfp4_grouped_gemm",
             "mxfp4_quantize", "mxfp4_gemm", "nvfp4_rht_rows_quantize",
             "nvfp4_grouped_gemm_k",
             "nvfp4_amax", "nvfp4_amax_pair", "nvfp4_workspace_size", "nvfp4_last_error",
@@ -65,6 +65,8 @@ def _load():
     pt = ctypes.POINTER(_CTensor)
     lib.nvfp4_quantize.argtypes = [vp, ctypes.c_int, i64, i64, i64, ctypes.c_int, ctypes.c_int,
                                    u64, u64, vp, i64, vp, pt, pt, vp, sz, vp]
+    lib.nvfp4_quantize_noalloc.argtypes = [vp, ctypes.c_int, i64, i64, i64, ctypes.c_int, ctypes.c_int,
+                                           u64, u64, vp, i64, vp, pt, pt, vp]
     lib.nvfp4_rht_quantize.argtypes = [vp, ctypes.c_int, i64, i64, i64, ctypes.c_uint16,
                                        ctypes.c_int, u64, u64, vp, i64, vp, pt, vp, sz, vp]
     lib.nvfp4_gemm.argtypes = [pt, pt, vp, i64, vp]
@@ -248,6 +250,37 @@ def quantize(x: torch.Tensor, block: str = "1x16", rounding: str = "rn", seed: i
                             _ptr(amax), ctypes.byref(oc),
                             ctypes.byref(otc) if otc is not None else None,
                             _ptr(workspace) if amax is None else None, ws_n, _stream(stream))
+    _check(st)
+    return out, (out_t if emit_transposed else None)
+
+
+@_on_stream
+def quantize_noalloc(x: torch.Tensor, block: str = "1x16", rounding: str = "rn", seed: int = 0,
+                     offset: int = 0, segments: torch.Tensor | None = None, amax: torch.Tensor | None = None,
+                     emit_transposed: bool = False, out: NVFP4Tensor | None = None,
+                     out_t: NVFP4Tensor | None = None, stream=None):
+    """nvfp4_quantize_noalloc: nvfp4_quantize without a workspace (the library's static device
+    array holds the amax partials). With `out` (and `out_t` when emit_transposed) given, this
+    allocates nothing; calls overlapping on one device race. Returns (q, q_t)."""
+    lib = _load()
+    dt, rows, cols, ld = _input(x)
+    nseg = 1 if segments is None else segments.numel() - 1
+    if out is None:
+        out = NVFP4Tensor.empty(rows, cols, nseg, x.device)
+    if emit_transposed and out_t is None:
+        out_t = (NVFP4Tensor.empty(cols, rows, 1, x.device) if segments is None
+                 else NVFP4Tensor.empty(nseg * cols, rows // nseg, nseg, x.device))
+    _check_table(segments, "segments")
+    _check_vec(amax, nseg, "amax")
+    _check_q(out, nseg, "out")
+    if emit_transposed:
+        _check_q(out_t, nseg if segments is not None else 1, "out_t")
+    oc = out.c()
+    otc = out_t.c() if emit_transposed else None
+    st = lib.nvfp4_quantize_noalloc(_ptr(x), dt, rows, cols, ld, _BLOCK[block], _ROUND[rounding],
+                                    seed & (2 ** 64 - 1), offset & (2 ** 64 - 1), _ptr(segments), nseg,
+                                    _ptr(amax), ctypes.byref(oc),
+                                    ctypes.byref(otc) if otc is not None else None, _stream(stream))
     _check(st)
     return out, (out_t if emit_transposed else None)
 

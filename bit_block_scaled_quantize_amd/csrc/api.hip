@@ -2,10 +2,20 @@
 // sizing and dispatch to the gfx950 kernels. Nothing here allocates device memory.
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "../../include/nvfp4.h"
 #include "launch.h"
+
+// Device memory of nvfp4_quantize_noalloc: the partial or per-segment tensor maxima of its amax
+// pass, which nvfp4_quantize keeps in the caller's workspace. One copy per device (the module is
+// loaded on each device it runs on), held until the process ends. In host code `scratch` names
+// a host-side stand-in, not device memory: kernels get the device address that
+// hipGetSymbolAddress returns for the current device (scratch_on_device below), never `scratch`.
+constexpr int64_t kNoAllocScratchFloats = 16384;        // 64 KiB: up to 16384 segments
+static_assert(kNoAllocScratchFloats >= nvfp4::kMaxAmaxPartials, "scratch holds the amax partials");
+static __device__ __align__(256) float scratch[kNoAllocScratchFloats];
 
 namespace {
 
@@ -27,6 +37,29 @@ int hip_status(hipError_t e, const char* what) {
 }
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Device address of `scratch` on the current device, looked up once per device (with that
+// device current) and kept.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices] = {};
+
+int scratch_on_device(float** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(NVFP4_ERR_UNSUPPORTED, "device %d beyond the %d devices supported", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(NVFP4_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_addr[dev] = p;
+  }
+  *out = static_cast<float*>(g_scratch_addr[dev]);
+  return NVFP4_OK;
+}
 
 constexpr size_t kWsAlign = 256;
 
@@ -190,11 +223,17 @@ int nvfp4_amax_pair(const void* x, nvfp4_dtype dt, int64_t tokens, int64_t cols,
   return hip_status(nvfp4::launch_reduce_partials(ws, parts, amax_out, s, 2), "amax reduce");
 }
 
-int nvfp4_quantize(const void* x, nvfp4_dtype dt, int64_t rows, int64_t cols, int64_t ld,
-                   nvfp4_block blk, nvfp4_round rnd, uint64_t seed, uint64_t offset,
-                   const int64_t* segments, int64_t nseg, const float* amax_in,
-                   nvfp4_tensor* out, nvfp4_tensor* out_t, void* workspace, size_t ws_bytes,
-                   void* hip_stream) {
+}  // extern "C"
+
+namespace {
+
+// nvfp4_quantize; with use_scratch the amax pass (when amax_in is NULL) takes the device's
+// static scratch array instead of the caller's workspace, looked up after validation.
+int quantize_impl(const void* x, nvfp4_dtype dt, int64_t rows, int64_t cols, int64_t ld,
+                  nvfp4_block blk, nvfp4_round rnd, uint64_t seed, uint64_t offset,
+                  const int64_t* segments, int64_t nseg, const float* amax_in,
+                  nvfp4_tensor* out, nvfp4_tensor* out_t, void* workspace, size_t ws_bytes,
+                  void* hip_stream, bool use_scratch) {
   int st = check_input(x, dt, rows, cols, ld);
   if (st) return st;
   if (blk != NVFP4_BLOCK_1X16 && blk != NVFP4_BLOCK_16X16) return fail(NVFP4_ERR_INVALID, "bad block mode %d", (int)blk);
@@ -211,6 +250,15 @@ int nvfp4_quantize(const void* x, nvfp4_dtype dt, int64_t rows, int64_t cols, in
   if (out_t && (st = check_out(out_t, segments ? nseg * cols : cols, rows / nseg, "out_t"))) return st;
   if (rows == 0) return NVFP4_OK;
   const float* amax = amax_in;
+  if (!amax && use_scratch) {
+    if (nseg > kNoAllocScratchFloats)
+      return fail(NVFP4_ERR_UNSUPPORTED, "nvfp4_quantize_noalloc handles at most %lld segments (got %lld); "
+                  "use nvfp4_quantize with a workspace", (long long)kNoAllocScratchFloats, (long long)nseg);
+    float* ws = nullptr;
+    if ((st = scratch_on_device(&ws))) return st;
+    workspace = ws;
+    ws_bytes = (size_t)kNoAllocScratchFloats * sizeof(float);
+  }
   if (!amax) {
     const size_t need = nvfp4_workspace_size(NVFP4_OP_QUANTIZE, rows, cols, nseg);
     if (!workspace || ws_bytes < need || !aligned(workspace, kWsAlign))
@@ -232,6 +280,27 @@ int nvfp4_quantize(const void* x, nvfp4_dtype dt, int64_t rows, int64_t cols, in
   if (out_t) qt = nvfp4::QuantOut{out_t->codes, out_t->scales, out_t->global_scale};
   return hip_status(nvfp4::launch_encode_16x16(x, f32, rows, cols, ld, segments, nseg, amax, parts, q,
                                                out_t ? &qt : nullptr, s), "encode 16x16");
+}
+
+}  // namespace
+
+extern "C" {
+
+int nvfp4_quantize(const void* x, nvfp4_dtype dt, int64_t rows, int64_t cols, int64_t ld,
+                   nvfp4_block blk, nvfp4_round rnd, uint64_t seed, uint64_t offset,
+                   const int64_t* segments, int64_t nseg, const float* amax_in,
+                   nvfp4_tensor* out, nvfp4_tensor* out_t, void* workspace, size_t ws_bytes,
+                   void* hip_stream) {
+  return quantize_impl(x, dt, rows, cols, ld, blk, rnd, seed, offset, segments, nseg, amax_in, out, out_t,
+                       workspace, ws_bytes, hip_stream, false);
+}
+
+int nvfp4_quantize_noalloc(const void* x, nvfp4_dtype dt, int64_t rows, int64_t cols, int64_t ld,
+                           nvfp4_block blk, nvfp4_round rnd, uint64_t seed, uint64_t offset,
+                           const int64_t* segments, int64_t nseg, const float* amax_in,
+                           nvfp4_tensor* out, nvfp4_tensor* out_t, void* hip_stream) {
+  return quantize_impl(x, dt, rows, cols, ld, blk, rnd, seed, offset, segments, nseg, amax_in, out, out_t,
+                       nullptr, 0, hip_stream, true);
 }
 
 int nvfp4_rht_quantize(const void* x, nvfp4_dtype dt, int64_t tokens, int64_t cols, int64_t ld,

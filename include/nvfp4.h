@@ -124,6 +124,24 @@ int nvfp4_quantize(const void* x, nvfp4_dtype dt, int64_t rows, int64_t cols, in
                    void* workspace, size_t ws_bytes, void* hip_stream);
 
 /*
+ * nvfp4_quantize_noalloc - nvfp4_quantize for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid allocation. Same
+ * arguments, results and errors as nvfp4_quantize minus the workspace: the amax pass keeps its
+ * partial (or per-segment) maxima in a static device array of the library, 64 KiB per device,
+ * held until the process ends. The call allocates nothing (its first call on a device looks up
+ * that device's array once); anything that must start at zero is cleared by a kernel, not a
+ * memset, so the call can be captured in a graph.
+ *   nseg       at most 16384 (NVFP4_ERR_UNSUPPORTED beyond, nothing enqueued).
+ * Every call on one device shares that device's array: calls that overlap on one device (on
+ * different streams, or from several threads without ordering) race and give unspecified
+ * results. Calls ordered on one stream are safe.
+ */
+int nvfp4_quantize_noalloc(const void* x, nvfp4_dtype dt, int64_t rows, int64_t cols, int64_t ld,
+                           nvfp4_block blk, nvfp4_round rnd, uint64_t seed, uint64_t offset,
+                           const int64_t* segments, int64_t nseg, const float* amax_in,
+                           nvfp4_tensor* out, nvfp4_tensor* out_t, void* hip_stream);
+
+/*
  * nvfp4_rht_quantize - random Hadamard transform along tokens, then 1x16 quantization of
  * the transposed result. Defined by: "Nemotron NVFP4" explainer, "Why 4-bit training
  * normally falls apart - and the three fixes" (a random Hadamard matrix on the wgrad inputs,

@@ -80,6 +80,29 @@ def test_quantize_validation(lib):
     assert _q(lib, ld=68, cols=64) == UNSUPPORTED                           # row stride not 16-byte
 
 
+def _qn(lib, **kw):
+    a = dict(x=FAKE, dt=0, rows=32, cols=64, ld=64, blk=0, rnd=0, seed=0, offset=0, seg=None,
+             nseg=1, amax=None, out=_tensor(32, 64), out_t=None, stream=None)
+    a.update(kw)
+    out_t = ctypes.byref(a["out_t"]) if a["out_t"] is not None else None
+    out = ctypes.byref(a["out"]) if a["out"] is not None else None
+    return lib.nvfp4_quantize_noalloc(a["x"], a["dt"], a["rows"], a["cols"], a["ld"], a["blk"], a["rnd"],
+                                      a["seed"], a["offset"], a["seg"], a["nseg"], a["amax"], out, out_t,
+                                      a["stream"])
+
+
+def test_quantize_noalloc_validation(lib):
+    # the allocation-free form validates like nvfp4_quantize, before touching its device array
+    assert _qn(lib, x=None) == INVALID
+    assert _qn(lib, cols=60, ld=64) == INVALID
+    assert _qn(lib, blk=1, rnd=1) == UNSUPPORTED
+    assert _qn(lib, out=None) == INVALID
+    assert _qn(lib, x=FAKE + 2) == UNSUPPORTED
+    # more segments than its 64 KiB device array holds: a clear error, nothing enqueued
+    assert _qn(lib, seg=FAKE, nseg=16385) == UNSUPPORTED
+    assert b"at most 16384 segments" in lib.nvfp4_last_error()
+
+
 def test_rht_validation(lib):
     out = _tensor(64, 32)
     f = lib.nvfp4_rht_quantize
