@@ -410,15 +410,16 @@ def bench_mx(nv, workloads, torch, dev, stream, flush, X, W, dY, args):
     """The comparison format of the pages, MXFP4 (E8M0 scale per 32 elements, no tensor scale),
     on the same layer: quantize (single pass: no amax) and the three GEMMs on gfx950's
     block-scaled FP4 matrix instruction, against its 10.1 PFLOP/s peak. Each GEMM operand is
-    quantized along its contraction; the transposed sources (W^T, dY^T, X^T) are laid out by
-    torch before timing. Cold caches, median of --kernel-reps."""
+    quantized along its contraction: W, dY and X row-wise for the forward and the gradients' left
+    operands, and W^T, dY^T, X^T by the column quantization straight from W, dY and X (no
+    transposed copies). Cold caches, median of --kernel-reps."""
     T = nv.MXFP4Tensor
-    Wt, dYt, Xt = W.t().contiguous(), dY.t().contiguous(), X.t().contiguous()
     qX, qW, qdY, qWt = T.empty(M, K_IN), T.empty(N_OUT, K_IN), T.empty(M, N_OUT), T.empty(K_IN, N_OUT)
     qdYt, qXt = T.empty(N_OUT, M), T.empty(K_IN, M)
-    for src, q, rnd in ((X, qX, "rn"), (W, qW, "rn"), (dY, qdY, "sr"), (Wt, qWt, "rn"), (dYt, qdYt, "sr"),
-                        (Xt, qXt, "rn")):
+    for src, q, rnd in ((X, qX, "rn"), (W, qW, "rn"), (dY, qdY, "sr")):
         nv.mx_quantize(src, rnd, seed=7, out=q)
+    for src, q, rnd in ((W, qWt, "rn"), (dY, qdYt, "sr"), (X, qXt, "rn")):
+        nv.mx_quantize_columns(src, rnd, seed=7, out=q)
     Y = torch.empty((M, N_OUT), dtype=torch.float32, device=dev)
     dX = torch.empty((M, K_IN), dtype=torch.float32, device=dev)
     dW = torch.empty((N_OUT, K_IN), dtype=torch.float32, device=dev)
@@ -428,6 +429,10 @@ def bench_mx(nv, workloads, torch, dev, stream, flush, X, W, dY, args):
         "mx_quantize_x_rn": (lambda: nv.mx_quantize(X, "rn", out=qX), "GB/s", mxq(M, K_IN)),
         "mx_quantize_dy_sr": (lambda: nv.mx_quantize(dY, "sr", seed=7, out=qdY), "GB/s", mxq(M, N_OUT)),
         "mx_quantize_w_rn": (lambda: nv.mx_quantize(W, "rn", out=qW), "GB/s", mxq(N_OUT, K_IN)),
+        "mx_quantize_columns_wt_rn": (lambda: nv.mx_quantize_columns(W, "rn", out=qWt), "GB/s", mxq(N_OUT, K_IN)),
+        "mx_quantize_columns_dyt_sr": (lambda: nv.mx_quantize_columns(dY, "sr", seed=7, out=qdYt), "GB/s",
+                                       mxq(M, N_OUT)),
+        "mx_quantize_columns_xt_rn": (lambda: nv.mx_quantize_columns(X, "rn", out=qXt), "GB/s", mxq(M, K_IN)),
         "mx_gemm_fprop": (lambda: nv.mx_gemm(qX, qW, out=Y), "TFLOP/s", flops),
         "mx_gemm_dgrad": (lambda: nv.mx_gemm(qdY, qWt, out=dX), "TFLOP/s", flops),
         "mx_gemm_wgrad": (lambda: nv.mx_gemm(qdYt, qXt, out=dW), "TFLOP/s", flops),

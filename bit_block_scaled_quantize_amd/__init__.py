@@ -6,7 +6,7 @@ returns; all arithmetic runs in the HIP kernels. If the library is not built the
 still succeeds but every call raises, so nothing can silently fall back to another path.
 
 Names follow the C entry points: quantize, quantize_noalloc, rht_quantize, rht_rows_quantize,
-gemm, gemm_ex, grouped_gemm, grouped_gemm_k, amax, amax_pair, mx_quantize, mx_gemm, dequantize.
+gemm, gemm_ex, grouped_gemm, grouped_gemm_k, amax, amax_pair, mx_quantize, mx_quantize_columns, mx_gemm, dequantize.
 """
 from __future__ import annotations
 
@@ -30,7 +30,7 @@ OP_QUANTIZE, OP_RHT_QUANTIZE, OP_GEMM, OP_GROUPED_GEMM, OP_AMAX_PAIR, OP_GEMM_EX
 OUT_FP32, OUT_FP32_ACCUMULATE, OUT_BF16 = 0, 1, 2
 
 EXPORTED = ("nvfp4_quantize", "nvfp4_quantize_noalloc", "nvfp4_rht_quantize", "nvfp4_gemm", "nvfp4_gemm_ex", "nvfp4_grouped_gemm",
-            "mxfp4_quantize", "mxfp4_gemm", "nvfp4_rht_rows_quantize",
+            "mxfp4_quantize", "mxfp4_quantize_columns", "mxfp4_gemm", "nvfp4_rht_rows_quantize",
             "nvfp4_grouped_gemm_k",
             "nvfp4_amax", "nvfp4_amax_pair", "nvfp4_workspace_size", "nvfp4_last_error",
             "nvfp4_dequantize")
@@ -72,6 +72,7 @@ def _load():
     lib.nvfp4_gemm.argtypes = [pt, pt, vp, i64, vp]
     mpt = ctypes.POINTER(_CMXTensor)
     lib.mxfp4_quantize.argtypes = [vp, ctypes.c_int, i64, i64, i64, ctypes.c_int, u64, u64, mpt, vp]
+    lib.mxfp4_quantize_columns.argtypes = [vp, ctypes.c_int, i64, i64, i64, ctypes.c_int, u64, u64, mpt, vp]
     lib.mxfp4_gemm.argtypes = [mpt, mpt, vp, i64, vp]
     lib.nvfp4_rht_rows_quantize.argtypes = [vp, ctypes.c_int, i64, i64, i64, ctypes.c_uint16, ctypes.c_int,
                                             u64, u64, vp, pt, vp, sz, vp]
@@ -323,6 +324,21 @@ def mx_quantize(x: torch.Tensor, rounding: str = "rn", seed: int = 0, offset: in
     oc = out.c()
     _check(lib.mxfp4_quantize(_ptr(x), dt, rows, cols, ld, _ROUND[rounding], seed & (2 ** 64 - 1),
                               offset & (2 ** 64 - 1), ctypes.byref(oc), _stream(stream)))
+    return out
+
+
+@_on_stream
+def mx_quantize_columns(x: torch.Tensor, rounding: str = "rn", seed: int = 0, offset: int = 0,
+                        out: MXFP4Tensor | None = None, stream=None) -> MXFP4Tensor:
+    """mxfp4_quantize_columns: x[rows, cols] -> MXFP4 of x^T, [cols, rows] (E8M0 per 32 rows)."""
+    lib = _load()
+    dt, rows, cols, ld = _input(x)
+    if out is None:
+        out = MXFP4Tensor.empty(cols, rows, x.device)
+    _check_q(out, what="out")
+    oc = out.c()
+    _check(lib.mxfp4_quantize_columns(_ptr(x), dt, rows, cols, ld, _ROUND[rounding], seed & (2 ** 64 - 1),
+                                      offset & (2 ** 64 - 1), ctypes.byref(oc), _stream(stream)))
     return out
 
 

@@ -362,6 +362,26 @@ int nvfp4_gemm(const nvfp4_tensor* A, const nvfp4_tensor* B, float* D, int64_t l
   return hip_status(nvfp4::launch_gemm(a, b, A->rows, B->rows, A->cols, D, ldd, (hipStream_t)hip_stream), "gemm");
 }
 
+int mxfp4_quantize_columns(const void* x, nvfp4_dtype dt, int64_t rows, int64_t cols, int64_t ld,
+                           nvfp4_round rnd, uint64_t seed, uint64_t offset, mxfp4_tensor* out,
+                           void* hip_stream) {
+  int st;
+  if ((st = check_input(x, dt, rows, cols, ld, false))) return st;
+  if (rows % 32) return fail(NVFP4_ERR_INVALID, "rows (%lld) must be a multiple of 32", (long long)rows);
+  if (rnd != NVFP4_ROUND_RN && rnd != NVFP4_ROUND_SR) return fail(NVFP4_ERR_INVALID, "bad rounding %d", (int)rnd);
+  if (!out) return fail(NVFP4_ERR_INVALID, "out is NULL");
+  if (out->rows != cols || out->cols != rows)
+    return fail(NVFP4_ERR_INVALID, "out shape [%lld, %lld] does not match [%lld, %lld]", (long long)out->rows,
+                (long long)out->cols, (long long)cols, (long long)rows);
+  if (rows == 0 || cols == 0) return NVFP4_OK;
+  if (!out->codes || !out->scales) return fail(NVFP4_ERR_INVALID, "out buffers are NULL");
+  if (!aligned(out->codes, 16) || !aligned(out->scales, 8))
+    return fail(NVFP4_ERR_INVALID, "out codes must be 16-byte and scales 8-byte aligned");
+  return hip_status(nvfp4::launch_encode_mx_cols(x, dt == NVFP4_IN_FP32, rows, cols, ld, rnd == NVFP4_ROUND_SR,
+                                                 seed, offset, out->codes, out->scales, (hipStream_t)hip_stream),
+                    "mxfp4 column encode");
+}
+
 int mxfp4_quantize(const void* x, nvfp4_dtype dt, int64_t rows, int64_t cols, int64_t ld,
                    nvfp4_round rnd, uint64_t seed, uint64_t offset, mxfp4_tensor* out,
                    void* hip_stream) {

@@ -62,6 +62,11 @@ hipError_t launch_encode_mx(const void* x, bool fp32, int64_t rows, int64_t cols
                             bool sr, uint64_t seed, uint64_t offset, uint8_t* codes,
                             uint8_t* scales, hipStream_t stream);
 
+// MXFP4 of x^T: x[rows, cols] -> codes [cols, rows/2], scales [cols, rows/32]; rows % 32 == 0.
+hipError_t launch_encode_mx_cols(const void* x, bool fp32, int64_t rows, int64_t cols, int64_t ld, bool sr,
+                                 uint64_t seed, uint64_t offset, uint8_t* codes, uint8_t* scales,
+                                 hipStream_t stream);
+
 // p[0..n) = v
 hipError_t launch_fill(float* p, int64_t n, float v, hipStream_t stream);
 

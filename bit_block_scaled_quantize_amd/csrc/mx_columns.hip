@@ -1,0 +1,201 @@
+// MXFP4 quantization of a tensor's columns: x[rows, cols] -> out[cols, rows], each output row (an
+// input column) quantized along the input rows in 32-element blocks. The format is the pages'
+// comparison format ("Nemotron NVFP4" explainer, "What NVFP4 actually is": E2M1 elements, one
+// power-of-two E8M0 scale per 32 elements, no tensor scale); the result is by definition the
+// row-wise MXFP4 quantization of x^T (mxfp4_quantize of the transposed tensor): shared exponent
+// e = floor(log2(block amax)) - 2 clamped to [-127, 127], elements E2M1(x * 2^-e) rounded to
+// nearest or stochastically with the Philox bytes of the 16-element half block at its place in
+// the output. The activation-gradient and weight-gradient GEMMs contract over the other
+// dimension of W, dY and X than the forward one, so these operands need exactly this.
+//
+// Layout: a tile is 128 columns x 256 rows (8 blocks of 32). Lane l of a wave owns columns 2l
+// and 2l+1, so a wave-wide load of one row is 256 contiguous bytes (BF16); wave w takes the
+// 32-row blocks w and w + 4 of the tile. Workgroups walk tiles with a stride of the grid (the
+// resident workgroup count); each wave requests its next block's 32 rows before encoding the
+// current one. Codes and E8M0 bytes are staged in LDS as [column][row] and written out as
+// 128-byte (codes) and 8-byte (scales) row segments of the transposed tensor.
+#include "device_common.h"
+#include "launch.h"
+
+namespace nvfp4 {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+constexpr int kTileCols = 128;                  // 64 lanes x 2 columns
+constexpr int kTileRows = 256;                  // 8 blocks of 32 rows
+constexpr int kBlocksPerTile = kTileRows / 32;
+constexpr int kItemsPerWave = kBlocksPerTile / kWaves;
+
+// Columns c and c+1 of one row, kept packed until use (as the Hadamard kernel's loads).
+template <typename TIn>
+struct ColPair;
+
+template <>
+struct ColPair<uint16_t> {
+  uint32_t w;
+  __device__ __forceinline__ void load(const uint16_t* p, bool both, bool paired) {
+    if (both && paired) w = *reinterpret_cast<const uint32_t*>(p);
+    else w = (uint32_t)p[0] | (both ? (uint32_t)p[1] << 16 : 0u);
+  }
+  __device__ __forceinline__ float get(int q) const { return q == 0 ? bf16_lo(w) : bf16_hi(w); }
+};
+
+template <>
+struct ColPair<float> {
+  v2f32 w;
+  __device__ __forceinline__ void load(const float* p, bool both, bool paired) {
+    if (both && paired) w = *reinterpret_cast<const v2f32*>(p);
+    else w = v2f32{p[0], both ? p[1] : 0.0f};
+  }
+  __device__ __forceinline__ float get(int q) const { return q == 0 ? w.x : w.y; }
+};
+
+template <typename TIn, bool SR>
+__global__ __launch_bounds__(kThreads) void k_encode_mx_cols(
+    const TIn* __restrict__ x, int64_t rows, int64_t cols, int64_t ld, uint8_t* __restrict__ codes,
+    uint8_t* __restrict__ scales, uint64_t seed, uint64_t offset) {
+  __shared__ __attribute__((aligned(16))) uint8_t tc[kTileCols][kTileRows / 2];
+  __shared__ __attribute__((aligned(16))) uint8_t ts[kTileCols][kBlocksPerTile];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t nblk = rows >> 5;                               // 32-row blocks
+  const int64_t tiles_c = (cols + kTileCols - 1) / kTileCols;
+  const int64_t tiles = tiles_c * ((nblk + kBlocksPerTile - 1) / kBlocksPerTile);
+  const bool paired = (ld & 1) == 0;
+  const int64_t halves = rows >> 4;                             // 16-element halves per output row
+
+  struct Geo { int64_t C0, B0; };
+  auto geo = [&](int64_t it) {
+    const int64_t tt = it / tiles_c;
+    return Geo{(it - tt * tiles_c) * kTileCols, tt * kBlocksPerTile};
+  };
+  auto load_item = [&](ColPair<TIn> (&raw)[32], int64_t it, int k) {
+    const Geo g = geo(it);
+    const int64_t c = g.C0 + 2 * lane;
+    const int64_t cl = c < cols ? c : 0;                          // clamped column for loads
+    const int64_t b = g.B0 + wave + kWaves * k;
+    const int64_t bl = b < nblk ? b : 0;                          // clamped block for loads
+    const TIn* p = x + bl * 32 * ld + cl;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) raw[j].load(p + j * ld, c + 1 < cols, paired);
+  };
+
+  ColPair<TIn> cur[32], nxt[32];
+  int64_t it = blockIdx.x;
+  int k = 0;
+  if (it < tiles) load_item(cur, it, 0);
+
+  auto step = [&](ColPair<TIn> (&cur)[32], ColPair<TIn> (&nxt)[32]) {
+    int64_t it_n = it;
+    int k_n = k + 1;
+    if (k_n == kItemsPerWave) {
+      k_n = 0;
+      it_n = it + gridDim.x;
+    }
+    if (it_n < tiles) load_item(nxt, it_n, k_n);
+
+    const Geo g = geo(it);
+    const int64_t c = g.C0 + 2 * lane;
+    const int bl = wave + kWaves * k;                             // block within the tile
+    const int64_t b = g.B0 + bl;
+    if (b < nblk) {
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        float v[32];
+#pragma unroll
+        for (int j = 0; j < 32; ++j) v[j] = cur[j].get(q);
+        float am = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 32; ++j) am = fmaxf(am, fabsf(v[j]));
+        int e = am > 0.0f ? __builtin_amdgcn_frexp_expf(am) - 3 : -127;   // floor(log2 am) - 2
+        e = e < -127 ? -127 : (e > 127 ? 127 : e);
+        const float mult = __builtin_ldexpf(1.0f, -e);
+        const int64_t orow = c + q;                               // output row = input column
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          float h16[16];
+#pragma unroll
+          for (int j = 0; j < 16; ++j) h16[j] = v[16 * hh + j];
+          u32x4 rnd{0, 0, 0, 0};
+          if constexpr (SR) rnd = block_random((uint64_t)(orow * halves + 2 * b + hh), seed, offset);
+          uint32_t lo, hi;
+          encode16<SR>(h16, mult, rnd, lo, hi);
+          *reinterpret_cast<uint2*>(&tc[2 * lane + q][bl * 16 + hh * 8]) = make_uint2(lo, hi);
+        }
+        ts[2 * lane + q][bl] = (uint8_t)(e + 127);
+      }
+    }
+
+    if (k == kItemsPerWave - 1) {                                 // tile complete: write x^T rows
+      __syncthreads();
+      const int64_t valid_cols = cols - g.C0 < kTileCols ? cols - g.C0 : kTileCols;
+      const int64_t valid_b = nblk - g.B0 < kBlocksPerTile ? nblk - g.B0 : kBlocksPerTile;
+      // codes: 128 columns x 8 blocks of 16 bytes, one 16-byte piece per thread and pass
+#pragma unroll
+      for (int pass = 0; pass < kTileCols * kBlocksPerTile / kThreads; ++pass) {
+        const int idx = pass * kThreads + threadIdx.x;
+        const int cr = idx >> 3, p = idx & 7;
+        if (cr < valid_cols && p < valid_b)
+          *reinterpret_cast<uint4*>(codes + (g.C0 + cr) * (rows >> 1) + (g.B0 + p) * 16) =
+              *reinterpret_cast<const uint4*>(&tc[cr][p * 16]);
+      }
+      if (threadIdx.x < valid_cols) {
+        const int cr = threadIdx.x;
+        uint8_t* dst = scales + (g.C0 + cr) * nblk + g.B0;
+        if (valid_b == kBlocksPerTile && ((reinterpret_cast<uintptr_t>(dst) & 7) == 0)) {
+          *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<const uint2*>(&ts[cr][0]);
+        } else {
+          for (int p = 0; p < valid_b; ++p) dst[p] = ts[cr][p];
+        }
+      }
+      __syncthreads();                                            // LDS reused by the next tile
+    }
+    it = it_n;
+    k = k_n;
+  };
+  while (it < tiles) {                                            // uniform across the workgroup
+    step(cur, nxt);
+    if (it >= tiles) break;
+    step(nxt, cur);
+  }
+}
+
+template <typename TIn, bool SR>
+int64_t resident_groups_mx() {
+  static const int64_t n = [] {
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_encode_mx_cols<TIn, SR>, kThreads, 0) != hipSuccess)
+      return (int64_t)1024;
+    return (int64_t)(cus > 0 ? cus : 1) * (per_cu > 0 ? per_cu : 1);
+  }();
+  return n;
+}
+
+template <typename TIn, bool SR>
+void launch_mx_cols_t(const void* x, int64_t rows, int64_t cols, int64_t ld, uint8_t* codes, uint8_t* scales,
+                      uint64_t seed, uint64_t offset, hipStream_t stream) {
+  const int64_t tiles = ((cols + kTileCols - 1) / kTileCols) * (((rows >> 5) + kBlocksPerTile - 1) / kBlocksPerTile);
+  const int64_t cap = resident_groups_mx<TIn, SR>();
+  const int grid = (int)(tiles < cap ? (tiles < 1 ? 1 : tiles) : cap);
+  hipLaunchKernelGGL((k_encode_mx_cols<TIn, SR>), dim3(grid), dim3(kThreads), 0, stream, (const TIn*)x, rows, cols, ld,
+                     codes, scales, seed, offset);
+}
+
+}  // namespace
+
+hipError_t launch_encode_mx_cols(const void* x, bool fp32, int64_t rows, int64_t cols, int64_t ld, bool sr,
+                                 uint64_t seed, uint64_t offset, uint8_t* codes, uint8_t* scales, hipStream_t stream) {
+  if (rows == 0 || cols == 0) return hipSuccess;
+  if (fp32) {
+    if (sr) launch_mx_cols_t<float, true>(x, rows, cols, ld, codes, scales, seed, offset, stream);
+    else launch_mx_cols_t<float, false>(x, rows, cols, ld, codes, scales, seed, offset, stream);
+  } else {
+    if (sr) launch_mx_cols_t<uint16_t, true>(x, rows, cols, ld, codes, scales, seed, offset, stream);
+    else launch_mx_cols_t<uint16_t, false>(x, rows, cols, ld, codes, scales, seed, offset, stream);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace nvfp4

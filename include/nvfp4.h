@@ -198,6 +198,23 @@ int mxfp4_quantize(const void* x, nvfp4_dtype dt, int64_t rows, int64_t cols, in
                    void* hip_stream);
 
 /*
+ * mxfp4_quantize_columns - MXFP4 quantization of x's columns: out [cols, rows] holds x^T
+ * quantized along its rows, exactly mxfp4_quantize of the transposed tensor (same scale rule,
+ * rounding and SR counters, with the half-block index b = (out_row*rows + out_col)/16 of the
+ * output), without materializing x^T. The activation- and weight-gradient GEMMs contract W,
+ * dY and X over their other dimension ("Nemotron NVFP4" explainer, "What NVFP4 actually is":
+ * the MXFP4 comparison format, 32-element blocks along the contraction).
+ *   x    device BF16 or FP32 [rows, cols], element (r, c) at x[r*ld + c]; element pairs aligned
+ *        (ld any); rows % 32 == 0.
+ *   out  out->rows == cols, out->cols == rows; codes 16-byte, scales 8-byte aligned.
+ * Errors: NVFP4_ERR_INVALID (null pointers, shapes, rows % 32, enums, alignment of out),
+ * NVFP4_ERR_UNSUPPORTED (misaligned x), NVFP4_ERR_HIP.
+ */
+int mxfp4_quantize_columns(const void* x, nvfp4_dtype dt, int64_t rows, int64_t cols, int64_t ld,
+                           nvfp4_round rnd, uint64_t seed, uint64_t offset, mxfp4_tensor* out,
+                           void* hip_stream);
+
+/*
  * mxfp4_gemm - D[M, N] (FP32, row stride ldd) = A[M, K] * B[N, K]^T with both operands MXFP4
  * (mxfp4_quantize along K): the comparison format of the pages ("Nemotron NVFP4" explainer,
  * "What NVFP4 actually is") on gfx950's block-scaled FP4 matrix instruction, which applies

@@ -225,6 +225,19 @@ def test_mx_quantize_validation(lib):
     assert f(FAKE + 2, 0, 32, 64, 64, 0, 0, 0, o, None) == UNSUPPORTED          # alignment
 
 
+def test_mx_quantize_columns_validation(lib):
+    f = lib.mxfp4_quantize_columns
+    out = nv._CMXTensor(FAKE, FAKE, 64, 32)                                      # [cols, rows]
+    o = ctypes.byref(out)
+    assert f(None, 0, 32, 64, 64, 0, 0, 0, o, None) == INVALID                  # x
+    assert f(FAKE, 0, 48, 64, 64, 0, 0, 0, ctypes.byref(nv._CMXTensor(FAKE, FAKE, 64, 48)), None) == INVALID
+    assert f(FAKE, 0, 32, 64, 64, 2, 0, 0, o, None) == INVALID                  # rounding
+    assert f(FAKE, 0, 32, 64, 64, 0, 0, 0, None, None) == INVALID               # out
+    assert f(FAKE, 0, 32, 64, 64, 0, 0, 0, ctypes.byref(nv._CMXTensor(FAKE, FAKE, 32, 64)), None) == INVALID
+    assert f(FAKE, 0, 32, 64, 64, 0, 0, 0, ctypes.byref(nv._CMXTensor(FAKE + 8, FAKE, 64, 32)), None) == INVALID
+    assert f(FAKE + 2, 0, 32, 64, 64, 0, 0, 0, o, None) == UNSUPPORTED          # pair alignment
+
+
 def test_binding_checks_buffers_before_calling(lib):
     # the C ABI sees only pointers: the binding refuses host tensors, short buffers and
     # outputs smaller than the result before anything reaches the library

@@ -102,3 +102,50 @@ def test_mx_gemm_unsupported_k():
     qb = nv.MXFP4Tensor.empty(16, 96)
     with pytest.raises(nv.NVFP4Error):
         nv.mx_gemm(qa, qb)
+
+
+@pytest.mark.parametrize("shape", [(32, 1), (64, 3), (96, 130), (256, 128), (288, 257), (2048, 640)])
+@pytest.mark.parametrize("rounding", ["rn", "sr"])
+def test_mx_quantize_columns_bf16(shape, rounding):
+    """x^T quantized without materializing it: equal to the oracle's row-wise MXFP4 of x^T
+    (ragged column tiles, rows not a multiple of the 256-row tile, SR counters of the output)."""
+    log(f"mx columns bf16 {shape} {rounding}")
+    bits = workloads.with_outliers_bf16(shape, 760 + shape[1])
+    q = nv.mx_quantize_columns(to_device_bf16(bits), rounding, seed=0x5EED, offset=9)
+    ref = oracle.quantize_mxfp4(np.ascontiguousarray(f32(bits).T), rounding, seed=0x5EED, offset=9)
+    _same(q, ref, f"mx columns {shape} {rounding}")
+
+
+@pytest.mark.parametrize("rounding", ["rn", "sr"])
+def test_mx_quantize_columns_fp32_strided_and_every_exponent(rounding):
+    """FP32 input with a row stride and an odd column count; and every finite BF16 pattern laid
+    out in columns (every exponent range, subnormals, zeros)."""
+    log(f"mx columns fp32 strided {rounding}")
+    rng = np.random.default_rng(77)
+    full = (rng.standard_normal((160, 100)) * np.exp2(rng.integers(-40, 40, (160, 1)))).astype(np.float32)
+    x = full[:, :77]
+    q = nv.mx_quantize_columns(to_device_f32(full)[:, :77], rounding, seed=3, offset=1 << 40)
+    _same(q, oracle.quantize_mxfp4(np.ascontiguousarray(x.T), rounding, seed=3, offset=1 << 40), "mx columns fp32")
+    u = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    u = u[((u >> 7) & 0xFF) != 0xFF]
+    n = len(u) // 2048 * 2048
+    bits = np.random.default_rng(2).permutation(u[:n]).reshape(-1, 64)          # [1020, 64]
+    bits = bits[: len(bits) // 32 * 32]
+    log(f"mx columns every bf16 pattern {rounding}")
+    q = nv.mx_quantize_columns(to_device_bf16(bits), rounding, seed=5)
+    _same(q, oracle.quantize_mxfp4(np.ascontiguousarray(f32(bits).T), rounding, seed=5), "mx columns every pattern")
+
+
+def test_mx_columns_feed_the_backward_gemms():
+    """The dgrad and wgrad operands made by the column quantization give the same GEMMs as the
+    row-wise quantization of torch's transposes (bit-identical operands, identical outputs)."""
+    log("mx columns in the backward GEMMs")
+    w = to_device_bf16(workloads.normal_bf16((256, 384), 780, std=0.02))      # W [N, K]
+    dy = to_device_bf16(workloads.normal_bf16((512, 256), 781, std=1e-3))     # dY [M, N]
+    qwt_c = nv.mx_quantize_columns(w, "rn")                                  # W^T [K, N]
+    qwt_t = nv.mx_quantize(w.t().contiguous(), "rn")
+    qdy = nv.mx_quantize(dy, "sr", seed=1)
+    a, b = nv.mx_gemm(qdy, qwt_c), nv.mx_gemm(qdy, qwt_t)
+    torch.cuda.synchronize()
+    assert torch.equal(qwt_c.codes, qwt_t.codes) and torch.equal(qwt_c.scales, qwt_t.scales)
+    assert torch.equal(a, b)
