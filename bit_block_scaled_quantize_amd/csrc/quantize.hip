@@ -606,8 +606,17 @@ __global__ __launch_bounds__(kThreads) void k_encode_16x16(
 
   const int64_t tiles_c = (cols + kTileCols - 1) / kTileCols;
   const int64_t tiles_r = (rows + kTileRows - 1) / kTileRows;
-  // reverse order of the amax pass
-  const int64_t t = tiles_r * tiles_c - 1 - (int64_t)blockIdx.x;
+  // Workgroups are dealt to the 8 XCDs round robin; XCD x takes a contiguous eighth of the
+  // tiles (whole rows of tiles), so the tiles that share a 128-byte line of codes (two tiles
+  // side by side) or of scales (up to sixteen) write it through one L2, which merges the
+  // pieces before the line goes to HBM (tiles on different XCDs wrote partial lines). Within
+  // an XCD the tiles run in the reverse order of the amax pass.
+  const int64_t n_tiles = tiles_r * tiles_c;
+  const int64_t per = (n_tiles + 7) / 8;
+  const int64_t xcd = blockIdx.x % 8, local = blockIdx.x / 8;
+  const int64_t tall = (n_tiles % 8) == 0 ? 8 : (n_tiles % 8);
+  const int64_t id = xcd < tall ? xcd * per + local : tall * per + (xcd - tall) * (per - 1) + local;
+  const int64_t t = n_tiles - 1 - id;
   const int64_t tile_r = t / tiles_c, tile_c = t - tile_r * tiles_c;
   const int64_t R0 = tile_r * kTileRows, C0 = tile_c * kTileCols;
 
