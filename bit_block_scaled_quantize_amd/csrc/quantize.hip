@@ -607,17 +607,31 @@ __global__ __launch_bounds__(kThreads) void k_encode_16x16(
   const int64_t tiles_c = (cols + kTileCols - 1) / kTileCols;
   const int64_t tiles_r = (rows + kTileRows - 1) / kTileRows;
   // Workgroups are dealt to the 8 XCDs round robin; XCD x takes a contiguous eighth of the
-  // tiles (whole rows of tiles), so the tiles that share a 128-byte line of codes (two tiles
-  // side by side) or of scales (up to sixteen) write it through one L2, which merges the
-  // pieces before the line goes to HBM (tiles on different XCDs wrote partial lines). Within
-  // an XCD the tiles run in the reverse order of the amax pass.
+  // walk, so the tiles that share a 128-byte line of codes or scales write it through one L2,
+  // which merges the pieces before the line goes to HBM (tiles on different XCDs wrote partial
+  // lines). The walk runs in the reverse order of the amax pass, by rows of tiles (side-by-side
+  // tiles share lines of x's codes and scales); with the transpose of one whole tensor, in
+  // bands of 8 rows of tiles, column by column, so that the up to 8 tiles stacked one above
+  // the other that share a line of x^T's scales also run back to back (measured 5% faster on
+  // a [20480, 5120] weight; on an expert stack the band walk measured 3% slower).
   const int64_t n_tiles = tiles_r * tiles_c;
   const int64_t per = (n_tiles + 7) / 8;
   const int64_t xcd = blockIdx.x % 8, local = blockIdx.x / 8;
   const int64_t tall = (n_tiles % 8) == 0 ? 8 : (n_tiles % 8);
   const int64_t id = xcd < tall ? xcd * per + local : tall * per + (xcd - tall) * (per - 1) + local;
   const int64_t t = n_tiles - 1 - id;
-  const int64_t tile_r = t / tiles_c, tile_c = t - tile_r * tiles_c;
+  int64_t tile_r, tile_c;
+  if constexpr (TRANS && !SEG) {
+    constexpr int64_t kBand = 8;
+    const int64_t first_r = (t / (kBand * tiles_c)) * kBand;
+    const int64_t gr = tiles_r - first_r < kBand ? tiles_r - first_r : kBand;
+    const int64_t in_band = t - first_r * tiles_c;
+    tile_r = first_r + in_band % gr;
+    tile_c = in_band / gr;
+  } else {
+    tile_r = t / tiles_c;
+    tile_c = t - tile_r * tiles_c;
+  }
   const int64_t R0 = tile_r * kTileRows, C0 = tile_c * kTileCols;
 
   const float a0 = fold_amax(amax, SEG ? 1 : amax_parts, red);
@@ -711,6 +725,38 @@ __global__ __launch_bounds__(kThreads) void k_encode_16x16(
     if constexpr (SEG) {
       // the rows R0 + 16 sp .. of a strip lie in one segment g: they go to x^T row
       // g*cols + C0 + cr at the strip's offset within its segment
+      if ((seg_rows & 63) == 0) {
+        // Segments then start on 4-strip boundaries (rows, and so R0 and valid_strips, are
+        // multiples of 64): the codes of strips 2i, 2i+1 and the scales of strips 4i .. 4i+3
+        // lie in one segment, 16- and 4-byte aligned in x^T (an expert's 928-byte x^T rows
+        // for 1856 rows put a tile's 128-byte pieces off line boundaries; whole 16-byte and
+        // 4-byte stores in place of 8-byte and single-byte ones).
+#pragma unroll
+        for (int pass = 0; pass < kTileCols * 8 / kThreads; ++pass) {
+          const int idx = pass * kThreads + threadIdx.x;
+          const int cr = idx >> 3, sp = (idx & 7) * 2;
+          if (cr < valid_cols && sp < valid_strips) {
+            const int64_t r = R0 + 16 * sp;
+            const int64_t g = r / seg_rows, lr = r - g * seg_rows;
+            const int64_t trow = g * cols + C0 + cr;
+            *reinterpret_cast<uint4*>(tcodes + trow * (seg_rows >> 1) + (lr >> 1)) =
+                *reinterpret_cast<const uint4*>(&tc[cr][sp * 8]);
+          }
+        }
+#pragma unroll
+        for (int pass = 0; pass < kTileCols * 4 / kThreads; ++pass) {
+          const int idx = pass * kThreads + threadIdx.x;
+          const int cr = idx >> 2, sp = (idx & 3) * 4;
+          if (cr < valid_cols && sp < valid_strips) {
+            const int64_t r = R0 + 16 * sp;
+            const int64_t g = r / seg_rows, lr = r - g * seg_rows;
+            const int64_t trow = g * cols + C0 + cr;
+            *reinterpret_cast<uint32_t*>(tscales + trow * (seg_rows >> 4) + (lr >> 4)) =
+                *reinterpret_cast<const uint32_t*>(&ts[cr][sp]);
+          }
+        }
+        return;
+      }
 #pragma unroll
       for (int pass = 0; pass < kTileCols * 16 / kThreads; ++pass) {
         const int idx = pass * kThreads + threadIdx.x;

@@ -255,7 +255,7 @@ def test_amax_pair(shape, dtype, ld):
         assert g[0] == nv.amax(dev).cpu().numpy()[0]
 
 
-@pytest.mark.parametrize("n,k,G", [(48, 272, 3), (1856, 160, 2), (16, 32, 5)])
+@pytest.mark.parametrize("n,k,G", [(48, 272, 3), (1856, 160, 2), (16, 32, 5), (320, 144, 3), (64, 400, 5)])
 def test_16x16_segments_with_transpose(n, k, G):
     """An expert weight stack [G*n, k] quantized in 16x16 tiles with one tensor scale per
     expert, and every expert's transpose stacked [G*k, n] (the grouped activation-gradient
