@@ -90,53 +90,166 @@ __global__ __launch_bounds__(kThreads) void k_amax_partial(const TIn* __restrict
 #pragma unroll
     for (int u = 0; u < kAmaxUnroll; ++u) m = fmaxf(m, a[u]);
   }
-  for (; q < q1; q += kThreads) {
-    const int64_t off = contiguous ? q * kVec : (q / vecs_per_row) * ld + (q % vecs_per_row) * kVec;
-    m = fmaxf(m, vec_absmax<TIn>(x + off));
+  if (q < q1) {
+    // the last (fewer than kAmaxUnroll) vectors of the thread, requested together: indices past
+    // the range read the range's last vector again, which leaves the maximum unchanged (a loop
+    // of single loads would pay one memory round trip per vector)
+    float a[kAmaxUnroll];
+#pragma unroll
+    for (int u = 0; u < kAmaxUnroll; ++u) {
+      const int64_t qq = q + u * kThreads < q1 ? q + u * kThreads : q1 - 1;
+      const int64_t off = contiguous ? qq * kVec : (qq / vecs_per_row) * ld + (qq % vecs_per_row) * kVec;
+      a[u] = vec_absmax<TIn>(x + off);
+    }
+#pragma unroll
+    for (int u = 0; u < kAmaxUnroll; ++u) m = fmaxf(m, a[u]);
   }
   m = block_max(m, red);
   if (threadIdx.x == 0) partial[blockIdx.x] = m;
 }
 
-// amax per row segment: each wave owns a contiguous row range, splits it at segment
-// boundaries (one table search per run, not per row), streams each run as one flat vector
-// range eight loads deep, and flushes one atomic max per run (the slots start at zero).
+// One 16-byte vector of inputs, loaded now and reduced later (so a batch of loads is in
+// flight before the first one is used).
+template <typename TIn>
+struct Vec16;
+
+template <>
+struct Vec16<uint16_t> {
+  v4u32 v;
+  __device__ __forceinline__ void load(const uint16_t* p) { v = ld_u32x4(p); }
+  __device__ __forceinline__ float absmax() const {
+    return fmaxf(fmaxf(fmaxf(fabsf(bf16_lo(v.x)), fabsf(bf16_hi(v.x))), fmaxf(fabsf(bf16_lo(v.y)), fabsf(bf16_hi(v.y)))),
+                 fmaxf(fmaxf(fabsf(bf16_lo(v.z)), fabsf(bf16_hi(v.z))), fmaxf(fabsf(bf16_lo(v.w)), fabsf(bf16_hi(v.w)))));
+  }
+};
+
+template <>
+struct Vec16<float> {
+  v4f32 v;
+  __device__ __forceinline__ void load(const float* p) { v = ld_f32x4(p); }
+  __device__ __forceinline__ float absmax() const {
+    return fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+  }
+};
+
+// amax per row segment (row r counts toward segment find_segment(seg, nseg, r)). Workgroup b
+// reduces a contiguous range of the tensor's 16-byte vectors, walked as in the unsegmented
+// pass (thread t takes vectors t, t + 256, ... of the range, eight requested at a time). A
+// thread's rows only grow along its walk, so it keeps the maximum of its current segment and
+// hands it to an LDS window of per-segment maxima (LDS atomics) when its row enters another
+// segment; the workgroup ends with one global atomic max per segment of the window it touched
+// (the slots start at zero). Offset tables of up to kSegTab entries are searched in LDS; the
+// table's loads are requested before the first vectors, so the search waits on one round trip
+// that the data loads share.
 template <typename TIn>
 __global__ __launch_bounds__(kThreads) void k_amax_seg(const TIn* __restrict__ x, int64_t rows,
                                                        int64_t vecs_per_row, int64_t ld,
                                                        const int64_t* __restrict__ seg, int64_t nseg,
                                                        float* __restrict__ amax_out) {
   constexpr int64_t kVec = 16 / sizeof(TIn);
-  const int lane = threadIdx.x & 63;
-  const int64_t wave = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
-  const int64_t nwaves = (int64_t)gridDim.x * kWavesPerBlock;
-  const int64_t per = (rows + nwaves - 1) / nwaves;
-  const int64_t r0 = wave * per;
-  const int64_t r1 = r0 + per < rows ? r0 + per : rows;
+  constexpr int kSegTab = 1024, kWin = 64;
+  __shared__ int64_t stab[kSegTab];
+  __shared__ unsigned int sacc[kWin];
+  __shared__ int64_t swin_s;
+  const int64_t total = rows * vecs_per_row;
+  const int64_t per = (total + gridDim.x - 1) / gridDim.x;
+  const int64_t q0 = (int64_t)blockIdx.x * per;
+  const int64_t q1 = q0 + per < total ? q0 + per : total;
+  if (q0 >= q1) return;                                     // uniform: an empty range
   const bool contiguous = ld == vecs_per_row * kVec;
-  int64_t r = r0;
-  while (r < r1) {
-    const int64_t sg = find_segment(seg, nseg, r);
-    int64_t e = sg + 1 <= nseg ? seg[sg + 1] : r1;
-    e = e > r1 ? r1 : (e <= r ? r + 1 : e);              // progress on a malformed table too
-    const TIn* xr = x + r * ld;
-    const int64_t total = (e - r) * vecs_per_row;
-    auto at = [&](int64_t q) {
-      return contiguous ? xr + q * kVec : xr + (q / vecs_per_row) * ld + (q % vecs_per_row) * kVec;
-    };
-    float m = 0.0f;
-    int64_t q = lane;
-    for (; q + (kAmaxUnroll - 1) * 64 < total; q += kAmaxUnroll * 64) {
-      float a[kAmaxUnroll];
+  const bool in_lds = nseg < kSegTab;                        // nseg + 1 offsets
+  const int64_t* off = in_lds ? stab : seg;
+
+  // the table's entries for this thread (clamped indices: every load is valid)
+  constexpr int kTabLoads = kSegTab / kThreads;
+  int64_t tv[kTabLoads];
+  if (in_lds) {
 #pragma unroll
-      for (int u = 0; u < kAmaxUnroll; ++u) a[u] = vec_absmax<TIn>(at(q + u * 64));
-#pragma unroll
-      for (int u = 0; u < kAmaxUnroll; ++u) m = fmaxf(m, a[u]);
+    for (int k = 0; k < kTabLoads; ++k) {
+      const int64_t i = threadIdx.x + k * kThreads;
+      tv[k] = seg[i <= nseg ? i : nseg];
     }
-    for (; q < total; q += 64) m = fmaxf(m, vec_absmax<TIn>(at(q)));
-    const float wm = wave_max(m);
-    if (lane == 0) atomic_max_nonneg(amax_out + sg, wm);
-    r = e;
+  }
+  // position of the thread's first vector, advanced by 256 vectors per step
+  const int64_t d_row = kThreads / vecs_per_row, d_col = kThreads % vecs_per_row;
+  int64_t q = q0 + threadIdx.x;
+  int64_t row = q / vecs_per_row, col = q - (q / vecs_per_row) * vecs_per_row;
+  const int64_t last_el = contiguous ? (q1 - 1) * kVec
+                                     : ((q1 - 1) / vecs_per_row) * ld + ((q1 - 1) % vecs_per_row) * kVec;
+  Vec16<TIn> a[kAmaxUnroll];
+  int64_t arow[kAmaxUnroll];
+  bool avalid[kAmaxUnroll];
+  // requests the next batch: vectors q, q + 256, ... (past the range: the range's last vector
+  // again, not counted)
+  auto issue = [&]() {
+#pragma unroll
+    for (int u = 0; u < kAmaxUnroll; ++u) {
+      const int64_t qq = q + u * kThreads;
+      avalid[u] = qq < q1;
+      arow[u] = row;
+      const int64_t off_el = !avalid[u] ? last_el : contiguous ? qq * kVec : row * ld + col * kVec;
+      a[u].load(x + off_el);
+      col += d_col;
+      row += d_row;
+      if (col >= vecs_per_row) {
+        col -= vecs_per_row;
+        ++row;
+      }
+    }
+    q += kAmaxUnroll * kThreads;
+  };
+  const bool any = q < q1;
+  if (any) issue();
+
+  if (in_lds) {
+#pragma unroll
+    for (int k = 0; k < kTabLoads; ++k) {
+      const int64_t i = threadIdx.x + k * kThreads;
+      if (i <= nseg) stab[i] = tv[k];
+    }
+  }
+  for (int i = threadIdx.x; i < kWin; i += kThreads) sacc[i] = 0u;
+  __syncthreads();
+  if (threadIdx.x == 0) swin_s = find_segment(off, nseg, q0 / vecs_per_row);
+  __syncthreads();
+  const int64_t swin = swin_s;
+
+  // the thread's current segment [.., seg_end) and its running maximum
+  int64_t cur = swin;
+  auto seg_end_of = [&](int64_t c) { return c + 1 < nseg ? off[c + 1] : INT64_MAX; };
+  int64_t seg_end = seg_end_of(cur);
+  float m = 0.0f;
+  auto flush = [&]() {
+    if (m > 0.0f) {
+      if (cur - swin < kWin) atomicMax(&sacc[cur - swin], __float_as_uint(m));
+      else atomic_max_nonneg(amax_out + cur, m);
+    }
+    m = 0.0f;
+  };
+  auto consume = [&]() {
+#pragma unroll
+    for (int u = 0; u < kAmaxUnroll; ++u) {
+      if (avalid[u]) {
+        if (arow[u] >= seg_end) {                            // rare: the next segment
+          flush();
+          while (cur + 1 < nseg && off[cur + 1] <= arow[u]) ++cur;
+          seg_end = seg_end_of(cur);
+        }
+        m = fmaxf(m, a[u].absmax());
+      }
+    }
+  };
+  bool pending = any;
+  while (pending) {
+    consume();
+    pending = q < q1;
+    if (pending) issue();
+  }
+  flush();
+  __syncthreads();
+  for (int i = threadIdx.x; i < kWin; i += kThreads) {
+    const unsigned int v = sacc[i];
+    if (v != 0u && swin + i < nseg) atomic_max_nonneg(amax_out + swin + i, __uint_as_float(v));
   }
 }
 
@@ -832,7 +945,7 @@ void amax_t(const void* x, int64_t rows, int64_t cols, int64_t ld, const int64_t
   const int64_t vpr = cols * (int64_t)sizeof(TIn) / 16;
   if (segments) {
     hipLaunchKernelGGL(k_fill, dim3(1), dim3(256), 0, stream, out, nseg, 0.0f);
-    const int grid = grid_for(rows, kWavesPerBlock, 1024);
+    const int grid = grid_for(rows * vpr, kThreads * 8, kMaxPartials);
     hipLaunchKernelGGL((k_amax_seg<TIn>), dim3(grid), dim3(kThreads), 0, stream, (const TIn*)x,
                        rows, vpr, ld, segments, nseg, out);
     *parts = 1;

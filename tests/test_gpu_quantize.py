@@ -108,6 +108,33 @@ def test_1x16_segments_and_amax_api():
         assert_quant_equal(host(q), ref, f"segments {rnd}")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("nseg,pad", [(7, 0), (300, 16), (1500, 0), (3000, 8)])
+def test_segment_amax_many_segments(dtype, nseg, pad):
+    """Per-segment maxima with many segments, empty ones included: offset tables searched in
+    LDS (up to 1023 segments) and in global memory, workgroups whose rows cross more segments
+    than their window of per-segment maxima, rows with a stride (pad columns between rows).
+    Every segment's maximum bit-exact against the oracle."""
+    log(f"segment amax nseg={nseg} pad={pad} {dtype}")
+    rng = np.random.default_rng(nseg + pad)
+    rows, cols = 6000, 48
+    seg = np.concatenate([[0], np.sort(rng.integers(0, rows + 1, nseg - 1)), [rows]]).astype(np.int64)
+    x = f32(workloads.normal_bf16((rows, cols), 700 + nseg))
+    x *= (np.float32(2.0) ** rng.integers(-30, 30, rows).astype(np.float32))[:, None]
+    x = f32(workloads.f32_to_bf16_bits(x)) if dtype == "bf16" else x
+    full = np.zeros((rows, cols + pad), np.float32)
+    full[:, :cols] = x
+    full[:, cols:] = 1e30                                     # must not count: past each row
+    if dtype == "bf16":
+        dev = to_device_bf16(workloads.f32_to_bf16_bits(full))[:, :cols]
+    else:
+        dev = torch.from_numpy(full).cuda()[:, :cols]
+    a = nv.amax(dev, torch.from_numpy(seg).cuda())
+    torch.cuda.synchronize()
+    assert_bytes_equal(a.cpu().numpy().view(np.uint32), oracle.amax(x, seg).view(np.uint32),
+                       f"segment amax nseg={nseg}")
+
+
 @pytest.mark.parametrize("shape", [(16, 16), (48, 80), (64, 1024), (160, 528)])
 def test_16x16_with_transpose(shape):
     log(f"16x16 {shape}")
