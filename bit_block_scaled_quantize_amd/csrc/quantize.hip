@@ -432,21 +432,36 @@ __global__ __launch_bounds__(kThreads) void k_encode_1x16(
   const int64_t nb = cols >> 4;
 
   // Rows are walked downwards (the amax pass left the last rows in cache): without segments
-  // with a stride of all waves, with segments as one contiguous row range per wave, so a wave
-  // meets few segment changes. Row r = base - it for it = it0, it0 + stride, ... < lim.
+  // with a stride of all waves; with segments, each workgroup takes a contiguous row range
+  // whose rows its waves share out in turn (wave w: the range's last row - w, then every
+  // fourth row), so a wave meets few segment changes and a workgroup's loads stay together.
+  // Row r = base - it for it = it0, it0 + stride, ... < lim.
   int64_t base = rows - 1, it0 = wave, stride = nwaves, lim = rows;
   if constexpr (SEG) {
-    const int64_t per = (rows + nwaves - 1) / nwaves;
-    const int64_t lo = wave * per < rows ? wave * per : rows;
+    const int64_t per = (rows + gridDim.x - 1) / gridDim.x;
+    const int64_t lo = (int64_t)blockIdx.x * per < rows ? (int64_t)blockIdx.x * per : rows;
     const int64_t hi = lo + per < rows ? lo + per : rows;
-    base = hi - 1;
+    const int w = threadIdx.x >> 6;
+    base = hi - 1 - w;
     it0 = 0;
-    stride = 1;
-    lim = hi - lo;
+    stride = kWavesPerBlock;
+    lim = hi - lo - w;
   }
   C cur, nxt;
   int64_t it = it0, b0 = 0;
   if (it < lim) cur.load(x + (base - it) * ld, b0, nb, lane);
+  // SEG: offset tables of up to kSegLds entries are searched in LDS (one round trip for the
+  // workgroup, requested behind the first chunk's loads, instead of a binary search through
+  // global memory per wave)
+  constexpr int kSegLds = SEG ? 1024 : 1;
+  __shared__ int64_t sseg[kSegLds];
+  const bool seg_in_lds = SEG && nseg < kSegLds;
+  if constexpr (SEG) {
+    if (seg_in_lds)
+      for (int64_t i = threadIdx.x; i <= nseg; i += kThreads) sseg[i] = seg[i];
+    __syncthreads();
+  }
+  const int64_t* off = seg_in_lds ? sseg : seg;
 
   const float a0 = fold_amax(amax, SEG ? 1 : amax_parts, red);
   if (blockIdx.x == 0) {
@@ -481,9 +496,9 @@ __global__ __launch_bounds__(kThreads) void k_encode_1x16(
     const int64_t r = base - it;
     if constexpr (SEG) {
       if (r < seg_lo || r >= seg_hi) {                       // uniform: another segment
-        const int64_t sg = find_segment(seg, nseg, r);
-        seg_lo = seg[sg];
-        seg_hi = seg[sg + 1];
+        const int64_t sg = find_segment(off, nseg, r);
+        seg_lo = off[sg];
+        seg_hi = off[sg + 1];
         s_enc = tensor_encode_scale(amax[sg]);
         __builtin_amdgcn_wave_barrier();                     // the wave's reads of the old table
         tab[lane] = block_recip(lane, s_enc);
