@@ -783,18 +783,33 @@ __global__ __launch_bounds__(kThreads) void k_encode_16x16(
   const bool active = r0 < rows && c0 < cols;
   const int64_t nb = cols >> 4;
 
-  float s_enc;
-  if constexpr (SEG) {
-    s_enc = tensor_encode_scale(amax[find_segment(seg, nseg, active ? r0 : 0)]);
-  } else {
-    s_enc = tensor_encode_scale(a0);
-  }
-
   Raw8<TIn> v[16];
   float m = 0.0f;
   const TIn* xp = x + (active ? r0 : 0) * ld + (active ? c0 : 0);
 #pragma unroll
   for (int j = 0; j < 16; ++j) v[j].load(xp + j * ld);
+
+  float s_enc;
+  if constexpr (SEG) {
+    // the segment starts and each segment's encode scale go to LDS in the round trip of the
+    // tile's loads (requested first) and the strip's segment is searched there (a binary
+    // search through global memory per thread cost several round trips per workgroup)
+    constexpr int kSegLds = 1024;
+    __shared__ int64_t sseg[kSegLds];
+    __shared__ float ssenc[kSegLds];
+    if (nseg < kSegLds) {
+      for (int64_t i = threadIdx.x; i <= nseg; i += kThreads) {
+        sseg[i] = seg[i];
+        if (i < nseg) ssenc[i] = tensor_encode_scale(amax[i]);
+      }
+      __syncthreads();
+      s_enc = ssenc[find_segment(sseg, nseg, active ? r0 : 0)];
+    } else {
+      s_enc = tensor_encode_scale(amax[find_segment(seg, nseg, active ? r0 : 0)]);
+    }
+  } else {
+    s_enc = tensor_encode_scale(a0);
+  }
 #pragma unroll
   for (int j = 0; j < 16; ++j)
 #pragma unroll
