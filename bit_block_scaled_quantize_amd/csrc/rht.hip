@@ -85,7 +85,7 @@ __device__ __forceinline__ float block_max(float m, float* red) {
 // touched (partial[segment], zeroed by the caller). The encode form takes the scale of the
 // item's segment.
 template <typename TIn, bool ENCODE, bool SR, bool PLAIN = false, bool SEG = false>
-__global__ __launch_bounds__(kThreads) void k_rht(
+__global__ __launch_bounds__(kThreads, (ENCODE && SEG && sizeof(TIn) == 2) ? 3 : 1) void k_rht(
     const TIn* __restrict__ x, int64_t tokens, int64_t cols, int64_t ld, uint32_t mask,
     const float* __restrict__ amax, int amax_parts, float* __restrict__ partial,
     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ gscale,
