@@ -38,6 +38,7 @@ struct ColPair<uint16_t> {
     if (both && paired) w = *reinterpret_cast<const uint32_t*>(p);
     else w = (uint32_t)p[0] | (both ? (uint32_t)p[1] << 16 : 0u);
   }
+  __device__ __forceinline__ void load_pair(const uint16_t* p) { w = *reinterpret_cast<const uint32_t*>(p); }
   __device__ __forceinline__ float get(int q) const { return q == 0 ? bf16_lo(w) : bf16_hi(w); }
 };
 
@@ -48,6 +49,7 @@ struct ColPair<float> {
     if (both && paired) w = *reinterpret_cast<const v2f32*>(p);
     else w = v2f32{p[0], both ? p[1] : 0.0f};
   }
+  __device__ __forceinline__ void load_pair(const float* p) { w = *reinterpret_cast<const v2f32*>(p); }
   __device__ __forceinline__ float get(int q) const { return q == 0 ? w.x : w.y; }
 };
 
@@ -76,8 +78,18 @@ __global__ __launch_bounds__(kThreads) void k_encode_mx_cols(
     const int64_t b = g.B0 + wave + kWaves * k;
     const int64_t bl = b < nblk ? b : 0;                          // clamped block for loads
     const TIn* p = x + bl * 32 * ld + cl;
+    if (paired && (g.C0 + kTileCols <= cols || (cols & 1) == 0)) {
+      // uniform: every lane's pair is whole and aligned (a full tile, or even rows; lanes past
+      // the row read columns 0 and 1, whose results are never written); branch-free loads keep
+      // all 32 rows in flight at once, where the per-element form's branches would make each
+      // load of a partial last tile wait for the one before. Odd strides or odd rows take the
+      // per-element loads.
 #pragma unroll
-    for (int j = 0; j < 32; ++j) raw[j].load(p + j * ld, c + 1 < cols, paired);
+      for (int j = 0; j < 32; ++j) raw[j].load_pair(p + j * ld);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 32; ++j) raw[j].load(p + j * ld, c + 1 < cols, paired);
+    }
   };
 
   ColPair<TIn> cur[32], nxt[32];

@@ -128,7 +128,12 @@ __global__ __launch_bounds__(kThreads, (ENCODE && SEG && sizeof(TIn) == 2) ? 3 :
     const int64_t tb = g.TB0 + wave + 4 * k;
     const int64_t tbl = tb < nbt ? tb : 0;                  // clamped token block for loads
     const TIn* p = x + tbl * 16 * ld + cl;
-    if (paired && g.C0 + kTileCols <= cols) {               // uniform: every pair whole, aligned
+    // uniform: every lane's pair is whole and aligned: in a full tile, or in the last, partial
+    // one when the rows are even (lanes past the row then read columns 0 and 1, whose results
+    // are never used). Only odd strides or odd rows take the per-element loads, whose branches
+    // make each load wait for the one before (a partial last tile read that way cost 2-3 full
+    // tiles: [102656, 1856] at 2.7 TB/s against 4.1 TB/s at 1920 columns).
+    if (paired && (g.C0 + kTileCols <= cols || (cols & 1) == 0)) {
 #pragma unroll
       for (int j = 0; j < 16; ++j) raw[j].load_pair(p + j * ld);
     } else {

@@ -156,7 +156,7 @@ def test_16x16_fp32_segments():
     assert_quant_equal(host(q), oracle.quantize_16x16(x, segments=seg), "16x16 segments")
 
 
-@pytest.mark.parametrize("shape", [(16, 1), (32, 7), (256, 129), (48, 513)])
+@pytest.mark.parametrize("shape", [(16, 1), (32, 7), (256, 129), (48, 513), (64, 200), (32, 130)])
 @pytest.mark.parametrize("rounding", ["rn", "sr"])
 def test_rht_quantize(shape, rounding):
     log(f"rht {shape} {rounding}")
