@@ -101,7 +101,8 @@ __global__ __launch_bounds__(kThreads, (ENCODE && SEG && sizeof(TIn) == 2) ? 3 :
   __shared__ float sexact[kWaves][kRhtExactLds];  // the exact transform's per-wave slots
   constexpr bool kBlocked = SEG;                 // contiguous tile range per workgroup
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: scalar registers
   const int64_t nbt = tokens >> 4;
   const u16x2 two = opaque_two();                  // for the range test's packed minimum
   const int64_t tiles_c = (cols + kTileCols - 1) / kTileCols;
