@@ -59,7 +59,8 @@ __global__ __launch_bounds__(kThreads) void k_encode_mx_cols(
     uint8_t* __restrict__ scales, uint64_t seed, uint64_t offset) {
   __shared__ __attribute__((aligned(16))) uint8_t tc[kTileCols][kTileRows / 2];
   __shared__ __attribute__((aligned(16))) uint8_t ts[kTileCols][kBlocksPerTile];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: scalar registers
   const int64_t nblk = rows >> 5;                               // 32-row blocks
   const int64_t tiles_c = (cols + kTileCols - 1) / kTileCols;
   const int64_t tiles = tiles_c * ((nblk + kBlocksPerTile - 1) / kBlocksPerTile);

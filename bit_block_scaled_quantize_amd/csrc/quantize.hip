@@ -427,7 +427,7 @@ __global__ __launch_bounds__(kThreads) void k_encode_1x16(
   __shared__ float red[kWavesPerBlock];
   __shared__ float rexact[ROT ? kWavesPerBlock : 1][ROT ? kRhtExactLds : 1];   // exact transform slots
   const int lane = threadIdx.x & 63;
-  const int64_t wave = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  const int64_t wave = (int64_t)blockIdx.x * kWavesPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t nwaves = (int64_t)gridDim.x * kWavesPerBlock;
   const int64_t nb = cols >> 4;
 
@@ -441,7 +441,7 @@ __global__ __launch_bounds__(kThreads) void k_encode_1x16(
     const int64_t per = (rows + gridDim.x - 1) / gridDim.x;
     const int64_t lo = (int64_t)blockIdx.x * per < rows ? (int64_t)blockIdx.x * per : rows;
     const int64_t hi = lo + per < rows ? lo + per : rows;
-    const int w = threadIdx.x >> 6;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     base = hi - 1 - w;
     it0 = 0;
     stride = kWavesPerBlock;
@@ -476,7 +476,7 @@ __global__ __launch_bounds__(kThreads) void k_encode_1x16(
   // wave, rebuilt when the wave enters another segment. seg_lo/seg_hi: the current segment's
   // row range (empty before the first row).
   __shared__ float rtab[SEG ? kWavesPerBlock : 1][128];
-  float* tab = rtab[SEG ? (threadIdx.x >> 6) : 0];
+  float* tab = rtab[SEG ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : 0];
   int64_t seg_lo = 0, seg_hi = 0;
   if constexpr (!SEG) {
     build_recip_table(s_enc, tab);
@@ -535,7 +535,7 @@ __global__ __launch_bounds__(kThreads) void k_encode_1x16(
       }
       finish(u, v, bm);
     }
-    if constexpr (ROT) rot_pending<true>(pending, x + r * ld, b0, nb, lane, mask, rexact[threadIdx.x >> 6], finish);
+    if constexpr (ROT) rot_pending<true>(pending, x + r * ld, b0, nb, lane, mask, rexact[__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)], finish);
     it = it_n;
     b0 = b0_n;
   };
@@ -557,7 +557,7 @@ __global__ __launch_bounds__(kThreads) void k_amax_rot(const TIn* __restrict__ x
   __shared__ float red[kWavesPerBlock];
   __shared__ float rexact[kWavesPerBlock][kRhtExactLds];                   // exact transform slots
   const int lane = threadIdx.x & 63;
-  const int64_t wave = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  const int64_t wave = (int64_t)blockIdx.x * kWavesPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t nwaves = (int64_t)gridDim.x * kWavesPerBlock;
   const int64_t nb = cols >> 4;
   C cur, nxt;
@@ -581,7 +581,7 @@ __global__ __launch_bounds__(kThreads) void k_amax_rot(const TIn* __restrict__ x
       if (rot_block(cur, u, lane, mask, y, bm)) finish(u, y, bm);
       else pending |= 1u << u;
     }
-    rot_pending<false>(pending, x + r * ld, b0, nb, lane, mask, rexact[threadIdx.x >> 6], finish);
+    rot_pending<false>(pending, x + r * ld, b0, nb, lane, mask, rexact[__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)], finish);
     r = r_n;
     b0 = b0_n;
   };
@@ -619,7 +619,7 @@ __global__ __launch_bounds__(kThreads) void k_encode_mx(const TIn* __restrict__ 
   constexpr int U = C::U;
   constexpr int64_t kSpan = 64 * U;
   const int lane = threadIdx.x & 63;
-  const int64_t wave = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  const int64_t wave = (int64_t)blockIdx.x * kWavesPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t nwaves = (int64_t)gridDim.x * kWavesPerBlock;
   const int64_t nb = cols >> 4;                        // 16-element halves per row (even)
 
