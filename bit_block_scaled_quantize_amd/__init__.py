@@ -153,16 +153,24 @@ class NVFP4Tensor:
 
 @dataclass
 class MXFP4Tensor:
-    """Device buffers of one MXFP4 tensor [rows, cols] quantized along cols."""
+    """Device buffers of one MXFP4 tensor [rows, cols] quantized along cols. The E8M0 scales
+    are stored K step by K step: [ceil(cols/128), rows, 4], scale j of row r at [j // 4, r,
+    j % 4] (one 128-element step's scales of all rows contiguous, as the GEMM reads them)."""
     codes: torch.Tensor         # uint8 [rows, cols/2]
-    scales: torch.Tensor        # uint8 [rows, cols/32] (E8M0 codes)
+    scales: torch.Tensor        # uint8 [ceil(cols/128), rows, 4] (E8M0 codes)
     rows: int
     cols: int
 
     @classmethod
     def empty(cls, rows: int, cols: int, device="cuda"):
         return cls(torch.empty((rows, cols // 2), dtype=torch.uint8, device=device),
-                   torch.empty((rows, cols // 32), dtype=torch.uint8, device=device), rows, cols)
+                   torch.empty(((cols + 127) // 128, rows, 4), dtype=torch.uint8, device=device), rows, cols)
+
+    def scales_by_row(self) -> torch.Tensor:
+        """The scales as [rows, cols/32] (row r's j-th scale at [r, j]), a copy."""
+        steps = (self.cols + 127) // 128
+        s = self.scales.reshape(steps, self.rows, 4).permute(1, 0, 2).reshape(self.rows, steps * 4)
+        return s[:, : self.cols // 32].contiguous()
 
     def c(self) -> _CMXTensor:
         return _CMXTensor(self.codes.data_ptr(), self.scales.data_ptr(), self.rows, self.cols)
@@ -180,7 +188,8 @@ def _check_q(q, nseg: int = 1, what: str = "tensor"):
     """The C ABI sees only pointers: make sure the torch buffers behind an NVFP4/MXFP4 tensor
     are as large as its rows and cols say (and contiguous), so no kernel writes past them."""
     mx = isinstance(q, MXFP4Tensor)
-    need = ((q.codes, q.rows * (q.cols // 2)), (q.scales, q.rows * (q.cols // (32 if mx else 16))))
+    need = ((q.codes, q.rows * (q.cols // 2)),
+            (q.scales, q.rows * 4 * ((q.cols + 127) // 128) if mx else q.rows * (q.cols // 16)))
     if not mx:
         need += ((q.global_scale, nseg),)
     for t, n in need:

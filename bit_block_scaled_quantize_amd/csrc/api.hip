@@ -409,6 +409,7 @@ static int check_mx_operand(const mxfp4_tensor* t, const char* name) {
   if (t->rows == 0) return NVFP4_OK;
   if (!t->codes || !t->scales) return fail(NVFP4_ERR_INVALID, "%s has a NULL codes/scales pointer", name);
   if (!aligned(t->codes, 16)) return fail(NVFP4_ERR_INVALID, "%s codes must be 16-byte aligned", name);
+  if (!aligned(t->scales, 4)) return fail(NVFP4_ERR_INVALID, "%s scales must be 4-byte aligned", name);
   if (t->rows * (t->cols / 2) > (int64_t)0x7FFFFFFF)
     return fail(NVFP4_ERR_UNSUPPORTED, "%s codes exceed 2 GiB", name);
   return NVFP4_OK;

@@ -986,22 +986,23 @@ void k_grouped_gemm_small(int64_t G, const int64_t* __restrict__ off, Operand A,
 // steps deep. The matrix instruction consumes a step's operands four times faster than the
 // FP16 path, so what limits this kernel is the number of L2 requests the buffer-to-LDS DMA
 // makes, not bytes: four lanes read a row's 64 bytes of a step (one request per row and step
-// instead of two), and the E8M0 bytes move 16 per row (four steps) per request into a
-// two-deep ring. (Stages of 256 elements, whose rows are whole 128-byte lines, fit only two
-// deep in LDS and were slower: the prefetch distance matters more than the request count.)
-// In LDS a fragment is 32 rows x 64 bytes, row-major, with the 16-byte chunk c of row r
-// stored at slot c ^ sw(r) (below), so the instruction's 16-byte reads (row r, chunk 2s + h)
-// fall in distinct banks.
+// instead of two). The scales are stored K step by K step (all rows' four E8M0 bytes of one
+// 128-element step contiguous, see mxfp4_tensor), so a wave's scale DMA of a step is 256
+// contiguous bytes (two requests for 64 rows, where row-major scales took one request per
+// row), lands in LDS as one dword per row, and the per-row scale reads are conflict-free
+// (row-major groups of 16 bytes per row put rows r, r+8, r+16, r+24 in one bank). (Stages
+// of 256 elements, whose rows are whole 128-byte lines, fit only two deep in LDS and were
+// slower: the prefetch distance matters more than the request count.) In LDS a fragment is
+// 32 rows x 64 bytes, row-major, with the 16-byte chunk c of row r stored at slot c ^ sw(r)
+// (below), so the instruction's 16-byte reads (row r, chunk 2s + h) fall in distinct banks.
 namespace mx {
 constexpr int kBlockM = 256, kBlockN = 256, kFragsA = 8, kFrags = 16;
 constexpr int kFragBytes = 2048;                                  // 32 rows x 64 bytes
 constexpr int kCodeBytes = kFrags * kFragBytes;                   // 32 KB per K step
 constexpr int kStages = 4;
-constexpr int kGroupSteps = 4;                                    // K steps per scale move
-constexpr int kScaleGroupBytes = (kBlockM + kBlockN) * 16;        // 16 bytes per row: 8 KB
+constexpr int kScaleStageBytes = (kBlockM + kBlockN) * 4;         // a step's E8M0 dword per row
 constexpr int kScaleBase = kStages * kCodeBytes;
-constexpr int kPadBase = kScaleBase + 2 * kScaleGroupBytes;       // target of idle scale moves
-constexpr int kLdsBytes = kPadBase + 1024;                        // 145 KB
+constexpr int kLdsBytes = kScaleBase + kStages * kScaleStageBytes;  // 136 KB
 }  // namespace mx
 constexpr int kMxThreads = 512;                                   // 8 waves, 2 per SIMD
 
@@ -1029,39 +1030,41 @@ void k_gemm_mx(Operand A, Operand B, int64_t K, float* __restrict__ D, int64_t l
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 31, h = lane >> 5;
   const int wm = wave >> 1, wn = wave & 1;
-  const uint32_t rs_codes = (uint32_t)(K >> 1), rs_scales = (uint32_t)(K >> 5);
+  const uint32_t rs_codes = (uint32_t)(K >> 1);
   constexpr uint32_t kBeyond = 0x80000000u;
   const int steps = __builtin_amdgcn_readfirstlane((int)(K / kStepK));
   const __amdgpu_buffer_rsrc_t a_codes = make_rsrc(A.codes, A.rows * (K >> 1));
   const __amdgpu_buffer_rsrc_t b_codes = make_rsrc(B.codes, B.rows * (K >> 1));
   const __amdgpu_buffer_rsrc_t a_scales = make_rsrc(A.scales, A.rows * (K >> 5));
   const __amdgpu_buffer_rsrc_t b_scales = make_rsrc(B.scales, B.rows * (K >> 5));
+  // scale DMA: wave w moves the step's dwords of rows 64 w .. 64 w + 63 of the tile's 512 (A
+  // rows for w < 4, then B), lane l one row; rows past the operand read as zero (a row's dword
+  // of step s sits at (s * rows + row) * 4, so a row past the end would alias the next step)
+  const int sblk = wave;
+  const bool s_is_a = sblk < 4;
+  const int64_t s_rows = s_is_a ? A.rows : B.rows;
+  const int64_t s_row = (s_is_a ? m0 : n0) + 64 * (s_is_a ? sblk : sblk - 4) + lane;
+  const uint32_t lane_scales = s_row < s_rows ? (uint32_t)(s_row * 4) : kBeyond;
+  const uint32_t step_scales = (uint32_t)(s_rows * 4);      // bytes per K step of scales
   // DMA for K step `step` (into code buffer `buf`), 5 operations per wave:
   //  p = 0..3: half q = p & 1 (rows 16q .. +15) of fragment f = wave + 8 (p >> 1) (A for
   //    p < 2, B after); lane l reads row 16q + l/4, chunk (l & 3) ^ sw(16q + l/4) of the
   //    step's 64 bytes into LDS f * 2 KB + q * 1 KB + l * 16 (row r's chunk c sits at 16-byte
   //    slot c ^ sw(r) of the row's 64 bytes; sw(16q + l/4) = ((l >> 3) & 3) ^ ((l >> 5) & 1)).
-  //  p = 4: the E8M0 bytes of steps step .. step+3 when step % 4 == 0 (group step/4 into scale
-  //    buffer (step/4) % 2), rows 64 wave .. +63 of the 512 (A then B), lane l one row's 16
-  //    bytes; other steps issue it idle (out of range, into a pad area), so every step issues
-  //    the same number of operations and the waits are constant.
+  //  p = 4: the step's E8M0 dwords of rows 64 wave .. +63 of the 512 (A then B), lane l one
+  //    row, into the stage's scale buffer.
   // Steps past the last are issued out of range too (zeros, no memory traffic) into buffers
   // nobody reads again, so the loop has no branches.
   constexpr int kOps = 5;
   const uint32_t lane_codes = (uint32_t)(lane >> 2) * rs_codes +
                               16u * (uint32_t)((lane & 3) ^ ((lane >> 3) & 3) ^ ((lane >> 5) & 1));
-  const uint32_t lane_scales = (uint32_t)lane * rs_scales;
   auto issue_dma_part = [&](int step, int buf, int p) {
     const bool live = step < steps;
     if (p == 4) {
-      const bool real = live && (step % kGroupSteps) == 0;
-      const int blk = wave;
-      const bool is_a = blk < 4;
-      const uint32_t row0 = (uint32_t)((is_a ? m0 : n0) + 64 * (is_a ? blk : blk - 4));
-      const uint32_t su = row0 * rs_scales + (uint32_t)(step * (kStepK / 32));
-      uint8_t* dst = real ? lds + kScaleBase + ((step / kGroupSteps) & 1) * kScaleGroupBytes + blk * 1024 : lds + kPadBase;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a ? a_scales : b_scales, (lds_ptr_t)dst, 16,
-                                               lane_scales + (real ? su : kBeyond), 0, 0, 0);
+      uint8_t* dst = lds + kScaleBase + buf * kScaleStageBytes + sblk * 256;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(s_is_a ? a_scales : b_scales, (lds_ptr_t)dst, 4,
+                                               live ? lane_scales + (uint32_t)step * step_scales : kBeyond,
+                                               0, 0, 0);
     } else {
       const int q = p & 1, f = wave + 8 * (p >> 1);
       const bool is_a = (p >> 1) == 0;
@@ -1083,9 +1086,8 @@ void k_gemm_mx(Operand A, Operand B, int64_t K, float* __restrict__ D, int64_t l
   // to byte 0 (the byte the instruction reads). The swizzle sw(r) = ((r >> 1) & 3) ^
   // ((r >> 3) & 1) spreads the 16-byte reads of any 8 consecutive rows over the 128 bytes of
   // 32 banks and of any 16 consecutive rows over the 256 bytes of 64 banks.
-  // The step's scale dwords are read from LDS with half 0 and kept for half 1 (the reads
-  // stride 16 bytes per row, so they meet bank conflicts: once per step halves them; whole
-  // 16-byte groups kept over four steps would not fit the registers of two waves per SIMD).
+  // The step's scale dwords (one per row, consecutive rows in consecutive banks) are read
+  // with half 0 and kept for half 1.
   struct Ops { v4u32 a[2], b[4]; uint32_t sa[2], sb[4]; };
   uint32_t raw_sa[2], raw_sb[4];
   auto read_ops = [&](int step, int buf, int s2, Ops& o) {
@@ -1096,11 +1098,11 @@ void k_gemm_mx(Operand A, Operand B, int64_t K, float* __restrict__ D, int64_t l
 #pragma unroll
     for (int j = 0; j < 4; ++j) o.b[j] = *reinterpret_cast<const v4u32*>(base + (kFragsA + wn * 4 + j) * kFragBytes);
     if (s2 == 0) {
-      const uint8_t* sc = lds + kScaleBase + ((step / kGroupSteps) & 1) * kScaleGroupBytes + (step % kGroupSteps) * 4 + r * 16;
+      const uint8_t* sc = lds + kScaleBase + buf * kScaleStageBytes + r * 4;
 #pragma unroll
-      for (int i = 0; i < 2; ++i) raw_sa[i] = *reinterpret_cast<const uint32_t*>(sc + ((wm * 2 + i) * 32) * 16);
+      for (int i = 0; i < 2; ++i) raw_sa[i] = *reinterpret_cast<const uint32_t*>(sc + ((wm * 2 + i) * 32) * 4);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) raw_sb[j] = *reinterpret_cast<const uint32_t*>(sc + (kBlockM + (wn * 4 + j) * 32) * 16);
+      for (int j = 0; j < 4; ++j) raw_sb[j] = *reinterpret_cast<const uint32_t*>(sc + (kBlockM + (wn * 4 + j) * 32) * 4);
     }
     const int sh = 8 * (2 * s2 + h);
 #pragma unroll

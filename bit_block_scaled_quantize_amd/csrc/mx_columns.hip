@@ -12,8 +12,9 @@
 // and 2l+1, so a wave-wide load of one row is 256 contiguous bytes (BF16); wave w takes the
 // 32-row blocks w and w + 4 of the tile. Workgroups walk tiles with a stride of the grid (the
 // resident workgroup count); each wave requests its next block's 32 rows before encoding the
-// current one. Codes and E8M0 bytes are staged in LDS as [column][row] and written out as
-// 128-byte (codes) and 8-byte (scales) row segments of the transposed tensor.
+// current one. Codes and E8M0 bytes are staged in LDS as [column][row]; codes go out as
+// 128-byte row segments of the transposed tensor, scales as two 4-byte pieces per output row
+// (the scale layout is K step by K step, so consecutive output rows' pieces are consecutive).
 #include "device_common.h"
 #include "launch.h"
 
@@ -152,13 +153,20 @@ __global__ __launch_bounds__(kThreads) void k_encode_mx_cols(
           *reinterpret_cast<uint4*>(codes + (g.C0 + cr) * (rows >> 1) + (g.B0 + p) * 16) =
               *reinterpret_cast<const uint4*>(&tc[cr][p * 16]);
       }
+      // scales K step by K step (block j of output row c at byte ((j / 4) * cols + c) * 4 +
+      // j % 4): the tile's 8 blocks are two 4-byte pieces of each output row, and consecutive
+      // output rows' pieces are consecutive dwords
       if (threadIdx.x < valid_cols) {
+        const int64_t c = g.C0 + threadIdx.x;
         const int cr = threadIdx.x;
-        uint8_t* dst = scales + (g.C0 + cr) * nblk + g.B0;
-        if (valid_b == kBlocksPerTile && ((reinterpret_cast<uintptr_t>(dst) & 7) == 0)) {
-          *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<const uint2*>(&ts[cr][0]);
+        if (valid_b == kBlocksPerTile) {
+          *reinterpret_cast<uint32_t*>(scales + ((g.B0 >> 2) * cols + c) * 4) =
+              *reinterpret_cast<const uint32_t*>(&ts[cr][0]);
+          *reinterpret_cast<uint32_t*>(scales + (((g.B0 >> 2) + 1) * cols + c) * 4) =
+              *reinterpret_cast<const uint32_t*>(&ts[cr][4]);
         } else {
-          for (int p = 0; p < valid_b; ++p) dst[p] = ts[cr][p];
+          for (int p = 0; p < valid_b; ++p)
+            scales[(((g.B0 + p) >> 2) * cols + c) * 4 + ((g.B0 + p) & 3)] = ts[cr][p];
         }
       }
       __syncthreads();                                            // LDS reused by the next tile

@@ -75,10 +75,14 @@ typedef struct nvfp4_tensor {
 } nvfp4_tensor;
 
 /* MXFP4 tensor [rows, cols] quantized along cols: codes as nvfp4_tensor, one E8M0 scale per
- * 32 elements (value 2^(code - 127)), no tensor-level scale. */
+ * 32 elements (value 2^(code - 127)), no tensor-level scale. The scales are stored K step by
+ * K step: scale j of row r (elements 32j .. 32j+31) at byte ((j / 4) * rows + r) * 4 + j % 4,
+ * ceil(cols/128) * rows * 4 bytes, so the four scales of one 128-element step of all rows are
+ * contiguous (one DMA request per 32 rows in the GEMM, conflict-free reads in LDS); bytes past
+ * a row's last block (cols % 128 != 0) are left unwritten. */
 typedef struct mxfp4_tensor {
-  uint8_t* codes;        /* device, [rows, cols/2]  */
-  uint8_t* scales;       /* device, [rows, cols/32] */
+  uint8_t* codes;        /* device, [rows, cols/2]                     */
+  uint8_t* scales;       /* device, [ceil(cols/128), rows, 4] (above)  */
   int64_t rows;
   int64_t cols;          /* % 32 == 0 */
 } mxfp4_tensor;
@@ -220,8 +224,8 @@ int mxfp4_quantize_columns(const void* x, nvfp4_dtype dt, int64_t rows, int64_t 
  * "What NVFP4 actually is") on gfx950's block-scaled FP4 matrix instruction, which applies
  * the E8M0 scales of each 32-element block itself. Products exact, FP32 accumulation.
  *   A: rows = M, cols = K; B: rows = N, cols = K (same K, K % 128 == 0); ldd >= N; each
- *   operand's codes below 2 GiB.
- * Errors: NVFP4_ERR_INVALID (null pointers, K mismatch, cols % 32, ldd < N),
+ *   operand's codes below 2 GiB, codes 16-byte and scales 4-byte aligned.
+ * Errors: NVFP4_ERR_INVALID (null pointers, K mismatch, cols % 32, ldd < N, alignment),
  * NVFP4_ERR_UNSUPPORTED (K % 128, operand size), NVFP4_ERR_HIP.
  */
 int mxfp4_gemm(const mxfp4_tensor* A, const mxfp4_tensor* B, float* D, int64_t ldd, void* hip_stream);

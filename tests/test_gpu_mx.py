@@ -20,7 +20,7 @@ def _need_gpu():
 
 def _host(q):
     torch.cuda.synchronize()
-    return q.codes.cpu().numpy(), q.scales.cpu().numpy()
+    return q.codes.cpu().numpy(), q.scales_by_row().cpu().numpy()
 
 
 def _same(q, ref, what):
@@ -51,6 +51,24 @@ def test_mx_quantize_fp32_strided_and_wide_exponents(rounding):
     dev = to_device_f32(x)[:, :cols]
     q = nv.mx_quantize(dev, rounding, seed=99, offset=1 << 33)
     _same(q, oracle.quantize_mxfp4(x[:, :cols], rounding, seed=99, offset=1 << 33), f"mx fp32 {rounding}")
+
+
+@pytest.mark.parametrize("dtype,shape", [("fp32", (64, 96)), ("fp32", (32, 2560)), ("bf16", (256, 32)),
+                                         ("bf16", (96, 1408))])
+def test_mx_quantize_contiguous_short_and_partial_rows(dtype, shape):
+    """Contiguous FP32 and BF16 inputs, rows down to one 32-block and rows that end inside a
+    128-column K step: every scale lands at its row and block of the K-step layout."""
+    log(f"mx flat {dtype} {shape}")
+    if dtype == "fp32":
+        x = np.random.default_rng(shape[1]).standard_normal(shape).astype(np.float32)
+        dev = to_device_f32(x)
+    else:
+        x = workloads.with_outliers_bf16(shape, 900 + shape[0])
+        dev = to_device_bf16(x)
+        x = f32(x)
+    for rounding in ("rn", "sr"):
+        q = nv.mx_quantize(dev, rounding, seed=21, offset=5)
+        _same(q, oracle.quantize_mxfp4(x, rounding, seed=21, offset=5), f"mx flat {dtype} {shape} {rounding}")
 
 
 def test_mx_quantize_every_bf16_pattern():
@@ -147,5 +165,5 @@ def test_mx_columns_feed_the_backward_gemms():
     qdy = nv.mx_quantize(dy, "sr", seed=1)
     a, b = nv.mx_gemm(qdy, qwt_c), nv.mx_gemm(qdy, qwt_t)
     torch.cuda.synchronize()
-    assert torch.equal(qwt_c.codes, qwt_t.codes) and torch.equal(qwt_c.scales, qwt_t.scales)
+    assert torch.equal(qwt_c.codes, qwt_t.codes) and torch.equal(qwt_c.scales_by_row(), qwt_t.scales_by_row())
     assert torch.equal(a, b)
