@@ -573,6 +573,44 @@ __device__ __forceinline__ void gemm_tile_big(Operand A, Operand B, int64_t m0, 
       return;
     }
   }
+  if constexpr (!EXT) {
+    if (!accumulate && ldd <= (int64_t(1) << 20)) {
+      // Plain FP32 stores through a buffer resource from the tile's corner to its last element
+      // inside D (row m1 - 1, column n1 - 1): stores of rows past m1 fall outside it and the
+      // buffer unit drops them, columns past n1 get an offset beyond any range. An element's
+      // offset is the lane's column offset (per j, a vector register) plus its row's offset
+      // (per i and q, uniform): no per-element bounds test or 64-bit address arithmetic, which
+      // cost about 8 us per 256 x 256 tile with one wave per SIMD. ldd <= 2^20 keeps every
+      // offset, pushed past the range or not, below 2^32.
+      // (base and size made scalar: the compiler cannot see that they are uniform, and a
+      // resource in vector registers makes it loop over the lanes for every store)
+      const uint32_t ld4 = (uint32_t)ldd * 4u;
+      const uint64_t base = reinterpret_cast<uint64_t>(D + m0 * ldd + n0);
+      const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)base);
+      const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(base >> 32));
+      const int64_t size = __builtin_amdgcn_readfirstlane((uint32_t)((m1 - m0 - 1) * ldd * 4 + (n1 - n0) * 4));
+      const __amdgpu_buffer_rsrc_t dr =
+          make_rsrc(reinterpret_cast<const void*>(((uint64_t)hi << 32) | lo), size);
+      uint32_t voff[kFragsN];
+#pragma unroll
+      for (int j = 0; j < kFragsN; ++j) {
+        const int cl = wn * kWaveN + 32 * j + r;                    // column within the tile
+        voff[j] = n0 + cl < n1 ? (uint32_t)(4 * h) * ld4 + (uint32_t)cl * 4u : kBeyond;
+      }
+#pragma unroll
+      for (int i = 0; i < kFragsM; ++i) {
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          const uint32_t ro = (uint32_t)(wm * kWaveM + 32 * i + 8 * (q >> 2) + (q & 3)) * ld4;
+#pragma unroll
+          for (int j = 0; j < kFragsN; ++j)          // non-temporal, as below
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][q] * alpha), dr,
+                                                  voff[j] + ro, 0, 2);
+        }
+      }
+      return;
+    }
+  }
 #pragma unroll
   for (int i = 0; i < kFragsM; ++i) {
 #pragma unroll
