@@ -509,6 +509,84 @@ __device__ __forceinline__ void gemm_tile_big(Operand A, Operand B, int64_t m0, 
   // D fragment layout (32 x 32): lane l holds column l % 32 and, for q = 0..15, row
   // 8*(q/4) + 4*(l/32) + q%4.
   float mx = 0.0f;
+  // Plain FP32 and BF16 outputs (not a K-split tile's partial sums) go through a buffer
+  // resource from the tile's corner to its last element in the output (row m1 - 1, column
+  // n1 - 1): stores to rows past m1 fall outside it and the buffer unit drops them, columns
+  // past n1 get an offset beyond any range. An element's offset is the lane's column offset
+  // (per j, a vector register) plus its row's offset (per i and q, uniform): no per-element
+  // bounds test or 64-bit address arithmetic, which cost about 8 us per 256 x 256 tile with one
+  // wave per SIMD. The maximum for the amax output counts only elements inside
+  // the tile's bounds (a grouped tile's rows past m1 hold the next group's products). A row
+  // pitch of at most 2^20 elements keeps every offset, pushed past the range or not, below 2^32.
+  {
+    constexpr int kES = (EXT && KIND == kOutBF16) ? 2 : 4;          // output element bytes
+    // (the FP32 outputs with an amax or an accumulate keep the path further below: with this
+    // one their kernels spill registers)
+    constexpr bool kFast = !EXT || KIND == kOutBF16;
+    const int64_t ldo = EXT ? ext.ldd : ldd;
+    if (kFast && !accumulate && ldo <= (int64_t(1) << 20)) {
+      uint8_t* const out = EXT ? static_cast<uint8_t*>(ext.d) : reinterpret_cast<uint8_t*>(D);
+      const uint32_t ldb = (uint32_t)ldo * kES;
+      // base and size made scalar: the compiler cannot see that they are uniform, and a
+      // resource in vector registers makes it loop over the lanes for every access
+      const uint64_t base = reinterpret_cast<uint64_t>(out + (m0 * ldo + n0) * kES);
+      const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)base);
+      const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(base >> 32));
+      const int64_t size = __builtin_amdgcn_readfirstlane((uint32_t)(((m1 - m0 - 1) * ldo + (n1 - n0)) * kES));
+      const __amdgpu_buffer_rsrc_t dr =
+          make_rsrc(reinterpret_cast<const void*>(((uint64_t)hi << 32) | lo), size);
+      uint32_t voff[kFragsN];
+      bool cok[kFragsN];
+#pragma unroll
+      for (int j = 0; j < kFragsN; ++j) {
+        const int cl = wn * kWaveN + 32 * j + r;                    // column within the tile
+        cok[j] = n0 + cl < n1;
+        voff[j] = cok[j] ? (uint32_t)(4 * h) * ldb + (uint32_t)cl * kES : kBeyond;
+      }
+      const int rlim = (int)(m1 - m0) - 4 * h;       // row (less the lane's 4h) inside iff below
+      auto row_of = [&](int i, int q) { return wm * kWaveM + 32 * i + 8 * (q >> 2) + (q & 3); };
+      auto take = [&](bool in, float v) {
+        if constexpr (EXT) mx = fmaxf(mx, in ? fabsf(v) : 0.0f);
+      };
+      if constexpr (EXT && KIND == kOutBF16) {
+        // rows q and q + 1 of the lane's column converted by one instruction
+#pragma unroll
+        for (int i = 0; i < kFragsM; ++i) {
+#pragma unroll
+          for (int q = 0; q < 16; q += 2) {
+            const int ri = row_of(i, q);
+#pragma unroll
+            for (int j = 0; j < kFragsN; ++j) {
+              const uint32_t b = bf16_rn_pair(acc[i][j][q] * alpha, acc[i][j][q + 1] * alpha);
+              const uint32_t o = voff[j] + (uint32_t)ri * ldb;
+              __builtin_amdgcn_raw_buffer_store_b16((uint16_t)b, dr, o, 0, 2);
+              __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(b >> 16), dr, o + ldb, 0, 2);
+              take(cok[j] && ri < rlim, __uint_as_float(b << 16));
+              take(cok[j] && ri + 1 < rlim, __uint_as_float(b & 0xFFFF0000u));
+            }
+          }
+        }
+      } else {
+        // FP32, non-temporal: D goes out to HBM while this compute-bound kernel runs instead of
+        // sitting dirty in the caches and being written back during the next kernel
+#pragma unroll
+        for (int i = 0; i < kFragsM; ++i) {
+#pragma unroll
+          for (int q = 0; q < 16; ++q) {
+            const int ri = row_of(i, q);
+#pragma unroll
+            for (int j = 0; j < kFragsN; ++j)
+              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][q] * alpha), dr,
+                                                    voff[j] + (uint32_t)ri * ldb, 0, 2);
+          }
+        }
+      }
+      if constexpr (EXT) {
+        if (ext.amax != nullptr) group_amax(mx, ext.amax);          // uniform
+      }
+      return;
+    }
+  }
   if constexpr (EXT && KIND == kOutF32Add) {
     if (!accumulate) {
       // D += tile: the old values of a row of fragments are all requested before any is
@@ -570,44 +648,6 @@ __device__ __forceinline__ void gemm_tile_big(Operand A, Operand B, int64_t m0, 
         }
       }
       if (ext.amax != nullptr) group_amax(mx, ext.amax);
-      return;
-    }
-  }
-  if constexpr (!EXT) {
-    if (!accumulate && ldd <= (int64_t(1) << 20)) {
-      // Plain FP32 stores through a buffer resource from the tile's corner to its last element
-      // inside D (row m1 - 1, column n1 - 1): stores of rows past m1 fall outside it and the
-      // buffer unit drops them, columns past n1 get an offset beyond any range. An element's
-      // offset is the lane's column offset (per j, a vector register) plus its row's offset
-      // (per i and q, uniform): no per-element bounds test or 64-bit address arithmetic, which
-      // cost about 8 us per 256 x 256 tile with one wave per SIMD. ldd <= 2^20 keeps every
-      // offset, pushed past the range or not, below 2^32.
-      // (base and size made scalar: the compiler cannot see that they are uniform, and a
-      // resource in vector registers makes it loop over the lanes for every store)
-      const uint32_t ld4 = (uint32_t)ldd * 4u;
-      const uint64_t base = reinterpret_cast<uint64_t>(D + m0 * ldd + n0);
-      const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)base);
-      const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(base >> 32));
-      const int64_t size = __builtin_amdgcn_readfirstlane((uint32_t)((m1 - m0 - 1) * ldd * 4 + (n1 - n0) * 4));
-      const __amdgpu_buffer_rsrc_t dr =
-          make_rsrc(reinterpret_cast<const void*>(((uint64_t)hi << 32) | lo), size);
-      uint32_t voff[kFragsN];
-#pragma unroll
-      for (int j = 0; j < kFragsN; ++j) {
-        const int cl = wn * kWaveN + 32 * j + r;                    // column within the tile
-        voff[j] = n0 + cl < n1 ? (uint32_t)(4 * h) * ld4 + (uint32_t)cl * 4u : kBeyond;
-      }
-#pragma unroll
-      for (int i = 0; i < kFragsM; ++i) {
-#pragma unroll
-        for (int q = 0; q < 16; ++q) {
-          const uint32_t ro = (uint32_t)(wm * kWaveM + 32 * i + 8 * (q >> 2) + (q & 3)) * ld4;
-#pragma unroll
-          for (int j = 0; j < kFragsN; ++j)          // non-temporal, as below
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][q] * alpha), dr,
-                                                  voff[j] + ro, 0, 2);
-        }
-      }
       return;
     }
   }
