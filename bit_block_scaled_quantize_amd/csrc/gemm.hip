@@ -1230,6 +1230,33 @@ void k_gemm_mx(Operand A, Operand B, int64_t K, float* __restrict__ D, int64_t l
     b_cur = b_next;
   }
   __builtin_amdgcn_s_waitcnt(big::waitcnt_imm(0, 15));
+  if (ldd <= (int64_t(1) << 20)) {
+    // stores through a buffer resource bounded at the tile's last element, as in the FP16-path
+    // kernel's epilogue: rows past m1 fall outside it, columns past n1 are pushed beyond it,
+    // and each element costs one add of a uniform row offset to the lane's column offset
+    const uint32_t ld4 = (uint32_t)ldd * 4u;
+    const uint64_t base = reinterpret_cast<uint64_t>(D + m0 * ldd + n0);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)base);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(base >> 32));
+    const int64_t size = __builtin_amdgcn_readfirstlane((uint32_t)(((m1 - m0 - 1) * ldd + (n1 - n0)) * 4));
+    const __amdgpu_buffer_rsrc_t dr = make_rsrc(reinterpret_cast<const void*>(((uint64_t)hi << 32) | lo), size);
+    uint32_t voff[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int cl = wn * 128 + 32 * j + r;
+      voff[j] = n0 + cl < n1 ? (uint32_t)(4 * h) * ld4 + (uint32_t)cl * 4u : kBeyond;
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const uint32_t ro = (uint32_t)(wm * 64 + 32 * i + 8 * (q >> 2) + (q & 3)) * ld4;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][q]), dr, voff[j] + ro, 0, 2);
+      }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
