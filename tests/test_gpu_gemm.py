@@ -197,6 +197,11 @@ def test_grouped_gemm_tile_shapes(n, k):
     (70, 33, [0, 1920]),                          # one group, ragged M and N
     (513, 300, [0, 640, 1280, 1344, 1920]),       # a 64-wide group inside one K step
     (448, 384, [0, 512, 1920]),                   # last row tile 192 high, last column 128 wide
+    # 24 groups x 5 row tiles (the last 76 high): 120 tiles on 32 workgroups, each walking four
+    # tiles whose shapes change along the walk (DMA of the next tile prefetched only between
+    # tiles of one shape), with empty groups and 64-wide groups between them
+    (1100, 200, [0, 64, 64, 192, 256, 448, 448, 512, 640, 704, 768, 1024, 1024, 1088, 1152, 1280,
+                 1344, 1408, 1408, 1536, 1600, 1664, 1728, 1856, 1920]),
 ])
 def test_grouped_gemm_k(m, n, offs):
     """GEMMs grouped along K (MoE weight gradient): each group's block against the FP64
