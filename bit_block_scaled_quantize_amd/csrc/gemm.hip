@@ -559,11 +559,13 @@ __device__ __forceinline__ void gemm_tile_big(Operand A, Operand B, int64_t m0, 
   // pitch of at most 2^20 elements keeps every offset, pushed past the range or not, below 2^32.
   {
     constexpr int kES = (EXT && KIND == kOutBF16) ? 2 : 4;          // output element bytes
-    // (the FP32 outputs with an amax or an accumulate keep the path further below: with this
-    // one their kernels spill registers)
-    constexpr bool kFast = !EXT || KIND == kOutBF16;
+    // (D += tile without an amax output adds by float atomics, fire and forget; the FP32
+    // outputs with an amax keep the path further below: with this one their kernels spill
+    // registers, holding the loaded old values)
+    constexpr bool kFast = !EXT || KIND == kOutBF16 || KIND == kOutF32Add;
     const int64_t ldo = EXT ? ext.ldd : ldd;
-    if (kFast && !accumulate && ldo <= (int64_t(1) << 20)) {
+    const bool no_amax_add = !(EXT && KIND == kOutF32Add) || ext.amax == nullptr;
+    if (kFast && !accumulate && no_amax_add && ldo <= (int64_t(1) << 20)) {
       uint8_t* const out = EXT ? static_cast<uint8_t*>(ext.d) : reinterpret_cast<uint8_t*>(D);
       const uint32_t ldb = (uint32_t)ldo * kES;
       // base and size made scalar: the compiler cannot see that they are uniform, and a
@@ -603,6 +605,20 @@ __device__ __forceinline__ void gemm_tile_big(Operand A, Operand B, int64_t m0, 
               take(cok[j] && ri < rlim, __uint_as_float(b << 16));
               take(cok[j] && ri + 1 < rlim, __uint_as_float(b & 0xFFFF0000u));
             }
+          }
+        }
+      } else if constexpr (EXT && KIND == kOutF32Add) {
+        // D += tile: one float atomic add per element, done where the line lives (L2), so the
+        // old values never come into registers and the epilogue does not wait for them
+#pragma unroll
+        for (int i = 0; i < kFragsM; ++i) {
+#pragma unroll
+          for (int q = 0; q < 16; ++q) {
+            const int ri = row_of(i, q);
+#pragma unroll
+            for (int j = 0; j < kFragsN; ++j)
+              (void)__builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(acc[i][j][q] * alpha, dr,
+                                                                   voff[j] + (uint32_t)ri * ldb, 0, 0);
           }
         }
       } else {

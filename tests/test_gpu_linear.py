@@ -101,6 +101,29 @@ def test_fp32_accumulate(mnk):
     assert_bytes_equal(out.cpu().numpy().view(np.uint32), ((d_old + d32) + d32).view(np.uint32), "twice")
 
 
+def test_fp32_accumulate_keeps_subnormals():
+    """D += A B^T (one K step, no split: each element gets one float atomic add) with a product of
+    exact zeros on a D holding subnormals of both signs, normals and signed zeros: one IEEE
+    addition per element, bit for bit (subnormals kept, -0 + 0 = +0)."""
+    m, n, k = 300, 520, 128
+    qa, _ = nv.quantize(to_device_bf16(workloads.normal_bf16((m, k), 3)), "1x16", "rn")
+    qb, _ = nv.quantize(torch.zeros((n, k), dtype=torch.bfloat16, device="cuda"), "1x16", "rn")
+    rng = np.random.default_rng(9)
+    bits = rng.integers(1, 1 << 23, (m, n), dtype=np.uint32)              # subnormal magnitudes
+    bits |= rng.integers(0, 2, (m, n)).astype(np.uint32) << 31
+    d_old = bits.view(np.float32).copy()
+    d_old[::7] = rng.standard_normal(d_old[::7].shape).astype(np.float32)
+    d_old[1, :] = 0.0
+    d_old[2, :] = -0.0
+    out = torch.from_numpy(d_old.copy()).cuda()
+    nv.gemm_ex(qa, qb, out=out, accumulate=True)
+    d = nv.gemm(qa, qb)
+    torch.cuda.synchronize()
+    d = d.cpu().numpy()
+    assert np.all(d == 0.0)
+    assert_bytes_equal(out.cpu().numpy().view(np.uint32), (d_old + d).view(np.uint32), "subnormals")
+
+
 def test_empty_output_clears_amax():
     full = nv.NVFP4Tensor.empty(16, 128)
     qa = nv.NVFP4Tensor(full.codes, full.scales, full.global_scale, 0, 128)   # M = 0
