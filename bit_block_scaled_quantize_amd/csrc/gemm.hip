@@ -548,10 +548,10 @@ __device__ __forceinline__ void gemm_tile_big(Operand A, Operand B, int64_t m0, 
   // D fragment layout (32 x 32): lane l holds column l % 32 and, for q = 0..15, row
   // 8*(q/4) + 4*(l/32) + q%4.
   float mx = 0.0f;
-  // Plain FP32 and BF16 outputs (not a K-split tile's partial sums) go through a buffer
-  // resource from the tile's corner to its last element in the output (row m1 - 1, column
-  // n1 - 1): stores to rows past m1 fall outside it and the buffer unit drops them, columns
-  // past n1 get an offset beyond any range. An element's offset is the lane's column offset
+  // Plain FP32 and BF16 outputs, and FP32 D += tile without an amax output (not a K-split
+  // tile's partial sums), go through a buffer resource from the tile's corner to its last
+  // element in the output (row m1 - 1, column n1 - 1): stores and atomics to rows past m1 fall
+  // outside it and the buffer unit drops them, columns past n1 get an offset beyond any range. An element's offset is the lane's column offset
   // (per j, a vector register) plus its row's offset (per i and q, uniform): no per-element
   // bounds test or 64-bit address arithmetic, which cost about 8 us per 256 x 256 tile with one
   // wave per SIMD. The maximum for the amax output counts only elements inside
