@@ -282,6 +282,51 @@ def test_amax_pair(shape, dtype, ld):
         assert g[0] == nv.amax(dev).cpu().numpy()[0]
 
 
+def _pair_vs_oracle(bits, what):
+    mask = workloads.wgrad_sign_mask()
+    got = nv.amax_pair(to_device_bf16(bits), mask)
+    torch.cuda.synchronize()
+    xf = f32(bits)
+    want = np.array([oracle.amax(xf)[0], oracle.amax(oracle.rht_columnwise(xf, mask))[0]], np.float32)
+    assert_bytes_equal(got.cpu().numpy().view(np.uint32), want.view(np.uint32), what)
+
+
+@pytest.mark.parametrize("tokens,cols", [(2048, 1024), (1024, 1000), (4096, 160)])
+def test_amax_pair_gaussian(tokens, cols):
+    """The BF16 pair on Gaussian data at sizes spanning many tiles, with column tiles cut by the
+    last column: bit for bit against the oracle."""
+    log(f"amax pair gaussian {tokens}x{cols}")
+    x = (np.random.default_rng(tokens + cols).standard_normal((tokens, cols)) * 1e-3).astype(np.float32)
+    _pair_vs_oracle((x.view(np.uint32) >> 16).astype(np.uint16), f"amax pair {tokens}x{cols}")
+
+
+def _planted_block(case):
+    j = np.arange(16)
+    if case == "zero":
+        return np.zeros(16, np.uint16)
+    if case.startswith("field"):                    # 3 binades wide, smallest exponent field f
+        f = int(case[5:])
+        return (((f + j % 3) << 7) | ((37 * j) & 0x7F) | np.where(j % 2 == 1, 0x8000, 0)).astype(np.uint16)
+    spread = int(case[6:])                          # one value 2^spread above the others
+    v = (((127 - spread) << 7) | ((29 * j) & 0x7F) | np.where(j % 3 == 1, 0x8000, 0)).astype(np.uint16)
+    v[5] = 0x3F80
+    return v
+
+
+@pytest.mark.parametrize("case", ["zero", "field9", "field10", "field11", "spread11", "spread12",
+                                  "spread13", "spread14", "spread30", "spread60", "spread118"])
+@pytest.mark.parametrize("col", [0, 1])
+def test_amax_pair_single_block(case, col):
+    """One 16-token block beside a zero column, so its maximum is the result: all zero, tiny
+    blocks (smallest exponent field 9, 10, 11), one value 11 to 118 binades above the others
+    (the binary64 butterfly's range and past it, the exact sums), in the even and the odd
+    column of a lane's pair."""
+    log(f"amax pair single block {case} col {col}")
+    bits = np.zeros((16, 2), np.uint16)
+    bits[:, col] = _planted_block(case)
+    _pair_vs_oracle(bits, f"single block {case} col {col}")
+
+
 @pytest.mark.parametrize("n,k,G", [(48, 272, 3), (1856, 160, 2), (16, 32, 5), (320, 144, 3), (64, 400, 5)])
 def test_16x16_segments_with_transpose(n, k, G):
     """An expert weight stack [G*n, k] quantized in 16x16 tiles with one tensor scale per
