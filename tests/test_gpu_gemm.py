@@ -334,3 +334,52 @@ def test_gemm_reproducible(mnk):
     d2 = nv.gemm(qa, qb)
     torch.cuda.synchronize()
     assert torch.equal(d1, d2)
+
+
+def test_output_row_pitch_past_the_buffer_range():
+    """Outputs with a row pitch above 2^20 elements take the indexed store path instead of the
+    tile-bounded buffer: plain FP32, BF16 with its amax, D += A B^T and the MXFP4 GEMM give the
+    same bits as into a compact output, and the columns beside the view stay untouched."""
+    log("gemm outputs with a row pitch past 2^20")
+    m, n, k = 300, 520, 128                         # one K step: no tile is split along K
+    pitch = (1 << 20) + 96
+    qa, qb, _, _ = _pair(m, n, k, 31)
+    sentinel = -7.0
+
+    def wide(dtype, fill=sentinel):
+        return torch.full((m, pitch), fill, dtype=dtype, device="cuda")
+
+    def check(big, ref, what):
+        torch.cuda.synchronize()
+        h = big[:, :n + 96].cpu()
+        assert torch.equal(h[:, :n], ref.cpu()), what
+        assert torch.all(h[:, n:] == sentinel), what + " (beside the view)"
+
+    ref = nv.gemm(qa, qb)
+    big = wide(torch.float32)
+    nv.gemm(qa, qb, out=big[:, :n])
+    check(big, ref, "fp32")
+
+    am_ref = torch.zeros((1,), device="cuda")
+    ref16 = nv.gemm_ex(qa, qb, out_dtype=torch.bfloat16, amax_out=am_ref)
+    big16 = wide(torch.bfloat16)
+    am = torch.zeros((1,), device="cuda")
+    nv.gemm_ex(qa, qb, out=big16[:, :n], out_dtype=torch.bfloat16, amax_out=am)
+    check(big16, ref16, "bf16")
+    assert torch.equal(am.cpu(), am_ref.cpu())
+
+    d_old = torch.randn((m, n), device="cuda")
+    acc_ref = d_old.clone()
+    nv.gemm_ex(qa, qb, out=acc_ref, accumulate=True)
+    bigacc = wide(torch.float32)
+    bigacc[:, :n] = d_old
+    nv.gemm_ex(qa, qb, out=bigacc[:, :n], accumulate=True)
+    check(bigacc, acc_ref, "accumulate")
+
+    xa = to_device_bf16(workloads.normal_bf16((m, k), 32))
+    xb = to_device_bf16(workloads.normal_bf16((n, k), 33, std=0.02))
+    ma, mb = nv.mx_quantize(xa), nv.mx_quantize(xb)
+    mref = nv.mx_gemm(ma, mb)
+    bigmx = wide(torch.float32)
+    nv.mx_gemm(ma, mb, out=bigmx[:, :n])
+    check(bigmx, mref, "mxfp4")
