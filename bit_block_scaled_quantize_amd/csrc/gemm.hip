@@ -744,6 +744,20 @@ void k_gemm_big(Operand A, const float* __restrict__ ag, Operand B, const float*
   const int64_t tiles_m = (A.rows + kBlockM - 1) / kBlockM;
   const int64_t tiles_n = (B.rows + kBlockN - 1) / kBlockN;
   const int64_t steps = (K + kStepK - 1) / kStepK;
+  // splits < 0: workgroups past tail_first take the last tiles in quarters of 64 columns, all
+  // of K (a last round of at most a quarter of the CUs then fills one round, with no atomics)
+  if (splits < 0 && (int64_t)blockIdx.x >= tail_first) {
+    const int64_t t = tail_first + ((int64_t)blockIdx.x - tail_first) / 4;
+    const int64_t quarter = ((int64_t)blockIdx.x - tail_first) % 4;
+    int64_t tm, tn;
+    tile_of(t, tiles_m, tiles_n, tm, tn);
+    const int64_t m0 = tm * kBlockM, n0 = tn * kBlockN + quarter * NTail::kBlockN;
+    if (n0 >= B.rows) return;                        // a narrower last column tile
+    const int64_t m1 = m0 + kBlockM < A.rows ? m0 + kBlockM : A.rows;
+    const int64_t n1 = n0 + NTail::kBlockN < B.rows ? n0 + NTail::kBlockN : B.rows;
+    gemm_tile_big<NTail>(A, B, m0, m1, n0, n1, K, 0, K, false, ag[0] * bg[0], D, ldd, lds_dyn);
+    return;
+  }
   // workgroups past tail_first share the last tiles, `splits` per tile, each over a K range
   int64_t t = blockIdx.x, s0 = 0, s1 = steps;
   if (t >= tail_first) {
@@ -803,6 +817,20 @@ void k_gemm_big_ext(Operand A, const float* __restrict__ ag, Operand B, const fl
   const int64_t tiles_m = (A.rows + kBlockM - 1) / kBlockM;
   const int64_t tiles_n = (B.rows + kBlockN - 1) / kBlockN;
   const int64_t steps = (K + kStepK - 1) / kStepK;
+  if (splits < 0 && (int64_t)blockIdx.x >= tail_first) {         // column quarters, as k_gemm_big
+    const int64_t t = tail_first + ((int64_t)blockIdx.x - tail_first) / 4;
+    const int64_t quarter = ((int64_t)blockIdx.x - tail_first) % 4;
+    int64_t tm, tn;
+    tile_of(t, tiles_m, tiles_n, tm, tn);
+    const int64_t m0 = tm * kBlockM, n0 = tn * kBlockN + quarter * NTail::kBlockN;
+    if (n0 >= B.rows) return;                        // a narrower last column tile
+    const int64_t m1 = m0 + kBlockM < A.rows ? m0 + kBlockM : A.rows;
+    const int64_t n1 = n0 + NTail::kBlockN < B.rows ? n0 + NTail::kBlockN : B.rows;
+    const ExtOut ext{D, ldd, nullptr, amax};
+    gemm_tile_big<NTail, false, KIND, true>(A, B, m0, m1, n0, n1, K, 0, K, false, ag[0] * bg[0], nullptr,
+                                            ldd, lds_dyn, ext);
+    return;
+  }
   int64_t t = blockIdx.x, s0 = 0, s1 = steps;
   const bool split = t >= tail_first;
   if (split) {
@@ -1398,13 +1426,20 @@ hipError_t enable_big_lds() {
 }
 
 // One workgroup per CU: when the tiles leave a partial last round of at most half the CUs,
-// its tiles (tail_first ..) are split along K in two halves. In launch_gemm the halves are
+// its tiles (tail_first ..) are split along K in two halves; a last round of at most a quarter
+// of the CUs is instead cut into column quarters (splits = -1: four 256 x 64 tiles per tile,
+// all of K, one round, no partial sums). In launch_gemm the halves are
 // atomically added into zeroed D: two parts keep D reproducible (0 + a + b rounds the same in
 // either order); more parts would make the rounding depend on the order the atomics land in.
 void split_plan(int64_t tiles, int64_t K, int64_t& tail_first, int64_t& splits) {
   const int64_t cus = compute_units();
   const int64_t steps = (K + kStepK - 1) / kStepK;
   const int64_t rem = tiles % cus;
+  if (rem && 4 * rem <= cus) {                     // column quarters: splits = -1
+    tail_first = tiles - rem;
+    splits = -1;
+    return;
+  }
   splits = rem ? cus / rem : 1;
   splits = splits > 2 ? 2 : splits;
   splits = splits > steps ? steps : splits;
@@ -1428,6 +1463,11 @@ hipError_t launch_gemm(GemmOperand a, GemmOperand b, int64_t M, int64_t N, int64
     const int64_t tiles = big_tiles(M, N);
     int64_t tail_first, splits;
     split_plan(tiles, K, tail_first, splits);
+    if (splits < 0) {
+      hipLaunchKernelGGL(k_gemm_big, dim3((unsigned)(tail_first + 4 * (tiles - tail_first))), dim3(kThreads),
+                         big::kLdsBytes, stream, A, a.global_scale, B, b.global_scale, K, D, ldd, tail_first, -1);
+      return hipGetLastError();
+    }
     if (tail_first < tiles) {
       const int vec = (ldd % 4) == 0 && (reinterpret_cast<uintptr_t>(D) % 16) == 0;
       hipLaunchKernelGGL(k_zero_tiles, dim3((unsigned)((tiles - tail_first) * kZeroParts)), dim3(kThreads), 0,
@@ -1462,6 +1502,7 @@ size_t gemm_ex_workspace_bytes(int64_t M, int64_t N) {
   const int64_t tiles = big_tiles(M, N);
   int64_t tail_first, splits;
   split_plan(tiles, 2 * kStepK, tail_first, splits);          // any K of two or more steps
+  if (splits < 2) return 0;                                   // no K-split tiles (column quarters)
   return (size_t)(tiles - tail_first) * (size_t)splits * big::kBlockM * big::kBlockN * sizeof(float);
 }
 
@@ -1479,11 +1520,11 @@ hipError_t launch_gemm_ex(GemmOperand a, GemmOperand b, int64_t M, int64_t N, in
     const int64_t tiles = big_tiles(M, N);
     int64_t tail_first, splits;
     split_plan(tiles, K, tail_first, splits);
-    const int64_t grid = tail_first + (tiles - tail_first) * splits;
+    const int64_t grid = tail_first + (tiles - tail_first) * (splits < 0 ? 4 : splits);
 #define NVFP4_GX(KD)                                                                                  \
   hipLaunchKernelGGL(k_gemm_big_ext<KD>, dim3((unsigned)grid), dim3(kThreads), big::kLdsBytes, stream, \
                      A, a.global_scale, B, b.global_scale, K, D, ldd, amax, ws, tail_first, (int)splits); \
-  if (tail_first < tiles)                                                                             \
+  if (tail_first < tiles && splits > 0)                                                               \
     hipLaunchKernelGGL(k_split_fixup<KD>, dim3((unsigned)((tiles - tail_first) * kZeroParts)),         \
                        dim3(kThreads), 0, stream, M, N, D, ldd, ws, tail_first, amax)
     if (kind == kOutBF16) { NVFP4_GX(kOutBF16); }

@@ -283,9 +283,11 @@ int nvfp4_gemm(const nvfp4_tensor* A, const nvfp4_tensor* B, float* D, int64_t l
  *              BF16 rounding; after the addition when accumulating). The library clears it.
  *   workspace  device scratch of nvfp4_workspace_size(NVFP4_OP_GEMM_EX, M, N, 1) bytes, sized
  *              for the current device, 256-byte aligned (0 bytes, NULL allowed, when the
- *              tiles fill whole rounds of the device's compute units): a partial last round
- *              is split along K and the two halves' sums meet there (lower half first), so D
- *              is reproducible.
+ *              tiles fill whole rounds of the device's compute units, or leave a last round of
+ *              at most a quarter of them, which is then computed as 64-column quarters of its
+ *              tiles over all of K): a partial last round of more than a quarter and at most
+ *              half of the compute units is split along K and the two halves' sums meet there
+ *              (lower half first), so D is reproducible.
  * The result is deterministic for a given device. Errors: NVFP4_ERR_INVALID (null pointers,
  * K mismatch, K % 16, ldd < N, bad kind, misaligned D), NVFP4_ERR_WORKSPACE, NVFP4_ERR_HIP.
  */

@@ -193,7 +193,9 @@ def test_workspace_sizes(lib):
     # split tile (sizes for 256 compute units, the count assumed without a device)
     assert lib.nvfp4_workspace_size(nv.OP_GEMM_EX, 8192, 20480, 1) == 0          # 10 whole rounds
     assert lib.nvfp4_workspace_size(nv.OP_GEMM_EX, 8192, 5120, 1) == 128 * 2 * 256 * 256 * 4
-    assert lib.nvfp4_workspace_size(nv.OP_GEMM_EX, 20480, 5120, 1) == 64 * 2 * 256 * 256 * 4
+    # 64 tiles left over (a quarter of the units or fewer): each becomes four 256 x 64 column
+    # tiles over all of K, with no partial tiles to park
+    assert lib.nvfp4_workspace_size(nv.OP_GEMM_EX, 20480, 5120, 1) == 0
     assert lib.nvfp4_workspace_size(nv.OP_GEMM_EX, 256 * 200, 256, 1) == 0       # 200 > 128 left over
 
 
