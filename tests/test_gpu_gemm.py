@@ -76,14 +76,32 @@ def test_gemm_output_row_stride_and_sr_operand():
     o = out.cpu().numpy()
     assert np.all(o[:, 90:] == -7.0)
     assert_gemm_within_bound(o[:, :90], ah, bh, "gemm ldd")
-    # odd row stride and a D that is not 16-byte aligned (the K-split tile is zeroed by
-    # scalar stores), neighbours untouched
+    # odd row stride and a D that is not 16-byte aligned, neighbours untouched
     out2 = torch.full((70, 131), -7.0, dtype=torch.float32, device="cuda")
     nv.gemm(qa, qb, out=out2[:, 1:91])
     torch.cuda.synchronize()
     o2 = out2.cpu().numpy()
     assert np.all(o2[:, 0] == -7.0) and np.all(o2[:, 91:] == -7.0)
     assert np.array_equal(o2[:, 1:91], o[:, :90])
+
+
+def test_gemm_k_split_tail_output_stride():
+    """90 tiles of 256 x 256 on 256 CUs leave a last round of more than a quarter of them: those
+    tiles are zeroed and split along K in two halves added with atomics. Into an odd row stride
+    at a D off 16-byte alignment (zeroed by scalar stores) the result equals the compact one bit
+    for bit, within the bound, and the neighbouring columns stay untouched."""
+    m, n, k = 2304, 2560, 256
+    log(f"gemm K-split tail, strided D {(m, n, k)}")
+    qa, qb, ah, bh = _pair(m, n, k, 41)
+    d = nv.gemm(qa, qb)
+    out = torch.full((m, n + 3), -7.0, dtype=torch.float32, device="cuda")
+    nv.gemm(qa, qb, out=out[:, 1:n + 1])
+    torch.cuda.synchronize()
+    o = out.cpu().numpy()
+    assert np.all(o[:, 0] == -7.0) and np.all(o[:, n + 1:] == -7.0)
+    ref = d.cpu().numpy()
+    assert np.array_equal(o[:, 1:n + 1], ref)
+    assert_gemm_within_bound(ref, ah, bh, "gemm K-split tail")
 
 
 def test_gemm_zero_and_one_hot():

@@ -36,9 +36,11 @@ def _bf16_values(t):
     return t.view(torch.int16).cpu().numpy().view(np.uint16).astype(np.uint32) << 16
 
 
-# K >= 256 with few tiles: every tile is split along K (workspace + fixup); K = 128: one step,
-# no split; K % 64 != 0: the general kernel
-SHAPES = [(300, 520, 512), (257, 33, 128), (1000, 700, 1344), (130, 257, 272), (64, 64, 2688)]
+# A last round of at most a quarter of the 256 CUs: 256 x 64 column quarters over all of K;
+# (2304, 2560, 256), 90 tiles: split along K (workspace + fixup); K = 128: one step, no split;
+# K % 64 != 0: the general kernel
+SHAPES = [(300, 520, 512), (257, 33, 128), (1000, 700, 1344), (130, 257, 272), (64, 64, 2688),
+          (2304, 2560, 256)]
 
 
 @pytest.mark.parametrize("mnk", SHAPES)
@@ -138,8 +140,8 @@ def test_empty_output_clears_amax():
 
 @pytest.mark.parametrize("shape", [(8192, 5120, 20480), (20480, 5120, 8192)])
 def test_full_size_bf16_and_accumulate(shape):
-    """The dense layer's activation-gradient and weight-gradient shapes (partial last rounds,
-    K split through the workspace): BF16 = rn(FP32 result) and D_old + FP32 result on every
+    """The dense layer's activation-gradient and weight-gradient shapes (partial last rounds:
+    128 tiles split along K through the workspace, 64 tiles cut into column quarters): BF16 = rn(FP32 result) and D_old + FP32 result on every
     element; the FP32 result itself is checked against the oracle on sampled elements by the
     dense GEMM tests."""
     m, n, k = shape
