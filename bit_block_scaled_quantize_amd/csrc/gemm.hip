@@ -736,6 +736,23 @@ __device__ __forceinline__ void gemm_tile_big(Operand A, Operand B, int64_t m0, 
   }
 }
 
+// Workgroup b (b < 4 rem) of the column quarters of the last rem tiles: its tile (counted from
+// the first of them) and quarter. Each run of 32 consecutive workgroups takes 8 tiles with the
+// four quarters of a tile 8 workgroups apart, so the four run on one XCD (workgroups are dealt
+// to the 8 XCDs round robin) and read the tile's A panel through one L2; the last rem % 8
+// tiles take the remaining workgroups in order.
+__device__ __forceinline__ void quarter_of(int64_t b, int64_t rem, int64_t& tile, int64_t& quarter) {
+  const int64_t whole = rem / 8 * 32;
+  if (b < whole) {
+    tile = b / 32 * 8 + b % 8;
+    quarter = b % 32 / 8;
+  } else {
+    const int64_t r = rem % 8, c = b - whole;                  // r > 0 here
+    tile = rem / 8 * 8 + c % r;
+    quarter = c / r;
+  }
+}
+
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_gemm_big(Operand A, const float* __restrict__ ag, Operand B, const float* __restrict__ bg,
                 int64_t K, float* __restrict__ D, int64_t ldd, int64_t tail_first, int splits) {
@@ -747,8 +764,9 @@ void k_gemm_big(Operand A, const float* __restrict__ ag, Operand B, const float*
   // splits < 0: workgroups past tail_first take the last tiles in quarters of 64 columns, all
   // of K (a last round of at most a quarter of the CUs then fills one round, with no atomics)
   if (splits < 0 && (int64_t)blockIdx.x >= tail_first) {
-    const int64_t t = tail_first + ((int64_t)blockIdx.x - tail_first) / 4;
-    const int64_t quarter = ((int64_t)blockIdx.x - tail_first) % 4;
+    int64_t tile, quarter;
+    quarter_of((int64_t)blockIdx.x - tail_first, tiles_m * tiles_n - tail_first, tile, quarter);
+    const int64_t t = tail_first + tile;
     int64_t tm, tn;
     tile_of(t, tiles_m, tiles_n, tm, tn);
     const int64_t m0 = tm * kBlockM, n0 = tn * kBlockN + quarter * NTail::kBlockN;
@@ -818,8 +836,9 @@ void k_gemm_big_ext(Operand A, const float* __restrict__ ag, Operand B, const fl
   const int64_t tiles_n = (B.rows + kBlockN - 1) / kBlockN;
   const int64_t steps = (K + kStepK - 1) / kStepK;
   if (splits < 0 && (int64_t)blockIdx.x >= tail_first) {         // column quarters, as k_gemm_big
-    const int64_t t = tail_first + ((int64_t)blockIdx.x - tail_first) / 4;
-    const int64_t quarter = ((int64_t)blockIdx.x - tail_first) % 4;
+    int64_t tile, quarter;
+    quarter_of((int64_t)blockIdx.x - tail_first, tiles_m * tiles_n - tail_first, tile, quarter);
+    const int64_t t = tail_first + tile;
     int64_t tm, tn;
     tile_of(t, tiles_m, tiles_n, tm, tn);
     const int64_t m0 = tm * kBlockM, n0 = tn * kBlockN + quarter * NTail::kBlockN;
