@@ -104,6 +104,27 @@ def test_gemm_k_split_tail_output_stride():
     assert_gemm_within_bound(ref, ah, bh, "gemm K-split tail")
 
 
+def test_column_quarters_equal_whole_tiles():
+    """A GEMM whose tiles leave a last round of at most a quarter of the CUs computes it as 256 x
+    64 column quarters; every output element still sums the same products in the same order as
+    in a whole 256 x 256 tile. So a 600 x 700 GEMM (9 tiles, all in quarters) equals bit for bit
+    the same rows and columns of a 4096 x 4096 GEMM of the same operands (256 whole tiles, one
+    round on 256 CUs)."""
+    log("column quarters = whole tiles")
+    m = n = 4096
+    k = 256
+    rng = np.random.default_rng(77)
+    qa, _ = nv.quantize(torch.from_numpy(rng.standard_normal((m, k)).astype(np.float32)).cuda(), "1x16", "rn")
+    qb, _ = nv.quantize(torch.from_numpy(rng.standard_normal((n, k)).astype(np.float32)).cuda(), "1x16", "sr",
+                        seed=3)
+    big = nv.gemm(qa, qb)
+    sa = nv.NVFP4Tensor(qa.codes, qa.scales, qa.global_scale, 600, k)
+    sb = nv.NVFP4Tensor(qb.codes, qb.scales, qb.global_scale, 700, k)
+    small = nv.gemm(sa, sb)
+    torch.cuda.synchronize()
+    assert torch.equal(small, big[:600, :700])
+
+
 def test_gemm_zero_and_one_hot():
     log("gemm special operands")
     k = 64
