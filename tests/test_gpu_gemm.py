@@ -202,7 +202,8 @@ def test_grouped_gemm_tile_shapes(n, k):
     """The LDS-staged grouped kernel (K % 64 == 0) with every tile shape it picks: full
     256 x 256 tiles, 128-row tiles for a group's last slot of at most 128 rows, and 64- or
     128-wide tiles for a last column of at most 64 or 128, over empty, tiny, exactly-128/256
-    and multi-slot groups."""
+    and multi-slot groups. Every row within bound, and each group's rows equal to the plain
+    GEMM of that group's operands bit for bit."""
     log(f"grouped gemm tiles n={n} k={k}")
     rows = [0, 5, 130, 128, 300, 513, 256, 1, 0, 129]
     G = len(rows)
@@ -228,6 +229,18 @@ def test_grouped_gemm_tile_shapes(n, k):
     bound = oracle.grouped_gemm_bound(xh, wh, off, n)
     assert np.all(np.abs(o[:, :n] - d64) <= bound)
     del d
+    # each group's rows equal the plain GEMM of that group's operands bit for bit: the tile
+    # shapes differ, the products and their order per element do not
+    for g in range(G):
+        r0, r1 = int(off[g]), int(off[g + 1])
+        if r1 == r0:
+            continue
+        ag = nv.NVFP4Tensor(qx.codes[r0:r1], qx.scales[r0:r1], qx.global_scale[g:g + 1], r1 - r0, k)
+        bg = nv.NVFP4Tensor(qw.codes[g * n:(g + 1) * n], qw.scales[g * n:(g + 1) * n],
+                            qw.global_scale[g:g + 1], n, k)
+        dg = nv.gemm(ag, bg)
+        torch.cuda.synchronize()
+        assert torch.equal(dg, out[r0:r1, :n]), f"group {g}"
 
 
 @pytest.mark.parametrize("m,n,offs", [
