@@ -89,26 +89,6 @@ __device__ __forceinline__ void tile_of(int64_t bid, int64_t tiles_m, int64_t ti
   tn = in_band / gm;
 }
 
-// Number of m-tile slots of height bm over all groups, offsets clamped as group_of clamps
-// them. The whole workgroup (all threads) calls it.
-__device__ __forceinline__ int64_t count_slots(int64_t G, const int64_t* __restrict__ off,
-                                               int64_t total_m, int64_t bm) {
-  __shared__ int64_t part[4];
-  int64_t n = 0;
-  for (int64_t q = threadIdx.x; q < G; q += 256) {
-    int64_t lo = off[q];
-    lo = lo < 0 ? 0 : (lo > total_m ? total_m : lo);
-    int64_t hi = off[q + 1];
-    hi = hi < lo ? lo : (hi > total_m ? total_m : hi);
-    n += (hi - lo + bm - 1) / bm;
-  }
-#pragma unroll
-  for (int d = 32; d > 0; d >>= 1) n += __shfl_xor(n, d);
-  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = n;
-  __syncthreads();
-  return part[0] + part[1] + part[2] + part[3];
-}
-
 // Group g and rows [m0, m1) of m-tile slot `slot_m` for tiles of height bm; false past the
 // last slot. The whole workgroup (256 threads, all of which must call it) searches: thread q
 // counts the slots of group c + q, a workgroup prefix sum over those counts brackets slot_m.
@@ -157,6 +137,117 @@ __device__ __forceinline__ bool group_of(int64_t G, const int64_t* __restrict__ 
   m0 = found[1];
   m1 = found[2];
   return g >= 0;
+}
+
+// Rows [lo, hi) of group g (offsets clamped as group_of clamps them) in 256-row slots: `full`
+// slots of 256 rows (the last of them cut at hi when more than 128 rows remain for it) and, when
+// 1..128 rows remain, one short slot, which the 128 x 256 tiles compute.
+__device__ __forceinline__ void group_slots(const int64_t* __restrict__ off, int64_t g, int64_t total_m,
+                                            int64_t& lo, int64_t& hi, int& full, int& shrt) {
+  lo = off[g];
+  lo = lo < 0 ? 0 : (lo > total_m ? total_m : lo);
+  hi = off[g + 1];
+  hi = hi < lo ? lo : (hi > total_m ? total_m : hi);
+  const int64_t m = hi - lo, rem = m % 256;
+  full = (int)(m / 256) + (rem > 128 ? 1 : 0);
+  shrt = rem > 0 && rem <= 128 ? 1 : 0;
+}
+
+// Tile j of XCD xcd in the grouped GEMM with 256-row slots: group g, rows [m0, m1) and column
+// tile tn; false past the XCD's tiles. Full-height slots are numbered over all groups in group
+// order, short slots likewise (F and Sh of them), and the two numberings are merged into one
+// slot order with the short slots spread evenly: position r (of T = F + Sh) is short iff
+// floor((r + 1) Sh / T) > floor(r Sh / T), and is then short slot floor(r Sh / T), else full
+// slot r - floor(r Sh / T). A short slot costs about 0.6 of a full one and short slots cluster
+// where the groups are small, so giving each XCD equal shares of one slot numbering left one XCD
+// with 15% more work than another on a Zipf-routed expert layer, and whole slots per XCD one
+// with a slot more than the rest. XCD x instead takes an equal run of the tiles before column
+// cols_main in merged slot order ([L x / 8, L (x + 1) / 8) of L = T cols_main, slot by slot, the
+// same mix of both kinds everywhere), then, when cols_main < tiles_n, the last column tiles of
+// the merged slots [T x / 8, T (x + 1) / 8) (narrowest last, to fill the gaps at the end; by
+// then a slot's A panel has long left the XCD's L2 wherever it ran). The whole workgroup (all
+// 256 threads) calls it: thread q walks groups [q p, q p + p), p = ceil(G / 256), twice (the
+// offsets come from the cache the second time), with one workgroup scan between.
+__device__ __forceinline__ bool grouped_slot(int64_t G, const int64_t* __restrict__ off, int64_t total_m,
+                                             int64_t xcd, int64_t j, int64_t cols_main, int64_t tiles_n,
+                                             int64_t& g, int64_t& m0, int64_t& m1, int64_t& tn) {
+  __shared__ int wsum[2][4];
+  __shared__ int64_t found[3];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t per = (G + 255) / 256;
+  const int64_t g0 = (int64_t)threadIdx.x * per < G ? (int64_t)threadIdx.x * per : G;
+  const int64_t g1 = g0 + per < G ? g0 + per : G;
+  int nf = 0, ns = 0;
+  for (int64_t q = g0; q < g1; ++q) {
+    int64_t lo, hi;
+    int f, sh;
+    group_slots(off, q, total_m, lo, hi, f, sh);
+    nf += f;
+    ns += sh;
+  }
+  int cf = nf, cs = ns;                           // inclusive scans within the wave
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int yf = __shfl_up(cf, d), ys = __shfl_up(cs, d);
+    if (lane >= d) {
+      cf += yf;
+      cs += ys;
+    }
+  }
+  if (lane == 63) {
+    wsum[0][wave] = cf;
+    wsum[1][wave] = cs;
+  }
+  __syncthreads();
+  int64_t bf = cf - nf, bs = cs - ns, F = 0, Sh = 0;
+  for (int w = 0; w < 4; ++w) {
+    if (w < wave) {
+      bf += wsum[0][w];
+      bs += wsum[1][w];
+    }
+    F += wsum[0][w];
+    Sh += wsum[1][w];
+  }
+  const int64_t T = F + Sh, L = T * cols_main;
+  const int64_t la = L * xcd / 8, nl = L * (xcd + 1) / 8 - la;
+  const int64_t ta = T * xcd / 8, nt = cols_main < tiles_n ? T * (xcd + 1) / 8 - ta : 0;
+  int64_t r;                                      // merged slot position
+  if (j < nl) {
+    r = (la + j) / cols_main;
+    tn = (la + j) % cols_main;
+  } else if (j < nl + nt) {
+    r = ta + (j - nl);
+    tn = tiles_n - 1;
+  } else {
+    return false;                                 // uniform over the workgroup
+  }
+  const int64_t before = r * Sh / T;              // short slots at merged positions < r
+  const bool is_short = (r + 1) * Sh / T > before;
+  const int64_t idx = is_short ? before : r - before;
+  // the one thread whose groups hold slot idx of its kind finds the group and its rows
+  const int64_t base = is_short ? bs : bf, cnt = is_short ? ns : nf;
+  if (idx >= base && idx < base + cnt) {
+    int64_t run = base;
+    for (int64_t q = g0; q < g1; ++q) {
+      int64_t lo, hi;
+      int f, sh;
+      group_slots(off, q, total_m, lo, hi, f, sh);
+      const int c = is_short ? sh : f;
+      if (idx < run + c) {
+        const int64_t r0 = lo + 256 * (is_short ? (int64_t)f : idx - run);
+        found[0] = q;
+        found[1] = r0;
+        found[2] = r0 + 256 < hi ? r0 + 256 : hi;
+        break;
+      }
+      run += c;
+    }
+  }
+  __syncthreads();
+  g = found[0];
+  m0 = found[1];
+  m1 = found[2];
+  return true;
 }
 
 struct Operand {
@@ -264,6 +355,7 @@ using MTail = Cfg<4, 2, 1, 4>;    // 128 x 256 (a group's last row slot at most 
 using NHalf = Cfg<4, 2, 2, 2>;    // 256 x 128 (a last column tile at most 128 wide)
 constexpr int kBlockM = Full::kBlockM, kBlockN = Full::kBlockN;
 constexpr int kLdsBytes = Full::kLdsBytes;
+static_assert(kBlockM == 256 && MTail::kBlockM == 128, "the slots of grouped_slot");
 static_assert(NTail::kLdsBytes <= kLdsBytes && MTail::kLdsBytes <= kLdsBytes &&
               NHalf::kLdsBytes <= kLdsBytes, "LDS");
 
@@ -916,26 +1008,12 @@ void k_grouped_gemm_big(int64_t G, const int64_t* __restrict__ off, Operand A,
   // A last column at most 128 wide is computed by the narrower 256 x 64 / 256 x 128 tiles.
   const bool narrow_last = tiles_n > 1 && N - (tiles_n - 1) * kBlockN <= NHalf::kBlockN;
   const int64_t cols_main = narrow_last ? tiles_n - 1 : tiles_n;
-  // Workgroups are dealt to the 8 XCDs round robin (XCD x runs ids x, x + 8, ...). XCD x takes
-  // the slots [S x / 8, S (x + 1) / 8) of the S real ones whole: every column tile of a slot
-  // runs on one XCD, so the slot's A panel and its group's B panels enter that XCD's L2 once,
-  // and the XCDs get equal shares of real slots. Its full-width tiles go first, slot by slot,
-  // then its narrow last-column tiles, which fill the gaps at the end.
-  const int64_t S = count_slots(G, off, A.rows, kBlockM);
-  const int64_t xcd = blockIdx.x % 8, j = blockIdx.x / 8;
-  const int64_t sa = S * xcd / 8, ns = S * (xcd + 1) / 8 - sa;
-  int64_t slot_m, tn;
-  if (j < ns * cols_main) {
-    slot_m = sa + j / cols_main;
-    tn = j % cols_main;
-  } else if (j < ns * tiles_n) {
-    slot_m = sa + (j - ns * cols_main);
-    tn = tiles_n - 1;
-  } else {
-    return;                                                  // uniform over the workgroup
-  }
-  int64_t g, m0, m1;
-  if (!group_of(G, off, A.rows, kBlockM, slot_m, g, m0, m1)) return;
+  // Workgroups are dealt to the 8 XCDs round robin (XCD x runs ids x, x + 8, ...), and XCD x
+  // takes its share of the slots whole (grouped_slot): every column tile of a slot runs on one
+  // XCD, so the slot's A panel and its group's B panels enter that XCD's L2 once.
+  int64_t g, m0, m1, tn;
+  if (!grouped_slot(G, off, A.rows, blockIdx.x % 8, blockIdx.x / 8, cols_main, tiles_n, g, m0, m1, tn))
+    return;
   const int64_t n0 = tn * kBlockN;
   const int64_t n1 = n0 + kBlockN < N ? n0 + kBlockN : N;
   const Operand Bg{B.codes + g * N * (K >> 1), B.scales + g * N * (K >> 4), N};
@@ -1572,8 +1650,10 @@ hipError_t launch_grouped_gemm(int64_t G, const int64_t* m_offsets, GemmOperand 
     if (e != hipSuccess) return e;
     const int64_t tiles_n = (N + big::kBlockN - 1) / big::kBlockN;
     const int64_t slots_m = total_m / big::kBlockM + G;       // >= sum_g ceil(M_g / 256)
-    // 8 XCDs, each with at most ceil(slots_m / 8) slots of tiles_n tiles
-    hipLaunchKernelGGL(k_grouped_gemm_big, dim3((unsigned)(8 * ((slots_m + 7) / 8) * tiles_n)),
+    // 8 XCDs, each with at most ceil(T c / 8) + ceil(T / 8) <= ceil(T tiles_n / 8) + 1 tiles
+    // (T <= slots_m slots, c + 1 = tiles_n column tiles before the last when that one is narrow;
+    // ceil(T tiles_n / 8) when it is not)
+    hipLaunchKernelGGL(k_grouped_gemm_big, dim3((unsigned)(8 * ((slots_m * tiles_n + 7) / 8 + 1))),
                        dim3(kThreads), big::kLdsBytes, stream, G, m_offsets, A, a.global_scale, B,
                        b.global_scale, N, K, D, ldd);
   } else {
