@@ -1053,7 +1053,13 @@ __device__ __forceinline__ KTile ktile_of(int64_t b, int64_t tiles, int64_t tile
   KTile t;
   t.g = b / tiles;
   int64_t tm, tn;
-  tile_of(b - t.g * tiles, tiles_m, tiles_n, tm, tn);
+  // the XCD region of the group's tile grid (tile_of deals regions by the id's residue mod 8)
+  // rotated by the group: the cheaper narrow tiles of the last tile row and column fall in a few
+  // regions, which with a fixed assignment went to the same XCDs for every group (one XCD
+  // finished 15% of the call early on the expert layer)
+  // (within whole runs of 8 ids only, so the ids stay a permutation of [0, tiles))
+  const int64_t q = b - t.g * tiles, q8 = q - q % 8;
+  tile_of(q8 + 8 <= tiles ? q8 + (q % 8 + t.g) % 8 : q, tiles_m, tiles_n, tm, tn);
   int64_t k0 = koff[t.g], k1 = koff[t.g + 1];
   k0 = k0 < 0 ? 0 : (k0 > K ? K : k0);
   k1 = k1 < k0 ? k0 : (k1 > K ? K : k1);
