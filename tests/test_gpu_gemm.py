@@ -243,6 +243,46 @@ def test_grouped_gemm_tile_shapes(n, k):
         assert torch.equal(dg, out[r0:r1, :n]), f"group {g}"
 
 
+def test_grouped_gemm_clustered_short_groups():
+    """48 groups, the first 24 of 300-900 rows and the last 24 of 1-128 rows (so every short
+    slot sits at the end of the slot numbering), N = 1856 (seven full column tiles and a 64-wide
+    last one): the XCDs take equal runs of one slot order with the short slots spread through
+    it and split runs inside slots. Every group's rows equal the plain GEMM of its operands bit
+    for bit, all rows are within bound of the FP64 GEMM, and the columns past N stay untouched."""
+    n, k = 1856, 128
+    rng = np.random.default_rng(90)
+    rows = list(rng.integers(300, 901, 24)) + list(rng.integers(1, 129, 24))
+    G = len(rows)
+    log(f"grouped gemm clustered short groups G={G} rows={sum(rows)}")
+    off = np.concatenate([[0], np.cumsum(rows)]).astype(np.int64)
+    x_bits = workloads.normal_bf16((int(off[-1]), k), 91)
+    w_bits = workloads.normal_bf16((G * n, k), 92)
+    offd = torch.from_numpy(off).cuda()
+    wseg = np.arange(G + 1, dtype=np.int64) * n
+    qx, _ = nv.quantize(to_device_bf16(x_bits), "1x16", "rn", segments=offd)
+    qw, _ = nv.quantize(to_device_bf16(w_bits), "16x16", "rn", segments=torch.from_numpy(wseg).cuda())
+    out = torch.full((int(off[-1]), n + 2), -5.0, dtype=torch.float32, device="cuda")
+    nv.grouped_gemm(offd, qx, qw, n, out=out[:, :n])
+    torch.cuda.synchronize()
+    o = out.cpu().numpy()
+    assert np.all(o[:, n:] == -5.0)
+    rx = oracle.quantize_1x16(f32(x_bits), segments=off)
+    rw = oracle.quantize_16x16(f32(w_bits), segments=wseg)
+    xh = oracle.dequantize(*rx, segments=off)
+    wh = oracle.dequantize(*rw, segments=wseg)
+    d64 = oracle.grouped_gemm_fp64(xh, wh, off, n)
+    bound = oracle.grouped_gemm_bound(xh, wh, off, n)
+    assert np.all(np.abs(o[:, :n] - d64) <= bound)
+    for g in range(G):
+        r0, r1 = int(off[g]), int(off[g + 1])
+        ag = nv.NVFP4Tensor(qx.codes[r0:r1], qx.scales[r0:r1], qx.global_scale[g:g + 1], r1 - r0, k)
+        bg = nv.NVFP4Tensor(qw.codes[g * n:(g + 1) * n], qw.scales[g * n:(g + 1) * n],
+                            qw.global_scale[g:g + 1], n, k)
+        dg = nv.gemm(ag, bg)
+        torch.cuda.synchronize()
+        assert torch.equal(dg, out[r0:r1, :n]), f"group {g}"
+
+
 @pytest.mark.parametrize("m,n,offs", [
     (300, 520, [0, 64, 64, 448, 1024, 1920]),     # empty group, half steps at both ends
     (256, 256, [128, 192, 1856]),                 # groups not starting at 0 / ending before K
