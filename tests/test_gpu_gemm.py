@@ -294,6 +294,9 @@ def test_grouped_gemm_clustered_short_groups():
     # tiles of one shape), with empty groups and 64-wide groups between them
     (1100, 200, [0, 64, 64, 192, 256, 448, 448, 512, 640, 704, 768, 1024, 1024, 1088, 1152, 1280,
                  1344, 1408, 1408, 1536, 1600, 1664, 1728, 1856, 1920]),
+    # 5 x 3 = 15 tiles per group: one whole run of 8 tile ids, whose XCD regions rotate with the
+    # group index, and a partial run of 7 that keeps its order; 11 groups cover every rotation
+    (1100, 600, [0, 128, 256, 256, 640, 768, 1024, 1152, 1280, 1536, 1792, 1920]),
 ])
 def test_grouped_gemm_k(m, n, offs):
     """GEMMs grouped along K (MoE weight gradient): each group's block against the FP64
